@@ -1,0 +1,334 @@
+/*
+ * path_oracle.c -- plain, slow fp64 CPU oracle for PaTH attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the bench's CPU-baseline
+ * leg do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes (PaTH summary, gist.science/ko/paper/2505.16381, section 2
+ * "core mechanism"): causal softmax attention whose logit for query i and key
+ * j <= i is
+ *
+ *     z_ij = scale * k_j^T (H_{j+1} H_{j+2} ... H_i) q_i  (+ PaTH-FoX bias)
+ *     H_s  = I - beta_s w_s w_s^T
+ *
+ * The product is written in increasing s from left to right: this is the order
+ * fixed by the summary's inference rule (section 3: cached keys are updated in
+ * place with the newest transition, k_j <- H_t k_j, which gives
+ * (H_i...H_{j+1} k_j)^T q_i).  The empty product (j = i) is the identity.
+ *
+ * PaTH-FoX (same page, section 2 "PaTH-FoX"): the additive forget bias
+ * sum_{s=j+1..i} f_s is added to the scaled logit before the softmax.
+ *
+ * The logits of one query row are produced by a downward scan: a running
+ * vector r starts at q_i; key j is scored against r, and only then is H_j
+ * applied to r.  No d x d matrix and no L x L matrix is ever formed (the
+ * lecture notes on PaTH, "idea" block, warn that the naive form needs one d x d
+ * product chain per score pair).  The softmax is the plain two-pass one:
+ * max, then sum of exponentials, then the weighted sum of values.
+ *
+ * Pins that tie this file to the pages and to mathematics (not to itself) live
+ * in tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+/* ------------------------------------------------------------------ basics */
+
+static double dot(const double* a, const double* b, int64_t n) {
+  double s = 0.0;
+  for (int64_t t = 0; t < n; ++t) s += a[t] * b[t];
+  return s;
+}
+
+/* r <- (I - beta w w^T) r : one Householder-like transition (summary, section 2). */
+static void apply_h(double* r, const double* w, double beta, int64_t d) {
+  double c = beta * dot(w, r, d);
+  for (int64_t t = 0; t < d; ++t) r[t] -= c * w[t];
+}
+
+/*
+ * Logits of query row i of one (batch, head): z[j] for j = 0..i.
+ * K, W are [L, d]; beta, logf are [L]; logf may be NULL (plain PaTH).
+ * r is caller scratch of length d.
+ */
+static void row_logits(const double* q_i, const double* K, const double* W, const double* beta,
+                       const double* logf, int64_t i, int64_t d, double scale, double* r, double* z) {
+  memcpy(r, q_i, (size_t)d * sizeof(double));
+  double bias = 0.0; /* sum_{s=j+1..i} f_s */
+  for (int64_t j = i; j >= 0; --j) {
+    z[j] = scale * dot(K + j * d, r, d) + bias;
+    apply_h(r, W + j * d, beta[j], d);
+    if (logf) bias += logf[j];
+  }
+}
+
+/* Exact two-pass softmax of z[0..n-1] applied to V [n, d]; lse = m + ln(sum exp(z - m)). */
+static void softmax_rows(const double* z, int64_t n, const double* V, int64_t d, double* o, double* lse) {
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n; ++j)
+    if (z[j] > m) m = z[j];
+  double l = 0.0;
+  for (int64_t j = 0; j < n; ++j) l += exp(z[j] - m);
+  for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    double p = exp(z[j] - m) / l;
+    const double* vj = V + j * d;
+    for (int64_t t = 0; t < d; ++t) o[t] += p * vj[t];
+  }
+  *lse = m + log(l);
+}
+
+static int resolve_threads(int nthreads) {
+  if (nthreads > 0) return nthreads;
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+/* ------------------------------------------------------------------ prefill */
+
+typedef struct {
+  const double *q, *k, *v, *w, *beta, *logf;
+  int64_t BH, L, d, nrows;
+  const int64_t* rows;
+  double scale;
+  double *out, *lse;
+  int64_t next; /* shared work counter, one item = (bh, row) */
+} fwd_job;
+
+static void* fwd_worker(void* arg) {
+  fwd_job* J = (fwd_job*)arg;
+  double* r = (double*)malloc((size_t)J->d * sizeof(double));
+  double* z = (double*)malloc((size_t)(J->L > 0 ? J->L : 1) * sizeof(double));
+  if (!r || !z) {
+    free(r);
+    free(z);
+    return (void*)1;
+  }
+  const int64_t total = J->BH * J->nrows;
+  for (;;) {
+    int64_t item = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+    if (item >= total) break;
+    int64_t bh = item / J->nrows, ri = item % J->nrows;
+    int64_t i = J->rows ? J->rows[ri] : ri;
+    const int64_t base = bh * J->L;
+    row_logits(J->q + (base + i) * J->d, J->k + base * J->d, J->w + base * J->d, J->beta + base,
+               J->logf ? J->logf + base : NULL, i, J->d, J->scale, r, z);
+    softmax_rows(z, i + 1, J->v + base * J->d, J->d, J->out + (bh * J->nrows + ri) * J->d,
+                 J->lse + bh * J->nrows + ri);
+  }
+  free(r);
+  free(z);
+  return NULL;
+}
+
+/*
+ * PaTH (or PaTH-FoX when logf != NULL) forward for BH independent (batch, head)
+ * slices.  q,k,v,w: [BH, L, d]; beta, logf: [BH, L].
+ * rows == NULL: every row 0..L-1 (nrows must equal L); otherwise only the listed
+ * rows, each in [0, L).  out: [BH, nrows, d]; lse: [BH, nrows].
+ */
+int path_oracle_fwd(const double* q, const double* k, const double* v, const double* w,
+                    const double* beta, const double* logf, int64_t BH, int64_t L, int64_t d,
+                    double scale, const int64_t* rows, int64_t nrows, double* out, double* lse,
+                    int nthreads) {
+  if (BH < 0 || L < 0 || d <= 0 || nrows < 0) return ORACLE_EINVAL;
+  if (!rows && nrows != L) return ORACLE_EINVAL;
+  if (rows)
+    for (int64_t r = 0; r < nrows; ++r)
+      if (rows[r] < 0 || rows[r] >= L) return ORACLE_EINVAL;
+  if (BH == 0 || nrows == 0) return ORACLE_OK;
+  fwd_job J = {q, k, v, w, beta, logf, BH, L, d, nrows, rows, scale, out, lse, 0};
+  int nt = resolve_threads(nthreads);
+  if ((int64_t)nt > BH * nrows) nt = (int)(BH * nrows);
+  pthread_t* th = (pthread_t*)malloc((size_t)nt * sizeof(pthread_t));
+  if (!th) return ORACLE_ENOMEM;
+  int rc = ORACLE_OK;
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, fwd_worker, &J);
+  for (int t = 0; t < nt; ++t) {
+    void* ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret) rc = ORACLE_ENOMEM;
+  }
+  free(th);
+  return rc;
+}
+
+/* Logits z[0..i] of one row of one (batch, head) slice; K, W: [L, d], beta, logf: [L]. */
+int path_oracle_row_logits(const double* q_i, const double* K, const double* W, const double* beta,
+                           const double* logf, int64_t i, int64_t d, double scale, double* z) {
+  if (i < 0 || d <= 0) return ORACLE_EINVAL;
+  double* r = (double*)malloc((size_t)d * sizeof(double));
+  if (!r) return ORACLE_ENOMEM;
+  row_logits(q_i, K, W, beta, logf, i, d, scale, r, z);
+  free(r);
+  return ORACLE_OK;
+}
+
+/* out = H_lo H_{lo+1} ... H_hi x   (H_hi is applied first; empty product when hi < lo). */
+int path_oracle_transport(const double* x, const double* W, const double* beta, int64_t lo, int64_t hi,
+                          int64_t d, double* out) {
+  if (d <= 0) return ORACLE_EINVAL;
+  memcpy(out, x, (size_t)d * sizeof(double));
+  for (int64_t s = hi; s >= lo; --s) apply_h(out, W + s * d, beta[s], d);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ decode */
+
+typedef struct {
+  double *kc, *vc;
+  int64_t BH, cap, t0, nsteps, d;
+  const double *qs, *ks, *vs, *ws, *betas;
+  double scale;
+  double *out, *lse;
+  int64_t next;
+} dec_job;
+
+static void* dec_worker(void* arg) {
+  dec_job* J = (dec_job*)arg;
+  const int64_t d = J->d;
+  double* z = (double*)malloc((size_t)(J->t0 + J->nsteps) * sizeof(double));
+  if (!z) return (void*)1;
+  for (;;) {
+    int64_t bh = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+    if (bh >= J->BH) break;
+    double* Kc = J->kc + bh * J->cap * d;
+    double* Vc = J->vc + bh * J->cap * d;
+    for (int64_t s = 0; s < J->nsteps; ++s) {
+      const int64_t t = J->t0 + s;
+      const int64_t tok = s * J->BH + bh;
+      const double* w = J->ws + tok * d;
+      const double beta = J->betas[tok];
+      /* Inference rule (summary, section 3): every cached key j < t takes the
+         newest transition in place; the new key enters untransformed. */
+      for (int64_t j = 0; j < t; ++j) apply_h(Kc + j * d, w, beta, d);
+      memcpy(Kc + t * d, J->ks + tok * d, (size_t)d * sizeof(double));
+      memcpy(Vc + t * d, J->vs + tok * d, (size_t)d * sizeof(double));
+      const double* qt = J->qs + tok * d;
+      for (int64_t j = 0; j <= t; ++j) z[j] = J->scale * dot(Kc + j * d, qt, d);
+      softmax_rows(z, t + 1, Vc, d, J->out + tok * d, J->lse + tok);
+    }
+  }
+  free(z);
+  return NULL;
+}
+
+/*
+ * nsteps decode steps for BH independent slices.  kc, vc: [BH, cap, d], the first
+ * t0 slots hold the current cache; they are updated in place and slots
+ * t0..t0+nsteps-1 are appended.  qs,ks,vs,ws: [nsteps, BH, d]; betas: [nsteps, BH].
+ * out: [nsteps, BH, d]; lse: [nsteps, BH].
+ */
+int path_oracle_decode(double* kc, double* vc, int64_t BH, int64_t cap, int64_t t0, int64_t nsteps,
+                       const double* qs, const double* ks, const double* vs, const double* ws,
+                       const double* betas, int64_t d, double scale, double* out, double* lse,
+                       int nthreads) {
+  if (BH < 0 || cap < 0 || t0 < 0 || nsteps < 0 || d <= 0 || t0 + nsteps > cap) return ORACLE_EINVAL;
+  if (BH == 0 || nsteps == 0) return ORACLE_OK;
+  dec_job J = {kc, vc, BH, cap, t0, nsteps, d, qs, ks, vs, ws, betas, scale, out, lse, 0};
+  int nt = resolve_threads(nthreads);
+  if ((int64_t)nt > BH) nt = (int)BH;
+  pthread_t* th = (pthread_t*)malloc((size_t)nt * sizeof(pthread_t));
+  if (!th) return ORACLE_ENOMEM;
+  int rc = ORACLE_OK;
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, dec_worker, &J);
+  for (int t = 0; t < nt; ++t) {
+    void* ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret) rc = ORACLE_ENOMEM;
+  }
+  free(th);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ chunk quantities */
+
+/*
+ * Compact (UT) form of a run of transitions (summary, section 3 "UT transform"):
+ * H_0 H_1 ... H_{n-1} = I - W^T T^{-1} W with W = [w_0; ...; w_{n-1}] (n x d) and T
+ * the upper-triangular matrix with diagonal 1/beta_s and strict upper part
+ * (W W^T)_{st}.  We never form 1/beta: T^{-1} = A^{-1} diag(beta) with
+ * A = I + diag(beta) * strict_upper(W W^T), a unit upper-triangular matrix solved
+ * here by plain back substitution, column by column.  tinv: n x n, row-major.
+ */
+int path_oracle_ut_tinv(const double* W, const double* beta, int64_t n, int64_t d, double* tinv) {
+  if (n < 0 || d <= 0) return ORACLE_EINVAL;
+  double* A = (double*)calloc((size_t)(n * n > 0 ? n * n : 1), sizeof(double));
+  if (!A) return ORACLE_ENOMEM;
+  for (int64_t s = 0; s < n; ++s)
+    for (int64_t t = s + 1; t < n; ++t) A[s * n + t] = beta[s] * dot(W + s * d, W + t * d, d);
+  /* Z = A^{-1}: Z[j][j] = 1, Z[i][j] = -sum_{k=i+1..j} A[i][k] Z[k][j] for i < j. */
+  for (int64_t j = 0; j < n; ++j) {
+    for (int64_t i = n - 1; i > j; --i) tinv[i * n + j] = 0.0;
+    tinv[j * n + j] = 1.0;
+    for (int64_t i = j - 1; i >= 0; --i) {
+      double s = 0.0;
+      for (int64_t k = i + 1; k <= j; ++k) s += A[i * n + k] * tinv[k * n + j];
+      tinv[i * n + j] = -s;
+    }
+  }
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < n; ++j) tinv[i * n + j] *= beta[j];
+  free(A);
+  return ORACLE_OK;
+}
+
+/* Explicit d x d product P = H_0 H_1 ... H_{n-1} (row-major), built as P <- P H_s. */
+int path_oracle_householder_product(const double* W, const double* beta, int64_t n, int64_t d,
+                                    double* P) {
+  if (n < 0 || d <= 0) return ORACLE_EINVAL;
+  double* pw = (double*)malloc((size_t)d * sizeof(double));
+  if (!pw) return ORACLE_ENOMEM;
+  for (int64_t a = 0; a < d; ++a)
+    for (int64_t b = 0; b < d; ++b) P[a * d + b] = (a == b) ? 1.0 : 0.0;
+  for (int64_t s = 0; s < n; ++s) {
+    const double* w = W + s * d;
+    for (int64_t a = 0; a < d; ++a) pw[a] = dot(P + a * d, w, d);
+    for (int64_t a = 0; a < d; ++a)
+      for (int64_t b = 0; b < d; ++b) P[a * d + b] -= beta[s] * pw[a] * w[b];
+  }
+  free(pw);
+  return ORACLE_OK;
+}
+
+/*
+ * Boundary-adjusted rows of one chunk of n tokens (summary, section 3,
+ * "FlashAttention-style algorithm": precomputed boundary-adjusted query and key
+ * rows), by their definitions:
+ *   qtilde_a = H_0 H_1 ... H_a q_a            (chunk prefix, token a included)
+ *   ktilde_b = H_{n-1} ... H_{b+1} k_b        (chunk suffix strictly after b)
+ *   sintra[a][b] = k_b^T H_{b+1} ... H_a q_a  for b <= a (unscaled), 0 above the diagonal.
+ * q, k, W: [n, d]; outputs qtilde, ktilde [n, d], sintra [n, n].
+ */
+int path_oracle_chunk_terms(const double* q, const double* k, const double* W, const double* beta,
+                            int64_t n, int64_t d, double* qtilde, double* ktilde, double* sintra) {
+  if (n < 0 || d <= 0) return ORACLE_EINVAL;
+  double* r = (double*)malloc((size_t)d * sizeof(double));
+  if (!r) return ORACLE_ENOMEM;
+  for (int64_t a = 0; a < n; ++a) {
+    /* The row scan gives sintra[a][*] and, after H_0, the prefix-adjusted query. */
+    memcpy(r, q + a * d, (size_t)d * sizeof(double));
+    for (int64_t b = a; b >= 0; --b) {
+      sintra[a * n + b] = dot(k + b * d, r, d);
+      apply_h(r, W + b * d, beta[b], d);
+    }
+    for (int64_t b = a + 1; b < n; ++b) sintra[a * n + b] = 0.0;
+    memcpy(qtilde + a * d, r, (size_t)d * sizeof(double));
+    /* ktilde_b = H_{n-1} ... H_{b+1} k_b : apply H_{b+1} first. */
+    memcpy(ktilde + a * d, k + a * d, (size_t)d * sizeof(double));
+    for (int64_t s = a + 1; s < n; ++s) apply_h(ktilde + a * d, W + s * d, beta[s], d);
+  }
+  free(r);
+  return ORACLE_OK;
+}
+
+int path_oracle_abi_version(void) { return 1; }
