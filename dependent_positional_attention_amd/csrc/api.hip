@@ -1,0 +1,182 @@
+// C ABI of libpathattn: argument validation, workspace planning and launches.
+// Every check runs on the host before anything is enqueued (see path_attn.h).
+#include "path_attn.h"
+
+#include "common.h"
+
+namespace pathattn {
+// vector_path.hip
+bool vec_supported(int d, int chunk);
+hipError_t vec_fwd(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
+                   const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L, float scale,
+                   float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st);
+// mfma_path.hip
+bool mfma_supported(int d, int chunk);
+hipError_t mfma_fwd(int chunk, int transport, const void* q, const void* k, const void* v, const void* w,
+                    const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
+                    float scale, void* qt, void* kt, void* vt, void* p_hi, void* p_lo, float* Sm, float* fl,
+                    float* ftot, hipStream_t st);
+// decode.hip
+bool decode_supported(int d);
+int64_t decode_auto_splits(int64_t keys);
+hipError_t decode_step(bool bf16, int d, void* kc, void* vc, int64_t cap, int64_t t, const void* q_t,
+                       const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out, float* lse,
+                       int64_t BH, float scale, int splits, float* part, hipStream_t st);
+}  // namespace pathattn
+
+using namespace pathattn;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxGridY = 65535;
+
+bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool valid_dtype(int dt) { return dt == PATH_DTYPE_F32 || dt == PATH_DTYPE_BF16; }
+
+// Which kernels serve (d, chunk, dtype): the matrix-core path for bf16 when built
+// for the shape, the vector path otherwise.
+path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype, int transport,
+                     path_ws_layout* lay) {
+  if (B < 0 || H < 0 || L < 0 || d <= 0 || chunk <= 0) return PATH_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return PATH_ERR_UNSUPPORTED;
+  if (transport != PATH_TRANSPORT_BF16 && transport != PATH_TRANSPORT_BF16X3) return PATH_ERR_INVALID_ARG;
+  const bool bf16 = dtype == PATH_DTYPE_BF16;
+  const bool mfma = bf16 && mfma_supported(d, chunk);
+  if (!mfma && !vec_supported(d, chunk)) return PATH_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  const int64_t M = (L + chunk - 1) / chunk;
+  const int64_t Lp = M * chunk;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = round_up(off + bytes, kAlign);
+    return o;
+  };
+  *lay = path_ws_layout{};
+  lay->num_chunks = M;
+  lay->off_vt = -1;
+  lay->off_p_lo = -1;
+  if (!mfma) {
+    lay->layout_id = 0;
+    lay->off_qtilde = take(BH * Lp * d * 4);
+    lay->off_ktilde = take(BH * Lp * d * 4);
+    lay->off_p = take(BH * M * d * d * 4);
+  } else {
+    lay->layout_id = 1;
+    lay->off_qtilde = take(BH * Lp * d * 2);
+    lay->off_ktilde = take(BH * Lp * d * 2);
+    lay->off_vt = take(BH * M * d * chunk * 2);
+    lay->off_p = take(BH * M * d * d * 2);
+    if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_lo = take(BH * M * d * d * 2);
+  }
+  lay->off_s = take(BH * M * (int64_t)chunk * chunk * 4);
+  lay->off_fox_local = take(BH * Lp * 4);
+  lay->off_fox_total = take(BH * M * 4);
+  lay->total_bytes = off;
+  return PATH_OK;
+}
+
+path_status from_hip(hipError_t e) { return e == hipSuccess ? PATH_OK : PATH_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int path_abi_version(void) { return PATH_ABI_VERSION; }
+
+const char* path_status_string(int status) {
+  switch (status) {
+    case PATH_OK:
+      return "ok";
+    case PATH_ERR_INVALID_ARG:
+      return "invalid argument";
+    case PATH_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case PATH_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+path_status path_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                                          int transport, size_t* bytes) {
+  if (bytes == nullptr) return PATH_ERR_INVALID_ARG;
+  path_ws_layout lay;
+  const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
+  if (s != PATH_OK) return s;
+  *bytes = (size_t)lay.total_bytes;
+  return PATH_OK;
+}
+
+path_status path_attn_workspace_layout(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                                       int transport, path_ws_layout* layout) {
+  if (layout == nullptr) return PATH_ERR_INVALID_ARG;
+  return plan_fwd(B, H, L, d, chunk, dtype, transport, layout);
+}
+
+path_status path_attn_fwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                          const float* log_forget, void* out, float* lse, int64_t B, int64_t H, int64_t L,
+                          int d, int chunk, float scale, int dtype, int transport, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  path_ws_layout lay;
+  const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
+  if (s != PATH_OK) return s;
+  const int64_t BH = B * H;
+  if (BH == 0 || L == 0) return PATH_OK;
+  if (!q || !k || !v || !w || !beta || !out || !workspace) return PATH_ERR_INVALID_ARG;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(w) || misaligned(beta) ||
+      misaligned(log_forget) || misaligned(out) || misaligned(lse) || misaligned(workspace))
+    return PATH_ERR_UNSUPPORTED;
+  if (workspace_bytes < (size_t)lay.total_bytes) return PATH_ERR_INVALID_ARG;
+  if (BH > kMaxGridY || lay.num_chunks > kMaxGridY) return PATH_ERR_UNSUPPORTED;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* fl = reinterpret_cast<float*>(ws + lay.off_fox_local);
+  float* ftot = reinterpret_cast<float*>(ws + lay.off_fox_total);
+  float* Sm = reinterpret_cast<float*>(ws + lay.off_s);
+  if (lay.layout_id == 1) {
+    return from_hip(mfma_fwd(chunk, transport, q, k, v, w, beta, log_forget, out, lse, BH, L, scale,
+                             ws + lay.off_qtilde, ws + lay.off_ktilde, ws + lay.off_vt, ws + lay.off_p,
+                             lay.off_p_lo >= 0 ? ws + lay.off_p_lo : nullptr, Sm, fl, ftot, st));
+  }
+  return from_hip(vec_fwd(dtype == PATH_DTYPE_BF16, d, chunk, q, k, v, w, beta, log_forget, out, lse, BH, L, scale,
+                          reinterpret_cast<float*>(ws + lay.off_qtilde), reinterpret_cast<float*>(ws + lay.off_ktilde),
+                          reinterpret_cast<float*>(ws + lay.off_p), Sm, fl, ftot, st));
+}
+
+path_status path_decode_workspace_bytes(int64_t B, int64_t H, int d, int64_t capacity, int splits,
+                                        size_t* bytes) {
+  if (bytes == nullptr || B < 0 || H < 0 || capacity < 0 || splits < 0) return PATH_ERR_INVALID_ARG;
+  if (!decode_supported(d)) return PATH_ERR_UNSUPPORTED;
+  const int64_t S = splits > 0 ? splits : decode_auto_splits(capacity);
+  *bytes = (size_t)(B * H * S * (int64_t)(d + 2) * 4);
+  return PATH_OK;
+}
+
+path_status path_decode_step(void* kcache, void* vcache, int64_t capacity, int64_t t, const void* q_t,
+                             const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out,
+                             float* lse, int64_t B, int64_t H, int d, float scale, int dtype, int splits,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || capacity < 0 || splits < 0) return PATH_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype) || !decode_supported(d)) return PATH_ERR_UNSUPPORTED;
+  if (t < 0 || t >= capacity) return PATH_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  if (BH == 0) return PATH_OK;
+  if (!kcache || !vcache || !q_t || !k_t || !v_t || !w_t || !beta_t || !out || !workspace)
+    return PATH_ERR_INVALID_ARG;
+  if (misaligned(kcache) || misaligned(vcache) || misaligned(q_t) || misaligned(k_t) || misaligned(v_t) ||
+      misaligned(w_t) || misaligned(beta_t) || misaligned(out) || misaligned(lse) || misaligned(workspace))
+    return PATH_ERR_UNSUPPORTED;
+  const int64_t S = splits > 0 ? splits : decode_auto_splits(t + 1);
+  if (S > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
+  if (workspace_bytes < (size_t)(BH * S * (int64_t)(d + 2) * 4)) return PATH_ERR_INVALID_ARG;
+  if (BH > kMaxGridY) return PATH_ERR_UNSUPPORTED;
+  return from_hip(decode_step(dtype == PATH_DTYPE_BF16, d, kcache, vcache, capacity, t, q_t, k_t, v_t, w_t, beta_t,
+                              out, lse, BH, scale, (int)S, static_cast<float*>(workspace),
+                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

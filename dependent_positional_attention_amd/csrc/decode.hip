@@ -1,0 +1,273 @@
+// PaTH decode step (PaTH summary, gist.science/ko/paper/2505.16381, section 3
+// "inference"): the cached keys absorb the newest transition in place,
+// k_j <- (I - beta_t w_t w_t^T) k_j for every cached j < t, so no transition
+// vectors are kept; the new token's key enters untransformed; the query then
+// attends over the updated cache with a FlashDecoding-style split over keys.
+//
+// Kernel 1 (update_attend): grid (splits, B*H).  A workgroup owns the key range
+// [j0, j1) of one (b, h) -- ranges are disjoint, so the in-place writes never
+// race.  Each key row is read with 16-byte loads by a group of LPK lanes
+// (LPK = d / elements-per-16-bytes); the group reduces w.k and q.k with lane
+// shuffles, writes the updated key back, and keeps an online-softmax state
+// (running max, sum, partial output slice).  Groups are merged through LDS and
+// the split's (m, l, o[d]) partial goes to the workspace.
+// Kernel 2 (combine): one workgroup per (b, h) merges the splits.
+#include "common.h"
+
+namespace pathattn {
+
+template <typename T>
+struct Vec16;  // 16 bytes of T
+template <>
+struct Vec16<__bf16> {
+  static constexpr int N = 8;
+  typedef uint4 raw;
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  typedef uint4 raw;
+};
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& r, float* f);
+template <>
+__device__ __forceinline__ void unpack16<__bf16>(const uint4& r, float* f) {
+  const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& r, float* f) {
+  f[0] = __uint_as_float(r.x);
+  f[1] = __uint_as_float(r.y);
+  f[2] = __uint_as_float(r.z);
+  f[3] = __uint_as_float(r.w);
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float* f);
+template <>
+__device__ __forceinline__ uint4 pack16<__bf16>(const float* f) {
+  uint32_t u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 lo = (__bf16)f[2 * i], hi = (__bf16)f[2 * i + 1];
+    u[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return make_uint4(u[0], u[1], u[2], u[3]);
+}
+template <>
+__device__ __forceinline__ uint4 pack16<float>(const float* f) {
+  return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+
+// Sum over the LPK lanes of a key group (groups are aligned runs of LPK lanes).
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < LPK; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+constexpr int kDecThreads = 256;
+constexpr int kDecUnroll = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
+    T* __restrict__ kc, T* __restrict__ vc, int64_t cap, int64_t t, const T* __restrict__ q_t,
+    const T* __restrict__ k_t, const T* __restrict__ v_t, const T* __restrict__ w_t, const float* __restrict__ beta_t,
+    float scale_log2, int splits, int64_t keys_per_split, float* __restrict__ part) {
+  constexpr int VN = Vec16<T>::N;  // elements per 16-byte vector
+  constexpr int LPK = D / VN;      // lanes per key
+  constexpr int GPB = kDecThreads / LPK;  // key groups per block
+  static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "bad lanes per key");
+
+  const int split = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int grp = tid / LPK, sub = tid % LPK;
+
+  const int64_t j0 = (int64_t)split * keys_per_split;
+  int64_t j1 = j0 + keys_per_split;
+  if (j1 > t + 1) j1 = t + 1;
+
+  float wv[VN], qv[VN];
+  {
+    const uint4* wp = (const uint4*)(w_t + bh * D) + sub;
+    const uint4* qp = (const uint4*)(q_t + bh * D) + sub;
+    unpack16<T>(*wp, wv);
+    unpack16<T>(*qp, qv);
+  }
+  const float beta = beta_t[bh];
+  T* kb = kc + (size_t)bh * cap * D;
+  T* vb = vc + (size_t)bh * cap * D;
+
+  float mrun = -INFINITY, lrun = 0.f, o[VN];
+#pragma unroll
+  for (int x = 0; x < VN; ++x) o[x] = 0.f;
+
+  for (int64_t base = j0 + grp; base < j1; base += (int64_t)GPB * kDecUnroll) {
+    uint4 kr[kDecUnroll], vr[kDecUnroll];
+    int64_t jj[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      jj[u] = base + (int64_t)u * GPB;
+      kr[u] = make_uint4(0u, 0u, 0u, 0u);  // keys past the range contribute exp2(-inf) * 0
+      vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (jj[u] < j1) {
+        if (jj[u] < t) {
+          kr[u] = *((const uint4*)(kb + jj[u] * D) + sub);
+        } else {  // jj == t: the new token
+          kr[u] = *((const uint4*)(k_t + bh * D) + sub);
+        }
+        vr[u] = (jj[u] < t) ? *((const uint4*)(vb + jj[u] * D) + sub) : *((const uint4*)(v_t + bh * D) + sub);
+      }
+    }
+    float z[kDecUnroll];
+    float vf[kDecUnroll][VN];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      float kf[VN];
+      unpack16<T>(kr[u], kf);
+      unpack16<T>(vr[u], vf[u]);
+      const bool live = jj[u] < j1;
+      if (live && jj[u] < t) {
+        float pd = 0.f;
+#pragma unroll
+        for (int x = 0; x < VN; ++x) pd += wv[x] * kf[x];
+        const float coef = beta * group_sum<LPK>(pd);
+#pragma unroll
+        for (int x = 0; x < VN; ++x) kf[x] -= coef * wv[x];
+        const uint4 nk = pack16<T>(kf);
+        *((uint4*)(kb + jj[u] * D) + sub) = nk;
+        unpack16<T>(nk, kf);  // attend with exactly the stored key
+      } else if (live) {  // slot t: the new token, stored untransformed
+        *((uint4*)(kb + jj[u] * D) + sub) = kr[u];
+        *((uint4*)(vb + jj[u] * D) + sub) = vr[u];
+      }
+      float sd = 0.f;
+#pragma unroll
+      for (int x = 0; x < VN; ++x) sd += qv[x] * kf[x];
+      sd = group_sum<LPK>(sd);
+      z[u] = live ? sd * scale_log2 : -INFINITY;
+    }
+    float bm = z[0];
+#pragma unroll
+    for (int u = 1; u < kDecUnroll; ++u) bm = fmaxf(bm, z[u]);
+    const float mnew = fmaxf(mrun, bm);
+    if (mnew != -INFINITY) {
+      const float alpha = fast_exp2(mrun - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int x = 0; x < VN; ++x) o[x] *= alpha;
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) {
+        const float p = fast_exp2(z[u] - mnew);
+        lrun += p;
+#pragma unroll
+        for (int x = 0; x < VN; ++x) o[x] += p * vf[u][x];
+      }
+      mrun = mnew;
+    }
+  }
+
+  // merge the GPB group states of this block through LDS
+  __shared__ float sm[GPB], sl[GPB];
+  __shared__ float so[GPB * D];
+  if (sub == 0) {
+    sm[grp] = mrun;
+    sl[grp] = lrun;
+  }
+#pragma unroll
+  for (int x = 0; x < VN; ++x) so[grp * D + sub * VN + x] = o[x];
+  __syncthreads();
+  if (tid < D) {
+    float M = -INFINITY;
+    for (int g = 0; g < GPB; ++g) M = fmaxf(M, sm[g]);
+    float Lsum = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+      for (int g = 0; g < GPB; ++g) {
+        const float f = fast_exp2(sm[g] - M);
+        Lsum += sl[g] * f;
+        acc += so[g * D + tid] * f;
+      }
+    }
+    float* pp = part + ((size_t)bh * splits + split) * (D + 2);
+    pp[2 + tid] = acc;
+    if (tid == 0) {
+      pp[0] = M;
+      pp[1] = Lsum;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part, int splits,
+                                                            T* __restrict__ out, float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;
+  const float* pp = part + (size_t)bh * splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
+  float Lsum = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float m = pp[(size_t)s * (D + 2)];
+    if (m != -INFINITY) Lsum += pp[(size_t)s * (D + 2) + 1] * fast_exp2(m - M);
+  }
+  const float inv = 1.f / Lsum;
+  for (int x = threadIdx.x; x < D; x += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float m = pp[(size_t)s * (D + 2)];
+      if (m != -INFINITY) acc += pp[(size_t)s * (D + 2) + 2 + x] * fast_exp2(m - M);
+    }
+    out[bh * D + x] = from_f32<T>(acc * inv);
+  }
+  if (lse != nullptr && threadIdx.x == 0) lse[bh] = (M + fast_log2(Lsum)) * kLn2;
+}
+
+template <typename T, int D>
+static hipError_t launch_decode(void* kc, void* vc, int64_t cap, int64_t t, const void* q_t, const void* k_t,
+                                const void* v_t, const void* w_t, const float* beta_t, void* out, float* lse,
+                                int64_t BH, float scale, int splits, float* part, hipStream_t st) {
+  const int64_t keys = t + 1;
+  const int64_t kps = (keys + splits - 1) / splits;
+  dim3 grid((unsigned)splits, (unsigned)BH);
+  decode_update_attend_kernel<T, D><<<grid, kDecThreads, 0, st>>>(
+      (T*)kc, (T*)vc, cap, t, (const T*)q_t, (const T*)k_t, (const T*)v_t, (const T*)w_t, beta_t, scale * kLog2e,
+      splits, kps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<T, D><<<(unsigned)BH, 64, 0, st>>>(part, splits, (T*)out, lse);
+  return hipGetLastError();
+}
+
+bool decode_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Keys per split chosen automatically: about 1024, so a 64K cache uses 64 splits per (b, h).
+int64_t decode_auto_splits(int64_t keys) {
+  int64_t s = (keys + 1023) / 1024;
+  return s < 1 ? 1 : s;
+}
+
+hipError_t decode_step(bool bf16, int d, void* kc, void* vc, int64_t cap, int64_t t, const void* q_t,
+                       const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out, float* lse,
+                       int64_t BH, float scale, int splits, float* part, hipStream_t st) {
+#define PATHATTN_DEC_CASE(DD)                                                                                     \
+  if (d == DD)                                                                                                    \
+    return bf16 ? launch_decode<__bf16, DD>(kc, vc, cap, t, q_t, k_t, v_t, w_t, beta_t, out, lse, BH, scale,     \
+                                            splits, part, st)                                                    \
+                : launch_decode<float, DD>(kc, vc, cap, t, q_t, k_t, v_t, w_t, beta_t, out, lse, BH, scale, splits, \
+                                           part, st);
+  PATHATTN_DEC_CASE(16)
+  PATHATTN_DEC_CASE(32)
+  PATHATTN_DEC_CASE(64)
+  PATHATTN_DEC_CASE(128)
+#undef PATHATTN_DEC_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pathattn

@@ -1,0 +1,179 @@
+"""ctypes binding of libpathattn.so -- argument marshalling only.
+
+Every step of PaTH attention runs in the HIP kernels behind the C ABI
+(include/path_attn.h); this module passes torch tensors' device pointers and
+the current HIP stream through, allocating outputs and workspace with torch
+when the caller does not pass them.  There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch  # imported first so the HIP runtime torch ships is the one in the process
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpathattn.so")
+
+PATH_OK, PATH_ERR_INVALID_ARG, PATH_ERR_UNSUPPORTED, PATH_ERR_HIP = 0, 1, 2, 3
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+TRANSPORT = {"bf16": 0, "bf16x3": 1}
+
+_lib = None
+
+
+class PathAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().path_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [("layout_id", ctypes.c_int), ("num_chunks", ctypes.c_int64), ("off_qtilde", ctypes.c_int64),
+                ("off_ktilde", ctypes.c_int64), ("off_vt", ctypes.c_int64), ("off_p", ctypes.c_int64),
+                ("off_p_lo", ctypes.c_int64), ("off_s", ctypes.c_int64), ("off_fox_local", ctypes.c_int64),
+                ("off_fox_total", ctypes.c_int64), ("total_bytes", ctypes.c_int64)]
+
+
+EXPORTS = ("path_abi_version", "path_status_string", "path_attn_fwd_workspace_bytes", "path_attn_fwd",
+           "path_attn_workspace_layout", "path_decode_workspace_bytes", "path_decode_step")
+
+
+def lib():
+    """Load libpathattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "or python -m dependent_positional_attention_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.path_abi_version.argtypes, L.path_abi_version.restype = [], i32
+        L.path_status_string.argtypes, L.path_status_string.restype = [i32], ctypes.c_char_p
+        L.path_attn_fwd_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.path_attn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(WsLayout)]
+        L.path_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32, vp, sz,
+                                    vp]
+        L.path_decode_workspace_bytes.argtypes = [i64, i64, i32, i64, i32, ctypes.POINTER(sz)]
+        L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, f32, i32, i32,
+                                       vp, sz, vp]
+        for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd",
+                  "path_decode_workspace_bytes", "path_decode_step"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != PATH_OK:
+        raise PathAttnError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def path_attn_fwd_workspace_bytes(B, H, L, d, chunk, dtype: torch.dtype, transport: str = "bf16") -> int:
+    n = ctypes.c_size_t(0)
+    _check("path_attn_fwd_workspace_bytes",
+           lib().path_attn_fwd_workspace_bytes(B, H, L, d, chunk, DTYPE[dtype], TRANSPORT[transport],
+                                               ctypes.byref(n)))
+    return n.value
+
+
+def path_attn_workspace_layout(B, H, L, d, chunk, dtype: torch.dtype, transport: str = "bf16") -> WsLayout:
+    lay = WsLayout()
+    _check("path_attn_workspace_layout",
+           lib().path_attn_workspace_layout(B, H, L, d, chunk, DTYPE[dtype], TRANSPORT[transport],
+                                            ctypes.byref(lay)))
+    return lay
+
+
+def path_attn_fwd(q, k, v, w, beta, log_forget=None, *, scale: Optional[float] = None, chunk: int = 64,
+                  transport: str = "bf16", out=None, lse=None, workspace=None, stream=None,
+                  want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """PaTH / PaTH-FoX prefill forward.  q,k,v,w: [B,H,L,d]; beta, log_forget: [B,H,L] fp32."""
+    _require(q, "q")
+    B, H, L, d = q.shape
+    for name, t in (("k", k), ("v", v), ("w", w)):
+        _require(t, name, q.dtype, q.shape)
+    _require(beta, "beta", torch.float32, (B, H, L))
+    if log_forget is not None:
+        _require(log_forget, "log_forget", torch.float32, (B, H, L))
+    if q.dtype not in DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", q.dtype, q.shape)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, (B, H, L))
+    nbytes = path_attn_fwd_workspace_bytes(B, H, L, d, chunk, q.dtype, transport)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), device=q.device, dtype=torch.uint8)
+    _require(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("path_attn_fwd", lib().path_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(out), _ptr(lse), B, H, L, d, chunk,
+        float(scale), DTYPE[q.dtype], TRANSPORT[transport], _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def path_decode_workspace_bytes(B, H, d, capacity, splits: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check("path_decode_workspace_bytes", lib().path_decode_workspace_bytes(B, H, d, capacity, splits,
+                                                                           ctypes.byref(n)))
+    return n.value
+
+
+def path_decode_step(kcache, vcache, t: int, q_t, k_t, v_t, w_t, beta_t, *, scale: Optional[float] = None,
+                     splits: int = 0, out=None, lse=None, workspace=None, stream=None,
+                     want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One decode step.  kcache, vcache: [B,H,capacity,d] (updated in place); q_t..w_t: [B,H,d]; beta_t: [B,H]."""
+    _require(kcache, "kcache")
+    B, H, cap, d = kcache.shape
+    _require(vcache, "vcache", kcache.dtype, kcache.shape)
+    for name, x in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _require(x, name, kcache.dtype, (B, H, d))
+    _require(beta_t, "beta_t", torch.float32, (B, H))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, d), device=kcache.device, dtype=kcache.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), device=kcache.device, dtype=torch.float32)
+    if workspace is None:
+        workspace = torch.empty(max(path_decode_workspace_bytes(B, H, d, cap, splits), 16), device=kcache.device,
+                                dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("path_decode_step", lib().path_decode_step(
+        _ptr(kcache), _ptr(vcache), cap, int(t), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t), _ptr(out),
+        _ptr(lse), B, H, d, float(scale), DTYPE[kcache.dtype], int(splits), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return out, lse

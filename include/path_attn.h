@@ -1,0 +1,161 @@
+/*
+ * path_attn.h -- C ABI of the PaTH attention library (libpathattn.so, gfx950).
+ *
+ * PaTH attention (PaTH summary, gist.science/ko/paper/2505.16381, section 2
+ * "core mechanism") is causal softmax attention whose logit for query i and
+ * key j <= i is
+ *
+ *     z_ij = scale * k_j^T (H_{j+1} H_{j+2} ... H_i) q_i + bias_ij,
+ *     H_s  = I - beta_s w_s w_s^T,
+ *
+ * with bias_ij = sum_{s=j+1..i} f_s for PaTH-FoX (same page, section 2
+ * "PaTH-FoX") and 0 otherwise.  out_i = sum_j softmax_j(z_ij) v_j and
+ * lse_i = ln sum_j exp(z_ij).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises, and keeps no global mutable
+ *     state.  All work is enqueued asynchronously on `stream` (a hipStream_t;
+ *     NULL is the null stream).
+ *   - Layouts are dense row-major: q, k, v, w, out are [B, H, L, d] with d
+ *     fastest; beta, log_forget, lse are [B, H, L].  Element type of q, k, v,
+ *     w and out is `dtype`; beta, log_forget and lse are always fp32.
+ *   - Every pointer must be 16-byte aligned.
+ *   - All validation happens on the host before any launch; a failed check
+ *     returns an error and enqueues nothing.  Launch failures return
+ *     PATH_ERR_HIP.  Device data is never inspected: NaN in gives NaN out,
+ *     and beta outside [0, 2] is accepted but its numerics are the caller's
+ *     concern.  w is used as given (no renormalisation).
+ *   - No call aborts or throws across the ABI.
+ */
+#ifndef PATH_ATTN_H
+#define PATH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PATH_ABI_VERSION 1
+
+typedef enum {
+  PATH_OK = 0,
+  PATH_ERR_INVALID_ARG = 1, /* null pointer, negative size, t >= capacity, workspace too small, ... */
+  PATH_ERR_UNSUPPORTED = 2, /* head dim / chunk / dtype combination not built, misaligned pointer */
+  PATH_ERR_HIP = 3          /* a HIP launch or runtime call failed */
+} path_status;
+
+typedef enum { PATH_DTYPE_F32 = 0, PATH_DTYPE_BF16 = 1 } path_dtype;
+
+/*
+ * Precision of the running-query transport between chunks (bf16 path only):
+ * PATH_TRANSPORT_BF16 rounds the running query and the chunk product to bf16
+ * for each matrix-core product; PATH_TRANSPORT_BF16X3 splits both into
+ * hi + lo bf16 parts and sums hi*hi + hi*lo + lo*hi, which keeps long scans
+ * (tens of thousands of tokens with beta near 2) within bf16-input tolerance.
+ * The fp32 path always transports in fp32.
+ */
+typedef enum { PATH_TRANSPORT_BF16 = 0, PATH_TRANSPORT_BF16X3 = 1 } path_transport;
+
+/* Library ABI version (PATH_ABI_VERSION of the build). */
+int path_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* path_status_string(int status);
+
+/*
+ * Bytes of device workspace path_attn_fwd needs for this problem (written to
+ * *bytes).  Pure host function.  Returns PATH_ERR_UNSUPPORTED for
+ * combinations the library does not build, PATH_ERR_INVALID_ARG for bad sizes.
+ */
+path_status path_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                                          int transport, size_t* bytes);
+
+/*
+ * PaTH / PaTH-FoX prefill forward (summary, section 3 "efficient training and
+ * inference": compact UT form of each chunk's transitions, boundary-adjusted
+ * query/key rows per chunk, right-to-left scan over key chunks that carries the
+ * transition product, FlashAttention-style online softmax).
+ *
+ *   q, k, v, w   [B,H,L,d] dtype        queries, keys, values, transition directions
+ *   beta         [B,H,L]   fp32         transition strengths (expected in [0, 2])
+ *   log_forget   [B,H,L]   fp32 or NULL PaTH-FoX per-token log forget gates f_s
+ *   out          [B,H,L,d] dtype        attention output (written)
+ *   lse          [B,H,L]   fp32 or NULL natural-log log-sum-exp of each row (written)
+ *   scale        multiplies k^T(...)q; the FoX bias is added after scaling
+ *   chunk        block length C of the scan; results do not depend on it beyond rounding
+ *   workspace    device buffer of at least path_attn_fwd_workspace_bytes bytes,
+ *                caller-owned; its contents on return hold the per-chunk terms
+ *                described by path_attn_workspace_layout
+ *
+ * Supported: dtype F32 with d in {16,32,64} and chunk in {16,32,64};
+ * dtype BF16 with the same set, plus d = 64 with chunk 64 on the matrix-core
+ * path.  Any L >= 0 (a ragged last chunk is padded internally with identity
+ * transitions); B, H, L may be 0 (nothing is enqueued).
+ */
+path_status path_attn_fwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                          const float* log_forget, void* out, float* lse, int64_t B, int64_t H, int64_t L,
+                          int d, int chunk, float scale, int dtype, int transport, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Where path_attn_fwd leaves its per-chunk terms inside the workspace (byte
+ * offsets, -1 when a term is not materialised by the selected kernels).  Used
+ * to inspect intermediate results; the layout of each term is stated in
+ * `layout_id`:
+ *   layout_id 0 (vector path): qtilde, ktilde [B*H, M*C, d] fp32; P [B*H, M, d, d] fp32
+ *     (row-major, P = H_first ... H_last of the chunk); S [B*H, M, C, C] fp32 ([query][key],
+ *     unscaled, lower triangle incl. diagonal).
+ *   layout_id 1 (matrix-core path): qtilde, ktilde [B*H, M*C, d] bf16 with columns permuted
+ *     within each 32-wide block (stored slot 8g+j holds column 16(j/4)+4g+(j%4));
+ *     vt [B*H, M, d, C] bf16 (value chunk transposed, key index permuted the same way);
+ *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S as layout 0.
+ * M = ceil(L / chunk).
+ */
+typedef struct {
+  int layout_id;
+  int64_t num_chunks;
+  int64_t off_qtilde, off_ktilde, off_vt, off_p, off_p_lo, off_s, off_fox_local, off_fox_total;
+  int64_t total_bytes;
+} path_ws_layout;
+
+path_status path_attn_workspace_layout(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                                       int transport, path_ws_layout* layout);
+
+/*
+ * Bytes of device workspace path_decode_step needs (written to *bytes) for
+ * `splits` key ranges per (batch, head); splits = 0 selects the automatic
+ * count for a cache of `capacity` slots.
+ */
+path_status path_decode_workspace_bytes(int64_t B, int64_t H, int d, int64_t capacity, int splits,
+                                        size_t* bytes);
+
+/*
+ * One PaTH decode step (summary, section 3 "inference": the cached keys are
+ * updated in place with the current transition, so no transition vectors are
+ * cached, and the attention itself is a FlashDecoding-style split-key pass).
+ *
+ *   kcache, vcache [B,H,capacity,d] dtype  slots 0..t-1 hold the current cache
+ *   t              tokens already cached (same for the whole batch), 0 <= t < capacity
+ *   q_t,k_t,v_t,w_t [B,H,d] dtype          the new token's query, key, value, direction
+ *   beta_t         [B,H] fp32              the new token's transition strength
+ *   out            [B,H,d] dtype           attention output of the new token (written)
+ *   lse            [B,H] fp32 or NULL      natural-log log-sum-exp (written)
+ *
+ * Effect, for every (b, h): k_j <- (I - beta_t w_t w_t^T) k_j for j < t, rounded
+ * to dtype and written back in place; slot t <- (k_t, v_t) untransformed; then
+ * out = softmax_j(scale * q_t . k_j) v_j over j = 0..t.  Slots beyond t are
+ * untouched.  Supported: d in {16,32,64,128}, dtype F32 or BF16.
+ */
+path_status path_decode_step(void* kcache, void* vcache, int64_t capacity, int64_t t, const void* q_t,
+                             const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out,
+                             float* lse, int64_t B, int64_t H, int d, float scale, int dtype, int splits,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATH_ATTN_H */

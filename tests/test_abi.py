@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): exports, workspace planning, validation codes.
+
+Every call here fails validation (or is a pure host query) before anything is enqueued, so it
+runs on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dependent_positional_attention_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "path_attn.h")
+
+OK, INVALID, UNSUPPORTED = native.PATH_OK, native.PATH_ERR_INVALID_ARG, native.PATH_ERR_UNSUPPORTED
+F32, BF16 = 0, 1
+FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:path_status|int|const char\*|size_t)\s+(path_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return native.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in path_attn.h but not exported"
+    assert set(names) == set(native.EXPORTS)
+
+
+def test_version_and_strings(L):
+    assert L.path_abi_version() == 1
+    for s in range(4):
+        assert L.path_status_string(s)
+    assert L.path_status_string(99) == b"unknown status"
+
+
+def ws_bytes(L, *args):
+    n = ctypes.c_size_t(0)
+    st = L.path_attn_fwd_workspace_bytes(*args, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_planning(L):
+    st, n = ws_bytes(L, 8, 24, 4096, 64, 64, BF16, 0)
+    assert st == OK and n > 8 * 24 * 4096 * 64 * 2 * 3
+    st, n0 = ws_bytes(L, 1, 1, 0, 16, 16, F32, 0)
+    assert st == OK
+    assert ws_bytes(L, 1, 1, 64, 48, 16, F32, 0)[0] == UNSUPPORTED  # head dim not built
+    assert ws_bytes(L, 1, 1, 64, 16, 24, F32, 0)[0] == UNSUPPORTED  # chunk not built
+    assert ws_bytes(L, 1, 1, 64, 16, 16, 7, 0)[0] == UNSUPPORTED  # dtype
+    assert ws_bytes(L, -1, 1, 64, 16, 16, F32, 0)[0] == INVALID
+    assert ws_bytes(L, 1, 1, 64, 16, 16, F32, 5)[0] == INVALID  # transport
+    lay = native.WsLayout()
+    assert L.path_attn_workspace_layout(2, 3, 100, 16, 16, F32, 0, ctypes.byref(lay)) == OK
+    assert lay.num_chunks == 7 and lay.layout_id == 0 and lay.off_vt == -1
+    offs = [lay.off_qtilde, lay.off_ktilde, lay.off_p, lay.off_s, lay.off_fox_local, lay.off_fox_total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and lay.total_bytes >= offs[-1]
+
+
+def fwd(L, q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=None, B=1, H=1, Lq=64, d=16,
+        chunk=16, scale=0.25, dtype=F32, transport=0, ws=FAKE, ws_n=1 << 30):
+    return L.path_attn_fwd(q, k, v, w, beta, logf, out, lse, B, H, Lq, d, chunk, scale, dtype, transport, ws, ws_n,
+                           None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, q=None) == INVALID
+    assert fwd(L, out=None) == INVALID
+    assert fwd(L, ws=None) == INVALID
+    assert fwd(L, beta=None) == INVALID
+    assert fwd(L, ws_n=100) == INVALID  # workspace too small
+    assert fwd(L, d=48) == UNSUPPORTED
+    assert fwd(L, chunk=8) == UNSUPPORTED
+    assert fwd(L, dtype=3) == UNSUPPORTED
+    assert fwd(L, q=MISALIGNED) == UNSUPPORTED
+    assert fwd(L, lse=MISALIGNED) == UNSUPPORTED
+    assert fwd(L, B=-1) == INVALID
+    # empty problems are valid and enqueue nothing, even with null tensors
+    assert fwd(L, Lq=0, q=None, k=None, out=None, ws=None) == OK
+    assert fwd(L, B=0, q=None, ws=None) == OK
+
+
+def dec(L, kc=FAKE, vc=FAKE, cap=128, t=10, q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, out=FAKE, lse=None, B=1, H=1,
+        d=64, scale=0.125, dtype=BF16, splits=0, ws=FAKE, ws_n=1 << 20):
+    return L.path_decode_step(kc, vc, cap, t, q, k, v, w, beta, out, lse, B, H, d, scale, dtype, splits, ws, ws_n,
+                              None)
+
+
+def test_decode_validation(L):
+    assert dec(L, t=128) == INVALID  # t >= capacity
+    assert dec(L, t=-1) == INVALID
+    assert dec(L, kc=None) == INVALID
+    assert dec(L, w=None) == INVALID
+    assert dec(L, d=48) == UNSUPPORTED
+    assert dec(L, dtype=9) == UNSUPPORTED
+    assert dec(L, vc=MISALIGNED) == UNSUPPORTED
+    assert dec(L, ws_n=16) == INVALID
+    assert dec(L, splits=-2) == INVALID
+    assert dec(L, B=0, kc=None) == OK
+    n = ctypes.c_size_t(0)
+    assert L.path_decode_workspace_bytes(32, 24, 64, 65536 + 128, 0, ctypes.byref(n)) == OK
+    assert n.value == 32 * 24 * 65 * 66 * 4
+    assert L.path_decode_workspace_bytes(1, 1, 48, 100, 0, ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        native.path_attn_fwd(x, x, x, x, torch.zeros(1, 1, 4))

@@ -1,0 +1,99 @@
+"""Parity of the decode step (in-place key update + split-key attention) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dependent_positional_attention_amd import native, synth
+from tests.gpu_util import assert_parity, dev, dev_f32, errors, host
+
+pytestmark = pytest.mark.gpu
+
+
+def check_cache(got, want, dtype, steps):
+    """The cache is stored state, re-rounded to the storage dtype at every step (the in-place update
+    rule itself), while the oracle keeps it in fp64.  Each rounding moves an element by at most half
+    an ulp (2^-8 relative for bf16) and the transitions never grow a key's norm, so after `steps`
+    steps a bf16 cache is within (steps + 1) half-ulps of the largest element.  An fp32 cache is held
+    to the fp32 output tolerance."""
+    bound = (steps + 1) * 2.0 ** -8 * np.max(np.abs(want)) if dtype == "bf16" else 1e-5
+    ma, rel = errors(got, want)
+    assert ma <= bound, f"cache max_abs {ma:.3e} > derived bound {bound:.3e}"
+    assert rel <= (1e-2 if dtype == "bf16" else 1e-5), f"cache rel_l2 {rel:.3e}"
+
+
+def run_steps(kc, vc, t0, steps: synth.DecodeStepInputs, splits=0):
+    outs, lses = [], []
+    S = steps.q.shape[0]
+    for s in range(S):
+        o, l = native.path_decode_step(kc, vc, t0 + s, dev(steps.q[s], steps.dtype), dev(steps.k[s], steps.dtype),
+                                       dev(steps.v[s], steps.dtype), dev(steps.w[s], steps.dtype),
+                                       dev_f32(steps.beta[s]), scale=steps.scale, splits=splits)
+        outs.append(host(o))
+        lses.append(host(l))
+    torch.cuda.synchronize()
+    return np.stack(outs), np.stack(lses)
+
+
+def oracle_steps(cache_k, cache_v, t0, cap, steps):
+    B, H, _, d = cache_k.shape
+    BH = B * H
+    kc = np.zeros((BH, cap, d))
+    vc = np.zeros((BH, cap, d))
+    kc[:, :t0] = cache_k.reshape(BH, -1, d)[:, :t0]
+    vc[:, :t0] = cache_v.reshape(BH, -1, d)[:, :t0]
+    S = steps.q.shape[0]
+    sh = lambda x: x.reshape(S, BH, -1) if x.ndim == 4 else x.reshape(S, BH)
+    out, lse = oracle.decode(kc, vc, t0, sh(steps.q), sh(steps.k), sh(steps.v), sh(steps.w), sh(steps.beta),
+                             steps.scale)
+    return out.reshape(S, B, H, d), lse.reshape(S, B, H), kc.reshape(B, H, cap, d)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 16), ("bf16", 128), ("f32", 64), ("bf16", 16),
+                                     ("f32", 128), ("bf16", 32)])
+def test_decode_with_cache(dtype, d):
+    B, H, T0, S = 2, 3, 700, 6
+    cap = T0 + S + 5
+    print(f"[case] decode dtype={dtype} d={d} T0={T0} steps={S}", flush=True)
+    ck, cv = synth.make_decode_cache(B, H, T0, d, dtype=dtype, seed=d)
+    steps = synth.make_decode_steps(S, B, H, d, dtype=dtype, seed=d)
+    kc = torch.zeros((B, H, cap, d), device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :T0] = dev(ck, dtype)
+    vc[:, :, :T0] = dev(cv, dtype)
+    go, gl = run_steps(kc, vc, T0, steps)
+    ro, rl, rk = oracle_steps(ck, cv, T0, cap, steps)
+    assert_parity(go, ro, dtype, "out")
+    assert_parity(gl, rl, dtype, "lse")
+    check_cache(host(kc)[:, :, :T0 + S], rk[:, :, :T0 + S], dtype, S)
+    assert np.all(host(kc)[:, :, T0 + S:] == 0)  # slots past t untouched
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_from_empty_equals_prefill(dtype):
+    """Decoding S tokens from an empty cache reproduces prefill rows 0..S-1 (oracle prefill)."""
+    B, H, S, d = 1, 4, 40, 64
+    steps = synth.make_decode_steps(S, B, H, d, dtype=dtype, seed=2)
+    kc = torch.zeros((B, H, S, d), device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    vc = torch.zeros_like(kc)
+    go, gl = run_steps(kc, vc, 0, steps)
+    tr = lambda x: np.ascontiguousarray(np.moveaxis(x, 0, 2))  # [S,B,H,...] -> [B,H,S,...]
+    ro, rl = oracle.fwd(tr(steps.q), tr(steps.k), tr(steps.v), tr(steps.w), tr(steps.beta), scale=steps.scale)
+    assert_parity(tr(go), ro, dtype, "out")
+    assert_parity(tr(gl), rl, dtype, "lse")
+
+
+def test_split_count_does_not_change_the_cache():
+    """Splits own disjoint key ranges: the updated cache is bit-identical for any split count."""
+    B, H, T0, d = 2, 2, 3000, 64
+    ck, cv = synth.make_decode_cache(B, H, T0 + 1, d, dtype="bf16", seed=5)
+    steps = synth.make_decode_steps(1, B, H, d, dtype="bf16", seed=5)
+    res = []
+    for splits in (1, 3, 0, 64):
+        kc, vc = dev(ck, "bf16"), dev(cv, "bf16")
+        o, _ = run_steps(kc, vc, T0, steps, splits=splits)
+        res.append((kc.view(torch.int16).cpu().numpy(), o))
+    for kbits, o in res[1:]:
+        assert np.array_equal(kbits, res[0][0])
+        ma, rel = errors(o, res[0][1])
+        assert ma <= 1e-3 and rel <= 1e-3

@@ -1,0 +1,148 @@
+"""Parity of the matrix-core prefill path (bf16 inputs, fp32 accumulation, head dim 64, chunk 64)
+against the fp64 oracle: per-chunk intermediates, end-to-end outputs at small shapes spanning several
+tiles and a ragged tail, and sampled rows at the full 760M-class / PaTH-FoX / long-context shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dependent_positional_attention_amd import native, synth
+from tests.gpu_util import assert_parity, errors, fwd_inputs_dev, host, TOL
+
+pytestmark = pytest.mark.gpu
+
+C, D = 64, 64
+
+
+def perm_src():
+    """Original column held by each stored slot (slot 8g+j of a 32-block holds 16(j/4)+4g+(j%4))."""
+    idx = np.zeros(64, dtype=np.int64)
+    for p in range(64):
+        blk, p32 = divmod(p, 32)
+        g, j = divmod(p32, 8)
+        idx[p] = 32 * blk + 16 * (j // 4) + 4 * g + (j % 4)
+    return idx
+
+
+PERM = perm_src()
+
+
+def unpermute_cols(x):
+    out = np.empty_like(x)
+    out[..., PERM] = x
+    return out
+
+
+def run(x, transport="bf16", chunk=C, keep_ws=False):
+    t = fwd_inputs_dev(x)
+    B, H, L, d = x.q.shape
+    n = native.path_attn_fwd_workspace_bytes(B, H, L, d, chunk, torch.bfloat16, transport)
+    ws = torch.zeros(max(n, 16), device="cuda", dtype=torch.uint8)
+    out, lse = native.path_attn_fwd(t["q"], t["k"], t["v"], t["w"], t["beta"], t["logf"], scale=x.scale,
+                                    chunk=chunk, transport=transport, workspace=ws)
+    torch.cuda.synchronize()
+    if keep_ws:
+        return host(out), host(lse), ws
+    return host(out), host(lse)
+
+
+def ws_view(ws, off, count, dtype):
+    b = ws[off:off + count * (2 if dtype == torch.bfloat16 else 4)]
+    return b.view(dtype).float().cpu().numpy().astype(np.float64)
+
+
+def test_layout_is_matrix_core():
+    lay = native.path_attn_workspace_layout(1, 1, 128, D, C, torch.bfloat16, "bf16x3")
+    assert lay.layout_id == 1 and lay.off_vt >= 0 and lay.off_p_lo >= 0
+
+
+@pytest.mark.parametrize("recipe", ["stress_qk", "beta2", "lm"])
+def test_chunk_intermediates(recipe):
+    """qtilde, ktilde, P (hi+lo), S and V^T of every chunk against the oracle's by-definition terms."""
+    B, H, L = 1, 2, 150
+    x = synth.make_fwd_inputs(B, H, L, D, recipe=recipe, dtype="bf16", seed=11)
+    print(f"[case] intermediates recipe={recipe}", flush=True)
+    _, _, ws = run(x, "bf16x3", keep_ws=True)
+    lay = native.path_attn_workspace_layout(B, H, L, D, C, torch.bfloat16, "bf16x3")
+    M = lay.num_chunks
+    Lp = M * C
+    qt = unpermute_cols(ws_view(ws, lay.off_qtilde, B * H * Lp * D, torch.bfloat16).reshape(B * H, Lp, D))
+    kt = unpermute_cols(ws_view(ws, lay.off_ktilde, B * H * Lp * D, torch.bfloat16).reshape(B * H, Lp, D))
+    ph = ws_view(ws, lay.off_p, B * H * M * D * D, torch.bfloat16).reshape(B * H, M, D, D)
+    pl = ws_view(ws, lay.off_p_lo, B * H * M * D * D, torch.bfloat16).reshape(B * H, M, D, D)
+    P = unpermute_cols(ph + pl)
+    S = ws_view(ws, lay.off_s, B * H * M * C * C, torch.float32).reshape(B * H, M, C, C)
+    vt = ws_view(ws, lay.off_vt, B * H * M * D * C, torch.bfloat16).reshape(B * H, M, D, C)
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        for c in range(M):
+            rows = slice(c * C, min((c + 1) * C, L))
+            n = rows.stop - rows.start
+            q, k, w, v = (getattr(x, a)[b, h, rows].astype(np.float64) for a in ("q", "k", "w", "v"))
+            beta = x.beta[b, h, rows].astype(np.float64)
+            rq, rk, rs = oracle.chunk_terms(q, k, w, beta)
+            scale = max(1.0, np.abs(rq).max())
+            assert errors(qt[bh, c * C:c * C + n], rq)[0] <= 2 ** -7 * scale, f"qtilde chunk {c}"
+            assert errors(kt[bh, c * C:c * C + n], rk)[0] <= 2 ** -7 * max(1.0, np.abs(rk).max()), f"ktilde {c}"
+            # the padded tail of a ragged chunk holds identity transitions
+            rp = oracle.householder_product(w, beta)
+            ma, _ = errors(P[bh, c], rp)
+            assert ma <= 2e-5, f"P chunk {c}: {ma:.2e}"
+            ms, _ = errors(np.tril(S[bh, c, :n, :n]), np.tril(rs))
+            assert ms <= 2e-2 * max(1.0, np.abs(rs).max()), f"S chunk {c}: {ms:.2e}"
+            vfull = np.zeros((C, D))
+            vfull[:n] = v
+            assert np.array_equal(unpermute_cols(vt[bh, c]), vfull.T), f"V^T chunk {c}"
+
+
+CASES = [
+    (2, 3, 64, "lm", "bf16"), (2, 3, 100, "stress_qk", "bf16"), (1, 2, 256, "beta2", "bf16"),
+    (1, 2, 700, "beta02", "bf16"), (2, 2, 1000, "stress_qk", "bf16x3"), (1, 3, 1, "lm", "bf16"),
+    (1, 2, 65, "fox", "bf16"), (2, 2, 777, "fox", "bf16x3"), (1, 2, 513, "stress_qk_beta2", "bf16x3"),
+    (1, 1, 300, "beta0", "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,L,recipe,transport", CASES)
+def test_small_shapes(B, H, L, recipe, transport):
+    x = synth.make_fwd_inputs(B, H, L, D, recipe=recipe, dtype="bf16", seed=L)
+    print(f"[case] mfma B={B} H={H} L={L} recipe={recipe} transport={transport}", flush=True)
+    go, gl = run(x, transport)
+    ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf, scale=x.scale)
+    assert_parity(go, ro, "bf16", "out")
+    assert_parity(gl, rl, "bf16", "lse")
+
+
+def test_negative_control_plain_attention_fails():
+    x = synth.make_fwd_inputs(1, 2, 512, D, recipe="stress_qk", dtype="bf16", seed=4)
+    ro, _ = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, scale=x.scale)
+    plain = synth.FwdInputs(**{**x.__dict__, "beta": np.zeros_like(x.beta)})
+    go, _ = run(plain)
+    ma, rel = errors(go, ro)
+    assert ma > TOL["bf16"]["max_abs"] and rel > TOL["bf16"]["rel_l2"]
+
+
+def sampled_rows(L, seed=0):
+    rng = np.random.default_rng(seed)
+    blocks = [np.arange(0, 64), np.arange(L - 64, L)]
+    for s in rng.choice(np.arange(1, L // 64 - 1), size=4, replace=False):
+        blocks.append(np.arange(64 * s, 64 * s + 64))
+    return np.unique(np.concatenate(blocks))
+
+
+@pytest.mark.parametrize("B,H,L,recipe,transport", [
+    (8, 24, 4096, "lm", "bf16"),         # 760M-class layer
+    (8, 24, 4096, "fox", "bf16"),        # PaTH-FoX at the same shape
+    (8, 24, 4096, "stress_qk", "bf16"),  # S1 at full shape
+    (1, 24, 32768, "lm", "bf16x3"),      # long-context extrapolation shape
+    (1, 24, 32768, "stress_qk_beta2", "bf16x3"),  # S1+S2: norm-preserving long-range transport
+])
+def test_full_size_sampled_rows(B, H, L, recipe, transport):
+    print(f"[case] full B={B} H={H} L={L} recipe={recipe} transport={transport}", flush=True)
+    x = synth.make_fwd_inputs(B, H, L, D, recipe=recipe, dtype="bf16", seed=0)
+    go, gl = run(x, transport)
+    rows = sampled_rows(L)
+    ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf, scale=x.scale, rows=rows)
+    assert_parity(go[:, :, rows], ro, "bf16", "out")
+    assert_parity(gl[:, :, rows], rl, "bf16", "lse")
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
