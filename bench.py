@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""PaTH attention benchmark on one MI355X.
+
+Prefill workload (the line's `value`): the 760M-class layer, B=8, H=24, L=4096,
+d=64, chunk 64, bf16 inputs with fp32 accumulation, synthetic seeded inputs
+(q,k,v ~ N(0,1)/sqrt(d), unit Gaussian w, beta = 2*sigmoid(N(0,1.5))).  One
+step = one path_attn_fwd call (per-chunk prep + attention scan) over inputs
+already resident in HBM; value = B*L / step time, in tokens/s.
+
+Also reported on the same JSON line:
+  roofline      the attention-scan kernel (the dominant one), timed alone with
+                HIP events on the stream it runs on: algorithmic flops per launch
+                (4 d L(L+1)/2 B H for QK^T and PV over the causal pairs, plus
+                2 C d^2 (M-1)(M-2)/2 B H for the chunk-to-chunk query transport)
+                over the measured launch time, against the bf16 MFMA peak.
+  cpu_baseline  the fp64 CPU oracle timed on this host over a bounded sample of
+                the same workload (whole heads), scaled to tokens/s.
+  decode        batch 32, H=24, d=64, 65536 cached tokens, 128 steps timed back
+                to back: HBM bytes the step must move (cached keys read and
+                written back, cached values read) over the measured time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU, dense
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--transport", default="bf16", choices=["bf16", "bf16x3"])
+    ap.add_argument("--fox", action="store_true", help="PaTH-FoX prefill (log-forget gates) instead of PaTH")
+    ap.add_argument("--L", type=int, default=4096)
+    ap.add_argument("--B", type=int, default=8)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--decode-cache", type=int, default=65536)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def prefill_flops(B, H, L, d, C):
+    M = -(-L // C)
+    return 4.0 * d * (L * (L + 1) / 2) * B * H + 2.0 * C * d * d * ((M - 1) * (M - 2) / 2) * B * H
+
+
+def timed(fn, n):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def bench_prefill(args):
+    import torch
+    from dependent_positional_attention_amd import native, synth
+
+    B, H, L, d, C = args.B, 24, args.L, 64, 64
+    recipe = "fox" if args.fox else "lm"
+    log(f"[bench] generating prefill inputs B={B} H={H} L={L} d={d} recipe={recipe}")
+    x = synth.make_fwd_inputs(B, H, L, d, recipe=recipe, dtype="bf16", seed=0)
+
+    def dev_bf16(a):
+        return torch.from_numpy(synth.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+
+    q, k, v, w = (dev_bf16(getattr(x, n)) for n in ("q", "k", "v", "w"))
+    beta = torch.from_numpy(x.beta).cuda()
+    logf = torch.from_numpy(x.logf).cuda() if x.logf is not None else None
+    nbytes = native.path_attn_fwd_workspace_bytes(B, H, L, d, C, torch.bfloat16, args.transport)
+    ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), device="cuda", dtype=torch.float32)
+
+    def step():
+        native.path_attn_fwd(q, k, v, w, beta, logf, scale=x.scale, chunk=C, transport=args.transport, out=out,
+                             lse=lse, workspace=ws)
+
+    def prep():
+        native.path_attn_prep(q, k, v, w, beta, logf, chunk=C, transport=args.transport, workspace=ws)
+
+    def scan():
+        native.path_attn_scan(v, logf, scale=x.scale, chunk=C, transport=args.transport, workspace=ws, out=out,
+                              lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] prefill warmup done; timing {args.steps} steps")
+    t0 = time.perf_counter()
+    ms_step = timed(step, args.steps)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the dominant kernel alone (scan), and the prep alone, same stream, same workspace
+    prep()
+    ms_prep = timed(prep, args.steps)
+    ms_scan = timed(scan, args.steps)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+    F = prefill_flops(B, H, L, d, C)
+    tflops = F / (ms_scan * 1e-3) / 1e12
+    log(f"[bench] prefill: step {ms_step:.3f} ms (wall {wall_ms:.3f}), prep {ms_prep:.3f} ms, scan {ms_scan:.3f} ms, "
+        f"scan {tflops:.1f} TFLOP/s = {tflops / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak; "
+        f"whole step {F / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s")
+    res = dict(B=B, H=H, L=L, d=d, C=C, recipe=recipe, ms_step=ms_step, wall_ms=wall_ms, ms_prep=ms_prep,
+               ms_scan=ms_scan, flops=F, scan_tflops=tflops, tokens_per_s=B * L / (ms_step * 1e-3))
+    return res, x
+
+
+def bench_cpu(x, args):
+    import numpy as np
+    import oracle
+
+    B, H, L, d = x.q.shape
+    cores = oracle.host_threads()
+    # calibrate on 2 heads, then size the sample to about args.cpu_seconds
+    heads = [(0, 0), (0, 1)]
+
+    def run(hs):
+        sel = lambda a: np.stack([a[b, h] for b, h in hs])
+        t0 = time.perf_counter()
+        oracle.fwd(sel(x.q), sel(x.k), sel(x.v), sel(x.w), sel(x.beta),
+                   logf=None if x.logf is None else sel(x.logf), scale=x.scale, nthreads=cores)
+        return time.perf_counter() - t0
+
+    t = run(heads)
+    per_head = t / len(heads)
+    n = int(max(1, min(B * H, args.cpu_seconds / max(per_head, 1e-3))))
+    hs = [divmod(i, H) for i in range(n)]
+    t = run(hs)
+    scale = (B * H) / n
+    tok_s = B * L / (t * scale)
+    log(f"[bench] cpu oracle: {n} of {B * H} heads (all {L} rows each) in {t:.2f} s on {cores} threads "
+        f"-> {tok_s:.1f} tokens/s for the full workload")
+    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {B * H} (batch, head) slices, every one of the {L} query rows, fp64; "
+                      f"time scaled by {scale:.2f} to the full B={B}, H={H} workload",
+            "seconds": t}
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+    from dependent_positional_attention_amd import native, synth
+
+    Bd, H, d = 32, 24, 64
+    T0, S = args.decode_cache, args.decode_steps
+    W = 3
+    cap = T0 + S
+    log(f"[bench] decode: batch {Bd}, H {H}, d {d}, cache {T0}, {S} steps; filling the cache on the GPU")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    kc = torch.empty((Bd, H, cap, d), device="cuda", dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+    for b in range(Bd):  # N(0,1)/sqrt(d) drawn on the device, one batch row at a time
+        kc[b] = (torch.randn((H, cap, d), device="cuda", generator=gen) / math.sqrt(d)).to(torch.bfloat16)
+        vc[b] = (torch.randn((H, cap, d), device="cuda", generator=gen) / math.sqrt(d)).to(torch.bfloat16)
+    st = synth.make_decode_steps(S + W, Bd, H, d, dtype="bf16", seed=0)
+
+    def dev_bf16(a):
+        return torch.from_numpy(synth.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+
+    qs, ks, vs, wsd = (dev_bf16(getattr(st, n)) for n in ("q", "k", "v", "w"))
+    betas = torch.from_numpy(st.beta).cuda()
+    out = torch.empty((Bd, H, d), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((Bd, H), device="cuda", dtype=torch.float32)
+    wsb = torch.empty(native.path_decode_workspace_bytes(Bd, H, d, cap), device="cuda", dtype=torch.uint8)
+
+    def step(i, t):
+        native.path_decode_step(kc, vc, t, qs[i], ks[i], vs[i], wsd[i], betas[i], scale=st.scale, out=out, lse=lse,
+                                workspace=wsb)
+
+    for i in range(W):
+        step(i, T0 - W + i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(S):
+        step(W + i, T0 + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    # bytes the step must move: cached keys read + written back, cached values read (t keys each),
+    # plus the new token's q, k, v, w read and its k, v written
+    nbytes = sum(Bd * H * (3 * (T0 + i) * d * 2 + 6 * d * 2) for i in range(S))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] decode: {S} steps in {ms:.2f} ms ({ms / S:.3f} ms/step), {gbs:.0f} GB/s "
+        f"= {gbs / HBM_PEAK_GBS:.3f} of HBM peak")
+    return {"metric": "PaTH decode step HBM GB/s at 64K cache", "value": gbs, "unit": "GB/s",
+            "ms_per_step": ms / S, "steps": S,
+            "config": {"workload": "decode batch 32 x 24 heads, d=64, bf16 cache of 65536 tokens growing by 1/step",
+                       "batch": Bd, "heads": H, "d": d, "cache_tokens": T0},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "decode update+attend and combine, whole step"}}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures PaTH attention on ONE MI355X: this build has no multi-GPU path, so "
+              "--gpus N with N > 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    res, x = bench_prefill(args)
+    cpu = None if args.no_cpu else bench_cpu(x, args)
+    dec = None if args.no_decode else bench_decode(args)
+    F = res["flops"]
+    achieved = F / (res["ms_scan"] * 1e-3) / 1e12
+    line = {
+        "metric": "PaTH fwd tokens/s + MFMA TFLOPS% at L=4096; decode GB/s% at 64K cache",
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"PaTH{'-FoX' if args.fox else ''} prefill forward, 760M-class layer",
+                   "B": res["B"], "H": res["H"], "L": res["L"], "d": res["d"], "chunk": res["C"],
+                   "transport": args.transport, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "mfma_attn_kernel",
+                     "launch_ms": res["ms_scan"], "flops_per_launch": F},
+        "prefill_detail": {"ms_prep": res["ms_prep"], "ms_scan": res["ms_scan"], "wall_ms_per_step": res["wall_ms"],
+                           "step_tflops": F / (res["ms_step"] * 1e-3) / 1e12,
+                           "step_frac_of_peak": F / (res["ms_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

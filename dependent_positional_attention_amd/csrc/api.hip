@@ -7,15 +7,15 @@
 namespace pathattn {
 // vector_path.hip
 bool vec_supported(int d, int chunk);
-hipError_t vec_fwd(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
-                   const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L, float scale,
-                   float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st);
+hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
+                   const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
+                   float scale, float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st);
 // mfma_path.hip
 bool mfma_supported(int d, int chunk);
-hipError_t mfma_fwd(int chunk, int transport, const void* q, const void* k, const void* v, const void* w,
-                    const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
-                    float scale, void* qt, void* kt, void* vt, void* p_hi, void* p_lo, float* Sm, float* fl,
-                    float* ftot, hipStream_t st);
+hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const void* k, const void* v,
+                    const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH,
+                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, float* Sm,
+                    float* fl, float* ftot, hipStream_t st);
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
@@ -56,8 +56,8 @@ path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   };
   *lay = path_ws_layout{};
   lay->num_chunks = M;
-  lay->off_vt = -1;
   lay->off_p_lo = -1;
+  lay->off_qtilde_lo = -1;
   if (!mfma) {
     lay->layout_id = 0;
     lay->off_qtilde = take(BH * Lp * d * 4);
@@ -66,8 +66,8 @@ path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   } else {
     lay->layout_id = 1;
     lay->off_qtilde = take(BH * Lp * d * 2);
+    if (transport == PATH_TRANSPORT_BF16X3) lay->off_qtilde_lo = take(BH * Lp * d * 2);
     lay->off_ktilde = take(BH * Lp * d * 2);
-    lay->off_vt = take(BH * M * d * chunk * 2);
     lay->off_p = take(BH * M * d * d * 2);
     if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_lo = take(BH * M * d * d * 2);
   }
@@ -117,16 +117,27 @@ path_status path_attn_workspace_layout(int64_t B, int64_t H, int64_t L, int d, i
   return plan_fwd(B, H, L, d, chunk, dtype, transport, layout);
 }
 
-path_status path_attn_fwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
-                          const float* log_forget, void* out, float* lse, int64_t B, int64_t H, int64_t L,
-                          int d, int chunk, float scale, int dtype, int transport, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kPhasePrep = 1, kPhaseScan = 2;
+
+// Shared body of path_attn_prep / path_attn_scan / path_attn_fwd.  The prep phase reads
+// q, k, v, w, beta, log_forget; the scan phase reads v (vector path) and log_forget
+// (only whether it is NULL) and writes out and lse.
+path_status run_fwd(int phases, const void* q, const void* k, const void* v, const void* w, const float* beta,
+                    const float* log_forget, void* out, float* lse, int64_t B, int64_t H, int64_t L, int d,
+                    int chunk, float scale, int dtype, int transport, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   path_ws_layout lay;
   const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
   if (s != PATH_OK) return s;
   const int64_t BH = B * H;
   if (BH == 0 || L == 0) return PATH_OK;
-  if (!q || !k || !v || !w || !beta || !out || !workspace) return PATH_ERR_INVALID_ARG;
+  if (!workspace) return PATH_ERR_INVALID_ARG;
+  if ((phases & kPhasePrep) && (!q || !k || !v || !w || !beta)) return PATH_ERR_INVALID_ARG;
+  if ((phases & kPhaseScan) && (!out || !v)) return PATH_ERR_INVALID_ARG;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(w) || misaligned(beta) ||
       misaligned(log_forget) || misaligned(out) || misaligned(lse) || misaligned(workspace))
     return PATH_ERR_UNSUPPORTED;
@@ -138,13 +149,41 @@ path_status path_attn_fwd(const void* q, const void* k, const void* v, const voi
   float* ftot = reinterpret_cast<float*>(ws + lay.off_fox_total);
   float* Sm = reinterpret_cast<float*>(ws + lay.off_s);
   if (lay.layout_id == 1) {
-    return from_hip(mfma_fwd(chunk, transport, q, k, v, w, beta, log_forget, out, lse, BH, L, scale,
-                             ws + lay.off_qtilde, ws + lay.off_ktilde, ws + lay.off_vt, ws + lay.off_p,
+    return from_hip(mfma_run(phases, chunk, transport, q, k, v, w, beta, log_forget, out, lse, BH, L, scale,
+                             ws + lay.off_qtilde, lay.off_qtilde_lo >= 0 ? ws + lay.off_qtilde_lo : nullptr,
+                             ws + lay.off_ktilde, ws + lay.off_p,
                              lay.off_p_lo >= 0 ? ws + lay.off_p_lo : nullptr, Sm, fl, ftot, st));
   }
-  return from_hip(vec_fwd(dtype == PATH_DTYPE_BF16, d, chunk, q, k, v, w, beta, log_forget, out, lse, BH, L, scale,
-                          reinterpret_cast<float*>(ws + lay.off_qtilde), reinterpret_cast<float*>(ws + lay.off_ktilde),
-                          reinterpret_cast<float*>(ws + lay.off_p), Sm, fl, ftot, st));
+  return from_hip(vec_run(phases, dtype == PATH_DTYPE_BF16, d, chunk, q, k, v, w, beta, log_forget, out, lse, BH, L,
+                          scale, reinterpret_cast<float*>(ws + lay.off_qtilde),
+                          reinterpret_cast<float*>(ws + lay.off_ktilde), reinterpret_cast<float*>(ws + lay.off_p),
+                          Sm, fl, ftot, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+path_status path_attn_fwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                          const float* log_forget, void* out, float* lse, int64_t B, int64_t H, int64_t L,
+                          int d, int chunk, float scale, int dtype, int transport, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return run_fwd(kPhasePrep | kPhaseScan, q, k, v, w, beta, log_forget, out, lse, B, H, L, d, chunk, scale, dtype,
+                 transport, workspace, workspace_bytes, stream);
+}
+
+path_status path_attn_prep(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                           const float* log_forget, int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                           int transport, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_fwd(kPhasePrep, q, k, v, w, beta, log_forget, nullptr, nullptr, B, H, L, d, chunk, 1.f, dtype,
+                 transport, workspace, workspace_bytes, stream);
+}
+
+path_status path_attn_scan(const void* v, const float* log_forget, void* out, float* lse, int64_t B, int64_t H,
+                           int64_t L, int d, int chunk, float scale, int dtype, int transport, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return run_fwd(kPhaseScan, nullptr, nullptr, v, nullptr, nullptr, log_forget, out, lse, B, H, L, d, chunk, scale,
+                 dtype, transport, workspace, workspace_bytes, stream);
 }
 
 path_status path_decode_workspace_bytes(int64_t B, int64_t H, int d, int64_t capacity, int splits,

@@ -20,18 +20,21 @@
 //
 // Kernel 2 (attention), one workgroup of 4 waves per 4 consecutive query chunks
 // (wave w owns chunk 4p+w, 64 queries = four 16-query MFMA column tiles), longest
-// rows first.  The waves share one LDS stream of key chunks n = 4p+2 ... 0
-// (ktilde_n, V_n^T, P_n, double-buffered); each A-fragment read from LDS feeds
-// four MFMAs (one per query tile).  Per key chunk and wave:
+// rows first.  The waves share one LDS stream of key chunks n = 4p+3 ... 0
+// (ktilde_n, V_n straight from the value tensor, P_n; double-buffered, filled by
+// direct global->LDS loads); each A-fragment read from LDS feeds four MFMAs (one
+// per query tile).  A wave scores its own chunk from the precomputed in-chunk
+// logits when the stream reaches it, and earlier chunks as follows:
 //   S^T = ktilde_n Q_run^T       (keys x queries: each lane holds one query column)
 //   online softmax (exp2), P^T kept in registers as the PV B-operand
 //   O^T += V_n^T P^T
 //   Q_run^T <- P_n Q_run^T       (fp32 accumulate, re-rounded to bf16 [hi+lo])
 // Column permutation: an MFMA accumulator gives each lane rows 4g..4g+3 of every
 // 16-row tile, while a B-operand wants rows 8g..8g+7 of every 32-row k-step.  The
-// contraction order is free, so qtilde, ktilde, P (columns) and V^T (key index)
-// are stored with stored slot 8g+j of each 32-block holding index 16(j/4)+4g+(j%4);
-// accumulators then convert to B-operands in registers with no data movement.
+// contraction order is free, so qtilde, ktilde and P (columns) are stored with
+// stored slot 8g+j of each 32-block holding index 16(j/4)+4g+(j%4), and V^T
+// fragments are read (LDS transpose reads) in the same key order; accumulators then
+// convert to B-operands in registers with no data movement.
 #include "common.h"
 
 namespace pathattn {
@@ -82,36 +85,58 @@ __device__ __forceinline__ void split_hi_lo(float v, __bf16& hi, __bf16& lo) {
   lo = (__bf16)(v - (float)hi);
 }
 
+// Four values -> hi and lo bf16 quads with v ~= hi + lo.
+__device__ __forceinline__ void split4(float v0, float v1, float v2, float v3, bf16x4& h, bf16x4& l) {
+  const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 hi = (__bf16)v[i];
+    h[i] = hi;
+    l[i] = (__bf16)(v[i] - (float)hi);
+  }
+}
+
 }  // namespace
 
 // =========================================================================== kernel 1: prep
-constexpr size_t kPrepLds = 11 * kMat * 2 + 64 * 4 + 2 * kC * kLDF * 4 + 3 * 256 * 4;
+// LDS plan (bytes): 13 padded bf16 64x64 matrices + beta + an fp32 region for A, Z = A^{-1}
+// and block temporaries.  Regions are reused once their contents are dead:
+//   R1 (4 mats): W, Q, K in phases A-B; X^T hi/lo and Y hi/lo in phases E-F
+//   R2 (1 mat):  W^T throughout
+//   R3 (4 mats): U^T hi/lo, R hi/lo
+//   R4 (4 mats): T^{-1} hi/lo, T^{-T} hi/lo
+//   R5 (fp32):   A, Z, temporaries in phases B-D; (T^{-1}W)^T hi/lo in phases E-F
+constexpr size_t kPrepLds = 13 * kMat * 2 + 64 * 4 + 2 * kC * kLDF * 4 + 3 * 256 * 4;
+static_assert(kPrepLds <= 160 * 1024, "prep LDS plan exceeds 160 KiB");
 
 __global__ __launch_bounds__(256) void mfma_prep_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ w, const float* __restrict__ beta, const float* __restrict__ logf, int64_t L,
-    int64_t M, __bf16* __restrict__ qt, __bf16* __restrict__ kt, __bf16* __restrict__ vt,
-    __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo, float* __restrict__ Sm, float* __restrict__ fl,
-    float* __restrict__ ftot) {
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
+    const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, __bf16* __restrict__ qt,
+    __bf16* __restrict__ qt_lo, __bf16* __restrict__ kt, __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo,
+    float* __restrict__ Sm, float* __restrict__ fl, float* __restrict__ ftot) {
   extern __shared__ __align__(16) char smem[];
-  __bf16* Ws = reinterpret_cast<__bf16*>(smem);  // W [s][x]
-  __bf16* WTs = Ws + kMat;                       // W^T [x][s]
-  __bf16* Qs = WTs + kMat;                       // Q [a][x]
-  __bf16* Ks = Qs + kMat;                        // K [b][x]
-  __bf16* VXs = Ks + kMat;                       // V [b][x], later X^T [a][s]
-  __bf16* UTs = VXs + kMat;                      // U^T [a][t]
-  __bf16* Rs = UTs + kMat;                       // R [b][s]
-  __bf16* TiH = Rs + kMat;                       // T^{-1} [s][t] hi / lo
-  __bf16* TiL = TiH + kMat;
-  __bf16* TiTH = TiL + kMat;                     // T^{-T} [t][s] hi / lo
-  __bf16* TiTL = TiTH + kMat;
-  float* Bs = reinterpret_cast<float*>(TiTL + kMat);  // beta [64]
-  float* Af = Bs + 64;                                // A [64][kLDF]
-  float* Zf = Af + kC * kLDF;                         // Z = A^{-1} [64][kLDF]
-  float* Tmp = Zf + kC * kLDF;                        // 3 x 16 x 16 block temporaries
-  // After T^{-1} is formed the fp32 A/Z region holds Y and (T^{-1}W)^T hi/lo.
-  __bf16* Ys = reinterpret_cast<__bf16*>(Af);  // Y [b][t]
-  __bf16* Z2H = Ys + kMat;                      // (T^{-1} W)^T [y][s] hi / lo
+  __bf16* R1 = reinterpret_cast<__bf16*>(smem);
+  __bf16* Ws = R1;                 // W [s][x]
+  __bf16* Qs = R1 + kMat;          // Q [a][x]
+  __bf16* Ks = R1 + 2 * kMat;      // K [b][x]
+  __bf16* XTH = R1;                // X^T [a][s] hi / lo   (after phase B)
+  __bf16* XTL = R1 + kMat;
+  __bf16* YH = R1 + 2 * kMat;      // Y [b][t] hi / lo     (after phase B)
+  __bf16* YL = R1 + 3 * kMat;
+  __bf16* WTs = R1 + 4 * kMat;     // W^T [x][s]
+  __bf16* UTH = R1 + 5 * kMat;     // U^T [a][t] hi / lo
+  __bf16* UTL = R1 + 6 * kMat;
+  __bf16* RH = R1 + 7 * kMat;      // R [b][s] hi / lo
+  __bf16* RL = R1 + 8 * kMat;
+  __bf16* TiH = R1 + 9 * kMat;     // T^{-1} [s][t] hi / lo
+  __bf16* TiL = R1 + 10 * kMat;
+  __bf16* TiTH = R1 + 11 * kMat;   // T^{-T} [t][s] hi / lo
+  __bf16* TiTL = R1 + 12 * kMat;
+  float* Bs = reinterpret_cast<float*>(R1 + 13 * kMat);  // beta [64]
+  float* Af = Bs + 64;                                   // A [64][kLDF]
+  float* Zf = Af + kC * kLDF;                            // Z = A^{-1} [64][kLDF]
+  float* Tmp = Zf + kC * kLDF;                           // 3 x 16 x 16 block temporaries
+  __bf16* Z2H = reinterpret_cast<__bf16*>(Af);           // (T^{-1} W)^T [y][s] hi / lo (after phase D)
   __bf16* Z2L = Z2H + kMat;
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
@@ -119,8 +144,9 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   const int64_t bh = blockIdx.y;
   const int64_t Lp = M * kC;
   const int64_t row0 = (int64_t)c * kC;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  // ---------------------------------------------------------------- A: stage W, W^T, Q, K, V, beta
+  // ---------------------------------------------------------------- A: stage W, W^T, Q, K, beta
   for (int e = tid; e < 512; e += 256) {
     const int a = e >> 3, c8 = (e & 7) * 8;
     const int64_t i = row0 + a;
@@ -131,8 +157,7 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
     *reinterpret_cast<uint4*>(Ws + a * kLDB + c8) = wv;
     *reinterpret_cast<uint4*>(Qs + a * kLDB + c8) = ok ? *reinterpret_cast<const uint4*>(q + go) : z4;
     *reinterpret_cast<uint4*>(Ks + a * kLDB + c8) = ok ? *reinterpret_cast<const uint4*>(k + go) : z4;
-    *reinterpret_cast<uint4*>(VXs + a * kLDB + c8) = ok ? *reinterpret_cast<const uint4*>(v + go) : z4;
-    const __bf16* wb = reinterpret_cast<const __bf16*>(&wv);
+    const bf16x8 wb = __builtin_bit_cast(bf16x8, wv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) WTs[(c8 + j) * kLDB + a] = wb[j];
   }
@@ -154,35 +179,32 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- B: V^T out, A, U^T, R, K Q^T
-  for (int e = tid; e < 512; e += 256) {
-    const int d = e >> 3, ks = (e >> 2) & 1, gg = e & 3;
-    bf16x8 o8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o8[j] = VXs[(32 * ks + 16 * (j >> 2) + 4 * gg + (j & 3)) * kLDB + d];
-    *reinterpret_cast<bf16x8*>(vt + (((size_t)bh * M + c) * kD + d) * kC + 32 * ks + 8 * gg) = o8;
-  }
+  // ---------------------------------------------------------------- B: A, U^T, R, K Q^T
   f32x4 kq[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     // A[s][t] = beta_s (w_s . w_t) for s < t  (rows s in block `wave`)
-    f32x4 ga = mm_tile(Ws, Ws, 16 * wave, 16 * nb, zero);
+    const f32x4 ga = mm_tile(Ws, Ws, 16 * wave, 16 * nb, zero);
     // D[t][a] = w_t . q_a  ->  U^T[a][t], t <= a
-    f32x4 ua = mm_tile(Ws, Qs, 16 * wave, 16 * nb, zero);
+    const f32x4 ua = mm_tile(Ws, Qs, 16 * wave, 16 * nb, zero);
     // D[s][b] = w_s . k_b  ->  R[b][s], s > b
-    f32x4 ra = mm_tile(Ws, Ks, 16 * wave, 16 * nb, zero);
+    const f32x4 ra = mm_tile(Ws, Ks, 16 * wave, 16 * nb, zero);
     const int col = 16 * nb + r;
-    float u4[4], r4[4];
+    float um[4], rm[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * wave + 4 * g + i;
       Af[row * kLDF + col] = (row < col) ? Bs[row] * ga[i] : 0.f;
-      u4[i] = (row <= col) ? ua[i] : 0.f;
-      r4[i] = (row > col) ? ra[i] : 0.f;
+      um[i] = (row <= col) ? ua[i] : 0.f;
+      rm[i] = (row > col) ? ra[i] : 0.f;
     }
-    *reinterpret_cast<bf16x4*>(UTs + col * kLDB + 16 * wave + 4 * g) = pack4(u4[0], u4[1], u4[2], u4[3]);
-    *reinterpret_cast<bf16x4*>(Rs + col * kLDB + 16 * wave + 4 * g) = pack4(r4[0], r4[1], r4[2], r4[3]);
+    bf16x4 uh, ul, rh, rl;
+    split4(um[0], um[1], um[2], um[3], uh, ul);
+    split4(rm[0], rm[1], rm[2], rm[3], rh, rl);
+    *reinterpret_cast<bf16x4*>(UTH + col * kLDB + 16 * wave + 4 * g) = uh;
+    *reinterpret_cast<bf16x4*>(UTL + col * kLDB + 16 * wave + 4 * g) = ul;
+    *reinterpret_cast<bf16x4*>(RH + col * kLDB + 16 * wave + 4 * g) = rh;
+    *reinterpret_cast<bf16x4*>(RL + col * kLDB + 16 * wave + 4 * g) = rl;
     // D[b][a] = k_b . q_a for queries a in block `wave`
     kq[nb] = mm_tile(Ks, Qs, 16 * nb, 16 * wave, zero);
   }
@@ -239,72 +261,81 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- E: X^T, Y, (T^{-1}W)^T
+  // ---------------------------------------------------------------- E: X^T, Y, (T^{-1}W)^T, each hi/lo
+  // (hi+lo)(hi+lo) products drop the lo*lo term.
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const int col = 16 * nb + r;
+    const int col = 16 * nb + r, m0 = 16 * wave, n0 = 16 * nb;
+    bf16x4 h4, l4;
     // D[s][a] = X[s][a]  ->  X^T[a][s]
-    f32x4 xa = mm_tile(TiL, UTs, 16 * wave, 16 * nb, mm_tile(TiH, UTs, 16 * wave, 16 * nb, zero));
-    *reinterpret_cast<bf16x4*>(VXs + col * kLDB + 16 * wave + 4 * g) = pack4(xa[0], xa[1], xa[2], xa[3]);
+    f32x4 xa = mm_tile(TiH, UTH, m0, n0, zero);
+    xa = mm_tile(TiH, UTL, m0, n0, xa);
+    xa = mm_tile(TiL, UTH, m0, n0, xa);
+    split4(xa[0], xa[1], xa[2], xa[3], h4, l4);
+    *reinterpret_cast<bf16x4*>(XTH + col * kLDB + m0 + 4 * g) = h4;
+    *reinterpret_cast<bf16x4*>(XTL + col * kLDB + m0 + 4 * g) = l4;
     // D[t][b] = Y[b][t]  ->  Y[b][t]
-    f32x4 ya = mm_tile(TiTL, Rs, 16 * wave, 16 * nb, mm_tile(TiTH, Rs, 16 * wave, 16 * nb, zero));
-    *reinterpret_cast<bf16x4*>(Ys + col * kLDB + 16 * wave + 4 * g) = pack4(ya[0], ya[1], ya[2], ya[3]);
-    // D[s][y] = (T^{-1} W)[s][y]  ->  Z2^T[y][s] hi / lo
-    f32x4 za = mm_tile(TiL, WTs, 16 * wave, 16 * nb, mm_tile(TiH, WTs, 16 * wave, 16 * nb, zero));
-    bf16x4 zh, zl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __bf16 hi, lo;
-      split_hi_lo(za[i], hi, lo);
-      zh[i] = hi;
-      zl[i] = lo;
-    }
-    *reinterpret_cast<bf16x4*>(Z2H + col * kLDB + 16 * wave + 4 * g) = zh;
-    *reinterpret_cast<bf16x4*>(Z2L + col * kLDB + 16 * wave + 4 * g) = zl;
+    f32x4 ya = mm_tile(TiTH, RH, m0, n0, zero);
+    ya = mm_tile(TiTH, RL, m0, n0, ya);
+    ya = mm_tile(TiTL, RH, m0, n0, ya);
+    split4(ya[0], ya[1], ya[2], ya[3], h4, l4);
+    *reinterpret_cast<bf16x4*>(YH + col * kLDB + m0 + 4 * g) = h4;
+    *reinterpret_cast<bf16x4*>(YL + col * kLDB + m0 + 4 * g) = l4;
+    // D[s][y] = (T^{-1} W)[s][y]  ->  Z2^T[y][s]
+    f32x4 za = mm_tile(TiH, WTs, m0, n0, zero);
+    za = mm_tile(TiL, WTs, m0, n0, za);
+    split4(za[0], za[1], za[2], za[3], h4, l4);
+    *reinterpret_cast<bf16x4*>(Z2H + col * kLDB + m0 + 4 * g) = h4;
+    *reinterpret_cast<bf16x4*>(Z2L + col * kLDB + m0 + 4 * g) = l4;
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- F: outputs
   const size_t chunk_rows = (size_t)bh * Lp + row0;
   const size_t chunk_mat = ((size_t)bh * M + c) * kD * kD;
+  const int a = 16 * wave + r;  // query / key / P-row handled by this lane
+  const int64_t ia = row0 + a;
+  const bool aok = ia < L;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const int x0 = 16 * mb + 4 * g;  // first of this lane's four consecutive columns
-    const int a = 16 * wave + r;     // query / key / P-row handled by this lane
     const int pos = perm_pos(x0);
+    const size_t gin = ((size_t)bh * L + (aok ? ia : 0)) * kD + x0;
     // qtilde[a][x] = q_a[x] - sum_s X[s][a] w_s[x]
     {
-      const f32x4 d4 = mm_tile(WTs, VXs, 16 * mb, 16 * wave, zero);
-      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qs + a * kLDB + x0);
-      *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) =
-          pack4((float)q4[0] - d4[0], (float)q4[1] - d4[1], (float)q4[2] - d4[2], (float)q4[3] - d4[3]);
+      f32x4 d4 = mm_tile(WTs, XTH, 16 * mb, 16 * wave, zero);
+      d4 = mm_tile(WTs, XTL, 16 * mb, 16 * wave, d4);
+      bf16x4 q4 = {};
+      if (aok) q4 = *reinterpret_cast<const bf16x4*>(q + gin);
+      bf16x4 h4, l4;
+      split4((float)q4[0] - d4[0], (float)q4[1] - d4[1], (float)q4[2] - d4[2], (float)q4[3] - d4[3], h4, l4);
+      *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
+      if (qt_lo != nullptr) *reinterpret_cast<bf16x4*>(qt_lo + (chunk_rows + a) * kD + pos) = l4;
     }
     // ktilde[b][x] = k_b[x] - sum_t Y[b][t] w_t[x]
     {
-      const f32x4 d4 = mm_tile(WTs, Ys, 16 * mb, 16 * wave, zero);
-      const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Ks + a * kLDB + x0);
+      f32x4 d4 = mm_tile(WTs, YH, 16 * mb, 16 * wave, zero);
+      d4 = mm_tile(WTs, YL, 16 * mb, 16 * wave, d4);
+      bf16x4 k4 = {};
+      if (aok) k4 = *reinterpret_cast<const bf16x4*>(k + gin);
       *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) =
           pack4((float)k4[0] - d4[0], (float)k4[1] - d4[1], (float)k4[2] - d4[2], (float)k4[3] - d4[3]);
     }
     // P[x][y] = delta - sum_s w_s[x] Z2[s][y]   (lane: row x = a, columns y = x0..x0+3)
     {
-      const f32x4 d4 = mm_tile(Z2L, WTs, 16 * mb, 16 * wave, mm_tile(Z2H, WTs, 16 * mb, 16 * wave, zero));
+      f32x4 d4 = mm_tile(Z2H, WTs, 16 * mb, 16 * wave, zero);
+      d4 = mm_tile(Z2L, WTs, 16 * mb, 16 * wave, d4);
       bf16x4 ph, pl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __bf16 hi, lo;
-        split_hi_lo(((x0 + i) == a ? 1.f : 0.f) - d4[i], hi, lo);
-        ph[i] = hi;
-        pl[i] = lo;
-      }
+      split4((x0 == a ? 1.f : 0.f) - d4[0], (x0 + 1 == a ? 1.f : 0.f) - d4[1], (x0 + 2 == a ? 1.f : 0.f) - d4[2],
+             (x0 + 3 == a ? 1.f : 0.f) - d4[3], ph, pl);
       *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)a * kD + pos) = ph;
       if (p_lo != nullptr) *reinterpret_cast<bf16x4*>(p_lo + chunk_mat + (size_t)a * kD + pos) = pl;
     }
     // S[a][b] = q_a.k_b - (Y U)[b][a]   (lane: query a, keys b = x0..x0+3)
     {
-      const f32x4 d4 = mm_tile(Ys, UTs, 16 * mb, 16 * wave, zero);
+      f32x4 d4 = mm_tile(YH, UTH, 16 * mb, 16 * wave, zero);
+      d4 = mm_tile(YH, UTL, 16 * mb, 16 * wave, d4);
+      d4 = mm_tile(YL, UTH, 16 * mb, 16 * wave, d4);
       const float4 s4 = make_float4(kq[mb][0] - d4[0], kq[mb][1] - d4[1], kq[mb][2] - d4[2], kq[mb][3] - d4[3]);
       *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kC + a) * kC + x0) = s4;
     }
@@ -312,231 +343,325 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(
 }
 
 // =========================================================================== kernel 2: attention
+// LDS tiles of the key-chunk stream are 64 rows x 128 B with no padding; the 16-byte chunk c of
+// row r sits at slot c ^ (r & 7) (an XOR swizzle), so the 16 rows an MFMA fragment read touches
+// land in distinct banks.  Tiles are filled by direct global->LDS loads (16 B per lane, lane i
+// of an instruction writes slot i of a 1 KiB run), so no staging registers are needed: each lane
+// simply fetches the global chunk that belongs in its slot.
+constexpr int kTile = kC * kD;  // bf16 elements of one swizzled 64x64 tile
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Direct global->LDS copy of one 64x64 bf16 tile (row stride `gstride` elements in global) by
+// one wave: instructions i0, i0+1 each cover 8 rows.  Rows at or beyond `rmax` are clamped to
+// rmax - 1 (finite data that only ever meets masked or discarded positions).
+__device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* src, int64_t gstride, int rmax, int i0) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int i = i0; i < i0 + 2; ++i) {
+    const int row = 8 * i + (l >> 3), slot = l & 7;
+    const int rs = row < rmax ? row : rmax - 1;
+    const __bf16* g = src + (int64_t)rs * gstride + ((slot ^ (row & 7)) << 3);
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(tile + i * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 tile_frag(const __bf16* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + swz(row, chunk));
+}
+
+// V^T A-fragment from a row-major V tile ([key][d]) with two LDS transpose reads: lane (r, g) of
+// d-tile dt, k-step ks receives V[key][16dt + r] for keys 32ks + 16h + 4g + (0..3), h = 0, 1
+// (the same key order as the P^T B-operand).  Within a 16-lane group the transpose read gives
+// lane d element (d & 3) of source lanes (d >> 2) + 4j; source lane s therefore points at
+// row base + (s >> 2), columns 16dt + 4(s & 3) .. +3.
+__device__ __forceinline__ bf16x8 vt_frag(const __bf16* tile, int dt, int ks) {
+  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+  const int col = 16 * dt + 4 * (s & 3);
+  bf16x8 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 32 * ks + 16 * h + 4 * g + (s >> 2);
+    const __bf16* p = tile + swz(row, col >> 3) + (col & 7);
+    const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * h + j] = __builtin_bit_cast(__bf16, (short)t[j]);
+  }
+  return out;
+}
+
+#ifndef PATHATTN_SCAN_WAVES_PER_SIMD
+#define PATHATTN_SCAN_WAVES_PER_SIMD 2
+#endif
+
+// Max / sum over the 4 lanes holding the same query column (lanes l, l^16, l^32, l^48): each
+// permlane swap returns the value pair {own, partner} for the two lane halves it exchanges.
+// The maxima use the NaN-propagating maximum, which needs no input canonicalisation.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return max2(max2(a, b), c); }
+__device__ __forceinline__ float colmax4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float colsum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Blocks are laid out for the 8 XCDs (workgroup b runs on XCD b % 8, each with its own L2):
+// every query block of one (batch, head) lands on the same XCD, heads are dealt round-robin
+// to XCDs, and within a head the longest rows go first.
+constexpr int kXcd = 8;
+// Work split: a block of 4 waves owns kCpb consecutive query chunks; each chunk's 64 queries
+// are shared by kWpc waves of kQt 16-query MFMA column tiles each.
+constexpr int kQt = 2;
+constexpr int kWpc = 4 / kQt;
+constexpr int kCpb = 4 / kWpc;
+
+// Waves per SIMD the scan is built for (register budget 512 / waves).
 template <bool FOX, bool X3>
-__global__ __launch_bounds__(256, X3 ? 1 : 2) void mfma_attn_kernel(
-    const __bf16* __restrict__ qt, const __bf16* __restrict__ kt, const __bf16* __restrict__ vt,
-    const __bf16* __restrict__ p_hi, const __bf16* __restrict__ p_lo, const float* __restrict__ Sm,
-    const float* __restrict__ fl, const float* __restrict__ ftot, __bf16* __restrict__ out,
-    float* __restrict__ lse, int64_t L, int64_t M, float sc) {
-  constexpr int NM = X3 ? 4 : 3;  // ktilde, V^T, P hi [, P lo]
-  __shared__ __align__(16) __bf16 lds[2][NM][kMat];
-  __shared__ float lfl[2][64];
+__global__ __launch_bounds__(256, X3 ? 2 : PATHATTN_SCAN_WAVES_PER_SIMD) void mfma_attn_kernel(
+    const __bf16* __restrict__ qt, const __bf16* __restrict__ qt_lo, const __bf16* __restrict__ kt,
+    const __bf16* __restrict__ v, const __bf16* __restrict__ p_hi, const __bf16* __restrict__ p_lo,
+    const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
+    __bf16* __restrict__ out, float* __restrict__ lse, int64_t L, int64_t M, int64_t BH, float sc) {
+  constexpr int NM = X3 ? 4 : 3;  // ktilde, V, P hi [, P lo]
+  constexpr float kRescale = 8.f;  // log2 headroom before the running max must be raised
+  __shared__ __align__(1024) __bf16 lds[2][NM][kTile];
+  __shared__ __align__(16) float lfl[2][64];
+
+  const int64_t nP = (M + kCpb - 1) / kCpb;
+  const int xcd = (int)(blockIdx.x % kXcd);
+  const int64_t slot = blockIdx.x / kXcd;
+  const int64_t heads_here = (BH - xcd + kXcd - 1) / kXcd;
+  if (slot >= heads_here * nP) return;  // whole block: this XCD has fewer heads
+  const int64_t bh = xcd + kXcd * (slot / nP);
+  const int64_t p = nP - 1 - slot % nP;
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-  const int64_t nP = (M + 3) / 4;
-  const int64_t p = nP - 1 - (int64_t)blockIdx.x;  // longest rows first
-  const int64_t bh = blockIdx.y;
-  const int64_t m = 4 * p + wave;
+  const int64_t m = kCpb * p + wave / kWpc;  // this wave's query chunk
+  const int q0 = 16 * kQt * (wave % kWpc);   // first query (within the chunk) of this wave
   const bool active = m < M;
   const int64_t Lp = M * kC;
-  const int64_t mtop = (4 * p + 3 < M - 1) ? 4 * p + 3 : M - 1;  // highest query chunk of this block
+  const int64_t mtop = (kCpb * p + kCpb - 1 < M - 1) ? kCpb * p + kCpb - 1 : M - 1;  // highest chunk here
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  f32x4 o[4][4];
-  float mrow[4], lrow[4];
-  bf16x8 qb[4][2], ql[4][2];
+  f32x4 o[4][kQt];  // O^T tiles [d tile][query tile]
+  float lsum[kQt];  // this lane's share of each column's softmax denominator (fp32)
+  float mref[kQt];  // running reference max per query column (log2 units)
+  bf16x8 qb[kQt][2], ql[kQt][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    mrow[a] = -INFINITY;
-    lrow[a] = 0.f;
+  for (int a = 0; a < kQt; ++a) {
+    mref[a] = -INFINITY;
+    lsum[a] = 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) o[a][b] = zero;
+    for (int b = 0; b < 4; ++b) o[b][a] = zero;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) qb[a][b] = ql[a][b] = bf16x8{};
   }
+  int buf = 0;  // LDS buffer holding the chunk being scored
 
-  // Online-softmax update with logits z[kt][qt][i] (log2 units); returns P^T as B-operands.
-  auto absorb = [&](f32x4 (&z)[4][4], bf16x8 (&pb)[4][2]) {
+  // Online softmax over one 32-key half (key tiles 2h, 2h+1) of a chunk.  z holds logits in
+  // log2 units.  The reference max is raised only when some column's max exceeds it by more
+  // than kRescale, so most halves skip the O rescale.  pb receives P^T for k-step h.
+  auto absorb = [&](f32x4 (&z)[2][kQt], bf16x8 (&pb)[kQt]) {
+    float mz[kQt];
+    bool raise = false;
 #pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-      float mx = -INFINITY;
+    for (int qi = 0; qi < kQt; ++qi) {
+      const float m0 = max3(z[0][qi][0], z[0][qi][1], z[0][qi][2]);
+      const float m1 = max3(z[0][qi][3], z[1][qi][0], z[1][qi][1]);
+      mz[qi] = colmax4(max3(max3(m0, m1, z[1][qi][2]), z[1][qi][3], -INFINITY));
+      raise |= mz[qi] > mref[qi] + kRescale;
+    }
+    if (__any(raise)) {
 #pragma unroll
-      for (int kti = 0; kti < 4; ++kti)
+      for (int qi = 0; qi < kQt; ++qi) {
+        const float mnew = max2(mref[qi], mz[qi]);
+        const float base = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = fast_exp2(mref[qi] - base);
+        lsum[qi] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[kti][qi][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qi], mx);
-      const float base = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(mrow[qi] - base);
-      lrow[qi] *= alpha;
+        for (int dt = 0; dt < 4; ++dt) o[dt][qi] *= alpha;
+        mref[qi] = base;
+      }
+    }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt][qi] *= alpha;
+    for (int qi = 0; qi < kQt; ++qi) {
       float ps = 0.f;
 #pragma unroll
-      for (int kti = 0; kti < 4; ++kti)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(z[kti][qi][i] - base);
+          const float pv = fast_exp2(z[u][qi][i] - mref[qi]);
           ps += pv;
-          pb[qi][kti >> 1][(kti & 1) * 4 + i] = (__bf16)pv;
+          pb[qi][4 * u + i] = (__bf16)pv;
         }
-      lrow[qi] += ps;
-      mrow[qi] = mnew;
+      lsum[qi] += ps;
     }
   };
-
-  // ---------------------------------------------------------------- diagonal block (own chunk)
-  if (active) {
-    f32x4 z[4][4];
-    const float* Sb = Sm + ((size_t)bh * M + m) * kC * kC;
-    float fb[4][4];
+  auto pv_update = [&](const __bf16* Vn, int ks, const bf16x8 (&pb)[kQt]) {
 #pragma unroll
-    for (int kti = 0; kti < 4; ++kti)
+    for (int dt = 0; dt < 4; ++dt) {
+      const bf16x8 a = vt_frag(Vn, dt, ks);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fb[kti][i] = FOX ? kLog2e * fl[bh * Lp + m * kC + 16 * kti + 4 * g + i] : 0.f;
+      for (int qi = 0; qi < kQt; ++qi) o[dt][qi] = mfma16(a, pb[qi], o[dt][qi]);
+    }
+  };
+  // Scaled logits (log2 units) of key tiles 2h, 2h+1 against the running queries, plus the
+  // PaTH-FoX bias sum_{s=j+1..i} f_s = (chunk-local prefix at i) + off - (prefix at j), whose
+  // row-constant first term cancels in the softmax.
+  auto logits_half = [&](const __bf16* Kn, int h, float offv, f32x4 (&z)[2][kQt]) {
 #pragma unroll
-    for (int qi = 0; qi < 4; ++qi)
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int kti = 0; kti < 4; ++kti) {
-        const float4 s4 = *reinterpret_cast<const float4*>(Sb + (16 * qi + r) * kC + 16 * kti + 4 * g);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      for (int qi = 0; qi < kQt; ++qi) z[u][qi] = zero;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int b = 16 * kti + 4 * g + i, a = 16 * qi + r;
-          z[kti][qi][i] = (b <= a) ? sv[i] * sc - fb[kti][i] : -INFINITY;
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = tile_frag(Kn, 16 * (2 * h + u) + r, 4 * ks + g);
+#pragma unroll
+        for (int qi = 0; qi < kQt; ++qi) {
+          z[u][qi] = mfma16(a, qb[qi][ks], z[u][qi]);
+          if (X3) z[u][qi] = mfma16(a, ql[qi][ks], z[u][qi]);  // logits see the query residual
         }
       }
-    bf16x8 pb[4][2];
-    absorb(z, pb);
-    const __bf16* vtm = vt + ((size_t)bh * M + m) * kD * kC;
+    }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vtm + (16 * dt + r) * kC + 32 * ks + 8 * g);
+      for (int i = 0; i < 4; ++i) {
+        const float bias = FOX ? kLog2e * (offv - lfl[buf][16 * (2 * h + u) + 4 * g + i]) : 0.f;
 #pragma unroll
-        for (int qi = 0; qi < 4; ++qi) o[dt][qi] = mfma16(a, pb[qi][ks], o[dt][qi]);
+        for (int qi = 0; qi < kQt; ++qi) z[u][qi][i] = __builtin_fmaf(z[u][qi][i], sc, bias);
       }
-#pragma unroll
-    for (int qi = 0; qi < 4; ++qi)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        qb[qi][ks] = *reinterpret_cast<const bf16x8*>(qt + ((size_t)bh * Lp + m * kC + 16 * qi + r) * kD + 32 * ks + 8 * g);
-        ql[qi][ks] = bf16x8{};
-      }
-  }
-
-  // ---------------------------------------------------------------- right-to-left scan over key chunks
-  const int64_t nstart = mtop - 1;
-  constexpr int NV = NM * 2;  // 16-byte vectors per thread per staged chunk
-  uint4 stage[NV];
-  float fstage = 0.f;
-  auto load_chunk = [&](int64_t n) {
-    const __bf16* src[4] = {kt + ((size_t)bh * Lp + n * kC) * kD, vt + ((size_t)bh * M + n) * kD * kC,
-                            p_hi + ((size_t)bh * M + n) * kD * kD,
-                            X3 ? p_lo + ((size_t)bh * M + n) * kD * kD : nullptr};
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = tid + 256 * h;
-        stage[mi * 2 + h] = *reinterpret_cast<const uint4*>(src[mi] + (e >> 3) * 64 + (e & 7) * 8);
-      }
-    if (FOX && tid < 64) fstage = fl[bh * Lp + n * kC + tid];
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = tid + 256 * h;
-        *reinterpret_cast<uint4*>(&lds[buf][mi][(e >> 3) * kLDB + (e & 7) * 8]) = stage[mi * 2 + h];
-      }
-    if (FOX && tid < 64) lfl[buf][tid] = fstage;
   };
 
-  if (nstart >= 0) {
-    load_chunk(nstart);
-    store_chunk(0);
-  }
+  // Stage key chunk n into LDS buffer b (each wave moves a quarter of every tile).
+  auto stage = [&](int64_t n, int b) {
+    const int i0 = 2 * wave;
+    dma_tile(lds[b][0], kt + ((size_t)bh * Lp + n * kC) * kD, kD, kC, i0);
+    const int64_t vrows = L - n * kC;
+    dma_tile(lds[b][1], v + ((size_t)bh * L + n * kC) * kD, kD, vrows < kC ? (int)vrows : kC, i0);
+    dma_tile(lds[b][2], p_hi + ((size_t)bh * M + n) * kD * kD, kD, kC, i0);
+    if (X3) dma_tile(lds[b][NM - 1], p_lo + ((size_t)bh * M + n) * kD * kD, kD, kC, i0);
+    if (FOX && wave == 0)
+      __builtin_amdgcn_global_load_lds((const void*)(fl + bh * Lp + n * kC + l), (lds_void*)lfl[b], 4, 0, 0);
+  };
+
+  stage(mtop, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS writes have landed
   __syncthreads();
-  int buf = 0;
   float off = 0.f;
-  for (int64_t n = nstart; n >= 0; --n) {
-    if (n > 0) load_chunk(n - 1);
-    if (active && n < m) {
-      const __bf16* Kn = lds[buf][0];
-      const __bf16* Vn = lds[buf][1];
-      const __bf16* Pn = lds[buf][2];
-      // S^T = ktilde_n Q_run^T
-      f32x4 z[4][4];
+  for (int64_t n = mtop; n >= 0; --n) {
+    if (n > 0) stage(n - 1, buf ^ 1);  // safe: every wave finished reading buf^1 before the last barrier
+    const __bf16* Kn = lds[buf][0];
+    const __bf16* Vn = lds[buf][1];
+    const __bf16* Pn = lds[buf][2];
+    if (active && n == m) {
+      // ---------------------------------------------------------- own chunk: in-chunk logits
+      const float* Sb = Sm + ((size_t)bh * M + m) * kC * kC;
 #pragma unroll
-      for (int kti = 0; kti < 4; ++kti) {
+      for (int h = 0; h < 2; ++h) {
+        f32x4 z[2][kQt];
 #pragma unroll
-        for (int qi = 0; qi < 4; ++qi) z[kti][qi] = zero;
+        for (int qi = 0; qi < kQt; ++qi)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = lds_frag(Kn, 16 * kti + r, 32 * ks + 8 * g);
+          for (int u = 0; u < 2; ++u) {
+            const int kti = 2 * h + u, a = q0 + 16 * qi + r;
+            const float4 s4 = *reinterpret_cast<const float4*>(Sb + a * kC + 16 * kti + 4 * g);
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-          for (int qi = 0; qi < 4; ++qi) z[kti][qi] = mfma16(a, qb[qi][ks], z[kti][qi]);
-        }
+            for (int i = 0; i < 4; ++i) {
+              const int b = 16 * kti + 4 * g + i;
+              const float fb = FOX ? kLog2e * lfl[buf][b] : 0.f;
+              z[u][qi][i] = (b <= a) ? sv[i] * sc - fb : -INFINITY;
+            }
+          }
+        bf16x8 pb[kQt];
+        absorb(z, pb);
+        pv_update(Vn, h, pb);
       }
-      if (FOX) off += ftot[bh * M + n];
 #pragma unroll
-      for (int kti = 0; kti < 4; ++kti)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float bias = FOX ? kLog2e * (off - lfl[buf][16 * kti + 4 * g + i]) : 0.f;
-#pragma unroll
-          for (int qi = 0; qi < 4; ++qi) z[kti][qi][i] = z[kti][qi][i] * sc + bias;
-        }
-      bf16x8 pb[4][2];
-      absorb(z, pb);
-      // O^T += V_n^T P^T
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int qi = 0; qi < kQt; ++qi)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = lds_frag(Vn, 16 * dt + r, 32 * ks + 8 * g);
-#pragma unroll
-          for (int qi = 0; qi < 4; ++qi) o[dt][qi] = mfma16(a, pb[qi][ks], o[dt][qi]);
+          const size_t qo = ((size_t)bh * Lp + m * kC + q0 + 16 * qi + r) * kD + 32 * ks + 8 * g;
+          qb[qi][ks] = *reinterpret_cast<const bf16x8*>(qt + qo);
+          if (X3) ql[qi][ks] = *reinterpret_cast<const bf16x8*>(qt_lo + qo);
         }
-      // Q_run^T <- P_n Q_run^T
-      if (n > 0) {
-        f32x4 qn[4][4];
+    } else if (active && n < m) {
+      // ---------------------------------------------------------- earlier chunk: transported queries
+      // Per 32-key half: logits S^T = ktilde_n Q_run^T, online softmax, O^T += V^T P^T.  The
+      // transport Q_run^T <- P_n Q_run^T for the next chunk is issued after the second half's
+      // logits (the last reader of the current queries), so the matrix cores run it while the
+      // vector units do that half's softmax.
+      if (FOX) off += ftot[bh * M + n];
+      {
+        f32x4 z[2][kQt];
+        logits_half(Kn, 0, off, z);
+        bf16x8 pb[kQt];
+        absorb(z, pb);
+        pv_update(Vn, 0, pb);
+      }
+      {
+        f32x4 z[2][kQt];
+        logits_half(Kn, 1, off, z);
+        if (n > 0) {
+          f32x4 qn[4][kQt];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+          for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-          for (int qi = 0; qi < 4; ++qi) qn[dt][qi] = zero;
+            for (int qi = 0; qi < kQt; ++qi) qn[dt][qi] = zero;
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 a = lds_frag(Pn, 16 * dt + r, 32 * ks + 8 * g);
+            for (int ks = 0; ks < 2; ++ks) {
+              const bf16x8 a = tile_frag(Pn, 16 * dt + r, 4 * ks + g);
 #pragma unroll
-            for (int qi = 0; qi < 4; ++qi) qn[dt][qi] = mfma16(a, qb[qi][ks], qn[dt][qi]);
-            if (X3) {
-              const bf16x8 alo = lds_frag(lds[buf][3], 16 * dt + r, 32 * ks + 8 * g);
+              for (int qi = 0; qi < kQt; ++qi) qn[dt][qi] = mfma16(a, qb[qi][ks], qn[dt][qi]);
+              if (X3) {
+                const bf16x8 alo = tile_frag(lds[buf][NM - 1], 16 * dt + r, 4 * ks + g);
 #pragma unroll
-              for (int qi = 0; qi < 4; ++qi) {
-                qn[dt][qi] = mfma16(a, ql[qi][ks], qn[dt][qi]);
-                qn[dt][qi] = mfma16(alo, qb[qi][ks], qn[dt][qi]);
+                for (int qi = 0; qi < kQt; ++qi) {
+                  qn[dt][qi] = mfma16(a, ql[qi][ks], qn[dt][qi]);
+                  qn[dt][qi] = mfma16(alo, qb[qi][ks], qn[dt][qi]);
+                }
               }
             }
           }
+#pragma unroll
+          for (int qi = 0; qi < kQt; ++qi)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const float vq = qn[2 * ks + (j >> 2)][qi][j & 3];
+                const __bf16 hi = (__bf16)vq;
+                qb[qi][ks][j] = hi;
+                if (X3) ql[qi][ks][j] = (__bf16)(vq - (float)hi);
+              }
         }
-#pragma unroll
-        for (int qi = 0; qi < 4; ++qi)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float vq = qn[2 * ks + (j >> 2)][qi][j & 3];
-              const __bf16 hi = (__bf16)vq;
-              qb[qi][ks][j] = hi;
-              if (X3) ql[qi][ks][j] = (__bf16)(vq - (float)hi);
-            }
+        bf16x8 pb[kQt];
+        absorb(z, pb);
+        pv_update(Vn, 1, pb);
       }
     }
-    if (n > 0) store_chunk(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's LDS writes from this wave have landed
     __syncthreads();
     buf ^= 1;
   }
 
   // ---------------------------------------------------------------- epilogue
 #pragma unroll
-  for (int qi = 0; qi < 4; ++qi) {
-    float lt = lrow[qi];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const int a = 16 * qi + r;
+  for (int qi = 0; qi < kQt; ++qi) {
+    const float lt = colsum4(lsum[qi]);
+    const int a = q0 + 16 * qi + r;
     const int64_t i = m * kC + a;
     if (active && i < L) {
       const float inv = 1.f / lt;
@@ -545,7 +670,7 @@ __global__ __launch_bounds__(256, X3 ? 1 : 2) void mfma_attn_kernel(
         *reinterpret_cast<bf16x4*>(out + ((size_t)bh * L + i) * kD + 16 * dt + 4 * g) =
             pack4(o[dt][qi][0] * inv, o[dt][qi][1] * inv, o[dt][qi][2] * inv, o[dt][qi][3] * inv);
       if (lse != nullptr && g == 0)
-        lse[bh * L + i] = (mrow[qi] + fast_log2(lt)) * kLn2 + (FOX ? fl[bh * Lp + i] : 0.f);
+        lse[bh * L + i] = (mref[qi] + fast_log2(lt)) * kLn2 + (FOX ? fl[bh * Lp + i] : 0.f);
     }
   }
 }
@@ -554,39 +679,48 @@ __global__ __launch_bounds__(256, X3 ? 1 : 2) void mfma_attn_kernel(
 bool mfma_supported(int d, int chunk) { return d == kD && chunk == kC; }
 
 template <bool FOX, bool X3>
-static void launch_attn(dim3 grid, hipStream_t st, const __bf16* qt, const __bf16* kt, const __bf16* vt,
-                        const __bf16* p_hi, const __bf16* p_lo, const float* Sm, const float* fl, const float* ftot,
-                        __bf16* out, float* lse, int64_t L, int64_t M, float sc) {
-  mfma_attn_kernel<FOX, X3><<<grid, 256, 0, st>>>(qt, kt, vt, p_hi, p_lo, Sm, fl, ftot, out, lse, L, M, sc);
+static void launch_attn(dim3 grid, hipStream_t st, const __bf16* qt, const __bf16* qt_lo, const __bf16* kt,
+                        const __bf16* v, const __bf16* p_hi, const __bf16* p_lo, const float* Sm, const float* fl,
+                        const float* ftot, __bf16* out, float* lse, int64_t L, int64_t M, int64_t BH, float sc) {
+  mfma_attn_kernel<FOX, X3><<<grid, 256, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, Sm, fl, ftot, out, lse, L, M, BH,
+                                                  sc);
 }
 
-hipError_t mfma_fwd(int chunk, int transport, const void* q, const void* k, const void* v, const void* w,
-                    const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
-                    float scale, void* qt, void* kt, void* vt, void* p_hi, void* p_lo, float* Sm, float* fl,
-                    float* ftot, hipStream_t st) {
+// phases: bit 0 = per-chunk prep, bit 1 = attention scan (reads what the prep left in the workspace).
+hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const void* k, const void* v,
+                    const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH,
+                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo,
+                    float* Sm, float* fl, float* ftot, hipStream_t st) {
   if (chunk != kC) return hipErrorInvalidValue;
   const int64_t M = (L + kC - 1) / kC;
-  hipError_t e = hipFuncSetAttribute((const void*)mfma_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kPrepLds);
-  if (e != hipSuccess) return e;
   const bool x3 = transport == 1;
-  mfma_prep_kernel<<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
-      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)w, beta, logf, L, M, (__bf16*)qt,
-      (__bf16*)kt, (__bf16*)vt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((M + 3) / 4), (unsigned)BH);
-  const float sc = scale * kLog2e;
-  const bool fox = logf != nullptr;
-  auto args = [&](auto fn) {
-    fn(grid, st, (const __bf16*)qt, (const __bf16*)kt, (const __bf16*)vt, (const __bf16*)p_hi,
-       (const __bf16*)p_lo, Sm, fl, ftot, (__bf16*)out, lse, L, M, sc);
-  };
-  if (fox && x3) args(launch_attn<true, true>);
-  else if (fox) args(launch_attn<true, false>);
-  else if (x3) args(launch_attn<false, true>);
-  else args(launch_attn<false, false>);
-  return hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (phases & 1) {
+    e = hipFuncSetAttribute((const void*)mfma_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kPrepLds);
+    if (e != hipSuccess) return e;
+    mfma_prep_kernel<<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
+        (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, (__bf16*)qt,
+        x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 2) {
+    const int64_t heads_per_xcd = (BH + kXcd - 1) / kXcd;
+    const dim3 grid((unsigned)(kXcd * heads_per_xcd * ((M + kCpb - 1) / kCpb)));
+    const float sc = scale * kLog2e;
+    const bool fox = logf != nullptr;
+    auto args = [&](auto fn) {
+      fn(grid, st, (const __bf16*)qt, (const __bf16*)qt_lo, (const __bf16*)kt, (const __bf16*)v,
+         (const __bf16*)p_hi, (const __bf16*)p_lo, Sm, fl, ftot, (__bf16*)out, lse, L, M, BH, sc);
+    };
+    if (fox && x3) args(launch_attn<true, true>);
+    else if (fox) args(launch_attn<true, false>);
+    else if (x3) args(launch_attn<false, true>);
+    else args(launch_attn<false, false>);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace pathattn

@@ -250,38 +250,46 @@ __global__ __launch_bounds__(C) void vec_attn_kernel(const float* __restrict__ q
 }
 
 // ------------------------------------------------------------------------------------ launch
+// phases: bit 0 = per-chunk prep, bit 1 = attention scan (reads what the prep left in the workspace).
 template <typename T, int D, int C>
-static hipError_t launch_vec(const void* q, const void* k, const void* v, const void* w, const float* beta,
-                             const float* logf, void* out, float* lse, int64_t BH, int64_t L, float scale,
-                             float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st) {
+static hipError_t launch_vec(int phases, const void* q, const void* k, const void* v, const void* w,
+                             const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
+                             float scale, float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot,
+                             hipStream_t st) {
   const int64_t M = (L + C - 1) / C;
   constexpr int CP = C + 1;
   constexpr int ZS = (C * CP > C * D) ? C * CP : C * D;
   constexpr size_t lds = sizeof(float) * (3 * C * D + C + ZS + 4 * C * CP);
   static_assert(lds <= 160 * 1024, "vector prep exceeds LDS");
-  hipError_t e = hipFuncSetAttribute((const void*)vec_prep_kernel<T, D, C>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   dim3 grid((unsigned)M, (unsigned)BH);
-  vec_prep_kernel<T, D, C><<<grid, 256, lds, st>>>((const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, qt,
-                                                  kt, Pm, Sm, fl, ftot);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  vec_attn_kernel<T, D, C><<<grid, C, 0, st>>>(qt, kt, (const T*)v, Pm, Sm, logf ? fl : nullptr, ftot, (T*)out,
-                                               lse, L, M, scale);
-  return hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (phases & 1) {
+    e = hipFuncSetAttribute((const void*)vec_prep_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+    if (e != hipSuccess) return e;
+    vec_prep_kernel<T, D, C><<<grid, 256, lds, st>>>((const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, qt,
+                                                    kt, Pm, Sm, fl, ftot);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 2) {
+    vec_attn_kernel<T, D, C><<<grid, C, 0, st>>>(qt, kt, (const T*)v, Pm, Sm, logf ? fl : nullptr, ftot, (T*)out,
+                                                 lse, L, M, scale);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
-#define PATHATTN_VEC_CASE(TT, DD, CC)                                                                       \
-  if (d == DD && chunk == CC)                                                                               \
-    return launch_vec<TT, DD, CC>(q, k, v, w, beta, logf, out, lse, BH, L, scale, qt, kt, Pm, Sm, fl, ftot, \
+#define PATHATTN_VEC_CASE(TT, DD, CC)                                                                              \
+  if (d == DD && chunk == CC)                                                                                      \
+    return launch_vec<TT, DD, CC>(phases, q, k, v, w, beta, logf, out, lse, BH, L, scale, qt, kt, Pm, Sm, fl, ftot, \
                                   st);
 
 template <typename T>
-static hipError_t dispatch_vec(int d, int chunk, const void* q, const void* k, const void* v, const void* w,
-                               const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
-                               float scale, float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot,
-                               hipStream_t st) {
+static hipError_t dispatch_vec(int phases, int d, int chunk, const void* q, const void* k, const void* v,
+                               const void* w, const float* beta, const float* logf, void* out, float* lse,
+                               int64_t BH, int64_t L, float scale, float* qt, float* kt, float* Pm, float* Sm,
+                               float* fl, float* ftot, hipStream_t st) {
   PATHATTN_VEC_CASE(T, 16, 16)
   PATHATTN_VEC_CASE(T, 16, 32)
   PATHATTN_VEC_CASE(T, 16, 64)
@@ -293,19 +301,20 @@ static hipError_t dispatch_vec(int d, int chunk, const void* q, const void* k, c
   PATHATTN_VEC_CASE(T, 64, 64)
   return hipErrorInvalidValue;
 }
+#undef PATHATTN_VEC_CASE
 
 bool vec_supported(int d, int chunk) {
   return (d == 16 || d == 32 || d == 64) && (chunk == 16 || chunk == 32 || chunk == 64);
 }
 
-hipError_t vec_fwd(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
-                   const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L, float scale,
-                   float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st) {
+hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
+                   const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
+                   float scale, float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st) {
   if (bf16)
-    return dispatch_vec<__bf16>(d, chunk, q, k, v, w, beta, logf, out, lse, BH, L, scale, qt, kt, Pm, Sm, fl,
+    return dispatch_vec<__bf16>(phases, d, chunk, q, k, v, w, beta, logf, out, lse, BH, L, scale, qt, kt, Pm, Sm, fl,
                                 ftot, st);
-  return dispatch_vec<float>(d, chunk, q, k, v, w, beta, logf, out, lse, BH, L, scale, qt, kt, Pm, Sm, fl, ftot,
-                             st);
+  return dispatch_vec<float>(phases, d, chunk, q, k, v, w, beta, logf, out, lse, BH, L, scale, qt, kt, Pm, Sm, fl,
+                             ftot, st);
 }
 
 }  // namespace pathattn

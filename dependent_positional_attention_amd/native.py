@@ -16,7 +16,8 @@ from typing import Optional, Tuple
 import torch  # imported first so the HIP runtime torch ships is the one in the process
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpathattn.so")
+# PATHATTN_LIB points the binding at another build of the same library (A/B comparisons).
+LIB_PATH = os.environ.get("PATHATTN_LIB") or os.path.join(_HERE, "libpathattn.so")
 
 PATH_OK, PATH_ERR_INVALID_ARG, PATH_ERR_UNSUPPORTED, PATH_ERR_HIP = 0, 1, 2, 3
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
@@ -34,13 +35,14 @@ class PathAttnError(RuntimeError):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [("layout_id", ctypes.c_int), ("num_chunks", ctypes.c_int64), ("off_qtilde", ctypes.c_int64),
-                ("off_ktilde", ctypes.c_int64), ("off_vt", ctypes.c_int64), ("off_p", ctypes.c_int64),
+                ("off_qtilde_lo", ctypes.c_int64), ("off_ktilde", ctypes.c_int64), ("off_p", ctypes.c_int64),
                 ("off_p_lo", ctypes.c_int64), ("off_s", ctypes.c_int64), ("off_fox_local", ctypes.c_int64),
                 ("off_fox_total", ctypes.c_int64), ("total_bytes", ctypes.c_int64)]
 
 
 EXPORTS = ("path_abi_version", "path_status_string", "path_attn_fwd_workspace_bytes", "path_attn_fwd",
-           "path_attn_workspace_layout", "path_decode_workspace_bytes", "path_decode_step")
+           "path_attn_prep", "path_attn_scan", "path_attn_workspace_layout", "path_decode_workspace_bytes",
+           "path_decode_step")
 
 
 def lib():
@@ -58,11 +60,13 @@ def lib():
         L.path_attn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(WsLayout)]
         L.path_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32, vp, sz,
                                     vp]
+        L.path_attn_prep.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, sz, vp]
+        L.path_attn_scan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32, vp, sz, vp]
         L.path_decode_workspace_bytes.argtypes = [i64, i64, i32, i64, i32, ctypes.POINTER(sz)]
         L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, f32, i32, i32,
                                        vp, sz, vp]
-        for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd",
-                  "path_decode_workspace_bytes", "path_decode_step"):
+        for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd", "path_attn_prep",
+                  "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -142,6 +146,42 @@ def path_attn_fwd(q, k, v, w, beta, log_forget=None, *, scale: Optional[float] =
     _check("path_attn_fwd", lib().path_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(out), _ptr(lse), B, H, L, d, chunk,
         float(scale), DTYPE[q.dtype], TRANSPORT[transport], _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def path_attn_prep(q, k, v, w, beta, log_forget=None, *, chunk: int = 64, transport: str = "bf16", workspace,
+                   stream=None) -> torch.Tensor:
+    """Per-chunk terms only (first phase of path_attn_fwd), written into `workspace`."""
+    _require(q, "q")
+    B, H, L, d = q.shape
+    for name, t in (("k", k), ("v", v), ("w", w)):
+        _require(t, name, q.dtype, q.shape)
+    _require(beta, "beta", torch.float32, (B, H, L))
+    if log_forget is not None:
+        _require(log_forget, "log_forget", torch.float32, (B, H, L))
+    _require(workspace, "workspace")
+    _check("path_attn_prep", lib().path_attn_prep(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), B, H, L, d, chunk, DTYPE[q.dtype],
+        TRANSPORT[transport], _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return workspace
+
+
+def path_attn_scan(v, log_forget=None, *, scale: Optional[float] = None, chunk: int = 64, transport: str = "bf16",
+                   workspace, out=None, lse=None, stream=None,
+                   want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention scan from a workspace filled by path_attn_prep with the same arguments."""
+    _require(v, "v")
+    B, H, L, d = v.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(v)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), device=v.device, dtype=torch.float32)
+    _require(workspace, "workspace")
+    _check("path_attn_scan", lib().path_attn_scan(
+        _ptr(v), _ptr(log_forget), _ptr(out), _ptr(lse), B, H, L, d, chunk, float(scale), DTYPE[v.dtype],
+        TRANSPORT[transport], _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

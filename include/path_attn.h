@@ -53,8 +53,9 @@ typedef enum { PATH_DTYPE_F32 = 0, PATH_DTYPE_BF16 = 1 } path_dtype;
  * Precision of the running-query transport between chunks (bf16 path only):
  * PATH_TRANSPORT_BF16 rounds the running query and the chunk product to bf16
  * for each matrix-core product; PATH_TRANSPORT_BF16X3 splits both into
- * hi + lo bf16 parts and sums hi*hi + hi*lo + lo*hi, which keeps long scans
- * (tens of thousands of tokens with beta near 2) within bf16-input tolerance.
+ * hi + lo bf16 parts and sums hi*hi + hi*lo + lo*hi, and also scores keys
+ * against the hi + lo query, which keeps long scans (tens of thousands of
+ * tokens with beta near 2) and large logits within bf16-input tolerance.
  * The fp32 path always transports in fp32.
  */
 typedef enum { PATH_TRANSPORT_BF16 = 0, PATH_TRANSPORT_BF16X3 = 1 } path_transport;
@@ -101,6 +102,25 @@ path_status path_attn_fwd(const void* q, const void* k, const void* v, const voi
                           size_t workspace_bytes, void* stream);
 
 /*
+ * The two phases of path_attn_fwd, for callers that time or reuse them
+ * separately.  path_attn_prep computes every chunk's compact-form terms into
+ * the workspace (reads q, k, v, w, beta, log_forget; writes only the
+ * workspace).  path_attn_scan runs the right-to-left attention scan from a
+ * workspace that path_attn_prep filled with the SAME B, H, L, d, chunk, dtype,
+ * transport and the same log_forget presence (non-NULL vs NULL); it reads v
+ * and writes out and lse.  log_forget is only tested for NULL by
+ * path_attn_scan, which reads v in both paths.  path_attn_fwd == prep followed
+ * by scan on the same stream.
+ */
+path_status path_attn_prep(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                           const float* log_forget, int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                           int transport, void* workspace, size_t workspace_bytes, void* stream);
+
+path_status path_attn_scan(const void* v, const float* log_forget, void* out, float* lse, int64_t B, int64_t H,
+                           int64_t L, int d, int chunk, float scale, int dtype, int transport, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * Where path_attn_fwd leaves its per-chunk terms inside the workspace (byte
  * offsets, -1 when a term is not materialised by the selected kernels).  Used
  * to inspect intermediate results; the layout of each term is stated in
@@ -110,14 +130,14 @@ path_status path_attn_fwd(const void* q, const void* k, const void* v, const voi
  *     unscaled, lower triangle incl. diagonal).
  *   layout_id 1 (matrix-core path): qtilde, ktilde [B*H, M*C, d] bf16 with columns permuted
  *     within each 32-wide block (stored slot 8g+j holds column 16(j/4)+4g+(j%4));
- *     vt [B*H, M, d, C] bf16 (value chunk transposed, key index permuted the same way);
+ *     qtilde_lo (bf16x3 transport only): the bf16 residual qtilde - qtilde_hi, same layout;
  *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S as layout 0.
  * M = ceil(L / chunk).
  */
 typedef struct {
   int layout_id;
   int64_t num_chunks;
-  int64_t off_qtilde, off_ktilde, off_vt, off_p, off_p_lo, off_s, off_fox_local, off_fox_total;
+  int64_t off_qtilde, off_qtilde_lo, off_ktilde, off_p, off_p_lo, off_s, off_fox_local, off_fox_total;
   int64_t total_bytes;
 } path_ws_layout;
 

@@ -64,7 +64,7 @@ def test_workspace_planning(L):
     assert ws_bytes(L, 1, 1, 64, 16, 16, F32, 5)[0] == INVALID  # transport
     lay = native.WsLayout()
     assert L.path_attn_workspace_layout(2, 3, 100, 16, 16, F32, 0, ctypes.byref(lay)) == OK
-    assert lay.num_chunks == 7 and lay.layout_id == 0 and lay.off_vt == -1
+    assert lay.num_chunks == 7 and lay.layout_id == 0 and lay.off_p_lo == -1 and lay.off_qtilde_lo == -1
     offs = [lay.off_qtilde, lay.off_ktilde, lay.off_p, lay.off_s, lay.off_fox_local, lay.off_fox_total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and lay.total_bytes >= offs[-1]
 
