@@ -41,28 +41,11 @@ namespace pathattn {
 
 namespace {
 
-constexpr int kD = 64;      // head dim
-constexpr int kC = 64;      // chunk
-constexpr int kLDB = 72;    // bf16 LDS row stride (144 B: conflict-free 16-byte row reads)
-constexpr int kLDF = 68;    // fp32 LDS row stride
-constexpr int kMat = kC * kLDB;  // elements of one padded 64x64 bf16 LDS matrix
+constexpr int kD = 64;  // head dim
+constexpr int kC = 64;  // chunk
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 lds_frag(const __bf16* m, int row, int col) {
-  return *reinterpret_cast<const bf16x8*>(m + row * kLDB + col);
-}
-
-// acc += X[m0..m0+15][0..63] . Y[n0..n0+15][0..63]^T; lane (r = l%16, g = l/16) receives
-// acc[i] = D[m0 + 4g + i][n0 + r].
-__device__ __forceinline__ f32x4 mm_tile(const __bf16* X, const __bf16* Y, int m0, int n0, f32x4 acc) {
-  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    acc = mfma16(lds_frag(X, m0 + r, ks * 32 + g * 8), lds_frag(Y, n0 + r, ks * 32 + g * 8), acc);
-  return acc;
 }
 
 // Stored slot of original column c (0..63) under the in-block permutation.
@@ -80,11 +63,6 @@ __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
   return v;
 }
 
-__device__ __forceinline__ void split_hi_lo(float v, __bf16& hi, __bf16& lo) {
-  hi = (__bf16)v;
-  lo = (__bf16)(v - (float)hi);
-}
-
 // Four values -> hi and lo bf16 quads with v ~= hi + lo.
 __device__ __forceinline__ void split4(float v0, float v1, float v2, float v3, bf16x4& h, bf16x4& l) {
   const float v[4] = {v0, v1, v2, v3};
@@ -98,251 +76,7 @@ __device__ __forceinline__ void split4(float v0, float v1, float v2, float v3, b
 
 }  // namespace
 
-// =========================================================================== kernel 1: prep
-// LDS plan (bytes): 13 padded bf16 64x64 matrices + beta + an fp32 region for A, Z = A^{-1}
-// and block temporaries.  Regions are reused once their contents are dead:
-//   R1 (4 mats): W, Q, K in phases A-B; X^T hi/lo and Y hi/lo in phases E-F
-//   R2 (1 mat):  W^T throughout
-//   R3 (4 mats): U^T hi/lo, R hi/lo
-//   R4 (4 mats): T^{-1} hi/lo, T^{-T} hi/lo
-//   R5 (fp32):   A, Z, temporaries in phases B-D; (T^{-1}W)^T hi/lo in phases E-F
-constexpr size_t kPrepLds = 13 * kMat * 2 + 64 * 4 + 2 * kC * kLDF * 4 + 3 * 256 * 4;
-static_assert(kPrepLds <= 160 * 1024, "prep LDS plan exceeds 160 KiB");
-
-__global__ __launch_bounds__(256) void mfma_prep_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
-    const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, __bf16* __restrict__ qt,
-    __bf16* __restrict__ qt_lo, __bf16* __restrict__ kt, __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo,
-    float* __restrict__ Sm, float* __restrict__ fl, float* __restrict__ ftot) {
-  extern __shared__ __align__(16) char smem[];
-  __bf16* R1 = reinterpret_cast<__bf16*>(smem);
-  __bf16* Ws = R1;                 // W [s][x]
-  __bf16* Qs = R1 + kMat;          // Q [a][x]
-  __bf16* Ks = R1 + 2 * kMat;      // K [b][x]
-  __bf16* XTH = R1;                // X^T [a][s] hi / lo   (after phase B)
-  __bf16* XTL = R1 + kMat;
-  __bf16* YH = R1 + 2 * kMat;      // Y [b][t] hi / lo     (after phase B)
-  __bf16* YL = R1 + 3 * kMat;
-  __bf16* WTs = R1 + 4 * kMat;     // W^T [x][s]
-  __bf16* UTH = R1 + 5 * kMat;     // U^T [a][t] hi / lo
-  __bf16* UTL = R1 + 6 * kMat;
-  __bf16* RH = R1 + 7 * kMat;      // R [b][s] hi / lo
-  __bf16* RL = R1 + 8 * kMat;
-  __bf16* TiH = R1 + 9 * kMat;     // T^{-1} [s][t] hi / lo
-  __bf16* TiL = R1 + 10 * kMat;
-  __bf16* TiTH = R1 + 11 * kMat;   // T^{-T} [t][s] hi / lo
-  __bf16* TiTL = R1 + 12 * kMat;
-  float* Bs = reinterpret_cast<float*>(R1 + 13 * kMat);  // beta [64]
-  float* Af = Bs + 64;                                   // A [64][kLDF]
-  float* Zf = Af + kC * kLDF;                            // Z = A^{-1} [64][kLDF]
-  float* Tmp = Zf + kC * kLDF;                           // 3 x 16 x 16 block temporaries
-  __bf16* Z2H = reinterpret_cast<__bf16*>(Af);           // (T^{-1} W)^T [y][s] hi / lo (after phase D)
-  __bf16* Z2L = Z2H + kMat;
-
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-  const int c = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int64_t Lp = M * kC;
-  const int64_t row0 = (int64_t)c * kC;
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-
-  // ---------------------------------------------------------------- A: stage W, W^T, Q, K, beta
-  for (int e = tid; e < 512; e += 256) {
-    const int a = e >> 3, c8 = (e & 7) * 8;
-    const int64_t i = row0 + a;
-    const bool ok = i < L;
-    const size_t go = ((size_t)bh * L + (ok ? i : 0)) * kD + c8;
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-    const uint4 wv = ok ? *reinterpret_cast<const uint4*>(w + go) : z4;
-    *reinterpret_cast<uint4*>(Ws + a * kLDB + c8) = wv;
-    *reinterpret_cast<uint4*>(Qs + a * kLDB + c8) = ok ? *reinterpret_cast<const uint4*>(q + go) : z4;
-    *reinterpret_cast<uint4*>(Ks + a * kLDB + c8) = ok ? *reinterpret_cast<const uint4*>(k + go) : z4;
-    const bf16x8 wb = __builtin_bit_cast(bf16x8, wv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) WTs[(c8 + j) * kLDB + a] = wb[j];
-  }
-  if (tid < 64) {
-    const int64_t i = row0 + tid;
-    Bs[tid] = i < L ? beta[bh * L + i] : 0.f;  // padded tokens: identity transitions
-  }
-  for (int e = tid; e < kC * kLDF; e += 256) Zf[e] = 0.f;
-  if (logf != nullptr && wave == 0) {  // chunk-local inclusive prefix sum of the log-forget gates
-    const int64_t i = row0 + l;
-    float f = i < L ? logf[bh * L + i] : 0.f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(f, o, 64);
-      if (l >= o) f += y;
-    }
-    fl[bh * Lp + i] = f;
-    if (l == 63) ftot[bh * M + c] = f;
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- B: A, U^T, R, K Q^T
-  f32x4 kq[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    // A[s][t] = beta_s (w_s . w_t) for s < t  (rows s in block `wave`)
-    const f32x4 ga = mm_tile(Ws, Ws, 16 * wave, 16 * nb, zero);
-    // D[t][a] = w_t . q_a  ->  U^T[a][t], t <= a
-    const f32x4 ua = mm_tile(Ws, Qs, 16 * wave, 16 * nb, zero);
-    // D[s][b] = w_s . k_b  ->  R[b][s], s > b
-    const f32x4 ra = mm_tile(Ws, Ks, 16 * wave, 16 * nb, zero);
-    const int col = 16 * nb + r;
-    float um[4], rm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * wave + 4 * g + i;
-      Af[row * kLDF + col] = (row < col) ? Bs[row] * ga[i] : 0.f;
-      um[i] = (row <= col) ? ua[i] : 0.f;
-      rm[i] = (row > col) ? ra[i] : 0.f;
-    }
-    bf16x4 uh, ul, rh, rl;
-    split4(um[0], um[1], um[2], um[3], uh, ul);
-    split4(rm[0], rm[1], rm[2], rm[3], rh, rl);
-    *reinterpret_cast<bf16x4*>(UTH + col * kLDB + 16 * wave + 4 * g) = uh;
-    *reinterpret_cast<bf16x4*>(UTL + col * kLDB + 16 * wave + 4 * g) = ul;
-    *reinterpret_cast<bf16x4*>(RH + col * kLDB + 16 * wave + 4 * g) = rh;
-    *reinterpret_cast<bf16x4*>(RL + col * kLDB + 16 * wave + 4 * g) = rl;
-    // D[b][a] = k_b . q_a for queries a in block `wave`
-    kq[nb] = mm_tile(Ks, Qs, 16 * nb, 16 * wave, zero);
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- C: diagonal 16x16 blocks of Z = A^{-1}
-  if (l < 16) {
-    const int base = 16 * wave;
-    float z[16];
-#pragma unroll
-    for (int ii = 15; ii >= 0; --ii) {
-      float s = 0.f;
-#pragma unroll
-      for (int kk = ii + 1; kk < 16; ++kk) s += Af[(base + ii) * kLDF + base + kk] * z[kk];
-      z[ii] = (ii == l) ? 1.f : (ii < l ? -s : 0.f);
-    }
-#pragma unroll
-    for (int ii = 0; ii < 16; ++ii) Zf[(base + ii) * kLDF + base + l] = z[ii];
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- D: off-diagonal blocks, by distance
-  // Z_IJ = -Z_II sum_{K=I+1..J} A_IK Z_KJ
-  for (int lv = 1; lv < 4; ++lv) {
-    const int nblk = 4 - lv;
-    for (int e = tid; e < nblk * 256; e += 256) {
-      const int I = e >> 8, ii = (e >> 4) & 15, jj = e & 15, J = I + lv;
-      float s = 0.f;
-      for (int K = I + 1; K <= J; ++K)
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) s += Af[(16 * I + ii) * kLDF + 16 * K + kk] * Zf[(16 * K + kk) * kLDF + 16 * J + jj];
-      Tmp[e] = s;
-    }
-    __syncthreads();
-    for (int e = tid; e < nblk * 256; e += 256) {
-      const int I = e >> 8, ii = (e >> 4) & 15, jj = e & 15, J = I + lv;
-      float s = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) s += Zf[(16 * I + ii) * kLDF + 16 * I + kk] * Tmp[(I << 8) + (kk << 4) + jj];
-      Zf[(16 * I + ii) * kLDF + 16 * J + jj] = -s;
-    }
-    __syncthreads();
-  }
-
-  // T^{-1} = Z diag(beta) as hi/lo bf16, row-major and transposed
-  for (int e = tid; e < kC * kC; e += 256) {
-    const int s = e >> 6, t = e & 63;
-    __bf16 hi, lo;
-    split_hi_lo(Zf[s * kLDF + t] * Bs[t], hi, lo);
-    TiH[s * kLDB + t] = hi;
-    TiL[s * kLDB + t] = lo;
-    TiTH[t * kLDB + s] = hi;
-    TiTL[t * kLDB + s] = lo;
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- E: X^T, Y, (T^{-1}W)^T, each hi/lo
-  // (hi+lo)(hi+lo) products drop the lo*lo term.
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int col = 16 * nb + r, m0 = 16 * wave, n0 = 16 * nb;
-    bf16x4 h4, l4;
-    // D[s][a] = X[s][a]  ->  X^T[a][s]
-    f32x4 xa = mm_tile(TiH, UTH, m0, n0, zero);
-    xa = mm_tile(TiH, UTL, m0, n0, xa);
-    xa = mm_tile(TiL, UTH, m0, n0, xa);
-    split4(xa[0], xa[1], xa[2], xa[3], h4, l4);
-    *reinterpret_cast<bf16x4*>(XTH + col * kLDB + m0 + 4 * g) = h4;
-    *reinterpret_cast<bf16x4*>(XTL + col * kLDB + m0 + 4 * g) = l4;
-    // D[t][b] = Y[b][t]  ->  Y[b][t]
-    f32x4 ya = mm_tile(TiTH, RH, m0, n0, zero);
-    ya = mm_tile(TiTH, RL, m0, n0, ya);
-    ya = mm_tile(TiTL, RH, m0, n0, ya);
-    split4(ya[0], ya[1], ya[2], ya[3], h4, l4);
-    *reinterpret_cast<bf16x4*>(YH + col * kLDB + m0 + 4 * g) = h4;
-    *reinterpret_cast<bf16x4*>(YL + col * kLDB + m0 + 4 * g) = l4;
-    // D[s][y] = (T^{-1} W)[s][y]  ->  Z2^T[y][s]
-    f32x4 za = mm_tile(TiH, WTs, m0, n0, zero);
-    za = mm_tile(TiL, WTs, m0, n0, za);
-    split4(za[0], za[1], za[2], za[3], h4, l4);
-    *reinterpret_cast<bf16x4*>(Z2H + col * kLDB + m0 + 4 * g) = h4;
-    *reinterpret_cast<bf16x4*>(Z2L + col * kLDB + m0 + 4 * g) = l4;
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- F: outputs
-  const size_t chunk_rows = (size_t)bh * Lp + row0;
-  const size_t chunk_mat = ((size_t)bh * M + c) * kD * kD;
-  const int a = 16 * wave + r;  // query / key / P-row handled by this lane
-  const int64_t ia = row0 + a;
-  const bool aok = ia < L;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int x0 = 16 * mb + 4 * g;  // first of this lane's four consecutive columns
-    const int pos = perm_pos(x0);
-    const size_t gin = ((size_t)bh * L + (aok ? ia : 0)) * kD + x0;
-    // qtilde[a][x] = q_a[x] - sum_s X[s][a] w_s[x]
-    {
-      f32x4 d4 = mm_tile(WTs, XTH, 16 * mb, 16 * wave, zero);
-      d4 = mm_tile(WTs, XTL, 16 * mb, 16 * wave, d4);
-      bf16x4 q4 = {};
-      if (aok) q4 = *reinterpret_cast<const bf16x4*>(q + gin);
-      bf16x4 h4, l4;
-      split4((float)q4[0] - d4[0], (float)q4[1] - d4[1], (float)q4[2] - d4[2], (float)q4[3] - d4[3], h4, l4);
-      *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
-      if (qt_lo != nullptr) *reinterpret_cast<bf16x4*>(qt_lo + (chunk_rows + a) * kD + pos) = l4;
-    }
-    // ktilde[b][x] = k_b[x] - sum_t Y[b][t] w_t[x]
-    {
-      f32x4 d4 = mm_tile(WTs, YH, 16 * mb, 16 * wave, zero);
-      d4 = mm_tile(WTs, YL, 16 * mb, 16 * wave, d4);
-      bf16x4 k4 = {};
-      if (aok) k4 = *reinterpret_cast<const bf16x4*>(k + gin);
-      *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) =
-          pack4((float)k4[0] - d4[0], (float)k4[1] - d4[1], (float)k4[2] - d4[2], (float)k4[3] - d4[3]);
-    }
-    // P[x][y] = delta - sum_s w_s[x] Z2[s][y]   (lane: row x = a, columns y = x0..x0+3)
-    {
-      f32x4 d4 = mm_tile(Z2H, WTs, 16 * mb, 16 * wave, zero);
-      d4 = mm_tile(Z2L, WTs, 16 * mb, 16 * wave, d4);
-      bf16x4 ph, pl;
-      split4((x0 == a ? 1.f : 0.f) - d4[0], (x0 + 1 == a ? 1.f : 0.f) - d4[1], (x0 + 2 == a ? 1.f : 0.f) - d4[2],
-             (x0 + 3 == a ? 1.f : 0.f) - d4[3], ph, pl);
-      *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)a * kD + pos) = ph;
-      if (p_lo != nullptr) *reinterpret_cast<bf16x4*>(p_lo + chunk_mat + (size_t)a * kD + pos) = pl;
-    }
-    // S[a][b] = q_a.k_b - (Y U)[b][a]   (lane: query a, keys b = x0..x0+3)
-    {
-      f32x4 d4 = mm_tile(YH, UTH, 16 * mb, 16 * wave, zero);
-      d4 = mm_tile(YH, UTL, 16 * mb, 16 * wave, d4);
-      d4 = mm_tile(YL, UTH, 16 * mb, 16 * wave, d4);
-      const float4 s4 = make_float4(kq[mb][0] - d4[0], kq[mb][1] - d4[1], kq[mb][2] - d4[2], kq[mb][3] - d4[3]);
-      *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kC + a) * kC + x0) = s4;
-    }
-  }
-}
-
-// =========================================================================== kernel 2: attention
+// =========================================================================== swizzled LDS tiles
 // LDS tiles of the key-chunk stream are 64 rows x 128 B with no padding; the 16-byte chunk c of
 // row r sits at slot c ^ (r & 7) (an XOR swizzle), so the 16 rows an MFMA fragment read touches
 // land in distinct banks.  Tiles are filled by direct global->LDS loads (16 B per lane, lane i
@@ -373,14 +107,17 @@ __device__ __forceinline__ bf16x8 tile_frag(const __bf16* tile, int row, int chu
   return *reinterpret_cast<const bf16x8*>(tile + swz(row, chunk));
 }
 
-// V^T A-fragment from a row-major V tile ([key][d]) with two LDS transpose reads: lane (r, g) of
-// d-tile dt, k-step ks receives V[key][16dt + r] for keys 32ks + 16h + 4g + (0..3), h = 0, 1
-// (the same key order as the P^T B-operand).  Within a 16-lane group the transpose read gives
-// lane d element (d & 3) of source lanes (d >> 2) + 4j; source lane s therefore points at
-// row base + (s >> 2), columns 16dt + 4(s & 3) .. +3.
-__device__ __forceinline__ bf16x8 vt_frag(const __bf16* tile, int dt, int ks) {
+// Transposed fragment: operand row/column index c0 + (l % 16) runs over the tile's COLUMNS and
+// the k index over its ROWS, in the key order an accumulator-derived operand uses: lane (r, g)
+// of k-step ks receives tile[row][c0 + r] for rows 32ks + 16h + 4g + (0..3), h = 0, 1.  Two LDS
+// transpose reads: within a 16-lane group the transpose read gives lane d element (d & 3) of
+// source lanes (d >> 2) + 4j, so source lane s points at row base + (s >> 2), columns
+// c0 + 4(s & 3) .. +3.  `pcol` maps a logical column to its stored slot (identity, or the
+// in-block permutation of tiles stored that way); it must keep aligned quads contiguous.
+template <typename ColMap>
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* tile, int c0, int ks, ColMap pcol) {
   const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
-  const int col = 16 * dt + 4 * (s & 3);
+  const int col = pcol(c0 + 4 * (s & 3));
   bf16x8 out;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -393,7 +130,336 @@ __device__ __forceinline__ bf16x8 vt_frag(const __bf16* tile, int dt, int ks) {
   }
   return out;
 }
+__device__ __forceinline__ int col_identity(int c) { return c; }
 
+// V^T A-fragment from a row-major V tile ([key][d]): rows d = 16dt + r, keys in the order of
+// the P^T B-operand.
+__device__ __forceinline__ bf16x8 vt_frag(const __bf16* tile, int dt, int ks) {
+  return tr_frag(tile, 16 * dt, ks, col_identity);
+}
+
+// Accumulator tiles D[16t + 4g + i][col] (t = 0..3) as the k = 0..63 operand (k order above).
+__device__ __forceinline__ void acc_to_op(const f32x4 (&acc)[4], bf16x8 (&hi)[2], bf16x8 (&lo)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = acc[2 * ks + (j >> 2)][j & 3];
+      const __bf16 h = (__bf16)v;
+      hi[ks][j] = h;
+      lo[ks][j] = (__bf16)(v - (float)h);
+    }
+}
+
+// =========================================================================== kernel 1: prep
+// One block of 4 waves per (b, h, chunk).  Operand conventions (16x16x32 MFMA, lane l, r = l%16,
+// g = l/16): an accumulator gives lane (r, g) rows 4g..4g+3 of column r; converted in registers it
+// serves directly as an A- or B-operand whose k index runs over those rows in the key order of
+// tr_frag.  Every product below pairs such an operand with a tr_frag read or with a tile stored in
+// permuted-column form, so the 64x64 intermediates X, Y, T^{-1}W, U and R never touch LDS:
+// wave w owns query block a = 16w.. (X, U, KQ), key block b = 16w.. (Y, R, S) and y block 16w.. of
+// T^{-1}W (for P).  LDS holds the DMA-loaded W, Q, K tiles, A (strict upper) with Z = A^{-1}
+// stored transposed in its lower triangle, T^{-T} (hi, lo) and U^T (hi, lo, for S).
+//   A      = I + diag(beta) strict_upper(W W^T)        (fp32)
+//   Z      = A^{-1}: 16x16 diagonal blocks by back substitution, then Z_IJ = -Z_II sum_K A_IK Z_KJ
+//   T^{-1} = Z diag(beta)                              (hi + lo bf16)
+//   X = T^{-1} U, U[t][a] = w_t.q_a (t <= a);  Y = R T^{-1}, R[b][s] = k_b.w_s (s > b)
+//   qtilde = Q - X^T W,  ktilde = K - Y W,  P = I - W^T (T^{-1} W),  S^T = K Q^T - Y U
+// hi/lo products drop lo*lo.  Padded tokens of a ragged last chunk are clamped copies of the last
+// row with beta = 0, which makes every T^{-1} entry that would touch them exactly zero.
+constexpr int kLDF = 68;  // fp32 row stride of A/Z
+constexpr size_t kPrepLds = 5 * kTile * 2 + 2 * kTile * 2 + kC * kLDF * 4 + 2 * 64 * 4;
+static_assert(kPrepLds <= 80 * 1024, "prep LDS plan must allow two blocks per CU");
+
+__device__ __forceinline__ int perm_col(int c) { return perm_pos(c); }
+
+__global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
+    const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, __bf16* __restrict__ qt,
+    __bf16* __restrict__ qt_lo, __bf16* __restrict__ kt, __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo,
+    float* __restrict__ Sm, float* __restrict__ fl, float* __restrict__ ftot) {
+  extern __shared__ __align__(1024) char smem[];
+  __bf16* Wt = reinterpret_cast<__bf16*>(smem);  // W [s][x]            (swizzled, natural columns)
+  __bf16* Qt = Wt + kTile;                       // Q [a][x]
+  __bf16* Kt = Qt + kTile;                       // K [b][x]
+  __bf16* TiH = Kt + kTile;                      // T^{-T} [t][s] hi / lo (swizzled, permuted columns)
+  __bf16* TiL = TiH + kTile;
+  __bf16* UH = TiL + kTile;                      // U^T [a][t] hi / lo   (swizzled, permuted columns)
+  __bf16* UL = UH + kTile;
+  float* Af = reinterpret_cast<float*>(UL + kTile);  // A strict upper, Z^T lower incl. diagonal
+  float* Bs = Af + kC * kLDF;                        // beta
+  float* Fs = Bs + 64;                               // unused pad (keeps the plan aligned)
+  (void)Fs;
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const int c = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t Lp = M * kC;
+  const int64_t row0 = (int64_t)c * kC;
+  const int64_t vr = L - row0;
+  const int valid = vr < kC ? (int)vr : kC;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto mm = [](const bf16x8& a, const bf16x8& b, const f32x4& acc) { return mfma16(a, b, acc); };
+  auto row_frag = [](const __bf16* tile, int row, int ks) {  // tile[row][32ks + 8g .. +7]
+    const int g_ = (threadIdx.x & 63) >> 4;
+    return tile_frag(tile, row, 4 * ks + g_);
+  };
+
+  // ---------------------------------------------------------------- A: stage W, Q, K, beta, FoX prefix
+  {
+    const int i0 = 2 * wave;
+    const size_t base = ((size_t)bh * L + row0) * kD;
+    dma_tile(Wt, w + base, kD, valid, i0);
+    dma_tile(Qt, q + base, kD, valid, i0);
+    dma_tile(Kt, k + base, kD, valid, i0);
+  }
+  if (tid < 64) Bs[tid] = tid < valid ? beta[bh * L + row0 + tid] : 0.f;  // padded tokens: identity
+  if (logf != nullptr && wave == 0) {  // chunk-local inclusive prefix sum of the log-forget gates
+    float f = l < valid ? logf[bh * L + row0 + l] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(f, o, 64);
+      if (l >= o) f += y;
+    }
+    fl[bh * Lp + row0 + l] = f;
+    if (l == 63) ftot[bh * M + c] = f;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed
+  __syncthreads();
+
+  // ---------------------------------------------------------------- B: A, U, R, K Q^T; diagonal block of Z
+  bf16x8 ubh[2], ubl[2], rbh[2], rbl[2];
+  f32x4 kq[4];
+  {
+    f32x4 ua[4], ra[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 ga = zero, u4 = zero, r4 = zero, k4 = zero;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 wr = row_frag(Wt, 16 * wave + r, ks);  // W rows of block `wave`
+        const bf16x8 wc = row_frag(Wt, 16 * tt + r, ks);    // W rows of block tt
+        ga = mm(wr, wc, ga);                                // D[s in wave][t in tt] = w_s . w_t
+        u4 = mm(wc, row_frag(Qt, 16 * wave + r, ks), u4);   // D[t in tt][a in wave] = w_t . q_a
+        r4 = mm(wc, row_frag(Kt, 16 * wave + r, ks), r4);   // D[s in tt][b in wave] = w_s . k_b
+        k4 = mm(row_frag(Kt, 16 * wave + r, ks), row_frag(Qt, 16 * tt + r, ks), k4);  // D[b][a] = k_b.q_a
+      }
+      const int col_wave = 16 * wave + r;  // a or b of this lane
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rw = 16 * tt + 4 * g + i;  // t (for U) or s (for R)
+        u4[i] = (rw <= col_wave) ? u4[i] : 0.f;
+        r4[i] = (rw > col_wave) ? r4[i] : 0.f;
+        const int srow = 16 * wave + 4 * g + i, tcol = 16 * tt + r;
+        if (srow < tcol) Af[srow * kLDF + tcol] = Bs[srow] * ga[i];
+      }
+      ua[tt] = u4;
+      ra[tt] = r4;
+      kq[tt] = k4;
+      // U^T[a][t] (hi/lo) for the S product of other waves: 4 consecutive t in permuted order
+      bf16x4 h4, l4;
+      split4(u4[0], u4[1], u4[2], u4[3], h4, l4);
+      const int pc = perm_pos(16 * tt + 4 * g);
+      *reinterpret_cast<bf16x4*>(UH + swz(col_wave, pc >> 3) + (pc & 7)) = h4;
+      *reinterpret_cast<bf16x4*>(UL + swz(col_wave, pc >> 3) + (pc & 7)) = l4;
+    }
+    acc_to_op(ua, ubh, ubl);
+    acc_to_op(ra, rbh, rbl);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // Z_II (block I = wave) by back substitution, lane l < 16 owning column l; stored transposed.
+  if (l < 16) {
+    const int base = 16 * wave;
+    float z[16];
+#pragma unroll
+    for (int ii = 15; ii >= 0; --ii) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int kk = ii + 1; kk < 16; ++kk) sacc += Af[(base + ii) * kLDF + base + kk] * z[kk];
+      z[ii] = (ii == l) ? 1.f : (ii < l ? -sacc : 0.f);
+    }
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii)
+      if (ii <= l) Af[(base + l) * kLDF + base + ii] = z[ii];
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- C: off-diagonal blocks of Z, by distance
+  // Z[i][j] (i <= j) lives at Af[j][i].  Wave I owns row block I:
+  //   T = sum_{K=I+1..J} A_IK Z_KJ,   Z_IJ^T = -T^T Z_II^T,   J = I + lv,
+  // both on the matrix cores with fp32 operands split into bf16 hi + lo (lo*lo dropped).
+  auto split8 = [](const float4& x0, const float4& x1, bf16x8& hi, bf16x8& lo) {
+    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 h = (__bf16)v[j];
+      hi[j] = h;
+      lo[j] = (__bf16)(v[j] - (float)h);
+    }
+  };
+  for (int lv = 1; lv < 4; ++lv) {
+    const int I = wave, J = wave + lv;
+    if (J < 4) {
+      f32x4 tacc = zero;
+      for (int st = 0; st < (lv + 1) / 2; ++st) {  // k = 16(I+1) + 32st + 8g + j, 16 lv values
+        const int kidx = 32 * st + 8 * g;
+        bf16x8 ah = {}, al = {}, bh = {}, bl = {};
+        if (kidx < 16 * lv) {
+          const int kc = 16 * (I + 1) + kidx;  // global column of A / row of Z
+          const float* ar = Af + (16 * I + r) * kLDF + kc;
+          split8(*reinterpret_cast<const float4*>(ar), *reinterpret_cast<const float4*>(ar + 4), ah, al);
+          const float* zr = Af + (16 * J + r) * kLDF + kc;  // Z[kc + j][16J + r]
+          float4 z0 = *reinterpret_cast<const float4*>(zr), z1 = *reinterpret_cast<const float4*>(zr + 4);
+          if (kc >= 16 * J) {  // diagonal block Z_JJ: zero below its diagonal (kk > jj)
+            const int kk0 = kc - 16 * J;
+            float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) zz[j] = (kk0 + j > r) ? 0.f : zz[j];
+            z0 = make_float4(zz[0], zz[1], zz[2], zz[3]);
+            z1 = make_float4(zz[4], zz[5], zz[6], zz[7]);
+          }
+          split8(z0, z1, bh, bl);
+        }
+        tacc = mfma16(ah, bh, tacc);  // D[ii][jj] = sum_k A[16I + ii][k] Z[k][16J + jj]
+        tacc = mfma16(ah, bl, tacc);
+        tacc = mfma16(al, bh, tacc);
+      }
+      // A-operand T^T over k = kk (rows 4g..4g+3 of the accumulator; slots 4..7 pad k to 32)
+      bf16x8 th = {}, tl = {};
+      // B-operand Z_II^T: column ii = r, k = kk = 4g + j: Z[16I + r][16I + kk] for kk >= r
+      bf16x8 zh = {}, zl = {};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const __bf16 h = (__bf16)tacc[j];
+        th[j] = h;
+        tl[j] = (__bf16)(tacc[j] - (float)h);
+        const int kk = 4 * g + j;
+        const float zv = (kk >= r) ? Af[(16 * I + kk) * kLDF + 16 * I + r] : 0.f;
+        const __bf16 zhh = (__bf16)zv;
+        zh[j] = zhh;
+        zl[j] = (__bf16)(zv - (float)zhh);
+      }
+      f32x4 zacc = zero;  // D[jj][ii] = sum_kk T[kk][jj] Z[16I + ii][16I + kk] = (Z_II T)^T
+      zacc = mfma16(th, zh, zacc);
+      zacc = mfma16(th, zl, zacc);
+      zacc = mfma16(tl, zh, zacc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Af[(16 * J + 4 * g + i) * kLDF + 16 * I + r] = -zacc[i];
+    }
+    __syncthreads();
+  }
+
+  // T^{-T}[t][s] = Z[s][t] beta_t (t >= s), hi/lo, stored with permuted columns
+  for (int e = tid; e < 512; e += 256) {
+    const int t = e >> 3, ch = e & 7;
+    bf16x8 h8, l8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int pslot = 8 * ch + j;
+      const int sc_ = (pslot & 32) + ((pslot & 7) >> 2) * 16 + ((pslot >> 3) & 3) * 4 + (pslot & 3);  // column held
+      const float v = (t >= sc_) ? Af[t * kLDF + sc_] * Bs[t] : 0.f;
+      const __bf16 hh = (__bf16)v;
+      h8[j] = hh;
+      l8[j] = (__bf16)(v - (float)hh);
+    }
+    *reinterpret_cast<bf16x8*>(TiH + swz(t, ch)) = h8;
+    *reinterpret_cast<bf16x8*>(TiL + swz(t, ch)) = l8;
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- D: register-resident products
+  const int a = 16 * wave + r;  // query / key row of this lane's output column
+  const int64_t ia = row0 + a;
+  const size_t chunk_rows = (size_t)bh * Lp + row0;
+  const size_t chunk_mat = ((size_t)bh * M + c) * kD * kD;
+  // X[s][a] = sum_t T^{-1}[s][t] U[t][a]          (s tiles st; a in this wave's block)
+  // Y^T[t][b] = sum_s T^{-T}[t][s] R[b][s]         (t tiles tt; b in this wave's block)
+  // Z2[s][y] = sum_t T^{-1}[s][t] W[t][y]          (s tiles st; y in this wave's block)
+  bf16x8 xbh[2], xbl[2], ybh[2], ybl[2], zbh[2], zbl[2];
+  {
+    f32x4 xa[4], ya[4], za[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      f32x4 x4 = zero, y4 = zero, z4 = zero;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 th = tr_frag(TiH, 16 * t4, ks, perm_col);  // T^{-1} rows s = 16 t4 + r, k = t
+        const bf16x8 tl = tr_frag(TiL, 16 * t4, ks, perm_col);
+        x4 = mm(th, ubh[ks], x4);
+        x4 = mm(th, ubl[ks], x4);
+        x4 = mm(tl, ubh[ks], x4);
+        const bf16x8 wy = tr_frag(Wt, 16 * wave, ks, col_identity);  // W[t][y], y in this block
+        z4 = mm(th, wy, z4);
+        z4 = mm(tl, wy, z4);
+        const bf16x8 gh = row_frag(TiH, 16 * t4 + r, ks);  // T^{-T} rows t = 16 t4 + r, k = s
+        const bf16x8 gl = row_frag(TiL, 16 * t4 + r, ks);
+        y4 = mm(gh, rbh[ks], y4);
+        y4 = mm(gh, rbl[ks], y4);
+        y4 = mm(gl, rbh[ks], y4);
+      }
+      xa[t4] = x4;
+      ya[t4] = y4;
+      za[t4] = z4;
+    }
+    acc_to_op(xa, xbh, xbl);  // X as an operand over k = s, column a
+    acc_to_op(ya, ybh, ybl);  // Y as an operand over k = t, row/column b
+    acc_to_op(za, zbh, zbl);  // (T^{-1}W)^T as an operand over k = s, row y
+  }
+#pragma unroll
+  for (int xt = 0; xt < 4; ++xt) {
+    const int x0 = 16 * xt + 4 * g;  // this lane's four consecutive output columns
+    const int pos = perm_pos(x0);
+    f32x4 dq = zero, dk = zero, dp = zero, ds = zero;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 wtx = tr_frag(Wt, 16 * xt, ks, col_identity);  // W^T rows x = 16 xt + r, k = s
+      dq = mm(wtx, xbh[ks], dq);  // D[x][a] = sum_s W[s][x] X[s][a]
+      dq = mm(wtx, xbl[ks], dq);
+      dk = mm(wtx, ybh[ks], dk);  // D[x][b] = sum_t W[t][x] Y[b][t]
+      dk = mm(wtx, ybl[ks], dk);
+      dp = mm(zbh[ks], wtx, dp);  // D[y][x] = sum_s Z2[s][y] W[s][x]
+      dp = mm(zbl[ks], wtx, dp);
+      const bf16x8 uh = row_frag(UH, 16 * xt + r, ks);  // U^T rows a = 16 xt + r, k = t
+      const bf16x8 ul = row_frag(UL, 16 * xt + r, ks);
+      ds = mm(ybh[ks], uh, ds);  // D[b][a] = sum_t Y[b][t] U[t][a]
+      ds = mm(ybh[ks], ul, ds);
+      ds = mm(ybl[ks], uh, ds);
+    }
+    // qtilde[a][x] = q_a[x] - D[x][a]  (lane: row a, columns x0..x0+3)
+    {
+      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qt + swz(a, x0 >> 3) + (x0 & 7));
+      bf16x4 h4, l4;
+      split4((float)q4[0] - dq[0], (float)q4[1] - dq[1], (float)q4[2] - dq[2], (float)q4[3] - dq[3], h4, l4);
+      *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
+      if (qt_lo != nullptr) *reinterpret_cast<bf16x4*>(qt_lo + (chunk_rows + a) * kD + pos) = l4;
+    }
+    // ktilde[b][x] = k_b[x] - D[x][b]
+    {
+      const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Kt + swz(a, x0 >> 3) + (x0 & 7));
+      *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) =
+          pack4((float)k4[0] - dk[0], (float)k4[1] - dk[1], (float)k4[2] - dk[2], (float)k4[3] - dk[3]);
+    }
+    // P[x][y] = delta - D[y][x]  (lane: row x = 16 xt + r, columns y = 16 wave + 4g .. +3)
+    {
+      const int xr = 16 * xt + r, y0 = 16 * wave + 4 * g;
+      bf16x4 ph, pl;
+      split4((y0 == xr ? 1.f : 0.f) - dp[0], (y0 + 1 == xr ? 1.f : 0.f) - dp[1],
+             (y0 + 2 == xr ? 1.f : 0.f) - dp[2], (y0 + 3 == xr ? 1.f : 0.f) - dp[3], ph, pl);
+      const int py = perm_pos(y0);
+      *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = ph;
+      if (p_lo != nullptr) *reinterpret_cast<bf16x4*>(p_lo + chunk_mat + (size_t)xr * kD + py) = pl;
+    }
+    // S[a][b] = q_a.k_b - D[b][a]  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3)
+    {
+      const int aq = 16 * xt + r, b0 = 16 * wave + 4 * g;
+      const float4 s4 = make_float4(kq[xt][0] - ds[0], kq[xt][1] - ds[1], kq[xt][2] - ds[2], kq[xt][3] - ds[3]);
+      *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kC + aq) * kC + b0) = s4;
+    }
+  }
+  (void)ia;
+}
+
+// =========================================================================== kernel 2: attention
 #ifndef PATHATTN_SCAN_WAVES_PER_SIMD
 #define PATHATTN_SCAN_WAVES_PER_SIMD 2
 #endif
