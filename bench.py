@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (a known-size reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -95,10 +97,11 @@ def bench_prefill(args):
                              lse=lse, workspace=ws)
 
     def prep():
-        native.path_attn_prep(q, k, v, w, beta, logf, chunk=C, transport=args.transport, workspace=ws)
+        native.path_attn_prep(q, k, v, w, beta, logf, scale=x.scale, chunk=C, transport=args.transport,
+                              workspace=ws)
 
     def scan():
-        native.path_attn_scan(v, logf, scale=x.scale, chunk=C, transport=args.transport, workspace=ws, out=out,
+        native.path_attn_scan(v, logf, chunk=C, transport=args.transport, workspace=ws, out=out,
                               lse=lse)
 
     for _ in range(args.warmup):
@@ -225,6 +228,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done (3 dispatches)")
+        del src, dst
     res, x = bench_prefill(args)
     cpu = None if args.no_cpu else bench_cpu(x, args)
     dec = None if args.no_decode else bench_decode(args)

@@ -173,16 +173,16 @@ path_status path_attn_fwd(const void* q, const void* k, const void* v, const voi
 }
 
 path_status path_attn_prep(const void* q, const void* k, const void* v, const void* w, const float* beta,
-                           const float* log_forget, int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
-                           int transport, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_fwd(kPhasePrep, q, k, v, w, beta, log_forget, nullptr, nullptr, B, H, L, d, chunk, 1.f, dtype,
+                           const float* log_forget, int64_t B, int64_t H, int64_t L, int d, int chunk, float scale,
+                           int dtype, int transport, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_fwd(kPhasePrep, q, k, v, w, beta, log_forget, nullptr, nullptr, B, H, L, d, chunk, scale, dtype,
                  transport, workspace, workspace_bytes, stream);
 }
 
 path_status path_attn_scan(const void* v, const float* log_forget, void* out, float* lse, int64_t B, int64_t H,
-                           int64_t L, int d, int chunk, float scale, int dtype, int transport, void* workspace,
+                           int64_t L, int d, int chunk, int dtype, int transport, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return run_fwd(kPhaseScan, nullptr, nullptr, v, nullptr, nullptr, log_forget, out, lse, B, H, L, d, chunk, scale,
+  return run_fwd(kPhaseScan, nullptr, nullptr, v, nullptr, nullptr, log_forget, out, lse, B, H, L, d, chunk, 1.f,
                  dtype, transport, workspace, workspace_bytes, stream);
 }
 

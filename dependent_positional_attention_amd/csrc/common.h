@@ -27,6 +27,9 @@ __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Lambdas inside kernels must inline (an outlined call passes register arrays through scratch).
+#define PA_INLINE __attribute__((always_inline))
+
 // Round x up to a multiple of a (a power of two).
 __host__ __device__ constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 

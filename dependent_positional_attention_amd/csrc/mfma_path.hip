@@ -14,19 +14,19 @@
 //   Z = A^{-1} by 16x16-blocked back substitution (fp32), T^{-1} = Z diag(beta)
 //   U^T[a][t] = q_a.w_t (t <= a), R[b][s] = k_b.w_s (s > b), X = T^{-1} U, Y = R T^{-1}
 //   qtilde = Q - X^T W, ktilde = K - Y W, P = I - W^T (T^{-1} W),
-//   S[a][b] = q_a.k_b - (Y U)[b][a]   (b <= a; in-chunk logits before scaling)
+//   S[a][b] = q_a.k_b - (Y U)[b][a]   (b <= a; in-chunk logits)
+// qtilde and S are stored multiplied by scale * log2(e), the scan's logit unit.
 // T^{-1} and T^{-1} W enter the matrix cores as hi+lo bf16 pairs so that P is
 // accurate enough to be split again into hi+lo for the long-range transport.
 //
-// Kernel 2 (attention), one workgroup of 4 waves per 4 consecutive query chunks
-// (wave w owns chunk 4p+w, 64 queries = four 16-query MFMA column tiles), longest
-// rows first.  The waves share one LDS stream of key chunks n = 4p+3 ... 0
-// (ktilde_n, V_n straight from the value tensor, P_n; double-buffered, filled by
-// direct global->LDS loads); each A-fragment read from LDS feeds four MFMAs (one
-// per query tile).  A wave scores its own chunk from the precomputed in-chunk
-// logits when the stream reaches it, and earlier chunks as follows:
-//   S^T = ktilde_n Q_run^T       (keys x queries: each lane holds one query column)
-//   online softmax (exp2), P^T kept in registers as the PV B-operand
+// Kernel 2 (attention), one workgroup of 4 waves per 2 consecutive query chunks (two waves of
+// 32 queries per chunk), longest rows first.  The waves share one LDS stream of key chunks
+// n = top ... 0 (ktilde_n, V_n straight from the value tensor, P_n; a ring of direct global->LDS
+// copies issued one step ahead).  A wave scores its own chunk from the precomputed in-chunk logits
+// when the stream reaches it, and earlier chunks as follows (queries pre-scaled by
+// scale * log2(e), so logits come out in log2 units):
+//   S^T = ktilde_n Q_run^T - m    (keys x queries; the running max m seeds the accumulator)
+//   p = exp2(S^T), lazily checked against the running max; P^T kept as the PV B-operand
 //   O^T += V_n^T P^T
 //   Q_run^T <- P_n Q_run^T       (fp32 accumulate, re-rounded to bf16 [hi+lo])
 // Column permutation: an MFMA accumulator gives each lane rows 4g..4g+3 of every
@@ -35,6 +35,8 @@
 // stored slot 8g+j of each 32-block holding index 16(j/4)+4g+(j%4), and V^T
 // fragments are read (LDS transpose reads) in the same key order; accumulators then
 // convert to B-operands in registers with no data movement.
+#include <type_traits>
+
 #include "common.h"
 
 namespace pathattn {
@@ -89,17 +91,19 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chu
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// Direct global->LDS copy of one 64x64 bf16 tile (row stride `gstride` elements in global) by
-// one wave: instructions i0, i0+1 each cover 8 rows.  Rows at or beyond `rmax` are clamped to
-// rmax - 1 (finite data that only ever meets masked or discarded positions).
-__device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* src, int64_t gstride, int rmax, int i0) {
+// Direct global->LDS copy of one 64x64 bf16 tile (64 contiguous rows of 128 B in global) by one
+// wave: instructions i0, i0+1 each cover 8 rows.  Rows at or beyond `rmax` are clamped to rmax - 1
+// (finite data that only ever meets masked or discarded positions).  The per-lane part of the
+// address is a 32-bit byte offset from the wave-uniform tile base (scalar base + vector offset).
+__device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* src, int rmax, int i0) {
   const int l = threadIdx.x & 63;
 #pragma unroll
   for (int i = i0; i < i0 + 2; ++i) {
     const int row = 8 * i + (l >> 3), slot = l & 7;
     const int rs = row < rmax ? row : rmax - 1;
-    const __bf16* g = src + (int64_t)rs * gstride + ((slot ^ (row & 7)) << 3);
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(tile + i * 512), 16, 0, 0);
+    const uint32_t off = (uint32_t)(rs * 128 + ((slot ^ (row & 7)) << 4));
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(src) + off),
+                                     (lds_void*)(tile + i * 512), 16, 0, 0);
   }
 }
 
@@ -175,8 +179,8 @@ __device__ __forceinline__ int perm_col(int c) { return perm_pos(c); }
 
 __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
-    const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, __bf16* __restrict__ qt,
-    __bf16* __restrict__ qt_lo, __bf16* __restrict__ kt, __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo,
+    const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, float qs,
+    __bf16* __restrict__ qt, __bf16* __restrict__ qt_lo, __bf16* __restrict__ kt, __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo,
     float* __restrict__ Sm, float* __restrict__ fl, float* __restrict__ ftot) {
   extern __shared__ __align__(1024) char smem[];
   __bf16* Wt = reinterpret_cast<__bf16*>(smem);  // W [s][x]            (swizzled, natural columns)
@@ -209,9 +213,9 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
   {
     const int i0 = 2 * wave;
     const size_t base = ((size_t)bh * L + row0) * kD;
-    dma_tile(Wt, w + base, kD, valid, i0);
-    dma_tile(Qt, q + base, kD, valid, i0);
-    dma_tile(Kt, k + base, kD, valid, i0);
+    dma_tile(Wt, w + base, valid, i0);
+    dma_tile(Qt, q + base, valid, i0);
+    dma_tile(Kt, k + base, valid, i0);
   }
   if (tid < 64) Bs[tid] = tid < valid ? beta[bh * L + row0 + tid] : 0.f;  // padded tokens: identity
   if (logf != nullptr && wave == 0) {  // chunk-local inclusive prefix sum of the log-forget gates
@@ -425,11 +429,12 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
       ds = mm(ybh[ks], ul, ds);
       ds = mm(ybl[ks], uh, ds);
     }
-    // qtilde[a][x] = q_a[x] - D[x][a]  (lane: row a, columns x0..x0+3)
+    // qtilde[a][x] = (q_a[x] - D[x][a]) * qs  (lane: row a, columns x0..x0+3)
     {
       const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qt + swz(a, x0 >> 3) + (x0 & 7));
       bf16x4 h4, l4;
-      split4((float)q4[0] - dq[0], (float)q4[1] - dq[1], (float)q4[2] - dq[2], (float)q4[3] - dq[3], h4, l4);
+      split4(((float)q4[0] - dq[0]) * qs, ((float)q4[1] - dq[1]) * qs, ((float)q4[2] - dq[2]) * qs,
+             ((float)q4[3] - dq[3]) * qs, h4, l4);
       *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
       if (qt_lo != nullptr) *reinterpret_cast<bf16x4*>(qt_lo + (chunk_rows + a) * kD + pos) = l4;
     }
@@ -449,10 +454,11 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
       *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = ph;
       if (p_lo != nullptr) *reinterpret_cast<bf16x4*>(p_lo + chunk_mat + (size_t)xr * kD + py) = pl;
     }
-    // S[a][b] = q_a.k_b - D[b][a]  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3)
+    // S[a][b] = (q_a.k_b - D[b][a]) * qs  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3)
     {
       const int aq = 16 * xt + r, b0 = 16 * wave + 4 * g;
-      const float4 s4 = make_float4(kq[xt][0] - ds[0], kq[xt][1] - ds[1], kq[xt][2] - ds[2], kq[xt][3] - ds[3]);
+      const float4 s4 = make_float4((kq[xt][0] - ds[0]) * qs, (kq[xt][1] - ds[1]) * qs, (kq[xt][2] - ds[2]) * qs,
+                                    (kq[xt][3] - ds[3]) * qs);
       *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kC + aq) * kC + b0) = s4;
     }
   }
@@ -460,10 +466,6 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
 }
 
 // =========================================================================== kernel 2: attention
-#ifndef PATHATTN_SCAN_WAVES_PER_SIMD
-#define PATHATTN_SCAN_WAVES_PER_SIMD 2
-#endif
-
 // Max / sum over the 4 lanes holding the same query column (lanes l, l^16, l^32, l^48): each
 // permlane swap returns the value pair {own, partner} for the two lane halves it exchanges.
 // The maxima use the NaN-propagating maximum, which needs no input canonicalisation.
@@ -482,27 +484,73 @@ __device__ __forceinline__ float colsum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Workgroup barrier that leaves outstanding global->LDS copies in flight (the plain
+// __syncthreads() drains every memory counter first).  LDS reads issued before it have
+// returned; the copies a later step reads are waited for explicitly, per wave, before it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// s_waitcnt vmcnt(n) (expcnt, lgkmcnt untouched), n < 16
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // Blocks are laid out for the 8 XCDs (workgroup b runs on XCD b % 8, each with its own L2):
 // every query block of one (batch, head) lands on the same XCD, heads are dealt round-robin
 // to XCDs, and within a head the longest rows go first.
 constexpr int kXcd = 8;
-// Work split: a block of 4 waves owns kCpb consecutive query chunks; each chunk's 64 queries
-// are shared by kWpc waves of kQt 16-query MFMA column tiles each.
-constexpr int kQt = 2;
-constexpr int kWpc = 4 / kQt;
-constexpr int kCpb = 4 / kWpc;
 
-// Waves per SIMD the scan is built for (register budget 512 / waves).
-template <bool FOX, bool X3>
-__global__ __launch_bounds__(256, X3 ? 2 : PATHATTN_SCAN_WAVES_PER_SIMD) void mfma_attn_kernel(
+#ifndef PATHATTN_SCAN_QT
+#define PATHATTN_SCAN_QT 2
+#endif
+// Key chunks reach LDS through registers (1) or by direct global->LDS copies (0).
+#ifndef PATHATTN_SCAN_REGSTAGE
+#define PATHATTN_SCAN_REGSTAGE 0
+#endif
+// Work split: a block of 4 waves owns QT consecutive query chunks; each chunk's 64 queries are
+// shared by 4 / QT waves of QT 16-query MFMA column tiles each.  QT = 2 runs two waves per SIMD,
+// QT = 4 one (each LDS fragment then feeds four MFMAs instead of two).
+template <bool X3, int QT>
+struct ScanShape {
+  static_assert(QT == 2 || QT == 4, "16-query tiles per wave");
+  static constexpr int kWpc = 4 / QT;                  // waves per query chunk
+  static constexpr int kCpb = QT;                      // query chunks per block
+  static constexpr int kWaves = QT == 2 ? 2 : 1;       // waves per SIMD
+  static constexpr int kNm = X3 ? 4 : 3;               // tiles per key group (ktilde, V, P hi [, P lo])
+  static constexpr int kBuf = (PATHATTN_SCAN_REGSTAGE || (X3 && QT == 2)) ? 2 : 3;  // LDS ring depth
+  static constexpr int kOps = 2 * kNm;                 // copy instructions per wave per group (+1 FoX)
+};
+
+// Attention scan.  Block-wide stream of key groups, group(n) = {ktilde_{n-1}, V_n, P_n [, P_lo n],
+// FoX prefix of chunk n-1} for n = top chunk ... 0 (chunk indices clamp at 0), so that one step of
+// a wave reads the values and transition of chunk n together with the keys of the chunk it scores
+// next.  Per wave, with its query chunk m:
+//   n == m (own chunk):  logits from the precomputed in-chunk S (masked), exact row max, P^T V_m;
+//                        running queries Q_run = qtilde; logits of chunk m-1.
+//   n <  m:              p = exp2(z) for the logits z of chunk n (computed one step earlier, already
+//                        minus the running max, which seeds the MFMA accumulator); O^T += V_n^T p^T;
+//                        Q_run^T <- P_n Q_run^T; logits of chunk n-1 with the moved queries.
+// The running max is raised lazily: a lane whose partial row sum exceeds 2^kRescale (so possibly
+// some p > 2^kRescale) sends the wave through the exact max, which raises the reference of any
+// column whose max exceeds it by more than kRescale and rescales O, the sums and the pending logits.
+template <bool FOX, bool X3, int QT>
+__global__ __launch_bounds__(256, (ScanShape<X3, QT>::kWaves)) void mfma_attn_kernel(
     const __bf16* __restrict__ qt, const __bf16* __restrict__ qt_lo, const __bf16* __restrict__ kt,
     const __bf16* __restrict__ v, const __bf16* __restrict__ p_hi, const __bf16* __restrict__ p_lo,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
-    __bf16* __restrict__ out, float* __restrict__ lse, int64_t L, int64_t M, int64_t BH, float sc) {
-  constexpr int NM = X3 ? 4 : 3;  // ktilde, V, P hi [, P lo]
-  constexpr float kRescale = 8.f;  // log2 headroom before the running max must be raised
-  __shared__ __align__(1024) __bf16 lds[2][NM][kTile];
-  __shared__ __align__(16) float lfl[2][64];
+    __bf16* __restrict__ out, float* __restrict__ lse, int64_t L, int64_t M, int64_t BH) {
+  using Sh = ScanShape<X3, QT>;
+  constexpr int NM = Sh::kNm, NB = Sh::kBuf, kWpc = Sh::kWpc, kCpb = Sh::kCpb;
+  constexpr int OPS = Sh::kOps + (FOX ? 1 : 0);
+  constexpr float kRescale = 8.f;     // log2 headroom before the running max must be raised
+  constexpr float kSumCap = 256.f;    // 2^kRescale
+  __shared__ __align__(1024) __bf16 lds[NB][NM][kTile];
+  __shared__ __align__(16) float lfl[NB][64];
 
   const int64_t nP = (M + kCpb - 1) / kCpb;
   const int xcd = (int)(blockIdx.x % kXcd);
@@ -512,220 +560,385 @@ __global__ __launch_bounds__(256, X3 ? 2 : PATHATTN_SCAN_WAVES_PER_SIMD) void mf
   const int64_t bh = xcd + kXcd * (slot / nP);
   const int64_t p = nP - 1 - slot % nP;
 
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  // the wave index is wave-uniform: keep it (and everything derived from it) in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, r = l & 15, g = l >> 4;
   const int64_t m = kCpb * p + wave / kWpc;  // this wave's query chunk
-  const int q0 = 16 * kQt * (wave % kWpc);   // first query (within the chunk) of this wave
+  const int q0 = 16 * QT * (wave % kWpc);    // first query (within the chunk) of this wave
   const bool active = m < M;
   const int64_t Lp = M * kC;
   const int64_t mtop = (kCpb * p + kCpb - 1 < M - 1) ? kCpb * p + kCpb - 1 : M - 1;  // highest chunk here
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  f32x4 o[4][kQt];  // O^T tiles [d tile][query tile]
-  float lsum[kQt];  // this lane's share of each column's softmax denominator (fp32)
-  float mref[kQt];  // running reference max per query column (log2 units)
-  bf16x8 qb[kQt][2], ql[kQt][2];
+  f32x4 o[4][QT];    // O^T tiles [d tile][query tile]
+  float lsum[QT];    // this lane's share of each column's softmax denominator
+  float mref[QT];    // running reference max per query column (log2 units)
+  f32x4 negm[QT];    // -mref in all four accumulator slots: the logits' MFMA seed
+  bf16x8 qb[QT][2], ql[QT][2];  // running queries as the logits' B-operand (hi [, lo])
 #pragma unroll
-  for (int a = 0; a < kQt; ++a) {
-    mref[a] = -INFINITY;
+  for (int a = 0; a < QT; ++a) {
+    mref[a] = 0.f;
     lsum[a] = 0.f;
+    negm[a] = zero;
 #pragma unroll
     for (int b = 0; b < 4; ++b) o[b][a] = zero;
 #pragma unroll
     for (int b = 0; b < 2; ++b) qb[a][b] = ql[a][b] = bf16x8{};
   }
-  int buf = 0;  // LDS buffer holding the chunk being scored
+  float off = 0.f;  // FoX: sum of the chunk totals from the chunk being scored up to chunk m - 1
 
-  // Online softmax over one 32-key half (key tiles 2h, 2h+1) of a chunk.  z holds logits in
-  // log2 units.  The reference max is raised only when some column's max exceeds it by more
-  // than kRescale, so most halves skip the O rescale.  pb receives P^T for k-step h.
-  auto absorb = [&](f32x4 (&z)[2][kQt], bf16x8 (&pb)[kQt]) {
-    float mz[kQt];
-    bool raise = false;
-#pragma unroll
-    for (int qi = 0; qi < kQt; ++qi) {
-      const float m0 = max3(z[0][qi][0], z[0][qi][1], z[0][qi][2]);
-      const float m1 = max3(z[0][qi][3], z[1][qi][0], z[1][qi][1]);
-      mz[qi] = colmax4(max3(max3(m0, m1, z[1][qi][2]), z[1][qi][3], -INFINITY));
-      raise |= mz[qi] > mref[qi] + kRescale;
-    }
-    if (__any(raise)) {
-#pragma unroll
-      for (int qi = 0; qi < kQt; ++qi) {
-        const float mnew = max2(mref[qi], mz[qi]);
-        const float base = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = fast_exp2(mref[qi] - base);
-        lsum[qi] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt][qi] *= alpha;
-        mref[qi] = base;
-      }
-    }
-#pragma unroll
-    for (int qi = 0; qi < kQt; ++qi) {
-      float ps = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(z[u][qi][i] - mref[qi]);
-          ps += pv;
-          pb[qi][4 * u + i] = (__bf16)pv;
-        }
-      lsum[qi] += ps;
-    }
-  };
-  auto pv_update = [&](const __bf16* Vn, int ks, const bf16x8 (&pb)[kQt]) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const bf16x8 a = vt_frag(Vn, dt, ks);
-#pragma unroll
-      for (int qi = 0; qi < kQt; ++qi) o[dt][qi] = mfma16(a, pb[qi], o[dt][qi]);
-    }
-  };
-  // Scaled logits (log2 units) of key tiles 2h, 2h+1 against the running queries, plus the
+  // ---------------------------------------------------------------- step pieces
+  // Logits (log2 units, minus the running max) of a key chunk against the running queries, plus the
   // PaTH-FoX bias sum_{s=j+1..i} f_s = (chunk-local prefix at i) + off - (prefix at j), whose
-  // row-constant first term cancels in the softmax.
-  auto logits_half = [&](const __bf16* Kn, int h, float offv, f32x4 (&z)[2][kQt]) {
+  // row-constant first term cancels in the softmax (it returns in the lse).  kfrag(t, ks) gives the
+  // A-fragment of key rows 16t.., lf the chunk-local prefix of the key chunk.
+  auto logits = [&](auto kfrag, const float* lf, float offv, f32x4 (&z)[4][QT]) PA_INLINE {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int t = 0; t < 4; ++t) {
+      f32x4 seed[QT];
+      if constexpr (FOX) {
+        const float4 f4 = *reinterpret_cast<const float4*>(lf + 16 * t + 4 * g);
+        const float fb[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-      for (int qi = 0; qi < kQt; ++qi) z[u][qi] = zero;
+        for (int qi = 0; qi < QT; ++qi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) seed[qi][i] = __builtin_fmaf(kLog2e, offv - fb[i], negm[qi][i]);
+      } else {
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) seed[qi] = negm[qi];
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = tile_frag(Kn, 16 * (2 * h + u) + r, 4 * ks + g);
+        const bf16x8 a = kfrag(t, ks);
 #pragma unroll
-        for (int qi = 0; qi < kQt; ++qi) {
-          z[u][qi] = mfma16(a, qb[qi][ks], z[u][qi]);
-          if (X3) z[u][qi] = mfma16(a, ql[qi][ks], z[u][qi]);  // logits see the query residual
+        for (int qi = 0; qi < QT; ++qi) {
+          z[t][qi] = mfma16(a, qb[qi][ks], ks == 0 ? seed[qi] : z[t][qi]);
+          if constexpr (X3) z[t][qi] = mfma16(a, ql[qi][ks], z[t][qi]);  // logits see the query residual
         }
       }
     }
+  };
+  auto lds_keys = [&](const __bf16* Kt_) PA_INLINE {
+    return [=](int t, int ks) PA_INLINE { return tile_frag(Kt_, 16 * t + r, 4 * ks + g); };
+  };
+  // Q_run^T <- P_n Q_run^T (fp32 accumulate).
+  auto transport = [&](const __bf16* Pt, const __bf16* Plt, f32x4 (&qn)[4][QT]) PA_INLINE {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float bias = FOX ? kLog2e * (offv - lfl[buf][16 * (2 * h + u) + 4 * g + i]) : 0.f;
+      for (int qi = 0; qi < QT; ++qi) qn[dt][qi] = zero;
 #pragma unroll
-        for (int qi = 0; qi < kQt; ++qi) z[u][qi][i] = __builtin_fmaf(z[u][qi][i], sc, bias);
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = tile_frag(Pt, 16 * dt + r, 4 * ks + g);
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) qn[dt][qi] = mfma16(a, qb[qi][ks], qn[dt][qi]);
+        if constexpr (X3) {
+          const bf16x8 alo = tile_frag(Plt, 16 * dt + r, 4 * ks + g);
+#pragma unroll
+          for (int qi = 0; qi < QT; ++qi) {
+            qn[dt][qi] = mfma16(a, ql[qi][ks], qn[dt][qi]);
+            qn[dt][qi] = mfma16(alo, qb[qi][ks], qn[dt][qi]);
+          }
+        }
+      }
+    }
+  };
+  // Accumulator tiles -> the logits' B-operand (bf16 hi [+ lo]).
+  auto requeue = [&](const f32x4 (&qn)[4][QT]) PA_INLINE {
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float vq = qn[2 * ks + (j >> 2)][qi][j & 3];
+          const __bf16 hi = (__bf16)vq;
+          qb[qi][ks][j] = hi;
+          if constexpr (X3) ql[qi][ks][j] = (__bf16)(vq - (float)hi);
+        }
+  };
+  // p = exp2(z - shift): this lane's partial row sums and P^T as the PV B-operand.
+  auto exps = [&](const f32x4 (&z)[4][QT], const float (&shift)[QT], bf16x8 (&pb)[QT][2], float (&ps)[QT]) PA_INLINE {
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = fast_exp2(z[t][qi][i] - shift[qi]);
+          s = (t == 0 && i == 0) ? pv : s + pv;
+          pb[qi][t >> 1][4 * (t & 1) + i] = (__bf16)pv;
+        }
+      ps[qi] = s;
+    }
+  };
+  auto pv = [&](const __bf16* Vt, const bf16x8 (&pb)[QT][2]) PA_INLINE {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = vt_frag(Vt, dt, ks);
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) o[dt][qi] = mfma16(a, pb[qi][ks], o[dt][qi]);
+      }
+  };
+  // Exact column max of z (relative to the reference); raise every column's reference to its max
+  // when some column exceeds it by more than kRescale.  Returns false when nothing moved.
+  auto raise_ref = [&](const f32x4 (&z)[4][QT], float (&d)[QT]) PA_INLINE {
+    bool up = false;
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      float mx = max3(z[0][qi][0], z[0][qi][1], z[0][qi][2]);
+      mx = max3(mx, z[0][qi][3], z[1][qi][0]);
+      mx = max3(mx, z[1][qi][1], z[1][qi][2]);
+      mx = max3(mx, z[1][qi][3], z[2][qi][0]);
+      mx = max3(mx, z[2][qi][1], z[2][qi][2]);
+      mx = max3(mx, z[2][qi][3], z[3][qi][0]);
+      mx = max3(mx, z[3][qi][1], z[3][qi][2]);
+      mx = max2(mx, z[3][qi][3]);
+      d[qi] = max2(colmax4(mx), 0.f);
+      up |= d[qi] > kRescale;
+    }
+    if (!__any(up)) return false;
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      const float alpha = fast_exp2(-d[qi]);
+      mref[qi] += d[qi];
+      negm[qi] = f32x4{-mref[qi], -mref[qi], -mref[qi], -mref[qi]};
+      lsum[qi] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt][qi] *= alpha;
+    }
+    return true;
+  };
+
+  // Own chunk: logits from the in-chunk S (already in log2 units), exact max, P^T V_m; then the
+  // running queries start at qtilde.
+  auto diag = [&](const __bf16* Vt_) PA_INLINE {
+    const float* Sb = Sm + ((size_t)bh * M + m) * kC * kC;
+    f32x4 z[4][QT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float fb[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FOX) {
+        const float4 f4 = *reinterpret_cast<const float4*>(fl + bh * Lp + m * kC + 16 * t + 4 * g);
+        fb[0] = kLog2e * f4.x, fb[1] = kLog2e * f4.y, fb[2] = kLog2e * f4.z, fb[3] = kLog2e * f4.w;
+      }
+#pragma unroll
+      for (int qi = 0; qi < QT; ++qi) {
+        const int a = q0 + 16 * qi + r;
+        const float4 s4 = *reinterpret_cast<const float4*>(Sb + a * kC + 16 * t + 4 * g);
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[t][qi][i] = (16 * t + 4 * g + i <= a) ? sv[i] - fb[i] : -INFINITY;
+      }
+    }
+    float shift[QT], ps[QT];
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) mx = max3(mx, max2(z[t][qi][0], z[t][qi][1]), max2(z[t][qi][2], z[t][qi][3]));
+      mref[qi] = colmax4(mx);  // finite: key a itself is never masked
+      negm[qi] = f32x4{-mref[qi], -mref[qi], -mref[qi], -mref[qi]};
+      shift[qi] = mref[qi];
+    }
+    bf16x8 pb[QT][2];
+    exps(z, shift, pb, ps);
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) lsum[qi] = ps[qi];
+    pv(Vt_, pb);
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const size_t qo = ((size_t)bh * Lp + m * kC + q0 + 16 * qi + r) * kD + 32 * ks + 8 * g;
+        qb[qi][ks] = *reinterpret_cast<const bf16x8*>(qt + qo);
+        if constexpr (X3) ql[qi][ks] = *reinterpret_cast<const bf16x8*>(qt_lo + qo);
       }
   };
 
-  // Stage key chunk n into LDS buffer b (each wave moves a quarter of every tile).
-  auto stage = [&](int64_t n, int b) {
-    const int i0 = 2 * wave;
-    dma_tile(lds[b][0], kt + ((size_t)bh * Lp + n * kC) * kD, kD, kC, i0);
+  // Earlier chunk n (< m); NEXT: chunk n - 1 exists (the running queries move on).  Logits of
+  // chunk n (seeded with -reference, plus the FoX bias), exponentials with the lazy check, then the
+  // transport and O^T += V_n^T P^T on the matrix cores; the requeue of the moved queries comes last
+  // so that the transport has drained by then.  The two waves of a SIMD overlap one's vector phase
+  // with the other's MFMAs.
+  auto step = [&](auto next_tag, const __bf16* Kt_, const __bf16* Vt_, const __bf16* Pt_, const __bf16* Plt_,
+                  const float* lf) PA_INLINE {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    f32x4 z[4][QT];
+    logits(lds_keys(Kt_), lf, off, z);
+    f32x4 qn[4][QT];
+    if constexpr (NEXT) transport(Pt_, Plt_, qn);
+    const float none[QT] = {};
+    bf16x8 pb[QT][2];
+    float ps[QT];
+    exps(z, none, pb, ps);
+    // Issue order: the logits' MFMAs first, then the transport's MFMAs interleaved with the
+    // exponentials, which only wait for the logits.
+    if constexpr (!X3 && !FOX && QT == 2) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // key fragments
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // logits
+      if constexpr (NEXT) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // transition fragments
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+      }
+    }
+    bool big = false;
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) big |= ps[qi] > kSumCap;
+    if (__any(big)) {  // rare: some p may exceed 2^kRescale
+      float d[QT];
+      if (raise_ref(z, d)) exps(z, d, pb, ps);
+    }
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) lsum[qi] += ps[qi];
+    pv(Vt_, pb);
+    if constexpr (NEXT) requeue(qn);
+  };
+
+  // ---------------------------------------------------------------- key-group stream
+  // Key chunk n = ktilde_n, V_n, P_n [, P_lo n] and the FoX prefix of chunk n.  Each wave moves a
+  // quarter of every tile (rows 8i.., i = 2 wave, 2 wave + 1; lane l carries 16 B of row 8i + l/8,
+  // written to slot l of the tile's i-th 1 KiB run) and of the prefix.
+  const int i0 = 2 * wave;
+  auto chunk_src = [&](int64_t n, int t) PA_INLINE -> const __bf16* {
+    if (t == 0) return kt + ((size_t)bh * Lp + n * kC) * kD;
+    if (t == 1) return v + ((size_t)bh * L + n * kC) * kD;
+    return (t == 2 ? p_hi : p_lo) + ((size_t)bh * M + n) * kD * kD;
+  };
+  auto chunk_rows = [&](int64_t n, int t) PA_INLINE -> int {
     const int64_t vrows = L - n * kC;
-    dma_tile(lds[b][1], v + ((size_t)bh * L + n * kC) * kD, kD, vrows < kC ? (int)vrows : kC, i0);
-    dma_tile(lds[b][2], p_hi + ((size_t)bh * M + n) * kD * kD, kD, kC, i0);
-    if (X3) dma_tile(lds[b][NM - 1], p_lo + ((size_t)bh * M + n) * kD * kD, kD, kC, i0);
-    if (FOX && wave == 0)
-      __builtin_amdgcn_global_load_lds((const void*)(fl + bh * Lp + n * kC + l), (lds_void*)lfl[b], 4, 0, 0);
+    return (t == 1 && vrows < kC) ? (int)vrows : kC;
   };
-
-  stage(mtop, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS writes have landed
-  __syncthreads();
-  float off = 0.f;
-  for (int64_t n = mtop; n >= 0; --n) {
-    if (n > 0) stage(n - 1, buf ^ 1);  // safe: every wave finished reading buf^1 before the last barrier
-    const __bf16* Kn = lds[buf][0];
-    const __bf16* Vn = lds[buf][1];
-    const __bf16* Pn = lds[buf][2];
-    if (active && n == m) {
-      // ---------------------------------------------------------- own chunk: in-chunk logits
-      const float* Sb = Sm + ((size_t)bh * M + m) * kC * kC;
+#if PATHATTN_SCAN_REGSTAGE
+  // Staged through registers: loads for chunk n-1 are issued at the end of the step on chunk n+1
+  // and written to LDS at the end of the step on chunk n, so two slots suffice.
+  bf16x8 sreg[NM][2];
+  float sfl = 0.f;
+  auto fetch = [&](int64_t n) PA_INLINE {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x4 z[2][kQt];
+    for (int t = 0; t < NM; ++t) {
+      const __bf16* src = chunk_src(n, t);
+      const int rmax = chunk_rows(n, t);
 #pragma unroll
-        for (int qi = 0; qi < kQt; ++qi)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int kti = 2 * h + u, a = q0 + 16 * qi + r;
-            const float4 s4 = *reinterpret_cast<const float4*>(Sb + a * kC + 16 * kti + 4 * g);
-            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int b = 16 * kti + 4 * g + i;
-              const float fb = FOX ? kLog2e * lfl[buf][b] : 0.f;
-              z[u][qi][i] = (b <= a) ? sv[i] * sc - fb : -INFINITY;
-            }
-          }
-        bf16x8 pb[kQt];
-        absorb(z, pb);
-        pv_update(Vn, h, pb);
-      }
-#pragma unroll
-      for (int qi = 0; qi < kQt; ++qi)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const size_t qo = ((size_t)bh * Lp + m * kC + q0 + 16 * qi + r) * kD + 32 * ks + 8 * g;
-          qb[qi][ks] = *reinterpret_cast<const bf16x8*>(qt + qo);
-          if (X3) ql[qi][ks] = *reinterpret_cast<const bf16x8*>(qt_lo + qo);
-        }
-    } else if (active && n < m) {
-      // ---------------------------------------------------------- earlier chunk: transported queries
-      // Per 32-key half: logits S^T = ktilde_n Q_run^T, online softmax, O^T += V^T P^T.  The
-      // transport Q_run^T <- P_n Q_run^T for the next chunk is issued after the second half's
-      // logits (the last reader of the current queries), so the matrix cores run it while the
-      // vector units do that half's softmax.
-      if (FOX) off += ftot[bh * M + n];
-      {
-        f32x4 z[2][kQt];
-        logits_half(Kn, 0, off, z);
-        bf16x8 pb[kQt];
-        absorb(z, pb);
-        pv_update(Vn, 0, pb);
-      }
-      {
-        f32x4 z[2][kQt];
-        logits_half(Kn, 1, off, z);
-        if (n > 0) {
-          f32x4 qn[4][kQt];
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-            for (int qi = 0; qi < kQt; ++qi) qn[dt][qi] = zero;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              const bf16x8 a = tile_frag(Pn, 16 * dt + r, 4 * ks + g);
-#pragma unroll
-              for (int qi = 0; qi < kQt; ++qi) qn[dt][qi] = mfma16(a, qb[qi][ks], qn[dt][qi]);
-              if (X3) {
-                const bf16x8 alo = tile_frag(lds[buf][NM - 1], 16 * dt + r, 4 * ks + g);
-#pragma unroll
-                for (int qi = 0; qi < kQt; ++qi) {
-                  qn[dt][qi] = mfma16(a, ql[qi][ks], qn[dt][qi]);
-                  qn[dt][qi] = mfma16(alo, qb[qi][ks], qn[dt][qi]);
-                }
-              }
-            }
-          }
-#pragma unroll
-          for (int qi = 0; qi < kQt; ++qi)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const float vq = qn[2 * ks + (j >> 2)][qi][j & 3];
-                const __bf16 hi = (__bf16)vq;
-                qb[qi][ks][j] = hi;
-                if (X3) ql[qi][ks][j] = (__bf16)(vq - (float)hi);
-              }
-        }
-        bf16x8 pb[kQt];
-        absorb(z, pb);
-        pv_update(Vn, 1, pb);
+      for (int j = 0; j < 2; ++j) {
+        const int row = 8 * (i0 + j) + (l >> 3), slot = l & 7;
+        const int rs = row < rmax ? row : rmax - 1;
+        sreg[t][j] = *reinterpret_cast<const bf16x8*>(src + rs * kD + ((slot ^ (row & 7)) << 3));
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's LDS writes from this wave have landed
-    __syncthreads();
-    buf ^= 1;
+    if constexpr (FOX) {
+      if (l < 16) sfl = fl[bh * Lp + n * kC + 16 * wave + l];
+    }
+  };
+  auto store = [&](int s) PA_INLINE {
+#pragma unroll
+    for (int t = 0; t < NM; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<bf16x8*>(lds[s][t] + (i0 + j) * 512 + 8 * l) = sreg[t][j];
+    if constexpr (FOX) {
+      if (l < 16) lfl[s][16 * wave + l] = sfl;
+    }
+  };
+  int cur = 0;
+  fetch(mtop);
+  store(0);
+  if (mtop >= 1) fetch(mtop - 1);
+  lds_barrier();
+  auto prefetch = [&](int64_t) PA_INLINE {};
+  auto advance = [&](int64_t n) PA_INLINE {
+    if (n >= 1) {
+      store(cur ^ 1);
+      if (n >= 2) fetch(n - 2);
+    }
+    lds_barrier();
+    cur ^= 1;
+  };
+#else
+  auto stage = [&](int64_t n, int s) PA_INLINE {
+#pragma unroll
+    for (int t = 0; t < NM; ++t) dma_tile(lds[s][t], chunk_src(n, t), chunk_rows(n, t), i0);
+    if constexpr (FOX) {
+      if (l < 16)
+        __builtin_amdgcn_global_load_lds((const void*)(fl + bh * Lp + n * kC + 16 * wave + l),
+                                         (lds_void*)(lfl[s] + 16 * wave), 4, 0, 0);
+    }
+  };
+
+  int cur = 0;
+  stage(mtop, 0);
+  if constexpr (NB == 3) {
+    if (mtop >= 1) {
+      stage(mtop - 1, 1);
+      wait_vm<OPS>();
+    } else {
+      wait_vm<0>();
+    }
+  } else {
+    wait_vm<0>();
   }
+  lds_barrier();
+  // With a 3-slot ring the copy of chunk n-2 is issued after the step's last LDS read (the compiler
+  // waits for outstanding copies before any LDS transpose read, so a copy issued earlier in the step
+  // would stall it); with 2 slots the copy of chunk n-1 has to go out first.
+  auto prefetch = [&](int64_t n) PA_INLINE {
+    if constexpr (NB == 2) {
+      if (n >= 1) stage(n - 1, cur ^ 1);
+    }
+  };
+  auto advance = [&](int64_t n) PA_INLINE {
+    if constexpr (NB == 3) {
+      if (n >= 2) {
+        stage(n - 2, cur == 0 ? 2 : cur - 1);
+        wait_vm<OPS>();  // chunk n-1 (issued one step earlier) has landed
+      } else {
+        wait_vm<0>();
+      }
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();
+    cur = (cur + 1 == NB) ? 0 : cur + 1;
+  };
+#endif
+  auto run_step = [&](auto next_tag, int64_t n) PA_INLINE {
+    if constexpr (FOX) off += ftot[bh * M + n];
+    step(next_tag, lds[cur][0], lds[cur][1], lds[cur][2], lds[cur][NM - 1], lfl[cur]);
+  };
+
+  // Head: the block's own query chunks mtop .. mlow.  A wave idles above its chunk, scores its own
+  // chunk from the in-chunk logits and steps below it.
+  const int64_t mlow = kCpb * p;
+  int64_t n = mtop;
+  for (; n >= mlow; --n) {
+    prefetch(n);
+    if (active && n == m) {
+      diag(lds[cur][1]);
+    } else if (active && n < m) {
+      if (n > 0)
+        run_step(std::true_type{}, n);
+      else
+        run_step(std::false_type{}, n);
+    }
+    advance(n);
+  }
+  // Body: every wave steps (a wave past the end of the sequence works on zero queries and stores
+  // nothing), so the loop has a single path.
+  for (; n >= 1; --n) {
+    prefetch(n);
+    run_step(std::true_type{}, n);
+    advance(n);
+  }
+  if (n == 0) run_step(std::false_type{}, 0);
 
   // ---------------------------------------------------------------- epilogue
 #pragma unroll
-  for (int qi = 0; qi < kQt; ++qi) {
+  for (int qi = 0; qi < QT; ++qi) {
     const float lt = colsum4(lsum[qi]);
     const int a = q0 + 16 * qi + r;
     const int64_t i = m * kC + a;
@@ -747,12 +960,13 @@ bool mfma_supported(int d, int chunk) { return d == kD && chunk == kC; }
 template <bool FOX, bool X3>
 static void launch_attn(dim3 grid, hipStream_t st, const __bf16* qt, const __bf16* qt_lo, const __bf16* kt,
                         const __bf16* v, const __bf16* p_hi, const __bf16* p_lo, const float* Sm, const float* fl,
-                        const float* ftot, __bf16* out, float* lse, int64_t L, int64_t M, int64_t BH, float sc) {
-  mfma_attn_kernel<FOX, X3><<<grid, 256, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, Sm, fl, ftot, out, lse, L, M, BH,
-                                                  sc);
+                        const float* ftot, __bf16* out, float* lse, int64_t L, int64_t M, int64_t BH) {
+  mfma_attn_kernel<FOX, X3, PATHATTN_SCAN_QT><<<grid, 256, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, Sm, fl, ftot, out,
+                                                                    lse, L, M, BH);
 }
 
 // phases: bit 0 = per-chunk prep, bit 1 = attention scan (reads what the prep left in the workspace).
+// The prep stores qtilde and the in-chunk logits multiplied by scale * log2(e).
 hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const void* k, const void* v,
                     const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH,
                     int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo,
@@ -766,19 +980,19 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
                             (int)kPrepLds);
     if (e != hipSuccess) return e;
     mfma_prep_kernel<<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
-        (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, (__bf16*)qt,
+        (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, scale * kLog2e, (__bf16*)qt,
         x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & 2) {
+    constexpr int kCpb = ScanShape<false, PATHATTN_SCAN_QT>::kCpb;
     const int64_t heads_per_xcd = (BH + kXcd - 1) / kXcd;
     const dim3 grid((unsigned)(kXcd * heads_per_xcd * ((M + kCpb - 1) / kCpb)));
-    const float sc = scale * kLog2e;
     const bool fox = logf != nullptr;
     auto args = [&](auto fn) {
       fn(grid, st, (const __bf16*)qt, (const __bf16*)qt_lo, (const __bf16*)kt, (const __bf16*)v,
-         (const __bf16*)p_hi, (const __bf16*)p_lo, Sm, fl, ftot, (__bf16*)out, lse, L, M, BH, sc);
+         (const __bf16*)p_hi, (const __bf16*)p_lo, Sm, fl, ftot, (__bf16*)out, lse, L, M, BH);
     };
     if (fox && x3) args(launch_attn<true, true>);
     else if (fox) args(launch_attn<true, false>);

@@ -32,7 +32,7 @@ template <typename T, int D, int C>
 __global__ __launch_bounds__(256) void vec_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const T* __restrict__ w, const float* __restrict__ beta,
                                                        const float* __restrict__ logf, int64_t L, int64_t M,
-                                                       float* __restrict__ qt, float* __restrict__ kt,
+                                                       float qscale, float* __restrict__ qt, float* __restrict__ kt,
                                                        float* __restrict__ Pm, float* __restrict__ Sm,
                                                        float* __restrict__ fl, float* __restrict__ ftot) {
   constexpr int CP = C + 1;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void vec_prep_kernel(const T* __restrict__ q, 
       for (int x = 0; x < D; ++x) sv += Qs[a * D + x] * Ks[b * D + x];
       for (int t = b + 1; t <= a; ++t) sv -= Ys[b * CP + t] * Us[t * CP + a];
     }
-    Sc[e] = sv;
+    Sc[e] = sv * qscale;
     const int s = e / C, aa = e % C;
     float xv = 0.f;
     for (int t = s; t <= aa; ++t) xv += Ti[s * CP + t] * Us[t * CP + aa];
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void vec_prep_kernel(const T* __restrict__ q, 
     for (int s = 0; s <= a; ++s) qv -= RX[s * CP + a] * Ws[s * D + x];
     for (int t = a + 1; t < C; ++t) kv -= Ys[a * CP + t] * Ws[t * D + x];
     for (int t = a; t < C; ++t) zv += Ti[a * CP + t] * Ws[t * D + x];
-    qtc[e] = qv;
+    qtc[e] = qv * qscale;
     ktc[e] = kv;
     Az[e] = zv;  // Z2[a][x]
   }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(C) void vec_attn_kernel(const float* __restrict__ q
                                                      const T* __restrict__ v, const float* __restrict__ Pm,
                                                      const float* __restrict__ Sm, const float* __restrict__ fl,
                                                      const float* __restrict__ ftot, T* __restrict__ out,
-                                                     float* __restrict__ lse, int64_t L, int64_t M, float scale) {
+                                                     float* __restrict__ lse, int64_t L, int64_t M) {
   __shared__ float Kl[C * D];
   __shared__ float Vl[C * D];
   __shared__ float Pl[D * D];
@@ -178,7 +178,6 @@ __global__ __launch_bounds__(C) void vec_attn_kernel(const float* __restrict__ q
   const int64_t Lp = M * C;
   const int64_t i = m * C + a;
   const bool fox = fl != nullptr;
-  const float sc = scale * kLog2e;
 
   float o[D], r[D], z[C];
   for (int x = 0; x < D; ++x) o[x] = 0.f;
@@ -210,7 +209,7 @@ __global__ __launch_bounds__(C) void vec_attn_kernel(const float* __restrict__ q
   stage_values(m);
   __syncthreads();
   const float* Srow = Sm + (((size_t)bh * M + m) * C + a) * C;
-  for (int b = 0; b < C; ++b) z[b] = (b <= a) ? sc * Srow[b] - (fox ? kLog2e * Fl[b] : 0.f) : -INFINITY;
+  for (int b = 0; b < C; ++b) z[b] = (b <= a) ? Srow[b] - (fox ? kLog2e * Fl[b] : 0.f) : -INFINITY;
   absorb();
 
   for (int x = 0; x < D; ++x) r[x] = qt[((size_t)bh * Lp + i) * D + x];
@@ -225,7 +224,7 @@ __global__ __launch_bounds__(C) void vec_attn_kernel(const float* __restrict__ q
     for (int b = 0; b < C; ++b) {
       float s = 0.f;
       for (int x = 0; x < D; ++x) s += Kl[b * D + x] * r[x];
-      z[b] = sc * s + (fox ? kLog2e * (off - Fl[b]) : 0.f);
+      z[b] = s + (fox ? kLog2e * (off - Fl[b]) : 0.f);
     }
     absorb();
     if (n > 0) {
@@ -267,14 +266,14 @@ static hipError_t launch_vec(int phases, const void* q, const void* k, const voi
     e = hipFuncSetAttribute((const void*)vec_prep_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
     if (e != hipSuccess) return e;
-    vec_prep_kernel<T, D, C><<<grid, 256, lds, st>>>((const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, qt,
-                                                    kt, Pm, Sm, fl, ftot);
+    vec_prep_kernel<T, D, C><<<grid, 256, lds, st>>>((const T*)q, (const T*)k, (const T*)w, beta, logf, L, M,
+                                                    scale * kLog2e, qt, kt, Pm, Sm, fl, ftot);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & 2) {
     vec_attn_kernel<T, D, C><<<grid, C, 0, st>>>(qt, kt, (const T*)v, Pm, Sm, logf ? fl : nullptr, ftot, (T*)out,
-                                                 lse, L, M, scale);
+                                                 lse, L, M);
     e = hipGetLastError();
   }
   return e;

@@ -60,8 +60,8 @@ def lib():
         L.path_attn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(WsLayout)]
         L.path_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32, vp, sz,
                                     vp]
-        L.path_attn_prep.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, sz, vp]
-        L.path_attn_scan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32, vp, sz, vp]
+        L.path_attn_prep.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32, vp, sz, vp]
+        L.path_attn_scan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, sz, vp]
         L.path_decode_workspace_bytes.argtypes = [i64, i64, i32, i64, i32, ctypes.POINTER(sz)]
         L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, f32, i32, i32,
                                        vp, sz, vp]
@@ -149,11 +149,14 @@ def path_attn_fwd(q, k, v, w, beta, log_forget=None, *, scale: Optional[float] =
     return out, lse
 
 
-def path_attn_prep(q, k, v, w, beta, log_forget=None, *, chunk: int = 64, transport: str = "bf16", workspace,
-                   stream=None) -> torch.Tensor:
-    """Per-chunk terms only (first phase of path_attn_fwd), written into `workspace`."""
+def path_attn_prep(q, k, v, w, beta, log_forget=None, *, scale: Optional[float] = None, chunk: int = 64,
+                   transport: str = "bf16", workspace, stream=None) -> torch.Tensor:
+    """Per-chunk terms only (first phase of path_attn_fwd), written into `workspace`; the logit
+    scale is folded into the stored queries and in-chunk logits."""
     _require(q, "q")
     B, H, L, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
     for name, t in (("k", k), ("v", v), ("w", w)):
         _require(t, name, q.dtype, q.shape)
     _require(beta, "beta", torch.float32, (B, H, L))
@@ -161,27 +164,25 @@ def path_attn_prep(q, k, v, w, beta, log_forget=None, *, chunk: int = 64, transp
         _require(log_forget, "log_forget", torch.float32, (B, H, L))
     _require(workspace, "workspace")
     _check("path_attn_prep", lib().path_attn_prep(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), B, H, L, d, chunk, DTYPE[q.dtype],
-        TRANSPORT[transport], _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), B, H, L, d, chunk, float(scale),
+        DTYPE[q.dtype], TRANSPORT[transport], _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return workspace
 
 
-def path_attn_scan(v, log_forget=None, *, scale: Optional[float] = None, chunk: int = 64, transport: str = "bf16",
-                   workspace, out=None, lse=None, stream=None,
-                   want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+def path_attn_scan(v, log_forget=None, *, chunk: int = 64, transport: str = "bf16", workspace, out=None, lse=None,
+                   stream=None, want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Attention scan from a workspace filled by path_attn_prep with the same arguments."""
     _require(v, "v")
     B, H, L, d = v.shape
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(v)
     if lse is None and want_lse:
         lse = torch.empty((B, H, L), device=v.device, dtype=torch.float32)
     _require(workspace, "workspace")
     _check("path_attn_scan", lib().path_attn_scan(
-        _ptr(v), _ptr(log_forget), _ptr(out), _ptr(lse), B, H, L, d, chunk, float(scale), DTYPE[v.dtype],
-        TRANSPORT[transport], _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(v), _ptr(log_forget), _ptr(out), _ptr(lse), B, H, L, d, chunk, DTYPE[v.dtype], TRANSPORT[transport],
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

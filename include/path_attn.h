@@ -105,7 +105,9 @@ path_status path_attn_fwd(const void* q, const void* k, const void* v, const voi
  * The two phases of path_attn_fwd, for callers that time or reuse them
  * separately.  path_attn_prep computes every chunk's compact-form terms into
  * the workspace (reads q, k, v, w, beta, log_forget; writes only the
- * workspace).  path_attn_scan runs the right-to-left attention scan from a
+ * workspace); the logit scale is applied here (the boundary-adjusted queries
+ * and in-chunk logits are stored multiplied by scale * log2(e)), so the scan
+ * takes no scale.  path_attn_scan runs the right-to-left attention scan from a
  * workspace that path_attn_prep filled with the SAME B, H, L, d, chunk, dtype,
  * transport and the same log_forget presence (non-NULL vs NULL); it reads v
  * and writes out and lse.  log_forget is only tested for NULL by
@@ -113,11 +115,11 @@ path_status path_attn_fwd(const void* q, const void* k, const void* v, const voi
  * by scan on the same stream.
  */
 path_status path_attn_prep(const void* q, const void* k, const void* v, const void* w, const float* beta,
-                           const float* log_forget, int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
-                           int transport, void* workspace, size_t workspace_bytes, void* stream);
+                           const float* log_forget, int64_t B, int64_t H, int64_t L, int d, int chunk, float scale,
+                           int dtype, int transport, void* workspace, size_t workspace_bytes, void* stream);
 
 path_status path_attn_scan(const void* v, const float* log_forget, void* out, float* lse, int64_t B, int64_t H,
-                           int64_t L, int d, int chunk, float scale, int dtype, int transport, void* workspace,
+                           int64_t L, int d, int chunk, int dtype, int transport, void* workspace,
                            size_t workspace_bytes, void* stream);
 
 /*
@@ -127,11 +129,12 @@ path_status path_attn_scan(const void* v, const float* log_forget, void* out, fl
  * `layout_id`:
  *   layout_id 0 (vector path): qtilde, ktilde [B*H, M*C, d] fp32; P [B*H, M, d, d] fp32
  *     (row-major, P = H_first ... H_last of the chunk); S [B*H, M, C, C] fp32 ([query][key],
- *     unscaled, lower triangle incl. diagonal).
+ *     lower triangle incl. diagonal).  qtilde and S are stored multiplied by scale * log2(e).
  *   layout_id 1 (matrix-core path): qtilde, ktilde [B*H, M*C, d] bf16 with columns permuted
  *     within each 32-wide block (stored slot 8g+j holds column 16(j/4)+4g+(j%4));
  *     qtilde_lo (bf16x3 transport only): the bf16 residual qtilde - qtilde_hi, same layout;
- *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S as layout 0.
+ *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S as layout 0;
+ *     qtilde (hi + lo) and S carry the factor scale * log2(e) as in layout 0.
  * M = ceil(L / chunk).
  */
 typedef struct {

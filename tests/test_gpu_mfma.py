@@ -12,6 +12,7 @@ from tests.gpu_util import assert_parity, errors, fwd_inputs_dev, host, TOL
 pytestmark = pytest.mark.gpu
 
 C, D = 64, 64
+LOG2E = 1.4426950408889634
 
 
 def perm_src():
@@ -58,7 +59,8 @@ def test_layout_is_matrix_core():
 
 @pytest.mark.parametrize("recipe", ["stress_qk", "beta2", "lm"])
 def test_chunk_intermediates(recipe):
-    """qtilde (hi+lo), ktilde, P (hi+lo) and S of every chunk against the oracle's by-definition terms."""
+    """qtilde (hi+lo), ktilde, P (hi+lo) and S of every chunk against the oracle's by-definition terms
+    (the workspace holds qtilde and S multiplied by scale * log2(e))."""
     B, H, L = 1, 2, 150
     x = synth.make_fwd_inputs(B, H, L, D, recipe=recipe, dtype="bf16", seed=11)
     print(f"[case] intermediates recipe={recipe}", flush=True)
@@ -81,15 +83,15 @@ def test_chunk_intermediates(recipe):
             q, k, w, v = (getattr(x, a)[b, h, rows].astype(np.float64) for a in ("q", "k", "w", "v"))
             beta = x.beta[b, h, rows].astype(np.float64)
             rq, rk, rs = oracle.chunk_terms(q, k, w, beta)
-            scale = max(1.0, np.abs(rq).max())
-            assert errors(qt[bh, c * C:c * C + n], rq)[0] <= 2 ** -14 * scale, f"qtilde (hi+lo) chunk {c}"
+            rq, rs = rq * x.scale * LOG2E, rs * x.scale * LOG2E
+            assert errors(qt[bh, c * C:c * C + n], rq)[0] <= 2 ** -14 * np.abs(rq).max(), f"qtilde (hi+lo) {c}"
             assert errors(kt[bh, c * C:c * C + n], rk)[0] <= 2 ** -7 * max(1.0, np.abs(rk).max()), f"ktilde {c}"
             # the padded tail of a ragged chunk holds identity transitions
             rp = oracle.householder_product(w, beta)
             ma, _ = errors(P[bh, c], rp)
             assert ma <= 2e-5, f"P chunk {c}: {ma:.2e}"
             ms, _ = errors(np.tril(S[bh, c, :n, :n]), np.tril(rs))
-            assert ms <= 2e-2 * max(1.0, np.abs(rs).max()), f"S chunk {c}: {ms:.2e}"
+            assert ms <= 2e-2 * max(x.scale * LOG2E, np.abs(rs).max()), f"S chunk {c}: {ms:.2e}"
 
 
 CASES = [
@@ -120,9 +122,9 @@ def test_prep_then_scan_equals_fwd(transport, fox):
     o1, l1 = native.path_attn_fwd(t["q"], t["k"], t["v"], t["w"], t["beta"], t["logf"], scale=x.scale, chunk=C,
                                   transport=transport, workspace=ws)
     ws2 = torch.zeros(n, device="cuda", dtype=torch.uint8)
-    native.path_attn_prep(t["q"], t["k"], t["v"], t["w"], t["beta"], t["logf"], chunk=C, transport=transport,
-                          workspace=ws2)
-    o2, l2 = native.path_attn_scan(t["v"], t["logf"], scale=x.scale, chunk=C, transport=transport, workspace=ws2)
+    native.path_attn_prep(t["q"], t["k"], t["v"], t["w"], t["beta"], t["logf"], scale=x.scale, chunk=C,
+                          transport=transport, workspace=ws2)
+    o2, l2 = native.path_attn_scan(t["v"], t["logf"], chunk=C, transport=transport, workspace=ws2)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
