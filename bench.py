@@ -55,6 +55,36 @@ def parse():
     return ap.parse_args()
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_B8_H24_L4096_d64_hbm_counters.md")
+DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_B32_H24_T65536_d64_hbm_counters.md")
+
+
+def kernel_digest(*sources):
+    """Digest of kernel sources (ties HBM counter readings to the code they measured)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sources + ("common.h",):
+        with open(os.path.join(ROOT, "dependent_positional_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(path, kernel, source):
+    """HBM bytes per launch (read + written) of `kernel` from a committed rocprofv3 counter summary,
+    or None when there is none or the kernel source has changed since the counters were taken."""
+    if not os.path.exists(path):
+        return None
+    digest = kernel_digest(source)
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic ") and f"kernel={kernel} " in line:
+                kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t and not t.startswith("kernel="))
+                if kv.get("source_digest") == digest:
+                    return float(kv["read_bytes"]) + float(kv["write_bytes"])
+    return None
+
+
 def prefill_flops(B, H, L, d, C):
     M = -(-L // C)
     return 4.0 * d * (L * (L + 1) / 2) * B * H + 2.0 * C * d * d * ((M - 1) * (M - 2) / 2) * B * H
@@ -213,7 +243,9 @@ def bench_decode(args):
             "config": {"workload": "decode batch 32 x 24 heads, d=64, bf16 cache of 65536 tokens growing by 1/step",
                        "batch": Bd, "heads": H, "d": d, "cache_tokens": T0},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(DECODE_COUNTERS, "decode_update_attend_kernel", "decode.hip"),
+                         "traffic_unit": "bytes per update+attend launch",
                          "kernel": "decode update+attend and combine, whole step"}}
 
 
@@ -259,7 +291,11 @@ def main():
                    "B": res["B"], "H": res["H"], "L": res["L"], "d": res["d"], "chunk": res["C"],
                    "transport": args.transport, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "mfma_attn_kernel",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(PREFILL_COUNTERS, "mfma_attn_kernel<{},{},2>".format(
+                         "true" if args.fox else "false", "true" if args.transport == "bf16x3" else "false"),
+                         "mfma_path.hip"),
+                     "traffic_unit": "bytes per launch", "kernel": "mfma_attn_kernel",
                      "launch_ms": res["ms_scan"], "flops_per_launch": F},
         "prefill_detail": {"ms_prep": res["ms_prep"], "ms_scan": res["ms_scan"], "wall_ms_per_step": res["wall_ms"],
                            "step_tflops": F / (res["ms_step"] * 1e-3) / 1e12,
