@@ -18,6 +18,9 @@ Also reported on the same JSON line:
   decode        batch 32, H=24, d=64, 65536 cached tokens, 128 steps timed back
                 to back: HBM bytes the step must move (cached keys read and
                 written back, cached values read) over the measured time.
+  long_context  B=1, H=24, L=32768: whole prefill step at chunk 64 and at
+                chunk 128 (transport once per 128 keys), tokens/s and the
+                fraction of bf16 peak for each chunk size's own flop count.
 """
 from __future__ import annotations
 
@@ -48,6 +51,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--decode-cache", type=int, default=65536)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the 32K-token prefill at chunk 64 and 128")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -188,6 +192,46 @@ def bench_cpu(x, args):
             "seconds": t}
 
 
+def bench_long(args):
+    """Long-context prefill (B=1, H=24, L=32768, d=64, bf16): chunk 64 and chunk 128, whole step."""
+    import torch
+    from dependent_positional_attention_amd import native, synth
+
+    B, H, L, d = 1, 24, 32768, 64
+    log(f"[bench] long context: generating inputs B={B} H={H} L={L} d={d}")
+    x = synth.make_fwd_inputs(B, H, L, d, recipe="lm", dtype="bf16", seed=0)
+
+    def dev_bf16(a):
+        return torch.from_numpy(synth.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+
+    q, k, v, w = (dev_bf16(getattr(x, n)) for n in ("q", "k", "v", "w"))
+    beta = torch.from_numpy(x.beta).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), device="cuda", dtype=torch.float32)
+    res = {}
+    for C in (64, 128):
+        nbytes = native.path_attn_fwd_workspace_bytes(B, H, L, d, C, torch.bfloat16, args.transport)
+        ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
+
+        def step():
+            native.path_attn_fwd(q, k, v, w, beta, None, scale=x.scale, chunk=C, transport=args.transport,
+                                 out=out, lse=lse, workspace=ws)
+
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        ms = timed(step, 5)
+        F = prefill_flops(B, H, L, d, C)
+        tf = F / (ms * 1e-3) / 1e12
+        log(f"[bench] long context chunk {C}: step {ms:.3f} ms, {B * L / (ms * 1e-3) / 1e6:.2f} M tokens/s, "
+            f"{tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak (whole step)")
+        res[f"chunk{C}"] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf,
+                            "frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+        del ws
+    return {"workload": "PaTH prefill, long context: B=1, H=24, L=32768, d=64, bf16, transport " + args.transport,
+            **res}
+
+
 def bench_decode(args):
     import numpy as np
     import torch
@@ -272,6 +316,7 @@ def main():
     res, x = bench_prefill(args)
     cpu = None if args.no_cpu else bench_cpu(x, args)
     dec = None if args.no_decode else bench_decode(args)
+    long_ctx = None if args.no_long else bench_long(args)
     F = res["flops"]
     achieved = F / (res["ms_scan"] * 1e-3) / 1e12
     line = {
@@ -302,6 +347,7 @@ def main():
                            "step_frac_of_peak": F / (res["ms_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
         "decode": dec,
+        "long_context": long_ctx,
     }
     print(json.dumps(line), flush=True)
 

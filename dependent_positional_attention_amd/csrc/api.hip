@@ -14,8 +14,8 @@ hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const
 bool mfma_supported(int d, int chunk);
 hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const void* k, const void* v,
                     const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH,
-                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, float* Sm,
-                    float* fl, float* ftot, hipStream_t st);
+                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, void* kt2,
+                    void* p2_hi, void* p2_lo, float* Sm, float* fl, float* ftot, hipStream_t st);
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
@@ -46,8 +46,11 @@ path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   const bool mfma = bf16 && mfma_supported(d, chunk);
   if (!mfma && !vec_supported(d, chunk)) return PATH_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
-  const int64_t M = (L + chunk - 1) / chunk;
-  const int64_t Lp = M * chunk;
+  const int64_t M2 = (L + chunk - 1) / chunk;
+  // the matrix-core path builds its per-chunk terms on 64-token (sub-)chunks
+  const int sub = mfma ? 64 : chunk;
+  const int64_t M = (L + sub - 1) / sub;
+  const int64_t Lp = M * sub;
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
     const int64_t o = off;
@@ -55,23 +58,30 @@ path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
     return o;
   };
   *lay = path_ws_layout{};
-  lay->num_chunks = M;
+  lay->num_chunks = M2;
+  lay->num_sub_chunks = M;
   lay->off_p_lo = -1;
   lay->off_qtilde_lo = -1;
+  lay->off_ktilde_c2 = lay->off_p_c2 = lay->off_p_c2_lo = -1;
   if (!mfma) {
     lay->layout_id = 0;
     lay->off_qtilde = take(BH * Lp * d * 4);
     lay->off_ktilde = take(BH * Lp * d * 4);
     lay->off_p = take(BH * M * d * d * 4);
   } else {
-    lay->layout_id = 1;
+    lay->layout_id = chunk == 128 ? 2 : 1;
     lay->off_qtilde = take(BH * Lp * d * 2);
     if (transport == PATH_TRANSPORT_BF16X3) lay->off_qtilde_lo = take(BH * Lp * d * 2);
     lay->off_ktilde = take(BH * Lp * d * 2);
     lay->off_p = take(BH * M * d * d * 2);
     if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_lo = take(BH * M * d * d * 2);
+    if (chunk == 128) {
+      lay->off_ktilde_c2 = take(BH * M2 * 64 * d * 2);
+      lay->off_p_c2 = take(BH * M2 * d * d * 2);
+      if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_c2_lo = take(BH * M2 * d * d * 2);
+    }
   }
-  lay->off_s = take(BH * M * (int64_t)chunk * chunk * 4);
+  lay->off_s = take(BH * M * (int64_t)sub * sub * 4);
   lay->off_fox_local = take(BH * Lp * 4);
   lay->off_fox_total = take(BH * M * 4);
   lay->total_bytes = off;
@@ -142,17 +152,18 @@ path_status run_fwd(int phases, const void* q, const void* k, const void* v, con
       misaligned(log_forget) || misaligned(out) || misaligned(lse) || misaligned(workspace))
     return PATH_ERR_UNSUPPORTED;
   if (workspace_bytes < (size_t)lay.total_bytes) return PATH_ERR_INVALID_ARG;
-  if (BH > kMaxGridY || lay.num_chunks > kMaxGridY) return PATH_ERR_UNSUPPORTED;
+  if (BH > kMaxGridY || lay.num_sub_chunks > kMaxGridY) return PATH_ERR_UNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* fl = reinterpret_cast<float*>(ws + lay.off_fox_local);
   float* ftot = reinterpret_cast<float*>(ws + lay.off_fox_total);
   float* Sm = reinterpret_cast<float*>(ws + lay.off_s);
-  if (lay.layout_id == 1) {
+  if (lay.layout_id >= 1) {
+    auto at = [&](int64_t o) -> void* { return o >= 0 ? ws + o : nullptr; };
     return from_hip(mfma_run(phases, chunk, transport, q, k, v, w, beta, log_forget, out, lse, BH, L, scale,
-                             ws + lay.off_qtilde, lay.off_qtilde_lo >= 0 ? ws + lay.off_qtilde_lo : nullptr,
-                             ws + lay.off_ktilde, ws + lay.off_p,
-                             lay.off_p_lo >= 0 ? ws + lay.off_p_lo : nullptr, Sm, fl, ftot, st));
+                             at(lay.off_qtilde), at(lay.off_qtilde_lo), at(lay.off_ktilde), at(lay.off_p),
+                             at(lay.off_p_lo), at(lay.off_ktilde_c2), at(lay.off_p_c2), at(lay.off_p_c2_lo), Sm, fl,
+                             ftot, st));
   }
   return from_hip(vec_run(phases, dtype == PATH_DTYPE_BF16, d, chunk, q, k, v, w, beta, log_forget, out, lse, BH, L,
                           scale, reinterpret_cast<float*>(ws + lay.off_qtilde),

@@ -1,4 +1,4 @@
-// Matrix-core (bf16 MFMA, fp32 accumulate) PaTH prefill for head dim 64, chunk 64.
+// Matrix-core (bf16 MFMA, fp32 accumulate) PaTH prefill for head dim 64, chunk 64 or 128.
 //
 // Scheme (PaTH summary, gist.science/ko/paper/2505.16381, section 3): each chunk's
 // transitions are held in compact UT form, H_0...H_{C-1} = I - W^T T^{-1} W; per
@@ -545,10 +545,11 @@ struct ScanShape {
 // The running max is raised lazily: a lane whose partial row sum exceeds 2^kRescale (so possibly
 // some p > 2^kRescale) sends the wave through the exact max, which raises the reference of any
 // column whose max exceeds it by more than kRescale and rescales O, the sums and the pending logits.
-template <bool FOX, bool X3, int QT, int W>
+template <bool FOX, bool X3, bool C2, int QT, int W>
 __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_attn_kernel(
     const __bf16* __restrict__ qt, const __bf16* __restrict__ qt_lo, const __bf16* __restrict__ kt,
     const __bf16* __restrict__ v, const __bf16* __restrict__ p_hi, const __bf16* __restrict__ p_lo,
+    const __bf16* __restrict__ kt2, const __bf16* __restrict__ p2_hi, const __bf16* __restrict__ p2_lo,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     __bf16* __restrict__ out, float* __restrict__ lse, int64_t L, int64_t M, int64_t BH) {
   using Sh = ScanShape<X3, QT, W>;
@@ -817,9 +818,16 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   // 1/W share of every tile (rows 8i.., i = kCp wave .. kCp wave + kCp - 1; lane l carries 16 B of
   // row 8i + l/8, written to slot l of the tile's i-th 1 KiB run) and of the prefix.
   const int i0 = kCp * wave;
+  const int64_t mlow = kCpb * p;  // lowest query chunk of the block
+  // With 128-token chunks (C2) the stream below the block's own chunks takes each 128-token chunk as
+  // two 64-token halves: the upper half with its own keys and no transport, the lower half with its
+  // keys carried through the upper half and the 128-token transport P_{2c} P_{2c+1}.
+  const int64_t M2 = (M + 1) >> 1;
   auto chunk_src = [&](int64_t n, int t) PA_INLINE -> const __bf16* {
-    if (t == 0) return kt + ((size_t)bh * Lp + n * kC) * kD;
+    const bool two = C2 && n < mlow && (n & 1) == 0;
+    if (t == 0) return two ? kt2 + ((size_t)bh * M2 + (n >> 1)) * kC * kD : kt + ((size_t)bh * Lp + n * kC) * kD;
     if (t == 1) return v + ((size_t)bh * L + n * kC) * kD;
+    if (two) return (t == 2 ? p2_hi : p2_lo) + ((size_t)bh * M2 + (n >> 1)) * kD * kD;
     return (t == 2 ? p_hi : p_lo) + ((size_t)bh * M + n) * kD * kD;
   };
   auto chunk_rows = [&](int64_t n, int t) PA_INLINE -> int {
@@ -878,7 +886,6 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
 
   // Head: the block's own query chunks mtop .. mlow.  A wave idles above its chunk, scores its own
   // chunk from the in-chunk logits and steps below it.
-  const int64_t mlow = kCpb * p;
   int64_t n = mtop;
   for (; n >= mlow; --n) {
     prefetch(n);
@@ -894,10 +901,28 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   }
   // Body: every wave steps (a wave past the end of the sequence works on zero queries and stores
   // nothing), so the loop has a single path.
-  for (; n >= 1; --n) {
-    prefetch(n);
-    run_step(std::true_type{}, n);
-    advance(n);
+  if constexpr (C2) {
+    // mlow is even: the body starts on an upper half (no transport), then its lower half
+    for (; n >= 3; n -= 2) {
+      prefetch(n);
+      run_step(std::false_type{}, n);
+      advance(n);
+      prefetch(n - 1);
+      run_step(std::true_type{}, n - 1);
+      advance(n - 1);
+    }
+    if (n == 1) {
+      prefetch(1);
+      run_step(std::false_type{}, 1);
+      advance(1);
+      n = 0;
+    }
+  } else {
+    for (; n >= 1; --n) {
+      prefetch(n);
+      run_step(std::true_type{}, n);
+      advance(n);
+    }
   }
   if (n == 0) run_step(std::false_type{}, 0);
 
@@ -1311,32 +1336,103 @@ __global__ __launch_bounds__(512, 2) void mfma_attn_pp_kernel(
   }
 }
 
+// =========================================================================== kernel 3: 128-token chunks
+// For chunk 128 the per-chunk terms are built on 64-token halves (kernel 1), and this kernel adds,
+// per 128-token chunk c, the two terms the scan needs below a query's own chunk:
+//   P_c2    = P_{2c} P_{2c+1}                      (the 128-token transition product)
+//   ktilde' = rows of ktilde_{2c} times P_{2c+1}   (keys of the lower half carried to the chunk end)
+// A missing upper half (ragged end) is the identity.  One block of 4 waves per (b, h, c); wave w owns
+// output columns y = 16w.. of both products, computed transposed so each lane writes 4 consecutive
+// stored columns.  bf16x3 operands (P hi + lo) enter as hi*hi + hi*lo + lo*hi.
+__global__ __launch_bounds__(256, 2) void mfma_merge_kernel(const __bf16* __restrict__ kt,
+                                                            const __bf16* __restrict__ p_hi,
+                                                            const __bf16* __restrict__ p_lo, int64_t M,
+                                                            __bf16* __restrict__ kt2, __bf16* __restrict__ p2_hi,
+                                                            __bf16* __restrict__ p2_lo) {
+  __shared__ __align__(1024) __bf16 t0h[kTile], t0l[kTile], t1h[kTile], t1l[kTile], tk[kTile];
+  const int64_t c = blockIdx.x, bh = blockIdx.y, M2 = (M + 1) >> 1;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, r = l & 15, g = l >> 4;
+  const bool x3 = p_lo != nullptr;
+  const bool upper = 2 * c + 1 < M;
+  const int64_t lo_c = 2 * c, hi_c = upper ? 2 * c + 1 : 2 * c;
+  const int i0 = 2 * wave;
+  dma_tile(t0h, p_hi + ((size_t)bh * M + lo_c) * kD * kD, kC, i0);
+  dma_tile(t1h, p_hi + ((size_t)bh * M + hi_c) * kD * kD, kC, i0);
+  dma_tile(tk, kt + ((size_t)bh * M * kC + lo_c * kC) * kD, kC, i0);
+  if (x3) {
+    dma_tile(t0l, p_lo + ((size_t)bh * M + lo_c) * kD * kD, kC, i0);
+    dma_tile(t1l, p_lo + ((size_t)bh * M + hi_c) * kD * kD, kC, i0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed
+  __syncthreads();
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const int y0 = 16 * wave + 4 * g;  // this lane's four output columns
+  const int ys = perm_pos(y0);       // their stored slots (contiguous)
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const int xr = 16 * jt + r;  // output row (x of P_c2, b of ktilde')
+    f32x4 dp = zero, dk = zero;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 ah = tr_frag(t1h, 16 * wave, ks, perm_col);  // P_{2c+1}[m][y], k over m
+      const bf16x8 bp = tile_frag(t0h, xr, 4 * ks + g);           // P_{2c}[x][m]
+      const bf16x8 bk = tile_frag(tk, xr, 4 * ks + g);            // ktilde_{2c}[b][m]
+      if (upper) {
+        dp = mfma16(ah, bp, dp);
+        dk = mfma16(ah, bk, dk);
+        if (x3) {
+          const bf16x8 al = tr_frag(t1l, 16 * wave, ks, perm_col);
+          dp = mfma16(ah, tile_frag(t0l, xr, 4 * ks + g), dp);
+          dp = mfma16(al, bp, dp);
+          dk = mfma16(al, bk, dk);
+        }
+      }
+    }
+    const size_t ob = ((size_t)bh * M2 + c) * kC * kD + (size_t)xr * kD + ys;
+    if (upper) {
+      bf16x4 h4, l4;
+      split4(dp[0], dp[1], dp[2], dp[3], h4, l4);
+      *reinterpret_cast<bf16x4*>(p2_hi + ob) = h4;
+      if (x3) *reinterpret_cast<bf16x4*>(p2_lo + ob) = l4;
+      *reinterpret_cast<bf16x4*>(kt2 + ob) = pack4(dk[0], dk[1], dk[2], dk[3]);
+    } else {  // identity upper half: copy
+      *reinterpret_cast<bf16x4*>(p2_hi + ob) = *reinterpret_cast<const bf16x4*>(t0h + swz(xr, ys >> 3) + (ys & 7));
+      if (x3) *reinterpret_cast<bf16x4*>(p2_lo + ob) = *reinterpret_cast<const bf16x4*>(t0l + swz(xr, ys >> 3) + (ys & 7));
+      *reinterpret_cast<bf16x4*>(kt2 + ob) = *reinterpret_cast<const bf16x4*>(tk + swz(xr, ys >> 3) + (ys & 7));
+    }
+  }
+}
+
 // =========================================================================== host
-bool mfma_supported(int d, int chunk) { return d == kD && chunk == kC; }
+bool mfma_supported(int d, int chunk) { return d == kD && (chunk == kC || chunk == 2 * kC); }
 
 #ifndef PATHATTN_SCAN_PINGPONG
 #define PATHATTN_SCAN_PINGPONG 0
 #endif
 
-template <bool FOX, bool X3>
+template <bool FOX, bool X3, bool C2>
 static void launch_attn(dim3 grid, hipStream_t st, const __bf16* qt, const __bf16* qt_lo, const __bf16* kt,
-                        const __bf16* v, const __bf16* p_hi, const __bf16* p_lo, const float* Sm, const float* fl,
+                        const __bf16* v, const __bf16* p_hi, const __bf16* p_lo, const __bf16* kt2,
+                        const __bf16* p2_hi, const __bf16* p2_lo, const float* Sm, const float* fl,
                         const float* ftot, __bf16* out, float* lse, int64_t L, int64_t M, int64_t BH) {
-  if (PATHATTN_SCAN_PINGPONG)
+  if constexpr (PATHATTN_SCAN_PINGPONG && !C2)
     mfma_attn_pp_kernel<FOX, X3><<<grid, 512, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, Sm, fl, ftot, out, lse, L, M, BH);
   else
-    mfma_attn_kernel<FOX, X3, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>
-        <<<grid, 64 * PATHATTN_SCAN_BLOCK_WAVES, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, Sm, fl, ftot, out, lse, L, M, BH);
+    mfma_attn_kernel<FOX, X3, C2, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>
+        <<<grid, 64 * PATHATTN_SCAN_BLOCK_WAVES, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, kt2, p2_hi, p2_lo, Sm, fl,
+                                                          ftot, out, lse, L, M, BH);
 }
 
 // phases: bit 0 = per-chunk prep, bit 1 = attention scan (reads what the prep left in the workspace).
-// The prep stores qtilde and the in-chunk logits multiplied by scale * log2(e).
+// The prep stores qtilde and the in-chunk logits multiplied by scale * log2(e).  Chunk 128 runs the
+// prep on 64-token halves and merges each pair (kernel 3) before the scan.
 hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const void* k, const void* v,
                     const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH,
-                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo,
-                    float* Sm, float* fl, float* ftot, hipStream_t st) {
-  if (chunk != kC) return hipErrorInvalidValue;
-  const int64_t M = (L + kC - 1) / kC;
+                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, void* kt2,
+                    void* p2_hi, void* p2_lo, float* Sm, float* fl, float* ftot, hipStream_t st) {
+  if (chunk != kC && chunk != 2 * kC) return hipErrorInvalidValue;
+  const bool c2 = chunk == 2 * kC;
+  const int64_t M = (L + kC - 1) / kC;  // 64-token (sub-)chunks
   const bool x3 = transport == 1;
   hipError_t e = hipSuccess;
   if (phases & 1) {
@@ -1348,20 +1444,39 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
         x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (c2) {
+      mfma_merge_kernel<<<dim3((unsigned)((M + 1) / 2), (unsigned)BH), 256, 0, st>>>(
+          (const __bf16*)kt, (const __bf16*)p_hi, x3 ? (const __bf16*)p_lo : nullptr, M, (__bf16*)kt2,
+          (__bf16*)p2_hi, x3 ? (__bf16*)p2_lo : nullptr);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (phases & 2) {
-    constexpr int kCpb = PATHATTN_SCAN_PINGPONG ? 4 : ScanShape<false, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>::kCpb;
+    constexpr int kCpb =
+        PATHATTN_SCAN_PINGPONG ? 4 : ScanShape<false, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>::kCpb;
+    static_assert(kCpb % 2 == 0, "blocks must cover whole 128-token chunks");
+    const int cpb = (PATHATTN_SCAN_PINGPONG && c2) ? ScanShape<false, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>::kCpb
+                                                   : kCpb;
     const int64_t heads_per_xcd = (BH + kXcd - 1) / kXcd;
-    const dim3 grid((unsigned)(kXcd * heads_per_xcd * ((M + kCpb - 1) / kCpb)));
+    const dim3 grid((unsigned)(kXcd * heads_per_xcd * ((M + cpb - 1) / cpb)));
     const bool fox = logf != nullptr;
     auto args = [&](auto fn) {
       fn(grid, st, (const __bf16*)qt, (const __bf16*)qt_lo, (const __bf16*)kt, (const __bf16*)v,
-         (const __bf16*)p_hi, (const __bf16*)p_lo, Sm, fl, ftot, (__bf16*)out, lse, L, M, BH);
+         (const __bf16*)p_hi, (const __bf16*)p_lo, (const __bf16*)kt2, (const __bf16*)p2_hi, (const __bf16*)p2_lo,
+         Sm, fl, ftot, (__bf16*)out, lse, L, M, BH);
     };
-    if (fox && x3) args(launch_attn<true, true>);
-    else if (fox) args(launch_attn<true, false>);
-    else if (x3) args(launch_attn<false, true>);
-    else args(launch_attn<false, false>);
+    if (c2) {
+      if (fox && x3) args(launch_attn<true, true, true>);
+      else if (fox) args(launch_attn<true, false, true>);
+      else if (x3) args(launch_attn<false, true, true>);
+      else args(launch_attn<false, false, true>);
+    } else {
+      if (fox && x3) args(launch_attn<true, true, false>);
+      else if (fox) args(launch_attn<true, false, false>);
+      else if (x3) args(launch_attn<false, true, false>);
+      else args(launch_attn<false, false, false>);
+    }
     e = hipGetLastError();
   }
   return e;

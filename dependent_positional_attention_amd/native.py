@@ -37,7 +37,9 @@ class WsLayout(ctypes.Structure):
     _fields_ = [("layout_id", ctypes.c_int), ("num_chunks", ctypes.c_int64), ("off_qtilde", ctypes.c_int64),
                 ("off_qtilde_lo", ctypes.c_int64), ("off_ktilde", ctypes.c_int64), ("off_p", ctypes.c_int64),
                 ("off_p_lo", ctypes.c_int64), ("off_s", ctypes.c_int64), ("off_fox_local", ctypes.c_int64),
-                ("off_fox_total", ctypes.c_int64), ("total_bytes", ctypes.c_int64)]
+                ("off_fox_total", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
+                ("num_sub_chunks", ctypes.c_int64), ("off_ktilde_c2", ctypes.c_int64), ("off_p_c2", ctypes.c_int64),
+                ("off_p_c2_lo", ctypes.c_int64)]
 
 
 EXPORTS = ("path_abi_version", "path_status_string", "path_attn_fwd_workspace_bytes", "path_attn_fwd",

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 1
+#define PATH_ABI_VERSION 2
 
 typedef enum {
   PATH_OK = 0,
@@ -92,9 +92,9 @@ path_status path_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d
  *                described by path_attn_workspace_layout
  *
  * Supported: dtype F32 with d in {16,32,64} and chunk in {16,32,64};
- * dtype BF16 with the same set, plus d = 64 with chunk 64 on the matrix-core
- * path.  Any L >= 0 (a ragged last chunk is padded internally with identity
- * transitions); B, H, L may be 0 (nothing is enqueued).
+ * dtype BF16 with the same set, plus d = 64 with chunk 64 or 128 on the
+ * matrix-core path.  Any L >= 0 (a ragged last chunk is padded internally with
+ * identity transitions); B, H, L may be 0 (nothing is enqueued).
  */
 path_status path_attn_fwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
                           const float* log_forget, void* out, float* lse, int64_t B, int64_t H, int64_t L,
@@ -135,13 +135,21 @@ path_status path_attn_scan(const void* v, const float* log_forget, void* out, fl
  *     qtilde_lo (bf16x3 transport only): the bf16 residual qtilde - qtilde_hi, same layout;
  *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S as layout 0;
  *     qtilde (hi + lo) and S carry the factor scale * log2(e) as in layout 0.
- * M = ceil(L / chunk).
+ *   layout_id 2 (matrix-core path, chunk 128): every term of layout 1 for the 64-token halves of
+ *     the chunks (C = 64, M = num_sub_chunks), plus per 128-token chunk c: ktilde_c2 [B*H, M2, 64, d]
+ *     bf16 = the first half's keys carried through the second half (ktilde_{2c} P_{2c+1} in row
+ *     form, columns permuted as ktilde) and P_c2 (hi) / P_c2_lo [B*H, M2, d, d] = P_{2c} P_{2c+1}
+ *     (layout of P), M2 = num_chunks.
+ * M = num_chunks = ceil(L / chunk); num_sub_chunks = ceil(L / 64) on the matrix-core path (else M);
+ * fields of terms a layout does not have are -1.
  */
 typedef struct {
   int layout_id;
   int64_t num_chunks;
   int64_t off_qtilde, off_qtilde_lo, off_ktilde, off_p, off_p_lo, off_s, off_fox_local, off_fox_total;
   int64_t total_bytes;
+  int64_t num_sub_chunks;
+  int64_t off_ktilde_c2, off_p_c2, off_p_c2_lo;
 } path_ws_layout;
 
 path_status path_attn_workspace_layout(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,

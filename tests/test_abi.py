@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 1
+    assert L.path_abi_version() == 2
     for s in range(4):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"
@@ -67,6 +67,23 @@ def test_workspace_planning(L):
     assert lay.num_chunks == 7 and lay.layout_id == 0 and lay.off_p_lo == -1 and lay.off_qtilde_lo == -1
     offs = [lay.off_qtilde, lay.off_ktilde, lay.off_p, lay.off_s, lay.off_fox_local, lay.off_fox_total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and lay.total_bytes >= offs[-1]
+    assert lay.num_sub_chunks == 7 and lay.off_ktilde_c2 == lay.off_p_c2 == lay.off_p_c2_lo == -1
+
+
+def test_workspace_planning_chunk128(L):
+    """Chunk 128 on the matrix-core path: 64-token halves plus the per-128-chunk merged terms."""
+    for transport in (0, 1):
+        lay = native.WsLayout()
+        assert L.path_attn_workspace_layout(2, 3, 300, 64, 128, BF16, transport, ctypes.byref(lay)) == OK
+        assert lay.layout_id == 2 and lay.num_chunks == 3 and lay.num_sub_chunks == 5
+        assert lay.off_ktilde_c2 >= 0 and lay.off_p_c2 >= 0 and (lay.off_p_c2_lo >= 0) == (transport == 1)
+        sizes = {lay.off_ktilde_c2: 6 * 3 * 64 * 64 * 2, lay.off_p_c2: 6 * 3 * 64 * 64 * 2}
+        for o, n in sizes.items():
+            assert o % 256 == 0 and o + n <= lay.total_bytes
+        st, n1 = ws_bytes(L, 2, 3, 300, 64, 128, BF16, transport)
+        assert st == OK and n1 == lay.total_bytes
+    assert ws_bytes(L, 1, 1, 300, 64, 128, F32, 0)[0] == UNSUPPORTED  # fp32 has no 128-token chunks
+    assert ws_bytes(L, 1, 1, 300, 32, 128, BF16, 0)[0] == UNSUPPORTED
 
 
 def fwd(L, q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=None, B=1, H=1, Lq=64, d=16,

@@ -112,6 +112,53 @@ def test_small_shapes(B, H, L, recipe, transport):
     assert_parity(gl, rl, "bf16", "lse")
 
 
+CASES_128 = [
+    (1, 2, 128, "lm", "bf16"), (2, 2, 300, "stress_qk", "bf16"), (1, 3, 64, "lm", "bf16"),
+    (1, 2, 700, "fox", "bf16x3"), (1, 3, 1000, "beta2", "bf16"), (1, 2, 513, "stress_qk_beta2", "bf16x3"),
+    (2, 2, 900, "fox", "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,L,recipe,transport", CASES_128)
+def test_small_shapes_chunk128(B, H, L, recipe, transport):
+    """128-token chunks: the scan moves queries once per 128 keys (lower-half keys pre-carried)."""
+    x = synth.make_fwd_inputs(B, H, L, D, recipe=recipe, dtype="bf16", seed=L + 1)
+    print(f"[case] mfma chunk 128 B={B} H={H} L={L} recipe={recipe} transport={transport}", flush=True)
+    go, gl = run(x, transport, chunk=128)
+    ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf, scale=x.scale)
+    assert_parity(go, ro, "bf16", "out")
+    assert_parity(gl, rl, "bf16", "lse")
+
+
+@pytest.mark.parametrize("transport", ["bf16", "bf16x3"])
+def test_chunk128_merged_terms(transport):
+    """P over each 128-token chunk and the lower half's keys carried to the chunk end, against the
+    oracle's explicit products / by-definition keys over the 128 tokens."""
+    B, H, L = 1, 2, 320  # 5 halves: chunks of 128, 128 and a lone 64-token half
+    x = synth.make_fwd_inputs(B, H, L, D, recipe="beta2", dtype="bf16", seed=3)
+    _, _, ws = run(x, transport, chunk=128, keep_ws=True)
+    lay = native.path_attn_workspace_layout(B, H, L, D, 128, torch.bfloat16, transport)
+    M2 = lay.num_chunks
+    assert lay.layout_id == 2 and M2 == 3 and lay.num_sub_chunks == 5
+    ph = ws_view(ws, lay.off_p_c2, B * H * M2 * D * D, torch.bfloat16).reshape(B * H, M2, D, D)
+    if transport == "bf16x3":
+        ph = ph + ws_view(ws, lay.off_p_c2_lo, B * H * M2 * D * D, torch.bfloat16).reshape(B * H, M2, D, D)
+    P2 = unpermute_cols(ph)
+    K2 = unpermute_cols(ws_view(ws, lay.off_ktilde_c2, B * H * M2 * 64 * D, torch.bfloat16).reshape(B * H, M2, 64, D))
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        for c in range(M2):
+            rows = slice(128 * c, min(128 * c + 128, L))
+            q, k, w = (getattr(x, a)[b, h, rows].astype(np.float64) for a in ("q", "k", "w"))
+            beta = x.beta[b, h, rows].astype(np.float64)
+            rp = oracle.householder_product(w, beta)
+            ma, _ = errors(P2[bh, c], rp)
+            assert ma <= (2e-5 if transport == "bf16x3" else 2e-2), f"P over 128 tokens, chunk {c}: {ma:.2e}"
+            _, rk, _ = oracle.chunk_terms(q, k, w, beta)  # keys carried to the end of the 128 tokens
+            n = min(64, rows.stop - rows.start)
+            assert errors(K2[bh, c, :n], rk[:n])[0] <= 2 ** -6 * max(1.0, np.abs(rk).max()), f"ktilde' {c}"
+
+
 @pytest.mark.parametrize("transport,fox", [("bf16", False), ("bf16x3", True)])
 def test_prep_then_scan_equals_fwd(transport, fox):
     """path_attn_prep followed by path_attn_scan is bit-identical to path_attn_fwd."""
@@ -146,17 +193,20 @@ def sampled_rows(L, seed=0):
     return np.unique(np.concatenate(blocks))
 
 
-@pytest.mark.parametrize("B,H,L,recipe,transport", [
-    (8, 24, 4096, "lm", "bf16"),         # 760M-class layer
-    (8, 24, 4096, "fox", "bf16"),        # PaTH-FoX at the same shape
-    (8, 24, 4096, "stress_qk", "bf16"),  # S1 at full shape
-    (1, 24, 32768, "lm", "bf16x3"),      # long-context extrapolation shape
-    (1, 24, 32768, "stress_qk_beta2", "bf16x3"),  # S1+S2: norm-preserving long-range transport
+@pytest.mark.parametrize("B,H,L,recipe,transport,chunk", [
+    (8, 24, 4096, "lm", "bf16", C),         # 760M-class layer
+    (8, 24, 4096, "fox", "bf16", C),        # PaTH-FoX at the same shape
+    (8, 24, 4096, "stress_qk", "bf16", C),  # S1 at full shape
+    (1, 24, 32768, "lm", "bf16x3", C),      # long-context extrapolation shape
+    (1, 24, 32768, "stress_qk_beta2", "bf16x3", C),  # S1+S2: norm-preserving long-range transport
+    (1, 24, 32768, "lm", "bf16x3", 128),    # long context, 128-token chunks
+    (1, 24, 32768, "stress_qk_beta2", "bf16x3", 128),
+    (8, 24, 4096, "stress_qk", "bf16", 128),
 ])
-def test_full_size_sampled_rows(B, H, L, recipe, transport):
-    print(f"[case] full B={B} H={H} L={L} recipe={recipe} transport={transport}", flush=True)
+def test_full_size_sampled_rows(B, H, L, recipe, transport, chunk):
+    print(f"[case] full B={B} H={H} L={L} recipe={recipe} transport={transport} chunk={chunk}", flush=True)
     x = synth.make_fwd_inputs(B, H, L, D, recipe=recipe, dtype="bf16", seed=0)
-    go, gl = run(x, transport)
+    go, gl = run(x, transport, chunk=chunk)
     rows = sampled_rows(L)
     ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf, scale=x.scale, rows=rows)
     assert_parity(go[:, :, rows], ro, "bf16", "out")
