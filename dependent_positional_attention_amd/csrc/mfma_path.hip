@@ -944,398 +944,6 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   }
 }
 
-// =========================================================================== kernel 2b: attention, ping-pong
-// Eight waves per block in two groups: waves 0-3 own query chunks 4p, 4p+1 and waves 4-7 own 4p+2,
-// 4p+3 (two waves of 32 queries per chunk), so every SIMD holds one wave of each group.  The key
-// stream advances in ticks separated by workgroup barriers; in each tick one group runs its
-// matrix-core phase and the other its vector phase, so a SIMD's matrix core is fed by one wave while
-// the other takes the exponentials.  For key chunk n (n = top ... 0, then -1):
-//   M(n): S^T_n = ktilde_n Q_run^T - m (+ FoX bias); O^T += V_{n+1}^T P_{n+1}^T; Q_run^T <- P_n Q_run^T
-//   V(n): p = exp2(S^T_n) with the lazy max check, row sums, P^T as the next PV operand
-// and on the own chunk m: M(m) prefetches the in-chunk logits and qtilde, V(m) scores them.  Group A
-// (waves 0-3) runs M(n) in tick 2j and V(n) in tick 2j+1 (n = top - j); group B one tick later.
-// Chunk n-1 is copied to LDS during tick 2j (group B at the start, in its vector phase; group A at
-// the end, after its last LDS transpose read) and waited for at the end of tick 2j+1.
-template <bool FOX, bool X3>
-__global__ __launch_bounds__(512, 2) void mfma_attn_pp_kernel(
-    const __bf16* __restrict__ qt, const __bf16* __restrict__ qt_lo, const __bf16* __restrict__ kt,
-    const __bf16* __restrict__ v, const __bf16* __restrict__ p_hi, const __bf16* __restrict__ p_lo,
-    const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
-    __bf16* __restrict__ out, float* __restrict__ lse, int64_t L, int64_t M, int64_t BH) {
-  constexpr int QT = 2, NM = X3 ? 4 : 3, NB = 3, kCpb = 4;
-  constexpr float kRescale = 8.f;     // log2 headroom before the running max must be raised
-  constexpr float kSumCap = 256.f;    // 2^kRescale
-  __shared__ __align__(1024) __bf16 lds[NB][NM][kTile];
-  __shared__ __align__(16) float lfl[NB][64];
-  // Own-chunk staging, one region per chunk parity (the own phases of chunks m and m - 1 overlap by
-  // a tick, those of m and m - 2 do not), one slice per wave of the chunk: the wave's 32 rows of the
-  // in-chunk logits and of qtilde, and the chunk's FoX prefix.
-  __shared__ __align__(16) float own_s[2][2][32 * kC];
-  __shared__ __align__(16) __bf16 own_q[2][2][32 * kD];
-  __shared__ __align__(16) float own_f[2][2][kC];
-
-  const int64_t nP = (M + kCpb - 1) / kCpb;
-  const int xcd = (int)(blockIdx.x % kXcd);
-  const int64_t slot = blockIdx.x / kXcd;
-  const int64_t heads_here = (BH - xcd + kXcd - 1) / kXcd;
-  if (slot >= heads_here * nP) return;  // whole block: this XCD has fewer heads
-  const int64_t grp_h = slot / (kHeadGroup * nP), in_grp = slot % (kHeadGroup * nP);
-  const int64_t grp_heads =
-      (heads_here - grp_h * kHeadGroup < kHeadGroup) ? heads_here - grp_h * kHeadGroup : kHeadGroup;
-  const int64_t bh = xcd + kXcd * (grp_h * kHeadGroup + in_grp % grp_heads);
-  const int64_t p = nP - 1 - in_grp / grp_heads;
-
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, r = l & 15,
-            g = l >> 4;
-  const int grp = wave >> 2;                   // 0: group A, 1: group B
-  const int64_t m = kCpb * p + (wave >> 1);    // this wave's query chunk
-  const int q0 = 32 * (wave & 1);              // first query (within the chunk) of this wave
-  const bool active = m < M;
-  const int64_t Lp = M * kC;
-  const int64_t mtop = (kCpb * p + kCpb - 1 < M - 1) ? kCpb * p + kCpb - 1 : M - 1;
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-
-  f32x4 o[4][QT];
-  float lsum[QT], mref[QT];
-  f32x4 negm[QT];
-  bf16x8 qb[QT][2], ql[QT][2];
-  f32x4 z[4][QT];              // logits awaiting the vector phase
-  bf16x8 pb[QT][2];            // P^T awaiting PV
-#pragma unroll
-  for (int a = 0; a < QT; ++a) {
-    mref[a] = 0.f;
-    lsum[a] = 0.f;
-    negm[a] = zero;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) o[b][a] = z[b][a] = zero;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) qb[a][b] = ql[a][b] = pb[a][b] = bf16x8{};
-  }
-  float off = 0.f;
-
-  // ---------------------------------------------------------------- step pieces
-  // Logits (log2 units, minus the running max) of a key chunk against the running queries, plus the
-  // PaTH-FoX bias sum_{s=j+1..i} f_s = (chunk-local prefix at i) + off - (prefix at j), whose
-  // row-constant first term cancels in the softmax (it returns in the lse).  kfrag(t, ks) gives the
-  // A-fragment of key rows 16t.., lf the chunk-local prefix of the key chunk.
-  auto logits = [&](auto kfrag, const float* lf, float offv, f32x4 (&z)[4][QT]) PA_INLINE {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 seed[QT];
-      if constexpr (FOX) {
-        const float4 f4 = *reinterpret_cast<const float4*>(lf + 16 * t + 4 * g);
-        const float fb[4] = {f4.x, f4.y, f4.z, f4.w};
-#pragma unroll
-        for (int qi = 0; qi < QT; ++qi)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) seed[qi][i] = __builtin_fmaf(kLog2e, offv - fb[i], negm[qi][i]);
-      } else {
-#pragma unroll
-        for (int qi = 0; qi < QT; ++qi) seed[qi] = negm[qi];
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = kfrag(t, ks);
-#pragma unroll
-        for (int qi = 0; qi < QT; ++qi) {
-          z[t][qi] = mfma16(a, qb[qi][ks], ks == 0 ? seed[qi] : z[t][qi]);
-          if constexpr (X3) z[t][qi] = mfma16(a, ql[qi][ks], z[t][qi]);  // logits see the query residual
-        }
-      }
-    }
-  };
-  auto lds_keys = [&](const __bf16* Kt_) PA_INLINE {
-    return [=](int t, int ks) PA_INLINE { return tile_frag(Kt_, 16 * t + r, 4 * ks + g); };
-  };
-  // Q_run^T <- P_n Q_run^T (fp32 accumulate).
-  auto transport = [&](const __bf16* Pt, const __bf16* Plt, f32x4 (&qn)[4][QT]) PA_INLINE {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int qi = 0; qi < QT; ++qi) qn[dt][qi] = zero;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = tile_frag(Pt, 16 * dt + r, 4 * ks + g);
-#pragma unroll
-        for (int qi = 0; qi < QT; ++qi) qn[dt][qi] = mfma16(a, qb[qi][ks], qn[dt][qi]);
-        if constexpr (X3) {
-          const bf16x8 alo = tile_frag(Plt, 16 * dt + r, 4 * ks + g);
-#pragma unroll
-          for (int qi = 0; qi < QT; ++qi) {
-            qn[dt][qi] = mfma16(a, ql[qi][ks], qn[dt][qi]);
-            qn[dt][qi] = mfma16(alo, qb[qi][ks], qn[dt][qi]);
-          }
-        }
-      }
-    }
-  };
-  // Accumulator tiles -> the logits' B-operand (bf16 hi [+ lo]).
-  auto requeue = [&](const f32x4 (&qn)[4][QT]) PA_INLINE {
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float vq = qn[2 * ks + (j >> 2)][qi][j & 3];
-          const __bf16 hi = (__bf16)vq;
-          qb[qi][ks][j] = hi;
-          if constexpr (X3) ql[qi][ks][j] = (__bf16)(vq - (float)hi);
-        }
-  };
-  // p = exp2(z - shift): this lane's partial row sums and P^T as the PV B-operand.
-  auto exps = [&](const f32x4 (&z)[4][QT], const float (&shift)[QT], bf16x8 (&pb)[QT][2], float (&ps)[QT]) PA_INLINE {
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(z[t][qi][i] - shift[qi]);
-          s = (t == 0 && i == 0) ? pv : s + pv;
-          pb[qi][t >> 1][4 * (t & 1) + i] = (__bf16)pv;
-        }
-      ps[qi] = s;
-    }
-  };
-  auto pv = [&](const __bf16* Vt, const bf16x8 (&pb)[QT][2]) PA_INLINE {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = vt_frag(Vt, dt, ks);
-#pragma unroll
-        for (int qi = 0; qi < QT; ++qi) o[dt][qi] = mfma16(a, pb[qi][ks], o[dt][qi]);
-      }
-  };
-  // Exact column max of z (relative to the reference); raise every column's reference to its max
-  // when some column exceeds it by more than kRescale.  Returns false when nothing moved.
-  auto raise_ref = [&](const f32x4 (&z)[4][QT], float (&d)[QT]) PA_INLINE {
-    bool up = false;
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-      float mx = max3(z[0][qi][0], z[0][qi][1], z[0][qi][2]);
-      mx = max3(mx, z[0][qi][3], z[1][qi][0]);
-      mx = max3(mx, z[1][qi][1], z[1][qi][2]);
-      mx = max3(mx, z[1][qi][3], z[2][qi][0]);
-      mx = max3(mx, z[2][qi][1], z[2][qi][2]);
-      mx = max3(mx, z[2][qi][3], z[3][qi][0]);
-      mx = max3(mx, z[3][qi][1], z[3][qi][2]);
-      mx = max2(mx, z[3][qi][3]);
-      d[qi] = max2(colmax4(mx), 0.f);
-      up |= d[qi] > kRescale;
-    }
-    if (!__any(up)) return false;
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-      const float alpha = fast_exp2(-d[qi]);
-      mref[qi] += d[qi];
-      negm[qi] = f32x4{-mref[qi], -mref[qi], -mref[qi], -mref[qi]};
-      lsum[qi] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt][qi] *= alpha;
-    }
-    return true;
-  };
-
-  auto slot_of = [&](int64_t n) PA_INLINE { return (int)((mtop - n) % NB); };
-  auto chunk_src = [&](int64_t n, int t) PA_INLINE -> const __bf16* {
-    if (t == 0) return kt + ((size_t)bh * Lp + n * kC) * kD;
-    if (t == 1) return v + ((size_t)bh * L + n * kC) * kD;
-    return (t == 2 ? p_hi : p_lo) + ((size_t)bh * M + n) * kD * kD;
-  };
-  auto chunk_rows = [&](int64_t n, int t) PA_INLINE -> int {
-    const int64_t vrows = L - n * kC;
-    return (t == 1 && vrows < kC) ? (int)vrows : kC;
-  };
-  // This wave's eighth of key chunk n: one 1 KiB run of every tile and 8 floats of the FoX prefix.
-  auto stage_share = [&](int64_t n) PA_INLINE {
-    const int s = slot_of(n);
-#pragma unroll
-    for (int t = 0; t < NM; ++t) dma_tile<1>(lds[s][t], chunk_src(n, t), chunk_rows(n, t), wave);
-    if constexpr (FOX) {
-      if (l < 8)
-        __builtin_amdgcn_global_load_lds((const void*)(fl + bh * Lp + n * kC + 8 * wave + l),
-                                         (lds_void*)(lfl[s] + 8 * wave), 4, 0, 0);
-    }
-  };
-
-  // Own chunk, matrix-core slot: copy the wave's rows of the in-chunk logits and of qtilde and the
-  // chunk's FoX prefix into its LDS slice (contiguous 1 KiB runs, 16 B a lane).
-  const int oreg = (int)(m & 1), oslice = wave & 1;
-  auto own_fetch = [&]() PA_INLINE {
-    const char* sg = reinterpret_cast<const char*>(Sm + (((size_t)bh * M + m) * kC + q0) * kC);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(sg + 1024 * i + 16 * l),
-                                       (lds_void*)(own_s[oreg][oslice] + 256 * i), 16, 0, 0);
-    const char* qg = reinterpret_cast<const char*>(qt + ((size_t)bh * Lp + m * kC + q0) * kD);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(qg + 1024 * i + 16 * l),
-                                       (lds_void*)(own_q[oreg][oslice] + 512 * i), 16, 0, 0);
-    if constexpr (FOX)
-      __builtin_amdgcn_global_load_lds((const void*)(fl + bh * Lp + m * kC + l), (lds_void*)own_f[oreg][oslice],
-                                       4, 0, 0);
-  };
-  // Own chunk, vector slot: masked in-chunk logits, exact max, P^T for PV; the running queries start
-  // at qtilde.
-  auto own_score = [&]() PA_INLINE {
-    wait_vm<0>();  // this wave's own-chunk copies have landed (nobody else reads them)
-    const float* sl = own_s[oreg][oslice];
-    f32x4 zz[4][QT];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float fb[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (FOX) {
-        const float4 f4 = *reinterpret_cast<const float4*>(own_f[oreg][oslice] + 16 * t + 4 * g);
-        fb[0] = kLog2e * f4.x, fb[1] = kLog2e * f4.y, fb[2] = kLog2e * f4.z, fb[3] = kLog2e * f4.w;
-      }
-#pragma unroll
-      for (int qi = 0; qi < QT; ++qi) {
-        const int a = q0 + 16 * qi + r;
-        const float4 s4 = *reinterpret_cast<const float4*>(sl + (16 * qi + r) * kC + 16 * t + 4 * g);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zz[t][qi][i] = (16 * t + 4 * g + i <= a) ? sv[i] - fb[i] : -INFINITY;
-      }
-    }
-    float shift[QT], ps[QT];
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        mx = max3(mx, max2(zz[t][qi][0], zz[t][qi][1]), max2(zz[t][qi][2], zz[t][qi][3]));
-      mref[qi] = colmax4(mx);  // finite: key a itself is never masked
-      negm[qi] = f32x4{-mref[qi], -mref[qi], -mref[qi], -mref[qi]};
-      shift[qi] = mref[qi];
-    }
-    exps(zz, shift, pb, ps);
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) {
-      lsum[qi] = ps[qi];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int e = (16 * qi + r) * kD + 32 * ks + 8 * g;
-        qb[qi][ks] = *reinterpret_cast<const bf16x8*>(own_q[oreg][oslice] + e);
-        if constexpr (X3)  // the residual comes straight from global memory (only the bf16x3 transport)
-          ql[qi][ks] = *reinterpret_cast<const bf16x8*>(qt_lo + ((size_t)bh * Lp + m * kC + q0) * kD + e);
-      }
-    }
-  };
-  // Matrix-core phase for chunk n < m (n = -1: only the last PV).
-  auto m_phase = [&](int64_t n) PA_INLINE {
-    if (n >= 0) {
-      const int s = slot_of(n);
-      if constexpr (FOX) off += ftot[bh * M + n];
-      logits(lds_keys(lds[s][0]), lfl[s], off, z);
-      if (n > 0) {
-        f32x4 qm[4][QT];
-        transport(lds[s][2], lds[s][NM - 1], qm);
-        pv(lds[slot_of(n + 1)][1], pb);
-        requeue(qm);  // the transport has drained behind PV
-        return;
-      }
-    }
-    pv(lds[slot_of(n + 1)][1], pb);
-  };
-  // Vector phase for chunk 0 <= n < m.
-  auto v_phase = [&](int64_t n) PA_INLINE {
-    const float none[QT] = {};
-    float ps[QT];
-    exps(z, none, pb, ps);
-    bool big = false;
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) big |= ps[qi] > kSumCap;
-    if (__any(big)) {  // rare: some p may exceed 2^kRescale
-      float d[QT];
-      if (raise_ref(z, d)) exps(z, d, pb, ps);
-    }
-#pragma unroll
-    for (int qi = 0; qi < QT; ++qi) lsum[qi] += ps[qi];
-  };
-
-  // ---------------------------------------------------------------- tick loop
-#pragma unroll
-  for (int t = 0; t < NM; ++t) dma_tile<1>(lds[slot_of(mtop)][t], chunk_src(mtop, t), chunk_rows(mtop, t), wave);
-  if constexpr (FOX) {
-    if (l < 8)
-      __builtin_amdgcn_global_load_lds((const void*)(fl + bh * Lp + mtop * kC + 8 * wave + l),
-                                       (lds_void*)(lfl[slot_of(mtop)] + 8 * wave), 4, 0, 0);
-  }
-  wait_vm<0>();
-  lds_barrier();
-  // Stream upkeep around a tick: chunk nb - 1 goes to LDS during the even tick of each pair (group B
-  // first, group A after its M phase) and has landed by the end of the odd tick.
-  const int ticks = 2 * (int)mtop + 4;
-  auto tick_begin = [&](int tau) PA_INLINE {
-    const int64_t nb = mtop - (tau >> 1);
-    if ((tau & 1) == 0 && grp == 1 && nb >= 1) stage_share(nb - 1);
-  };
-  auto tick_end = [&](int tau) PA_INLINE {
-    const int64_t nb = mtop - (tau >> 1);
-    if ((tau & 1) == 0 && grp == 0 && nb >= 1) stage_share(nb - 1);
-    if (tau & 1) wait_vm<0>();
-    lds_barrier();
-  };
-  // Head: ticks that include the waves' own chunks (the last own-chunk phase is group B's vector
-  // phase on the block's lowest chunk).
-  const int64_t mlow = kCpb * p;
-  const int head = (int)(2 * (mtop - mlow) + 3) < ticks ? (int)(2 * (mtop - mlow) + 3) : ticks;
-  int tau = 0;
-  for (; tau < head; ++tau) {
-    tick_begin(tau);
-    const int tl = tau - grp;
-    if (active && tl >= 0) {
-      const int64_t n = mtop - (tl >> 1);
-      if ((tl & 1) == 0) {
-        if (n == m)
-          own_fetch();
-        else if (n < m)
-          m_phase(n);
-      } else {
-        if (n == m) {
-          own_score();
-        } else if (n < m && n >= 0) {
-          v_phase(n);
-        }
-      }
-    }
-    tick_end(tau);
-  }
-  // Body: every wave is past its own chunk (a wave without a chunk works on zero state and stores
-  // nothing), so each tick is one M or V phase.
-  for (; tau < ticks; ++tau) {
-    tick_begin(tau);
-    const int tl = tau - grp;
-    const int64_t n = mtop - (tl >> 1);
-    if ((tl & 1) == 0)
-      m_phase(n);
-    else if (n >= 0)
-      v_phase(n);
-    tick_end(tau);
-  }
-
-  // ---------------------------------------------------------------- epilogue
-#pragma unroll
-  for (int qi = 0; qi < QT; ++qi) {
-    const float lt = colsum4(lsum[qi]);
-    const int a = q0 + 16 * qi + r;
-    const int64_t i = m * kC + a;
-    if (active && i < L) {
-      const float inv = 1.f / lt;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        *reinterpret_cast<bf16x4*>(out + ((size_t)bh * L + i) * kD + 16 * dt + 4 * g) =
-            pack4(o[dt][qi][0] * inv, o[dt][qi][1] * inv, o[dt][qi][2] * inv, o[dt][qi][3] * inv);
-      if (lse != nullptr && g == 0)
-        lse[bh * L + i] = (mref[qi] + fast_log2(lt)) * kLn2 + (FOX ? fl[bh * Lp + i] : 0.f);
-    }
-  }
-}
-
 // =========================================================================== kernel 3: 128-token chunks
 // For chunk 128 the per-chunk terms are built on 64-token halves (kernel 1), and this kernel adds,
 // per 128-token chunk c, the two terms the scan needs below a query's own chunk:
@@ -1406,21 +1014,14 @@ __global__ __launch_bounds__(256, 2) void mfma_merge_kernel(const __bf16* __rest
 // =========================================================================== host
 bool mfma_supported(int d, int chunk) { return d == kD && (chunk == kC || chunk == 2 * kC); }
 
-#ifndef PATHATTN_SCAN_PINGPONG
-#define PATHATTN_SCAN_PINGPONG 0
-#endif
-
 template <bool FOX, bool X3, bool C2>
 static void launch_attn(dim3 grid, hipStream_t st, const __bf16* qt, const __bf16* qt_lo, const __bf16* kt,
                         const __bf16* v, const __bf16* p_hi, const __bf16* p_lo, const __bf16* kt2,
                         const __bf16* p2_hi, const __bf16* p2_lo, const float* Sm, const float* fl,
                         const float* ftot, __bf16* out, float* lse, int64_t L, int64_t M, int64_t BH) {
-  if constexpr (PATHATTN_SCAN_PINGPONG && !C2)
-    mfma_attn_pp_kernel<FOX, X3><<<grid, 512, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, Sm, fl, ftot, out, lse, L, M, BH);
-  else
-    mfma_attn_kernel<FOX, X3, C2, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>
-        <<<grid, 64 * PATHATTN_SCAN_BLOCK_WAVES, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, kt2, p2_hi, p2_lo, Sm, fl,
-                                                          ftot, out, lse, L, M, BH);
+  mfma_attn_kernel<FOX, X3, C2, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>
+      <<<grid, 64 * PATHATTN_SCAN_BLOCK_WAVES, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, kt2, p2_hi, p2_lo, Sm, fl, ftot,
+                                                        out, lse, L, M, BH);
 }
 
 // phases: bit 0 = per-chunk prep, bit 1 = attention scan (reads what the prep left in the workspace).
@@ -1453,13 +1054,10 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
     }
   }
   if (phases & 2) {
-    constexpr int kCpb =
-        PATHATTN_SCAN_PINGPONG ? 4 : ScanShape<false, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>::kCpb;
+    constexpr int kCpb = ScanShape<false, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>::kCpb;
     static_assert(kCpb % 2 == 0, "blocks must cover whole 128-token chunks");
-    const int cpb = (PATHATTN_SCAN_PINGPONG && c2) ? ScanShape<false, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>::kCpb
-                                                   : kCpb;
     const int64_t heads_per_xcd = (BH + kXcd - 1) / kXcd;
-    const dim3 grid((unsigned)(kXcd * heads_per_xcd * ((M + cpb - 1) / cpb)));
+    const dim3 grid((unsigned)(kXcd * heads_per_xcd * ((M + kCpb - 1) / kCpb)));
     const bool fox = logf != nullptr;
     auto args = [&](auto fn) {
       fn(grid, st, (const __bf16*)qt, (const __bf16*)qt_lo, (const __bf16*)kt, (const __bf16*)v,
