@@ -725,22 +725,41 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   };
 
   // Own chunk: logits from the in-chunk S (already in log2 units), exact max, P^T V_m; then the
-  // running queries start at qtilde.
-  auto diag = [&](const __bf16* Vt_) PA_INLINE {
+  // running queries start at qtilde.  The in-chunk logits, FoX prefix and qtilde rows are fetched
+  // into registers at the block's start (own_load), while the first key chunk streams in.
+  float4 own_s[4][QT], own_f[4];
+  bf16x8 own_q[QT][2], own_ql[QT][2];
+  auto own_load = [&]() PA_INLINE {
     const float* Sb = Sm + ((size_t)bh * M + m) * kC * kC;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (FOX) own_f[t] = *reinterpret_cast<const float4*>(fl + bh * Lp + m * kC + 16 * t + 4 * g);
+#pragma unroll
+      for (int qi = 0; qi < QT; ++qi)
+        own_s[t][qi] = *reinterpret_cast<const float4*>(Sb + (q0 + 16 * qi + r) * kC + 16 * t + 4 * g);
+    }
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const size_t qo = ((size_t)bh * Lp + m * kC + q0 + 16 * qi + r) * kD + 32 * ks + 8 * g;
+        own_q[qi][ks] = *reinterpret_cast<const bf16x8*>(qt + qo);
+        if constexpr (X3) own_ql[qi][ks] = *reinterpret_cast<const bf16x8*>(qt_lo + qo);
+      }
+  };
+  auto diag = [&](const __bf16* Vt_) PA_INLINE {
     f32x4 z[4][QT];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float fb[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (FOX) {
-        const float4 f4 = *reinterpret_cast<const float4*>(fl + bh * Lp + m * kC + 16 * t + 4 * g);
-        fb[0] = kLog2e * f4.x, fb[1] = kLog2e * f4.y, fb[2] = kLog2e * f4.z, fb[3] = kLog2e * f4.w;
+        fb[0] = kLog2e * own_f[t].x, fb[1] = kLog2e * own_f[t].y, fb[2] = kLog2e * own_f[t].z,
+        fb[3] = kLog2e * own_f[t].w;
       }
 #pragma unroll
       for (int qi = 0; qi < QT; ++qi) {
         const int a = q0 + 16 * qi + r;
-        const float4 s4 = *reinterpret_cast<const float4*>(Sb + a * kC + 16 * t + 4 * g);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+        const float sv[4] = {own_s[t][qi].x, own_s[t][qi].y, own_s[t][qi].z, own_s[t][qi].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[t][qi][i] = (16 * t + 4 * g + i <= a) ? sv[i] - fb[i] : -INFINITY;
       }
@@ -764,9 +783,8 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
     for (int qi = 0; qi < QT; ++qi)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const size_t qo = ((size_t)bh * Lp + m * kC + q0 + 16 * qi + r) * kD + 32 * ks + 8 * g;
-        qb[qi][ks] = *reinterpret_cast<const bf16x8*>(qt + qo);
-        if constexpr (X3) ql[qi][ks] = *reinterpret_cast<const bf16x8*>(qt_lo + qo);
+        qb[qi][ks] = own_q[qi][ks];
+        if constexpr (X3) ql[qi][ks] = own_ql[qi][ks];
       }
   };
 
@@ -845,6 +863,9 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   };
 
   int cur = 0;
+  // The own-chunk loads go out first, so waiting for the first key chunk covers them too.
+  if (active) own_load();
+  __asm__ __volatile__("" ::: "memory");  // keep them ahead of the copies in issue order
   stage(mtop, 0);
   if constexpr (NB == 3) {
     if (mtop >= 1) {
@@ -887,7 +908,9 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   // Head: the block's own query chunks mtop .. mlow.  A wave idles above its chunk, scores its own
   // chunk from the in-chunk logits and steps below it.
   int64_t n = mtop;
-  for (; n >= mlow; --n) {
+#pragma unroll
+  for (int it = 0; it < kCpb; ++it, --n) {
+    if (n < mlow) break;
     prefetch(n);
     if (active && n == m) {
       diag(lds[cur][1]);
