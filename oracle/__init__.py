@@ -51,9 +51,10 @@ def lib():
         L.path_oracle_ut_tinv.argtypes = [_D, _D, _I64, _I64, _D]
         L.path_oracle_householder_product.argtypes = [_D, _D, _I64, _I64, _D]
         L.path_oracle_chunk_terms.argtypes = [_D, _D, _D, _D, _I64, _I64, _D, _D, _D]
+        L.path_oracle_cache_keys.argtypes = [_D, _D, _D, _I64, _I64, _I64, _I64, _D]
         for f in ("path_oracle_fwd", "path_oracle_row_logits", "path_oracle_transport",
                   "path_oracle_decode", "path_oracle_ut_tinv", "path_oracle_householder_product",
-                  "path_oracle_chunk_terms"):
+                  "path_oracle_chunk_terms", "path_oracle_cache_keys"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -166,3 +167,18 @@ def chunk_terms(q, k, W, beta):
     _check(lib().path_oracle_chunk_terms(_p(q), _p(k), _p(W), _p(beta), n, d, _p(qt), _p(kt), _p(s)),
            "path_oracle_chunk_terms")
     return qt, kt, s
+
+
+def cache_keys(K, W, beta, rows=None):
+    """Key cache slots after a prompt of L tokens: slot j = H_{L-1} ... H_{j+1} k_j.
+
+    K, W: [L, d]; beta: [L] (one batch/head).  rows: optional (j0, j1) range; default all.
+    Returns [(j1 - j0), d] float64.
+    """
+    K, W, beta = map(_f64, (K, W, beta))
+    L, d = K.shape
+    j0, j1 = (0, L) if rows is None else rows
+    out = np.zeros((max(j1 - j0, 0), d))
+    _check(lib().path_oracle_cache_keys(_p(K), _p(W), _p(beta), L, d, j0, j1, _p(out)),
+           "path_oracle_cache_keys")
+    return out

@@ -250,6 +250,27 @@ int path_oracle_decode(double* kc, double* vc, int64_t BH, int64_t cap, int64_t 
   return rc;
 }
 
+/* ------------------------------------------------------------------ prefill -> decode cache */
+
+/*
+ * Key cache after a prompt of L tokens (summary, section 3, inference rule): once the
+ * prompt has been consumed, every cached key has taken each later transition in
+ * place, so slot j holds H_{L-1} ... H_{j+2} H_{j+1} k_j (H_{j+1} applied first;
+ * slot L-1 holds k_{L-1} itself).  Then q^T slot_j = k_j^T H_{j+1} ... H_{L-1} q, the
+ * unscaled logit a query at position L-1 gives key j.
+ * K, W: [L, d]; beta: [L].  Writes rows j0 .. j1-1 of the cache into out [(j1 - j0), d].
+ */
+int path_oracle_cache_keys(const double* K, const double* W, const double* beta, int64_t L, int64_t d,
+                           int64_t j0, int64_t j1, double* out) {
+  if (L < 0 || d <= 0 || j0 < 0 || j1 < j0 || j1 > L) return ORACLE_EINVAL;
+  for (int64_t j = j0; j < j1; ++j) {
+    double* r = out + (j - j0) * d;
+    memcpy(r, K + j * d, (size_t)d * sizeof(double));
+    for (int64_t s = j + 1; s < L; ++s) apply_h(r, W + s * d, beta[s], d);
+  }
+  return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------ chunk quantities */
 
 /*

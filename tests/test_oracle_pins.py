@@ -14,6 +14,8 @@ P7  chunked     boundary-adjusted rows + right-to-left chunk scan reproduce the 
 P8  special     row 0, constant values, f = 0, closed-form FoX bias with beta = 0
 P9  decode      in-place key updates (summary, section 3 "inference") == prefill rows
 P10 mutations   plausible mistakes planted in a copy of the oracle make the pins fail
+P11 cache       key cache after a prompt (summary, section 3 "inference"): explicit products,
+                last-row logits, the decode recurrence, norms under beta = 2
 """
 import ctypes
 import json
@@ -461,3 +463,84 @@ def test_p10_planted_mistakes_are_caught(oracle_lib, name, monkeypatch):
             except AssertionError:
                 failures += 1
         assert failures >= 1, f"mutation {name} slipped through every pin"
+
+
+# ----------------------------------------------------------------------------- P11
+
+def _explicit_cache(k, w, beta):
+    """slot j = H_{L-1} ... H_{j+1} k_j from explicit d x d matrices."""
+    L, d = k.shape
+    out = np.zeros_like(k)
+    for j in range(L):
+        M = np.eye(d)
+        for s in range(L - 1, j, -1):
+            M = M @ H(w[s], beta[s])
+        out[j] = M @ k[j]
+    return out
+
+
+@pytest.mark.parametrize("L,d,beta_mode", [(1, 4, "sigmoid"), (9, 5, "sigmoid"), (17, 8, "two"), (6, 3, "zero")])
+def test_p11_cache_keys_explicit_products(oracle_lib, L, d, beta_mode):
+    q, k, v, w, beta, _ = rand_problem(L, d, 40 + L, beta_mode=beta_mode)
+    got = oracle_lib.cache_keys(k, w, beta)
+    assert_close(got, _explicit_cache(k, w, beta), 1e-12, "cache keys")
+    if beta_mode == "zero":
+        assert_close(got, k, 0.0, "beta = 0 keeps the keys")
+    if beta_mode == "two":  # reflections keep norms
+        assert_close(np.linalg.norm(got, axis=1), np.linalg.norm(k, axis=1), 1e-12, "norms")
+    # a row range equals the matching slice of the full cache
+    if L > 2:
+        assert_close(oracle_lib.cache_keys(k, w, beta, rows=(1, L - 1)), got[1:L - 1], 0.0, "row range")
+
+
+def test_p11_cache_keys_give_last_row_logits(oracle_lib):
+    L, d, scale = 23, 6, 0.7
+    q, k, v, w, beta, _ = rand_problem(L, d, 77)
+    cache = oracle_lib.cache_keys(k, w, beta)
+    z = brute_logits(q, k, w, beta, scale)
+    # the query at position L-1 scores the cache exactly as the definition does
+    assert_close(scale * cache @ q[L - 1], z[L - 1], 1e-12, "last-row logits")
+    # and so does any other query placed at position L-1
+    r = np.random.default_rng(5).standard_normal((4, d))
+    for qq in r:
+        q2 = q.copy()
+        q2[L - 1] = qq
+        assert_close(scale * cache @ qq, brute_logits(q2, k, w, beta, scale)[L - 1], 1e-12, "probe query")
+
+
+def test_p11_cache_keys_equal_decode_recurrence(oracle_lib):
+    BH, L, d = 2, 31, 8
+    r = np.random.default_rng(21)
+    q, k, v, w = r.standard_normal((4, L, BH, d))
+    w /= np.linalg.norm(w, axis=-1, keepdims=True)
+    beta = r.uniform(0, 2, (L, BH))
+    kc, vc = np.zeros((BH, L, d)), np.zeros((BH, L, d))
+    oracle_lib.decode(kc, vc, 0, q, k, v, w, beta, scale=0.5)
+    for bh in range(BH):
+        assert_close(oracle_lib.cache_keys(k[:, bh], w[:, bh], beta[:, bh]), kc[bh], 1e-12, f"head {bh}")
+
+
+CACHE_MUTATIONS = {
+    # H_j itself applied to key j
+    "includes_own": ("for (int64_t s = j + 1; s < L; ++s) apply_h(r,", "for (int64_t s = j; s < L; ++s) apply_h(r,"),
+    # newest transition applied first
+    "reversed": ("for (int64_t s = j + 1; s < L; ++s) apply_h(r,", "for (int64_t s = L - 1; s > j; --s) apply_h(r,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CACHE_MUTATIONS))
+def test_p11_planted_cache_mistakes_are_caught(oracle_lib, name, monkeypatch):
+    src = open(os.path.join(os.path.dirname(oracle_lib.__file__), "path_oracle.c")).read()
+    old, new = CACHE_MUTATIONS[name]
+    assert old in src, f"mutation site for {name} not found"
+    with tempfile.TemporaryDirectory() as tdir:
+        c, so = os.path.join(tdir, "m.c"), os.path.join(tdir, "m.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", so, c, "-lm"],
+                       check=True)
+        mutated = ctypes.CDLL(so)
+        mutated.path_oracle_cache_keys.argtypes = oracle_lib.lib().path_oracle_cache_keys.argtypes
+        mutated.path_oracle_cache_keys.restype = ctypes.c_int
+        monkeypatch.setattr(oracle_lib, "_lib", mutated)
+        with pytest.raises(AssertionError):
+            test_p11_cache_keys_explicit_products(oracle_lib, 9, 5, "sigmoid")
