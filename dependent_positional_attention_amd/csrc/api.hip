@@ -10,12 +10,16 @@ bool vec_supported(int d, int chunk);
 hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
                    const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
                    float scale, float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st);
+hipError_t vec_cache_run(bool bf16, int d, int chunk, const float* kt, const float* Pm, const void* v, int64_t BH,
+                         int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st);
 // mfma_path.hip
 bool mfma_supported(int d, int chunk);
 hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const void* k, const void* v,
                     const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH,
                     int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, void* kt2,
                     void* p2_hi, void* p2_lo, float* Sm, float* fl, float* ftot, hipStream_t st);
+hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
+                          int64_t BH, int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st);
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
@@ -195,6 +199,30 @@ path_status path_attn_scan(const void* v, const float* log_forget, void* out, fl
                            size_t workspace_bytes, void* stream) {
   return run_fwd(kPhaseScan, nullptr, nullptr, v, nullptr, nullptr, log_forget, out, lse, B, H, L, d, chunk, 1.f,
                  dtype, transport, workspace, workspace_bytes, stream);
+}
+
+path_status path_attn_cache_from_prefill(const void* v, const void* workspace, size_t workspace_bytes, void* kcache,
+                                         void* vcache, int64_t capacity, int64_t B, int64_t H, int64_t L, int d,
+                                         int chunk, int dtype, int transport, void* stream) {
+  path_ws_layout lay;
+  const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
+  if (s != PATH_OK) return s;
+  if (capacity < L) return PATH_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  if (BH == 0 || L == 0) return PATH_OK;
+  if (!v || !workspace || !kcache || !vcache) return PATH_ERR_INVALID_ARG;
+  if (misaligned(v) || misaligned(workspace) || misaligned(kcache) || misaligned(vcache)) return PATH_ERR_UNSUPPORTED;
+  if (workspace_bytes < (size_t)lay.total_bytes) return PATH_ERR_INVALID_ARG;
+  if (BH > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
+  const char* ws = static_cast<const char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (lay.layout_id >= 1)
+    return from_hip(mfma_cache_run(transport, ws + lay.off_ktilde, ws + lay.off_p,
+                                   lay.off_p_lo >= 0 ? ws + lay.off_p_lo : nullptr, v, BH, L, capacity, kcache,
+                                   vcache, st));
+  return from_hip(vec_cache_run(dtype == PATH_DTYPE_BF16, d, chunk, reinterpret_cast<const float*>(ws + lay.off_ktilde),
+                                reinterpret_cast<const float*>(ws + lay.off_p), v, BH, L, capacity, kcache, vcache,
+                                st));
 }
 
 path_status path_decode_workspace_bytes(int64_t B, int64_t H, int d, int64_t capacity, int splits,

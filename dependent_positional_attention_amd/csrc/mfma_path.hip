@@ -1034,6 +1034,121 @@ __global__ __launch_bounds__(256, 2) void mfma_merge_kernel(const __bf16* __rest
   }
 }
 
+// =========================================================================== kernel 4: decode cache
+// Prefill -> decode hand-off (PaTH summary, section 3, inference: a decode cache slot j holds
+// the key after every later transition, H_{L-1} ... H_{j+1} k_j).  In chunk terms, with R_n the
+// product of the chunk matrices after chunk n,
+//   R_{M-1} = I,   R_{n-1} = P_n R_n,   cache rows of chunk n = ktilde_n R_n   (row form),
+// a right-to-left chain over the 64-token (sub-)chunks that reuses the prep's ktilde and P.
+// Columns of R are independent, so wave w of the block for head bh carries the 64 x 16 column
+// block y = 16w .. 16w+15 of R in fp32 accumulators and never talks to the other waves: the
+// accumulator of R_{n-1} = P_n R_n is already the B-operand of the next product (stored key order),
+// and it is also the A-operand of the key product, computed transposed (key^T = R^T ktilde^T), so
+// every operand comes straight from global memory or registers and no LDS is used.  R enters the
+// matrix cores as hi + lo bf16 pairs, P as hi (+ lo with bf16x3 transport).  The wave also copies
+// its quarter of the chunk's value rows.  Loads for chunk n-1 are issued before chunk n's products.
+struct CacheFrags {
+  bf16x8 ph[4][2], pl[4][2], k[4][2];
+};
+
+template <bool X3>
+__global__ __launch_bounds__(256, 1) void mfma_cache_kernel(const __bf16* __restrict__ kt,
+                                                            const __bf16* __restrict__ p_hi,
+                                                            const __bf16* __restrict__ p_lo,
+                                                            const __bf16* __restrict__ v, int64_t L, int64_t M,
+                                                            int64_t cap, __bf16* __restrict__ kc,
+                                                            __bf16* __restrict__ vc) {
+  const int64_t bh = blockIdx.x, Lp = M * kC;
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // R[x][y] for x = 16 jt + 4g + e, y = 16 wave + r; R_{M-1} = I
+  f32x4 racc[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) racc[jt][e] = (16 * jt + 4 * g + e == 16 * wave + r) ? 1.f : 0.f;
+
+  auto load = [&](int64_t n, CacheFrags& F) PA_INLINE {
+    const __bf16* pb = p_hi + ((size_t)bh * M + n) * kD * kD;
+    const __bf16* kb = kt + ((size_t)bh * Lp + n * kC) * kD;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int o = (16 * t + r) * kD + 32 * ks + 8 * g;
+        F.ph[t][ks] = *reinterpret_cast<const bf16x8*>(pb + o);
+        if constexpr (X3) F.pl[t][ks] = *reinterpret_cast<const bf16x8*>(p_lo + ((size_t)bh * M + n) * kD * kD + o);
+        F.k[t][ks] = *reinterpret_cast<const bf16x8*>(kb + o);
+      }
+  };
+
+  auto step = [&](int64_t n, const CacheFrags& F) PA_INLINE {
+    bf16x8 rh[2], rl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x4 h0, l0, h1, l1;
+      split4(racc[2 * ks][0], racc[2 * ks][1], racc[2 * ks][2], racc[2 * ks][3], h0, l0);
+      split4(racc[2 * ks + 1][0], racc[2 * ks + 1][1], racc[2 * ks + 1][2], racc[2 * ks + 1][3], h1, l1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rh[ks][e] = h0[e];
+        rh[ks][4 + e] = h1[e];
+        rl[ks][e] = l0[e];
+        rl[ks][4 + e] = l1[e];
+      }
+    }
+    // values of chunk n: rows 16 wave .. 16 wave + 15, 32 B per lane
+    {
+      const int64_t j = n * kC + 16 * wave + (l >> 2);
+      if (j < L) {
+        const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)bh * L + j) * kD + 16 * (l & 3));
+        uint4* dst = reinterpret_cast<uint4*>(vc + ((size_t)bh * cap + j) * kD + 16 * (l & 3));
+        dst[0] = src[0];
+        dst[1] = src[1];
+      }
+    }
+    // keys of chunk n: key^T[y][b] = sum_m R[m][y] ktilde[b][m]; lane: key b = 16 bt + r, y = 16 wave + 4g ..
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+      f32x4 a = zero;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        a = mfma16(rh[ks], F.k[bt][ks], a);
+        a = mfma16(rl[ks], F.k[bt][ks], a);
+      }
+      const int64_t j = n * kC + 16 * bt + r;
+      if (j < L)
+        *reinterpret_cast<bf16x4*>(kc + ((size_t)bh * cap + j) * kD + 16 * wave + 4 * g) = pack4(a[0], a[1], a[2], a[3]);
+    }
+    // R_{n-1} = P_n R_n
+    if (n > 0) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        f32x4 a = zero;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          a = mfma16(F.ph[jt][ks], rh[ks], a);
+          a = mfma16(F.ph[jt][ks], rl[ks], a);
+          if constexpr (X3) a = mfma16(F.pl[jt][ks], rh[ks], a);
+        }
+        racc[jt] = a;
+      }
+    }
+  };
+
+  CacheFrags A, B;
+  int64_t n = M - 1;
+  load(n, A);
+  for (; n >= 1; n -= 2) {
+    load(n - 1, B);
+    step(n, A);
+    if (n >= 2) load(n - 2, A);
+    step(n - 1, B);
+  }
+  if (n == 0) step(0, A);
+}
+
 // =========================================================================== host
 bool mfma_supported(int d, int chunk) { return d == kD && (chunk == kC || chunk == 2 * kC); }
 
@@ -1101,6 +1216,21 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
     e = hipGetLastError();
   }
   return e;
+}
+
+// Decode cache from a prefill workspace (kernel 4): one block of 4 waves per (b, h).
+hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
+                          int64_t BH, int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st) {
+  const int64_t M = (L + kC - 1) / kC;
+  if (transport == 1)
+    mfma_cache_kernel<true><<<dim3((unsigned)BH), 256, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi,
+                                                                (const __bf16*)p_lo, (const __bf16*)v, L, M, cap,
+                                                                (__bf16*)kc, (__bf16*)vc);
+  else
+    mfma_cache_kernel<false><<<dim3((unsigned)BH), 256, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi, nullptr,
+                                                                 (const __bf16*)v, L, M, cap, (__bf16*)kc,
+                                                                 (__bf16*)vc);
+  return hipGetLastError();
 }
 
 }  // namespace pathattn

@@ -248,6 +248,49 @@ __global__ __launch_bounds__(C) void vec_attn_kernel(const float* __restrict__ q
   }
 }
 
+// ------------------------------------------------------------------------------------ decode cache
+// Prefill -> decode hand-off (inference rule of the same section: a decode cache slot j holds
+// H_{L-1} ... H_{j+1} k_j).  With R_n = P_{n+1} ... P_{M-1} (identity for the last chunk), the
+// slots of chunk n are the rows ktilde_n R_n; R is carried right to left, R_{n-1} = P_n R_n, in LDS,
+// one block per (batch, head).  Values are copied alongside.
+template <typename T, int D, int C>
+__global__ __launch_bounds__(256) void vec_cache_kernel(const float* __restrict__ kt, const float* __restrict__ Pm,
+                                                        const T* __restrict__ v, int64_t L, int64_t M, int64_t cap,
+                                                        T* __restrict__ kc, T* __restrict__ vc) {
+  __shared__ float R[2][D * D];
+  const int64_t bh = blockIdx.x, Lp = M * C;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < D * D; e += blockDim.x) R[0][e] = (e / D == e % D) ? 1.f : 0.f;
+  __syncthreads();
+  int cur = 0;
+  for (int64_t n = M - 1; n >= 0; --n) {
+    const float* Rc = R[cur];
+    for (int e = tid; e < C * D; e += blockDim.x) {
+      const int b = e / D, y = e % D;
+      const int64_t j = n * C + b;
+      if (j < L) {
+        const float* kr = kt + ((size_t)bh * Lp + j) * D;
+        float s = 0.f;
+        for (int m = 0; m < D; ++m) s += kr[m] * Rc[m * D + y];
+        kc[((size_t)bh * cap + j) * D + y] = from_f32<T>(s);
+        vc[((size_t)bh * cap + j) * D + y] = v[((size_t)bh * L + j) * D + y];
+      }
+    }
+    if (n > 0) {
+      float* Rn = R[cur ^ 1];
+      const float* Pn = Pm + ((size_t)bh * M + n) * D * D;
+      for (int e = tid; e < D * D; e += blockDim.x) {
+        const int x = e / D, y = e % D;
+        float s = 0.f;
+        for (int m = 0; m < D; ++m) s += Pn[x * D + m] * Rc[m * D + y];
+        Rn[e] = s;
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+}
+
 // ------------------------------------------------------------------------------------ launch
 // phases: bit 0 = per-chunk prep, bit 1 = attention scan (reads what the prep left in the workspace).
 template <typename T, int D, int C>
@@ -301,6 +344,35 @@ static hipError_t dispatch_vec(int phases, int d, int chunk, const void* q, cons
   return hipErrorInvalidValue;
 }
 #undef PATHATTN_VEC_CASE
+
+template <typename T>
+static hipError_t dispatch_vec_cache(int d, int chunk, const float* kt, const float* Pm, const void* v, int64_t BH,
+                                     int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st) {
+  const int64_t M = (L + chunk - 1) / chunk;
+#define PATHATTN_VEC_CACHE_CASE(DD, CC)                                                                     \
+  if (d == DD && chunk == CC) {                                                                             \
+    vec_cache_kernel<T, DD, CC><<<dim3((unsigned)BH), 256, 0, st>>>(kt, Pm, (const T*)v, L, M, cap, (T*)kc, \
+                                                                    (T*)vc);                                \
+    return hipGetLastError();                                                                               \
+  }
+  PATHATTN_VEC_CACHE_CASE(16, 16)
+  PATHATTN_VEC_CACHE_CASE(16, 32)
+  PATHATTN_VEC_CACHE_CASE(16, 64)
+  PATHATTN_VEC_CACHE_CASE(32, 16)
+  PATHATTN_VEC_CACHE_CASE(32, 32)
+  PATHATTN_VEC_CACHE_CASE(32, 64)
+  PATHATTN_VEC_CACHE_CASE(64, 16)
+  PATHATTN_VEC_CACHE_CASE(64, 32)
+  PATHATTN_VEC_CACHE_CASE(64, 64)
+#undef PATHATTN_VEC_CACHE_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t vec_cache_run(bool bf16, int d, int chunk, const float* kt, const float* Pm, const void* v, int64_t BH,
+                         int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st) {
+  if (bf16) return dispatch_vec_cache<__bf16>(d, chunk, kt, Pm, v, BH, L, cap, kc, vc, st);
+  return dispatch_vec_cache<float>(d, chunk, kt, Pm, v, BH, L, cap, kc, vc, st);
+}
 
 bool vec_supported(int d, int chunk) {
   return (d == 16 || d == 32 || d == 64) && (chunk == 16 || chunk == 32 || chunk == 64);

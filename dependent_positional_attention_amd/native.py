@@ -44,7 +44,7 @@ class WsLayout(ctypes.Structure):
 
 EXPORTS = ("path_abi_version", "path_status_string", "path_attn_fwd_workspace_bytes", "path_attn_fwd",
            "path_attn_prep", "path_attn_scan", "path_attn_workspace_layout", "path_decode_workspace_bytes",
-           "path_decode_step")
+           "path_decode_step", "path_attn_cache_from_prefill")
 
 
 def lib():
@@ -67,8 +67,9 @@ def lib():
         L.path_decode_workspace_bytes.argtypes = [i64, i64, i32, i64, i32, ctypes.POINTER(sz)]
         L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, f32, i32, i32,
                                        vp, sz, vp]
+        L.path_attn_cache_from_prefill.argtypes = [vp, vp, sz, vp, vp, i64, i64, i64, i64, i32, i32, i32, i32, vp]
         for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd", "path_attn_prep",
-                  "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step"):
+                  "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step", "path_attn_cache_from_prefill"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -186,6 +187,30 @@ def path_attn_scan(v, log_forget=None, *, chunk: int = 64, transport: str = "bf1
         _ptr(v), _ptr(log_forget), _ptr(out), _ptr(lse), B, H, L, d, chunk, DTYPE[v.dtype], TRANSPORT[transport],
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
+
+
+def path_attn_cache_from_prefill(v, *, workspace, capacity: Optional[int] = None, chunk: int = 64,
+                                 transport: str = "bf16", kcache=None, vcache=None,
+                                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode caches [B,H,capacity,d] after a prompt, from a workspace filled by path_attn_prep /
+    path_attn_fwd with the same arguments.  v: the prompt's values [B,H,L,d]."""
+    _require(v, "v")
+    B, H, L, d = v.shape
+    if kcache is None:
+        cap = L if capacity is None else int(capacity)
+        kcache = torch.empty((B, H, cap, d), device=v.device, dtype=v.dtype)
+    _require(kcache, "kcache", v.dtype)
+    B2, H2, cap, d2 = kcache.shape
+    if (B2, H2, d2) != (B, H, d):
+        raise ValueError(f"kcache shape {tuple(kcache.shape)} does not match v {tuple(v.shape)}")
+    if vcache is None:
+        vcache = torch.empty_like(kcache)
+    _require(vcache, "vcache", v.dtype, kcache.shape)
+    _require(workspace, "workspace")
+    _check("path_attn_cache_from_prefill", lib().path_attn_cache_from_prefill(
+        _ptr(v), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(kcache), _ptr(vcache), cap, B,
+        H, L, d, chunk, DTYPE[v.dtype], TRANSPORT[transport], _stream(stream)))
+    return kcache, vcache
 
 
 def path_decode_workspace_bytes(B, H, d, capacity, splits: int = 0) -> int:

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 2
+#define PATH_ABI_VERSION 3
 
 typedef enum {
   PATH_OK = 0,
@@ -184,6 +184,32 @@ path_status path_decode_step(void* kcache, void* vcache, int64_t capacity, int64
                              const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out,
                              float* lse, int64_t B, int64_t H, int d, float scale, int dtype, int splits,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill -> decode hand-off: fills a decode cache from a prefill workspace
+ * (summary, section 3, inference: decoding keeps the keys updated in place by
+ * every later transition, so after a prompt of L tokens cache slot j must hold
+ * H_{L-1} ... H_{j+2} H_{j+1} k_j).  The slots are built from the per-chunk
+ * terms path_attn_prep (or path_attn_fwd) left in `workspace` for the SAME
+ * B, H, L, d, chunk, dtype and transport: slot j of chunk n is the row
+ * ktilde_j (P_{n+1} ... P_{M-1}) (row form; the chunk products are chained right
+ * to left), so the prompt's transitions are not read again.  path_decode_step
+ * can then continue at t = L.
+ *
+ *   v               [B,H,L,d] dtype         the prompt's values (copied)
+ *   workspace       prefill workspace (read only; log_forget terms unused)
+ *   kcache, vcache  [B,H,capacity,d] dtype  slots 0..L-1 written; slots >= L untouched
+ *   capacity        >= L (PATH_ERR_INVALID_ARG otherwise)
+ *
+ * The bf16 path chains the chunk products with fp32 accumulation (the running
+ * product enters the matrix cores as hi + lo bf16) and rounds each slot to bf16
+ * once; the fp32 path works in fp32.  The slots do not depend on the forget
+ * gates, so a PaTH-FoX prompt fills its cache with the same call (the running
+ * forget sums a FoX decode also needs are not produced here).
+ */
+path_status path_attn_cache_from_prefill(const void* v, const void* workspace, size_t workspace_bytes, void* kcache,
+                                         void* vcache, int64_t capacity, int64_t B, int64_t H, int64_t L, int d,
+                                         int chunk, int dtype, int transport, void* stream);
 
 #ifdef __cplusplus
 }

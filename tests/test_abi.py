@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 2
+    assert L.path_abi_version() == 3
     for s in range(4):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"
@@ -130,6 +130,27 @@ def test_decode_validation(L):
     assert L.path_decode_workspace_bytes(32, 24, 64, 65536 + 128, 0, ctypes.byref(n)) == OK
     assert n.value == 32 * 24 * 65 * 66 * 4
     assert L.path_decode_workspace_bytes(1, 1, 48, 100, 0, ctypes.byref(n)) == UNSUPPORTED
+
+
+def handoff(L, v=FAKE, ws=FAKE, ws_n=1 << 40, kc=FAKE, vc=FAKE, cap=4096, B=1, H=2, Lq=4096, d=64, chunk=64,
+            dtype=BF16, transport=0):
+    return L.path_attn_cache_from_prefill(v, ws, ws_n, kc, vc, cap, B, H, Lq, d, chunk, dtype, transport, None)
+
+
+def test_cache_handoff_validation(L):
+    assert handoff(L, cap=4095) == INVALID  # capacity below the prompt length
+    assert handoff(L, v=None) == INVALID
+    assert handoff(L, kc=None) == INVALID
+    assert handoff(L, ws=None) == INVALID
+    assert handoff(L, ws_n=1024) == INVALID  # workspace smaller than the prefill plan
+    assert handoff(L, vc=MISALIGNED) == UNSUPPORTED
+    assert handoff(L, d=48) == UNSUPPORTED
+    assert handoff(L, chunk=8) == UNSUPPORTED
+    assert handoff(L, transport=5) == INVALID
+    assert handoff(L, B=-1) == INVALID
+    # an empty prompt or batch is valid and enqueues nothing
+    assert handoff(L, Lq=0, v=None, ws=None, kc=None, vc=None) == OK
+    assert handoff(L, H=0, v=None) == OK
 
 
 def test_python_binding_rejects_cpu_tensors():
