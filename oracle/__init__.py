@@ -46,15 +46,16 @@ def lib():
                                       ctypes.POINTER(_I64), _I64, _D, _D, ctypes.c_int]
         L.path_oracle_row_logits.argtypes = [_D, _D, _D, _D, _D, _I64, _I64, ctypes.c_double, _D]
         L.path_oracle_transport.argtypes = [_D, _D, _D, _I64, _I64, _I64, _D]
-        L.path_oracle_decode.argtypes = [_D, _D, _I64, _I64, _I64, _I64, _D, _D, _D, _D, _D, _I64,
+        L.path_oracle_decode.argtypes = [_D, _D, _D, _I64, _I64, _I64, _I64, _D, _D, _D, _D, _D, _D, _I64,
                                          ctypes.c_double, _D, _D, ctypes.c_int]
+        L.path_oracle_cache_bias.argtypes = [_D, _I64, _D]
         L.path_oracle_ut_tinv.argtypes = [_D, _D, _I64, _I64, _D]
         L.path_oracle_householder_product.argtypes = [_D, _D, _I64, _I64, _D]
         L.path_oracle_chunk_terms.argtypes = [_D, _D, _D, _D, _I64, _I64, _D, _D, _D]
         L.path_oracle_cache_keys.argtypes = [_D, _D, _D, _I64, _I64, _I64, _I64, _D]
         for f in ("path_oracle_fwd", "path_oracle_row_logits", "path_oracle_transport",
                   "path_oracle_decode", "path_oracle_ut_tinv", "path_oracle_householder_product",
-                  "path_oracle_chunk_terms", "path_oracle_cache_keys"):
+                  "path_oracle_chunk_terms", "path_oracle_cache_keys", "path_oracle_cache_bias"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -122,20 +123,25 @@ def transport(x, W, beta, lo: int, hi: int):
     return out
 
 
-def decode(kcache, vcache, t0: int, q, k, v, w, beta, scale: float, nthreads: int = 0):
+def decode(kcache, vcache, t0: int, q, k, v, w, beta, scale: float, nthreads: int = 0, fcache=None, logf=None):
     """Run nsteps decode steps.  kcache/vcache: [BH, cap, d] float64, modified in place.
 
-    q,k,v,w: [nsteps, BH, d]; beta: [nsteps, BH].  Returns (out [nsteps,BH,d], lse [nsteps,BH]).
+    q,k,v,w: [nsteps, BH, d]; beta: [nsteps, BH].  PaTH-FoX: fcache [BH, cap] float64 per-slot forget
+    bias (modified in place) and logf [nsteps, BH].  Returns (out [nsteps,BH,d], lse [nsteps,BH]).
     """
     assert kcache.dtype == np.float64 and kcache.flags.c_contiguous
     assert vcache.dtype == np.float64 and vcache.flags.c_contiguous
+    assert (fcache is None) == (logf is None)
+    if fcache is not None:
+        assert fcache.dtype == np.float64 and fcache.flags.c_contiguous
+        logf = _f64(logf)
     q, k, v, w, beta = map(_f64, (q, k, v, w, beta))
     nsteps, BH, d = q.shape
     cap = kcache.shape[1]
     out = np.zeros((nsteps, BH, d))
     lse = np.zeros((nsteps, BH))
-    _check(lib().path_oracle_decode(_p(kcache), _p(vcache), BH, cap, t0, nsteps, _p(q), _p(k), _p(v),
-                                    _p(w), _p(beta), d, float(scale), _p(out), _p(lse),
+    _check(lib().path_oracle_decode(_p(kcache), _p(vcache), _p(fcache), BH, cap, t0, nsteps, _p(q), _p(k),
+                                    _p(v), _p(w), _p(beta), _p(logf), d, float(scale), _p(out), _p(lse),
                                     int(nthreads or host_threads())), "path_oracle_decode")
     return out, lse
 
@@ -181,4 +187,12 @@ def cache_keys(K, W, beta, rows=None):
     out = np.zeros((max(j1 - j0, 0), d))
     _check(lib().path_oracle_cache_keys(_p(K), _p(W), _p(beta), L, d, j0, j1, _p(out)),
            "path_oracle_cache_keys")
+    return out
+
+
+def cache_bias(logf):
+    """PaTH-FoX forget bias of each cache slot after a prompt: slot j = sum_{s=j+1..L-1} f_s.  logf: [L]."""
+    logf = _f64(logf)
+    out = np.zeros(logf.shape[0])
+    _check(lib().path_oracle_cache_bias(_p(logf), logf.shape[0], _p(out)), "path_oracle_cache_bias")
     return out

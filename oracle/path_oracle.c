@@ -185,9 +185,9 @@ int path_oracle_transport(const double* x, const double* W, const double* beta, 
 /* ------------------------------------------------------------------ decode */
 
 typedef struct {
-  double *kc, *vc;
+  double *kc, *vc, *fc;
   int64_t BH, cap, t0, nsteps, d;
-  const double *qs, *ks, *vs, *ws, *betas;
+  const double *qs, *ks, *vs, *ws, *betas, *fs;
   double scale;
   double *out, *lse;
   int64_t next;
@@ -203,6 +203,7 @@ static void* dec_worker(void* arg) {
     if (bh >= J->BH) break;
     double* Kc = J->kc + bh * J->cap * d;
     double* Vc = J->vc + bh * J->cap * d;
+    double* Fc = J->fc ? J->fc + bh * J->cap : NULL;
     for (int64_t s = 0; s < J->nsteps; ++s) {
       const int64_t t = J->t0 + s;
       const int64_t tok = s * J->BH + bh;
@@ -213,8 +214,14 @@ static void* dec_worker(void* arg) {
       for (int64_t j = 0; j < t; ++j) apply_h(Kc + j * d, w, beta, d);
       memcpy(Kc + t * d, J->ks + tok * d, (size_t)d * sizeof(double));
       memcpy(Vc + t * d, J->vs + tok * d, (size_t)d * sizeof(double));
+      /* PaTH-FoX (section 2): slot j carries the forget bias sum_{s=j+1..t} f_s,
+         grown in place by the newest gate like the keys; the new slot starts at 0. */
+      if (Fc) {
+        for (int64_t j = 0; j < t; ++j) Fc[j] += J->fs[tok];
+        Fc[t] = 0.0;
+      }
       const double* qt = J->qs + tok * d;
-      for (int64_t j = 0; j <= t; ++j) z[j] = J->scale * dot(Kc + j * d, qt, d);
+      for (int64_t j = 0; j <= t; ++j) z[j] = J->scale * dot(Kc + j * d, qt, d) + (Fc ? Fc[j] : 0.0);
       softmax_rows(z, t + 1, Vc, d, J->out + tok * d, J->lse + tok);
     }
   }
@@ -226,15 +233,18 @@ static void* dec_worker(void* arg) {
  * nsteps decode steps for BH independent slices.  kc, vc: [BH, cap, d], the first
  * t0 slots hold the current cache; they are updated in place and slots
  * t0..t0+nsteps-1 are appended.  qs,ks,vs,ws: [nsteps, BH, d]; betas: [nsteps, BH].
+ * PaTH-FoX: fc [BH, cap] per-slot forget bias (first t0 slots current, updated in
+ * place) and fs [nsteps, BH] the new tokens' gates; both NULL for plain PaTH.
  * out: [nsteps, BH, d]; lse: [nsteps, BH].
  */
-int path_oracle_decode(double* kc, double* vc, int64_t BH, int64_t cap, int64_t t0, int64_t nsteps,
+int path_oracle_decode(double* kc, double* vc, double* fc, int64_t BH, int64_t cap, int64_t t0, int64_t nsteps,
                        const double* qs, const double* ks, const double* vs, const double* ws,
-                       const double* betas, int64_t d, double scale, double* out, double* lse,
+                       const double* betas, const double* fs, int64_t d, double scale, double* out, double* lse,
                        int nthreads) {
   if (BH < 0 || cap < 0 || t0 < 0 || nsteps < 0 || d <= 0 || t0 + nsteps > cap) return ORACLE_EINVAL;
+  if ((fc == NULL) != (fs == NULL)) return ORACLE_EINVAL;
   if (BH == 0 || nsteps == 0) return ORACLE_OK;
-  dec_job J = {kc, vc, BH, cap, t0, nsteps, d, qs, ks, vs, ws, betas, scale, out, lse, 0};
+  dec_job J = {kc, vc, fc, BH, cap, t0, nsteps, d, qs, ks, vs, ws, betas, fs, scale, out, lse, 0};
   int nt = resolve_threads(nthreads);
   if ((int64_t)nt > BH) nt = (int)BH;
   pthread_t* th = (pthread_t*)malloc((size_t)nt * sizeof(pthread_t));
@@ -267,6 +277,20 @@ int path_oracle_cache_keys(const double* K, const double* W, const double* beta,
     double* r = out + (j - j0) * d;
     memcpy(r, K + j * d, (size_t)d * sizeof(double));
     for (int64_t s = j + 1; s < L; ++s) apply_h(r, W + s * d, beta[s], d);
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * PaTH-FoX part of the same cache: slot j's forget bias after a prompt of L tokens,
+ * sum_{s=j+1..L-1} f_s (0 for the last slot), summed from s = j+1 upwards.
+ */
+int path_oracle_cache_bias(const double* logf, int64_t L, double* out) {
+  if (L < 0) return ORACLE_EINVAL;
+  for (int64_t j = 0; j < L; ++j) {
+    double b = 0.0;
+    for (int64_t s = j + 1; s < L; ++s) b += logf[s];
+    out[j] = b;
   }
   return ORACLE_OK;
 }

@@ -12,7 +12,8 @@ P5  beta = 2    absolute form: logits = (A_j k_j).(A_i q_i) with A_i = H_0...H_i
 P6  det         det(H_0...H_{n-1}) = prod_s (1 - beta_s |w_s|^2)
 P7  chunked     boundary-adjusted rows + right-to-left chunk scan reproduce the oracle (summary, section 3)
 P8  special     row 0, constant values, f = 0, closed-form FoX bias with beta = 0
-P9  decode      in-place key updates (summary, section 3 "inference") == prefill rows
+P9  decode      in-place key updates (summary, section 3 "inference") == prefill rows; PaTH-FoX decode
+                (per-slot forget bias grown in place) == FoX prefill rows and the beta = 0 closed form
 P10 mutations   plausible mistakes planted in a copy of the oracle make the pins fail
 P11 cache       key cache after a prompt (summary, section 3 "inference"): explicit products,
                 last-row logits, the decode recurrence, norms under beta = 2
@@ -393,6 +394,42 @@ def test_p9_decode_from_empty_equals_prefill(oracle_lib):
             assert_close(kc[bh, j], M @ k[j, bh], 1e-12, f"cache key {j}")
 
 
+def test_p9_fox_decode_from_empty_equals_prefill(oracle_lib):
+    """PaTH-FoX decode (per-slot forget bias grown in place) == the FoX prefill definition, row by row."""
+    BH, S, d = 3, 29, 6
+    r = np.random.default_rng(17)
+    q, k, v, w = r.standard_normal((4, S, BH, d))
+    w /= np.linalg.norm(w, axis=-1, keepdims=True)
+    beta = r.uniform(0, 2, (S, BH))
+    f = -np.log1p(np.exp(-(1.0 + r.standard_normal((S, BH)))))
+    kc, vc, fc = np.zeros((BH, S, d)), np.zeros((BH, S, d)), np.zeros((BH, S))
+    out, lse = oracle_lib.decode(kc, vc, 0, q, k, v, w, beta, scale=0.4, fcache=fc, logf=f)
+    tr = lambda x: np.ascontiguousarray(np.moveaxis(x, 0, 1))
+    po, pl = oracle_lib.fwd(tr(q), tr(k), tr(v), tr(w), tr(beta), logf=tr(f), scale=0.4)
+    assert_close(tr(out), po, 1e-12, "out")
+    assert_close(tr(lse), pl, 1e-12, "lse")
+    # the slot biases are the suffix sums of the gates after each slot
+    for bh in range(BH):
+        want = np.array([f[j + 1:, bh].sum() for j in range(S)])
+        assert_close(fc[bh], want, 1e-12, "slot bias")
+        assert_close(oracle_lib.cache_bias(f[:, bh]), want, 1e-12, "cache_bias")
+
+
+def test_p9_fox_bias_beta_zero_closed_form(oracle_lib):
+    """beta = 0 and constant gate f: logits are scale q.k_j + (t - j) f (ALiBi-like closed form)."""
+    BH, S, d, fval = 1, 12, 4, -0.3
+    r = np.random.default_rng(3)
+    q, k, v, w = r.standard_normal((4, S, BH, d))
+    kc, vc, fc = np.zeros((BH, S, d)), np.zeros((BH, S, d)), np.zeros((BH, S))
+    out, lse = oracle_lib.decode(kc, vc, 0, q, k, v, w, np.zeros((S, BH)), scale=1.0, fcache=fc,
+                                 logf=np.full((S, BH), fval))
+    for t in range(S):
+        z = k[:t + 1, 0] @ q[t, 0] + fval * (t - np.arange(t + 1))
+        p = np.exp(z - z.max())
+        assert_close(out[t, 0], (p / p.sum()) @ v[:t + 1, 0], 1e-12, "out")
+        assert_close(lse[t, 0], z.max() + np.log(p.sum()), 1e-12, "lse")
+
+
 def test_p9_decode_with_initial_cache(oracle_lib):
     BH, T0, S, d = 2, 20, 5, 8
     r = np.random.default_rng(13)
@@ -544,3 +581,31 @@ def test_p11_planted_cache_mistakes_are_caught(oracle_lib, name, monkeypatch):
         monkeypatch.setattr(oracle_lib, "_lib", mutated)
         with pytest.raises(AssertionError):
             test_p11_cache_keys_explicit_products(oracle_lib, 9, 5, "sigmoid")
+
+
+FOX_DECODE_MUTATIONS = {
+    # the new slot starts with its own gate
+    "own_gate": ("        Fc[t] = 0.0;", "        Fc[t] = J->fs[tok];"),
+    # the bias is subtracted
+    "bias_sign": ("+ (Fc ? Fc[j] : 0.0);", "- (Fc ? Fc[j] : 0.0);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FOX_DECODE_MUTATIONS))
+def test_p9_planted_fox_decode_mistakes_are_caught(oracle_lib, name, monkeypatch):
+    src = open(os.path.join(os.path.dirname(oracle_lib.__file__), "path_oracle.c")).read()
+    old, new = FOX_DECODE_MUTATIONS[name]
+    assert old in src, f"mutation site for {name} not found"
+    with tempfile.TemporaryDirectory() as tdir:
+        c, so = os.path.join(tdir, "m.c"), os.path.join(tdir, "m.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", so, c, "-lm"],
+                       check=True)
+        real = oracle_lib.lib()
+        mutated = ctypes.CDLL(so)
+        for f in ("path_oracle_decode", "path_oracle_fwd", "path_oracle_cache_bias"):
+            getattr(mutated, f).argtypes = getattr(real, f).argtypes
+            getattr(mutated, f).restype = ctypes.c_int
+        monkeypatch.setattr(oracle_lib, "_lib", mutated)
+        with pytest.raises(AssertionError):
+            test_p9_fox_bias_beta_zero_closed_form(oracle_lib)
