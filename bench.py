@@ -18,6 +18,8 @@ Also reported on the same JSON line:
   decode        batch 32, H=24, d=64, 65536 cached tokens, 128 steps timed back
                 to back: HBM bytes the step must move (cached keys read and
                 written back, cached values read) over the measured time.
+  cache_handoff the prefill workspace turned into a decode cache (path_attn_cache_from_prefill)
+                at the prefill shape: time and HBM bytes it must move.
   long_context  B=1, H=24, L=32768: whole prefill step at chunk 64 and at
                 chunk 128 (transport once per 128 keys), tokens/s and the
                 fraction of bf16 peak for each chunk size's own flop count.
@@ -158,7 +160,39 @@ def bench_prefill(args):
         f"whole step {F / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s")
     res = dict(B=B, H=H, L=L, d=d, C=C, recipe=recipe, ms_step=ms_step, wall_ms=wall_ms, ms_prep=ms_prep,
                ms_scan=ms_scan, flops=F, scan_tflops=tflops, tokens_per_s=B * L / (ms_step * 1e-3))
-    return res, x
+    return res, x, dict(v=v, ws=ws)
+
+
+def bench_handoff(args, res, ctx):
+    """Prefill -> decode cache hand-off from the prefill workspace just timed (same shape and chunk)."""
+    import torch
+    from dependent_positional_attention_amd import native
+
+    B, H, L, d, C = res["B"], res["H"], res["L"], res["d"], res["C"]
+    v, ws = ctx["v"], ctx["ws"]
+    kc = torch.empty((B, H, L, d), device="cuda", dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+
+    def run():
+        native.path_attn_cache_from_prefill(v, workspace=ws, chunk=C, transport=args.transport, kcache=kc,
+                                            vcache=vc)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    ms = timed(run, args.steps)
+    assert torch.isfinite(kc.float()).all(), "non-finite cache"
+    # bytes the hand-off must move: ktilde, the chunk products (hi, + lo for bf16x3) and the values read,
+    # both caches written
+    M = -(-L // 64)
+    p_parts = 2 if args.transport == "bf16x3" else 1
+    nbytes = B * H * (L * d * 2 + M * d * d * 2 * p_parts + L * d * 2 + 2 * L * d * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] cache hand-off: {ms * 1e3:.1f} us, {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of HBM peak "
+        f"({M} chained 64-token chunks per head)")
+    return {"workload": f"prefill -> decode cache hand-off, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16",
+            "ms": ms, "bytes": nbytes, "achieved_gbs": gbs, "peak_gbs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+            "chained_steps_per_head": M}
 
 
 def bench_cpu(x, args):
@@ -313,7 +347,9 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done (3 dispatches)")
         del src, dst
-    res, x = bench_prefill(args)
+    res, x, ctx = bench_prefill(args)
+    handoff = bench_handoff(args, res, ctx)
+    del ctx
     cpu = None if args.no_cpu else bench_cpu(x, args)
     dec = None if args.no_decode else bench_decode(args)
     long_ctx = None if args.no_long else bench_long(args)
@@ -347,6 +383,7 @@ def main():
                            "step_frac_of_peak": F / (res["ms_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
         "decode": dec,
+        "cache_handoff": handoff,
         "long_context": long_ctx,
     }
     print(json.dumps(line), flush=True)

@@ -23,9 +23,11 @@ hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
-hipError_t decode_step(bool bf16, int d, void* kc, void* vc, int64_t cap, int64_t t, const void* q_t,
-                       const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out, float* lse,
-                       int64_t BH, float scale, int splits, float* part, hipStream_t st);
+hipError_t decode_step(bool bf16, int d, void* kc, void* vc, float* fc, int64_t cap, int64_t t, const int* t_batch,
+                       int H, const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                       const float* beta_t, const float* f_t, void* out, float* lse, int64_t BH, float scale,
+                       int splits, float* part, hipStream_t st);
+hipError_t slot_bias_run(const float* logf, int64_t BH, int64_t L, int64_t cap, float* fc, hipStream_t st);
 }  // namespace pathattn
 
 using namespace pathattn;
@@ -201,28 +203,34 @@ path_status path_attn_scan(const void* v, const float* log_forget, void* out, fl
                  dtype, transport, workspace, workspace_bytes, stream);
 }
 
-path_status path_attn_cache_from_prefill(const void* v, const void* workspace, size_t workspace_bytes, void* kcache,
-                                         void* vcache, int64_t capacity, int64_t B, int64_t H, int64_t L, int d,
-                                         int chunk, int dtype, int transport, void* stream) {
+path_status path_attn_cache_from_prefill(const void* v, const float* log_forget, const void* workspace,
+                                         size_t workspace_bytes, void* kcache, void* vcache, float* fcache,
+                                         int64_t capacity, int64_t B, int64_t H, int64_t L, int d, int chunk,
+                                         int dtype, int transport, void* stream) {
   path_ws_layout lay;
   const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
   if (s != PATH_OK) return s;
   if (capacity < L) return PATH_ERR_INVALID_ARG;
+  if ((log_forget == nullptr) != (fcache == nullptr)) return PATH_ERR_INVALID_ARG;
   const int64_t BH = B * H;
   if (BH == 0 || L == 0) return PATH_OK;
   if (!v || !workspace || !kcache || !vcache) return PATH_ERR_INVALID_ARG;
-  if (misaligned(v) || misaligned(workspace) || misaligned(kcache) || misaligned(vcache)) return PATH_ERR_UNSUPPORTED;
+  if (misaligned(v) || misaligned(workspace) || misaligned(kcache) || misaligned(vcache) || misaligned(log_forget) ||
+      misaligned(fcache))
+    return PATH_ERR_UNSUPPORTED;
   if (workspace_bytes < (size_t)lay.total_bytes) return PATH_ERR_INVALID_ARG;
   if (BH > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
   const char* ws = static_cast<const char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
   if (lay.layout_id >= 1)
-    return from_hip(mfma_cache_run(transport, ws + lay.off_ktilde, ws + lay.off_p,
-                                   lay.off_p_lo >= 0 ? ws + lay.off_p_lo : nullptr, v, BH, L, capacity, kcache,
-                                   vcache, st));
-  return from_hip(vec_cache_run(dtype == PATH_DTYPE_BF16, d, chunk, reinterpret_cast<const float*>(ws + lay.off_ktilde),
-                                reinterpret_cast<const float*>(ws + lay.off_p), v, BH, L, capacity, kcache, vcache,
-                                st));
+    e = mfma_cache_run(transport, ws + lay.off_ktilde, ws + lay.off_p, lay.off_p_lo >= 0 ? ws + lay.off_p_lo : nullptr,
+                       v, BH, L, capacity, kcache, vcache, st);
+  else
+    e = vec_cache_run(dtype == PATH_DTYPE_BF16, d, chunk, reinterpret_cast<const float*>(ws + lay.off_ktilde),
+                      reinterpret_cast<const float*>(ws + lay.off_p), v, BH, L, capacity, kcache, vcache, st);
+  if (e == hipSuccess && log_forget != nullptr) e = slot_bias_run(log_forget, BH, L, capacity, fcache, st);
+  return from_hip(e);
 }
 
 path_status path_decode_workspace_bytes(int64_t B, int64_t H, int d, int64_t capacity, int splits,
@@ -234,27 +242,31 @@ path_status path_decode_workspace_bytes(int64_t B, int64_t H, int d, int64_t cap
   return PATH_OK;
 }
 
-path_status path_decode_step(void* kcache, void* vcache, int64_t capacity, int64_t t, const void* q_t,
-                             const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out,
-                             float* lse, int64_t B, int64_t H, int d, float scale, int dtype, int splits,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+path_status path_decode_step(void* kcache, void* vcache, float* fcache, int64_t capacity, int64_t t,
+                             const int* t_batch, const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                             const float* beta_t, const float* log_forget_t, void* out, float* lse, int64_t B,
+                             int64_t H, int d, float scale, int dtype, int splits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 0 || capacity < 0 || splits < 0) return PATH_ERR_INVALID_ARG;
   if (!valid_dtype(dtype) || !decode_supported(d)) return PATH_ERR_UNSUPPORTED;
   if (t < 0 || t >= capacity) return PATH_ERR_INVALID_ARG;
+  if ((log_forget_t == nullptr) != (fcache == nullptr)) return PATH_ERR_INVALID_ARG;
   const int64_t BH = B * H;
   if (BH == 0) return PATH_OK;
   if (!kcache || !vcache || !q_t || !k_t || !v_t || !w_t || !beta_t || !out || !workspace)
     return PATH_ERR_INVALID_ARG;
   if (misaligned(kcache) || misaligned(vcache) || misaligned(q_t) || misaligned(k_t) || misaligned(v_t) ||
-      misaligned(w_t) || misaligned(beta_t) || misaligned(out) || misaligned(lse) || misaligned(workspace))
+      misaligned(w_t) || misaligned(beta_t) || misaligned(out) || misaligned(lse) || misaligned(workspace) ||
+      misaligned(fcache) || misaligned(log_forget_t) || misaligned(t_batch))
     return PATH_ERR_UNSUPPORTED;
+  if (H > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
   const int64_t S = splits > 0 ? splits : decode_auto_splits(t + 1);
   if (S > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
   if (workspace_bytes < (size_t)(BH * S * (int64_t)(d + 2) * 4)) return PATH_ERR_INVALID_ARG;
   if (BH > kMaxGridY) return PATH_ERR_UNSUPPORTED;
-  return from_hip(decode_step(dtype == PATH_DTYPE_BF16, d, kcache, vcache, capacity, t, q_t, k_t, v_t, w_t, beta_t,
-                              out, lse, BH, scale, (int)S, static_cast<float*>(workspace),
-                              static_cast<hipStream_t>(stream)));
+  return from_hip(decode_step(dtype == PATH_DTYPE_BF16, d, kcache, vcache, fcache, capacity, t, t_batch, (int)H, q_t,
+                              k_t, v_t, w_t, beta_t, log_forget_t, out, lse, BH, scale, (int)S,
+                              static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

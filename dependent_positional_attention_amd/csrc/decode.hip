@@ -12,6 +12,12 @@
 // (running max, sum, partial output slice).  Groups are merged through LDS and
 // the split's (m, l, o[d]) partial goes to the workspace.
 // Kernel 2 (combine): one workgroup per (b, h) merges the splits.
+//
+// PaTH-FoX (same page, section 2): each slot also carries its forget bias
+// sum_{s=j+1..t} f_s as an fp32 value that grows in place by the newest gate,
+// exactly like the keys absorb the newest transition; the new slot starts at 0.
+// Ragged batches: an optional per-sequence token count replaces the uniform t;
+// the split of the key range is sized for the uniform bound.
 #include "common.h"
 
 namespace pathattn {
@@ -76,11 +82,19 @@ __device__ __forceinline__ float group_sum(float x) {
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
 
-template <typename T, int D>
+// Token count of sequence b: the uniform t, or t_batch[b] when given; -1 marks an entry outside [0, t].
+__device__ __forceinline__ int64_t seq_tokens(const int* t_batch, int64_t bh, int H, int64_t t) {
+  if (t_batch == nullptr) return t;
+  const int64_t tb = t_batch[bh / H];
+  return (tb < 0 || tb > t) ? -1 : tb;
+}
+
+template <typename T, int D, bool FOX>
 __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
-    T* __restrict__ kc, T* __restrict__ vc, int64_t cap, int64_t t, const T* __restrict__ q_t,
-    const T* __restrict__ k_t, const T* __restrict__ v_t, const T* __restrict__ w_t, const float* __restrict__ beta_t,
-    float scale_log2, int splits, int64_t keys_per_split, float* __restrict__ part) {
+    T* __restrict__ kc, T* __restrict__ vc, float* __restrict__ fc, int64_t cap, int64_t t_max,
+    const int* __restrict__ t_batch, int H, const T* __restrict__ q_t, const T* __restrict__ k_t,
+    const T* __restrict__ v_t, const T* __restrict__ w_t, const float* __restrict__ beta_t,
+    const float* __restrict__ f_t, float scale_log2, int splits, int64_t keys_per_split, float* __restrict__ part) {
   constexpr int VN = Vec16<T>::N;  // elements per 16-byte vector
   constexpr int LPK = D / VN;      // lanes per key
   constexpr int GPB = kDecThreads / LPK;  // key groups per block
@@ -91,6 +105,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
   const int tid = threadIdx.x;
   const int grp = tid / LPK, sub = tid % LPK;
 
+  const int64_t t = seq_tokens(t_batch, bh, H, t_max);  // -1: no keys, nothing written
   const int64_t j0 = (int64_t)split * keys_per_split;
   int64_t j1 = j0 + keys_per_split;
   if (j1 > t + 1) j1 = t + 1;
@@ -105,6 +120,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
   const float beta = beta_t[bh];
   T* kb = kc + (size_t)bh * cap * D;
   T* vb = vc + (size_t)bh * cap * D;
+  float* fb = FOX ? fc + (size_t)bh * cap : nullptr;
+  const float fnew = FOX ? f_t[bh] : 0.f;
 
   float mrun = -INFINITY, lrun = 0.f, o[VN];
 #pragma unroll
@@ -113,14 +130,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
   for (int64_t base = j0 + grp; base < j1; base += (int64_t)GPB * kDecUnroll) {
     uint4 kr[kDecUnroll], vr[kDecUnroll];
     int64_t jj[kDecUnroll];
+    float fb_old[kDecUnroll];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       jj[u] = base + (int64_t)u * GPB;
       kr[u] = make_uint4(0u, 0u, 0u, 0u);  // keys past the range contribute exp2(-inf) * 0
       vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      fb_old[u] = 0.f;
       if (jj[u] < j1) {
         if (jj[u] < t) {
           kr[u] = *((const uint4*)(kb + jj[u] * D) + sub);
+          if constexpr (FOX) fb_old[u] = fb[jj[u]];
         } else {  // jj == t: the new token
           kr[u] = *((const uint4*)(k_t + bh * D) + sub);
         }
@@ -135,6 +155,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
       unpack16<T>(kr[u], kf);
       unpack16<T>(vr[u], vf[u]);
       const bool live = jj[u] < j1;
+      float bias = 0.f;  // forget bias of the slot after this step (the new slot: 0)
+      if constexpr (FOX) {
+        if (live && jj[u] < t) bias = fb_old[u] + fnew;
+        if (live && sub == 0) fb[jj[u]] = bias;
+      }
       if (live && jj[u] < t) {
         float pd = 0.f;
 #pragma unroll
@@ -153,7 +178,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
 #pragma unroll
       for (int x = 0; x < VN; ++x) sd += qv[x] * kf[x];
       sd = group_sum<LPK>(sd);
-      z[u] = live ? sd * scale_log2 : -INFINITY;
+      z[u] = live ? sd * scale_log2 + (FOX ? bias * kLog2e : 0.f) : -INFINITY;
     }
     float bm = z[0];
 #pragma unroll
@@ -207,8 +232,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part, int splits,
+                                                            const int* __restrict__ t_batch, int H, int64_t t_max,
                                                             T* __restrict__ out, float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;
+  if (seq_tokens(t_batch, bh, H, t_max) < 0) {  // invalid token count: NaN out, nothing else touched
+    for (int x = threadIdx.x; x < D; x += blockDim.x) out[bh * D + x] = from_f32<T>(__builtin_nanf(""));
+    if (lse != nullptr && threadIdx.x == 0) lse[bh] = __builtin_nanf("");
+    return;
+  }
   const float* pp = part + (size_t)bh * splits * (D + 2);
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
@@ -230,18 +261,24 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 }
 
 template <typename T, int D>
-static hipError_t launch_decode(void* kc, void* vc, int64_t cap, int64_t t, const void* q_t, const void* k_t,
-                                const void* v_t, const void* w_t, const float* beta_t, void* out, float* lse,
-                                int64_t BH, float scale, int splits, float* part, hipStream_t st) {
+static hipError_t launch_decode(void* kc, void* vc, float* fc, int64_t cap, int64_t t, const int* t_batch, int H,
+                                const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                                const float* beta_t, const float* f_t, void* out, float* lse, int64_t BH, float scale,
+                                int splits, float* part, hipStream_t st) {
   const int64_t keys = t + 1;
   const int64_t kps = (keys + splits - 1) / splits;
   dim3 grid((unsigned)splits, (unsigned)BH);
-  decode_update_attend_kernel<T, D><<<grid, kDecThreads, 0, st>>>(
-      (T*)kc, (T*)vc, cap, t, (const T*)q_t, (const T*)k_t, (const T*)v_t, (const T*)w_t, beta_t, scale * kLog2e,
-      splits, kps, part);
+  if (f_t != nullptr)
+    decode_update_attend_kernel<T, D, true><<<grid, kDecThreads, 0, st>>>(
+        (T*)kc, (T*)vc, fc, cap, t, t_batch, H, (const T*)q_t, (const T*)k_t, (const T*)v_t, (const T*)w_t, beta_t,
+        f_t, scale * kLog2e, splits, kps, part);
+  else
+    decode_update_attend_kernel<T, D, false><<<grid, kDecThreads, 0, st>>>(
+        (T*)kc, (T*)vc, nullptr, cap, t, t_batch, H, (const T*)q_t, (const T*)k_t, (const T*)v_t, (const T*)w_t,
+        beta_t, nullptr, scale * kLog2e, splits, kps, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<T, D><<<(unsigned)BH, 64, 0, st>>>(part, splits, (T*)out, lse);
+  decode_combine_kernel<T, D><<<(unsigned)BH, 64, 0, st>>>(part, splits, t_batch, H, t, (T*)out, lse);
   return hipGetLastError();
 }
 
@@ -253,21 +290,58 @@ int64_t decode_auto_splits(int64_t keys) {
   return s < 1 ? 1 : s;
 }
 
-hipError_t decode_step(bool bf16, int d, void* kc, void* vc, int64_t cap, int64_t t, const void* q_t,
-                       const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out, float* lse,
-                       int64_t BH, float scale, int splits, float* part, hipStream_t st) {
-#define PATHATTN_DEC_CASE(DD)                                                                                     \
-  if (d == DD)                                                                                                    \
-    return bf16 ? launch_decode<__bf16, DD>(kc, vc, cap, t, q_t, k_t, v_t, w_t, beta_t, out, lse, BH, scale,     \
-                                            splits, part, st)                                                    \
-                : launch_decode<float, DD>(kc, vc, cap, t, q_t, k_t, v_t, w_t, beta_t, out, lse, BH, scale, splits, \
-                                           part, st);
+hipError_t decode_step(bool bf16, int d, void* kc, void* vc, float* fc, int64_t cap, int64_t t, const int* t_batch,
+                       int H, const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                       const float* beta_t, const float* f_t, void* out, float* lse, int64_t BH, float scale,
+                       int splits, float* part, hipStream_t st) {
+#define PATHATTN_DEC_CASE(DD)                                                                                    \
+  if (d == DD)                                                                                                   \
+    return bf16 ? launch_decode<__bf16, DD>(kc, vc, fc, cap, t, t_batch, H, q_t, k_t, v_t, w_t, beta_t, f_t, out, \
+                                            lse, BH, scale, splits, part, st)                                   \
+                : launch_decode<float, DD>(kc, vc, fc, cap, t, t_batch, H, q_t, k_t, v_t, w_t, beta_t, f_t, out,  \
+                                           lse, BH, scale, splits, part, st);
   PATHATTN_DEC_CASE(16)
   PATHATTN_DEC_CASE(32)
   PATHATTN_DEC_CASE(64)
   PATHATTN_DEC_CASE(128)
 #undef PATHATTN_DEC_CASE
   return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------------------------ prompt slot biases
+// PaTH-FoX slot biases after a prompt of L tokens: fc[j] = sum_{s=j+1..L-1} f_s.  One block per (b, h):
+// thread i sums its contiguous segment, a suffix scan over the 256 segment sums (LDS) gives what lies
+// to the right of each segment, and each thread then walks its segment right to left.
+__global__ __launch_bounds__(256) void slot_bias_kernel(const float* __restrict__ logf, int64_t L, int64_t cap,
+                                                        float* __restrict__ fc) {
+  __shared__ float seg[256];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* f = logf + (size_t)bh * L;
+  const int64_t per = (L + 255) / 256;
+  const int64_t a = (int64_t)tid * per < L ? (int64_t)tid * per : L;
+  const int64_t b = a + per < L ? a + per : L;
+  float s = 0.f;
+  for (int64_t j = a; j < b; ++j) s += f[j];
+  seg[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive suffix sums of the segment sums
+    const float v = seg[tid] + (tid + off < 256 ? seg[tid + off] : 0.f);
+    __syncthreads();
+    seg[tid] = v;
+    __syncthreads();
+  }
+  float acc = tid + 1 < 256 ? seg[tid + 1] : 0.f;  // gates after this segment
+  float* out = fc + (size_t)bh * cap;
+  for (int64_t j = b - 1; j >= a; --j) {
+    out[j] = acc;
+    acc += f[j];
+  }
+}
+
+hipError_t slot_bias_run(const float* logf, int64_t BH, int64_t L, int64_t cap, float* fc, hipStream_t st) {
+  slot_bias_kernel<<<dim3((unsigned)BH), 256, 0, st>>>(logf, L, cap, fc);
+  return hipGetLastError();
 }
 
 }  // namespace pathattn

@@ -65,9 +65,10 @@ def lib():
         L.path_attn_prep.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32, vp, sz, vp]
         L.path_attn_scan.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp, sz, vp]
         L.path_decode_workspace_bytes.argtypes = [i64, i64, i32, i64, i32, ctypes.POINTER(sz)]
-        L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, f32, i32, i32,
-                                       vp, sz, vp]
-        L.path_attn_cache_from_prefill.argtypes = [vp, vp, sz, vp, vp, i64, i64, i64, i64, i32, i32, i32, i32, vp]
+        L.path_decode_step.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, f32,
+                                       i32, i32, vp, sz, vp]
+        L.path_attn_cache_from_prefill.argtypes = [vp, vp, vp, sz, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, i32,
+                                                   vp]
         for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd", "path_attn_prep",
                   "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step", "path_attn_cache_from_prefill"):
             getattr(L, f).restype = i32
@@ -189,11 +190,13 @@ def path_attn_scan(v, log_forget=None, *, chunk: int = 64, transport: str = "bf1
     return out, lse
 
 
-def path_attn_cache_from_prefill(v, *, workspace, capacity: Optional[int] = None, chunk: int = 64,
-                                 transport: str = "bf16", kcache=None, vcache=None,
-                                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+def path_attn_cache_from_prefill(v, log_forget=None, *, workspace, capacity: Optional[int] = None, chunk: int = 64,
+                                 transport: str = "bf16", kcache=None, vcache=None, fcache=None,
+                                 stream=None):
     """Decode caches [B,H,capacity,d] after a prompt, from a workspace filled by path_attn_prep /
-    path_attn_fwd with the same arguments.  v: the prompt's values [B,H,L,d]."""
+    path_attn_fwd with the same arguments.  v: the prompt's values [B,H,L,d].  With the prompt's
+    log_forget [B,H,L] (PaTH-FoX) the slot biases fcache [B,H,capacity] fp32 are filled too.
+    Returns (kcache, vcache, fcache) (fcache None for plain PaTH)."""
     _require(v, "v")
     B, H, L, d = v.shape
     if kcache is None:
@@ -206,11 +209,18 @@ def path_attn_cache_from_prefill(v, *, workspace, capacity: Optional[int] = None
     if vcache is None:
         vcache = torch.empty_like(kcache)
     _require(vcache, "vcache", v.dtype, kcache.shape)
+    if log_forget is not None:
+        _require(log_forget, "log_forget", torch.float32, (B, H, L))
+        if fcache is None:
+            fcache = torch.empty((B, H, cap), device=v.device, dtype=torch.float32)
+        _require(fcache, "fcache", torch.float32, (B, H, cap))
+    elif fcache is not None:
+        raise ValueError("fcache is filled from log_forget: pass both or neither")
     _require(workspace, "workspace")
     _check("path_attn_cache_from_prefill", lib().path_attn_cache_from_prefill(
-        _ptr(v), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(kcache), _ptr(vcache), cap, B,
-        H, L, d, chunk, DTYPE[v.dtype], TRANSPORT[transport], _stream(stream)))
-    return kcache, vcache
+        _ptr(v), _ptr(log_forget), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(kcache),
+        _ptr(vcache), _ptr(fcache), cap, B, H, L, d, chunk, DTYPE[v.dtype], TRANSPORT[transport], _stream(stream)))
+    return kcache, vcache, fcache
 
 
 def path_decode_workspace_bytes(B, H, d, capacity, splits: int = 0) -> int:
@@ -220,16 +230,26 @@ def path_decode_workspace_bytes(B, H, d, capacity, splits: int = 0) -> int:
     return n.value
 
 
-def path_decode_step(kcache, vcache, t: int, q_t, k_t, v_t, w_t, beta_t, *, scale: Optional[float] = None,
-                     splits: int = 0, out=None, lse=None, workspace=None, stream=None,
-                     want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """One decode step.  kcache, vcache: [B,H,capacity,d] (updated in place); q_t..w_t: [B,H,d]; beta_t: [B,H]."""
+def path_decode_step(kcache, vcache, t: int, q_t, k_t, v_t, w_t, beta_t, log_forget_t=None, *, fcache=None,
+                     t_batch=None, scale: Optional[float] = None, splits: int = 0, out=None, lse=None,
+                     workspace=None, stream=None, want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One decode step.  kcache, vcache: [B,H,capacity,d] (updated in place); q_t..w_t: [B,H,d]; beta_t: [B,H].
+
+    PaTH-FoX: log_forget_t [B,H] and fcache [B,H,capacity] fp32 (slot biases, updated in place).
+    Ragged batch: t_batch [B] int32 per-sequence token counts, each <= t (t sizes the key split)."""
     _require(kcache, "kcache")
     B, H, cap, d = kcache.shape
     _require(vcache, "vcache", kcache.dtype, kcache.shape)
     for name, x in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
         _require(x, name, kcache.dtype, (B, H, d))
     _require(beta_t, "beta_t", torch.float32, (B, H))
+    if (log_forget_t is None) != (fcache is None):
+        raise ValueError("PaTH-FoX decode needs both log_forget_t and fcache")
+    if log_forget_t is not None:
+        _require(log_forget_t, "log_forget_t", torch.float32, (B, H))
+        _require(fcache, "fcache", torch.float32, (B, H, cap))
+    if t_batch is not None:
+        _require(t_batch, "t_batch", torch.int32, (B,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -241,7 +261,7 @@ def path_decode_step(kcache, vcache, t: int, q_t, k_t, v_t, w_t, beta_t, *, scal
                                 dtype=torch.uint8)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("path_decode_step", lib().path_decode_step(
-        _ptr(kcache), _ptr(vcache), cap, int(t), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t), _ptr(out),
-        _ptr(lse), B, H, d, float(scale), DTYPE[kcache.dtype], int(splits), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        _ptr(kcache), _ptr(vcache), _ptr(fcache), cap, int(t), _ptr(t_batch), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+        _ptr(w_t), _ptr(beta_t), _ptr(log_forget_t), _ptr(out), _ptr(lse), B, H, d, float(scale),
+        DTYPE[kcache.dtype], int(splits), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse

@@ -164,26 +164,38 @@ path_status path_decode_workspace_bytes(int64_t B, int64_t H, int d, int64_t cap
                                         size_t* bytes);
 
 /*
- * One PaTH decode step (summary, section 3 "inference": the cached keys are
- * updated in place with the current transition, so no transition vectors are
- * cached, and the attention itself is a FlashDecoding-style split-key pass).
+ * One PaTH / PaTH-FoX decode step (summary, section 3 "inference": the cached
+ * keys are updated in place with the current transition, so no transition
+ * vectors are cached, and the attention itself is a FlashDecoding-style
+ * split-key pass).
  *
- *   kcache, vcache [B,H,capacity,d] dtype  slots 0..t-1 hold the current cache
- *   t              tokens already cached (same for the whole batch), 0 <= t < capacity
+ *   kcache, vcache [B,H,capacity,d] dtype  slots 0..t_b-1 hold the current cache
+ *   fcache         [B,H,capacity] fp32 or NULL  PaTH-FoX slot biases (see below)
+ *   t              tokens already cached, the same for the whole batch, 0 <= t < capacity;
+ *                  with t_batch, an upper bound on every entry of t_batch
+ *   t_batch        [B] int32 or NULL       per-sequence token counts t_b (ragged batch);
+ *                  NULL means t_b = t for every sequence
  *   q_t,k_t,v_t,w_t [B,H,d] dtype          the new token's query, key, value, direction
  *   beta_t         [B,H] fp32              the new token's transition strength
+ *   log_forget_t   [B,H] fp32 or NULL      PaTH-FoX: the new token's log forget gate f_t
  *   out            [B,H,d] dtype           attention output of the new token (written)
  *   lse            [B,H] fp32 or NULL      natural-log log-sum-exp (written)
  *
- * Effect, for every (b, h): k_j <- (I - beta_t w_t w_t^T) k_j for j < t, rounded
- * to dtype and written back in place; slot t <- (k_t, v_t) untransformed; then
- * out = softmax_j(scale * q_t . k_j) v_j over j = 0..t.  Slots beyond t are
- * untouched.  Supported: d in {16,32,64,128}, dtype F32 or BF16.
+ * Effect, for every (b, h) with t_b = t_batch[b] (or t): k_j <- (I - beta_t w_t w_t^T) k_j for
+ * j < t_b, rounded to dtype and written back in place; slot t_b <- (k_t, v_t) untransformed;
+ * then out = softmax_j(scale * q_t . k_j + bias_j) v_j over j = 0..t_b.  Slots beyond t_b are
+ * untouched.  PaTH-FoX (summary, section 2 "PaTH-FoX": bias_j = sum_{s=j+1..t_b} f_s): fcache
+ * holds each slot's bias as of the previous step; the step adds f_t to slots j < t_b in place
+ * and sets slot t_b to 0, the same in-place rule the keys follow.  Plain PaTH: both fcache and
+ * log_forget_t NULL (bias 0); passing exactly one of them is PATH_ERR_INVALID_ARG.  An entry of
+ * t_batch outside [0, t] is not an error the host can see: that sequence's out and lse are NaN
+ * and none of its slots are touched.  Supported: d in {16,32,64,128}, dtype F32 or BF16.
  */
-path_status path_decode_step(void* kcache, void* vcache, int64_t capacity, int64_t t, const void* q_t,
-                             const void* k_t, const void* v_t, const void* w_t, const float* beta_t, void* out,
-                             float* lse, int64_t B, int64_t H, int d, float scale, int dtype, int splits,
-                             void* workspace, size_t workspace_bytes, void* stream);
+path_status path_decode_step(void* kcache, void* vcache, float* fcache, int64_t capacity, int64_t t,
+                             const int* t_batch, const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                             const float* beta_t, const float* log_forget_t, void* out, float* lse, int64_t B,
+                             int64_t H, int d, float scale, int dtype, int splits, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Prefill -> decode hand-off: fills a decode cache from a prefill workspace
@@ -197,19 +209,21 @@ path_status path_decode_step(void* kcache, void* vcache, int64_t capacity, int64
  * can then continue at t = L.
  *
  *   v               [B,H,L,d] dtype         the prompt's values (copied)
- *   workspace       prefill workspace (read only; log_forget terms unused)
+ *   log_forget      [B,H,L] fp32 or NULL    PaTH-FoX: the prompt's gates
+ *   workspace       prefill workspace (read only)
  *   kcache, vcache  [B,H,capacity,d] dtype  slots 0..L-1 written; slots >= L untouched
+ *   fcache          [B,H,capacity] fp32 or NULL  PaTH-FoX: slot j <- sum_{s=j+1..L-1} f_s
+ *                   (the slot bias path_decode_step expects); given iff log_forget is
  *   capacity        >= L (PATH_ERR_INVALID_ARG otherwise)
  *
  * The bf16 path chains the chunk products with fp32 accumulation (the running
  * product enters the matrix cores as hi + lo bf16) and rounds each slot to bf16
- * once; the fp32 path works in fp32.  The slots do not depend on the forget
- * gates, so a PaTH-FoX prompt fills its cache with the same call (the running
- * forget sums a FoX decode also needs are not produced here).
+ * once; the fp32 path works in fp32.  Slot biases are fp32 sums.
  */
-path_status path_attn_cache_from_prefill(const void* v, const void* workspace, size_t workspace_bytes, void* kcache,
-                                         void* vcache, int64_t capacity, int64_t B, int64_t H, int64_t L, int d,
-                                         int chunk, int dtype, int transport, void* stream);
+path_status path_attn_cache_from_prefill(const void* v, const float* log_forget, const void* workspace,
+                                         size_t workspace_bytes, void* kcache, void* vcache, float* fcache,
+                                         int64_t capacity, int64_t B, int64_t H, int64_t L, int d, int chunk,
+                                         int dtype, int transport, void* stream);
 
 #ifdef __cplusplus
 }

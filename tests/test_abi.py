@@ -109,10 +109,10 @@ def test_fwd_validation(L):
     assert fwd(L, B=0, q=None, ws=None) == OK
 
 
-def dec(L, kc=FAKE, vc=FAKE, cap=128, t=10, q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, out=FAKE, lse=None, B=1, H=1,
-        d=64, scale=0.125, dtype=BF16, splits=0, ws=FAKE, ws_n=1 << 20):
-    return L.path_decode_step(kc, vc, cap, t, q, k, v, w, beta, out, lse, B, H, d, scale, dtype, splits, ws, ws_n,
-                              None)
+def dec(L, kc=FAKE, vc=FAKE, fc=None, cap=128, t=10, tb=None, q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, f=None,
+        out=FAKE, lse=None, B=1, H=1, d=64, scale=0.125, dtype=BF16, splits=0, ws=FAKE, ws_n=1 << 20):
+    return L.path_decode_step(kc, vc, fc, cap, t, tb, q, k, v, w, beta, f, out, lse, B, H, d, scale, dtype, splits, ws,
+                              ws_n, None)
 
 
 def test_decode_validation(L):
@@ -125,6 +125,10 @@ def test_decode_validation(L):
     assert dec(L, vc=MISALIGNED) == UNSUPPORTED
     assert dec(L, ws_n=16) == INVALID
     assert dec(L, splits=-2) == INVALID
+    assert dec(L, fc=FAKE) == INVALID  # FoX slot biases without the gate
+    assert dec(L, f=FAKE) == INVALID  # gate without slot biases
+    assert dec(L, fc=MISALIGNED, f=FAKE) == UNSUPPORTED
+    assert dec(L, tb=MISALIGNED) == UNSUPPORTED
     assert dec(L, B=0, kc=None) == OK
     n = ctypes.c_size_t(0)
     assert L.path_decode_workspace_bytes(32, 24, 64, 65536 + 128, 0, ctypes.byref(n)) == OK
@@ -132,9 +136,10 @@ def test_decode_validation(L):
     assert L.path_decode_workspace_bytes(1, 1, 48, 100, 0, ctypes.byref(n)) == UNSUPPORTED
 
 
-def handoff(L, v=FAKE, ws=FAKE, ws_n=1 << 40, kc=FAKE, vc=FAKE, cap=4096, B=1, H=2, Lq=4096, d=64, chunk=64,
-            dtype=BF16, transport=0):
-    return L.path_attn_cache_from_prefill(v, ws, ws_n, kc, vc, cap, B, H, Lq, d, chunk, dtype, transport, None)
+def handoff(L, v=FAKE, lf=None, ws=FAKE, ws_n=1 << 40, kc=FAKE, vc=FAKE, fc=None, cap=4096, B=1, H=2, Lq=4096, d=64,
+            chunk=64, dtype=BF16, transport=0):
+    return L.path_attn_cache_from_prefill(v, lf, ws, ws_n, kc, vc, fc, cap, B, H, Lq, d, chunk, dtype, transport,
+                                          None)
 
 
 def test_cache_handoff_validation(L):
@@ -148,6 +153,9 @@ def test_cache_handoff_validation(L):
     assert handoff(L, chunk=8) == UNSUPPORTED
     assert handoff(L, transport=5) == INVALID
     assert handoff(L, B=-1) == INVALID
+    assert handoff(L, lf=FAKE) == INVALID  # FoX gates without a slot-bias output
+    assert handoff(L, fc=FAKE) == INVALID
+    assert handoff(L, lf=FAKE, fc=MISALIGNED) == UNSUPPORTED
     # an empty prompt or batch is valid and enqueues nothing
     assert handoff(L, Lq=0, v=None, ws=None, kc=None, vc=None) == OK
     assert handoff(L, H=0, v=None) == OK

@@ -97,3 +97,111 @@ def test_split_count_does_not_change_the_cache():
         assert np.array_equal(kbits, res[0][0])
         ma, rel = errors(o, res[0][1])
         assert ma <= 1e-3 and rel <= 1e-3
+
+
+def initial_slot_bias(B, H, T0, cap, seed):
+    """PaTH-FoX slot biases of a T0-token cache: suffix sums of gates drawn like the prompts' (fp32 values)."""
+    g = synth.logsigmoid(np.random.default_rng(seed).normal(3.0, 1.0, (B, H, T0)))
+    suf = np.zeros((B, H, cap), dtype=np.float32)
+    rev = np.cumsum(g[:, :, ::-1], axis=-1)[:, :, ::-1]  # sum_{s>=j}
+    suf[:, :, :T0 - 1] = rev[:, :, 1:]
+    return suf
+
+
+def fox_gates(S, B, H, seed):
+    return synth.logsigmoid(np.random.default_rng(seed + 1).normal(3.0, 1.0, (S, B, H))).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 32), ("bf16", 128)])
+def test_fox_decode_with_cache(dtype, d):
+    """PaTH-FoX decode: slot biases grow in place by each new gate; outputs and the bias state vs the oracle."""
+    B, H, T0, S = 2, 3, 900, 4
+    cap = T0 + S + 3
+    print(f"[case] fox decode dtype={dtype} d={d} T0={T0} steps={S}", flush=True)
+    ck, cv = synth.make_decode_cache(B, H, T0, d, dtype=dtype, seed=d + 1)
+    steps = synth.make_decode_steps(S, B, H, d, dtype=dtype, seed=d + 1)
+    fc0 = initial_slot_bias(B, H, T0, cap, seed=d)
+    gates = fox_gates(S, B, H, seed=d)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.zeros((B, H, cap, d), device="cuda", dtype=td)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :T0] = dev(ck, dtype)
+    vc[:, :, :T0] = dev(cv, dtype)
+    fc = dev_f32(fc0)
+    outs, lses = [], []
+    for s in range(S):
+        o, l = native.path_decode_step(kc, vc, T0 + s, dev(steps.q[s], dtype), dev(steps.k[s], dtype),
+                                       dev(steps.v[s], dtype), dev(steps.w[s], dtype), dev_f32(steps.beta[s]),
+                                       dev_f32(gates[s]), fcache=fc, scale=steps.scale)
+        outs.append(host(o))
+        lses.append(host(l))
+    torch.cuda.synchronize()
+    BH = B * H
+    okc, ovc = np.zeros((BH, cap, d)), np.zeros((BH, cap, d))
+    okc[:, :T0] = ck.reshape(BH, T0, d)
+    ovc[:, :T0] = cv.reshape(BH, T0, d)
+    ofc = fc0.reshape(BH, cap).astype(np.float64)
+    sh = lambda x: x.reshape(S, BH, -1) if x.ndim == 4 else x.reshape(S, BH)
+    ro, rl = oracle.decode(okc, ovc, T0, sh(steps.q), sh(steps.k), sh(steps.v), sh(steps.w), sh(steps.beta),
+                           steps.scale, fcache=ofc, logf=sh(gates))
+    assert_parity(np.stack(outs), ro.reshape(S, B, H, d), dtype, "out")
+    assert_parity(np.stack(lses), rl.reshape(S, B, H), dtype, "lse")
+    # fp32 slot biases: one rounding per added gate
+    want = ofc.reshape(B, H, cap)[:, :, :T0 + S]
+    got = host(fc)[:, :, :T0 + S]
+    bound = (S + 1) * 2.0 ** -24 * np.max(np.abs(want)) + 1e-7
+    assert np.max(np.abs(got - want)) <= bound, f"slot bias error {np.max(np.abs(got - want)):.3e} > {bound:.3e}"
+    assert np.all(host(fc)[:, :, T0 + S:] == 0)
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_ragged_batch(fox):
+    """Per-sequence token counts: each sequence matches the oracle run on its own cache; an out-of-range count
+    gives NaN for that sequence and leaves its slots untouched."""
+    B, H, d, S = 4, 2, 64, 2
+    counts = np.array([1500, 37, 0, -1], dtype=np.int32)  # the last one is invalid
+    t_bound = 1500
+    cap = t_bound + S + 1
+    print(f"[case] ragged decode fox={fox} counts={counts.tolist()}", flush=True)
+    ck, cv = synth.make_decode_cache(B, H, cap, d, dtype="bf16", seed=11)
+    steps = synth.make_decode_steps(S, B, H, d, dtype="bf16", seed=11)
+    gates = fox_gates(S, B, H, seed=11) if fox else None
+    # each sequence's slot biases as of its own count (suffix sums of its prompt gates)
+    fc0 = np.zeros((B, H, cap), dtype=np.float32)
+    if fox:
+        g = synth.logsigmoid(np.random.default_rng(12).normal(3.0, 1.0, (B, H, cap)))
+        for b, tb0 in enumerate(counts):
+            if tb0 > 1:
+                rev = np.cumsum(g[b, :, :tb0][:, ::-1], axis=-1)[:, ::-1]
+                fc0[b, :, :tb0 - 1] = rev[:, 1:]
+    kc, vc = dev(ck, "bf16"), dev(cv, "bf16")
+    fc = dev_f32(fc0) if fox else None
+    kc_before = kc.clone()
+    outs, lses = [], []
+    for s in range(S):
+        tb = torch.from_numpy(np.where(counts >= 0, counts + s, counts).astype(np.int32)).cuda()
+        o, l = native.path_decode_step(kc, vc, t_bound + s, dev(steps.q[s], "bf16"), dev(steps.k[s], "bf16"),
+                                       dev(steps.v[s], "bf16"), dev(steps.w[s], "bf16"), dev_f32(steps.beta[s]),
+                                       dev_f32(gates[s]) if fox else None, fcache=fc, t_batch=tb, scale=steps.scale)
+        outs.append(host(o))
+        lses.append(host(l))
+    torch.cuda.synchronize()
+    go, gl = np.stack(outs), np.stack(lses)
+    for b, tb0 in enumerate(counts):
+        if tb0 < 0:
+            assert np.all(np.isnan(go[:, b])) and np.all(np.isnan(gl[:, b]))
+            assert torch.equal(kc[b], kc_before[b]), "an invalid sequence's slots were touched"
+            if fox:
+                assert np.array_equal(host(fc)[b], fc0[b].astype(np.float64))
+            continue
+        okc, ovc = np.zeros((H, cap, d)), np.zeros((H, cap, d))
+        okc[:, :tb0] = ck[b, :, :tb0]
+        ovc[:, :tb0] = cv[b, :, :tb0]
+        sl = lambda x: np.ascontiguousarray(x[:, b])
+        kw = dict(fcache=fc0[b].astype(np.float64), logf=sl(gates)) if fox else {}
+        ro, rl = oracle.decode(okc, ovc, int(tb0), sl(steps.q), sl(steps.k), sl(steps.v), sl(steps.w),
+                               sl(steps.beta), steps.scale, **kw)
+        assert_parity(go[:, b], ro, "bf16", f"out seq {b}")
+        assert_parity(gl[:, b], rl, "bf16", f"lse seq {b}")
+        # slots past this sequence's own count are untouched
+        assert torch.equal(kc[b, :, tb0 + S:], kc_before[b, :, tb0 + S:])

@@ -28,23 +28,27 @@ def torch_dtype(dtype):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
-def prefill_cache(x, chunk, transport, cap, L=None):
-    """Prefill (prep) on the first L tokens of x, then fill caches of `cap` slots pre-set to SENTINEL."""
+def prefill_cache(x, chunk, transport, cap, L=None, fox=False):
+    """Prefill on the first L tokens of x, then fill caches of `cap` slots pre-set to SENTINEL
+    (and, for PaTH-FoX, the slot biases)."""
     B, H, Lx, d = x.q.shape
     L = Lx if L is None else L
     cut = lambda a: np.ascontiguousarray(a[:, :, :L])
     t = {n: dev(cut(getattr(x, n)), x.dtype) for n in ("q", "k", "v", "w")}
     beta = dev_f32(cut(x.beta))
+    logf = dev_f32(cut(x.logf)) if fox else None
     td = torch_dtype(x.dtype)
     nbytes = native.path_attn_fwd_workspace_bytes(B, H, L, d, chunk, td, transport)
     ws = torch.zeros(max(nbytes, 16), device="cuda", dtype=torch.uint8)
-    out, lse = native.path_attn_fwd(t["q"], t["k"], t["v"], t["w"], beta, scale=x.scale, chunk=chunk,
+    out, lse = native.path_attn_fwd(t["q"], t["k"], t["v"], t["w"], beta, logf, scale=x.scale, chunk=chunk,
                                     transport=transport, workspace=ws)
     kc = torch.full((B, H, cap, d), SENTINEL, device="cuda", dtype=td)
     vc = torch.full_like(kc, SENTINEL)
-    native.path_attn_cache_from_prefill(t["v"], workspace=ws, chunk=chunk, transport=transport, kcache=kc,
-                                        vcache=vc)
+    fc = torch.full((B, H, cap), SENTINEL, device="cuda", dtype=torch.float32) if fox else None
+    native.path_attn_cache_from_prefill(t["v"], logf, workspace=ws, chunk=chunk, transport=transport, kcache=kc,
+                                        vcache=vc, fcache=fc)
     torch.cuda.synchronize()
+    t["fcache"] = fc
     return kc, vc, t, (out, lse)
 
 
@@ -168,3 +172,39 @@ def test_full_size_handoff_sampled(B, H, L, chunk, transport, recipe):
         ro, rl = oracle.fwd(sl(x.q), sl(x.k), sl(x.v), sl(x.w), sl(x.beta), scale=x.scale, rows=[L])
         assert_parity(go[b, h], ro[0, 0, 0], "bf16", f"decode out head {(b, h)}")
         assert_parity(gl[b, h], rl[0, 0, 0], "bf16", f"decode lse head {(b, h)}")
+
+
+@pytest.mark.parametrize("dtype,chunk,transport,L,S", [
+    ("bf16", 64, "bf16", 700, 3),
+    ("bf16", 128, "bf16x3", 4096, 2),
+    ("f32", 32, "bf16", 150, 2),
+])
+def test_fox_prefill_then_decode(dtype, chunk, transport, L, S):
+    """PaTH-FoX prompt: slot biases are the suffix sums of the prompt's gates, and FoX decode from the handed-off
+    cache gives the oracle's FoX prefill rows L..L+S-1."""
+    print(f"[case] fox prefill+decode dtype={dtype} chunk={chunk} transport={transport} L={L} S={S}", flush=True)
+    B, H = 2, 2
+    d = 64 if dtype == "bf16" else 32
+    x = synth.make_fwd_inputs(B, H, L + S, d, recipe="fox", dtype=dtype, seed=21)
+    kc, vc, t, _ = prefill_cache(x, chunk, transport, L + S, L=L, fox=True)
+    fc = t["fcache"]
+    got = host(fc)
+    for b in range(B):
+        for h in range(H):
+            want = oracle.cache_bias(x.logf[b, h, :L])
+            bound = 1e-5 * np.sum(np.abs(x.logf[b, h, :L])) + 1e-7
+            err = np.max(np.abs(got[b, h, :L] - want))
+            assert err <= bound, f"slot bias head {(b, h)}: {err:.3e} > {bound:.3e}"
+    assert np.all(got[:, :, L:] == SENTINEL)
+    outs, lses = [], []
+    for s in range(S):
+        tok = lambda a: dev(np.ascontiguousarray(a[:, :, L + s]), dtype)
+        o, l = native.path_decode_step(kc, vc, L + s, tok(x.q), tok(x.k), tok(x.v), tok(x.w),
+                                       dev_f32(np.ascontiguousarray(x.beta[:, :, L + s])),
+                                       dev_f32(np.ascontiguousarray(x.logf[:, :, L + s])), fcache=fc, scale=x.scale)
+        outs.append(host(o))
+        lses.append(host(l))
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf, scale=x.scale, rows=list(range(L, L + S)))
+    assert_parity(np.stack(outs, axis=2), ro, dtype, "fox decode out")
+    assert_parity(np.stack(lses, axis=2), rl, dtype, "fox decode lse")
