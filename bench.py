@@ -18,6 +18,8 @@ Also reported on the same JSON line:
   decode        batch 32, H=24, d=64, 65536 cached tokens, 128 steps timed back
                 to back: HBM bytes the step must move (cached keys read and
                 written back, cached values read) over the measured time.
+  chunk_sweep   the same prefill step at chunk 64, 128 and 256 (chunks above 64 are grouped
+                64-token sub-chunks; the scan moves its queries once per chunk).
   cache_handoff the prefill workspace turned into a decode cache (path_attn_cache_from_prefill)
                 at the prefill shape: time and HBM bytes it must move.
   long_context  B=1, H=24, L=32768: whole prefill step at chunk 64 and at
@@ -45,7 +47,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--transport", default="bf16", choices=["bf16", "bf16x3"])
     ap.add_argument("--fox", action="store_true", help="PaTH-FoX prefill (log-forget gates) instead of PaTH")
     ap.add_argument("--L", type=int, default=4096)
@@ -55,6 +57,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the 32K-token prefill at chunk 64 and 128")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the chunk 64 / 128 / 256 comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (a known-size reference for HBM counters)")
@@ -160,7 +163,7 @@ def bench_prefill(args):
         f"whole step {F / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s")
     res = dict(B=B, H=H, L=L, d=d, C=C, recipe=recipe, ms_step=ms_step, wall_ms=wall_ms, ms_prep=ms_prep,
                ms_scan=ms_scan, flops=F, scan_tflops=tflops, tokens_per_s=B * L / (ms_step * 1e-3))
-    return res, x, dict(v=v, ws=ws)
+    return res, x, dict(q=q, k=k, v=v, w=w, beta=beta, logf=logf, scale=x.scale, ws=ws)
 
 
 def bench_handoff(args, res, ctx):
@@ -193,6 +196,38 @@ def bench_handoff(args, res, ctx):
     return {"workload": f"prefill -> decode cache hand-off, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16",
             "ms": ms, "bytes": nbytes, "achieved_gbs": gbs, "peak_gbs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
             "chained_steps_per_head": M}
+
+
+def bench_chunks(args, ctx):
+    """Whole prefill step at chunk 64, 128 and 256 on the same inputs, interleaved round by round so
+    that clock drift treats every chunk size alike."""
+    import torch
+    from dependent_positional_attention_amd import native
+
+    q, k, v, w, beta, logf, scale = (ctx[n] for n in ("q", "k", "v", "w", "beta", "logf", "scale"))
+    B, H, L, d = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), device="cuda", dtype=torch.float32)
+    chunks = (64, 128, 256)
+    wss = {C: torch.empty(native.path_attn_fwd_workspace_bytes(B, H, L, d, C, torch.bfloat16, args.transport),
+                          device="cuda", dtype=torch.uint8) for C in chunks}
+    steps = {C: (lambda C=C: native.path_attn_fwd(q, k, v, w, beta, logf, scale=scale, chunk=C,
+                                                  transport=args.transport, out=out, lse=lse, workspace=wss[C]))
+             for C in chunks}
+    times = {C: [] for C in chunks}
+    for C in chunks:
+        steps[C]()
+    torch.cuda.synchronize()
+    for _ in range(4):
+        for C in chunks:
+            times[C].append(timed(steps[C], 5))
+    res = {}
+    for C in chunks:
+        ms = sorted(times[C])[len(times[C]) // 2]
+        res[f"chunk{C}"] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3)}
+        log(f"[bench] chunk sweep: chunk {C}: {ms:.3f} ms per step, {B * L / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+    return {"workload": f"PaTH prefill step at B={B}, H={H}, L={L}, d={d}, bf16, transport {args.transport}; "
+                        "median of 4 interleaved rounds of 5 steps", **res}
 
 
 def bench_cpu(x, args):
@@ -349,6 +384,7 @@ def main():
         del src, dst
     res, x, ctx = bench_prefill(args)
     handoff = bench_handoff(args, res, ctx)
+    sweep = None if args.no_sweep else bench_chunks(args, ctx)
     del ctx
     cpu = None if args.no_cpu else bench_cpu(x, args)
     dec = None if args.no_decode else bench_decode(args)
@@ -384,6 +420,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": dec,
         "cache_handoff": handoff,
+        "chunk_sweep": sweep,
         "long_context": long_ctx,
     }
     print(json.dumps(line), flush=True)

@@ -41,10 +41,19 @@ bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintpt
 
 bool valid_dtype(int dt) { return dt == PATH_DTYPE_F32 || dt == PATH_DTYPE_BF16; }
 
+// chunk 0 selects the chunk measured fastest for the path: 256 on the matrix-core path (the scan then
+// moves its queries once per 256 keys), 64 on the vector path.
+int resolve_chunk(int d, int dtype, int chunk) {
+  if (chunk != 0) return chunk;
+  if (dtype == PATH_DTYPE_BF16 && mfma_supported(d, 256)) return 256;
+  return 64;
+}
+
 // Which kernels serve (d, chunk, dtype): the matrix-core path for bf16 when built
 // for the shape, the vector path otherwise.
 path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype, int transport,
                      path_ws_layout* lay) {
+  chunk = resolve_chunk(d, dtype, chunk);
   if (B < 0 || H < 0 || L < 0 || d <= 0 || chunk <= 0) return PATH_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return PATH_ERR_UNSUPPORTED;
   if (transport != PATH_TRANSPORT_BF16 && transport != PATH_TRANSPORT_BF16X3) return PATH_ERR_INVALID_ARG;
@@ -75,16 +84,17 @@ path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
     lay->off_ktilde = take(BH * Lp * d * 4);
     lay->off_p = take(BH * M * d * d * 4);
   } else {
-    lay->layout_id = chunk == 128 ? 2 : 1;
+    lay->layout_id = chunk > 64 ? 2 : 1;
     lay->off_qtilde = take(BH * Lp * d * 2);
     if (transport == PATH_TRANSPORT_BF16X3) lay->off_qtilde_lo = take(BH * Lp * d * 2);
     lay->off_ktilde = take(BH * Lp * d * 2);
     lay->off_p = take(BH * M * d * d * 2);
     if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_lo = take(BH * M * d * d * 2);
-    if (chunk == 128) {
-      lay->off_ktilde_c2 = take(BH * M2 * 64 * d * 2);
-      lay->off_p_c2 = take(BH * M2 * d * d * 2);
-      if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_c2_lo = take(BH * M2 * d * d * 2);
+    if (chunk > 64) {  // chunks of G = chunk / 64 sub-chunks: carried keys, products of whole groups
+      const int64_t MG = M / (chunk / 64);
+      lay->off_ktilde_c2 = take(BH * Lp * d * 2);
+      lay->off_p_c2 = take(BH * MG * d * d * 2);
+      if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_c2_lo = take(BH * MG * d * d * 2);
     }
   }
   lay->off_s = take(BH * M * (int64_t)sub * sub * 4);
@@ -149,6 +159,7 @@ path_status run_fwd(int phases, const void* q, const void* k, const void* v, con
   path_ws_layout lay;
   const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
   if (s != PATH_OK) return s;
+  chunk = resolve_chunk(d, dtype, chunk);
   const int64_t BH = B * H;
   if (BH == 0 || L == 0) return PATH_OK;
   if (!workspace) return PATH_ERR_INVALID_ARG;
@@ -210,6 +221,7 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
   path_ws_layout lay;
   const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
   if (s != PATH_OK) return s;
+  chunk = resolve_chunk(d, dtype, chunk);
   if (capacity < L) return PATH_ERR_INVALID_ARG;
   if ((log_forget == nullptr) != (fcache == nullptr)) return PATH_ERR_INVALID_ARG;
   const int64_t BH = B * H;

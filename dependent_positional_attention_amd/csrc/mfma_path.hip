@@ -494,11 +494,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-// s_waitcnt vmcnt(n) (expcnt, lgkmcnt untouched), n < 16
+// s_waitcnt vmcnt(n) (expcnt, lgkmcnt untouched), n < 64: the count's low 4 bits sit in bits 3:0 of
+// the immediate, its high 2 bits in bits 15:14
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Blocks are laid out for the 8 XCDs (workgroup b runs on XCD b % 8, each with its own L2):
@@ -545,11 +546,11 @@ struct ScanShape {
 // The running max is raised lazily: a lane whose partial row sum exceeds 2^kRescale (so possibly
 // some p > 2^kRescale) sends the wave through the exact max, which raises the reference of any
 // column whose max exceeds it by more than kRescale and rescales O, the sums and the pending logits.
-template <bool FOX, bool X3, bool C2, int QT, int W>
+template <bool FOX, bool X3, int G, int QT, int W>
 __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_attn_kernel(
     const __bf16* __restrict__ qt, const __bf16* __restrict__ qt_lo, const __bf16* __restrict__ kt,
     const __bf16* __restrict__ v, const __bf16* __restrict__ p_hi, const __bf16* __restrict__ p_lo,
-    const __bf16* __restrict__ kt2, const __bf16* __restrict__ p2_hi, const __bf16* __restrict__ p2_lo,
+    const __bf16* __restrict__ ktc, const __bf16* __restrict__ pg_hi, const __bf16* __restrict__ pg_lo,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     __bf16* __restrict__ out, float* __restrict__ lse, int64_t L, int64_t M, int64_t BH) {
   using Sh = ScanShape<X3, QT, W>;
@@ -837,15 +838,19 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   // row 8i + l/8, written to slot l of the tile's i-th 1 KiB run) and of the prefix.
   const int i0 = kCp * wave;
   const int64_t mlow = kCpb * p;  // lowest query chunk of the block
-  // With 128-token chunks (C2) the stream below the block's own chunks takes each 128-token chunk as
-  // two 64-token halves: the upper half with its own keys and no transport, the lower half with its
-  // keys carried through the upper half and the 128-token transport P_{2c} P_{2c+1}.
-  const int64_t M2 = (M + 1) >> 1;
+  // With chunks of G > 1 sub-chunks the stream below the block takes whole groups from galign down:
+  // each sub-chunk with its keys carried to the group's top and no transport, except the group's
+  // bottom sub-chunk, which moves the queries across the whole group (P_group).  Sub-chunks between
+  // the block's own chunks and galign (the group boundary at or below them) step one by one.
+  static_assert(G == 1 || G == 2 || G == 4, "sub-chunks per chunk");
+  const int64_t MG = M / G;
+  const int64_t galign = (mlow / G) * G;
   auto chunk_src = [&](int64_t n, int t) PA_INLINE -> const __bf16* {
-    const bool two = C2 && n < mlow && (n & 1) == 0;
-    if (t == 0) return two ? kt2 + ((size_t)bh * M2 + (n >> 1)) * kC * kD : kt + ((size_t)bh * Lp + n * kC) * kD;
+    const bool grouped = G > 1 && n < galign;
+    if (t == 0)
+      return (grouped && n % G != G - 1 ? ktc : kt) + ((size_t)bh * Lp + n * kC) * kD;
     if (t == 1) return v + ((size_t)bh * L + n * kC) * kD;
-    if (two) return (t == 2 ? p2_hi : p2_lo) + ((size_t)bh * M2 + (n >> 1)) * kD * kD;
+    if (grouped && n % G == 0) return (t == 2 ? pg_hi : pg_lo) + ((size_t)bh * MG + n / G) * kD * kD;
     return (t == 2 ? p_hi : p_lo) + ((size_t)bh * M + n) * kD * kD;
   };
   auto chunk_rows = [&](int64_t n, int t) PA_INLINE -> int {
@@ -924,21 +929,34 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   }
   // Body: every wave steps (a wave past the end of the sequence works on zero queries and stores
   // nothing), so the loop has a single path.
-  if constexpr (C2) {
-    // mlow is even: the body starts on an upper half (no transport), then its lower half
-    for (; n >= 3; n -= 2) {
-      prefetch(n);
-      run_step(std::false_type{}, n);
-      advance(n);
-      prefetch(n - 1);
-      run_step(std::true_type{}, n - 1);
-      advance(n - 1);
+  if constexpr (G > 1) {
+    if constexpr (kCpb % G != 0) {
+      for (; n >= galign && n >= 1; --n) {  // down to the group boundary, one sub-chunk at a time
+        prefetch(n);
+        run_step(std::true_type{}, n);
+        advance(n);
+      }
     }
-    if (n == 1) {
-      prefetch(1);
-      run_step(std::false_type{}, 1);
-      advance(1);
-      n = 0;
+    // from here n is the top of a group (n % G == G - 1) or 0
+    for (; n >= 2 * G - 1; n -= G) {  // whole groups with more below: transport at the bottom only
+#pragma unroll
+      for (int j = 0; j < G - 1; ++j) {
+        prefetch(n - j);
+        run_step(std::false_type{}, n - j);
+        advance(n - j);
+      }
+      prefetch(n - G + 1);
+      run_step(std::true_type{}, n - G + 1);
+      advance(n - G + 1);
+    }
+#pragma unroll
+    for (int j = 0; j < G - 1; ++j) {  // the lowest group: nothing below it
+      if (n >= 1) {
+        prefetch(n);
+        run_step(std::false_type{}, n);
+        advance(n);
+        --n;
+      }
     }
   } else {
     for (; n >= 1; --n) {
@@ -967,69 +985,174 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   }
 }
 
-// =========================================================================== kernel 3: 128-token chunks
-// For chunk 128 the per-chunk terms are built on 64-token halves (kernel 1), and this kernel adds,
-// per 128-token chunk c, the two terms the scan needs below a query's own chunk:
-//   P_c2    = P_{2c} P_{2c+1}                      (the 128-token transition product)
-//   ktilde' = rows of ktilde_{2c} times P_{2c+1}   (keys of the lower half carried to the chunk end)
-// A missing upper half (ragged end) is the identity.  One block of 4 waves per (b, h, c); wave w owns
-// output columns y = 16w.. of both products, computed transposed so each lane writes 4 consecutive
-// stored columns.  bf16x3 operands (P hi + lo) enter as hi*hi + hi*lo + lo*hi.
-__global__ __launch_bounds__(256, 2) void mfma_merge_kernel(const __bf16* __restrict__ kt,
-                                                            const __bf16* __restrict__ p_hi,
-                                                            const __bf16* __restrict__ p_lo, int64_t M,
-                                                            __bf16* __restrict__ kt2, __bf16* __restrict__ p2_hi,
-                                                            __bf16* __restrict__ p2_lo) {
-  __shared__ __align__(1024) __bf16 t0h[kTile], t0l[kTile], t1h[kTile], t1l[kTile], tk[kTile];
-  const int64_t c = blockIdx.x, bh = blockIdx.y, M2 = (M + 1) >> 1;
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, r = l & 15, g = l >> 4;
-  const bool x3 = p_lo != nullptr;
-  const bool upper = 2 * c + 1 < M;
-  const int64_t lo_c = 2 * c, hi_c = upper ? 2 * c + 1 : 2 * c;
-  const int i0 = 2 * wave;
-  dma_tile(t0h, p_hi + ((size_t)bh * M + lo_c) * kD * kD, kC, i0);
-  dma_tile(t1h, p_hi + ((size_t)bh * M + hi_c) * kD * kD, kC, i0);
-  dma_tile(tk, kt + ((size_t)bh * M * kC + lo_c * kC) * kD, kC, i0);
-  if (x3) {
-    dma_tile(t0l, p_lo + ((size_t)bh * M + lo_c) * kD * kD, kC, i0);
-    dma_tile(t1l, p_lo + ((size_t)bh * M + hi_c) * kD * kD, kC, i0);
+// =========================================================================== chains of chunk products
+// Kernels 3 and 4 carry a running product R of consecutive chunk matrices from right to left,
+// R <- P_s R, and emit rows ktilde_s R on the way.  Columns of R evolve independently, so compute
+// wave w of a block carries the 64 x 16 column block y = 16w .. 16w+15 in fp32 accumulators (lane
+// (r, g): rows 16jt + 4g + e, column 16w + r).  That accumulator is already the B-operand of the next
+// product in the stored key order (acc_to_op), and the A-operand of the key product taken transposed
+// (key^T = R^T ktilde^T), so R never leaves registers.  R enters the matrix cores as hi + lo bf16, P
+// as hi (+ lo with bf16x3 transport).  A fifth wave streams the P and ktilde tiles of the coming steps
+// into an NB-slot LDS ring (direct global->LDS copies) and is the only wave that waits for them, so
+// its wait counts are exact while the compute waves store their results.
+struct ChainFrags {
+  bf16x8 ph[4][2], pl[4][2], k[4][2];
+};
+
+constexpr int kChainThreads = 320;  // 4 compute waves + the copy wave
+
+__device__ __forceinline__ void chain_identity(f32x4 (&racc)[4]) {
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) racc[jt][e] = (16 * jt + 4 * g + e == 16 * wave + r) ? 1.f : 0.f;
+}
+
+// key^T[y][b] = sum_m R[m][y] ktilde[b][m] for key tile bt: lane gets key b = 16 bt + r, y = 16w + 4g ..
+__device__ __forceinline__ f32x4 chain_keys(const bf16x8 (&rh)[2], const bf16x8 (&rl)[2], const bf16x8 (&k)[2]) {
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    a = mfma16(rh[ks], k[ks], a);
+    a = mfma16(rl[ks], k[ks], a);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed
-  __syncthreads();
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  const int y0 = 16 * wave + 4 * g;  // this lane's four output columns
-  const int ys = perm_pos(y0);       // their stored slots (contiguous)
+  return a;
+}
+
+// R <- P R
+template <bool X3>
+__device__ __forceinline__ void chain_advance(const ChainFrags& F, const bf16x8 (&rh)[2], const bf16x8 (&rl)[2],
+                                              f32x4 (&racc)[4]) {
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
-    const int xr = 16 * jt + r;  // output row (x of P_c2, b of ktilde')
-    f32x4 dp = zero, dk = zero;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 ah = tr_frag(t1h, 16 * wave, ks, perm_col);  // P_{2c+1}[m][y], k over m
-      const bf16x8 bp = tile_frag(t0h, xr, 4 * ks + g);           // P_{2c}[x][m]
-      const bf16x8 bk = tile_frag(tk, xr, 4 * ks + g);            // ktilde_{2c}[b][m]
-      if (upper) {
-        dp = mfma16(ah, bp, dp);
-        dk = mfma16(ah, bk, dk);
-        if (x3) {
-          const bf16x8 al = tr_frag(t1l, 16 * wave, ks, perm_col);
-          dp = mfma16(ah, tile_frag(t0l, xr, 4 * ks + g), dp);
-          dp = mfma16(al, bp, dp);
-          dk = mfma16(al, bk, dk);
+      a = mfma16(F.ph[jt][ks], rh[ks], a);
+      a = mfma16(F.ph[jt][ks], rl[ks], a);
+      if constexpr (X3) a = mfma16(F.pl[jt][ks], rh[ks], a);
+    }
+    racc[jt] = a;
+  }
+}
+
+// Run `steps` chain steps.  src(i, t) is the global tile of step i (t = 0: P hi, 1: ktilde, 2: P lo);
+// emit(i, rh, rl, F) runs on the compute waves before the step's R <- P R (skipped for the last step
+// unless advance_last).  All waves of the block call this.
+template <bool X3, int NB, typename Src, typename Emit>
+__device__ __forceinline__ void chain_run(__bf16 (*ring)[X3 ? 3 : 2][kTile], int64_t steps, bool advance_last,
+                                          f32x4 (&racc)[4], Src src, Emit emit) {
+  constexpr int NT = X3 ? 3 : 2;
+  constexpr int D = 8 * NT;  // copy instructions per step (the copy wave moves whole tiles)
+  static_assert((NB - 2) * D <= 63, "vmcnt field");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const bool copier = wave == 4;
+  auto stage = [&](int64_t i) PA_INLINE {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dma_tile<8>(ring[i % NB][t], src(i, t), kC, 0);
+  };
+  if (copier) {
+    for (int64_t i = 0; i < NB - 1 && i < steps; ++i) stage(i);
+    wait_vm<0>();
+  }
+  lds_barrier();
+  for (int64_t i = 0; i < steps; ++i) {
+    if (copier) {
+      if (i + NB - 1 < steps) {
+        stage(i + NB - 1);
+        wait_vm<(NB - 2) * D>();  // step i + 1 has landed
+      } else {
+        wait_vm<0>();
+      }
+    } else {
+      ChainFrags F;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          F.ph[t][ks] = tile_frag(ring[i % NB][0], 16 * t + r, 4 * ks + g);
+          F.k[t][ks] = tile_frag(ring[i % NB][1], 16 * t + r, 4 * ks + g);
+          if constexpr (X3) F.pl[t][ks] = tile_frag(ring[i % NB][NT - 1], 16 * t + r, 4 * ks + g);
         }
+      bf16x8 rh[2], rl[2];
+      acc_to_op(racc, rh, rl);
+      emit(i, rh, rl, F);
+      if (i + 1 < steps || advance_last) chain_advance<X3>(F, rh, rl, racc);
+    }
+    lds_barrier();
+  }
+}
+
+// =========================================================================== kernel 3: grouped chunks
+// Chunks of 64 G tokens (G = 2, 4) are built from G 64-token sub-chunks (kernel 1); this kernel adds,
+// per group g of sub-chunks s0 = gG .. s0+G-1, what the scan needs below a query's own chunks:
+//   carried keys  ktilde_s (P_{s+1} ... P_{s0+G-1})   for s < s0+G-1  (keys moved to the group's top)
+//   P_group       P_{s0} ... P_{s0+G-1}                (the group's transition product)
+// so that the scan moves its queries once per group.  One block of 4 waves per (group, b, h): every
+// tile of the group arrives in LDS at once, then the chain above runs top first without further
+// barriers; the last product is taken transposed (P_group^T = R^T P_{s0}^T, the key product's shape)
+// so that each lane stores four consecutive columns.  Only whole groups are materialised.
+template <bool X3, int G>
+__global__ __launch_bounds__(256) void mfma_group_kernel(const __bf16* __restrict__ kt,
+                                                         const __bf16* __restrict__ p_hi,
+                                                         const __bf16* __restrict__ p_lo, int64_t M,
+                                                         __bf16* __restrict__ ktc, __bf16* __restrict__ pg_hi,
+                                                         __bf16* __restrict__ pg_lo) {
+  __shared__ __align__(1024) __bf16 tp[G][kTile], tpl[X3 ? G : 1][kTile], tk[G - 1][kTile];
+  const int64_t grp = blockIdx.x, bh = blockIdx.y, Lp = M * kC, MG = M / G, s0 = grp * G;
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    dma_tile<2>(tp[j], p_hi + ((size_t)bh * M + s0 + j) * kD * kD, kC, 2 * wave);
+    if constexpr (X3) dma_tile<2>(tpl[j], p_lo + ((size_t)bh * M + s0 + j) * kD * kD, kC, 2 * wave);
+    if (j < G - 1) dma_tile<2>(tk[j], kt + ((size_t)bh * Lp + (s0 + j) * kC) * kD, kC, 2 * wave);
+  }
+  wait_vm<0>();
+  __syncthreads();
+  f32x4 racc[4];
+  chain_identity(racc);
+#pragma unroll
+  for (int j = G - 1; j >= 0; --j) {
+    bf16x8 rh[2], rl[2];
+    acc_to_op(racc, rh, rl);
+    if (j < G - 1) {  // keys of sub-chunk s0 + j carried to the group's top
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const bf16x8 k[2] = {tile_frag(tk[j], 16 * bt + r, g), tile_frag(tk[j], 16 * bt + r, 4 + g)};
+        const f32x4 a = chain_keys(rh, rl, k);
+        *reinterpret_cast<bf16x4*>(ktc + ((size_t)bh * Lp + (s0 + j) * kC + 16 * bt + r) * kD +
+                                   perm_pos(16 * wave + 4 * g)) = pack4(a[0], a[1], a[2], a[3]);
       }
     }
-    const size_t ob = ((size_t)bh * M2 + c) * kC * kD + (size_t)xr * kD + ys;
-    if (upper) {
-      bf16x4 h4, l4;
-      split4(dp[0], dp[1], dp[2], dp[3], h4, l4);
-      *reinterpret_cast<bf16x4*>(p2_hi + ob) = h4;
-      if (x3) *reinterpret_cast<bf16x4*>(p2_lo + ob) = l4;
-      *reinterpret_cast<bf16x4*>(kt2 + ob) = pack4(dk[0], dk[1], dk[2], dk[3]);
-    } else {  // identity upper half: copy
-      *reinterpret_cast<bf16x4*>(p2_hi + ob) = *reinterpret_cast<const bf16x4*>(t0h + swz(xr, ys >> 3) + (ys & 7));
-      if (x3) *reinterpret_cast<bf16x4*>(p2_lo + ob) = *reinterpret_cast<const bf16x4*>(t0l + swz(xr, ys >> 3) + (ys & 7));
-      *reinterpret_cast<bf16x4*>(kt2 + ob) = *reinterpret_cast<const bf16x4*>(tk + swz(xr, ys >> 3) + (ys & 7));
+    if (j > 0) {  // R <- P_j R
+      ChainFrags F;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          F.ph[t][ks] = tile_frag(tp[j], 16 * t + r, 4 * ks + g);
+          if constexpr (X3) F.pl[t][ks] = tile_frag(tpl[j], 16 * t + r, 4 * ks + g);
+        }
+      chain_advance<X3>(F, rh, rl, racc);
+    } else {  // P_group^T[y][x] = sum_m R[m][y] P_{s0}[x][m]: lane gets row x = 16xt + r, y = 16 wave + 4g ..
+#pragma unroll
+      for (int xt = 0; xt < 4; ++xt) {
+        const bf16x8 ph[2] = {tile_frag(tp[0], 16 * xt + r, g), tile_frag(tp[0], 16 * xt + r, 4 + g)};
+        f32x4 a = chain_keys(rh, rl, ph);
+        if constexpr (X3) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) a = mfma16(rh[ks], tile_frag(tpl[0], 16 * xt + r, 4 * ks + g), a);
+        }
+        bf16x4 h4, l4;
+        split4(a[0], a[1], a[2], a[3], h4, l4);
+        const size_t o = ((size_t)bh * MG + grp) * kD * kD + (size_t)(16 * xt + r) * kD + perm_pos(16 * wave + 4 * g);
+        *reinterpret_cast<bf16x4*>(pg_hi + o) = h4;
+        if constexpr (X3) *reinterpret_cast<bf16x4*>(pg_lo + o) = l4;
+      }
     }
   }
 }
@@ -1039,139 +1162,98 @@ __global__ __launch_bounds__(256, 2) void mfma_merge_kernel(const __bf16* __rest
 // the key after every later transition, H_{L-1} ... H_{j+1} k_j).  In chunk terms, with R_n the
 // product of the chunk matrices after chunk n,
 //   R_{M-1} = I,   R_{n-1} = P_n R_n,   cache rows of chunk n = ktilde_n R_n   (row form),
-// a right-to-left chain over the 64-token (sub-)chunks that reuses the prep's ktilde and P.
-// Columns of R are independent, so wave w of the block for head bh carries the 64 x 16 column
-// block y = 16w .. 16w+15 of R in fp32 accumulators and never talks to the other waves: the
-// accumulator of R_{n-1} = P_n R_n is already the B-operand of the next product (stored key order),
-// and it is also the A-operand of the key product, computed transposed (key^T = R^T ktilde^T), so
-// every operand comes straight from global memory or registers and no LDS is used.  R enters the
-// matrix cores as hi + lo bf16 pairs, P as hi (+ lo with bf16x3 transport).  The wave also copies
-// its quarter of the chunk's value rows.  Loads for chunk n-1 are issued before chunk n's products.
-struct CacheFrags {
-  bf16x8 ph[4][2], pl[4][2], k[4][2];
-};
-
+// the chain above over all 64-token (sub-)chunks, reusing the prep's ktilde and P.  One block per
+// (b, h); each compute wave also copies its quarter of the chunk's value rows.
 template <bool X3>
-__global__ __launch_bounds__(256, 1) void mfma_cache_kernel(const __bf16* __restrict__ kt,
-                                                            const __bf16* __restrict__ p_hi,
-                                                            const __bf16* __restrict__ p_lo,
-                                                            const __bf16* __restrict__ v, int64_t L, int64_t M,
-                                                            int64_t cap, __bf16* __restrict__ kc,
-                                                            __bf16* __restrict__ vc) {
+__global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf16* __restrict__ kt,
+                                                                      const __bf16* __restrict__ p_hi,
+                                                                      const __bf16* __restrict__ p_lo,
+                                                                      const __bf16* __restrict__ v, int64_t L,
+                                                                      int64_t M, int64_t cap,
+                                                                      __bf16* __restrict__ kc,
+                                                                      __bf16* __restrict__ vc) {
+  constexpr int NB = 4;
+  __shared__ __align__(1024) __bf16 ring[NB][X3 ? 3 : 2][kTile];
   const int64_t bh = blockIdx.x, Lp = M * kC;
   const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  // R[x][y] for x = 16 jt + 4g + e, y = 16 wave + r; R_{M-1} = I
   f32x4 racc[4];
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) racc[jt][e] = (16 * jt + 4 * g + e == 16 * wave + r) ? 1.f : 0.f;
-
-  auto load = [&](int64_t n, CacheFrags& F) PA_INLINE {
-    const __bf16* pb = p_hi + ((size_t)bh * M + n) * kD * kD;
-    const __bf16* kb = kt + ((size_t)bh * Lp + n * kC) * kD;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int o = (16 * t + r) * kD + 32 * ks + 8 * g;
-        F.ph[t][ks] = *reinterpret_cast<const bf16x8*>(pb + o);
-        if constexpr (X3) F.pl[t][ks] = *reinterpret_cast<const bf16x8*>(p_lo + ((size_t)bh * M + n) * kD * kD + o);
-        F.k[t][ks] = *reinterpret_cast<const bf16x8*>(kb + o);
-      }
+  if (wave < 4) chain_identity(racc);
+  auto src = [&](int64_t i, int t) -> const __bf16* {
+    const int64_t n = M - 1 - i;
+    if (t == 1) return kt + ((size_t)bh * Lp + n * kC) * kD;
+    return (t == 0 ? p_hi : p_lo) + ((size_t)bh * M + n) * kD * kD;
   };
-
-  auto step = [&](int64_t n, const CacheFrags& F) PA_INLINE {
-    bf16x8 rh[2], rl[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x4 h0, l0, h1, l1;
-      split4(racc[2 * ks][0], racc[2 * ks][1], racc[2 * ks][2], racc[2 * ks][3], h0, l0);
-      split4(racc[2 * ks + 1][0], racc[2 * ks + 1][1], racc[2 * ks + 1][2], racc[2 * ks + 1][3], h1, l1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rh[ks][e] = h0[e];
-        rh[ks][4 + e] = h1[e];
-        rl[ks][e] = l0[e];
-        rl[ks][4 + e] = l1[e];
-      }
+  // values of chunk n: rows 16 wave .. 16 wave + 15, 32 B per lane, loaded one chunk ahead
+  uint4 va = {}, vb = {};
+  auto vload = [&](int64_t n) PA_INLINE {
+    const int64_t j = n * kC + 16 * wave + (l >> 2);
+    if (n >= 0 && j < L) {
+      const uint4* s = reinterpret_cast<const uint4*>(v + ((size_t)bh * L + j) * kD + 16 * (l & 3));
+      va = s[0];
+      vb = s[1];
     }
-    // values of chunk n: rows 16 wave .. 16 wave + 15, 32 B per lane
+  };
+  if (wave < 4) vload(M - 1);
+  auto emit = [&](int64_t i, const bf16x8 (&rh)[2], const bf16x8 (&rl)[2], const ChainFrags& F) PA_INLINE {
+    const int64_t n = M - 1 - i;
     {
       const int64_t j = n * kC + 16 * wave + (l >> 2);
       if (j < L) {
-        const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)bh * L + j) * kD + 16 * (l & 3));
-        uint4* dst = reinterpret_cast<uint4*>(vc + ((size_t)bh * cap + j) * kD + 16 * (l & 3));
-        dst[0] = src[0];
-        dst[1] = src[1];
+        uint4* d = reinterpret_cast<uint4*>(vc + ((size_t)bh * cap + j) * kD + 16 * (l & 3));
+        d[0] = va;
+        d[1] = vb;
       }
+      vload(n - 1);
     }
-    // keys of chunk n: key^T[y][b] = sum_m R[m][y] ktilde[b][m]; lane: key b = 16 bt + r, y = 16 wave + 4g ..
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
-      f32x4 a = zero;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        a = mfma16(rh[ks], F.k[bt][ks], a);
-        a = mfma16(rl[ks], F.k[bt][ks], a);
-      }
+      const f32x4 a = chain_keys(rh, rl, F.k[bt]);
       const int64_t j = n * kC + 16 * bt + r;
       if (j < L)
         *reinterpret_cast<bf16x4*>(kc + ((size_t)bh * cap + j) * kD + 16 * wave + 4 * g) = pack4(a[0], a[1], a[2], a[3]);
     }
-    // R_{n-1} = P_n R_n
-    if (n > 0) {
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        f32x4 a = zero;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          a = mfma16(F.ph[jt][ks], rh[ks], a);
-          a = mfma16(F.ph[jt][ks], rl[ks], a);
-          if constexpr (X3) a = mfma16(F.pl[jt][ks], rh[ks], a);
-        }
-        racc[jt] = a;
-      }
-    }
   };
-
-  CacheFrags A, B;
-  int64_t n = M - 1;
-  load(n, A);
-  for (; n >= 1; n -= 2) {
-    load(n - 1, B);
-    step(n, A);
-    if (n >= 2) load(n - 2, A);
-    step(n - 1, B);
-  }
-  if (n == 0) step(0, A);
+  chain_run<X3, NB>(ring, M, false, racc, src, emit);
 }
 
 // =========================================================================== host
-bool mfma_supported(int d, int chunk) { return d == kD && (chunk == kC || chunk == 2 * kC); }
+bool mfma_supported(int d, int chunk) { return d == kD && (chunk == kC || chunk == 2 * kC || chunk == 4 * kC); }
 
-template <bool FOX, bool X3, bool C2>
+template <bool FOX, bool X3, int G>
 static void launch_attn(dim3 grid, hipStream_t st, const __bf16* qt, const __bf16* qt_lo, const __bf16* kt,
-                        const __bf16* v, const __bf16* p_hi, const __bf16* p_lo, const __bf16* kt2,
-                        const __bf16* p2_hi, const __bf16* p2_lo, const float* Sm, const float* fl,
+                        const __bf16* v, const __bf16* p_hi, const __bf16* p_lo, const __bf16* ktc,
+                        const __bf16* pg_hi, const __bf16* pg_lo, const float* Sm, const float* fl,
                         const float* ftot, __bf16* out, float* lse, int64_t L, int64_t M, int64_t BH) {
-  mfma_attn_kernel<FOX, X3, C2, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>
-      <<<grid, 64 * PATHATTN_SCAN_BLOCK_WAVES, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, kt2, p2_hi, p2_lo, Sm, fl, ftot,
+  mfma_attn_kernel<FOX, X3, G, PATHATTN_SCAN_QT, PATHATTN_SCAN_BLOCK_WAVES>
+      <<<grid, 64 * PATHATTN_SCAN_BLOCK_WAVES, 0, st>>>(qt, qt_lo, kt, v, p_hi, p_lo, ktc, pg_hi, pg_lo, Sm, fl, ftot,
                                                         out, lse, L, M, BH);
 }
 
+template <int G>
+static void launch_attn_g(bool fox, bool x3, dim3 grid, hipStream_t st, const __bf16* qt, const __bf16* qt_lo,
+                          const __bf16* kt, const __bf16* v, const __bf16* p_hi, const __bf16* p_lo,
+                          const __bf16* ktc, const __bf16* pg_hi, const __bf16* pg_lo, const float* Sm,
+                          const float* fl, const float* ftot, __bf16* out, float* lse, int64_t L, int64_t M,
+                          int64_t BH) {
+  auto go = [&](auto fn) { fn(grid, st, qt, qt_lo, kt, v, p_hi, p_lo, ktc, pg_hi, pg_lo, Sm, fl, ftot, out, lse, L, M, BH); };
+  if (fox && x3) go(launch_attn<true, true, G>);
+  else if (fox) go(launch_attn<true, false, G>);
+  else if (x3) go(launch_attn<false, true, G>);
+  else go(launch_attn<false, false, G>);
+}
+
 // phases: bit 0 = per-chunk prep, bit 1 = attention scan (reads what the prep left in the workspace).
-// The prep stores qtilde and the in-chunk logits multiplied by scale * log2(e).  Chunk 128 runs the
-// prep on 64-token halves and merges each pair (kernel 3) before the scan.
+// The prep stores qtilde and the in-chunk logits multiplied by scale * log2(e).  Chunks of 128 or 256
+// tokens run the prep on 64-token sub-chunks and group them (kernel 3) before the scan.
 hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const void* k, const void* v,
                     const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH,
-                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, void* kt2,
-                    void* p2_hi, void* p2_lo, float* Sm, float* fl, float* ftot, hipStream_t st) {
-  if (chunk != kC && chunk != 2 * kC) return hipErrorInvalidValue;
-  const bool c2 = chunk == 2 * kC;
+                    int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, void* ktc,
+                    void* pg_hi, void* pg_lo, float* Sm, float* fl, float* ftot, hipStream_t st) {
+  if (!mfma_supported(kD, chunk)) return hipErrorInvalidValue;
+  const int G = chunk / kC;
   const int64_t M = (L + kC - 1) / kC;  // 64-token (sub-)chunks
+  const int64_t MG = M / G;             // whole groups
   const bool x3 = transport == 1;
   hipError_t e = hipSuccess;
   if (phases & 1) {
@@ -1183,10 +1265,22 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
         x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (c2) {
-      mfma_merge_kernel<<<dim3((unsigned)((M + 1) / 2), (unsigned)BH), 256, 0, st>>>(
-          (const __bf16*)kt, (const __bf16*)p_hi, x3 ? (const __bf16*)p_lo : nullptr, M, (__bf16*)kt2,
-          (__bf16*)p2_hi, x3 ? (__bf16*)p2_lo : nullptr);
+    if (G > 1 && MG > 0) {
+      const dim3 gg((unsigned)MG, (unsigned)BH);
+      const auto* a_kt = (const __bf16*)kt;
+      const auto* a_ph = (const __bf16*)p_hi;
+      const auto* a_pl = x3 ? (const __bf16*)p_lo : nullptr;
+      auto* a_kc = (__bf16*)ktc;
+      auto* a_gh = (__bf16*)pg_hi;
+      auto* a_gl = x3 ? (__bf16*)pg_lo : nullptr;
+      if (G == 4 && x3)
+        mfma_group_kernel<true, 4><<<gg, 256, 0, st>>>(a_kt, a_ph, a_pl, M, a_kc, a_gh, a_gl);
+      else if (G == 4)
+        mfma_group_kernel<false, 4><<<gg, 256, 0, st>>>(a_kt, a_ph, a_pl, M, a_kc, a_gh, a_gl);
+      else if (x3)
+        mfma_group_kernel<true, 2><<<gg, 256, 0, st>>>(a_kt, a_ph, a_pl, M, a_kc, a_gh, a_gl);
+      else
+        mfma_group_kernel<false, 2><<<gg, 256, 0, st>>>(a_kt, a_ph, a_pl, M, a_kc, a_gh, a_gl);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1197,37 +1291,39 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
     const int64_t heads_per_xcd = (BH + kXcd - 1) / kXcd;
     const dim3 grid((unsigned)(kXcd * heads_per_xcd * ((M + kCpb - 1) / kCpb)));
     const bool fox = logf != nullptr;
-    auto args = [&](auto fn) {
-      fn(grid, st, (const __bf16*)qt, (const __bf16*)qt_lo, (const __bf16*)kt, (const __bf16*)v,
-         (const __bf16*)p_hi, (const __bf16*)p_lo, (const __bf16*)kt2, (const __bf16*)p2_hi, (const __bf16*)p2_lo,
-         Sm, fl, ftot, (__bf16*)out, lse, L, M, BH);
-    };
-    if (c2) {
-      if (fox && x3) args(launch_attn<true, true, true>);
-      else if (fox) args(launch_attn<true, false, true>);
-      else if (x3) args(launch_attn<false, true, true>);
-      else args(launch_attn<false, false, true>);
-    } else {
-      if (fox && x3) args(launch_attn<true, true, false>);
-      else if (fox) args(launch_attn<true, false, false>);
-      else if (x3) args(launch_attn<false, true, false>);
-      else args(launch_attn<false, false, false>);
-    }
+    const auto* a_qt = (const __bf16*)qt;
+    const auto* a_qtl = (const __bf16*)qt_lo;
+    const auto* a_kt = (const __bf16*)kt;
+    const auto* a_v = (const __bf16*)v;
+    const auto* a_ph = (const __bf16*)p_hi;
+    const auto* a_pl = (const __bf16*)p_lo;
+    const auto* a_kc = (const __bf16*)ktc;
+    const auto* a_gh = (const __bf16*)pg_hi;
+    const auto* a_gl = (const __bf16*)pg_lo;
+    if (G == 4)
+      launch_attn_g<4>(fox, x3, grid, st, a_qt, a_qtl, a_kt, a_v, a_ph, a_pl, a_kc, a_gh, a_gl, Sm, fl, ftot,
+                       (__bf16*)out, lse, L, M, BH);
+    else if (G == 2)
+      launch_attn_g<2>(fox, x3, grid, st, a_qt, a_qtl, a_kt, a_v, a_ph, a_pl, a_kc, a_gh, a_gl, Sm, fl, ftot,
+                       (__bf16*)out, lse, L, M, BH);
+    else
+      launch_attn_g<1>(fox, x3, grid, st, a_qt, a_qtl, a_kt, a_v, a_ph, a_pl, a_kc, a_gh, a_gl, Sm, fl, ftot,
+                       (__bf16*)out, lse, L, M, BH);
     e = hipGetLastError();
   }
   return e;
 }
 
-// Decode cache from a prefill workspace (kernel 4): one block of 4 waves per (b, h).
+// Decode cache from a prefill workspace (kernel 4): one block (4 compute waves + the copy wave) per (b, h).
 hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
                           int64_t BH, int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st) {
   const int64_t M = (L + kC - 1) / kC;
   if (transport == 1)
-    mfma_cache_kernel<true><<<dim3((unsigned)BH), 256, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi,
+    mfma_cache_kernel<true><<<dim3((unsigned)BH), kChainThreads, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi,
                                                                 (const __bf16*)p_lo, (const __bf16*)v, L, M, cap,
                                                                 (__bf16*)kc, (__bf16*)vc);
   else
-    mfma_cache_kernel<false><<<dim3((unsigned)BH), 256, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi, nullptr,
+    mfma_cache_kernel<false><<<dim3((unsigned)BH), kChainThreads, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi, nullptr,
                                                                  (const __bf16*)v, L, M, cap, (__bf16*)kc,
                                                                  (__bf16*)vc);
   return hipGetLastError();

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 3
+#define PATH_ABI_VERSION 4
 
 typedef enum {
   PATH_OK = 0,
@@ -86,14 +86,17 @@ path_status path_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d
  *   out          [B,H,L,d] dtype        attention output (written)
  *   lse          [B,H,L]   fp32 or NULL natural-log log-sum-exp of each row (written)
  *   scale        multiplies k^T(...)q; the FoX bias is added after scaling
- *   chunk        block length C of the scan; results do not depend on it beyond rounding
+ *   chunk        block length C of the scan; results do not depend on it beyond rounding;
+ *                0 selects the fastest measured chunk for the path (256 on the
+ *                matrix-core path, 64 on the vector path), the same in every call
  *   workspace    device buffer of at least path_attn_fwd_workspace_bytes bytes,
  *                caller-owned; its contents on return hold the per-chunk terms
  *                described by path_attn_workspace_layout
  *
  * Supported: dtype F32 with d in {16,32,64} and chunk in {16,32,64};
- * dtype BF16 with the same set, plus d = 64 with chunk 64 or 128 on the
- * matrix-core path.  Any L >= 0 (a ragged last chunk is padded internally with
+ * dtype BF16 with the same set, plus d = 64 with chunk 64, 128 or 256 on the
+ * matrix-core path (128 and 256 are built from 64-token sub-chunks; the scan
+ * then moves its queries once per chunk).  Any L >= 0 (a ragged last chunk is padded internally with
  * identity transitions); B, H, L may be 0 (nothing is enqueued).
  */
 path_status path_attn_fwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
@@ -135,11 +138,12 @@ path_status path_attn_scan(const void* v, const float* log_forget, void* out, fl
  *     qtilde_lo (bf16x3 transport only): the bf16 residual qtilde - qtilde_hi, same layout;
  *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S as layout 0;
  *     qtilde (hi + lo) and S carry the factor scale * log2(e) as in layout 0.
- *   layout_id 2 (matrix-core path, chunk 128): every term of layout 1 for the 64-token halves of
- *     the chunks (C = 64, M = num_sub_chunks), plus per 128-token chunk c: ktilde_c2 [B*H, M2, 64, d]
- *     bf16 = the first half's keys carried through the second half (ktilde_{2c} P_{2c+1} in row
- *     form, columns permuted as ktilde) and P_c2 (hi) / P_c2_lo [B*H, M2, d, d] = P_{2c} P_{2c+1}
- *     (layout of P), M2 = num_chunks.
+ *   layout_id 2 (matrix-core path, chunk 128 or 256 = G sub-chunks of 64): every term of layout 1
+ *     for the 64-token sub-chunks (C = 64, M = num_sub_chunks), plus ktilde_c2 [B*H, M*64, d] bf16:
+ *     each sub-chunk's keys carried to the top of its chunk (ktilde_s P_{s+1} ... P_{top} in row
+ *     form, columns permuted as ktilde; rows of a chunk's top sub-chunk are not written), and
+ *     P_c2 (hi) / P_c2_lo [B*H, floor(M / G), d, d] = the product of each whole chunk's G sub-chunk
+ *     matrices (layout of P).
  * M = num_chunks = ceil(L / chunk); num_sub_chunks = ceil(L / 64) on the matrix-core path (else M);
  * fields of terms a layout does not have are -1.
  */

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 3
+    assert L.path_abi_version() == 4
     for s in range(4):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"
@@ -70,20 +70,35 @@ def test_workspace_planning(L):
     assert lay.num_sub_chunks == 7 and lay.off_ktilde_c2 == lay.off_p_c2 == lay.off_p_c2_lo == -1
 
 
-def test_workspace_planning_chunk128(L):
-    """Chunk 128 on the matrix-core path: 64-token halves plus the per-128-chunk merged terms."""
+@pytest.mark.parametrize("chunk,groups", [(128, 2), (256, 1)])
+def test_workspace_planning_grouped_chunks(L, chunk, groups):
+    """Chunks of 128 / 256 on the matrix-core path: 64-token sub-chunks plus carried keys for every
+    sub-chunk and the products of whole chunks."""
     for transport in (0, 1):
         lay = native.WsLayout()
-        assert L.path_attn_workspace_layout(2, 3, 300, 64, 128, BF16, transport, ctypes.byref(lay)) == OK
-        assert lay.layout_id == 2 and lay.num_chunks == 3 and lay.num_sub_chunks == 5
+        assert L.path_attn_workspace_layout(2, 3, 300, 64, chunk, BF16, transport, ctypes.byref(lay)) == OK
+        assert lay.layout_id == 2 and lay.num_chunks == -(-300 // chunk) and lay.num_sub_chunks == 5
         assert lay.off_ktilde_c2 >= 0 and lay.off_p_c2 >= 0 and (lay.off_p_c2_lo >= 0) == (transport == 1)
-        sizes = {lay.off_ktilde_c2: 6 * 3 * 64 * 64 * 2, lay.off_p_c2: 6 * 3 * 64 * 64 * 2}
+        sizes = {lay.off_ktilde_c2: 6 * 5 * 64 * 64 * 2, lay.off_p_c2: 6 * groups * 64 * 64 * 2}
         for o, n in sizes.items():
             assert o % 256 == 0 and o + n <= lay.total_bytes
-        st, n1 = ws_bytes(L, 2, 3, 300, 64, 128, BF16, transport)
+        st, n1 = ws_bytes(L, 2, 3, 300, 64, chunk, BF16, transport)
         assert st == OK and n1 == lay.total_bytes
-    assert ws_bytes(L, 1, 1, 300, 64, 128, F32, 0)[0] == UNSUPPORTED  # fp32 has no 128-token chunks
-    assert ws_bytes(L, 1, 1, 300, 32, 128, BF16, 0)[0] == UNSUPPORTED
+    assert ws_bytes(L, 1, 1, 300, 64, chunk, F32, 0)[0] == UNSUPPORTED  # fp32 has no grouped chunks
+    assert ws_bytes(L, 1, 1, 300, 32, chunk, BF16, 0)[0] == UNSUPPORTED
+    assert ws_bytes(L, 1, 1, 300, 64, 512, BF16, 0)[0] == UNSUPPORTED
+
+
+def test_chunk_zero_selects_the_fastest_chunk(L):
+    """chunk 0 plans exactly what chunk 256 plans on the matrix-core path and chunk 64 on the vector path."""
+    for args, chunk in (((2, 3, 1000, 64), 256), ((1, 2, 100, 16), 64)):
+        dtype = BF16 if chunk == 256 else F32
+        for transport in (0, 1):
+            a, b = native.WsLayout(), native.WsLayout()
+            assert L.path_attn_workspace_layout(*args, 0, dtype, transport, ctypes.byref(a)) == OK
+            assert L.path_attn_workspace_layout(*args, chunk, dtype, transport, ctypes.byref(b)) == OK
+            assert bytes(a) == bytes(b)
+    assert ws_bytes(L, 1, 1, 64, 64, -1, BF16, 0)[0] == INVALID
 
 
 def fwd(L, q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=None, B=1, H=1, Lq=64, d=16,

@@ -119,44 +119,57 @@ CASES_128 = [
 ]
 
 
+@pytest.mark.parametrize("chunk", [128, 256])
 @pytest.mark.parametrize("B,H,L,recipe,transport", CASES_128)
-def test_small_shapes_chunk128(B, H, L, recipe, transport):
-    """128-token chunks: the scan moves queries once per 128 keys (lower-half keys pre-carried)."""
+def test_small_shapes_grouped_chunks(B, H, L, recipe, transport, chunk):
+    """128- and 256-token chunks: the scan moves queries once per chunk (keys carried to the chunk top)."""
     x = synth.make_fwd_inputs(B, H, L, D, recipe=recipe, dtype="bf16", seed=L + 1)
-    print(f"[case] mfma chunk 128 B={B} H={H} L={L} recipe={recipe} transport={transport}", flush=True)
-    go, gl = run(x, transport, chunk=128)
+    print(f"[case] mfma chunk {chunk} B={B} H={H} L={L} recipe={recipe} transport={transport}", flush=True)
+    go, gl = run(x, transport, chunk=chunk)
     ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf, scale=x.scale)
     assert_parity(go, ro, "bf16", "out")
     assert_parity(gl, rl, "bf16", "lse")
 
 
-@pytest.mark.parametrize("transport", ["bf16", "bf16x3"])
-def test_chunk128_merged_terms(transport):
-    """P over each 128-token chunk and the lower half's keys carried to the chunk end, against the
-    oracle's explicit products / by-definition keys over the 128 tokens."""
-    B, H, L = 1, 2, 320  # 5 halves: chunks of 128, 128 and a lone 64-token half
+def test_chunk_zero_is_chunk_256():
+    """The automatic chunk on the matrix-core path is 256: bit-identical outputs."""
+    x = synth.make_fwd_inputs(2, 2, 777, D, recipe="fox", dtype="bf16", seed=6)
+    a_out, a_lse = run(x, "bf16", chunk=0)
+    b_out, b_lse = run(x, "bf16", chunk=256)
+    assert np.array_equal(a_out, b_out) and np.array_equal(a_lse, b_lse)
+
+
+@pytest.mark.parametrize("transport,chunk", [("bf16", 128), ("bf16x3", 128), ("bf16", 256), ("bf16x3", 256)])
+def test_grouped_chunk_terms(transport, chunk):
+    """P over each whole chunk and every sub-chunk's keys carried to its chunk's top, against the oracle's
+    explicit products / by-definition keys over the chunk's tokens."""
+    G = chunk // 64
+    B, H, L = 1, 2, 576  # 9 sub-chunks: whole chunks of 128 (4) or 256 (2) and a ragged rest
     x = synth.make_fwd_inputs(B, H, L, D, recipe="beta2", dtype="bf16", seed=3)
-    _, _, ws = run(x, transport, chunk=128, keep_ws=True)
-    lay = native.path_attn_workspace_layout(B, H, L, D, 128, torch.bfloat16, transport)
-    M2 = lay.num_chunks
-    assert lay.layout_id == 2 and M2 == 3 and lay.num_sub_chunks == 5
-    ph = ws_view(ws, lay.off_p_c2, B * H * M2 * D * D, torch.bfloat16).reshape(B * H, M2, D, D)
+    _, _, ws = run(x, transport, chunk=chunk, keep_ws=True)
+    lay = native.path_attn_workspace_layout(B, H, L, D, chunk, torch.bfloat16, transport)
+    M = lay.num_sub_chunks
+    MG = M // G
+    assert lay.layout_id == 2 and M == 9
+    ph = ws_view(ws, lay.off_p_c2, B * H * MG * D * D, torch.bfloat16).reshape(B * H, MG, D, D)
     if transport == "bf16x3":
-        ph = ph + ws_view(ws, lay.off_p_c2_lo, B * H * M2 * D * D, torch.bfloat16).reshape(B * H, M2, D, D)
-    P2 = unpermute_cols(ph)
-    K2 = unpermute_cols(ws_view(ws, lay.off_ktilde_c2, B * H * M2 * 64 * D, torch.bfloat16).reshape(B * H, M2, 64, D))
+        ph = ph + ws_view(ws, lay.off_p_c2_lo, B * H * MG * D * D, torch.bfloat16).reshape(B * H, MG, D, D)
+    PG = unpermute_cols(ph)
+    KC = unpermute_cols(ws_view(ws, lay.off_ktilde_c2, B * H * M * 64 * D, torch.bfloat16).reshape(B * H, M, 64, D))
     for bh in range(B * H):
         b, h = divmod(bh, H)
-        for c in range(M2):
-            rows = slice(128 * c, min(128 * c + 128, L))
+        for c in range(MG):
+            rows = slice(chunk * c, chunk * c + chunk)
             q, k, w = (getattr(x, a)[b, h, rows].astype(np.float64) for a in ("q", "k", "w"))
             beta = x.beta[b, h, rows].astype(np.float64)
             rp = oracle.householder_product(w, beta)
-            ma, _ = errors(P2[bh, c], rp)
-            assert ma <= (2e-5 if transport == "bf16x3" else 2e-2), f"P over 128 tokens, chunk {c}: {ma:.2e}"
-            _, rk, _ = oracle.chunk_terms(q, k, w, beta)  # keys carried to the end of the 128 tokens
-            n = min(64, rows.stop - rows.start)
-            assert errors(K2[bh, c, :n], rk[:n])[0] <= 2 ** -6 * max(1.0, np.abs(rk).max()), f"ktilde' {c}"
+            ma, _ = errors(PG[bh, c], rp)
+            assert ma <= (2e-5 if transport == "bf16x3" else 2e-2), f"P over {chunk} tokens, chunk {c}: {ma:.2e}"
+            _, rk, _ = oracle.chunk_terms(q, k, w, beta)  # keys carried to the end of the chunk's tokens
+            for j in range(G - 1):  # every sub-chunk but the top one
+                want = rk[64 * j:64 * j + 64]
+                got = KC[bh, G * c + j]
+                assert errors(got, want)[0] <= 2 ** -6 * max(1.0, np.abs(want).max()), f"carried keys {c}/{j}"
 
 
 @pytest.mark.parametrize("transport,fox", [("bf16", False), ("bf16x3", True)])
@@ -202,6 +215,8 @@ def sampled_rows(L, seed=0):
     (1, 24, 32768, "lm", "bf16x3", 128),    # long context, 128-token chunks
     (1, 24, 32768, "stress_qk_beta2", "bf16x3", 128),
     (8, 24, 4096, "stress_qk", "bf16", 128),
+    (8, 24, 4096, "lm", "bf16", 256),       # 256-token chunks
+    (1, 24, 32768, "stress_qk_beta2", "bf16x3", 256),
 ])
 def test_full_size_sampled_rows(B, H, L, recipe, transport, chunk):
     print(f"[case] full B={B} H={H} L={L} recipe={recipe} transport={transport} chunk={chunk}", flush=True)
