@@ -409,7 +409,7 @@ def main():
                    "transport": args.transport, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(PREFILL_COUNTERS, "mfma_attn_kernel<{},{},false,2,4>".format(
+                     "traffic": measured_traffic(PREFILL_COUNTERS, "mfma_attn_kernel<{},{},1,2,4>".format(
                          "true" if args.fox else "false", "true" if args.transport == "bf16x3" else "false"),
                          "mfma_path.hip"),
                      "traffic_unit": "bytes per launch", "kernel": "mfma_attn_kernel",
