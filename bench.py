@@ -18,6 +18,7 @@ Also reported on the same JSON line:
   decode        batch 32, H=24, d=64, 65536 cached tokens, 128 steps timed back
                 to back: HBM bytes the step must move (cached keys read and
                 written back, cached values read) over the measured time.
+  fox_prefill   the PaTH-FoX prefill at the same shape (adds log-forget gates): step and scan.
   chunk_sweep   the same prefill step at chunk 64, 128 and 256 (chunks above 64 are grouped
                 64-token sub-chunks; the scan moves its queries once per chunk).
   cache_handoff the prefill workspace turned into a decode cache (path_attn_cache_from_prefill)
@@ -196,6 +197,42 @@ def bench_handoff(args, res, ctx):
     return {"workload": f"prefill -> decode cache hand-off, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16",
             "ms": ms, "bytes": nbytes, "achieved_gbs": gbs, "peak_gbs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
             "chained_steps_per_head": M}
+
+
+def bench_fox(args, ctx):
+    """PaTH-FoX prefill at the same shape (the same q, k, v, w, beta plus log-forget gates
+    logsigmoid(N(3, 1))): whole step and the scan alone."""
+    import numpy as np
+    import torch
+    from dependent_positional_attention_amd import native, synth
+
+    q, k, v, w, beta, scale, ws = (ctx[n] for n in ("q", "k", "v", "w", "beta", "scale", "ws"))
+    B, H, L, d = q.shape
+    C = 64
+    logf = torch.from_numpy(synth.logsigmoid(synth._normal(0, "logf", (B, H, L), 1.0, 3.0)).astype(np.float32)).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), device="cuda", dtype=torch.float32)
+
+    def step():
+        native.path_attn_fwd(q, k, v, w, beta, logf, scale=scale, chunk=C, transport=args.transport, out=out,
+                             lse=lse, workspace=ws)
+
+    def scan():
+        native.path_attn_scan(v, logf, chunk=C, transport=args.transport, workspace=ws, out=out, lse=lse)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    ms = timed(step, 10)
+    ms_scan = timed(scan, 10)
+    assert torch.isfinite(out.float()).all(), "non-finite FoX output"
+    F = prefill_flops(B, H, L, d, C)
+    tf = F / (ms_scan * 1e-3) / 1e12
+    log(f"[bench] PaTH-FoX prefill: step {ms:.3f} ms, {B * L / (ms * 1e-3) / 1e6:.2f} M tokens/s; scan {ms_scan:.3f} ms "
+        f"= {tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak")
+    return {"workload": f"PaTH-FoX prefill forward, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16, "
+                        f"transport {args.transport}", "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
+            "scan_ms": ms_scan, "scan_tflops": tf, "scan_frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
 
 
 def bench_chunks(args, ctx):
@@ -385,6 +422,7 @@ def main():
     res, x, ctx = bench_prefill(args)
     handoff = bench_handoff(args, res, ctx)
     sweep = None if args.no_sweep else bench_chunks(args, ctx)
+    fox = None if (args.no_sweep or args.fox) else bench_fox(args, ctx)
     del ctx
     cpu = None if args.no_cpu else bench_cpu(x, args)
     dec = None if args.no_decode else bench_decode(args)
@@ -421,6 +459,7 @@ def main():
         "decode": dec,
         "cache_handoff": handoff,
         "chunk_sweep": sweep,
+        "fox_prefill": fox,
         "long_context": long_ctx,
     }
     print(json.dumps(line), flush=True)

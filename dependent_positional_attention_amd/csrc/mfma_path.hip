@@ -534,15 +534,14 @@ struct ScanShape {
   static constexpr int kOps = kNm * kCopies;           // copy instructions per wave per chunk (+1 FoX)
 };
 
-// Attention scan.  Block-wide stream of key groups, group(n) = {ktilde_{n-1}, V_n, P_n [, P_lo n],
-// FoX prefix of chunk n-1} for n = top chunk ... 0 (chunk indices clamp at 0), so that one step of
-// a wave reads the values and transition of chunk n together with the keys of the chunk it scores
-// next.  Per wave, with its query chunk m:
+// Attention scan.  Block-wide stream of key chunks n = top chunk ... 0, each {ktilde_n (or its
+// carried form), V_n, P_n [, P_lo n] (or the group product), FoX prefix of chunk n}.  Per wave, with
+// its query chunk m (chunks above m are skipped):
 //   n == m (own chunk):  logits from the precomputed in-chunk S (masked), exact row max, P^T V_m;
-//                        running queries Q_run = qtilde; logits of chunk m-1.
-//   n <  m:              p = exp2(z) for the logits z of chunk n (computed one step earlier, already
-//                        minus the running max, which seeds the MFMA accumulator); O^T += V_n^T p^T;
-//                        Q_run^T <- P_n Q_run^T; logits of chunk n-1 with the moved queries.
+//                        running queries Q_run = qtilde.
+//   n <  m:              z = ktilde_n Q_run^T minus the running max (which seeds the MFMA
+//                        accumulator), p = exp2(z), O^T += V_n^T p^T, and, when a chunk below
+//                        follows, Q_run^T <- P_n Q_run^T.
 // The running max is raised lazily: a lane whose partial row sum exceeds 2^kRescale (so possibly
 // some p > 2^kRescale) sends the wave through the exact max, which raises the reference of any
 // column whose max exceeds it by more than kRescale and rescales O, the sums and the pending logits.
@@ -1174,6 +1173,7 @@ __global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf
                                                                       __bf16* __restrict__ vc) {
   constexpr int NB = 4;
   __shared__ __align__(1024) __bf16 ring[NB][X3 ? 3 : 2][kTile];
+  __shared__ __align__(1024) __bf16 kst[2][kTile];  // finished key rows of the last two chunks (swizzled)
   const int64_t bh = blockIdx.x, Lp = M * kC;
   const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1195,6 +1195,16 @@ __global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf
     }
   };
   if (wave < 4) vload(M - 1);
+  // key rows 16 wave .. 16 wave + 15 of chunk n from a staging tile: 8 lanes per 128-byte row
+  auto flush = [&](int64_t n, const __bf16* tile) PA_INLINE {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 16 * wave + 8 * h + (l >> 3), c = l & 7;
+      const int64_t j = n * kC + row;
+      if (j < L)
+        *reinterpret_cast<bf16x8*>(kc + ((size_t)bh * cap + j) * kD + 8 * c) = tile_frag(tile, row, c);
+    }
+  };
   auto emit = [&](int64_t i, const bf16x8 (&rh)[2], const bf16x8 (&rl)[2], const ChainFrags& F) PA_INLINE {
     const int64_t n = M - 1 - i;
     {
@@ -1206,15 +1216,18 @@ __global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf
       }
       vload(n - 1);
     }
+    // keys: this wave's 16 columns go to the staging tile; the previous chunk's tile, complete since
+    // the last barrier, is stored as whole 128-byte rows
+    if (i > 0) flush(n + 1, kst[(i - 1) & 1]);
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
       const f32x4 a = chain_keys(rh, rl, F.k[bt]);
-      const int64_t j = n * kC + 16 * bt + r;
-      if (j < L)
-        *reinterpret_cast<bf16x4*>(kc + ((size_t)bh * cap + j) * kD + 16 * wave + 4 * g) = pack4(a[0], a[1], a[2], a[3]);
+      const int row = 16 * bt + r, c0 = 16 * wave + 4 * g;
+      *reinterpret_cast<bf16x4*>(kst[i & 1] + swz(row, c0 >> 3) + (c0 & 7)) = pack4(a[0], a[1], a[2], a[3]);
     }
   };
   chain_run<X3, NB>(ring, M, false, racc, src, emit);
+  if (wave < 4) flush(0, kst[(M - 1) & 1]);
 }
 
 // =========================================================================== host
