@@ -291,65 +291,31 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
 
   // ---------------------------------------------------------------- C: off-diagonal blocks of Z, by distance
   // Z[i][j] (i <= j) lives at Af[j][i].  Wave I owns row block I:
-  //   T = sum_{K=I+1..J} A_IK Z_KJ,   Z_IJ^T = -T^T Z_II^T,   J = I + lv,
-  // both on the matrix cores with fp32 operands split into bf16 hi + lo (lo*lo dropped).
-  auto split8 = [](const float4& x0, const float4& x1, bf16x8& hi, bf16x8& lo) {
-    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 h = (__bf16)v[j];
-      hi[j] = h;
-      lo[j] = (__bf16)(v[j] - (float)h);
-    }
-  };
+  //   T = sum_{K=I+1..J} A_IK Z_KJ,   Z_IJ = -Z_II T,   J = I + lv,
+  // both on the fp32 matrix cores (16x16x4: lane (r, q) brings A[r][q] and B[q][r]), straight from LDS.
+  // In the second product the contraction index kk = 4q + m of step m makes T's accumulator slot m
+  // the B-operand of the same lane.
   for (int lv = 1; lv < 4; ++lv) {
     const int I = wave, J = wave + lv;
     if (J < 4) {
       f32x4 tacc = zero;
-      for (int st = 0; st < (lv + 1) / 2; ++st) {  // k = 16(I+1) + 32st + 8g + j, 16 lv values
-        const int kidx = 32 * st + 8 * g;
-        bf16x8 ah = {}, al = {}, bh = {}, bl = {};
-        if (kidx < 16 * lv) {
-          const int kc = 16 * (I + 1) + kidx;  // global column of A / row of Z
-          const float* ar = Af + (16 * I + r) * kLDF + kc;
-          split8(*reinterpret_cast<const float4*>(ar), *reinterpret_cast<const float4*>(ar + 4), ah, al);
-          const float* zr = Af + (16 * J + r) * kLDF + kc;  // Z[kc + j][16J + r]
-          float4 z0 = *reinterpret_cast<const float4*>(zr), z1 = *reinterpret_cast<const float4*>(zr + 4);
-          if (kc >= 16 * J) {  // diagonal block Z_JJ: zero below its diagonal (kk > jj)
-            const int kk0 = kc - 16 * J;
-            float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) zz[j] = (kk0 + j > r) ? 0.f : zz[j];
-            z0 = make_float4(zz[0], zz[1], zz[2], zz[3]);
-            z1 = make_float4(zz[4], zz[5], zz[6], zz[7]);
-          }
-          split8(z0, z1, bh, bl);
-        }
-        tacc = mfma16(ah, bh, tacc);  // D[ii][jj] = sum_k A[16I + ii][k] Z[k][16J + jj]
-        tacc = mfma16(ah, bl, tacc);
-        tacc = mfma16(al, bh, tacc);
+      for (int k0 = 16 * (I + 1); k0 < 16 * (J + 1); k0 += 4) {
+        const int kk = k0 + g;
+        const float a = Af[(16 * I + r) * kLDF + kk];  // A[16I + r][kk]
+        const float zb = Af[(16 * J + r) * kLDF + kk];  // Z[kk][16J + r]; Z_JJ is upper triangular
+        const float b = (kk >= 16 * J && kk - 16 * J > r) ? 0.f : zb;
+        tacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, tacc, 0, 0, 0);
       }
-      // A-operand T^T over k = kk (rows 4g..4g+3 of the accumulator; slots 4..7 pad k to 32)
-      bf16x8 th = {}, tl = {};
-      // B-operand Z_II^T: column ii = r, k = kk = 4g + j: Z[16I + r][16I + kk] for kk >= r
-      bf16x8 zh = {}, zl = {};
+      f32x4 zacc = zero;  // D[ii][jj] = sum_kk Z[16I + ii][16I + kk] T[kk][jj]
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const __bf16 h = (__bf16)tacc[j];
-        th[j] = h;
-        tl[j] = (__bf16)(tacc[j] - (float)h);
-        const int kk = 4 * g + j;
-        const float zv = (kk >= r) ? Af[(16 * I + kk) * kLDF + 16 * I + r] : 0.f;
-        const __bf16 zhh = (__bf16)zv;
-        zh[j] = zhh;
-        zl[j] = (__bf16)(zv - (float)zhh);
+      for (int m = 0; m < 4; ++m) {
+        const int kk = 4 * g + m;
+        const float a = (kk >= r) ? Af[(16 * I + kk) * kLDF + 16 * I + r] : 0.f;  // Z[16I + r][16I + kk]
+        zacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, tacc[m], zacc, 0, 0, 0);
       }
-      f32x4 zacc = zero;  // D[jj][ii] = sum_kk T[kk][jj] Z[16I + ii][16I + kk] = (Z_II T)^T
-      zacc = mfma16(th, zh, zacc);
-      zacc = mfma16(th, zl, zacc);
-      zacc = mfma16(tl, zh, zacc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Af[(16 * J + 4 * g + i) * kLDF + 16 * I + r] = -zacc[i];
+      // lane (r, g) holds Z_IJ[4g + e][r] = Z[16I + 4g + e][16J + r], stored at Af[16J + r][16I + 4g + e]
+      *reinterpret_cast<float4*>(Af + (16 * J + r) * kLDF + 16 * I + 4 * g) =
+          make_float4(-zacc[0], -zacc[1], -zacc[2], -zacc[3]);
     }
     __syncthreads();
   }
