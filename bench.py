@@ -346,7 +346,7 @@ def bench_decode(args):
     Bd, H, d = 32, 24, 64
     T0, S = args.decode_cache, args.decode_steps
     W = 3
-    cap = T0 + S
+    cap = T0 + 2 * S  # room for the deferred-update steps that follow the timed in-place ones
     log(f"[bench] decode: batch {Bd}, H {H}, d {d}, cache {T0}, {S} steps; filling the cache on the GPU")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
@@ -388,8 +388,35 @@ def bench_decode(args):
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] decode: {S} steps in {ms:.2f} ms ({ms / S:.3f} ms/step), {gbs:.0f} GB/s "
         f"= {gbs / HBM_PEAK_GBS:.3f} of HBM peak")
+    # the same steps with the key updates deferred (period 16), continuing from the cache just left
+    P = 16
+    state = torch.zeros(native.path_decode_deferred_state_bytes(Bd, H, d) // 4, device="cuda", dtype=torch.float32)
+    t_cur = T0 + S
+    tdef = T0 + S
+    ndef = min(S, cap - tdef)
+    dbytes, ms_def = 0, float("nan")
+    if ndef >= P:
+        ndef -= ndef % P
+        e0.record()
+        for i in range(ndef):
+            t = tdef + i
+            _, _, t_cur = native.path_decode_step_deferred(kc, vc, t, t_cur, qs[i % (S + W)], ks[i % (S + W)],
+                                                           vs[i % (S + W)], wsd[i % (S + W)], betas[i % (S + W)],
+                                                           period=P, state=state, scale=st.scale, out=out, lse=lse,
+                                                           workspace=wsb)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_def = e0.elapsed_time(e1)
+        dbytes = sum(Bd * H * (((3 if (i + 1) % P == 0 else 2) * (tdef + i)) * d * 2 + 6 * d * 2) for i in range(ndef))
+        log(f"[bench] decode, key updates deferred (period {P}): {ndef} steps in {ms_def:.2f} ms "
+            f"({ms_def / ndef:.3f} ms/step, {ms / S / (ms_def / ndef):.2f}x the in-place step), "
+            f"{dbytes / (ms_def * 1e-3) / 1e9:.0f} GB/s")
+    deferred = None if not ndef >= P else {
+        "period": P, "steps": ndef, "ms_per_step": ms_def / ndef, "speedup_vs_in_place": (ms / S) / (ms_def / ndef),
+        "achieved_gbs": dbytes / (ms_def * 1e-3) / 1e9,
+        "note": "keys brought up to date every 16 steps; between updates the query is moved instead (same outputs)"}
     return {"metric": "PaTH decode step HBM GB/s at 64K cache", "value": gbs, "unit": "GB/s",
-            "ms_per_step": ms / S, "steps": S,
+            "ms_per_step": ms / S, "steps": S, "deferred_updates": deferred,
             "config": {"workload": "decode batch 32 x 24 heads, d=64, bf16 cache of 65536 tokens growing by 1/step",
                        "batch": Bd, "heads": H, "d": d, "cache_tokens": T0},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -28,6 +28,11 @@ hipError_t decode_step(bool bf16, int d, void* kc, void* vc, float* fc, int64_t 
                        const float* beta_t, const float* f_t, void* out, float* lse, int64_t BH, float scale,
                        int splits, float* part, hipStream_t st);
 hipError_t slot_bias_run(const float* logf, int64_t BH, int64_t L, int64_t cap, float* fc, hipStream_t st);
+int decode_max_period();
+hipError_t decode_step_deferred(bool bf16, int d, void* kc, void* vc, float* fc, int64_t cap, int64_t t,
+                                int64_t t_cur, int period, float* state, const void* q_t, const void* k_t,
+                                const void* v_t, const void* w_t, const float* beta_t, const float* f_t, void* out,
+                                float* lse, int64_t BH, float scale, int splits, float* part, hipStream_t st);
 }  // namespace pathattn
 
 using namespace pathattn;
@@ -279,6 +284,42 @@ path_status path_decode_step(void* kcache, void* vcache, float* fcache, int64_t 
   return from_hip(decode_step(dtype == PATH_DTYPE_BF16, d, kcache, vcache, fcache, capacity, t, t_batch, (int)H, q_t,
                               k_t, v_t, w_t, beta_t, log_forget_t, out, lse, BH, scale, (int)S,
                               static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+path_status path_decode_deferred_state_bytes(int64_t B, int64_t H, int d, size_t* bytes) {
+  if (bytes == nullptr || B < 0 || H < 0) return PATH_ERR_INVALID_ARG;
+  if (!decode_supported(d)) return PATH_ERR_UNSUPPORTED;
+  *bytes = (size_t)(B * H * (int64_t)decode_max_period() * (d + 2) * 4);
+  return PATH_OK;
+}
+
+path_status path_decode_step_deferred(void* kcache, void* vcache, float* fcache, int64_t capacity, int64_t t,
+                                      int64_t t_cur, int period, float* state, size_t state_bytes,
+                                      const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                                      const float* beta_t, const float* log_forget_t, void* out, float* lse,
+                                      int64_t B, int64_t H, int d, float scale, int dtype, int splits,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || capacity < 0 || splits < 0) return PATH_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype) || !decode_supported(d)) return PATH_ERR_UNSUPPORTED;
+  if (t < 0 || t >= capacity || t_cur < 0 || t_cur > t) return PATH_ERR_INVALID_ARG;
+  if (period < 1 || period > decode_max_period() || t - t_cur >= period) return PATH_ERR_INVALID_ARG;
+  if ((log_forget_t == nullptr) != (fcache == nullptr)) return PATH_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  if (BH == 0) return PATH_OK;
+  if (!kcache || !vcache || !state || !q_t || !k_t || !v_t || !w_t || !beta_t || !out || !workspace)
+    return PATH_ERR_INVALID_ARG;
+  if (misaligned(kcache) || misaligned(vcache) || misaligned(q_t) || misaligned(k_t) || misaligned(v_t) ||
+      misaligned(w_t) || misaligned(beta_t) || misaligned(out) || misaligned(lse) || misaligned(workspace) ||
+      misaligned(fcache) || misaligned(log_forget_t) || misaligned(state))
+    return PATH_ERR_UNSUPPORTED;
+  if (state_bytes < (size_t)(BH * (int64_t)decode_max_period() * (d + 2) * 4)) return PATH_ERR_INVALID_ARG;
+  const int64_t S = splits > 0 ? splits : decode_auto_splits(t + 1);
+  if (S > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
+  if (workspace_bytes < (size_t)(BH * S * (int64_t)(d + 2) * 4)) return PATH_ERR_INVALID_ARG;
+  if (BH > kMaxGridY) return PATH_ERR_UNSUPPORTED;
+  return from_hip(decode_step_deferred(dtype == PATH_DTYPE_BF16, d, kcache, vcache, fcache, capacity, t, t_cur, period,
+                                       state, q_t, k_t, v_t, w_t, beta_t, log_forget_t, out, lse, BH, scale, (int)S,
+                                       static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -82,6 +82,64 @@ __device__ __forceinline__ float group_sum(float x) {
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
 
+// Merge the key groups' online-softmax states (m, l, o) of one block through LDS and write the
+// block's partial (m, l, o[D]) for the combine kernel.
+template <int D, int VN, int LPK>
+__device__ __forceinline__ void merge_block(float mrun, float lrun, const float (&o)[VN], float* __restrict__ pp) {
+  constexpr int GPB = kDecThreads / LPK;
+  const int tid = threadIdx.x, grp = tid / LPK, sub = tid % LPK;
+  __shared__ float sm[GPB], sl[GPB];
+  __shared__ float so[GPB * D];
+  if (sub == 0) {
+    sm[grp] = mrun;
+    sl[grp] = lrun;
+  }
+#pragma unroll
+  for (int x = 0; x < VN; ++x) so[grp * D + sub * VN + x] = o[x];
+  __syncthreads();
+  if (tid < D) {
+    float M = -INFINITY;
+    for (int g = 0; g < GPB; ++g) M = fmaxf(M, sm[g]);
+    float Lsum = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+      for (int g = 0; g < GPB; ++g) {
+        const float f = fast_exp2(sm[g] - M);
+        Lsum += sl[g] * f;
+        acc += so[g * D + tid] * f;
+      }
+    }
+    pp[2 + tid] = acc;
+    if (tid == 0) {
+      pp[0] = M;
+      pp[1] = Lsum;
+    }
+  }
+}
+
+// Online-softmax update of a group's state with kDecUnroll logits z (log2 units) and their values.
+template <int VN>
+__device__ __forceinline__ void absorb(float& mrun, float& lrun, float (&o)[VN], const float (&z)[kDecUnroll],
+                                       const float (&vf)[kDecUnroll][VN]) {
+  float bm = z[0];
+#pragma unroll
+  for (int u = 1; u < kDecUnroll; ++u) bm = fmaxf(bm, z[u]);
+  const float mnew = fmaxf(mrun, bm);
+  if (mnew != -INFINITY) {
+    const float alpha = fast_exp2(mrun - mnew);
+    lrun *= alpha;
+#pragma unroll
+    for (int x = 0; x < VN; ++x) o[x] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const float p = fast_exp2(z[u] - mnew);
+      lrun += p;
+#pragma unroll
+      for (int x = 0; x < VN; ++x) o[x] += p * vf[u][x];
+    }
+    mrun = mnew;
+  }
+}
+
 // Token count of sequence b: the uniform t, or t_batch[b] when given; -1 marks an entry outside [0, t].
 __device__ __forceinline__ int64_t seq_tokens(const int* t_batch, int64_t bh, int H, int64_t t) {
   if (t_batch == nullptr) return t;
@@ -180,54 +238,181 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
       sd = group_sum<LPK>(sd);
       z[u] = live ? sd * scale_log2 + (FOX ? bias * kLog2e : 0.f) : -INFINITY;
     }
-    float bm = z[0];
-#pragma unroll
-    for (int u = 1; u < kDecUnroll; ++u) bm = fmaxf(bm, z[u]);
-    const float mnew = fmaxf(mrun, bm);
-    if (mnew != -INFINITY) {
-      const float alpha = fast_exp2(mrun - mnew);
-      lrun *= alpha;
-#pragma unroll
-      for (int x = 0; x < VN; ++x) o[x] *= alpha;
-#pragma unroll
-      for (int u = 0; u < kDecUnroll; ++u) {
-        const float p = fast_exp2(z[u] - mnew);
-        lrun += p;
-#pragma unroll
-        for (int x = 0; x < VN; ++x) o[x] += p * vf[u][x];
-      }
-      mrun = mnew;
-    }
+    absorb<VN>(mrun, lrun, o, z, vf);
   }
 
-  // merge the GPB group states of this block through LDS
-  __shared__ float sm[GPB], sl[GPB];
-  __shared__ float so[GPB * D];
-  if (sub == 0) {
-    sm[grp] = mrun;
-    sl[grp] = lrun;
+  merge_block<D, VN, LPK>(mrun, lrun, o, part + ((size_t)bh * splits + split) * (D + 2));
+}
+
+// ------------------------------------------------------------------------------------ deferred updates
+// The same step with the key updates deferred: the slots are brought up to date only every `period`
+// steps, and in between each step transports its query instead, which leaves the cached keys
+// untouched (read once, not read and written).  With t_cur the number of slots that are current
+// (they have absorbed every transition of steps < t_cur) and np = t - t_cur pending steps whose
+// transitions T_0 .. T_{np-1} (steps t_cur .. t-1) sit in `state`, plus T_np = H_t:
+//   slot j <  t_cur:         logit = slot_j . Q_0                  Q_i = T_i T_{i+1} ... T_np q_t
+//   slot t_cur <= j < t:     logit = slot_j . Q_{j - t_cur + 1}    (raw key, transitions after it)
+//   slot t:                  logit = k_t . q_t                     (Q_{np+1} = q_t)
+// which is k_j(t) . q_t for every j, the in-place rule's logit, transition for transition.  On the
+// step with np + 1 == period the slots take all pending transitions in order (T_0 first for the
+// current slots, T_{j - t_cur + 1} first for the raw ones), are written back, and score against q_t as
+// in the in-place kernel.  PaTH-FoX: with G_i = sum of the gates of steps t_cur + i .. t, a current
+// slot's bias is its stored value plus G_0 and a raw slot's is G_{j - t_cur + 1}; the update step
+// stores them.  State per (b, h): kMaxPeriod directions (fp32, d each), then kMaxPeriod strengths and
+// kMaxPeriod gates.
+constexpr int kMaxPeriod = 16;
+
+template <typename T, int D, bool FOX>
+__global__ __launch_bounds__(kDecThreads) void decode_deferred_kernel(
+    T* __restrict__ kc, T* __restrict__ vc, float* __restrict__ fc, int64_t cap, int64_t t, int64_t t_cur,
+    int period, float* __restrict__ state, const T* __restrict__ q_t, const T* __restrict__ k_t,
+    const T* __restrict__ v_t, const T* __restrict__ w_t, const float* __restrict__ beta_t,
+    const float* __restrict__ f_t, float scale_log2, int splits, int64_t keys_per_split, float* __restrict__ part) {
+  constexpr int VN = Vec16<T>::N;
+  constexpr int LPK = D / VN;
+  constexpr int GPB = kDecThreads / LPK;
+  constexpr int SS = kMaxPeriod * (D + 2);  // state floats per (b, h)
+  __shared__ float Wl[kMaxPeriod][D], Ql[kMaxPeriod + 1][D], Bl[kMaxPeriod], Gl[kMaxPeriod + 1];
+
+  const int split = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int grp = tid / LPK, sub = tid % LPK;
+  const int np = (int)(t - t_cur);
+  const bool flush = np + 1 == period;
+  float* st = state + (size_t)bh * SS;
+
+  // transitions T_0 .. T_np, their strengths and gates, and q_t
+  for (int e = tid; e < (np + 1) * D; e += kDecThreads) {
+    const int i = e / D, x = e % D;
+    Wl[i][x] = i < np ? st[i * D + x] : to_f32(w_t[bh * D + x]);
   }
-#pragma unroll
-  for (int x = 0; x < VN; ++x) so[grp * D + sub * VN + x] = o[x];
+  if (tid <= np) Bl[tid] = tid < np ? st[kMaxPeriod * D + tid] : beta_t[bh];
+  if (tid < D) Ql[np + 1][tid] = to_f32(q_t[bh * D + tid]);
   __syncthreads();
-  if (tid < D) {
-    float M = -INFINITY;
-    for (int g = 0; g < GPB; ++g) M = fmaxf(M, sm[g]);
-    float Lsum = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int g = 0; g < GPB; ++g) {
-        const float f = fast_exp2(sm[g] - M);
-        Lsum += sl[g] * f;
-        acc += so[g * D + tid] * f;
+  // Q_i = T_i Q_{i+1} for i = np .. 0 (wave 0, two elements per lane), gate suffix sums G_i
+  if (tid < 64) {
+    float q0 = tid < D ? Ql[np + 1][tid] : 0.f, q1 = tid + 64 < D ? Ql[np + 1][tid + 64] : 0.f;
+    float gs = 0.f;
+    if (tid == 0) Gl[np + 1] = 0.f;
+    for (int i = np; i >= 0; --i) {
+      const float w0 = tid < D ? Wl[i][tid] : 0.f, w1 = tid + 64 < D ? Wl[i][tid + 64] : 0.f;
+      float dp = w0 * q0 + w1 * q1;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) dp += __shfl_xor(dp, o, 64);
+      const float c = Bl[i] * dp;
+      q0 -= c * w0;
+      q1 -= c * w1;
+      if (tid < D) Ql[i][tid] = q0;
+      if (tid + 64 < D) Ql[i][tid + 64] = q1;
+      if constexpr (FOX) {
+        gs += i < np ? st[kMaxPeriod * (D + 1) + i] : f_t[bh];
+        if (tid == 0) Gl[i] = gs;
       }
     }
-    float* pp = part + ((size_t)bh * splits + split) * (D + 2);
-    pp[2 + tid] = acc;
+  }
+  __syncthreads();
+
+  const int64_t j0 = (int64_t)split * keys_per_split;
+  int64_t j1 = j0 + keys_per_split;
+  if (j1 > t + 1) j1 = t + 1;
+  T* kb = kc + (size_t)bh * cap * D;
+  T* vb = vc + (size_t)bh * cap * D;
+  float* fb = FOX ? fc + (size_t)bh * cap : nullptr;
+  // the current slots score against Q_0 (flush: against q_t after their update)
+  float qv[VN];
+#pragma unroll
+  for (int x = 0; x < VN; ++x) qv[x] = Ql[flush ? np + 1 : 0][sub * VN + x];
+  const float g0 = FOX ? Gl[0] : 0.f;
+
+  float mrun = -INFINITY, lrun = 0.f, o[VN];
+#pragma unroll
+  for (int x = 0; x < VN; ++x) o[x] = 0.f;
+
+  for (int64_t base = j0 + grp; base < j1; base += (int64_t)GPB * kDecUnroll) {
+    uint4 kr[kDecUnroll], vr[kDecUnroll];
+    int64_t jj[kDecUnroll];
+    float fb_old[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      jj[u] = base + (int64_t)u * GPB;
+      kr[u] = make_uint4(0u, 0u, 0u, 0u);
+      vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      fb_old[u] = 0.f;
+      if (jj[u] < j1) {
+        if (jj[u] < t) {
+          kr[u] = *((const uint4*)(kb + jj[u] * D) + sub);
+          if constexpr (FOX) {
+            if (jj[u] < t_cur) fb_old[u] = fb[jj[u]];
+          }
+        } else {
+          kr[u] = *((const uint4*)(k_t + bh * D) + sub);
+        }
+        vr[u] = (jj[u] < t) ? *((const uint4*)(vb + jj[u] * D) + sub) : *((const uint4*)(v_t + bh * D) + sub);
+      }
+    }
+    float z[kDecUnroll];
+    float vf[kDecUnroll][VN];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      float kf[VN];
+      unpack16<T>(kr[u], kf);
+      unpack16<T>(vr[u], vf[u]);
+      const int64_t j = jj[u];
+      const bool live = j < j1;
+      const bool raw = j >= t_cur && j < t;        // key added since the last update
+      const int i0 = raw ? (int)(j - t_cur) + 1 : 0;  // its first pending transition
+      float bias = 0.f;
+      if constexpr (FOX) bias = j < t_cur ? fb_old[u] + g0 : (raw ? Gl[i0] : 0.f);
+      float qj[VN];
+#pragma unroll
+      for (int x = 0; x < VN; ++x) qj[x] = qv[x];
+      if (live && j < t) {
+        if (flush) {
+          for (int i = i0; i <= np; ++i) {
+            float pd = 0.f;
+#pragma unroll
+            for (int x = 0; x < VN; ++x) pd += Wl[i][sub * VN + x] * kf[x];
+            const float c = Bl[i] * group_sum<LPK>(pd);
+#pragma unroll
+            for (int x = 0; x < VN; ++x) kf[x] -= c * Wl[i][sub * VN + x];
+          }
+          const uint4 nk = pack16<T>(kf);
+          *((uint4*)(kb + j * D) + sub) = nk;
+          unpack16<T>(nk, kf);  // attend with exactly the stored key
+          if constexpr (FOX) {
+            if (sub == 0) fb[j] = bias;
+          }
+        } else if (raw) {
+#pragma unroll
+          for (int x = 0; x < VN; ++x) qj[x] = Ql[i0][sub * VN + x];
+        }
+      } else if (live) {  // slot t: the new token, stored untransformed
+        *((uint4*)(kb + j * D) + sub) = kr[u];
+        *((uint4*)(vb + j * D) + sub) = vr[u];
+        if constexpr (FOX) {
+          if (sub == 0) fb[j] = 0.f;
+        }
+#pragma unroll
+        for (int x = 0; x < VN; ++x) qj[x] = Ql[np + 1][sub * VN + x];
+      }
+      float sd = 0.f;
+#pragma unroll
+      for (int x = 0; x < VN; ++x) sd += qj[x] * kf[x];
+      sd = group_sum<LPK>(sd);
+      z[u] = live ? sd * scale_log2 + (FOX ? bias * kLog2e : 0.f) : -INFINITY;
+    }
+    absorb<VN>(mrun, lrun, o, z, vf);
+  }
+  // keep this step's transition for the steps until the next update (one block per (b, h) writes it)
+  if (!flush && split == 0) {
+    for (int x = tid; x < D; x += kDecThreads) st[np * D + x] = Wl[np][x];
     if (tid == 0) {
-      pp[0] = M;
-      pp[1] = Lsum;
+      st[kMaxPeriod * D + np] = Bl[np];
+      if constexpr (FOX) st[kMaxPeriod * (D + 1) + np] = f_t[bh];
     }
   }
+  merge_block<D, VN, LPK>(mrun, lrun, o, part + ((size_t)bh * splits + split) * (D + 2));
 }
 
 template <typename T, int D>
@@ -280,6 +465,48 @@ static hipError_t launch_decode(void* kc, void* vc, float* fc, int64_t cap, int6
   if (e != hipSuccess) return e;
   decode_combine_kernel<T, D><<<(unsigned)BH, 64, 0, st>>>(part, splits, t_batch, H, t, (T*)out, lse);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_deferred(void* kc, void* vc, float* fc, int64_t cap, int64_t t, int64_t t_cur, int period,
+                                  float* state, const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                                  const float* beta_t, const float* f_t, void* out, float* lse, int64_t BH,
+                                  float scale, int splits, float* part, hipStream_t st) {
+  const int64_t keys = t + 1;
+  const int64_t kps = (keys + splits - 1) / splits;
+  dim3 grid((unsigned)splits, (unsigned)BH);
+  if (f_t != nullptr)
+    decode_deferred_kernel<T, D, true><<<grid, kDecThreads, 0, st>>>(
+        (T*)kc, (T*)vc, fc, cap, t, t_cur, period, state, (const T*)q_t, (const T*)k_t, (const T*)v_t,
+        (const T*)w_t, beta_t, f_t, scale * kLog2e, splits, kps, part);
+  else
+    decode_deferred_kernel<T, D, false><<<grid, kDecThreads, 0, st>>>(
+        (T*)kc, (T*)vc, nullptr, cap, t, t_cur, period, state, (const T*)q_t, (const T*)k_t, (const T*)v_t,
+        (const T*)w_t, beta_t, nullptr, scale * kLog2e, splits, kps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<T, D><<<(unsigned)BH, 64, 0, st>>>(part, splits, nullptr, 1, t, (T*)out, lse);
+  return hipGetLastError();
+}
+
+int decode_max_period() { return kMaxPeriod; }
+
+hipError_t decode_step_deferred(bool bf16, int d, void* kc, void* vc, float* fc, int64_t cap, int64_t t,
+                                int64_t t_cur, int period, float* state, const void* q_t, const void* k_t,
+                                const void* v_t, const void* w_t, const float* beta_t, const float* f_t, void* out,
+                                float* lse, int64_t BH, float scale, int splits, float* part, hipStream_t st) {
+#define PATHATTN_DEF_CASE(DD)                                                                                  \
+  if (d == DD)                                                                                                 \
+    return bf16 ? launch_deferred<__bf16, DD>(kc, vc, fc, cap, t, t_cur, period, state, q_t, k_t, v_t, w_t,    \
+                                              beta_t, f_t, out, lse, BH, scale, splits, part, st)              \
+                : launch_deferred<float, DD>(kc, vc, fc, cap, t, t_cur, period, state, q_t, k_t, v_t, w_t,     \
+                                             beta_t, f_t, out, lse, BH, scale, splits, part, st);
+  PATHATTN_DEF_CASE(16)
+  PATHATTN_DEF_CASE(32)
+  PATHATTN_DEF_CASE(64)
+  PATHATTN_DEF_CASE(128)
+#undef PATHATTN_DEF_CASE
+  return hipErrorInvalidValue;
 }
 
 bool decode_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }

@@ -44,7 +44,8 @@ class WsLayout(ctypes.Structure):
 
 EXPORTS = ("path_abi_version", "path_status_string", "path_attn_fwd_workspace_bytes", "path_attn_fwd",
            "path_attn_prep", "path_attn_scan", "path_attn_workspace_layout", "path_decode_workspace_bytes",
-           "path_decode_step", "path_attn_cache_from_prefill")
+           "path_decode_step", "path_attn_cache_from_prefill", "path_decode_deferred_state_bytes",
+           "path_decode_step_deferred")
 
 
 def lib():
@@ -69,8 +70,12 @@ def lib():
                                        i32, i32, vp, sz, vp]
         L.path_attn_cache_from_prefill.argtypes = [vp, vp, vp, sz, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, i32,
                                                    vp]
+        L.path_decode_deferred_state_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
+        L.path_decode_step_deferred.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, i64, i64, i32, f32, i32, i32, vp, sz, vp]
         for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd", "path_attn_prep",
-                  "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step", "path_attn_cache_from_prefill"):
+                  "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step", "path_attn_cache_from_prefill",
+                  "path_decode_deferred_state_bytes", "path_decode_step_deferred"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -265,3 +270,45 @@ def path_decode_step(kcache, vcache, t: int, q_t, k_t, v_t, w_t, beta_t, log_for
         _ptr(w_t), _ptr(beta_t), _ptr(log_forget_t), _ptr(out), _ptr(lse), B, H, d, float(scale),
         DTYPE[kcache.dtype], int(splits), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
+
+
+def path_decode_deferred_state_bytes(B, H, d) -> int:
+    n = ctypes.c_size_t(0)
+    _check("path_decode_deferred_state_bytes", lib().path_decode_deferred_state_bytes(B, H, d, ctypes.byref(n)))
+    return n.value
+
+
+def path_decode_step_deferred(kcache, vcache, t: int, t_cur: int, q_t, k_t, v_t, w_t, beta_t, log_forget_t=None, *,
+                              period: int, state, fcache=None, scale: Optional[float] = None, splits: int = 0,
+                              out=None, lse=None, workspace=None, stream=None,
+                              want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor], int]:
+    """One decode step with deferred key updates (see path_attn.h).  Returns (out, lse, next t_cur): the keys
+    are brought up to date when t - t_cur + 1 == period, after which t_cur becomes t + 1."""
+    _require(kcache, "kcache")
+    B, H, cap, d = kcache.shape
+    _require(vcache, "vcache", kcache.dtype, kcache.shape)
+    for name, x in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _require(x, name, kcache.dtype, (B, H, d))
+    _require(beta_t, "beta_t", torch.float32, (B, H))
+    if (log_forget_t is None) != (fcache is None):
+        raise ValueError("PaTH-FoX decode needs both log_forget_t and fcache")
+    if log_forget_t is not None:
+        _require(log_forget_t, "log_forget_t", torch.float32, (B, H))
+        _require(fcache, "fcache", torch.float32, (B, H, cap))
+    _require(state, "state", torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, d), device=kcache.device, dtype=kcache.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), device=kcache.device, dtype=torch.float32)
+    if workspace is None:
+        workspace = torch.empty(max(path_decode_workspace_bytes(B, H, d, cap, splits), 16), device=kcache.device,
+                                dtype=torch.uint8)
+    _check("path_decode_step_deferred", lib().path_decode_step_deferred(
+        _ptr(kcache), _ptr(vcache), _ptr(fcache), cap, int(t), int(t_cur), int(period), _ptr(state),
+        state.numel() * state.element_size(), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t),
+        _ptr(log_forget_t), _ptr(out), _ptr(lse), B, H, d, float(scale), DTYPE[kcache.dtype], int(splits),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    nxt = t + 1 if t - t_cur + 1 == period else t_cur
+    return out, lse, nxt

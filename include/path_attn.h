@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 4
+#define PATH_ABI_VERSION 5
 
 typedef enum {
   PATH_OK = 0,
@@ -200,6 +200,39 @@ path_status path_decode_step(void* kcache, void* vcache, float* fcache, int64_t 
                              const float* beta_t, const float* log_forget_t, void* out, float* lse, int64_t B,
                              int64_t H, int d, float scale, int dtype, int splits, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * Decode with deferred key updates.  The step is path_decode_step's (same
+ * attention output for the same inputs, up to rounding), but the cached keys
+ * are brought up to date only every `period` steps; in between, a step moves
+ * its query back through the transitions not yet applied to the keys
+ * (k_j^T (H_{j+1} ... H_t q_t) is the in-place rule's logit read from the other
+ * side), so the keys are only read, not read and written.  The transitions
+ * waiting to be applied (and their PaTH-FoX gates) live in `state`.
+ *
+ *   t_cur     slots 0..t_cur-1 are current (they have absorbed every transition
+ *             of steps < t_cur); slots t_cur..t-1 hold their keys as appended;
+ *             t_cur <= t and t - t_cur < period
+ *   period    1..16: the step with t - t_cur + 1 == period applies every waiting
+ *             transition to the keys (and FoX gates to fcache), writes them back,
+ *             and leaves all slots 0..t current: the next step passes t_cur = t + 1.
+ *             Any other step leaves t_cur unchanged and records its own transition
+ *             in `state`.  Passing period = t - t_cur + 1 forces the update now.
+ *   state     device buffer of path_decode_deferred_state_bytes bytes per batch,
+ *             owned by the caller, carried from step to step; no initialisation
+ *             needed when starting from a current cache (t_cur = t)
+ * Other arguments as path_decode_step (uniform t; no ragged batches here).
+ * The cache after an updating step equals path_decode_step's up to rounding
+ * (fewer roundings: each slot is rounded once per update).
+ */
+path_status path_decode_deferred_state_bytes(int64_t B, int64_t H, int d, size_t* bytes);
+
+path_status path_decode_step_deferred(void* kcache, void* vcache, float* fcache, int64_t capacity, int64_t t,
+                                      int64_t t_cur, int period, float* state, size_t state_bytes,
+                                      const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                                      const float* beta_t, const float* log_forget_t, void* out, float* lse,
+                                      int64_t B, int64_t H, int d, float scale, int dtype, int splits,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Prefill -> decode hand-off: fills a decode cache from a prefill workspace

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 4
+    assert L.path_abi_version() == 5
     for s in range(4):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"
@@ -174,6 +174,30 @@ def test_cache_handoff_validation(L):
     # an empty prompt or batch is valid and enqueues nothing
     assert handoff(L, Lq=0, v=None, ws=None, kc=None, vc=None) == OK
     assert handoff(L, H=0, v=None) == OK
+
+
+def deferred(L, kc=FAKE, vc=FAKE, fc=None, cap=128, t=10, t_cur=8, period=4, state=FAKE, state_n=1 << 20, q=FAKE,
+             k=FAKE, v=FAKE, w=FAKE, beta=FAKE, f=None, out=FAKE, lse=None, B=1, H=1, d=64, dtype=BF16, splits=0,
+             ws=FAKE, ws_n=1 << 20):
+    return L.path_decode_step_deferred(kc, vc, fc, cap, t, t_cur, period, state, state_n, q, k, v, w, beta, f, out, lse,
+                                       B, H, d, 0.125, dtype, splits, ws, ws_n, None)
+
+
+def test_deferred_decode_validation(L):
+    assert deferred(L, period=0) == INVALID
+    assert deferred(L, period=17) == INVALID
+    assert deferred(L, t_cur=11) == INVALID  # t_cur > t
+    assert deferred(L, t_cur=6, period=4) == INVALID  # 4 waiting steps exceed the period
+    assert deferred(L, t=128) == INVALID
+    assert deferred(L, state=None) == INVALID
+    assert deferred(L, state_n=64) == INVALID
+    assert deferred(L, fc=FAKE) == INVALID
+    assert deferred(L, state=MISALIGNED) == UNSUPPORTED
+    assert deferred(L, d=48) == UNSUPPORTED
+    assert deferred(L, B=0, kc=None) == OK
+    n = ctypes.c_size_t(0)
+    assert L.path_decode_deferred_state_bytes(32, 24, 64, ctypes.byref(n)) == OK
+    assert n.value == 32 * 24 * 16 * 66 * 4
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -205,3 +205,131 @@ def test_ragged_batch(fox):
         assert_parity(gl[:, b], rl, "bf16", f"lse seq {b}")
         # slots past this sequence's own count are untouched
         assert torch.equal(kc[b, :, tb0 + S:], kc_before[b, :, tb0 + S:])
+
+
+def run_deferred(kc, vc, fc, t0, steps, period, gates=None, force_at=None):
+    """Decode with deferred key updates from a current cache at t0; returns outputs, lse and the final t_cur."""
+    B, H, cap, d = kc.shape
+    dtype = steps.dtype
+    state = torch.zeros(native.path_decode_deferred_state_bytes(B, H, d) // 4, device="cuda", dtype=torch.float32)
+    outs, lses = [], []
+    t_cur = t0
+    for s in range(steps.q.shape[0]):
+        t = t0 + s
+        per = (t - t_cur + 1) if (force_at is not None and s == force_at) else period
+        o, l, t_cur = native.path_decode_step_deferred(
+            kc, vc, t, t_cur, dev(steps.q[s], dtype), dev(steps.k[s], dtype), dev(steps.v[s], dtype),
+            dev(steps.w[s], dtype), dev_f32(steps.beta[s]), dev_f32(gates[s]) if gates is not None else None,
+            period=per, state=state, fcache=fc, scale=steps.scale)
+        outs.append(host(o))
+        lses.append(host(l))
+    torch.cuda.synchronize()
+    return np.stack(outs), np.stack(lses), t_cur
+
+
+@pytest.mark.parametrize("dtype,d,fox,period", [("bf16", 64, False, 8), ("bf16", 64, True, 16), ("f32", 32, True, 4),
+                                                ("bf16", 128, False, 3), ("bf16", 16, False, 1), ("f32", 64, False, 5)])
+def test_deferred_decode_matches_oracle(dtype, d, fox, period):
+    """Deferred key updates give the in-place rule's outputs at every step; after an updating step the slots
+    equal the oracle's cache."""
+    B, H, T0 = 2, 3, 600
+    S = 2 * period + 3
+    cap = T0 + S + 2
+    print(f"[case] deferred decode dtype={dtype} d={d} fox={fox} period={period} steps={S}", flush=True)
+    ck, cv = synth.make_decode_cache(B, H, T0, d, dtype=dtype, seed=d + period)
+    steps = synth.make_decode_steps(S, B, H, d, dtype=dtype, seed=d + period)
+    gates = fox_gates(S, B, H, seed=period) if fox else None
+    fc0 = initial_slot_bias(B, H, T0, cap, seed=period) if fox else None
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.zeros((B, H, cap, d), device="cuda", dtype=td)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :T0] = dev(ck, dtype)
+    vc[:, :, :T0] = dev(cv, dtype)
+    fc = dev_f32(fc0) if fox else None
+    go, gl, t_cur = run_deferred(kc, vc, fc, T0, steps, period, gates)
+    BH = B * H
+    okc, ovc = np.zeros((BH, cap, d)), np.zeros((BH, cap, d))
+    okc[:, :T0] = ck.reshape(BH, T0, d)
+    ovc[:, :T0] = cv.reshape(BH, T0, d)
+    sh = lambda x: x.reshape(S, BH, -1) if x.ndim == 4 else x.reshape(S, BH)
+    kw = dict(fcache=fc0.reshape(BH, cap).astype(np.float64), logf=sh(gates)) if fox else {}
+    ro, rl = oracle.decode(okc, ovc, T0, sh(steps.q), sh(steps.k), sh(steps.v), sh(steps.w), sh(steps.beta),
+                           steps.scale, **kw)
+    assert_parity(go, ro.reshape(S, B, H, d), dtype, "out")
+    assert_parity(gl, rl.reshape(S, B, H), dtype, "lse")
+    # the last updating step left slots 0 .. t_cur - 1 current; the oracle's cache after that step
+    assert t_cur > T0
+    n_upd = t_cur - T0
+    okc2, ovc2 = np.zeros((BH, cap, d)), np.zeros((BH, cap, d))
+    okc2[:, :T0] = ck.reshape(BH, T0, d)
+    ovc2[:, :T0] = cv.reshape(BH, T0, d)
+    kw2 = dict(fcache=fc0.reshape(BH, cap).astype(np.float64), logf=sh(gates)[:n_upd]) if fox else {}
+    oracle.decode(okc2, ovc2, T0, sh(steps.q)[:n_upd], sh(steps.k)[:n_upd], sh(steps.v)[:n_upd],
+                  sh(steps.w)[:n_upd], sh(steps.beta)[:n_upd], steps.scale, **kw2)
+    check_cache(host(kc)[:, :, :t_cur], okc2.reshape(B, H, cap, d)[:, :, :t_cur], dtype, n_upd)
+    if fox:
+        want = kw2["fcache"].reshape(B, H, cap)[:, :, :t_cur]
+        got = host(fc)[:, :, :t_cur]
+        bound = (n_upd + 1) * 2.0 ** -24 * np.max(np.abs(want)) + 1e-6
+        assert np.max(np.abs(got - want)) <= bound
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_deferred_period_one_is_the_in_place_step(fox):
+    """period 1 updates the keys at every step: outputs and caches bit-identical to path_decode_step."""
+    B, H, T0, S, d = 2, 2, 900, 4, 64
+    cap = T0 + S
+    ck, cv = synth.make_decode_cache(B, H, T0, d, dtype="bf16", seed=31)
+    steps = synth.make_decode_steps(S, B, H, d, dtype="bf16", seed=31)
+    gates = fox_gates(S, B, H, seed=31) if fox else None
+    fc0 = initial_slot_bias(B, H, T0, cap, seed=31) if fox else None
+    caches = []
+    for deferred in (False, True):
+        kc = torch.zeros((B, H, cap, d), device="cuda", dtype=torch.bfloat16)
+        vc = torch.zeros_like(kc)
+        kc[:, :, :T0] = dev(ck, "bf16")
+        vc[:, :, :T0] = dev(cv, "bf16")
+        fc = dev_f32(fc0) if fox else None
+        if deferred:
+            go, gl, _ = run_deferred(kc, vc, fc, T0, steps, 1, gates)
+        else:
+            outs, lses = [], []
+            for s in range(S):
+                o, l = native.path_decode_step(kc, vc, T0 + s, dev(steps.q[s], "bf16"), dev(steps.k[s], "bf16"),
+                                               dev(steps.v[s], "bf16"), dev(steps.w[s], "bf16"),
+                                               dev_f32(steps.beta[s]), dev_f32(gates[s]) if fox else None,
+                                               fcache=fc, scale=steps.scale)
+                outs.append(host(o))
+                lses.append(host(l))
+            go, gl = np.stack(outs), np.stack(lses)
+        torch.cuda.synchronize()
+        caches.append((go, gl, kc.view(torch.int16).cpu().numpy(), host(fc) if fox else None))
+    a, b = caches
+    assert np.array_equal(a[2], b[2]), "key caches differ"
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "outputs differ"
+    if fox:
+        assert np.array_equal(a[3], b[3])
+
+
+def test_deferred_forced_update():
+    """An update forced mid-period (period = t - t_cur + 1) leaves the cache current, like the oracle's."""
+    B, H, T0, S, d, period = 1, 2, 300, 9, 64, 8
+    cap = T0 + S
+    ck, cv = synth.make_decode_cache(B, H, T0, d, dtype="bf16", seed=41)
+    steps = synth.make_decode_steps(S, B, H, d, dtype="bf16", seed=41)
+    kc = torch.zeros((B, H, cap, d), device="cuda", dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :T0] = dev(ck, "bf16")
+    vc[:, :, :T0] = dev(cv, "bf16")
+    go, gl, t_cur = run_deferred(kc, vc, None, T0, steps, period, force_at=4)
+    assert t_cur == T0 + 5
+    BH = B * H
+    okc, ovc = np.zeros((BH, cap, d)), np.zeros((BH, cap, d))
+    okc[:, :T0] = ck.reshape(BH, T0, d)
+    ovc[:, :T0] = cv.reshape(BH, T0, d)
+    sh = lambda x: x.reshape(S, BH, -1) if x.ndim == 4 else x.reshape(S, BH)
+    ro, rl = oracle.decode(okc, ovc, T0, sh(steps.q)[:5], sh(steps.k)[:5], sh(steps.v)[:5], sh(steps.w)[:5],
+                           sh(steps.beta)[:5], steps.scale)
+    assert_parity(go[:5], ro.reshape(5, B, H, d), "bf16", "out")
+    # slots 0 .. T0 + 4 became current at the forced update (step 4); nothing updated them since
+    check_cache(host(kc)[:, :, :T0 + 5], okc.reshape(B, H, cap, d)[:, :, :T0 + 5], "bf16", 5)
