@@ -352,40 +352,59 @@ __global__ __launch_bounds__(kDecThreads) void decode_deferred_kernel(
       }
     }
     float z[kDecUnroll];
-    float vf[kDecUnroll][VN];
+    float vf[kDecUnroll][VN], kf[kDecUnroll][VN];
+    int i0[kDecUnroll];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      float kf[VN];
-      unpack16<T>(kr[u], kf);
+      unpack16<T>(kr[u], kf[u]);
       unpack16<T>(vr[u], vf[u]);
       const int64_t j = jj[u];
+      i0[u] = (j >= t_cur && j < t) ? (int)(j - t_cur) + 1 : 0;  // first pending transition of a raw key
+    }
+    if (flush) {  // every slot below t takes its pending transitions, the four keys interleaved
+      for (int i = 0; i <= np; ++i) {
+        float w[VN], pd[kDecUnroll];
+#pragma unroll
+        for (int x = 0; x < VN; ++x) w[x] = Wl[i][sub * VN + x];
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+          pd[u] = 0.f;
+#pragma unroll
+          for (int x = 0; x < VN; ++x) pd[u] += w[x] * kf[u][x];
+        }
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) pd[u] = group_sum<LPK>(pd[u]);
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+          if (jj[u] < t && i >= i0[u]) {
+            const float c = Bl[i] * pd[u];
+#pragma unroll
+            for (int x = 0; x < VN; ++x) kf[u][x] -= c * w[x];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int64_t j = jj[u];
       const bool live = j < j1;
-      const bool raw = j >= t_cur && j < t;        // key added since the last update
-      const int i0 = raw ? (int)(j - t_cur) + 1 : 0;  // its first pending transition
+      const bool raw = j >= t_cur && j < t;  // key appended since the last update
       float bias = 0.f;
-      if constexpr (FOX) bias = j < t_cur ? fb_old[u] + g0 : (raw ? Gl[i0] : 0.f);
+      if constexpr (FOX) bias = j < t_cur ? fb_old[u] + g0 : (raw ? Gl[i0[u]] : 0.f);
       float qj[VN];
 #pragma unroll
       for (int x = 0; x < VN; ++x) qj[x] = qv[x];
       if (live && j < t) {
         if (flush) {
-          for (int i = i0; i <= np; ++i) {
-            float pd = 0.f;
-#pragma unroll
-            for (int x = 0; x < VN; ++x) pd += Wl[i][sub * VN + x] * kf[x];
-            const float c = Bl[i] * group_sum<LPK>(pd);
-#pragma unroll
-            for (int x = 0; x < VN; ++x) kf[x] -= c * Wl[i][sub * VN + x];
-          }
-          const uint4 nk = pack16<T>(kf);
+          const uint4 nk = pack16<T>(kf[u]);
           *((uint4*)(kb + j * D) + sub) = nk;
-          unpack16<T>(nk, kf);  // attend with exactly the stored key
+          unpack16<T>(nk, kf[u]);  // attend with exactly the stored key
           if constexpr (FOX) {
             if (sub == 0) fb[j] = bias;
           }
         } else if (raw) {
 #pragma unroll
-          for (int x = 0; x < VN; ++x) qj[x] = Ql[i0][sub * VN + x];
+          for (int x = 0; x < VN; ++x) qj[x] = Ql[i0[u]][sub * VN + x];
         }
       } else if (live) {  // slot t: the new token, stored untransformed
         *((uint4*)(kb + j * D) + sub) = kr[u];
@@ -398,7 +417,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_deferred_kernel(
       }
       float sd = 0.f;
 #pragma unroll
-      for (int x = 0; x < VN; ++x) sd += qj[x] * kf[x];
+      for (int x = 0; x < VN; ++x) sd += qj[x] * kf[u][x];
       sd = group_sum<LPK>(sd);
       z[u] = live ? sd * scale_log2 + (FOX ? bias * kLog2e : 0.f) : -INFINITY;
     }
