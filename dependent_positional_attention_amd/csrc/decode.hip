@@ -80,7 +80,10 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 constexpr int kDecThreads = 256;
-constexpr int kDecUnroll = 4;
+#ifndef PATHATTN_DEC_UNROLL
+#define PATHATTN_DEC_UNROLL 4
+#endif
+constexpr int kDecUnroll = PATHATTN_DEC_UNROLL;
 
 // Merge the key groups' online-softmax states (m, l, o) of one block through LDS and write the
 // block's partial (m, l, o[D]) for the combine kernel.

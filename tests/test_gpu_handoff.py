@@ -208,3 +208,29 @@ def test_fox_prefill_then_decode(dtype, chunk, transport, L, S):
     ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf, scale=x.scale, rows=list(range(L, L + S)))
     assert_parity(np.stack(outs, axis=2), ro, dtype, "fox decode out")
     assert_parity(np.stack(lses, axis=2), rl, dtype, "fox decode lse")
+
+
+@pytest.mark.parametrize("fox,period", [(False, 4), (True, 3)])
+def test_prefill_then_deferred_decode(fox, period):
+    """Prompt through prefill + hand-off, then decode with deferred key updates: rows L..L+S-1 of the oracle."""
+    B, H, d, L, S = 2, 2, 64, 640, 9
+    print(f"[case] prefill+deferred decode fox={fox} period={period} L={L} S={S}", flush=True)
+    x = synth.make_fwd_inputs(B, H, L + S, d, recipe="fox" if fox else "lm", dtype="bf16", seed=13)
+    kc, vc, t, _ = prefill_cache(x, 64, "bf16", L + S, L=L, fox=fox)
+    fc = t["fcache"]
+    state = torch.zeros(native.path_decode_deferred_state_bytes(B, H, d) // 4, device="cuda", dtype=torch.float32)
+    outs, lses, t_cur = [], [], L
+    for s in range(S):
+        tok = lambda a: dev(np.ascontiguousarray(a[:, :, L + s]), "bf16")
+        f = dev_f32(np.ascontiguousarray(x.logf[:, :, L + s])) if fox else None
+        o, l, t_cur = native.path_decode_step_deferred(
+            kc, vc, L + s, t_cur, tok(x.q), tok(x.k), tok(x.v), tok(x.w),
+            dev_f32(np.ascontiguousarray(x.beta[:, :, L + s])), f, period=period, state=state, fcache=fc,
+            scale=x.scale)
+        outs.append(host(o))
+        lses.append(host(l))
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(x.q, x.k, x.v, x.w, x.beta, logf=x.logf if fox else None, scale=x.scale,
+                        rows=list(range(L, L + S)))
+    assert_parity(np.stack(outs, axis=2), ro, "bf16", "deferred decode out")
+    assert_parity(np.stack(lses, axis=2), rl, "bf16", "deferred decode lse")
