@@ -71,6 +71,19 @@ __device__ __forceinline__ uint4 pack16<float>(const float* f) {
   return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
 }
 
+// Non-temporal cache accesses for the in-place step, which reads and rewrites every cached key once:
+// with both its loads and its stores marked streaming it runs 7% faster at a 64K-token cache (either
+// alone changes nothing), while the read-only steps of the deferred kernel are faster with plain loads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void stream_store(uint4* p, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
 // Sum over the LPK lanes of a key group (groups are aligned runs of LPK lanes).
 template <int LPK>
 __device__ __forceinline__ float group_sum(float x) {
@@ -200,12 +213,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
       fb_old[u] = 0.f;
       if (jj[u] < j1) {
         if (jj[u] < t) {
-          kr[u] = *((const uint4*)(kb + jj[u] * D) + sub);
+          kr[u] = stream_load((const uint4*)(kb + jj[u] * D) + sub);
           if constexpr (FOX) fb_old[u] = fb[jj[u]];
         } else {  // jj == t: the new token
           kr[u] = *((const uint4*)(k_t + bh * D) + sub);
         }
-        vr[u] = (jj[u] < t) ? *((const uint4*)(vb + jj[u] * D) + sub) : *((const uint4*)(v_t + bh * D) + sub);
+        vr[u] = (jj[u] < t) ? stream_load((const uint4*)(vb + jj[u] * D) + sub) : *((const uint4*)(v_t + bh * D) + sub);
       }
     }
     float z[kDecUnroll];
@@ -229,7 +242,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_update_attend_kernel(
 #pragma unroll
         for (int x = 0; x < VN; ++x) kf[x] -= coef * wv[x];
         const uint4 nk = pack16<T>(kf);
-        *((uint4*)(kb + jj[u] * D) + sub) = nk;
+        stream_store((uint4*)(kb + jj[u] * D) + sub, nk);
         unpack16<T>(nk, kf);  // attend with exactly the stored key
       } else if (live) {  // slot t: the new token, stored untransformed
         *((uint4*)(kb + jj[u] * D) + sub) = kr[u];
