@@ -164,7 +164,10 @@ __device__ __forceinline__ void acc_to_op(const f32x4 (&acc)[4], bf16x8 (&hi)[2]
 // permuted-column form, so the 64x64 intermediates X, Y, T^{-1}W, U and R never touch LDS:
 // wave w owns query block a = 16w.. (X, U, KQ), key block b = 16w.. (Y, R, S) and y block 16w.. of
 // T^{-1}W (for P).  LDS holds the DMA-loaded W, Q, K tiles, A (strict upper) with Z = A^{-1}
-// stored transposed in its lower triangle, T^{-T} (hi, lo) and U^T (hi, lo, for S).
+// stored transposed in its lower triangle, T^{-T} (hi, lo) and U^T (hi, lo, for S); T^{-T} reuses the
+// space of Q and K (dead once the products of phase B are done; the final phase reads its q and k
+// rows from global memory), U^T that of A (written once T^{-T} has been formed), so that three
+// blocks share a CU.
 //   A      = I + diag(beta) strict_upper(W W^T)        (fp32)
 //   Z      = A^{-1}: 16x16 diagonal blocks by back substitution, then Z_IJ = -Z_II sum_K A_IK Z_KJ
 //   T^{-1} = Z diag(beta)                              (hi + lo bf16)
@@ -173,12 +176,13 @@ __device__ __forceinline__ void acc_to_op(const f32x4 (&acc)[4], bf16x8 (&hi)[2]
 // hi/lo products drop lo*lo.  Padded tokens of a ragged last chunk are clamped copies of the last
 // row with beta = 0, which makes every T^{-1} entry that would touch them exactly zero.
 constexpr int kLDF = 68;  // fp32 row stride of A/Z
-constexpr size_t kPrepLds = 5 * kTile * 2 + 2 * kTile * 2 + kC * kLDF * 4 + 2 * 64 * 4;
-static_assert(kPrepLds <= 80 * 1024, "prep LDS plan must allow two blocks per CU");
+constexpr size_t kPrepLds = 3 * kTile * 2 + kC * kLDF * 4 + 2 * 64 * 4;
+static_assert(kC * kLDF * 4 >= 2 * kTile * 2, "U^T hi/lo must fit in the space of A");
+static_assert(kPrepLds <= 160 * 1024 / 3, "prep LDS plan must allow three blocks per CU");
 
 __device__ __forceinline__ int perm_col(int c) { return perm_pos(c); }
 
-__global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
+__global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
     const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, float qs,
     __bf16* __restrict__ qt, __bf16* __restrict__ qt_lo, __bf16* __restrict__ kt, __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo,
@@ -187,11 +191,11 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
   __bf16* Wt = reinterpret_cast<__bf16*>(smem);  // W [s][x]            (swizzled, natural columns)
   __bf16* Qt = Wt + kTile;                       // Q [a][x]
   __bf16* Kt = Qt + kTile;                       // K [b][x]
-  __bf16* TiH = Kt + kTile;                      // T^{-T} [t][s] hi / lo (swizzled, permuted columns)
-  __bf16* TiL = TiH + kTile;
-  __bf16* UH = TiL + kTile;                      // U^T [a][t] hi / lo   (swizzled, permuted columns)
+  __bf16* TiH = Qt;                              // later: T^{-T} [t][s] hi / lo (swizzled, permuted columns)
+  __bf16* TiL = Kt;
+  float* Af = reinterpret_cast<float*>(Kt + kTile);  // A strict upper, Z^T lower incl. diagonal
+  __bf16* UH = reinterpret_cast<__bf16*>(Af);        // later: U^T [a][t] hi / lo (swizzled, permuted columns)
   __bf16* UL = UH + kTile;
-  float* Af = reinterpret_cast<float*>(UL + kTile);  // A strict upper, Z^T lower incl. diagonal
   float* Bs = Af + kC * kLDF;                        // beta
   float* Fs = Bs + 64;                               // unused pad (keeps the plan aligned)
   (void)Fs;
@@ -261,12 +265,6 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
       ua[tt] = u4;
       ra[tt] = r4;
       kq[tt] = k4;
-      // U^T[a][t] (hi/lo) for the S product of other waves: 4 consecutive t in permuted order
-      bf16x4 h4, l4;
-      split4(u4[0], u4[1], u4[2], u4[3], h4, l4);
-      const int pc = perm_pos(16 * tt + 4 * g);
-      *reinterpret_cast<bf16x4*>(UH + swz(col_wave, pc >> 3) + (pc & 7)) = h4;
-      *reinterpret_cast<bf16x4*>(UL + swz(col_wave, pc >> 3) + (pc & 7)) = l4;
     }
     acc_to_op(ua, ubh, ubl);
     acc_to_op(ra, rbh, rbl);
@@ -337,6 +335,17 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
     *reinterpret_cast<bf16x8*>(TiL + swz(t, ch)) = l8;
   }
   __syncthreads();
+  // A is no longer needed: U^T[a][t] (hi/lo) for the S product of the other waves, from this wave's U
+  // operand (4 consecutive t of column a = 16 wave + r per accumulator tile, in permuted order)
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int ks = tt >> 1, h = tt & 1;
+    const bf16x4 h4 = {ubh[ks][4 * h], ubh[ks][4 * h + 1], ubh[ks][4 * h + 2], ubh[ks][4 * h + 3]};
+    const bf16x4 l4 = {ubl[ks][4 * h], ubl[ks][4 * h + 1], ubl[ks][4 * h + 2], ubl[ks][4 * h + 3]};
+    const int pc = perm_pos(16 * tt + 4 * g), col_wave = 16 * wave + r;
+    *reinterpret_cast<bf16x4*>(UH + swz(col_wave, pc >> 3) + (pc & 7)) = h4;
+    *reinterpret_cast<bf16x4*>(UL + swz(col_wave, pc >> 3) + (pc & 7)) = l4;
+  }
 
   // ---------------------------------------------------------------- D: register-resident products
   const int a = 16 * wave + r;  // query / key row of this lane's output column
@@ -376,6 +385,9 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
     acc_to_op(ya, ybh, ybl);  // Y as an operand over k = t, row/column b
     acc_to_op(za, zbh, zbl);  // (T^{-1}W)^T as an operand over k = s, row y
   }
+  __syncthreads();  // every wave's U^T is in place
+  // this lane's q and k rows (clamped in a ragged last chunk, as the tile copies were)
+  const size_t grow = ((size_t)bh * L + row0 + (a < valid ? a : valid - 1)) * kD;
 #pragma unroll
   for (int xt = 0; xt < 4; ++xt) {
     const int x0 = 16 * xt + 4 * g;  // this lane's four consecutive output columns
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
     }
     // qtilde[a][x] = (q_a[x] - D[x][a]) * qs  (lane: row a, columns x0..x0+3)
     {
-      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qt + swz(a, x0 >> 3) + (x0 & 7));
+      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(q + grow + x0);
       bf16x4 h4, l4;
       split4(((float)q4[0] - dq[0]) * qs, ((float)q4[1] - dq[1]) * qs, ((float)q4[2] - dq[2]) * qs,
              ((float)q4[3] - dq[3]) * qs, h4, l4);
@@ -407,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void mfma_prep_kernel(
     }
     // ktilde[b][x] = k_b[x] - D[x][b]
     {
-      const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Kt + swz(a, x0 >> 3) + (x0 & 7));
+      const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(k + grow + x0);
       *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) =
           pack4((float)k4[0] - dk[0], (float)k4[1] - dk[1], (float)k4[2] - dk[2], (float)k4[3] - dk[3]);
     }
