@@ -165,9 +165,9 @@ __device__ __forceinline__ void acc_to_op(const f32x4 (&acc)[4], bf16x8 (&hi)[2]
 // wave w owns query block a = 16w.. (X, U, KQ), key block b = 16w.. (Y, R, S) and y block 16w.. of
 // T^{-1}W (for P).  LDS holds the DMA-loaded W, Q, K tiles, A (strict upper) with Z = A^{-1}
 // stored transposed in its lower triangle, T^{-T} (hi, lo) and U^T (hi, lo, for S); T^{-T} reuses the
-// space of Q and K (dead once the products of phase B are done; the final phase reads its q and k
-// rows from global memory), U^T that of A (written once T^{-T} has been formed), so that three
-// blocks share a CU.
+// space of Q and K (dead once the products of phase B are done; the few q and k values the final
+// phase needs are kept in registers), U^T that of A (written once T^{-T} has been formed), so that
+// three blocks share a CU.
 //   A      = I + diag(beta) strict_upper(W W^T)        (fp32)
 //   Z      = A^{-1}: 16x16 diagonal blocks by back substitution, then Z_IJ = -Z_II sum_K A_IK Z_KJ
 //   T^{-1} = Z diag(beta)                              (hi + lo bf16)
@@ -268,6 +268,15 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     }
     acc_to_op(ua, ubh, ubl);
     acc_to_op(ra, rbh, rbl);
+  }
+  // the q and k values the final phase needs (row 16 wave + r, columns 16 xt + 4g ..), taken from the
+  // tiles before their space is reused
+  bf16x4 q4s[4], k4s[4];
+#pragma unroll
+  for (int xt = 0; xt < 4; ++xt) {
+    const int row = 16 * wave + r, x0 = 16 * xt + 4 * g;
+    q4s[xt] = *reinterpret_cast<const bf16x4*>(Qt + swz(row, x0 >> 3) + (x0 & 7));
+    k4s[xt] = *reinterpret_cast<const bf16x4*>(Kt + swz(row, x0 >> 3) + (x0 & 7));
   }
   __builtin_amdgcn_wave_barrier();
   // Z_II (block I = wave) by back substitution, lane l < 16 owning column l; stored transposed.
@@ -386,8 +395,6 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     acc_to_op(za, zbh, zbl);  // (T^{-1}W)^T as an operand over k = s, row y
   }
   __syncthreads();  // every wave's U^T is in place
-  // this lane's q and k rows (clamped in a ragged last chunk, as the tile copies were)
-  const size_t grow = ((size_t)bh * L + row0 + (a < valid ? a : valid - 1)) * kD;
 #pragma unroll
   for (int xt = 0; xt < 4; ++xt) {
     const int x0 = 16 * xt + 4 * g;  // this lane's four consecutive output columns
@@ -410,7 +417,7 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     }
     // qtilde[a][x] = (q_a[x] - D[x][a]) * qs  (lane: row a, columns x0..x0+3)
     {
-      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(q + grow + x0);
+      const bf16x4 q4 = q4s[xt];
       bf16x4 h4, l4;
       split4(((float)q4[0] - dq[0]) * qs, ((float)q4[1] - dq[1]) * qs, ((float)q4[2] - dq[2]) * qs,
              ((float)q4[3] - dq[3]) * qs, h4, l4);
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     }
     // ktilde[b][x] = k_b[x] - D[x][b]
     {
-      const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(k + grow + x0);
+      const bf16x4 k4 = k4s[xt];
       *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) =
           pack4((float)k4[0] - dk[0], (float)k4[1] - dk[1], (float)k4[2] - dk[2], (float)k4[3] - dk[3]);
     }
