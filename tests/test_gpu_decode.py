@@ -333,3 +333,18 @@ def test_deferred_forced_update():
     assert_parity(go[:5], ro.reshape(5, B, H, d), "bf16", "out")
     # slots 0 .. T0 + 4 became current at the forced update (step 4); nothing updated them since
     check_cache(host(kc)[:, :, :T0 + 5], okc.reshape(B, H, cap, d)[:, :, :T0 + 5], "bf16", 5)
+
+
+@pytest.mark.parametrize("dtype,period", [("bf16", 4), ("f32", 3)])
+def test_deferred_decode_from_empty_equals_prefill(dtype, period):
+    """Deferred decoding of S tokens from an empty cache reproduces prefill rows 0..S-1 (oracle prefill)."""
+    B, H, S, d = 1, 3, 23, 64
+    steps = synth.make_decode_steps(S, B, H, d, dtype=dtype, seed=7)
+    kc = torch.zeros((B, H, S, d), device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    vc = torch.zeros_like(kc)
+    go, gl, t_cur = run_deferred(kc, vc, None, 0, steps, period)
+    assert t_cur == S - S % period
+    tr = lambda x: np.ascontiguousarray(np.moveaxis(x, 0, 2))  # [S,B,H,...] -> [B,H,S,...]
+    ro, rl = oracle.fwd(tr(steps.q), tr(steps.k), tr(steps.v), tr(steps.w), tr(steps.beta), scale=steps.scale)
+    assert_parity(tr(go), ro, dtype, "out")
+    assert_parity(tr(gl), rl, dtype, "lse")
