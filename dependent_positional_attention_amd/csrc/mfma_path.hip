@@ -890,7 +890,7 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
     cur = (cur + 1 == NB) ? 0 : cur + 1;
   };
   auto run_step = [&](auto next_tag, int64_t n) PA_INLINE {
-    if constexpr (FOX) off += ftot[bh * M + n];
+    if constexpr (FOX) off += lfl[cur][63];  // the chunk's total: its last inclusive prefix, already staged
     step(next_tag, lds[cur][0], lds[cur][1], lds[cur][2], lds[cur][NM - 1], lfl[cur]);
   };
 
