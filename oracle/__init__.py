@@ -53,9 +53,12 @@ def lib():
         L.path_oracle_householder_product.argtypes = [_D, _D, _I64, _I64, _D]
         L.path_oracle_chunk_terms.argtypes = [_D, _D, _D, _D, _I64, _I64, _D, _D, _D]
         L.path_oracle_cache_keys.argtypes = [_D, _D, _D, _I64, _I64, _I64, _I64, _D]
+        L.path_oracle_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _I64, _I64, _I64, ctypes.c_double,
+                                      _D, _D, _D, _D, _D, _D, ctypes.c_int]
         for f in ("path_oracle_fwd", "path_oracle_row_logits", "path_oracle_transport",
                   "path_oracle_decode", "path_oracle_ut_tinv", "path_oracle_householder_product",
-                  "path_oracle_chunk_terms", "path_oracle_cache_keys", "path_oracle_cache_bias"):
+                  "path_oracle_chunk_terms", "path_oracle_cache_keys", "path_oracle_cache_bias",
+                  "path_oracle_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -196,3 +199,22 @@ def cache_bias(logf):
     out = np.zeros(logf.shape[0])
     _check(lib().path_oracle_cache_bias(_p(logf), logf.shape[0], _p(out)), "path_oracle_cache_bias")
     return out
+
+
+def bwd(q, k, v, w, beta, dout, logf=None, scale: float = 1.0, nthreads: int = 0):
+    """Gradients of the forward for the loss sum(dout * out).  Shapes as in fwd, dout like q.
+
+    Returns (dq, dk, dv, dw, dbeta, dlogf) in float64; dlogf is None without logf.
+    """
+    q, k, v, w, beta, dout = map(_f64, (q, k, v, w, beta, dout))
+    logf = None if logf is None else _f64(logf)
+    lead = q.shape[:-2]
+    L, d = q.shape[-2], q.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    dq, dk, dv, dw = (np.zeros(lead + (L, d)) for _ in range(4))
+    dbeta = np.zeros(lead + (L,))
+    dlogf = None if logf is None else np.zeros(lead + (L,))
+    _check(lib().path_oracle_bwd(_p(q), _p(k), _p(v), _p(w), _p(beta), _p(logf), _p(dout), BH, L, d,
+                                 float(scale), _p(dq), _p(dk), _p(dv), _p(dw), _p(dbeta), _p(dlogf),
+                                 int(nthreads or host_threads())), "path_oracle_bwd")
+    return dq, dk, dv, dw, dbeta, dlogf

@@ -162,6 +162,183 @@ int path_oracle_fwd(const double* q, const double* k, const double* v, const dou
   return rc;
 }
 
+/* ------------------------------------------------------------------ backward */
+/*
+ * Gradients of the forward above for an upstream gradient dO of the outputs
+ * (loss = sum_i dO_i . o_i).  The pages print no backward pass (the lecture
+ * notes only warn, under "limitations", that it is costlier than RoPE's); this is
+ * the chain rule applied to the definition and nothing else:
+ *
+ *   p_ij = softmax_j(z_ij)                 dv_j  = sum_i p_ij dO_i
+ *   D_i  = sum_j p_ij (dO_i . v_j)         dz_ij = p_ij (dO_i . v_j - D_i)
+ *
+ *   a_{j,s} = H_{s-1} ... H_{j+1} k_j   (key j carried up to just below s; a_{j,j+1} = k_j)
+ *   g_{s,i} = H_{s+1} ... H_i q_i       (query i carried down to just above s; g_{i,i} = q_i)
+ *
+ * Because every H is symmetric, z_ij = scale a_{j,s}^T H_s g_{s,i} + bias_ij for
+ * any s in (j, i], and z_ij = scale k_j . g_{j,i} + bias_ij.  Hence
+ *
+ *   dq_i  = scale sum_{j<=i} dz_ij a_{j,i+1}
+ *   dk_j  = scale sum_{i>=j} dz_ij g_{j,i}
+ *   dH_s  = scale sum_{j<s<=i} dz_ij a_{j,s} g_{s,i}^T      (d x d; only dH_s w_s and
+ *                                                           dH_s^T w_s are formed)
+ *   H_s = I - beta_s w_s w_s^T:  dbeta_s = -w_s^T dH_s w_s,
+ *                                dw_s    = -beta_s (dH_s + dH_s^T) w_s
+ *   PaTH-FoX, bias_ij = sum_{s=j+1..i} f_s:  df_s = sum_{j<s<=i} dz_ij.
+ */
+typedef struct {
+  const double *q, *k, *v, *w, *beta, *logf, *dout;
+  int64_t BH, L, d;
+  double scale;
+  double *dq, *dk, *dv, *dw, *dbeta, *dlogf;
+  int64_t next; /* shared work counter, one item = one (batch, head) */
+} bwd_job;
+
+static void bwd_one(const bwd_job* J, int64_t bh, double* P, double* dZ, double* G, double* A, double* r,
+                    double* gw, double* aw, double* cu, double* cv) {
+  const int64_t L = J->L, d = J->d, base = bh * L;
+  const double *Q = J->q + base * d, *K = J->k + base * d, *V = J->v + base * d, *W = J->w + base * d;
+  const double *beta = J->beta + base, *logf = J->logf ? J->logf + base : NULL, *dO = J->dout + base * d;
+  double *dq = J->dq + base * d, *dk = J->dk + base * d, *dv = J->dv + base * d, *dw = J->dw + base * d;
+  double *dbeta = J->dbeta + base, *dlogf = J->dlogf ? J->dlogf + base : NULL;
+  const double scale = J->scale;
+
+  /* probabilities: logits of each row, then the exact softmax */
+  for (int64_t i = 0; i < L; ++i) {
+    double* z = P + i * L;
+    row_logits(Q + i * d, K, W, beta, logf, i, d, scale, r, z);
+    double m = -INFINITY, l = 0.0;
+    for (int64_t j = 0; j <= i; ++j)
+      if (z[j] > m) m = z[j];
+    for (int64_t j = 0; j <= i; ++j) l += exp(z[j] - m);
+    for (int64_t j = 0; j <= i; ++j) z[j] = exp(z[j] - m) / l;
+  }
+  /* dv, D, dz */
+  memset(dv, 0, (size_t)(L * d) * sizeof(double));
+  for (int64_t i = 0; i < L; ++i) {
+    const double* p = P + i * L;
+    double D = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+      const double dp = dot(dO + i * d, V + j * d, d);
+      dZ[i * L + j] = dp;
+      D += p[j] * dp;
+      for (int64_t t = 0; t < d; ++t) dv[j * d + t] += p[j] * dO[i * d + t];
+    }
+    for (int64_t j = 0; j <= i; ++j) dZ[i * L + j] = p[j] * (dZ[i * L + j] - D);
+  }
+  /* carried queries g_{s,i} (G[(i L + s) d]) and keys a_{j,s} (A[(j (L+1) + s) d]) */
+  for (int64_t i = 0; i < L; ++i) {
+    memcpy(r, Q + i * d, (size_t)d * sizeof(double));
+    for (int64_t s = i; s >= 0; --s) {
+      memcpy(G + (i * L + s) * d, r, (size_t)d * sizeof(double));
+      apply_h(r, W + s * d, beta[s], d);
+    }
+  }
+  for (int64_t j = 0; j < L; ++j) {
+    memcpy(r, K + j * d, (size_t)d * sizeof(double));
+    for (int64_t s = j + 1; s <= L; ++s) {
+      memcpy(A + (j * (L + 1) + s) * d, r, (size_t)d * sizeof(double));
+      if (s < L) apply_h(r, W + s * d, beta[s], d);
+    }
+  }
+  /* dq, dk */
+  for (int64_t i = 0; i < L; ++i) {
+    for (int64_t t = 0; t < d; ++t) dq[i * d + t] = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+      const double c = scale * dZ[i * L + j];
+      const double* a = A + (j * (L + 1) + i + 1) * d;
+      for (int64_t t = 0; t < d; ++t) dq[i * d + t] += c * a[t];
+    }
+  }
+  for (int64_t j = 0; j < L; ++j) {
+    for (int64_t t = 0; t < d; ++t) dk[j * d + t] = 0.0;
+    for (int64_t i = j; i < L; ++i) {
+      const double c = scale * dZ[i * L + j];
+      const double* g = G + (i * L + j) * d;
+      for (int64_t t = 0; t < d; ++t) dk[j * d + t] += c * g[t];
+    }
+  }
+  /* dH_s w_s and dH_s^T w_s over the pairs j < s <= i, then dbeta, dw, df */
+  for (int64_t s = 0; s < L; ++s) {
+    const double* ws = W + s * d;
+    for (int64_t i = s; i < L; ++i) gw[i] = dot(G + (i * L + s) * d, ws, d);
+    for (int64_t j = 0; j < s; ++j) aw[j] = dot(A + (j * (L + 1) + s) * d, ws, d);
+    for (int64_t t = 0; t < d; ++t) cu[t] = cv[t] = 0.0;
+    double df = 0.0;
+    for (int64_t j = 0; j < s; ++j) {
+      double c = 0.0; /* sum_i dz_ij (g_{s,i} . w_s) */
+      for (int64_t i = s; i < L; ++i) c += dZ[i * L + j] * gw[i];
+      const double* a = A + (j * (L + 1) + s) * d;
+      for (int64_t t = 0; t < d; ++t) cu[t] += scale * c * a[t];
+    }
+    for (int64_t i = s; i < L; ++i) {
+      double c = 0.0; /* sum_j dz_ij (a_{j,s} . w_s) */
+      for (int64_t j = 0; j < s; ++j) {
+        c += dZ[i * L + j] * aw[j];
+        df += dZ[i * L + j];
+      }
+      const double* g = G + (i * L + s) * d;
+      for (int64_t t = 0; t < d; ++t) cv[t] += scale * c * g[t];
+    }
+    dbeta[s] = -dot(ws, cu, d);
+    for (int64_t t = 0; t < d; ++t) dw[s * d + t] = -beta[s] * (cu[t] + cv[t]);
+    if (dlogf) dlogf[s] = df;
+  }
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job* J = (bwd_job*)arg;
+  const int64_t L = J->L, d = J->d;
+  double* P = (double*)malloc((size_t)(L * L) * sizeof(double));
+  double* dZ = (double*)malloc((size_t)(L * L) * sizeof(double));
+  double* G = (double*)malloc((size_t)(L * L * d) * sizeof(double));
+  double* A = (double*)malloc((size_t)(L * (L + 1) * d) * sizeof(double));
+  double* r = (double*)malloc((size_t)(3 * d + 2 * L) * sizeof(double)); /* r, gw, aw, cu, cv */
+  void* ret = NULL;
+  if (!P || !dZ || !G || !A || !r) {
+    ret = (void*)1;
+  } else {
+    for (;;) {
+      int64_t bh = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+      if (bh >= J->BH) break;
+      bwd_one(J, bh, P, dZ, G, A, r, r + d, r + d + L, r + d + 2 * L, r + 2 * d + 2 * L);
+    }
+  }
+  free(P);
+  free(dZ);
+  free(G);
+  free(A);
+  free(r);
+  return ret;
+}
+
+/*
+ * Backward of path_oracle_fwd over all rows.  Inputs as there plus dout [BH, L, d].
+ * Outputs dq, dk, dv, dw [BH, L, d]; dbeta [BH, L]; dlogf [BH, L] (only when logf != NULL).
+ * Memory: about (2 L^2 + 2 L^2 d) doubles per worker thread.
+ */
+int path_oracle_bwd(const double* q, const double* k, const double* v, const double* w, const double* beta,
+                    const double* logf, const double* dout, int64_t BH, int64_t L, int64_t d, double scale,
+                    double* dq, double* dk, double* dv, double* dw, double* dbeta, double* dlogf, int nthreads) {
+  if (BH < 0 || L < 0 || d <= 0) return ORACLE_EINVAL;
+  if ((logf == NULL) != (dlogf == NULL)) return ORACLE_EINVAL;
+  if (BH == 0 || L == 0) return ORACLE_OK;
+  bwd_job J = {q, k, v, w, beta, logf, dout, BH, L, d, scale, dq, dk, dv, dw, dbeta, dlogf, 0};
+  int nt = resolve_threads(nthreads);
+  if ((int64_t)nt > BH) nt = (int)BH;
+  pthread_t* th = (pthread_t*)malloc((size_t)nt * sizeof(pthread_t));
+  if (!th) return ORACLE_ENOMEM;
+  int rc = ORACLE_OK;
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, bwd_worker, &J);
+  for (int t = 0; t < nt; ++t) {
+    void* ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret) rc = ORACLE_ENOMEM;
+  }
+  free(th);
+  return rc;
+}
+
 /* Logits z[0..i] of one row of one (batch, head) slice; K, W: [L, d], beta, logf: [L]. */
 int path_oracle_row_logits(const double* q_i, const double* K, const double* W, const double* beta,
                            const double* logf, int64_t i, int64_t d, double scale, double* z) {

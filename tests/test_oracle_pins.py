@@ -17,6 +17,9 @@ P9  decode      in-place key updates (summary, section 3 "inference") == prefill
 P10 mutations   plausible mistakes planted in a copy of the oracle make the pins fail
 P11 cache       key cache after a prompt (summary, section 3 "inference"): explicit products,
                 last-row logits, the decode recurrence, norms under beta = 2
+P12 backward    gradients of every input (q, k, v, w, beta, f) against central finite differences of
+                the pinned forward, against torch autograd through explicit d x d products, and for
+                beta = 0 against the gradient of plain causal attention; planted mistakes are caught
 """
 import ctypes
 import json
@@ -609,3 +612,135 @@ def test_p9_planted_fox_decode_mistakes_are_caught(oracle_lib, name, monkeypatch
         monkeypatch.setattr(oracle_lib, "_lib", mutated)
         with pytest.raises(AssertionError):
             test_p9_fox_bias_beta_zero_closed_form(oracle_lib)
+
+
+# ----------------------------------------------------------------------------- P12
+
+def _fd_grads(oracle_lib, q, k, v, w, beta, logf, dout, scale, h=1e-6):
+    """Central differences of sum(dout * out) for every input coordinate (tiny problems only)."""
+    args = [q, k, v, w, beta] + ([logf] if logf is not None else [])
+
+    def loss(a):
+        out, _ = oracle_lib.fwd(*a[:5], logf=a[5] if len(a) > 5 else None, scale=scale, nthreads=1)
+        return float((out * dout).sum())
+
+    grads = []
+    for ai in range(len(args)):
+        g = np.zeros_like(args[ai])
+        for idx in np.ndindex(args[ai].shape):
+            a = [x.copy() for x in args]
+            a[ai][idx] += h
+            lp = loss(a)
+            a[ai][idx] -= 2 * h
+            g[idx] = (lp - loss(a)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("L,d,beta_mode,fox", [(1, 3, "sigmoid", True), (7, 3, "sigmoid", True),
+                                               (12, 5, "sigmoid", False), (9, 4, "two", True),
+                                               (8, 3, "zero", True)])
+def test_p12_backward_matches_finite_differences(oracle_lib, L, d, beta_mode, fox):
+    q, k, v, w, beta, logf = rand_problem(L, d, 300 + L, beta_mode=beta_mode, fox=fox)
+    dout = np.random.default_rng(301 + L).standard_normal((L, d))
+    got = oracle_lib.bwd(q, k, v, w, beta, dout, logf=logf, scale=0.6, nthreads=1)
+    want = _fd_grads(oracle_lib, q, k, v, w, beta, logf, dout, 0.6)
+    names = ("dq", "dk", "dv", "dw", "dbeta", "dlogf")
+    for name, g, fd in zip(names, got, want):
+        assert_close(g, fd, 2e-8 * max(1.0, np.abs(fd).max()), name)
+    if not fox:
+        assert got[5] is None
+
+
+def _torch_explicit_grads(q, k, v, w, beta, logf, dout, scale):
+    """torch autograd through the definition built from explicit d x d matrices."""
+    import torch
+    t = lambda x: torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    tq, tk, tv, tw, tb = map(t, (q, k, v, w, beta))
+    tf = t(logf) if logf is not None else None
+    L, d = q.shape
+    eye = torch.eye(d, dtype=torch.float64)
+    rows = []
+    for i in range(L):
+        zi = []
+        M = eye
+        bias = torch.zeros((), dtype=torch.float64)
+        for j in range(i, -1, -1):  # M = H_{j+1} ... H_i
+            zi.append(scale * (tk[j] @ (M @ tq[i])) + bias)
+            M = (eye - tb[j] * torch.outer(tw[j], tw[j])) @ M
+            if tf is not None:
+                bias = bias + tf[j]
+        z = torch.stack(zi[::-1])
+        rows.append(torch.softmax(z, 0) @ tv[: i + 1])
+    out = torch.stack(rows)
+    (out * torch.tensor(dout)).sum().backward()
+    gs = [x.grad.numpy() for x in (tq, tk, tv, tw, tb)]
+    return gs + [tf.grad.numpy() if tf is not None else None]
+
+
+@pytest.mark.parametrize("L,d,fox", [(6, 4, True), (10, 3, False)])
+def test_p12_backward_matches_autograd_of_explicit_products(oracle_lib, L, d, fox):
+    q, k, v, w, beta, logf = rand_problem(L, d, 320 + L, fox=fox, unit=False)  # raw w: no norm assumed
+    dout = np.random.default_rng(321).standard_normal((L, d))
+    got = oracle_lib.bwd(q, k, v, w, beta, dout, logf=logf, scale=0.45, nthreads=1)
+    want = _torch_explicit_grads(q, k, v, w, beta, logf, dout, 0.45)
+    for name, g, a in zip(("dq", "dk", "dv", "dw", "dbeta", "dlogf"), got, want):
+        if a is None:
+            assert g is None
+        else:
+            assert_close(g, a, 1e-11 * max(1.0, np.abs(a).max()), name)
+
+
+def test_p12_beta_zero_is_plain_attention_gradient(oracle_lib):
+    import torch
+    L, d, scale = 29, 8, 0.35
+    q, k, v, w, beta, _ = rand_problem(L, d, 340, beta_mode="zero")
+    dout = np.random.default_rng(341).standard_normal((L, d))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    z = scale * tq @ tk.T
+    z = z.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+    z.retain_grad()
+    (torch.softmax(z, 1) @ tv * torch.tensor(dout)).sum().backward()
+    dq, dk, dv, dw, dbeta, _ = oracle_lib.bwd(q, k, v, w, beta, dout, scale=scale)
+    for name, g, a in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+        assert_close(g, a.numpy(), 1e-12, name)
+    assert np.all(dw == 0.0), "with beta = 0 the output does not depend on w"
+    # at beta = 0, d z_ij / d beta_s = -scale (w_s . k_j)(w_s . q_i) for every pair j < s <= i
+    dz = z.grad.numpy()
+    want = np.array([-scale * sum(dz[i, j] * (w[s] @ k[j]) * (w[s] @ q[i])
+                                  for i in range(s, L) for j in range(s)) for s in range(L)])
+    assert_close(dbeta, want, 1e-12, "dbeta closed form")
+
+
+BWD_MUTATIONS = {
+    # dbeta with the wrong sign
+    "dbeta_sign": ("dbeta[s] = -dot(ws, cu, d);", "dbeta[s] = dot(ws, cu, d);"),
+    # dw from dH_s w_s only (the transpose term dropped)
+    "dw_no_transpose": ("-beta[s] * (cu[t] + cv[t]);", "-beta[s] * (2.0 * cu[t]);"),
+    # query gradient carried one transition too far (a_{j,i+1} -> a_{j,i+1} moved by H_i ... starting at i)
+    "dq_index": ("const double* a = A + (j * (L + 1) + i + 1) * d;",
+                 "const double* a = A + (j * (L + 1) + (i > j ? i : i + 1)) * d;"),
+    # forget gradient counts the pairs j <= s instead of j < s
+    "df_range": ("for (int64_t j = 0; j < s; ++j) {\n        c += dZ[i * L + j] * aw[j];\n        df += dZ[i * L + j];\n      }",
+                 "for (int64_t j = 0; j < s; ++j) {\n        c += dZ[i * L + j] * aw[j];\n        df += dZ[i * L + j];\n      }\n      df += dZ[i * L + s];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_p12_planted_backward_mistakes_are_caught(oracle_lib, name, monkeypatch):
+    src = open(os.path.join(os.path.dirname(oracle_lib.__file__), "path_oracle.c")).read()
+    old, new = BWD_MUTATIONS[name]
+    assert old in src, f"mutation site for {name} not found"
+    with tempfile.TemporaryDirectory() as tdir:
+        c, so = os.path.join(tdir, "m.c"), os.path.join(tdir, "m.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", so, c, "-lm"],
+                       check=True)
+        real = oracle_lib.lib()
+        mutated = ctypes.CDLL(so)
+        for f in ("path_oracle_bwd", "path_oracle_fwd"):
+            getattr(mutated, f).argtypes = getattr(real, f).argtypes
+            getattr(mutated, f).restype = ctypes.c_int
+        monkeypatch.setattr(oracle_lib, "_lib", mutated)
+        with pytest.raises(AssertionError):
+            test_p12_backward_matches_finite_differences(oracle_lib, 7, 3, "sigmoid", True)
