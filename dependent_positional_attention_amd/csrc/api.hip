@@ -20,6 +20,11 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
                     void* p2_hi, void* p2_lo, float* Sm, float* fl, float* ftot, hipStream_t st);
 hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
                           int64_t BH, int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st);
+// backward.hip
+hipError_t bwd_run(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
+                   const float* beta, const float* logf, const void* out, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, void* dw, float* dbeta, float* dlogf, int64_t BH, int64_t L,
+                   float scale, const bwd_buffers& b, hipStream_t st);
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
@@ -320,6 +325,91 @@ path_status path_decode_step_deferred(void* kcache, void* vcache, float* fcache,
   return from_hip(decode_step_deferred(dtype == PATH_DTYPE_BF16, d, kcache, vcache, fcache, capacity, t, t_cur, period,
                                        state, q_t, k_t, v_t, w_t, beta_t, log_forget_t, out, lse, BH, scale, (int)S,
                                        static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------------------- backward
+
+}  // extern "C"
+
+namespace {
+
+// Byte offsets of the backward's buffers in its workspace (chunk already resolved).
+struct bwd_plan {
+  int64_t off[17];
+  int64_t total;
+};
+
+path_status plan_bwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype, bwd_plan* p) {
+  if (B < 0 || H < 0 || L < 0 || d <= 0 || chunk <= 0) return PATH_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return PATH_ERR_UNSUPPORTED;
+  if (!vec_supported(d, chunk)) return PATH_ERR_UNSUPPORTED;
+  const int64_t BH = B * H, M = (L + chunk - 1) / chunk, Lp = M * chunk, NP = M * (M - 1) / 2;
+  const int64_t rows = BH * Lp * 4, mat = BH * Lp * d * 4, dd = BH * M * d * d * 4, cc = BH * M * chunk * chunk * 4;
+  const int64_t pairs = BH * NP * chunk * d * 4;
+  const int64_t sizes[17] = {mat, mat, dd, cc, rows, BH * M * 4,      // qt kt Pm Sm fl ftot
+                             pairs, pairs, BH * NP * 4,               // St Gst Off
+                             rows, rows, rows, rows,                  // lse2 Dv drow dcol
+                             mat, mat, dd, cc};                       // dqt dkt dPm dSm
+  int64_t o = 0;
+  for (int i = 0; i < 17; ++i) {
+    p->off[i] = o;
+    o = round_up(o + sizes[i], kAlign);
+  }
+  p->total = o;
+  return PATH_OK;
+}
+
+int bwd_chunk(int chunk) { return chunk == 0 ? 64 : chunk; }
+
+}  // namespace
+
+extern "C" {
+
+path_status path_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                                          size_t* bytes) {
+  if (bytes == nullptr) return PATH_ERR_INVALID_ARG;
+  bwd_plan p;
+  const path_status s = plan_bwd(B, H, L, d, bwd_chunk(chunk), dtype, &p);
+  if (s != PATH_OK) return s;
+  *bytes = (size_t)p.total;
+  return PATH_OK;
+}
+
+path_status path_attn_bwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                          const float* log_forget, const void* out, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, void* dw, float* dbeta, float* dlog_forget, int64_t B, int64_t H,
+                          int64_t L, int d, int chunk, float scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  chunk = bwd_chunk(chunk);
+  bwd_plan p;
+  const path_status s = plan_bwd(B, H, L, d, chunk, dtype, &p);
+  if (s != PATH_OK) return s;
+  if ((log_forget == nullptr) != (dlog_forget == nullptr)) return PATH_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  if (BH == 0 || L == 0) return PATH_OK;
+  if (!q || !k || !v || !w || !beta || !out || !lse || !dout || !dq || !dk || !dv || !dw || !dbeta || !workspace)
+    return PATH_ERR_INVALID_ARG;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(w) || misaligned(beta) ||
+      misaligned(log_forget) || misaligned(out) || misaligned(lse) || misaligned(dout) || misaligned(dq) ||
+      misaligned(dk) || misaligned(dv) || misaligned(dw) || misaligned(dbeta) || misaligned(dlog_forget) ||
+      misaligned(workspace))
+    return PATH_ERR_UNSUPPORTED;
+  if (workspace_bytes < (size_t)p.total) return PATH_ERR_INVALID_ARG;
+  const int64_t M = (L + chunk - 1) / chunk;
+  if (BH > kMaxGridY || M > kMaxGridY) return PATH_ERR_UNSUPPORTED;
+  char* ws = static_cast<char*>(workspace);
+  auto f = [&](int i) { return reinterpret_cast<float*>(ws + p.off[i]); };
+  const bwd_buffers b{f(0), f(1), f(2), f(3), f(4), f(5), f(6), f(7), f(8),
+                      f(9), f(10), f(11), f(12), f(13), f(14), f(15), f(16)};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == PATH_DTYPE_BF16;
+  // the forward's per-chunk terms, fp32, as the vector path builds them
+  hipError_t e = vec_run(kPhasePrep, bf16, d, chunk, q, k, v, w, beta, log_forget, nullptr, nullptr, BH, L, scale,
+                         b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot, st);
+  if (e == hipSuccess)
+    e = bwd_run(bf16, d, chunk, q, k, v, w, beta, log_forget, out, lse, dout, dq, dk, dv, dw, dbeta, dlog_forget, BH,
+                L, scale, b, st);
+  return from_hip(e);
 }
 
 }  // extern "C"

@@ -1,0 +1,856 @@
+// PaTH / PaTH-FoX backward pass (fp32 arithmetic throughout, vector ALU).
+//
+// The pages give the forward only (PaTH summary, gist.science/ko/paper/2505.16381, section 3, and the
+// lecture notes on PaTH, brianyu43.github.io/gpumode/lecture_074.html, whose "limitations" part only
+// says the backward costs more than RoPE's).  This file differentiates the blockwise forward of
+// vector_path.hip step by step, chunk size C, head dim D:
+//
+//   forward per query chunk m:  r^(m-1) = qtilde_m (scaled by scale*log2e),
+//                               z_mn = r^(n) ktilde_n^T (+ FoX bias), r^(n-1) = r^(n) P_n^T
+//   backward per query chunk m: the states r^(n) are kept (they cannot be recovered from r^(n-1):
+//                               P_n is singular when some beta_s = 1), then, for n = 0 .. m-1,
+//                               dr^(n) = g_mn ktilde_n + dr^(n-1) P_n,   g = ln2 * dz
+//   dP_n     = sum_{m > n} dr^(n-1)_m^T r^(n)_m          (d x d, reduced per key chunk)
+//   dktilde_n = sum_{m > n} g_mn^T r^(n)_m,  dv_n = sum_{m >= n} p_mn^T dO_m
+//   dz_ij    = p_ij (dO_i . v_j - D_i),  D_i = dO_i . o_i,  p_ij = exp2(z2_ij - lse2_i)
+//
+// then each chunk's UT-transform terms (qtilde, ktilde, P, in-chunk logits S) are differentiated back
+// to q, k, w, beta:
+//
+//   A = I + diag(beta) strict_upper(W W^T),  Ti = A^{-1} diag(beta)
+//   U = (W Q^T) on t <= a,  R = (K W^T) on s > b,  X = Ti U,  Y = R Ti
+//   qtilde = Q - X^T W,  ktilde = K - Y W,  P = I - W^T Ti W,  S^T = (K Q^T - Y U) on b <= a
+//
+//   dX = -W dqtilde^T      dY = -dktilde W^T - dS^T U^T      dU = Ti^T dX - (dS Y)^T      dR = dY Ti^T
+//   dTi = dX U^T + R^T dY - W dP W^T
+//   dA  = -A^{-T} dTi Ti^T (strict upper),  dbeta = diag(A^{-T} dTi) + rowsum(dA o W W^T)
+//   dW  = -X dqtilde - Y^T dktilde - Ti W dP^T - Ti^T W dP + dU Q + dR^T K + (dN + dN^T) W,
+//         dN = diag(beta) dA
+//   dQ  = dqtilde + dS K + dU^T W,   dK = dktilde + dS^T Q + dR W
+//
+// PaTH-FoX: z_ij carries F_i - F_j, so dF_t = sum_j dz_tj - sum_i dz_it and df_s = sum_{t >= s} dF_t.
+#include "common.h"
+
+namespace pathattn {
+
+namespace {
+
+template <int C, int D>
+struct BwdShape {
+  static constexpr int DP = D + 1, CP = C + 1, CD = C * D, CC = C * C;
+  static constexpr int NE = (CD + 255) / 256;  // C x D elements per thread
+  static constexpr int NC = (CC + 255) / 256;  // C x C elements per thread
+  static constexpr int NDD = (D * D + 255) / 256;
+  static constexpr int SL = (C * CP > C * DP ? (C * CP > D * DP ? C * CP : D * DP) : (C * DP > D * DP ? C * DP : D * DP));
+  static constexpr size_t lds_query = sizeof(float) * (5 * C * DP + D * DP + C * CP + 4 * C);
+  static constexpr size_t lds_key = sizeof(float) * (5 * C * DP + 2 * C * CP + 4 * C);
+  static constexpr size_t lds_prep = sizeof(float) * (9 * SL + 2 * C);
+};
+
+__host__ __device__ inline int64_t pair_index(int64_t m, int64_t n) { return m * (m - 1) / 2 + n; }
+
+}  // namespace
+
+// ------------------------------------------------------------------------------- query chunks
+// One block per (query chunk m, batch*head).  Writes the states r^(n) and incoming gradients
+// dr^(n-1) of every pair (m, n < m), the FoX offsets of each pair, the row statistics, the
+// in-chunk logit gradient dS (unscaled units), d qtilde (unscaled) and the row sums of dz.
+template <typename T, int D, int C>
+__global__ __launch_bounds__(256) void bwd_query_kernel(
+    const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
+    const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
+    const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
+    int64_t L, int64_t M, float scale, float* __restrict__ St, float* __restrict__ Gst, float* __restrict__ Off,
+    float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow, float* __restrict__ dqt,
+    float* __restrict__ dSm) {
+  using S = BwdShape<C, D>;
+  constexpr int DP = S::DP, CP = S::CP, CD = S::CD, NE = S::NE;
+  extern __shared__ float sm[];
+  float* Rs = sm;           // r^(n)          [C][DP]
+  float* Ks = Rs + C * DP;  // ktilde_n       [C][DP]
+  float* Vs = Ks + C * DP;  // v_n            [C][DP]
+  float* Os = Vs + C * DP;  // dO_m           [C][DP]
+  float* Qd = Os + C * DP;  // dr^(n-1)       [C][DP]
+  float* Ps = Qd + C * DP;  // P_n            [D][DP]
+  float* Gs = Ps + D * DP;  // dz             [C][CP]
+  float* l2 = Gs + C * CP;  // lse2 of the rows
+  float* Dv = l2 + C;       // D of the rows
+  float* Fn = Dv + C;       // local FoX prefix of key chunk n
+  float* rs = Fn + C;       // row sums of dz
+
+  const int tid = threadIdx.x;
+  const int64_t m = (int64_t)gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int64_t bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const bool fox = fl != nullptr;
+  const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
+
+  auto stage_rows = [&](float* dst, const T* src, int64_t c0) PA_INLINE {
+    for (int e = tid; e < CD; e += 256) {
+      const int a = e / D, x = e % D;
+      const int64_t i = c0 + a;
+      dst[a * DP + x] = i < L ? to_f32(src[((size_t)bh * L + i) * D + x]) : 0.f;
+    }
+  };
+
+  stage_rows(Os, dout, m * C);
+  __syncthreads();
+  for (int a = tid; a < C; a += 256) {
+    const int64_t i = m * C + a;
+    float dv = 0.f, l2v = INFINITY;  // padded rows: p = 0
+    if (i < L) {
+      const T* orow = out + ((size_t)bh * L + i) * D;
+      #pragma unroll 4
+      for (int x = 0; x < D; ++x) dv += Os[a * DP + x] * to_f32(orow[x]);
+      l2v = kLog2e * (lse[bh * L + i] - (fox ? fl[row0 + a] : 0.f));
+    }
+    Dv[a] = dv;
+    l2[a] = l2v;
+    rs[a] = 0.f;
+    lse2w[row0 + a] = l2v;
+    Dw[row0 + a] = dv;
+  }
+
+  // pass 1: states r^(n), n = m-1 .. 0, in the forward's order (and its FoX offsets)
+  float R[NE], G[NE];
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    R[j] = e < CD ? qt[row0 * D + e] : 0.f;
+    G[j] = 0.f;
+  }
+  float off = 0.f;
+  for (int64_t n = m - 1; n >= 0; --n) {
+    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    if (fox) off += ftot[bh * M + n];
+    if (tid == 0) Off[pr] = off;
+    for (int j = 0; j < NE; ++j) {
+      const int e = tid + 256 * j;
+      if (e < CD) St[pr * CD + e] = R[j];
+    }
+    if (n > 0) {
+      for (int j = 0; j < NE; ++j) {
+        const int e = tid + 256 * j;
+        if (e < CD) Rs[(e / D) * DP + e % D] = R[j];
+      }
+      const float* Pn = Pm + ((size_t)bh * M + n) * D * D;
+      for (int e = tid; e < D * D; e += 256) Ps[(e / D) * DP + e % D] = Pn[e];
+      __syncthreads();
+      for (int j = 0; j < NE; ++j) {
+        const int e = tid + 256 * j;
+        if (e < CD) {
+          const int a = e / D, x = e % D;
+          float s = 0.f;
+          #pragma unroll 4
+          for (int y = 0; y < D; ++y) s += Rs[a * DP + y] * Ps[x * DP + y];
+          R[j] = s;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // in-chunk block: logits from S
+  stage_rows(Vs, v, m * C);
+  if (fox)
+    for (int a = tid; a < C; a += 256) Fn[a] = fl[row0 + a];
+  __syncthreads();
+  {
+    const float* Sc = Sm + ((size_t)bh * M + m) * C * C;
+    float* dSc = dSm + ((size_t)bh * M + m) * C * C;
+    for (int e = tid; e < C * C; e += 256) {
+      const int a = e / C, b = e % C;
+      float dz = 0.f;
+      if (b <= a) {
+        const float z2 = Sc[e] - (fox ? kLog2e * Fn[b] : 0.f);
+        const float p = fast_exp2(z2 - l2[a]);
+        float dp = 0.f;
+        #pragma unroll 4
+        for (int x = 0; x < D; ++x) dp += Os[a * DP + x] * Vs[b * DP + x];
+        dz = p * (dp - Dv[a]);
+      }
+      Gs[a * CP + b] = dz;
+      dSc[e] = scale * dz;
+    }
+  }
+  __syncthreads();
+  for (int a = tid; a < C; a += 256) {
+    float s = 0.f;
+    #pragma unroll 4
+    for (int b = 0; b < C; ++b) s += Gs[a * CP + b];
+    rs[a] += s;
+  }
+
+  // pass 2: n = 0 .. m-1, gradients flow back up the chain of transports
+  for (int64_t n = 0; n < m; ++n) {
+    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    __syncthreads();
+    for (int j = 0; j < NE; ++j) {
+      const int e = tid + 256 * j;
+      if (e < CD) {
+        const int a = e / D, x = e % D;
+        Rs[a * DP + x] = St[pr * CD + e];
+        Ks[a * DP + x] = kt[((size_t)bh * Lp + (size_t)n * C) * D + e];
+        if (n > 0) {
+          Qd[a * DP + x] = G[j];
+          Gst[pr * CD + e] = G[j];
+        }
+      }
+    }
+    stage_rows(Vs, v, n * C);
+    if (n > 0) {
+      const float* Pn = Pm + ((size_t)bh * M + n) * D * D;
+      for (int e = tid; e < D * D; e += 256) Ps[(e / D) * DP + e % D] = Pn[e];
+    }
+    if (fox)
+      for (int a = tid; a < C; a += 256) Fn[a] = fl[(size_t)bh * Lp + (size_t)n * C + a];
+    const float offn = fox ? Off[pr] : 0.f;
+    __syncthreads();
+    for (int e = tid; e < C * C; e += 256) {
+      const int a = e / C, b = e % C;
+      float z2 = fox ? kLog2e * (offn - Fn[b]) : 0.f, dp = 0.f;
+      #pragma unroll 4
+      for (int x = 0; x < D; ++x) {
+        z2 += Rs[a * DP + x] * Ks[b * DP + x];
+        dp += Os[a * DP + x] * Vs[b * DP + x];
+      }
+      const float p = fast_exp2(z2 - l2[a]);
+      Gs[a * CP + b] = p * (dp - Dv[a]);
+    }
+    __syncthreads();
+    for (int a = tid; a < C; a += 256) {
+      float s = 0.f;
+      #pragma unroll 4
+      for (int b = 0; b < C; ++b) s += Gs[a * CP + b];
+      rs[a] += s;
+    }
+    for (int j = 0; j < NE; ++j) {
+      const int e = tid + 256 * j;
+      if (e < CD) {
+        const int a = e / D, y = e % D;
+        float s = 0.f, t = 0.f;
+        if (n > 0)
+          #pragma unroll 4
+          for (int x = 0; x < D; ++x) s += Qd[a * DP + x] * Ps[x * DP + y];
+        #pragma unroll 4
+        for (int b = 0; b < C; ++b) t += Gs[a * CP + b] * Ks[b * DP + y];
+        G[j] = s + kLn2 * t;
+      }
+    }
+  }
+
+  const float c = scale * kLog2e;  // qtilde entered the scan scaled by c
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) dqt[row0 * D + e] = c * G[j];
+  }
+  for (int a = tid; a < C; a += 256) drow[row0 + a] = rs[a];
+}
+
+// ------------------------------------------------------------------------------- key chunks
+// One block per (key chunk n, batch*head): dv, d ktilde, dP_n and the column sums of dz.
+template <typename T, int D, int C>
+__global__ __launch_bounds__(256) void bwd_key_kernel(
+    const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
+    const T* __restrict__ v, const T* __restrict__ dout, const float* __restrict__ St, const float* __restrict__ Gst,
+    const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
+    int64_t M, T* __restrict__ dv, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol) {
+  using S = BwdShape<C, D>;
+  constexpr int DP = S::DP, CP = S::CP, CD = S::CD, NE = S::NE, NDD = S::NDD;
+  extern __shared__ float sm[];
+  float* Ks = sm;           // ktilde_n  [C][DP]
+  float* Vs = Ks + C * DP;  // v_n
+  float* Rs = Vs + C * DP;  // r^(n)_m
+  float* Os = Rs + C * DP;  // dO_m
+  float* Gq = Os + C * DP;  // dr^(n-1)_m
+  float* Pp = Gq + C * DP;  // p     [C][CP]
+  float* Zs = Pp + C * CP;  // dz    [C][CP]
+  float* l2 = Zs + C * CP;
+  float* Dv = l2 + C;
+  float* Fn = Dv + C;
+  float* cs = Fn + C;
+
+  const int tid = threadIdx.x;
+  const int64_t n = blockIdx.x, bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const bool fox = fl != nullptr;
+  const size_t rown = (size_t)bh * Lp + (size_t)n * C;
+
+  auto stage_rows = [&](float* dst, const T* src, int64_t c0) PA_INLINE {
+    for (int e = tid; e < CD; e += 256) {
+      const int a = e / D, x = e % D;
+      const int64_t i = c0 + a;
+      dst[a * DP + x] = i < L ? to_f32(src[((size_t)bh * L + i) * D + x]) : 0.f;
+    }
+  };
+  auto stage_stats = [&](int64_t mm) PA_INLINE {
+    const size_t r0 = (size_t)bh * Lp + (size_t)mm * C;
+    for (int a = tid; a < C; a += 256) {
+      l2[a] = lse2w[r0 + a];
+      Dv[a] = Dw[r0 + a];
+    }
+  };
+
+  for (int e = tid; e < CD; e += 256) Ks[(e / D) * DP + e % D] = kt[rown * D + e];
+  stage_rows(Vs, v, n * C);
+  for (int a = tid; a < C; a += 256) {
+    Fn[a] = fox ? fl[rown + a] : 0.f;
+    cs[a] = 0.f;
+  }
+  stage_rows(Os, dout, n * C);
+  stage_stats(n);
+  float aK[NE], aV[NE], aP[NDD];
+  for (int j = 0; j < NE; ++j) aK[j] = aV[j] = 0.f;
+  for (int j = 0; j < NDD; ++j) aP[j] = 0.f;
+  __syncthreads();
+
+  // in-chunk block
+  {
+    const float* Sc = Sm + ((size_t)bh * M + n) * C * C;
+    for (int e = tid; e < C * C; e += 256) {
+      const int a = e / C, b = e % C;
+      float p = 0.f, dz = 0.f;
+      if (b <= a) {
+        const float z2 = Sc[e] - (fox ? kLog2e * Fn[b] : 0.f);
+        p = fast_exp2(z2 - l2[a]);
+        float dp = 0.f;
+        #pragma unroll 4
+        for (int x = 0; x < D; ++x) dp += Os[a * DP + x] * Vs[b * DP + x];
+        dz = p * (dp - Dv[a]);
+      }
+      Pp[a * CP + b] = p;
+      Zs[a * CP + b] = dz;
+    }
+  }
+  __syncthreads();
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int b = e / D, x = e % D;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int a = 0; a < C; ++a) s += Pp[a * CP + b] * Os[a * DP + x];
+      aV[j] += s;
+    }
+  }
+  for (int b = tid; b < C; b += 256) {
+    float s = 0.f;
+    #pragma unroll 4
+    for (int a = 0; a < C; ++a) s += Zs[a * CP + b];
+    cs[b] += s;
+  }
+
+  for (int64_t m = n + 1; m < M; ++m) {
+    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    __syncthreads();
+    for (int e = tid; e < CD; e += 256) {
+      const int a = e / D, x = e % D;
+      Rs[a * DP + x] = St[pr * CD + e];
+      if (n > 0) Gq[a * DP + x] = Gst[pr * CD + e];
+    }
+    stage_rows(Os, dout, m * C);
+    stage_stats(m);
+    const float offn = fox ? Off[pr] : 0.f;
+    __syncthreads();
+    for (int e = tid; e < C * C; e += 256) {
+      const int a = e / C, b = e % C;
+      float z2 = fox ? kLog2e * (offn - Fn[b]) : 0.f, dp = 0.f;
+      #pragma unroll 4
+      for (int x = 0; x < D; ++x) {
+        z2 += Rs[a * DP + x] * Ks[b * DP + x];
+        dp += Os[a * DP + x] * Vs[b * DP + x];
+      }
+      const float p = fast_exp2(z2 - l2[a]);
+      Pp[a * CP + b] = p;
+      Zs[a * CP + b] = p * (dp - Dv[a]);
+    }
+    __syncthreads();
+    for (int j = 0; j < NE; ++j) {
+      const int e = tid + 256 * j;
+      if (e < CD) {
+        const int b = e / D, x = e % D;
+        float sv = 0.f, sk = 0.f;
+        #pragma unroll 4
+        for (int a = 0; a < C; ++a) {
+          sv += Pp[a * CP + b] * Os[a * DP + x];
+          sk += Zs[a * CP + b] * Rs[a * DP + x];
+        }
+        aV[j] += sv;
+        aK[j] += kLn2 * sk;
+      }
+    }
+    for (int b = tid; b < C; b += 256) {
+      float s = 0.f;
+      #pragma unroll 4
+      for (int a = 0; a < C; ++a) s += Zs[a * CP + b];
+      cs[b] += s;
+    }
+    if (n > 0)
+      for (int j = 0; j < NDD; ++j) {
+        const int e = tid + 256 * j;
+        if (e < D * D) {
+          const int x = e / D, y = e % D;
+          float s = 0.f;
+          #pragma unroll 4
+          for (int a = 0; a < C; ++a) s += Gq[a * DP + x] * Rs[a * DP + y];
+          aP[j] += s;
+        }
+      }
+  }
+
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int b = e / D;
+      dkt[rown * D + e] = aK[j];
+      if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * D + e % D] = from_f32<T>(aV[j]);
+    }
+  }
+  for (int j = 0; j < NDD; ++j) {
+    const int e = tid + 256 * j;
+    if (e < D * D) dPm[((size_t)bh * M + n) * D * D + e] = aP[j];
+  }
+  for (int b = tid; b < C; b += 256) dcol[rown + b] = cs[b];
+}
+
+// ------------------------------------------------------------------------------- UT-transform terms
+// One block per (chunk c, batch*head): from d qtilde, d ktilde, dP and dS of the chunk to dq, dk, dw,
+// dbeta.  Nine LDS tiles; the C x C intermediates pass through registers where a tile is rewritten.
+template <typename T, int D, int C>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ w, const float* __restrict__ beta,
+    const float* __restrict__ dqt, const float* __restrict__ dkt, const float* __restrict__ dPm,
+    const float* __restrict__ dSm, int64_t L, int64_t M, T* __restrict__ dq, T* __restrict__ dk,
+    T* __restrict__ dw, float* __restrict__ dbeta) {
+  using S = BwdShape<C, D>;
+  constexpr int DP = S::DP, CP = S::CP, CD = S::CD, CC = S::CC, NE = S::NE, NC = S::NC, SL = S::SL;
+  extern __shared__ float sm[];
+  float* Wt = sm;         // W [C][DP]
+  float* Qt = Wt + SL;    // Q
+  float* Kt = Qt + SL;    // K
+  float* Ai = Kt + SL;    // A^{-1} [C][CP] (unit upper triangular; Ti = Ai diag(beta))
+  float* Ut = Ai + SL;    // U, later W dP
+  float* Rt = Ut + SL;    // R, later W dP^T
+  float* X6 = Rt + SL;    // A, dS, dY, dTi
+  float* X7 = X6 + SL;    // dktilde, dqtilde, dU, dR, dP, dN
+  float* X8 = X7 + SL;    // Y, X, dX, A^{-T} dTi
+  float* Bs = X8 + SL;    // beta [C]
+  float* dB = Bs + C;     // dbeta [C]
+
+  const int tid = threadIdx.x;
+  const int64_t c = blockIdx.x, bh = blockIdx.y, Lp = M * C;
+  const size_t row0 = (size_t)bh * Lp + (size_t)c * C;
+
+  for (int e = tid; e < CD; e += 256) {
+    const int a = e / D, x = e % D;
+    const int64_t i = c * C + a;
+    const bool ok = i < L;
+    const size_t g = ((size_t)bh * L + (ok ? i : 0)) * D + x;
+    Wt[a * DP + x] = ok ? to_f32(w[g]) : 0.f;
+    Qt[a * DP + x] = ok ? to_f32(q[g]) : 0.f;
+    Kt[a * DP + x] = ok ? to_f32(k[g]) : 0.f;
+  }
+  for (int a = tid; a < C; a += 256) {
+    const int64_t i = c * C + a;
+    Bs[a] = i < L ? beta[bh * L + i] : 0.f;
+    dB[a] = 0.f;
+  }
+  __syncthreads();
+
+  // A (into X6), U, R
+  for (int e = tid; e < CC; e += 256) {
+    const int r = e / C, s = e % C;
+    float g = 0.f, u = 0.f, rr = 0.f;
+    #pragma unroll 4
+    for (int x = 0; x < D; ++x) {
+      g += Wt[r * DP + x] * Wt[s * DP + x];
+      u += Wt[r * DP + x] * Qt[s * DP + x];
+      rr += Kt[r * DP + x] * Wt[s * DP + x];
+    }
+    X6[r * CP + s] = r < s ? Bs[r] * g : 0.f;
+    Ut[r * CP + s] = r <= s ? u : 0.f;
+    Rt[r * CP + s] = s > r ? rr : 0.f;
+  }
+  __syncthreads();
+  // A^{-1} by back substitution, one column per thread
+  for (int j = tid; j < C; j += 256) {
+    for (int i = C - 1; i > j; --i) Ai[i * CP + j] = 0.f;
+    Ai[j * CP + j] = 1.f;
+    for (int i = j - 1; i >= 0; --i) {
+      float s = 0.f;
+      for (int kk = i + 1; kk <= j; ++kk) s += X6[i * CP + kk] * Ai[kk * CP + j];
+      Ai[i * CP + j] = -s;
+    }
+  }
+  __syncthreads();
+  // dS into X6, Y = R Ti into X8
+  {
+    const float* dSc = dSm + ((size_t)bh * M + c) * CC;
+    for (int e = tid; e < CC; e += 256) {
+      const int b = e / C, t = e % C;
+      X6[b * CP + t] = dSc[e];
+      float y = 0.f;
+      for (int s = b + 1; s <= t; ++s) y += Rt[b * CP + s] * Ai[s * CP + t];
+      X8[b * CP + t] = y * Bs[t];
+    }
+  }
+  __syncthreads();
+
+  float aq[NE], ak[NE], aw[NE], rA[NC], rB[NC];
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    aw[j] = 0.f;
+    if (e < CD) {
+      const int a = e / D, x = e % D;
+      float sq = dqt[row0 * D + e], sk = dkt[row0 * D + e];
+      #pragma unroll 4
+      for (int b = 0; b < C; ++b) {
+        sq += X6[a * CP + b] * Kt[b * DP + x];  // dS K
+        sk += X6[b * CP + a] * Qt[b * DP + x];  // dS^T Q
+      }
+      aq[j] = sq;
+      ak[j] = sk;
+    }
+  }
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    rA[j] = rB[j] = 0.f;
+    if (e < CC) {
+      const int r = e / C, s = e % C;
+      float u = 0.f, y = 0.f;
+      #pragma unroll 4
+      for (int b = 0; b < C; ++b) {
+        u += X6[s * CP + b] * X8[b * CP + r];  // (dS Y)[s][r]   -> dU[r][s]
+        y += X6[b * CP + r] * Ut[s * CP + b];  // (dS^T U^T)[r][s] -> dY[r][s]
+      }
+      rA[j] = -u;
+      rB[j] = -y;
+    }
+  }
+  __syncthreads();
+  // d ktilde into X7: dW -= Y^T dktilde, dY -= dktilde W^T
+  for (int e = tid; e < CD; e += 256) X7[(e / D) * DP + e % D] = dkt[row0 * D + e];
+  __syncthreads();
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int t = e / D, x = e % D;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int b = 0; b < C; ++b) s += X8[b * CP + t] * X7[b * DP + x];
+      aw[j] -= s;
+    }
+  }
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) {
+      const int b = e / C, t = e % C;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int x = 0; x < D; ++x) s += X7[b * DP + x] * Wt[t * DP + x];
+      rB[j] -= s;
+    }
+  }
+  __syncthreads();
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) X6[(e / C) * CP + e % C] = rB[j];  // dY
+  }
+  // d qtilde into X7, X = Ti U into X8
+  for (int e = tid; e < CD; e += 256) X7[(e / D) * DP + e % D] = dqt[row0 * D + e];
+  for (int e = tid; e < CC; e += 256) {
+    const int t = e / C, a = e % C;
+    float s = 0.f;
+    for (int u = t; u <= a; ++u) s += Ai[t * CP + u] * Bs[u] * Ut[u * CP + a];
+    X8[t * CP + a] = s;
+  }
+  __syncthreads();
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int t = e / D, x = e % D;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int a = 0; a < C; ++a) s += X8[t * CP + a] * X7[a * DP + x];
+      aw[j] -= s;  // dW -= X dqtilde
+    }
+  }
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) {
+      const int t = e / C, a = e % C;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int x = 0; x < D; ++x) s += Wt[t * DP + x] * X7[a * DP + x];
+      rB[j] = -s;  // dX
+    }
+  }
+  __syncthreads();
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) X8[(e / C) * CP + e % C] = rB[j];  // dX
+  }
+  __syncthreads();
+  // dU = Ti^T dX - (dS Y)^T on t <= a, into X7
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) {
+      const int t = e / C, a = e % C;
+      float s = 0.f;
+      for (int u = 0; u <= t; ++u) s += Ai[u * CP + t] * X8[u * CP + a];
+      X7[t * CP + a] = t <= a ? rA[j] + Bs[t] * s : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int r = e / D, x = e % D;
+      float sw = 0.f, sq = 0.f;
+      #pragma unroll 4
+      for (int a = 0; a < C; ++a) {
+        sw += X7[r * CP + a] * Qt[a * DP + x];  // dW += dU Q
+        sq += X7[a * CP + r] * Wt[a * DP + x];  // dQ += dU^T W
+      }
+      aw[j] += sw;
+      aq[j] += sq;
+    }
+  }
+  __syncthreads();
+  // dR = dY Ti^T on s > b, into X7
+  for (int e = tid; e < CC; e += 256) {
+    const int b = e / C, s = e % C;
+    float acc = 0.f;
+    for (int t = s; t < C; ++t) acc += X6[b * CP + t] * Ai[s * CP + t] * Bs[t];
+    X7[b * CP + s] = s > b ? acc : 0.f;
+  }
+  __syncthreads();
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int r = e / D, x = e % D;
+      float sk = 0.f, sw = 0.f;
+      #pragma unroll 4
+      for (int s = 0; s < C; ++s) {
+        sk += X7[r * CP + s] * Wt[s * DP + x];  // dK += dR W
+        sw += X7[s * CP + r] * Kt[s * DP + x];  // dW += dR^T K
+      }
+      ak[j] += sk;
+      aw[j] += sw;
+    }
+  }
+  // dTi = dX U^T + R^T dY (registers), then - W dP W^T
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) {
+      const int t = e / C, u = e % C;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int a = 0; a < C; ++a) s += X8[t * CP + a] * Ut[u * CP + a] + Rt[a * CP + t] * X6[a * CP + u];
+      rA[j] = s;
+    }
+  }
+  __syncthreads();
+  {
+    const float* dPc = dPm + ((size_t)bh * M + c) * D * D;
+    for (int e = tid; e < D * D; e += 256) X7[(e / D) * DP + e % D] = dPc[e];
+  }
+  __syncthreads();
+  for (int e = tid; e < CD; e += 256) {
+    const int t = e / D, y = e % D;
+    float a1 = 0.f, a2 = 0.f;
+    #pragma unroll 4
+    for (int x = 0; x < D; ++x) {
+      a1 += Wt[t * DP + x] * X7[x * DP + y];  // (W dP)[t][y]
+      a2 += Wt[t * DP + x] * X7[y * DP + x];  // (W dP^T)[t][y]
+    }
+    Ut[t * DP + y] = a1;
+    Rt[t * DP + y] = a2;
+  }
+  __syncthreads();
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) {
+      const int t = e / C, u = e % C;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int y = 0; y < D; ++y) s += Ut[t * DP + y] * Wt[u * DP + y];
+      rA[j] -= s;
+    }
+  }
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int t = e / D, x = e % D;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int u = 0; u < C; ++u)
+        s += Ai[t * CP + u] * Bs[u] * Rt[u * DP + x] + Ai[u * CP + t] * Bs[t] * Ut[u * DP + x];
+      aw[j] -= s;  // dW -= Ti W dP^T + Ti^T W dP
+    }
+  }
+  __syncthreads();
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) X6[(e / C) * CP + e % C] = rA[j];  // dTi
+  }
+  __syncthreads();
+  // M1 = A^{-T} dTi into X8; dbeta += diag(M1)
+  for (int j = 0; j < NC; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CC) {
+      const int r = e / C, s = e % C;
+      float acc = 0.f;
+      for (int u = 0; u <= r; ++u) acc += Ai[u * CP + r] * X6[u * CP + s];
+      X8[r * CP + s] = acc;
+      if (r == s) atomicAdd(&dB[r], acc);
+    }
+  }
+  __syncthreads();
+  // dA = -M1 Ti^T on r < s; dbeta_r += sum_s dA[r][s] (w_r . w_s); dN = diag(beta) dA into X7
+  for (int e = tid; e < CC; e += 256) {
+    const int r = e / C, s = e % C;
+    float z = 0.f;
+    if (r < s) {
+      for (int u = s; u < C; ++u) z -= X8[r * CP + u] * Ai[s * CP + u] * Bs[u];
+      float g = 0.f;
+      #pragma unroll 4
+      for (int x = 0; x < D; ++x) g += Wt[r * DP + x] * Wt[s * DP + x];
+      atomicAdd(&dB[r], z * g);
+    }
+    X7[r * CP + s] = Bs[r] * z;
+  }
+  __syncthreads();
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int t = e / D, x = e % D;
+      float s = 0.f;
+      #pragma unroll 4
+      for (int u = 0; u < C; ++u) s += (X7[t * CP + u] + X7[u * CP + t]) * Wt[u * DP + x];
+      aw[j] += s;
+    }
+  }
+
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < CD) {
+      const int a = e / D, x = e % D;
+      const int64_t i = c * C + a;
+      if (i < L) {
+        const size_t g = ((size_t)bh * L + i) * D + x;
+        dq[g] = from_f32<T>(aq[j]);
+        dk[g] = from_f32<T>(ak[j]);
+        dw[g] = from_f32<T>(aw[j]);
+      }
+    }
+  }
+  for (int a = tid; a < C; a += 256) {
+    const int64_t i = c * C + a;
+    if (i < L) dbeta[bh * L + i] = dB[a];
+  }
+}
+
+// ------------------------------------------------------------------------------- forget gates
+// df_s = sum_{t >= s} (rowsum_t - colsum_t): a suffix sum per (batch, head), one block each.
+__global__ __launch_bounds__(256) void bwd_forget_kernel(const float* __restrict__ drow,
+                                                         const float* __restrict__ dcol, int64_t L, int64_t Lp,
+                                                         float* __restrict__ dlogf) {
+  __shared__ float part[256];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t seg = (L + 255) / 256, lo = tid * seg, hi = lo + seg < L ? lo + seg : L;
+  const float* r = drow + bh * Lp;
+  const float* cc = dcol + bh * Lp;
+  float s = 0.f;
+  for (int64_t t = lo; t < hi; ++t) s += r[t] - cc[t];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;  // exclusive suffix over the later segments
+    for (int u = 255; u >= 0; --u) {
+      const float x = part[u];
+      part[u] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  float acc = part[tid];
+  for (int64_t t = hi - 1; t >= lo; --t) {
+    acc += r[t] - cc[t];
+    dlogf[bh * L + t] = acc;
+  }
+}
+
+// ------------------------------------------------------------------------------- launch
+template <typename T, int D, int C>
+static hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                             const float* logf, const void* out, const float* lse, const void* dout, void* dq,
+                             void* dk, void* dv, void* dw, float* dbeta, float* dlogf, int64_t BH, int64_t L,
+                             float scale, const bwd_buffers& b, hipStream_t st) {
+  using S = BwdShape<C, D>;
+  static_assert(S::lds_query <= 160 * 1024 && S::lds_key <= 160 * 1024 && S::lds_prep <= 160 * 1024,
+                "backward tiles exceed LDS");
+  const int64_t M = (L + C - 1) / C;
+  const dim3 grid((unsigned)M, (unsigned)BH);
+  hipError_t e;
+  const bool fox = logf != nullptr;
+  e = hipFuncSetAttribute((const void*)bwd_query_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)S::lds_query);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)bwd_key_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)S::lds_key);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)bwd_prep_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)S::lds_prep);
+  if (e != hipSuccess) return e;
+  bwd_query_kernel<T, D, C><<<grid, 256, S::lds_query, st>>>(
+      b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
+      scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_key_kernel<T, D, C><<<grid, 256, S::lds_key, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
+                                                        (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
+                                                        (T*)dv, b.dkt, b.dPm, b.dcol);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_prep_kernel<T, D, C><<<grid, 256, S::lds_prep, st>>>((const T*)q, (const T*)k, (const T*)w, beta, b.dqt,
+                                                          b.dkt, b.dPm, b.dSm, L, M, (T*)dq, (T*)dk, (T*)dw,
+                                                          dbeta);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (fox) {
+    bwd_forget_kernel<<<dim3((unsigned)BH), 256, 0, st>>>(b.drow, b.dcol, L, M * C, dlogf);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <typename T>
+static hipError_t dispatch_bwd(int d, int chunk, const void* q, const void* k, const void* v, const void* w,
+                               const float* beta, const float* logf, const void* out, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, void* dw, float* dbeta, float* dlogf,
+                               int64_t BH, int64_t L, float scale, const bwd_buffers& b, hipStream_t st) {
+#define PATHATTN_BWD_CASE(DD, CC)                                                                                 \
+  if (d == DD && chunk == CC)                                                                                     \
+    return launch_bwd<T, DD, CC>(q, k, v, w, beta, logf, out, lse, dout, dq, dk, dv, dw, dbeta, dlogf, BH, L, scale, \
+                                 b, st);
+  PATHATTN_BWD_CASE(16, 16)
+  PATHATTN_BWD_CASE(16, 32)
+  PATHATTN_BWD_CASE(16, 64)
+  PATHATTN_BWD_CASE(32, 16)
+  PATHATTN_BWD_CASE(32, 32)
+  PATHATTN_BWD_CASE(32, 64)
+  PATHATTN_BWD_CASE(64, 16)
+  PATHATTN_BWD_CASE(64, 32)
+  PATHATTN_BWD_CASE(64, 64)
+#undef PATHATTN_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t bwd_run(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
+                   const float* beta, const float* logf, const void* out, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, void* dw, float* dbeta, float* dlogf, int64_t BH, int64_t L,
+                   float scale, const bwd_buffers& b, hipStream_t st) {
+  if (bf16)
+    return dispatch_bwd<__bf16>(d, chunk, q, k, v, w, beta, logf, out, lse, dout, dq, dk, dv, dw, dbeta, dlogf, BH,
+                                L, scale, b, st);
+  return dispatch_bwd<float>(d, chunk, q, k, v, w, beta, logf, out, lse, dout, dq, dk, dv, dw, dbeta, dlogf, BH, L,
+                             scale, b, st);
+}
+
+}  // namespace pathattn

@@ -45,7 +45,7 @@ class WsLayout(ctypes.Structure):
 EXPORTS = ("path_abi_version", "path_status_string", "path_attn_fwd_workspace_bytes", "path_attn_fwd",
            "path_attn_prep", "path_attn_scan", "path_attn_workspace_layout", "path_decode_workspace_bytes",
            "path_decode_step", "path_attn_cache_from_prefill", "path_decode_deferred_state_bytes",
-           "path_decode_step_deferred")
+           "path_decode_step_deferred", "path_attn_bwd_workspace_bytes", "path_attn_bwd")
 
 
 def lib():
@@ -73,9 +73,12 @@ def lib():
         L.path_decode_deferred_state_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         L.path_decode_step_deferred.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, i64, i64, i32, f32, i32, i32, vp, sz, vp]
+        L.path_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(sz)]
+        L.path_attn_bwd.argtypes = [vp] * 15 + [i64, i64, i64, i32, i32, f32, i32, vp, sz, vp]
         for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd", "path_attn_prep",
                   "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step", "path_attn_cache_from_prefill",
-                  "path_decode_deferred_state_bytes", "path_decode_step_deferred"):
+                  "path_decode_deferred_state_bytes", "path_decode_step_deferred", "path_attn_bwd_workspace_bytes",
+                  "path_attn_bwd"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -312,3 +315,53 @@ def path_decode_step_deferred(kcache, vcache, t: int, t_cur: int, q_t, k_t, v_t,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     nxt = t + 1 if t - t_cur + 1 == period else t_cur
     return out, lse, nxt
+
+
+def path_attn_bwd_workspace_bytes(B, H, L, d, chunk, dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check("path_attn_bwd_workspace_bytes",
+           lib().path_attn_bwd_workspace_bytes(B, H, L, d, chunk, DTYPE[dtype], ctypes.byref(n)))
+    return n.value
+
+
+def path_attn_bwd(q, k, v, w, beta, out, lse, dout, log_forget=None, *, scale: Optional[float] = None,
+                  chunk: int = 64, workspace=None, grads=None, stream=None):
+    """Gradients of path_attn_fwd for the upstream gradient dout (loss = sum(dout * out)).
+
+    q,k,v,w,out,dout: [B,H,L,d]; beta, log_forget, lse: [B,H,L] fp32 (lse as path_attn_fwd wrote it).
+    Returns (dq, dk, dv, dw, dbeta, dlog_forget); dlog_forget is None without log_forget.  ``grads`` may
+    hold those six tensors preallocated (dlog_forget None without log_forget).
+    """
+    _require(q, "q")
+    B, H, L, d = q.shape
+    for name, t in (("k", k), ("v", v), ("w", w), ("out", out), ("dout", dout)):
+        _require(t, name, q.dtype, q.shape)
+    for name, t in (("beta", beta), ("lse", lse)):
+        _require(t, name, torch.float32, (B, H, L))
+    if log_forget is not None:
+        _require(log_forget, "log_forget", torch.float32, (B, H, L))
+    if q.dtype not in DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
+                 torch.empty((B, H, L), device=q.device, dtype=torch.float32),
+                 None if log_forget is None else torch.empty((B, H, L), device=q.device, dtype=torch.float32))
+    dq, dk, dv, dw, dbeta, dlogf = grads
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dw", dw)):
+        _require(t, name, q.dtype, q.shape)
+    _require(dbeta, "dbeta", torch.float32, (B, H, L))
+    if dlogf is not None:
+        _require(dlogf, "dlog_forget", torch.float32, (B, H, L))
+    nbytes = path_attn_bwd_workspace_bytes(B, H, L, d, chunk, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), device=q.device, dtype=torch.uint8)
+    _require(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("path_attn_bwd", lib().path_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(out), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(dbeta), _ptr(dlogf), B, H, L, d, chunk, float(scale),
+        DTYPE[q.dtype], _ptr(workspace), ws_bytes, _stream(stream)))
+    return dq, dk, dv, dw, dbeta, dlogf
+

@@ -36,6 +36,7 @@ STREAM_IDS = {
     "q": 1, "k": 2, "v": 3, "w": 4, "beta": 5, "logf": 6,
     "dec_q": 11, "dec_k": 12, "dec_v": 13, "dec_w": 14, "dec_beta": 15,
     "cache_k": 21, "cache_v": 22,
+    "dout": 31,
 }
 
 
@@ -166,6 +167,11 @@ def make_fwd_inputs(B: int, H: int, L: int, d: int, *, recipe: str = "lm", dtype
     return FwdInputs(q=q, k=k, v=v, w=w, beta=beta, logf=logf, dtype=dtype,
                      scale=(1.0 / math.sqrt(d)) if scale is None else float(scale),
                      recipe=recipe, seed=seed)
+
+
+def make_out_grad(shape, *, dtype: str = "bf16", seed: int = 0, std: float = 1.0) -> np.ndarray:
+    """Upstream gradient of the prefill output for backward tests: Gaussian, stored values of ``dtype``."""
+    return round_to(_normal(seed, "dout", tuple(shape), std), dtype)
 
 
 @dataclasses.dataclass

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 5
+#define PATH_ABI_VERSION 6
 
 typedef enum {
   PATH_OK = 0,
@@ -261,6 +261,43 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
                                          size_t workspace_bytes, void* kcache, void* vcache, float* fcache,
                                          int64_t capacity, int64_t B, int64_t H, int64_t L, int d, int chunk,
                                          int dtype, int transport, void* stream);
+
+/*
+ * Backward pass: gradients of the prefill (PaTH or PaTH-FoX) for an upstream
+ * gradient dout of its output, i.e. of the loss sum(dout * out).  The pages give
+ * the forward only (summary, sections 2 and 3; the lecture notes' "limitations"
+ * say the backward is the costlier part); this differentiates the blockwise
+ * forward with the chain rule: logits of each pair of chunks are recomputed from
+ * lse, the running queries of every (query chunk, key chunk) pair are kept in the
+ * workspace (a transition with beta = 1 is singular, so they cannot be recovered
+ * backwards), and each chunk's UT-transform terms are differentiated back to
+ * q, k, w and beta.
+ *
+ *   q, k, v, w     [B,H,L,d] dtype          the forward's inputs
+ *   beta           [B,H,L] fp32
+ *   log_forget     [B,H,L] fp32 or NULL     PaTH-FoX gates f (as in the forward)
+ *   out            [B,H,L,d] dtype          the forward's output
+ *   lse            [B,H,L] fp32             the forward's log-sum-exp (required)
+ *   dout           [B,H,L,d] dtype          upstream gradient of out
+ *   dq, dk, dv, dw [B,H,L,d] dtype          written
+ *   dbeta          [B,H,L] fp32             written
+ *   dlog_forget    [B,H,L] fp32 or NULL     written; given iff log_forget is
+ *   chunk          16, 32 or 64 (0 = 64); d 16, 32 or 64
+ *
+ * All arithmetic is fp32 (bf16 inputs are widened, gradients rounded once).
+ * Workspace: path_attn_bwd_workspace_bytes; it grows as B*H*(L/chunk)^2*chunk*d
+ * (two fp32 vectors per key of every chunk pair: about 12.7 GB at B=8, H=24,
+ * L=4096, d=64, chunk 64).  Errors as for path_attn_fwd; nothing is enqueued
+ * on an error.
+ */
+path_status path_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
+                                          size_t* bytes);
+
+path_status path_attn_bwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
+                          const float* log_forget, const void* out, const float* lse, const void* dout, void* dq,
+                          void* dk, void* dv, void* dw, float* dbeta, float* dlog_forget, int64_t B, int64_t H,
+                          int64_t L, int d, int chunk, float scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 5
+    assert L.path_abi_version() == 6
     for s in range(4):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"
@@ -205,3 +205,48 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         native.path_attn_fwd(x, x, x, x, torch.zeros(1, 1, 4))
+
+
+def bwd_call(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE,
+             dv=FAKE, dw=FAKE, dbeta=FAKE, dlogf=None, B=1, H=2, Lq=100, d=16, chunk=16, scale=0.25, dt=F32, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.path_attn_bwd(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"], a["out"], a["lse"], a["dout"],
+                           a["dq"], a["dk"], a["dv"], a["dw"], a["dbeta"], a["dlogf"], a["B"], a["H"], a["Lq"],
+                           a["d"], a["chunk"], ctypes.c_float(a["scale"]), a["dt"], a["ws"], a["ws_bytes"],
+                           a["stream"])
+
+
+def test_bwd_workspace_planning(L):
+    n = ctypes.c_size_t(0)
+    assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 64, BF16, ctypes.byref(n)) == OK
+    pairs = 64 * 63 // 2
+    assert n.value >= 2 * 8 * 24 * pairs * 64 * 64 * 4  # kept states and their gradients
+    assert n.value < 2 * 8 * 24 * pairs * 64 * 64 * 4 + (2 << 30)
+    n0 = ctypes.c_size_t(0)
+    assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 0, BF16, ctypes.byref(n0)) == OK
+    assert n0.value == n.value  # chunk 0 = 64
+    assert L.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 128, BF16, ctypes.byref(n)) == UNSUPPORTED
+    assert L.path_attn_bwd_workspace_bytes(1, 1, 64, 48, 64, F32, ctypes.byref(n)) == UNSUPPORTED
+    assert L.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 64, 9, ctypes.byref(n)) == UNSUPPORTED
+    assert L.path_attn_bwd_workspace_bytes(1, -1, 64, 64, 64, F32, ctypes.byref(n)) == INVALID
+    assert L.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 64, F32, None) == INVALID
+    assert L.path_attn_bwd_workspace_bytes(1, 1, 64, 16, 16, F32, ctypes.byref(n)) == OK  # one chunk... of 4
+    assert L.path_attn_bwd_workspace_bytes(1, 1, 16, 16, 16, F32, ctypes.byref(n)) == OK and n.value > 0
+
+
+def test_bwd_validation(L):
+    assert bwd_call(L, q=None) == INVALID
+    assert bwd_call(L, lse=None) == INVALID  # the backward needs the forward's lse
+    assert bwd_call(L, dbeta=None) == INVALID
+    assert bwd_call(L, logf=FAKE) == INVALID  # dlog_forget missing
+    assert bwd_call(L, dlogf=FAKE) == INVALID  # dlog_forget without log_forget
+    assert bwd_call(L, ws_bytes=16) == INVALID
+    assert bwd_call(L, dq=MISALIGNED) == UNSUPPORTED
+    assert bwd_call(L, d=48) == UNSUPPORTED
+    assert bwd_call(L, chunk=128) == UNSUPPORTED
+    assert bwd_call(L, dt=3) == UNSUPPORTED
+    assert bwd_call(L, Lq=-1) == INVALID
+    assert bwd_call(L, Lq=0, q=None) == OK  # empty: nothing to do
+    assert bwd_call(L, B=0) == OK

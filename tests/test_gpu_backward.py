@@ -1,0 +1,83 @@
+"""Parity of the backward pass (path_attn_bwd) against the fp64 oracle's gradients, element by element on
+seeded inputs.  The GPU forward supplies out and lse, as in a training step; the oracle differentiates its
+own exact forward.
+
+Tolerance (per gradient tensor, relative to its largest reference entry): the fp32 path keeps fp32
+throughout, so its error is fp32 rounding carried through the chunk chain; the bf16 path widens bf16
+inputs, works in fp32, and rounds each gradient to bf16 once (2^-9 relative) after using the forward's
+bf16-rounded output in D_i = dO_i . o_i, which moves every dz by up to p_ij |dO_i| |o_i| 2^-9.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dependent_positional_attention_amd import native, synth
+from tests.gpu_util import dev, errors, fwd_inputs_dev, host
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = {"f32": 1e-5, "bf16": 1.5e-2}
+NAMES = ("dq", "dk", "dv", "dw", "dbeta", "dlogf")
+
+
+def gpu_grads(x: synth.FwdInputs, dout: np.ndarray, chunk: int, fwd_chunk: int = 0):
+    t = fwd_inputs_dev(x)
+    out, lse = native.path_attn_fwd(t["q"], t["k"], t["v"], t["w"], t["beta"], t["logf"], scale=x.scale,
+                                    chunk=fwd_chunk or (64 if x.dtype == "bf16" else chunk))
+    g = native.path_attn_bwd(t["q"], t["k"], t["v"], t["w"], t["beta"], out, lse, dev(dout, x.dtype), t["logf"],
+                             scale=x.scale, chunk=chunk)
+    torch.cuda.synchronize()
+    return [None if a is None else host(a) for a in g]
+
+
+def check(x: synth.FwdInputs, chunk: int, what: str, seed: int = 0):
+    print(f"[case] backward {what} shape={x.shape} dtype={x.dtype} recipe={x.recipe} chunk={chunk}", flush=True)
+    dout = synth.make_out_grad(x.shape, dtype=x.dtype, seed=seed)
+    got = gpu_grads(x, dout, chunk)
+    want = oracle.bwd(x.q, x.k, x.v, x.w, x.beta, dout, logf=x.logf, scale=x.scale)
+    tol = GRAD_TOL[x.dtype]
+    worst = {}
+    for name, g, r in zip(NAMES, got, want):
+        if r is None:
+            assert g is None, f"{what}: {name} returned without log_forget"
+            continue
+        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite values"
+        ma, rel = errors(g, r)
+        ref = max(float(np.max(np.abs(r))), 1e-30)
+        worst[name] = (ma / ref, rel)
+        assert ma <= tol * ref and rel <= tol, \
+            f"{what} {name}: max_abs {ma:.3e} vs max|ref| {ref:.3e} (tol {tol:.0e} of it), rel_l2 {rel:.3e}"
+    print("   " + "  ".join(f"{n} {a:.1e}/{b:.1e}" for n, (a, b) in worst.items()), flush=True)
+    return got, want
+
+
+@pytest.mark.parametrize("d,chunk", [(16, 16), (32, 32), (64, 64), (16, 64), (64, 16), (32, 64)])
+@pytest.mark.parametrize("recipe", ["tiny", "fox", "beta2"])
+def test_fp32_backward_shapes(d, chunk, recipe):
+    x = synth.make_fwd_inputs(1, 2, 150, d, recipe=recipe, dtype="f32", seed=d + chunk)
+    check(x, chunk, f"f32 d={d} C={chunk}", seed=d)
+
+
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 65])
+def test_fp32_backward_ragged(L):
+    x = synth.make_fwd_inputs(1, 2, L, 16, recipe="fox", dtype="f32", seed=L)
+    check(x, 16, f"ragged L={L}", seed=L)
+
+
+def test_beta_zero_leaves_w_without_gradient():
+    """With every beta = 0 the output does not depend on w: dw must be exactly zero."""
+    x = synth.make_fwd_inputs(1, 2, 130, 32, recipe="beta0", dtype="f32", seed=4)
+    got, _ = check(x, 32, "beta0")
+    assert np.all(got[3] == 0.0)
+
+
+@pytest.mark.parametrize("recipe", ["lm", "fox", "stress_qk"])
+def test_bf16_backward(recipe):
+    x = synth.make_fwd_inputs(1, 2, 300, 64, recipe=recipe, dtype="bf16", seed=11)
+    check(x, 64, f"bf16 {recipe}", seed=12)
+
+
+def test_bf16_backward_several_heads():
+    x = synth.make_fwd_inputs(2, 3, 520, 64, recipe="fox", dtype="bf16", seed=21)
+    check(x, 64, "bf16 B=2 H=3", seed=22)
