@@ -38,6 +38,7 @@ import time
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU, dense
 HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CUs x 2.4 GHz x 128 fp32 lanes x 2 flop (FMA) per clock
 
 
 def log(*a):
@@ -59,6 +60,7 @@ def parse():
     ap.add_argument("--no-long", action="store_true", help="skip the 32K-token prefill at chunk 64 and 128")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the chunk 64 / 128 / 256 comparison")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (a known-size reference for HBM counters)")
@@ -164,7 +166,53 @@ def bench_prefill(args):
         f"whole step {F / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s")
     res = dict(B=B, H=H, L=L, d=d, C=C, recipe=recipe, ms_step=ms_step, wall_ms=wall_ms, ms_prep=ms_prep,
                ms_scan=ms_scan, flops=F, scan_tflops=tflops, tokens_per_s=B * L / (ms_step * 1e-3))
-    return res, x, dict(q=q, k=k, v=v, w=w, beta=beta, logf=logf, scale=x.scale, ws=ws)
+    return res, x, dict(q=q, k=k, v=v, w=w, beta=beta, logf=logf, scale=x.scale, ws=ws, out=out, lse=lse)
+
+
+def backward_flops(B, H, L, d, C):
+    """Algorithmic flops of the backward: the five attention products (logits, dO V^T, dV, dK, dQ:
+    2.5x the forward's two) and, per chunk pair crossed, three d x d transports (the kept state, its
+    gradient, and the reduction into dP)."""
+    M = -(-L // C)
+    return 2.5 * 4.0 * d * (L * (L + 1) / 2) * B * H + 3 * 2.0 * C * d * d * ((M - 1) * (M - 2) / 2) * B * H
+
+
+def bench_backward(args, res, ctx):
+    """Gradients of the prefill just timed (same inputs, its out and lse), for a Gaussian upstream gradient."""
+    import torch
+    from dependent_positional_attention_amd import native, synth
+
+    q, k, v, w, beta, logf, scale, out, lse = (ctx[n] for n in ("q", "k", "v", "w", "beta", "logf", "scale", "out",
+                                                                  "lse"))
+    B, H, L, d = q.shape
+    C = 64
+    dout = torch.from_numpy(synth.bf16_bits(synth.make_out_grad((B, H, L, d), dtype="bf16", seed=0)).view("int16")
+                            ).view(torch.bfloat16).cuda()
+    nbytes = native.path_attn_bwd_workspace_bytes(B, H, L, d, C, torch.bfloat16)
+    ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
+    grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
+             torch.empty((B, H, L), device="cuda", dtype=torch.float32),
+             None if logf is None else torch.empty((B, H, L), device="cuda", dtype=torch.float32))
+
+    def run():
+        native.path_attn_bwd(q, k, v, w, beta, out, lse, dout, logf, scale=scale, chunk=C, workspace=ws, grads=grads)
+
+    run()
+    torch.cuda.synchronize()
+    n = 3
+    ms = timed(run, n)
+    for g in grads:
+        if g is not None:
+            assert torch.isfinite(g.float()).all(), "non-finite gradient"
+    F = backward_flops(B, H, L, d, C)
+    tf = F / (ms * 1e-3) / 1e12
+    log(f"[bench] backward: {ms:.2f} ms, {B * L / (ms * 1e-3) / 1e6:.3f} M tokens/s, {tf:.2f} TFLOP/s = "
+        f"{tf / FP32_VECTOR_PEAK_TFLOPS:.3f} of fp32 vector peak (workspace {nbytes / 2**30:.1f} GiB)")
+    del ws
+    return {"workload": f"PaTH backward, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16 in/out, fp32 arithmetic",
+            "ms": ms, "steps": n, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf, "bound": "alu",
+            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / FP32_VECTOR_PEAK_TFLOPS,
+            "workspace_bytes": nbytes}
 
 
 def bench_handoff(args, res, ctx):
@@ -450,6 +498,7 @@ def main():
     handoff = bench_handoff(args, res, ctx)
     sweep = None if args.no_sweep else bench_chunks(args, ctx)
     fox = None if (args.no_sweep or args.fox) else bench_fox(args, ctx)
+    bwd = None if args.no_backward else bench_backward(args, res, ctx)
     del ctx
     cpu = None if args.no_cpu else bench_cpu(x, args)
     dec = None if args.no_decode else bench_decode(args)
@@ -487,6 +536,7 @@ def main():
         "cache_handoff": handoff,
         "chunk_sweep": sweep,
         "fox_prefill": fox,
+        "backward": bwd,
         "long_context": long_ctx,
     }
     print(json.dumps(line), flush=True)
