@@ -410,6 +410,376 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
   for (int b = tid; b < C; b += 256) dcol[rown + b] = cs[b];
 }
 
+// ------------------------------------------------------------------------------- matrix-core variants
+// C = D = 64: the 64 x 64 x 64 products of the two chunk-pair kernels above run on the fp32 matrix
+// cores (16x16x4), so the fp32 accuracy is kept.  Four waves; wave w owns output rows 16w .. 16w+15.
+// Tiles are row-major in LDS with a 68-float row stride (16-byte aligned rows).  In one 16x16x4 step
+// lane (r, g) (r = lane % 16, g = lane / 16) brings A[row r][slot g] and B[slot g][col r], and holds
+// D[4g + e][r] (e = 0..3) of the accumulator; within 16-wide k blocks slot g of step j is
+// k = k0 + 4g + j, so an operand stored k-contiguous is read as one float4.
+namespace {
+
+constexpr int kS = 68;  // LDS row stride (floats) of the 64-wide tiles
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc[cb] += sum_{k<64} A(16w + r', k) B(k, 16cb + r'') over the wave's strip.
+//   AT = false: A(i, k) = A[i][k] (float4 reads)    AT = true: A(i, k) = A[k][i]
+//   BK = false: B(k, j) = B[j][k] (float4 reads)    BK = true: B(k, j) = B[k][j]
+template <bool AT, bool BK>
+__device__ __forceinline__ void mm64(f32x4 (&acc)[4], const float* __restrict__ A, const float* __restrict__ B,
+                                     int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll 2
+  for (int k0 = 0; k0 < 64; k0 += 16) {
+    float a[4];
+    if constexpr (!AT) {
+      const float4 v = *reinterpret_cast<const float4*>(A + (16 * w + r) * kS + k0 + 4 * g);
+      a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = A[(k0 + 4 * g + j) * kS + 16 * w + r];
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      float b[4];
+      if constexpr (!BK) {
+        const float4 v = *reinterpret_cast<const float4*>(B + (16 * cb + r) * kS + k0 + 4 * g);
+        b[0] = v.x, b[1] = v.y, b[2] = v.z, b[3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = B[(k0 + 4 * g + j) * kS + 16 * cb + r];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[cb] = mfma4(a[j], b[j], acc[cb]);
+    }
+  }
+}
+
+__device__ __forceinline__ void zero4(f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// accumulator layout <-> row-major 64 x 64 (LDS stride kS, or global stride 64)
+__device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[4], float* T, int w, int lane, float mul = 1.f) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) T[(16 * w + 4 * g + e) * kS + 16 * cb + r] = mul * acc[cb][e];
+}
+__device__ __forceinline__ void acc_to_global(const f32x4 (&acc)[4], float* T, int w, int lane, float mul = 1.f) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) T[(16 * w + 4 * g + e) * 64 + 16 * cb + r] = mul * acc[cb][e];
+}
+__device__ __forceinline__ void global_to_acc(f32x4 (&acc)[4], const float* T, int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[cb][e] = T[(16 * w + 4 * g + e) * 64 + 16 * cb + r];
+}
+
+// 64 x 64 fp32 tile from global (row stride 64) into LDS (stride kS), float4 loads.
+__device__ __forceinline__ void tile_f32(float* dst, const float* __restrict__ src, int tid) {
+  for (int e = tid; e < 64 * 16; e += 256) {
+    const int row = e >> 4, c4 = (e & 15) * 4;
+    *reinterpret_cast<float4*>(dst + row * kS + c4) = *reinterpret_cast<const float4*>(src + row * 64 + c4);
+  }
+}
+
+// 64 rows of a [.., L, 64] input starting at row c0 (rows >= L read as zero), widened to fp32.
+template <typename T>
+__device__ __forceinline__ void tile_rows(float* dst, const T* __restrict__ src, int64_t c0, int64_t L, int tid) {
+  for (int e = tid; e < 64 * 16; e += 256) {
+    const int row = e >> 4, c4 = (e & 15) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c0 + row < L) {
+      const T* p = src + (size_t)(c0 + row) * 64 + c4;
+      v = make_float4(to_f32(p[0]), to_f32(p[1]), to_f32(p[2]), to_f32(p[3]));
+    }
+    *reinterpret_cast<float4*>(dst + row * kS + c4) = v;
+  }
+}
+
+constexpr size_t kLdsPairMfma = sizeof(float) * (7 * 64 * kS + 3 * 64);
+
+}  // namespace
+
+// Query-chunk kernel on the matrix cores (same outputs as bwd_query_kernel<T, 64, 64>).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
+    const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
+    const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
+    const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
+    int64_t L, int64_t M, float scale, float* __restrict__ St, float* __restrict__ Gst, float* __restrict__ Off,
+    float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow, float* __restrict__ dqt,
+    float* __restrict__ dSm) {
+  constexpr int C = 64, CD = 64 * 64;
+  extern __shared__ float sm[];
+  float* Rs = sm;           // r^(n)       [64][kS]
+  float* Ks = Rs + C * kS;  // ktilde_n
+  float* Vs = Ks + C * kS;  // v_n
+  float* Os = Vs + C * kS;  // dO_m
+  float* Qd = Os + C * kS;  // dr^(n-1)
+  float* Ps = Qd + C * kS;  // P_n
+  float* Gs = Ps + C * kS;  // ln2 * dz
+  float* l2 = Gs + C * kS;
+  float* Dv = l2 + C;
+  float* Fn = Dv + C;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int64_t m = (int64_t)gridDim.x - 1 - blockIdx.x;
+  const int64_t bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const bool fox = fl != nullptr;
+  const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
+  const T* vb = v + (size_t)bh * L * 64;
+
+  tile_rows(Os, dout + (size_t)bh * L * 64, m * C, L, tid);
+  __syncthreads();
+  if (tid < C) {
+    const int a = tid;
+    const int64_t i = m * C + a;
+    float dv = 0.f, l2v = INFINITY;  // padded rows: p = 0
+    if (i < L) {
+      const T* orow = out + ((size_t)bh * L + i) * 64;
+#pragma unroll 8
+      for (int x = 0; x < 64; ++x) dv += Os[a * kS + x] * to_f32(orow[x]);
+      l2v = kLog2e * (lse[bh * L + i] - (fox ? fl[row0 + a] : 0.f));
+    }
+    Dv[a] = dv;
+    l2[a] = l2v;
+    lse2w[row0 + a] = l2v;
+    Dw[row0 + a] = dv;
+  }
+
+  // pass 1: states r^(n), n = m-1 .. 0
+  f32x4 R[4], G[4];
+  global_to_acc(R, qt + row0 * 64, w, lane);
+  zero4(G);
+  float off = 0.f;
+  for (int64_t n = m - 1; n >= 0; --n) {
+    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    if (fox) off += ftot[bh * M + n];
+    if (tid == 0) Off[pr] = off;
+    acc_to_global(R, St + pr * CD, w, lane);
+    if (n > 0) {
+      acc_to_lds(R, Rs, w, lane);
+      tile_f32(Ps, Pm + ((size_t)bh * M + n) * CD, tid);
+      __syncthreads();
+      zero4(R);
+      mm64<false, false>(R, Rs, Ps, w, lane);  // r P_n^T
+      __syncthreads();
+    }
+  }
+
+  // in-chunk block: logits from S, D = dO_m V_m^T on the matrix cores
+  tile_rows(Vs, vb, m * C, L, tid);
+  if (fox && tid < C) Fn[tid] = fl[row0 + tid];
+  __syncthreads();
+  float rsum[4] = {0.f, 0.f, 0.f, 0.f};  // rows 16w + 4g + e, partial over this lane's columns
+  {
+    f32x4 DP[4];
+    zero4(DP);
+    mm64<false, false>(DP, Os, Vs, w, lane);
+    const float* Sc = Sm + ((size_t)bh * M + m) * C * C;
+    float* dSc = dSm + ((size_t)bh * M + m) * C * C;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * w + 4 * g + e, b = 16 * cb + r;
+        float dz = 0.f;
+        if (b <= a) {
+          const float z2 = Sc[a * C + b] - (fox ? kLog2e * Fn[b] : 0.f);
+          dz = fast_exp2(z2 - l2[a]) * (DP[cb][e] - Dv[a]);
+        }
+        rsum[e] += dz;
+        dSc[a * C + b] = scale * dz;
+      }
+  }
+
+  // pass 2: n = 0 .. m-1
+  for (int64_t n = 0; n < m; ++n) {
+    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    __syncthreads();
+    tile_f32(Rs, St + pr * CD, tid);
+    tile_f32(Ks, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
+    tile_rows(Vs, vb, n * C, L, tid);
+    if (n > 0) {
+      tile_f32(Ps, Pm + ((size_t)bh * M + n) * CD, tid);
+      acc_to_lds(G, Qd, w, lane);
+      acc_to_global(G, Gst + pr * CD, w, lane);
+    }
+    if (fox && tid < C) Fn[tid] = fl[(size_t)bh * Lp + (size_t)n * C + tid];
+    const float offn = fox ? Off[pr] : 0.f;
+    __syncthreads();
+    f32x4 Z[4], DP[4];
+    zero4(Z);
+    zero4(DP);
+    mm64<false, false>(Z, Rs, Ks, w, lane);
+    mm64<false, false>(DP, Os, Vs, w, lane);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * w + 4 * g + e, b = 16 * cb + r;
+        const float z2 = Z[cb][e] + (fox ? kLog2e * (offn - Fn[b]) : 0.f);
+        const float dz = fast_exp2(z2 - l2[a]) * (DP[cb][e] - Dv[a]);
+        rsum[e] += dz;
+        Gs[a * kS + b] = kLn2 * dz;
+      }
+    __syncthreads();
+    zero4(G);
+    if (n > 0) mm64<false, true>(G, Qd, Ps, w, lane);  // dr^(n-1) P_n
+    mm64<false, true>(G, Gs, Ks, w, lane);              // + g ktilde_n
+  }
+
+  acc_to_global(G, dqt + row0 * 64, w, lane, scale * kLog2e);  // qtilde entered the scan scaled
+  // row sums: reduce over the 16 lanes that share g
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float s = rsum[e];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 8);
+    if (r == 0) drow[row0 + 16 * w + 4 * g + e] = s;
+  }
+}
+
+// Key-chunk kernel on the matrix cores (same outputs as bwd_key_kernel<T, 64, 64>).  The logits of a
+// pair are formed transposed (rows = keys of chunk n), so that p and g are stored k-contiguous for
+// the products that reduce over the queries.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_key_mfma_kernel(
+    const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
+    const T* __restrict__ v, const T* __restrict__ dout, const float* __restrict__ St, const float* __restrict__ Gst,
+    const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
+    int64_t M, T* __restrict__ dv, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol) {
+  constexpr int C = 64, CD = 64 * 64;
+  extern __shared__ float sm[];
+  float* Ks = sm;           // ktilde_n       [64][kS]
+  float* Vs = Ks + C * kS;  // v_n
+  float* Rs = Vs + C * kS;  // r^(n)_m
+  float* Os = Rs + C * kS;  // dO_m
+  float* Gq = Os + C * kS;  // dr^(n-1)_m
+  float* PT = Gq + C * kS;  // p^T     [key][query]
+  float* GT = PT + C * kS;  // (ln2 dz)^T
+  float* l2 = GT + C * kS;
+  float* Dv = l2 + C;
+  float* Fn = Dv + C;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int64_t n = blockIdx.x, bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const bool fox = fl != nullptr;
+  const size_t rown = (size_t)bh * Lp + (size_t)n * C;
+  const T* vb = v + (size_t)bh * L * 64;
+  const T* ob = dout + (size_t)bh * L * 64;
+
+  auto stats = [&](int64_t mm) PA_INLINE {
+    if (tid < C) {
+      const size_t r0 = (size_t)bh * Lp + (size_t)mm * C;
+      l2[tid] = lse2w[r0 + tid];
+      Dv[tid] = Dw[r0 + tid];
+    }
+  };
+
+  tile_f32(Ks, kt + rown * 64, tid);
+  tile_rows(Vs, vb, n * C, L, tid);
+  tile_rows(Os, ob, n * C, L, tid);
+  if (tid < C) Fn[tid] = fox ? fl[rown + tid] : 0.f;
+  stats(n);
+  __syncthreads();
+
+  f32x4 aV[4], aK[4], aP[4];
+  zero4(aV);
+  zero4(aK);
+  zero4(aP);
+  float csum[4] = {0.f, 0.f, 0.f, 0.f};  // key rows 16w + 4g + e
+
+  // in-chunk block (m = n): D^T = V dO^T on the matrix cores, logits from S
+  {
+    f32x4 DT[4];
+    zero4(DT);
+    mm64<false, false>(DT, Vs, Os, w, lane);
+    const float* Sc = Sm + ((size_t)bh * M + n) * C * C;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b = 16 * w + 4 * g + e, a = 16 * cb + r;
+        float p = 0.f, dz = 0.f;
+        if (b <= a) {
+          const float z2 = Sc[a * C + b] - (fox ? kLog2e * Fn[b] : 0.f);
+          p = fast_exp2(z2 - l2[a]);
+          dz = p * (DT[cb][e] - Dv[a]);
+        }
+        csum[e] += dz;
+        PT[b * kS + a] = p;
+      }
+  }
+  __syncthreads();
+  mm64<false, true>(aV, PT, Os, w, lane);  // dv_n += p^T dO_n
+
+  for (int64_t m = n + 1; m < M; ++m) {
+    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    __syncthreads();
+    tile_f32(Rs, St + pr * CD, tid);
+    if (n > 0) tile_f32(Gq, Gst + pr * CD, tid);
+    tile_rows(Os, ob, m * C, L, tid);
+    stats(m);
+    const float offn = fox ? Off[pr] : 0.f;
+    __syncthreads();
+    f32x4 ZT[4], DT[4];
+    zero4(ZT);
+    zero4(DT);
+    mm64<false, false>(ZT, Ks, Rs, w, lane);  // (r ktilde^T)^T
+    mm64<false, false>(DT, Vs, Os, w, lane);  // (dO v^T)^T
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b = 16 * w + 4 * g + e, a = 16 * cb + r;
+        const float z2 = ZT[cb][e] + (fox ? kLog2e * (offn - Fn[b]) : 0.f);
+        const float p = fast_exp2(z2 - l2[a]);
+        const float dz = p * (DT[cb][e] - Dv[a]);
+        csum[e] += dz;
+        PT[b * kS + a] = p;
+        GT[b * kS + a] = kLn2 * dz;
+      }
+    __syncthreads();
+    mm64<false, true>(aV, PT, Os, w, lane);               // dv_n += p^T dO_m
+    mm64<false, true>(aK, GT, Rs, w, lane);               // d ktilde_n += g^T r
+    if (n > 0) mm64<true, true>(aP, Gq, Rs, w, lane);     // dP_n += dr^(n-1)^T r
+  }
+
+  acc_to_global(aK, dkt + rown * 64, w, lane);
+  acc_to_global(aP, dPm + ((size_t)bh * M + n) * CD, w, lane);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 16 * w + 4 * g + e;
+      if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * 64 + 16 * cb + r] = from_f32<T>(aV[cb][e]);
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float s = csum[e];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 8);
+    if (r == 0) dcol[rown + 16 * w + 4 * g + e] = s;
+  }
+}
+
 // ------------------------------------------------------------------------------- UT-transform terms
 // One block per (chunk c, batch*head): from d qtilde, d ktilde, dP and dS of the chunk to dq, dk, dw,
 // dbeta.  Nine LDS tiles; the C x C intermediates pass through registers where a tile is rewritten.
@@ -792,23 +1162,42 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   const dim3 grid((unsigned)M, (unsigned)BH);
   hipError_t e;
   const bool fox = logf != nullptr;
-  e = hipFuncSetAttribute((const void*)bwd_query_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)S::lds_query);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)bwd_key_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)S::lds_key);
-  if (e != hipSuccess) return e;
+  if constexpr (!(D == 64 && C == 64)) {
+    e = hipFuncSetAttribute((const void*)bwd_query_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)S::lds_query);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)bwd_key_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)S::lds_key);
+    if (e != hipSuccess) return e;
+  }
   e = hipFuncSetAttribute((const void*)bwd_prep_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)S::lds_prep);
   if (e != hipSuccess) return e;
-  bwd_query_kernel<T, D, C><<<grid, 256, S::lds_query, st>>>(
-      b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
-      scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_key_kernel<T, D, C><<<grid, 256, S::lds_key, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
-                                                        (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
-                                                        (T*)dv, b.dkt, b.dPm, b.dcol);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (D == 64 && C == 64) {  // the chunk-pair kernels on the matrix cores
+    e = hipFuncSetAttribute((const void*)bwd_query_mfma_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsPairMfma);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)bwd_key_mfma_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsPairMfma);
+    if (e != hipSuccess) return e;
+    bwd_query_mfma_kernel<T><<<grid, 256, kLdsPairMfma, st>>>(
+        b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
+        scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_key_mfma_kernel<T><<<grid, 256, kLdsPairMfma, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
+                                                            (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
+                                                            (T*)dv, b.dkt, b.dPm, b.dcol);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    bwd_query_kernel<T, D, C><<<grid, 256, S::lds_query, st>>>(
+        b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
+        scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_key_kernel<T, D, C><<<grid, 256, S::lds_key, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
+                                                          (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
+                                                          (T*)dv, b.dkt, b.dPm, b.dcol);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   bwd_prep_kernel<T, D, C><<<grid, 256, S::lds_prep, st>>>((const T*)q, (const T*)k, (const T*)w, beta, b.dqt,
                                                           b.dkt, b.dPm, b.dSm, L, M, (T*)dq, (T*)dk, (T*)dw,
                                                           dbeta);
