@@ -403,13 +403,8 @@ path_status path_attn_bwd(const void* q, const void* k, const void* v, const voi
                       f(9), f(10), f(11), f(12), f(13), f(14), f(15), f(16)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == PATH_DTYPE_BF16;
-  // the forward's per-chunk terms, fp32, as the vector path builds them
-  hipError_t e = vec_run(kPhasePrep, bf16, d, chunk, q, k, v, w, beta, log_forget, nullptr, nullptr, BH, L, scale,
-                         b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot, st);
-  if (e == hipSuccess)
-    e = bwd_run(bf16, d, chunk, q, k, v, w, beta, log_forget, out, lse, dout, dq, dk, dv, dw, dbeta, dlog_forget, BH,
-                L, scale, b, st);
-  return from_hip(e);
+  return from_hip(bwd_run(bf16, d, chunk, q, k, v, w, beta, log_forget, out, lse, dout, dq, dk, dv, dw, dbeta,
+                          dlog_forget, BH, L, scale, b, st));
 }
 
 }  // extern "C"

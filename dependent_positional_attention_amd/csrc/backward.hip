@@ -29,6 +29,8 @@
 //   dQ  = dqtilde + dS K + dU^T W,   dK = dktilde + dS^T Q + dR W
 //
 // PaTH-FoX: z_ij carries F_i - F_j, so dF_t = sum_j dz_tj - sum_i dz_it and df_s = sum_{t >= s} dF_t.
+#include <type_traits>
+
 #include "common.h"
 
 namespace pathattn {
@@ -425,10 +427,11 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// acc[cb] += sum_{k<64} A(16w + r', k) B(k, 16cb + r'') over the wave's strip.
+// acc[cb] += sum_{k<64} A(16w + r', k) B(k, 16cb + r'') over the wave's strip; SA, SB are the
+// operands' row strides (kS for LDS tiles, 64 for fp32 tiles read straight from global memory).
 //   AT = false: A(i, k) = A[i][k] (float4 reads)    AT = true: A(i, k) = A[k][i]
 //   BK = false: B(k, j) = B[j][k] (float4 reads)    BK = true: B(k, j) = B[k][j]
-template <bool AT, bool BK>
+template <bool AT, bool BK, int SA = kS, int SB = kS>
 __device__ __forceinline__ void mm64(f32x4 (&acc)[4], const float* __restrict__ A, const float* __restrict__ B,
                                      int w, int lane) {
   const int r = lane & 15, g = lane >> 4;
@@ -436,21 +439,21 @@ __device__ __forceinline__ void mm64(f32x4 (&acc)[4], const float* __restrict__ 
   for (int k0 = 0; k0 < 64; k0 += 16) {
     float a[4];
     if constexpr (!AT) {
-      const float4 v = *reinterpret_cast<const float4*>(A + (16 * w + r) * kS + k0 + 4 * g);
+      const float4 v = *reinterpret_cast<const float4*>(A + (16 * w + r) * SA + k0 + 4 * g);
       a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[j] = A[(k0 + 4 * g + j) * kS + 16 * w + r];
+      for (int j = 0; j < 4; ++j) a[j] = A[(k0 + 4 * g + j) * SA + 16 * w + r];
     }
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       float b[4];
       if constexpr (!BK) {
-        const float4 v = *reinterpret_cast<const float4*>(B + (16 * cb + r) * kS + k0 + 4 * g);
+        const float4 v = *reinterpret_cast<const float4*>(B + (16 * cb + r) * SB + k0 + 4 * g);
         b[0] = v.x, b[1] = v.y, b[2] = v.z, b[3] = v.w;
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = B[(k0 + 4 * g + j) * kS + 16 * cb + r];
+        for (int j = 0; j < 4; ++j) b[j] = B[(k0 + 4 * g + j) * SB + 16 * cb + r];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[cb] = mfma4(a[j], b[j], acc[cb]);
@@ -778,6 +781,331 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(
     s += __shfl_xor(s, 8);
     if (r == 0) dcol[rown + 16 * w + 4 * g + e] = s;
   }
+}
+
+// ------------------------------------------------------------------------------- per-chunk terms, matrix cores
+namespace {
+
+constexpr int kT = 64 * kS;                                     // one 64 x 64 LDS tile
+constexpr size_t kLdsChunkMfma = sizeof(float) * (9 * kT + 2 * 64);     // gradient kernel
+constexpr size_t kLdsChunkFwdMfma = sizeof(float) * (8 * kT + 64);   // forward-terms kernel
+
+// Element (i, j) of the accumulator layout: i = 16w + 4g + e, j = 16cb + r.
+template <typename F>
+__device__ __forceinline__ void acc_store(const f32x4 (&acc)[4], float* T, int w, int lane, F f) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e, j = 16 * cb + r;
+      T[i * kS + j] = f(i, j, acc[cb][e]);
+    }
+}
+
+__device__ __forceinline__ void sub4(f32x4 (&acc)[4], const f32x4 (&t)[4]) {
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] -= t[cb];
+}
+
+// A = I + diag(beta) strict_upper(W W^T) is read from tile Aa (only r < s), A^{-1} written to Ai
+// (unit upper triangular, zeros below) by back substitution, one column per thread.
+__device__ __forceinline__ void unit_upper_inverse(const float* Aa, float* Ai, int tid) {
+  if (tid < 64) {
+    const int j = tid;
+    for (int i = 63; i > j; --i) Ai[i * kS + j] = 0.f;
+    Ai[j * kS + j] = 1.f;
+    for (int i = j - 1; i >= 0; --i) {
+      float s = 0.f;
+      for (int kk = i + 1; kk <= j; ++kk) s += Aa[i * kS + kk] * Ai[kk * kS + j];
+      Ai[i * kS + j] = -s;
+    }
+  }
+}
+
+// W, Q, K of chunk c (rows >= L zero), beta, then A (into Aa), U (t <= a), R (s > b).
+template <typename T>
+__device__ __forceinline__ void chunk_setup(const T* q, const T* k, const T* w, const float* beta, int64_t bh,
+                                            int64_t c, int64_t L, float* Wt, float* Qt, float* Kt, float* Aa,
+                                            float* Ut, float* Rt, float* Bs, int tid, int wv, int lane) {
+  const size_t base = (size_t)bh * L * 64;
+  tile_rows(Wt, w + base, c * 64, L, tid);
+  tile_rows(Qt, q + base, c * 64, L, tid);
+  tile_rows(Kt, k + base, c * 64, L, tid);
+  if (tid < 64) Bs[tid] = c * 64 + tid < L ? beta[bh * L + c * 64 + tid] : 0.f;  // padded: identity
+  __syncthreads();
+  f32x4 t[4];
+  zero4(t);
+  mm64<false, false>(t, Wt, Wt, wv, lane);  // w_r . w_s
+  acc_store(t, Aa, wv, lane, [&](int i, int j, float x) { return i < j ? Bs[i] * x : 0.f; });
+  zero4(t);
+  mm64<false, false>(t, Wt, Qt, wv, lane);  // w_t . q_a
+  acc_store(t, Ut, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; });
+  zero4(t);
+  mm64<false, false>(t, Kt, Wt, wv, lane);  // k_b . w_s
+  acc_store(t, Rt, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; });
+}
+
+}  // namespace
+
+// The forward's per-chunk terms in fp32 (the same outputs as vec_prep_kernel<T, 64, 64>): qtilde and S
+// scaled by qscale = scale * log2e, ktilde, P_c, FoX local prefix and chunk totals.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ w, const float* __restrict__ beta,
+    const float* __restrict__ logf, int64_t L, int64_t M, float qscale, float* __restrict__ qt,
+    float* __restrict__ kt, float* __restrict__ Pm, float* __restrict__ Sm, float* __restrict__ fl,
+    float* __restrict__ ftot) {
+  extern __shared__ float sm[];
+  float* Wt = sm;
+  float* Qt = Wt + kT;
+  float* Kt = Qt + kT;
+  float* Ta = Kt + kT;  // A, then Ti
+  float* Ai = Ta + kT;  // A^{-1}, then Y
+  float* Ut = Ai + kT;
+  float* Rt = Ut + kT;  // R, then Z2 = Ti W
+  float* Xt = Rt + kT;
+  float* Bs = Xt + kT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t c = blockIdx.x, bh = blockIdx.y, Lp = M * 64;
+  const size_t row0 = (size_t)bh * Lp + (size_t)c * 64;
+
+  if (logf != nullptr && tid == 0) {
+    float s = 0.f;
+    for (int a = 0; a < 64; ++a) {
+      const int64_t i = c * 64 + a;
+      s += i < L ? logf[bh * L + i] : 0.f;
+      fl[row0 + a] = s;
+    }
+    ftot[bh * M + c] = s;
+  }
+  chunk_setup(q, k, w, beta, bh, c, L, Wt, Qt, Kt, Ta, Ut, Rt, Bs, tid, wv, lane);
+  __syncthreads();
+  unit_upper_inverse(Ta, Ai, tid);
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += 256) Ta[(e >> 6) * kS + (e & 63)] = Ai[(e >> 6) * kS + (e & 63)] * Bs[e & 63];
+  __syncthreads();
+  f32x4 t[4], u[4];
+  zero4(t);
+  mm64<false, true>(t, Ta, Ut, wv, lane);  // X = Ti U
+  acc_store(t, Xt, wv, lane, [](int, int, float x) { return x; });
+  zero4(u);
+  mm64<false, true>(u, Rt, Ta, wv, lane);  // Y = R Ti
+  zero4(t);
+  mm64<false, true>(t, Ta, Wt, wv, lane);  // Z2 = Ti W
+  __syncthreads();
+  acc_store(u, Ai, wv, lane, [](int, int, float x) { return x; });  // Y
+  acc_store(t, Rt, wv, lane, [](int, int, float x) { return x; });  // Z2
+  __syncthreads();
+  // S[a][b] = q_a . k_b - (Y U)[b][a] for b <= a
+  zero4(t);
+  mm64<false, false>(t, Qt, Kt, wv, lane);
+  zero4(u);
+  mm64<true, false>(u, Ut, Ai, wv, lane);
+  sub4(t, u);
+  {
+    const int r = lane & 15, g = lane >> 4;
+    float* Sc = Sm + ((size_t)bh * M + c) * 64 * 64;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * wv + 4 * g + e, b = 16 * cb + r;
+        Sc[a * 64 + b] = b <= a ? qscale * t[cb][e] : 0.f;
+      }
+  }
+  // qtilde = Q - X^T W (scaled), ktilde = K - Y W, P = I - W^T Z2
+  zero4(t);
+  mm64<true, true>(t, Xt, Wt, wv, lane);
+  {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 16 * wv + 4 * g + e, x = 16 * cb + r;
+        qt[(row0 + a) * 64 + x] = qscale * (Qt[a * kS + x] - t[cb][e]);
+      }
+  }
+  zero4(t);
+  mm64<false, true>(t, Ai, Wt, wv, lane);
+  {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b = 16 * wv + 4 * g + e, x = 16 * cb + r;
+        kt[(row0 + b) * 64 + x] = Kt[b * kS + x] - t[cb][e];
+      }
+  }
+  zero4(t);
+  mm64<true, true>(t, Wt, Rt, wv, lane);
+  {
+    const int r = lane & 15, g = lane >> 4;
+    float* Pc = Pm + ((size_t)bh * M + c) * 64 * 64;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = 16 * wv + 4 * g + e, y = 16 * cb + r;
+        Pc[x * 64 + y] = (x == y ? 1.f : 0.f) - t[cb][e];
+      }
+  }
+}
+
+// Gradients of the per-chunk terms back to q, k, w, beta (the same outputs as bwd_prep_kernel<T, 64, 64>).
+// d qtilde, d ktilde, dS and dP are read straight from global memory (fp32 tiles, row stride 64).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ w, const float* __restrict__ beta,
+    const float* __restrict__ dqt, const float* __restrict__ dkt, const float* __restrict__ dPm,
+    const float* __restrict__ dSm, int64_t L, int64_t M, T* __restrict__ dq, T* __restrict__ dk,
+    T* __restrict__ dw, float* __restrict__ dbeta) {
+  extern __shared__ float sm[];
+  float* S0 = sm;        // W
+  float* S1 = S0 + kT;   // Q
+  float* S2 = S1 + kT;   // K
+  float* S3 = S2 + kT;   // A, then Ti
+  float* S4 = S3 + kT;   // U, dU, dTi
+  float* S5 = S4 + kT;   // R, dR, M1
+  float* S6 = S5 + kT;   // A^{-1}
+  float* S7 = S6 + kT;   // X, dX, W dP, dN
+  float* S8 = S7 + kT;   // Y, dY, W dP^T
+  float* Bs = S8 + kT;
+  float* dB = Bs + 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int64_t c = blockIdx.x, bh = blockIdx.y, Lp = M * 64;
+  const size_t row0 = (size_t)bh * Lp + (size_t)c * 64;
+  const float* dQ = dqt + row0 * 64;                         // d qtilde  [a][x]
+  const float* dK = dkt + row0 * 64;                         // d ktilde  [b][x]
+  const float* dS = dSm + ((size_t)bh * M + c) * 64 * 64;   // dS        [a][b]
+  const float* dP = dPm + ((size_t)bh * M + c) * 64 * 64;   // dP        [x][y]
+
+  if (tid < 64) dB[tid] = 0.f;
+  chunk_setup(q, k, w, beta, bh, c, L, S0, S1, S2, S3, S4, S5, Bs, tid, wv, lane);
+  __syncthreads();
+  unit_upper_inverse(S3, S6, tid);
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += 256) S3[(e >> 6) * kS + (e & 63)] = S6[(e >> 6) * kS + (e & 63)] * Bs[e & 63];
+  __syncthreads();
+
+  auto keep = [](int, int, float x) { return x; };
+  auto neg = [](int, int, float x) { return -x; };
+  f32x4 aq[4], ak[4], aw[4], t[4], u[4], rU[4], rG[4];
+  global_to_acc(aq, dQ, wv, lane);  // dq = d qtilde + ...
+  global_to_acc(ak, dK, wv, lane);  // dk = d ktilde + ...
+  zero4(aw);
+  zero4(t);
+  mm64<false, true>(t, S3, S4, wv, lane);  // X = Ti U
+  acc_store(t, S7, wv, lane, keep);
+  zero4(t);
+  mm64<false, true>(t, S5, S3, wv, lane);  // Y = R Ti
+  acc_store(t, S8, wv, lane, keep);
+  mm64<false, true, 64, kS>(aq, dS, S2, wv, lane);  // dq += dS K
+  mm64<true, true, 64, kS>(ak, dS, S1, wv, lane);   // dk += dS^T Q
+  __syncthreads();
+  zero4(t);
+  mm64<false, true, kS, 64>(t, S7, dQ, wv, lane);  // X dqtilde
+  mm64<true, true, kS, 64>(t, S8, dK, wv, lane);   // + Y^T dktilde
+  sub4(aw, t);
+  zero4(u);
+  mm64<false, false, kS, 64>(u, S0, dQ, wv, lane);  // -dX = W dqtilde^T
+  zero4(t);
+  mm64<false, false, 64, kS>(t, dK, S0, wv, lane);  // -dY = dktilde W^T
+  mm64<true, false, 64, kS>(t, dS, S4, wv, lane);   //       + dS^T U^T
+  zero4(rU);
+  mm64<true, false, kS, 64>(rU, S8, dS, wv, lane);  // (dS Y)^T
+  __syncthreads();
+  acc_store(u, S7, wv, lane, neg);  // dX
+  acc_store(t, S8, wv, lane, neg);  // dY
+  __syncthreads();
+  zero4(u);
+  mm64<true, true>(u, S3, S7, wv, lane);  // dU = Ti^T dX - (dS Y)^T
+  sub4(u, rU);
+  zero4(rG);
+  mm64<false, false>(rG, S7, S4, wv, lane);  // dTi = dX U^T
+  mm64<true, true>(rG, S5, S8, wv, lane);    //     + R^T dY
+  zero4(t);
+  mm64<false, false>(t, S8, S3, wv, lane);  // dR = dY Ti^T
+  __syncthreads();
+  acc_store(u, S4, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; });
+  acc_store(t, S5, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; });
+  __syncthreads();
+  mm64<false, true>(aw, S4, S1, wv, lane);  // dW += dU Q
+  mm64<true, true>(aw, S5, S2, wv, lane);   //     + dR^T K
+  mm64<true, true>(aq, S4, S0, wv, lane);   // dq += dU^T W
+  mm64<false, true>(ak, S5, S0, wv, lane);  // dk += dR W
+  zero4(t);
+  mm64<false, true, kS, 64>(t, S0, dP, wv, lane);  // W dP
+  zero4(u);
+  mm64<false, false, kS, 64>(u, S0, dP, wv, lane);  // W dP^T
+  acc_store(t, S7, wv, lane, keep);
+  acc_store(u, S8, wv, lane, keep);
+  __syncthreads();
+  zero4(t);
+  mm64<false, false>(t, S7, S0, wv, lane);  // dTi -= W dP W^T
+  sub4(rG, t);
+  zero4(t);
+  mm64<false, true>(t, S3, S8, wv, lane);  // dW -= Ti W dP^T
+  mm64<true, true>(t, S3, S7, wv, lane);   //      + Ti^T W dP
+  sub4(aw, t);
+  __syncthreads();
+  acc_store(rG, S4, wv, lane, keep);
+  __syncthreads();
+  zero4(t);
+  mm64<true, true>(t, S6, S4, wv, lane);  // M1 = A^{-T} dTi; dbeta += diag(M1)
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (16 * wv + 4 * g + e == 16 * cb + r) atomicAdd(&dB[16 * cb + r], t[cb][e]);
+  acc_store(t, S5, wv, lane, keep);
+  __syncthreads();
+  zero4(t);
+  mm64<false, false>(t, S5, S3, wv, lane);  // M1 Ti^T
+  zero4(u);
+  mm64<false, false>(u, S0, S0, wv, lane);  // w_r . w_s
+  {
+    float rowp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * wv + 4 * g + e, j = 16 * cb + r;
+        const float z = i < j ? -t[cb][e] : 0.f;  // dA[i][j]
+        rowp[e] += z * u[cb][e];
+        t[cb][e] = Bs[i] * z;  // dN
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = rowp[e];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if (r == 0) atomicAdd(&dB[16 * wv + 4 * g + e], x);
+    }
+  }
+  acc_store(t, S7, wv, lane, keep);
+  __syncthreads();
+  mm64<false, true>(aw, S7, S0, wv, lane);  // dW += dN W
+  mm64<true, true>(aw, S7, S0, wv, lane);   //      + dN^T W
+  __syncthreads();
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int a = 16 * wv + 4 * g + e, x = 16 * cb + r;
+      const int64_t i = c * 64 + a;
+      if (i < L) {
+        const size_t o = ((size_t)bh * L + i) * 64 + x;
+        dq[o] = from_f32<T>(aq[cb][e]);
+        dk[o] = from_f32<T>(ak[cb][e]);
+        dw[o] = from_f32<T>(aw[cb][e]);
+      }
+    }
+  if (tid < 64 && c * 64 + tid < L) dbeta[bh * L + c * 64 + tid] = dB[tid];
 }
 
 // ------------------------------------------------------------------------------- UT-transform terms
@@ -1150,6 +1478,11 @@ __global__ __launch_bounds__(256) void bwd_forget_kernel(const float* __restrict
 }
 
 // ------------------------------------------------------------------------------- launch
+// vector_path.hip: the forward's per-chunk terms in fp32 (other shapes than d = chunk = 64)
+hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
+                   const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
+                   float scale, float* qt, float* kt, float* Pm, float* Sm, float* fl, float* ftot, hipStream_t st);
+
 template <typename T, int D, int C>
 static hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* w, const float* beta,
                              const float* logf, const void* out, const float* lse, const void* dout, void* dq,
@@ -1158,28 +1491,22 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   using S = BwdShape<C, D>;
   static_assert(S::lds_query <= 160 * 1024 && S::lds_key <= 160 * 1024 && S::lds_prep <= 160 * 1024,
                 "backward tiles exceed LDS");
+  static_assert(kLdsPairMfma <= 160 * 1024 && kLdsChunkMfma <= 160 * 1024, "backward tiles exceed LDS");
   const int64_t M = (L + C - 1) / C;
   const dim3 grid((unsigned)M, (unsigned)BH);
   hipError_t e;
   const bool fox = logf != nullptr;
-  if constexpr (!(D == 64 && C == 64)) {
-    e = hipFuncSetAttribute((const void*)bwd_query_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)S::lds_query);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_key_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)S::lds_key);
-    if (e != hipSuccess) return e;
-  }
-  e = hipFuncSetAttribute((const void*)bwd_prep_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)S::lds_prep);
-  if (e != hipSuccess) return e;
-  if constexpr (D == 64 && C == 64) {  // the chunk-pair kernels on the matrix cores
-    e = hipFuncSetAttribute((const void*)bwd_query_mfma_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kLdsPairMfma);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_key_mfma_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kLdsPairMfma);
-    if (e != hipSuccess) return e;
+  auto lds = [](const void* f, size_t bytes) {
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  };
+  if constexpr (D == 64 && C == 64) {  // everything on the fp32 matrix cores
+    if ((e = lds((const void*)bwd_chunk_fwd_mfma_kernel<T>, kLdsChunkFwdMfma)) != hipSuccess) return e;
+    if ((e = lds((const void*)bwd_query_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
+    if ((e = lds((const void*)bwd_key_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
+    if ((e = lds((const void*)bwd_chunk_grad_mfma_kernel<T>, kLdsChunkMfma)) != hipSuccess) return e;
+    bwd_chunk_fwd_mfma_kernel<T><<<grid, 256, kLdsChunkFwdMfma, st>>>(
+        (const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_query_mfma_kernel<T><<<grid, 256, kLdsPairMfma, st>>>(
         b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
         scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
@@ -1188,7 +1515,17 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
                                                             (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
                                                             (T*)dv, b.dkt, b.dPm, b.dcol);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_chunk_grad_mfma_kernel<T><<<grid, 256, kLdsChunkMfma, st>>>((const T*)q, (const T*)k, (const T*)w, beta,
+                                                                    b.dqt, b.dkt, b.dPm, b.dSm, L, M, (T*)dq,
+                                                                    (T*)dk, (T*)dw, dbeta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
+    e = vec_run(1, std::is_same<T, __bf16>::value, D, C, q, k, v, w, beta, logf, nullptr, nullptr, BH, L, scale, b.qt,
+                b.kt, b.Pm, b.Sm, b.fl, b.ftot, st);
+    if (e != hipSuccess) return e;
+    if ((e = lds((const void*)bwd_query_kernel<T, D, C>, S::lds_query)) != hipSuccess) return e;
+    if ((e = lds((const void*)bwd_key_kernel<T, D, C>, S::lds_key)) != hipSuccess) return e;
+    if ((e = lds((const void*)bwd_prep_kernel<T, D, C>, S::lds_prep)) != hipSuccess) return e;
     bwd_query_kernel<T, D, C><<<grid, 256, S::lds_query, st>>>(
         b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
         scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
@@ -1197,11 +1534,11 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
                                                           (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
                                                           (T*)dv, b.dkt, b.dPm, b.dcol);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    bwd_prep_kernel<T, D, C><<<grid, 256, S::lds_prep, st>>>((const T*)q, (const T*)k, (const T*)w, beta, b.dqt,
+                                                            b.dkt, b.dPm, b.dSm, L, M, (T*)dq, (T*)dk, (T*)dw,
+                                                            dbeta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  bwd_prep_kernel<T, D, C><<<grid, 256, S::lds_prep, st>>>((const T*)q, (const T*)k, (const T*)w, beta, b.dqt,
-                                                          b.dkt, b.dPm, b.dSm, L, M, (T*)dq, (T*)dk, (T*)dw,
-                                                          dbeta);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (fox) {
     bwd_forget_kernel<<<dim3((unsigned)BH), 256, 0, st>>>(b.drow, b.dcol, L, M * C, dlogf);
     e = hipGetLastError();
