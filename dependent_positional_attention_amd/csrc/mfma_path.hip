@@ -589,6 +589,12 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   // row-constant first term cancels in the softmax (it returns in the lse).  kfrag(t, ks) gives the
   // A-fragment of key rows 16t.., lf the chunk-local prefix of the key chunk.
   auto logits = [&](auto kfrag, const float* lf, float offv, f32x4 (&z)[4][QT]) PA_INLINE {
+    // FoX: seed = -mref + log2e (off - prefix_j) = fma(-log2e, prefix_j, base), base per query column
+    float base[QT];
+    if constexpr (FOX) {
+#pragma unroll
+      for (int qi = 0; qi < QT; ++qi) base[qi] = __builtin_fmaf(kLog2e, offv, negm[qi][0]);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x4 seed[QT];
@@ -598,7 +604,7 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) seed[qi][i] = __builtin_fmaf(kLog2e, offv - fb[i], negm[qi][i]);
+          for (int i = 0; i < 4; ++i) seed[qi][i] = __builtin_fmaf(-kLog2e, fb[i], base[qi]);
       } else {
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) seed[qi] = negm[qi];
