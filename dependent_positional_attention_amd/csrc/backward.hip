@@ -511,13 +511,151 @@ __device__ __forceinline__ void tile_rows(float* dst, const T* __restrict__ src,
   }
 }
 
-constexpr size_t kLdsPairMfma = sizeof(float) * (7 * 64 * kS + 3 * 64);
+// Registers <-> 64 x 64 tiles, so that the next chunk pair's tiles can be fetched while the current pair
+// computes: thread tid carries rows (tid + 256 i) / 16, columns 4 ((tid + 256 i) % 16) .. +3, i = 0..3.
+__device__ __forceinline__ void fetch_tile(f32x4 (&reg)[4], const float* __restrict__ src, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, row = e >> 4, c4 = (e & 15) * 4;
+    reg[i] = *reinterpret_cast<const f32x4*>(src + row * 64 + c4);
+  }
+}
+// Rows of a [.., L, 64] input: fetched raw (in the input's type) from a clamped, always valid row, and
+// widened and masked (rows >= L read as zero) only when stored, so that no wait for the data is forced
+// at the fetch.
+template <typename T>
+using raw4 = typename std::conditional<std::is_same<T, float>::value, f32x4, bf16x4>::type;
+template <typename T>
+__device__ __forceinline__ f32x4 widen4(const raw4<T>& x) {
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+template <typename T>
+__device__ __forceinline__ void fetch_rows(raw4<T> (&reg)[4], const T* __restrict__ src, int64_t c0, int64_t L,
+                                           int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, row = e >> 4, c4 = (e & 15) * 4;
+    const int64_t rr = c0 + row < L ? c0 + row : L - 1;
+    reg[i] = *reinterpret_cast<const raw4<T>*>(src + (size_t)rr * 64 + c4);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void put_rows(float* dst, const raw4<T> (&reg)[4], int64_t c0, int64_t L, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, row = e >> 4, c4 = (e & 15) * 4;
+    const f32x4 v = widen4<T>(reg[i]);
+    *reinterpret_cast<f32x4*>(dst + row * kS + c4) = c0 + row < L ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+__device__ __forceinline__ void put_tile(float* dst, const f32x4 (&reg)[4], int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, row = e >> 4, c4 = (e & 15) * 4;
+    *reinterpret_cast<f32x4*>(dst + row * kS + c4) = reg[i];
+  }
+}
+
+// A-operand of mm64 held in registers: a[4 kb + j] = A(16w + r, 16 kb + 4g + j), i.e. the wave's own
+// 16 rows of a row-major 64 x 64 operand.
+__device__ __forceinline__ void frag_f32(float (&a)[16], const float* __restrict__ src, int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (16 * w + r) * 64 + 16 * kb + 4 * g);
+    a[4 * kb] = v[0], a[4 * kb + 1] = v[1], a[4 * kb + 2] = v[2], a[4 * kb + 3] = v[3];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void frag_rows(float (&a)[16], const T* __restrict__ src, int64_t c0, int64_t L, int w,
+                                          int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t row = c0 + 16 * w + r;
+  const int64_t rr = row < L ? row : L - 1;  // clamped (valid) row; masked below
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const f32x4 v = widen4<T>(*reinterpret_cast<const raw4<T>*>(src + (size_t)rr * 64 + 16 * kb + 4 * g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[4 * kb + j] = row < L ? v[j] : 0.f;
+  }
+}
+
+// acc[cb] += sum_k A(16w + r', k) B(k, 16cb + r'') with A from registers (frag_f32 / frag_rows layout);
+// B as in mm64.
+template <bool BK, int SB = kS>
+__device__ __forceinline__ void mm64_ra(f32x4 (&acc)[4], const float (&a)[16], const float* __restrict__ B,
+                                        int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int k0 = 16 * kb;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      float b[4];
+      if constexpr (!BK) {
+        const float4 v = *reinterpret_cast<const float4*>(B + (16 * cb + r) * SB + k0 + 4 * g);
+        b[0] = v.x, b[1] = v.y, b[2] = v.z, b[3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = B[(k0 + 4 * g + j) * SB + 16 * cb + r];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[cb] = mfma4(a[4 * kb + j], b[j], acc[cb]);
+    }
+  }
+}
+
+// The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
+// (plain functions rather than capturing lambdas, so that the arrays stay in registers).
+template <typename T>
+__device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4], f32x4 (&pP)[4], float (&pra)[16],
+                                                 float& pF, float& poff, const float* __restrict__ kt,
+                                                 const T* __restrict__ vb, const float* __restrict__ Pm,
+                                                 const float* __restrict__ St, const float* __restrict__ fl,
+                                                 const float* __restrict__ Off, int64_t bh, int64_t m, int64_t n,
+                                                 int64_t M, int64_t L, int tid, int w, int lane) {
+  constexpr int C = 64, CD = 64 * 64;
+  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
+  const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+  fetch_tile(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
+  fetch_rows(pV, vb, n * C, L, tid);
+  fetch_tile(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
+  frag_f32(pra, St + pr * CD, w, lane);
+  if (fl != nullptr) {
+    pF = fl[(size_t)bh * Lp + (size_t)n * C + (tid & 63)];
+    poff = Off[pr];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void fetch_key_pair(f32x4 (&pR)[4], f32x4 (&pG)[4], raw4<T> (&pO)[4], float& pl2,
+                                               float& pDv, float& poff, const float* __restrict__ St,
+                                               const float* __restrict__ Gst, const T* __restrict__ ob,
+                                               const float* __restrict__ lse2w, const float* __restrict__ Dw,
+                                               const float* __restrict__ Off, bool fox, int64_t bh, int64_t m,
+                                               int64_t n, int64_t M, int64_t L, int tid) {
+  constexpr int C = 64, CD = 64 * 64;
+  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
+  const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+  fetch_tile(pR, St + pr * CD, tid);
+  fetch_tile(pG, Gst + pr * CD, tid);  // not written for n = 0 (no transport there): fetched, not used
+  fetch_rows(pO, ob, m * C, L, tid);
+  const size_t r0 = (size_t)bh * Lp + (size_t)m * C;
+  pl2 = lse2w[r0 + (tid & 63)];
+  pDv = Dw[r0 + (tid & 63)];
+  if (fox) poff = Off[pr];
+}
+
+// Both chunk-pair kernels keep four 64 x 64 LDS tiles (about 70 KB, so two blocks share a CU): three
+// tiles that every wave reads whole, and one whose rows 16w .. 16w+15 only wave w writes and reads
+// (accumulators turned into A-operands), which needs no block barrier.  Operands a wave reads only
+// for its own rows stay in registers.
+constexpr size_t kLdsPairMfma = sizeof(float) * (4 * 64 * kS + 3 * 64);
 
 }  // namespace
 
 // Query-chunk kernel on the matrix cores (same outputs as bwd_query_kernel<T, 64, 64>).
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
@@ -526,14 +664,11 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
     float* __restrict__ dSm) {
   constexpr int C = 64, CD = 64 * 64;
   extern __shared__ float sm[];
-  float* Rs = sm;           // r^(n)       [64][kS]
-  float* Ks = Rs + C * kS;  // ktilde_n
+  float* Ks = sm;           // ktilde_n
   float* Vs = Ks + C * kS;  // v_n
-  float* Os = Vs + C * kS;  // dO_m
-  float* Qd = Os + C * kS;  // dr^(n-1)
-  float* Ps = Qd + C * kS;  // P_n
-  float* Gs = Ps + C * kS;  // ln2 * dz
-  float* l2 = Gs + C * kS;
+  float* Ps = Vs + C * kS;  // P_n
+  float* Xs = Ps + C * kS;  // wave rows: r^(n) (pass 1), dr^(n-1) then ln2 * dz (pass 2)
+  float* l2 = Xs + C * kS;
   float* Dv = l2 + C;
   float* Fn = Dv + C;
 
@@ -544,28 +679,36 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
   const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
   const T* vb = v + (size_t)bh * L * 64;
 
-  tile_rows(Os, dout + (size_t)bh * L * 64, m * C, L, tid);
-  __syncthreads();
-  if (tid < C) {
-    const int a = tid;
-    const int64_t i = m * C + a;
-    float dv = 0.f, l2v = INFINITY;  // padded rows: p = 0
-    if (i < L) {
-      const T* orow = out + ((size_t)bh * L + i) * 64;
-#pragma unroll 8
-      for (int x = 0; x < 64; ++x) dv += Os[a * kS + x] * to_f32(orow[x]);
-      l2v = kLog2e * (lse[bh * L + i] - (fox ? fl[row0 + a] : 0.f));
+  // dO_m rows of this wave (the A-operand of dO V^T), and D_i = dO_i . o_i from the same fragments
+  float oa[16];
+  frag_rows(oa, dout + (size_t)bh * L * 64, m * C, L, w, lane);
+  {
+    float ob[16];
+    frag_rows(ob, out + (size_t)bh * L * 64, m * C, L, w, lane);
+    float dv = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) dv += oa[x] * ob[x];
+    dv += __shfl_xor(dv, 16);
+    dv += __shfl_xor(dv, 32);
+    if (g == 0) {
+      const int a = 16 * w + r;
+      const int64_t i = m * C + a;
+      const float l2v = i < L ? kLog2e * (lse[bh * L + i] - (fox ? fl[row0 + a] : 0.f)) : INFINITY;  // padded: p = 0
+      Dv[a] = dv;
+      l2[a] = l2v;
+      lse2w[row0 + a] = l2v;
+      Dw[row0 + a] = dv;
     }
-    Dv[a] = dv;
-    l2[a] = l2v;
-    lse2w[row0 + a] = l2v;
-    Dw[row0 + a] = dv;
   }
 
-  // pass 1: states r^(n), n = m-1 .. 0
+  // pass 1: states r^(n), n = m-1 .. 0; P_{n} arrives in registers one step ahead
   f32x4 R[4], G[4];
   global_to_acc(R, qt + row0 * 64, w, lane);
   zero4(G);
+  // (fetched unconditionally, at a clamped index: a conditionally written register array would be
+  // kept in scratch memory)
+  f32x4 pP[4];
+  fetch_tile(pP, Pm + ((size_t)bh * M + (m > 0 ? m - 1 : 0)) * CD, tid);
   float off = 0.f;
   for (int64_t n = m - 1; n >= 0; --n) {
     const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
@@ -573,16 +716,18 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
     if (tid == 0) Off[pr] = off;
     acc_to_global(R, St + pr * CD, w, lane);
     if (n > 0) {
-      acc_to_lds(R, Rs, w, lane);
-      tile_f32(Ps, Pm + ((size_t)bh * M + n) * CD, tid);
+      acc_to_lds(R, Xs, w, lane);
+      __syncthreads();  // every wave is done with the previous P
+      put_tile(Ps, pP, tid);
       __syncthreads();
+      fetch_tile(pP, Pm + ((size_t)bh * M + (n > 1 ? n - 1 : 0)) * CD, tid);
       zero4(R);
-      mm64<false, false>(R, Rs, Ps, w, lane);  // r P_n^T
-      __syncthreads();
+      mm64<false, false>(R, Xs, Ps, w, lane);  // r P_n^T
     }
   }
 
   // in-chunk block: logits from S, D = dO_m V_m^T on the matrix cores
+  __syncthreads();
   tile_rows(Vs, vb, m * C, L, tid);
   if (fox && tid < C) Fn[tid] = fl[row0 + tid];
   __syncthreads();
@@ -590,7 +735,7 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
   {
     f32x4 DP[4];
     zero4(DP);
-    mm64<false, false>(DP, Os, Vs, w, lane);
+    mm64_ra<false>(DP, oa, Vs, lane);
     const float* Sc = Sm + ((size_t)bh * M + m) * C * C;
     float* dSc = dSm + ((size_t)bh * M + m) * C * C;
 #pragma unroll
@@ -608,26 +753,39 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
       }
   }
 
-  // pass 2: n = 0 .. m-1
+  // pass 2: n = 0 .. m-1; the next pair's ktilde, v, P (whole tiles) and this wave's rows of r^(n)
+  // arrive in registers one step ahead
+  if (m > 0) {
+  f32x4 pK[4];
+  raw4<T> pV[4];
+  float pra[16], ra[16];
+  float pF = 0.f, poff = 0.f;
+  fetch_query_pair(pK, pV, pP, pra, pF, poff, kt, vb, Pm, St, fl, Off, bh, m, 0, M, L, tid, w, lane);
   for (int64_t n = 0; n < m; ++n) {
     const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
-    __syncthreads();
-    tile_f32(Rs, St + pr * CD, tid);
-    tile_f32(Ks, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
-    tile_rows(Vs, vb, n * C, L, tid);
+    __syncthreads();  // every wave is done with the previous ktilde, v, P, FoX prefix
+    put_tile(Ks, pK, tid);
+    put_rows<T>(Vs, pV, n * C, L, tid);
+    if (n > 0) put_tile(Ps, pP, tid);
+    if (fox && tid < C) Fn[tid] = pF;
+    const float offn = poff;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) ra[x] = pra[x];
     if (n > 0) {
-      tile_f32(Ps, Pm + ((size_t)bh * M + n) * CD, tid);
-      acc_to_lds(G, Qd, w, lane);
+      acc_to_lds(G, Xs, w, lane);  // dr^(n-1), this wave's rows
       acc_to_global(G, Gst + pr * CD, w, lane);
     }
-    if (fox && tid < C) Fn[tid] = fl[(size_t)bh * Lp + (size_t)n * C + tid];
-    const float offn = fox ? Off[pr] : 0.f;
     __syncthreads();
+    // the last step fetches its own pair again (not used)
+    fetch_query_pair(pK, pV, pP, pra, pF, poff, kt, vb, Pm, St, fl, Off, bh, m, n + 1 < m ? n + 1 : n, M, L, tid, w,
+                     lane);
     f32x4 Z[4], DP[4];
+    zero4(G);
+    if (n > 0) mm64<false, true>(G, Xs, Ps, w, lane);  // dr^(n-1) P_n
     zero4(Z);
     zero4(DP);
-    mm64<false, false>(Z, Rs, Ks, w, lane);
-    mm64<false, false>(DP, Os, Vs, w, lane);
+    mm64_ra<false>(Z, ra, Ks, lane);
+    mm64_ra<false>(DP, oa, Vs, lane);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -636,12 +794,10 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
         const float z2 = Z[cb][e] + (fox ? kLog2e * (offn - Fn[b]) : 0.f);
         const float dz = fast_exp2(z2 - l2[a]) * (DP[cb][e] - Dv[a]);
         rsum[e] += dz;
-        Gs[a * kS + b] = kLn2 * dz;
+        Xs[a * kS + b] = kLn2 * dz;  // the wave's own rows; the reads of dr^(n-1) above came first
       }
-    __syncthreads();
-    zero4(G);
-    if (n > 0) mm64<false, true>(G, Qd, Ps, w, lane);  // dr^(n-1) P_n
-    mm64<false, true>(G, Gs, Ks, w, lane);              // + g ktilde_n
+    mm64<false, true>(G, Xs, Ks, w, lane);  // + g ktilde_n
+  }
   }
 
   acc_to_global(G, dqt + row0 * 64, w, lane, scale * kLog2e);  // qtilde entered the scan scaled
@@ -661,21 +817,18 @@ __global__ __launch_bounds__(256) void bwd_query_mfma_kernel(
 // pair are formed transposed (rows = keys of chunk n), so that p and g are stored k-contiguous for
 // the products that reduce over the queries.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_key_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
     const T* __restrict__ v, const T* __restrict__ dout, const float* __restrict__ St, const float* __restrict__ Gst,
     const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
     int64_t M, T* __restrict__ dv, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol) {
   constexpr int C = 64, CD = 64 * 64;
   extern __shared__ float sm[];
-  float* Ks = sm;           // ktilde_n       [64][kS]
-  float* Vs = Ks + C * kS;  // v_n
-  float* Rs = Vs + C * kS;  // r^(n)_m
+  float* Rs = sm;           // r^(n)_m
   float* Os = Rs + C * kS;  // dO_m
   float* Gq = Os + C * kS;  // dr^(n-1)_m
-  float* PT = Gq + C * kS;  // p^T     [key][query]
-  float* GT = PT + C * kS;  // (ln2 dz)^T
-  float* l2 = GT + C * kS;
+  float* Xs = Gq + C * kS;  // wave rows: p^T, then (ln2 dz)^T  [key][query]
+  float* l2 = Xs + C * kS;
   float* Dv = l2 + C;
   float* Fn = Dv + C;
 
@@ -686,19 +839,17 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(
   const T* vb = v + (size_t)bh * L * 64;
   const T* ob = dout + (size_t)bh * L * 64;
 
-  auto stats = [&](int64_t mm) PA_INLINE {
-    if (tid < C) {
-      const size_t r0 = (size_t)bh * Lp + (size_t)mm * C;
-      l2[tid] = lse2w[r0 + tid];
-      Dv[tid] = Dw[r0 + tid];
-    }
-  };
+  // this wave's rows of ktilde_n and v_n: the A-operands of the transposed logits and of V dO^T
+  float ka[16], va[16];
+  frag_f32(ka, kt + rown * 64, w, lane);
+  frag_rows(va, vb, n * C, L, w, lane);
 
-  tile_f32(Ks, kt + rown * 64, tid);
-  tile_rows(Vs, vb, n * C, L, tid);
   tile_rows(Os, ob, n * C, L, tid);
-  if (tid < C) Fn[tid] = fox ? fl[rown + tid] : 0.f;
-  stats(n);
+  if (tid < C) {
+    Fn[tid] = fox ? fl[rown + tid] : 0.f;
+    l2[tid] = lse2w[rown + tid];
+    Dv[tid] = Dw[rown + tid];
+  }
   __syncthreads();
 
   f32x4 aV[4], aK[4], aP[4];
@@ -711,7 +862,7 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(
   {
     f32x4 DT[4];
     zero4(DT);
-    mm64<false, false>(DT, Vs, Os, w, lane);
+    mm64_ra<false>(DT, va, Os, lane);
     const float* Sc = Sm + ((size_t)bh * M + n) * C * C;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -725,26 +876,37 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(
           dz = p * (DT[cb][e] - Dv[a]);
         }
         csum[e] += dz;
-        PT[b * kS + a] = p;
+        Xs[b * kS + a] = p;  // the wave's own rows
       }
   }
-  __syncthreads();
-  mm64<false, true>(aV, PT, Os, w, lane);  // dv_n += p^T dO_n
+  mm64<false, true>(aV, Xs, Os, w, lane);  // dv_n += p^T dO_n
 
+  // query chunks m = n+1 .. M-1; the next pair's tiles arrive in registers one step ahead
+  if (n + 1 < M) {
+  f32x4 pR[4], pG[4];
+  raw4<T> pO[4];
+  float pl2 = 0.f, pDv = 0.f, poff = 0.f;
+  fetch_key_pair(pR, pG, pO, pl2, pDv, poff, St, Gst, ob, lse2w, Dw, Off, fox, bh, n + 1, n, M, L, tid);
   for (int64_t m = n + 1; m < M; ++m) {
-    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    __syncthreads();  // every wave is done with the previous r, dO, dr, row statistics
+    put_tile(Rs, pR, tid);
+    if (n > 0) put_tile(Gq, pG, tid);
+    put_rows<T>(Os, pO, m * C, L, tid);
+    if (tid < C) {
+      l2[tid] = pl2;
+      Dv[tid] = pDv;
+    }
+    const float offn = poff;
     __syncthreads();
-    tile_f32(Rs, St + pr * CD, tid);
-    if (n > 0) tile_f32(Gq, Gst + pr * CD, tid);
-    tile_rows(Os, ob, m * C, L, tid);
-    stats(m);
-    const float offn = fox ? Off[pr] : 0.f;
-    __syncthreads();
+    // the last step fetches its own pair again (not used)
+    fetch_key_pair(pR, pG, pO, pl2, pDv, poff, St, Gst, ob, lse2w, Dw, Off, fox, bh, m + 1 < M ? m + 1 : m, n, M, L,
+                   tid);
     f32x4 ZT[4], DT[4];
     zero4(ZT);
     zero4(DT);
-    mm64<false, false>(ZT, Ks, Rs, w, lane);  // (r ktilde^T)^T
-    mm64<false, false>(DT, Vs, Os, w, lane);  // (dO v^T)^T
+    mm64_ra<false>(ZT, ka, Rs, lane);  // (r ktilde^T)^T
+    mm64_ra<false>(DT, va, Os, lane);  // (dO v^T)^T
+    float gz[4][4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -754,13 +916,17 @@ __global__ __launch_bounds__(256) void bwd_key_mfma_kernel(
         const float p = fast_exp2(z2 - l2[a]);
         const float dz = p * (DT[cb][e] - Dv[a]);
         csum[e] += dz;
-        PT[b * kS + a] = p;
-        GT[b * kS + a] = kLn2 * dz;
+        Xs[b * kS + a] = p;
+        gz[cb][e] = kLn2 * dz;
       }
-    __syncthreads();
-    mm64<false, true>(aV, PT, Os, w, lane);               // dv_n += p^T dO_m
-    mm64<false, true>(aK, GT, Rs, w, lane);               // d ktilde_n += g^T r
-    if (n > 0) mm64<true, true>(aP, Gq, Rs, w, lane);     // dP_n += dr^(n-1)^T r
+    mm64<false, true>(aV, Xs, Os, w, lane);  // dv_n += p^T dO_m
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xs[(16 * w + 4 * g + e) * kS + 16 * cb + r] = gz[cb][e];  // after the reads of p
+    mm64<false, true>(aK, Xs, Rs, w, lane);            // d ktilde_n += g^T r
+    if (n > 0) mm64<true, true>(aP, Gq, Rs, w, lane);  // dP_n += dr^(n-1)^T r
+  }
   }
 
   acc_to_global(aK, dkt + rown * 64, w, lane);
