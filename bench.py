@@ -474,6 +474,37 @@ def bench_decode(args):
                          "kernel": "decode update+attend and combine, whole step"}}
 
 
+def measure_peaks(args):
+    """Ceilings measured on this GPU, beside the published ones: a large bf16 GEMM through the vendor
+    library (hipBLASLt via torch.mm; dense, contiguous operands) for the matrix cores, and a plain 2 GiB
+    device copy for HBM (bytes read + written over time).  The kernels' fractions are also reported
+    against these."""
+    import torch
+    n = 8192
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    a = torch.randn((n, n), device="cuda", dtype=torch.float32, generator=gen).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.float32, generator=gen).to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.mm(a, b, out=c)
+    ms_mm = timed(lambda: torch.mm(a, b, out=c), 20)
+    gemm = 2.0 * n ** 3 / (ms_mm * 1e-3) / 1e12
+    del a, b, c
+    nbytes = 2 << 30
+    src = torch.ones(nbytes, device="cuda", dtype=torch.uint8)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ms_cp = timed(lambda: dst.copy_(src), 10)
+    copy = 2.0 * nbytes / (ms_cp * 1e-3) / 1e9
+    del src, dst
+    log(f"[bench] measured ceilings: bf16 GEMM {n}^3 {gemm:.0f} TFLOP/s ({gemm / MFMA_BF16_PEAK_TFLOPS:.3f} of the "
+        f"published peak), 2 GiB device copy {copy:.0f} GB/s ({copy / HBM_PEAK_GBS:.3f})")
+    return {"bf16_gemm_tflops": gemm, "gemm": f"torch.mm bf16 {n}x{n}x{n} (hipBLASLt)", "copy_gbs": copy,
+            "copy": "2 GiB device-to-device copy, read + write bytes"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -503,6 +534,7 @@ def main():
     cpu = None if args.no_cpu else bench_cpu(x, args)
     dec = None if args.no_decode else bench_decode(args)
     long_ctx = None if args.no_long else bench_long(args)
+    peaks = measure_peaks(args)
     F = res["flops"]
     achieved = F / (res["ms_scan"] * 1e-3) / 1e12
     line = {
@@ -527,7 +559,8 @@ def main():
                          "true" if args.fox else "false", "true" if args.transport == "bf16x3" else "false"),
                          "mfma_path.hip"),
                      "traffic_unit": "bytes per launch", "kernel": "mfma_attn_kernel",
-                     "launch_ms": res["ms_scan"], "flops_per_launch": F},
+                     "launch_ms": res["ms_scan"], "flops_per_launch": F,
+                     "frac_of_measured_gemm": achieved / peaks["bf16_gemm_tflops"]},
         "prefill_detail": {"ms_prep": res["ms_prep"], "ms_scan": res["ms_scan"], "wall_ms_per_step": res["wall_ms"],
                            "step_tflops": F / (res["ms_step"] * 1e-3) / 1e12,
                            "step_frac_of_peak": F / (res["ms_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
@@ -538,7 +571,10 @@ def main():
         "fox_prefill": fox,
         "backward": bwd,
         "long_context": long_ctx,
+        "measured_ceilings": peaks,
     }
+    if dec is not None:
+        dec["roofline"]["frac_of_measured_copy"] = dec["value"] / peaks["copy_gbs"]
     print(json.dumps(line), flush=True)
 
 
