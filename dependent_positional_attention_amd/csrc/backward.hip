@@ -645,6 +645,21 @@ __device__ __forceinline__ void fetch_key_pair(f32x4 (&pR)[4], f32x4 (&pG)[4], r
   if (fox) poff = Off[pr];
 }
 
+// Block -> (batch*head, chunk) of the two chunk-pair kernels (1-D grid of kBwdXcd * ceil(BH / kBwdXcd) * M
+// blocks): workgroup b runs on XCD b % 8, each with its own L2, so every block of one (batch, head),
+// which all read that head's ktilde, v and P tiles, lands on the same XCD; heads are dealt round-robin
+// to XCDs and within an XCD the q-th block of every head goes before the (q+1)-th.  Returns false for
+// the surplus blocks of XCDs with fewer heads.
+constexpr int kBwdXcd = 8;
+__device__ __forceinline__ bool bwd_pair_block(int64_t BH, int64_t M, int64_t& bh, int64_t& q) {
+  const int64_t xcd = blockIdx.x % kBwdXcd, slot = blockIdx.x / kBwdXcd;
+  const int64_t heads_here = (BH - xcd + kBwdXcd - 1) / kBwdXcd;
+  if (slot >= heads_here * M) return false;
+  bh = xcd + kBwdXcd * (slot % heads_here);
+  q = slot / heads_here;
+  return true;
+}
+
 // Both chunk-pair kernels keep four 64 x 64 LDS tiles (about 70 KB, so two blocks share a CU): three
 // tiles that every wave reads whole, and one whose rows 16w .. 16w+15 only wave w writes and reads
 // (accumulators turned into A-operands), which needs no block barrier.  Operands a wave reads only
@@ -661,7 +676,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
     int64_t L, int64_t M, float scale, float* __restrict__ St, float* __restrict__ Gst, float* __restrict__ Off,
     float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow, float* __restrict__ dqt,
-    float* __restrict__ dSm) {
+    float* __restrict__ dSm, int64_t BH) {
   constexpr int C = 64, CD = 64 * 64;
   extern __shared__ float sm[];
   float* Ks = sm;           // ktilde_n
@@ -672,9 +687,11 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   float* Dv = l2 + C;
   float* Fn = Dv + C;
 
+  int64_t bh, q;
+  if (!bwd_pair_block(BH, M, bh, q)) return;  // whole block
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
-  const int64_t m = (int64_t)gridDim.x - 1 - blockIdx.x;
-  const int64_t bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const int64_t m = M - 1 - q;  // longest first
+  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
   const bool fox = fl != nullptr;
   const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
   const T* vb = v + (size_t)bh * L * 64;
@@ -821,7 +838,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
     const T* __restrict__ v, const T* __restrict__ dout, const float* __restrict__ St, const float* __restrict__ Gst,
     const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
-    int64_t M, T* __restrict__ dv, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol) {
+    int64_t M, T* __restrict__ dv, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol,
+    int64_t BH) {
   constexpr int C = 64, CD = 64 * 64;
   extern __shared__ float sm[];
   float* Rs = sm;           // r^(n)_m
@@ -832,8 +850,10 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   float* Dv = l2 + C;
   float* Fn = Dv + C;
 
+  int64_t bh, n;
+  if (!bwd_pair_block(BH, M, bh, n)) return;  // whole block; low key chunks (the longest) first
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
-  const int64_t n = blockIdx.x, bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
   const bool fox = fl != nullptr;
   const size_t rown = (size_t)bh * Lp + (size_t)n * C;
   const T* vb = v + (size_t)bh * L * 64;
@@ -1673,13 +1693,14 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
     bwd_chunk_fwd_mfma_kernel<T><<<grid, 256, kLdsChunkFwdMfma, st>>>(
         (const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_query_mfma_kernel<T><<<grid, 256, kLdsPairMfma, st>>>(
+    const dim3 pair_grid((unsigned)(kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd) * M));
+    bwd_query_mfma_kernel<T><<<pair_grid, 256, kLdsPairMfma, st>>>(
         b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
-        scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
+        scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm, BH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_key_mfma_kernel<T><<<grid, 256, kLdsPairMfma, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
-                                                            (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
-                                                            (T*)dv, b.dkt, b.dPm, b.dcol);
+    bwd_key_mfma_kernel<T><<<pair_grid, 256, kLdsPairMfma, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
+                                                                 (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv,
+                                                                 L, M, (T*)dv, b.dkt, b.dPm, b.dcol, BH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_chunk_grad_mfma_kernel<T><<<grid, 256, kLdsChunkMfma, st>>>((const T*)q, (const T*)k, (const T*)w, beta,
                                                                     b.dqt, b.dkt, b.dPm, b.dSm, L, M, (T*)dq,
