@@ -996,16 +996,23 @@ __device__ __forceinline__ void sub4(f32x4 (&acc)[4], const f32x4 (&t)[4]) {
 
 // A = I + diag(beta) strict_upper(W W^T) is read from tile Aa (only r < s), A^{-1} written to Ai
 // (unit upper triangular, zeros below) by back substitution, one column per thread.
+// The thread's column z stays in registers; the loops run over fixed bounds (z[kk] = 0 below the
+// diagonal and z[j] = 1 make the extra terms vanish), and each sum is split over four accumulators
+// so that the dependent FMA chains overlap.
 __device__ __forceinline__ void unit_upper_inverse(const float* Aa, float* Ai, int tid) {
   if (tid < 64) {
     const int j = tid;
-    for (int i = 63; i > j; --i) Ai[i * kS + j] = 0.f;
-    Ai[j * kS + j] = 1.f;
-    for (int i = j - 1; i >= 0; --i) {
-      float s = 0.f;
-      for (int kk = i + 1; kk <= j; ++kk) s += Aa[i * kS + kk] * Ai[kk * kS + j];
-      Ai[i * kS + j] = -s;
+    float z[64];
+#pragma unroll
+    for (int i = 63; i >= 0; --i) {
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = i + 1; kk < 64; ++kk) s4[(kk - i - 1) & 3] = __builtin_fmaf(Aa[i * kS + kk], z[kk], s4[(kk - i - 1) & 3]);
+      const float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      z[i] = i == j ? 1.f : (i < j ? -sum : 0.f);
     }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) Ai[i * kS + j] = z[i];
   }
 }
 
