@@ -81,3 +81,29 @@ def test_bf16_backward(recipe):
 def test_bf16_backward_several_heads():
     x = synth.make_fwd_inputs(2, 3, 520, 64, recipe="fox", dtype="bf16", seed=21)
     check(x, 64, "bf16 B=2 H=3", seed=22)
+
+
+def test_full_size_backward_sampled_heads_equal_single_head_runs():
+    """The backward at the benchmark's size (B=8, H=24, L=4096, bf16, PaTH-FoX) in its launch configuration.
+    The fp64 oracle's backward needs minutes per head at this length, so the full-size run is tied to the
+    oracle-checked kernels through a property that holds at any size: (batch, head) slices are independent
+    and the kernels are deterministic, so every sampled head's gradients equal, bit for bit, those of the
+    same head run on its own (B = H = 1, a different grid)."""
+    B, H, L, d = 8, 24, 4096, 64
+    print(f"[case] full-size backward B={B} H={H} L={L} d={d} bf16 fox", flush=True)
+    x = synth.make_fwd_inputs(B, H, L, d, recipe="fox", dtype="bf16", seed=31)
+    dout = synth.make_out_grad(x.shape, dtype="bf16", seed=32)
+    t = fwd_inputs_dev(x)
+    out, lse = native.path_attn_fwd(t["q"], t["k"], t["v"], t["w"], t["beta"], t["logf"], scale=x.scale, chunk=64)
+    do = dev(dout, "bf16")
+    full = native.path_attn_bwd(t["q"], t["k"], t["v"], t["w"], t["beta"], out, lse, do, t["logf"], scale=x.scale,
+                                chunk=64)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (7, 23), (3, 17)]:
+        sl = lambda a: a[b:b + 1, h:h + 1].contiguous()
+        one = native.path_attn_bwd(sl(t["q"]), sl(t["k"]), sl(t["v"]), sl(t["w"]), sl(t["beta"]), sl(out), sl(lse),
+                                   sl(do), sl(t["logf"]), scale=x.scale, chunk=64)
+        torch.cuda.synchronize()
+        for name, gf, g1 in zip(NAMES, full, one):
+            assert torch.equal(sl(gf), g1), f"head ({b}, {h}) {name}: full-size run differs from the single-head run"
+            assert torch.isfinite(g1.float()).all()
