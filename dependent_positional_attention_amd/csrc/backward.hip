@@ -853,7 +853,7 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   int64_t bh, n;
   if (!bwd_pair_block(BH, M, bh, n)) return;  // whole block; low key chunks (the longest) first
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
-  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
+  const int64_t Lp = M * C;
   const bool fox = fl != nullptr;
   const size_t rown = (size_t)bh * Lp + (size_t)n * C;
   const T* vb = v + (size_t)bh * L * 64;
