@@ -182,6 +182,8 @@ static_assert(kPrepLds <= 160 * 1024 / 3, "prep LDS plan must allow three blocks
 
 __device__ __forceinline__ int perm_col(int c) { return perm_pos(c); }
 
+// X3: the lo halves of qtilde and P (bf16x3 transport) are formed and stored; without it only hi.
+template <bool X3>
 __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
     const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, float qs,
@@ -418,11 +420,16 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     // qtilde[a][x] = (q_a[x] - D[x][a]) * qs  (lane: row a, columns x0..x0+3)
     {
       const bf16x4 q4 = q4s[xt];
-      bf16x4 h4, l4;
-      split4(((float)q4[0] - dq[0]) * qs, ((float)q4[1] - dq[1]) * qs, ((float)q4[2] - dq[2]) * qs,
-             ((float)q4[3] - dq[3]) * qs, h4, l4);
-      *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
-      if (qt_lo != nullptr) *reinterpret_cast<bf16x4*>(qt_lo + (chunk_rows + a) * kD + pos) = l4;
+      const float v0 = ((float)q4[0] - dq[0]) * qs, v1 = ((float)q4[1] - dq[1]) * qs,
+                  v2 = ((float)q4[2] - dq[2]) * qs, v3 = ((float)q4[3] - dq[3]) * qs;
+      if constexpr (X3) {
+        bf16x4 h4, l4;
+        split4(v0, v1, v2, v3, h4, l4);
+        *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
+        *reinterpret_cast<bf16x4*>(qt_lo + (chunk_rows + a) * kD + pos) = l4;
+      } else {
+        *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = pack4(v0, v1, v2, v3);
+      }
     }
     // ktilde[b][x] = k_b[x] - D[x][b]
     {
@@ -433,12 +440,17 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     // P[x][y] = delta - D[y][x]  (lane: row x = 16 xt + r, columns y = 16 wave + 4g .. +3)
     {
       const int xr = 16 * xt + r, y0 = 16 * wave + 4 * g;
-      bf16x4 ph, pl;
-      split4((y0 == xr ? 1.f : 0.f) - dp[0], (y0 + 1 == xr ? 1.f : 0.f) - dp[1],
-             (y0 + 2 == xr ? 1.f : 0.f) - dp[2], (y0 + 3 == xr ? 1.f : 0.f) - dp[3], ph, pl);
+      const float e0 = (y0 == xr ? 1.f : 0.f) - dp[0], e1 = (y0 + 1 == xr ? 1.f : 0.f) - dp[1],
+                  e2 = (y0 + 2 == xr ? 1.f : 0.f) - dp[2], e3 = (y0 + 3 == xr ? 1.f : 0.f) - dp[3];
       const int py = perm_pos(y0);
-      *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = ph;
-      if (p_lo != nullptr) *reinterpret_cast<bf16x4*>(p_lo + chunk_mat + (size_t)xr * kD + py) = pl;
+      if constexpr (X3) {
+        bf16x4 ph, pl;
+        split4(e0, e1, e2, e3, ph, pl);
+        *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = ph;
+        *reinterpret_cast<bf16x4*>(p_lo + chunk_mat + (size_t)xr * kD + py) = pl;
+      } else {
+        *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = pack4(e0, e1, e2, e3);
+      }
     }
     // S[a][b] = (q_a.k_b - D[b][a]) * qs  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3)
     {
@@ -1261,13 +1273,16 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
   const bool x3 = transport == 1;
   hipError_t e = hipSuccess;
   if (phases & 1) {
-    e = hipFuncSetAttribute((const void*)mfma_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kPrepLds);
-    if (e != hipSuccess) return e;
-    mfma_prep_kernel<<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
-        (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, scale * kLog2e, (__bf16*)qt,
-        x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
-    e = hipGetLastError();
+    auto prep = [&](auto kernel) {
+      hipError_t err = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)kPrepLds);
+      if (err != hipSuccess) return err;
+      kernel<<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
+          (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, scale * kLog2e, (__bf16*)qt,
+          x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
+      return hipGetLastError();
+    };
+    e = x3 ? prep(mfma_prep_kernel<true>) : prep(mfma_prep_kernel<false>);
     if (e != hipSuccess) return e;
     if (G > 1 && MG > 0) {
       const dim3 gg((unsigned)MG, (unsigned)BH);
