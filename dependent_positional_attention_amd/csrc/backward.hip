@@ -605,6 +605,36 @@ __device__ __forceinline__ void mm64_ra(f32x4 (&acc)[4], const float (&a)[16], c
   }
 }
 
+// Products of bf16 numbers (v and dO of a bf16 input) are exact in fp32, so with bf16 inputs the dO v^T
+// products run on the bf16 matrix cores (16x16x32, fp32 accumulation; only the summation order differs
+// from the fp32 16x16x4 products).  A-fragments a[ks] = A(16w + r, 32 ks + 8g .. +7) come from global
+// memory (rows >= L zero); B(k, j) = B[j][k] from an fp32 LDS tile (stride kS) that holds bf16 numbers.
+__device__ __forceinline__ void frag_bf16(bf16x8 (&a)[2], const __bf16* __restrict__ src, int64_t c0, int64_t L,
+                                          int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t row = c0 + 16 * w + r;
+  const int64_t rr = row < L ? row : L - 1;  // clamped (valid) row; masked below
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + (size_t)rr * 64 + 32 * ks + 8 * g);
+    a[ks] = row < L ? v : bf16x8{};
+  }
+}
+__device__ __forceinline__ void mm64_bf16(f32x4 (&acc)[4], const bf16x8 (&a)[2], const float* __restrict__ B,
+                                          int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float* p = B + (16 * cb + r) * kS + 32 * ks + 8 * g;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+      const bf16x8 b = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                        (__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc[cb], 0, 0, 0);
+    }
+}
+
 // The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
 // (plain functions rather than capturing lambdas, so that the arrays stay in registers).
 template <typename T>
@@ -696,9 +726,12 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
   const T* vb = v + (size_t)bh * L * 64;
 
-  // dO_m rows of this wave (the A-operand of dO V^T), and D_i = dO_i . o_i from the same fragments
+  // dO_m rows of this wave (the A-operand of dO V^T: bf16 fragments for a bf16 input), and D_i = dO_i . o_i
+  constexpr bool kBf = std::is_same<T, __bf16>::value;
   float oa[16];
   frag_rows(oa, dout + (size_t)bh * L * 64, m * C, L, w, lane);
+  bf16x8 ob16[2];
+  if constexpr (kBf) frag_bf16(ob16, reinterpret_cast<const __bf16*>(dout) + (size_t)bh * L * 64, m * C, L, w, lane);
   {
     float ob[16];
     frag_rows(ob, out + (size_t)bh * L * 64, m * C, L, w, lane);
@@ -752,7 +785,8 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   {
     f32x4 DP[4];
     zero4(DP);
-    mm64_ra<false>(DP, oa, Vs, lane);
+    if constexpr (kBf) mm64_bf16(DP, ob16, Vs, lane);
+    else mm64_ra<false>(DP, oa, Vs, lane);
     const float* Sc = Sm + ((size_t)bh * M + m) * C * C;
     float* dSc = dSm + ((size_t)bh * M + m) * C * C;
 #pragma unroll
@@ -802,7 +836,8 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     zero4(Z);
     zero4(DP);
     mm64_ra<false>(Z, ra, Ks, lane);
-    mm64_ra<false>(DP, oa, Vs, lane);
+    if constexpr (kBf) mm64_bf16(DP, ob16, Vs, lane);
+    else mm64_ra<false>(DP, oa, Vs, lane);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -859,10 +894,14 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   const T* vb = v + (size_t)bh * L * 64;
   const T* ob = dout + (size_t)bh * L * 64;
 
-  // this wave's rows of ktilde_n and v_n: the A-operands of the transposed logits and of V dO^T
+  // this wave's rows of ktilde_n and v_n: the A-operands of the transposed logits and of V dO^T (bf16
+  // fragments for a bf16 input)
+  constexpr bool kBf = std::is_same<T, __bf16>::value;
   float ka[16], va[16];
+  bf16x8 vb16[2];
   frag_f32(ka, kt + rown * 64, w, lane);
-  frag_rows(va, vb, n * C, L, w, lane);
+  if constexpr (kBf) frag_bf16(vb16, reinterpret_cast<const __bf16*>(vb), n * C, L, w, lane);
+  else frag_rows(va, vb, n * C, L, w, lane);
 
   tile_rows(Os, ob, n * C, L, tid);
   if (tid < C) {
@@ -882,7 +921,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   {
     f32x4 DT[4];
     zero4(DT);
-    mm64_ra<false>(DT, va, Os, lane);
+    if constexpr (kBf) mm64_bf16(DT, vb16, Os, lane);
+    else mm64_ra<false>(DT, va, Os, lane);
     const float* Sc = Sm + ((size_t)bh * M + n) * C * C;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -925,7 +965,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     zero4(ZT);
     zero4(DT);
     mm64_ra<false>(ZT, ka, Rs, lane);  // (r ktilde^T)^T
-    mm64_ra<false>(DT, va, Os, lane);  // (dO v^T)^T
+    if constexpr (kBf) mm64_bf16(DT, vb16, Os, lane);  // (dO v^T)^T
+    else mm64_ra<false>(DT, va, Os, lane);
     float gz[4][4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
