@@ -635,6 +635,35 @@ __device__ __forceinline__ void mm64_bf16(f32x4 (&acc)[4], const bf16x8 (&a)[2],
     }
 }
 
+// acc[cb] += sum_k A(16w + r', k) B(k, 16cb + r'') on the bf16 matrix cores for B holding bf16 numbers
+// (dO of a bf16 input): A from the wave's own rows of an fp32 LDS tile, split into hi + lo bf16 (about
+// 2^-16 relative), B(k, j) = B[k][j] from an fp32 LDS tile, converted exactly.
+__device__ __forceinline__ void mm64_split_bf16(f32x4 (&acc)[4], const float* __restrict__ A,
+                                                const float* __restrict__ B, int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {  // one k-block's fragments live at a time
+    const float* p = A + (16 * w + r) * kS + 32 * ks + 8 * g;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+    bf16x8 ah, al;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float vi = i < 4 ? x[i] : y[i - 4];
+      const __bf16 hi = (__bf16)vi;
+      ah[i] = hi;
+      al[i] = (__bf16)(vi - (float)hi);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      bf16x8 b;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = (__bf16)B[(32 * ks + 8 * g + i) * kS + 16 * cb + r];
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[cb], 0, 0, 0);
+    }
+  }
+}
+
 // The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
 // (plain functions rather than capturing lambdas, so that the arrays stay in registers).
 template <typename T>
@@ -939,7 +968,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
         Xs[b * kS + a] = p;  // the wave's own rows
       }
   }
-  mm64<false, true>(aV, Xs, Os, w, lane);  // dv_n += p^T dO_n
+  if constexpr (kBf) mm64_split_bf16(aV, Xs, Os, w, lane);  // dv_n += p^T dO_n
+  else mm64<false, true>(aV, Xs, Os, w, lane);
 
   // query chunks m = n+1 .. M-1; the next pair's tiles arrive in registers one step ahead
   if (n + 1 < M) {
@@ -980,7 +1010,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
         Xs[b * kS + a] = p;
         gz[cb][e] = kLn2 * dz;
       }
-    mm64<false, true>(aV, Xs, Os, w, lane);  // dv_n += p^T dO_m
+    if constexpr (kBf) mm64_split_bf16(aV, Xs, Os, w, lane);  // dv_n += p^T dO_m
+    else mm64<false, true>(aV, Xs, Os, w, lane);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
