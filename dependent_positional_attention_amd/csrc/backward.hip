@@ -1088,6 +1088,32 @@ __device__ __forceinline__ void unit_upper_inverse(const float* Aa, float* Ai, i
   }
 }
 
+// acc[cb] += sum_k A[16w + r'][k] B[16cb + r''][k] on the bf16 matrix cores, for fp32 LDS tiles (stride
+// kS) holding bf16 numbers (w, q, k of a bf16 input): the conversions and the products are exact.
+__device__ __forceinline__ bf16x8 row8_bf16(const float* p) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+  return bf16x8{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                (__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+}
+__device__ __forceinline__ void mm64_rows_bf16(f32x4 (&acc)[4], const float* __restrict__ A,
+                                               const float* __restrict__ B, int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 a = row8_bf16(A + (16 * w + r) * kS + 32 * ks + 8 * g);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, row8_bf16(B + (16 * cb + r) * kS + 32 * ks + 8 * g),
+                                                        acc[cb], 0, 0, 0);
+  }
+}
+// mm64<false, false>, on the bf16 matrix cores when the operands hold bf16 numbers
+template <typename T>
+__device__ __forceinline__ void mm64_rows(f32x4 (&acc)[4], const float* A, const float* B, int w, int lane) {
+  if constexpr (std::is_same<T, __bf16>::value) mm64_rows_bf16(acc, A, B, w, lane);
+  else mm64<false, false>(acc, A, B, w, lane);
+}
+
 // W, Q, K of chunk c (rows >= L zero), beta, then A (into Aa), U (t <= a), R (s > b).
 template <typename T>
 __device__ __forceinline__ void chunk_setup(const T* q, const T* k, const T* w, const float* beta, int64_t bh,
@@ -1101,13 +1127,13 @@ __device__ __forceinline__ void chunk_setup(const T* q, const T* k, const T* w, 
   __syncthreads();
   f32x4 t[4];
   zero4(t);
-  mm64<false, false>(t, Wt, Wt, wv, lane);  // w_r . w_s
+  mm64_rows<T>(t, Wt, Wt, wv, lane);  // w_r . w_s
   acc_store(t, Aa, wv, lane, [&](int i, int j, float x) { return i < j ? Bs[i] * x : 0.f; });
   zero4(t);
-  mm64<false, false>(t, Wt, Qt, wv, lane);  // w_t . q_a
+  mm64_rows<T>(t, Wt, Qt, wv, lane);  // w_t . q_a
   acc_store(t, Ut, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; });
   zero4(t);
-  mm64<false, false>(t, Kt, Wt, wv, lane);  // k_b . w_s
+  mm64_rows<T>(t, Kt, Wt, wv, lane);  // k_b . w_s
   acc_store(t, Rt, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; });
 }
 
@@ -1164,7 +1190,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
   __syncthreads();
   // S[a][b] = q_a . k_b - (Y U)[b][a] for b <= a
   zero4(t);
-  mm64<false, false>(t, Qt, Kt, wv, lane);
+  mm64_rows<T>(t, Qt, Kt, wv, lane);
   zero4(u);
   mm64<true, false>(u, Ut, Ai, wv, lane);
   sub4(t, u);
@@ -1330,7 +1356,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
   zero4(t);
   mm64<false, false>(t, S5, S3, wv, lane);  // M1 Ti^T
   zero4(u);
-  mm64<false, false>(u, S0, S0, wv, lane);  // w_r . w_s
+  mm64_rows<T>(u, S0, S0, wv, lane);  // w_r . w_s
   {
     float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
