@@ -664,6 +664,64 @@ __device__ __forceinline__ void mm64_split_bf16(f32x4 (&acc)[4], const float* __
   }
 }
 
+// bf16x3 products (bf16 inputs): an fp32 operand x = hi + lo with hi = bf16(x), lo = bf16(x - hi); a product
+// sums hi*hi + hi*lo + lo*hi on the bf16 matrix cores (about 2^-16 relative; lo*lo dropped).
+__device__ __forceinline__ void split8(const f32x4& x, const f32x4& y, bf16x8& h, bf16x8& l) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = i < 4 ? x[i] : y[i - 4];
+    const __bf16 hi = (__bf16)v;
+    h[i] = hi;
+    l[i] = (__bf16)(v - (float)hi);
+  }
+}
+// A-fragments of the wave's rows, a[ks] = A(16w + r, 32 ks + 8g .. +7), from fp32 rows of stride S
+template <int S>
+__device__ __forceinline__ void split_rows(bf16x8 (&h)[2], bf16x8 (&l)[2], const float* __restrict__ A, int w,
+                                          int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const float* p = A + (16 * w + r) * S + 32 * ks + 8 * g;
+    split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), h[ks], l[ks]);
+  }
+}
+// the same fragments from fp32 values in registers, v[8 ks + i] = A(16w + r, 32 ks + 8g + i)
+__device__ __forceinline__ void split_regs(bf16x8 (&h)[2], bf16x8 (&l)[2], const float (&v)[16]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    split8(f32x4{v[8 * ks], v[8 * ks + 1], v[8 * ks + 2], v[8 * ks + 3]},
+           f32x4{v[8 * ks + 4], v[8 * ks + 5], v[8 * ks + 6], v[8 * ks + 7]}, h[ks], l[ks]);
+}
+// fp32 values of the wave's rows in that layout, from a global fp32 tile (row stride 64)
+__device__ __forceinline__ void rows32(float (&v)[16], const float* __restrict__ A, int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const float* p = A + (16 * w + r) * 64 + 32 * ks + 8 * g;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[8 * ks + i] = x[i], v[8 * ks + 4 + i] = y[i];
+  }
+}
+// acc[cb] += sum_k A(16w + r', k) B[16cb + r''][k]: A as split fragments, B an fp32 LDS tile (stride kS)
+// split while it is read
+__device__ __forceinline__ void mm64_x3(f32x4 (&acc)[4], const bf16x8 (&ah)[2], const bf16x8 (&al)[2],
+                                        const float* __restrict__ B, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const float* p = B + (16 * cb + r) * kS + 32 * ks + 8 * g;
+      bf16x8 bh, bl;
+      split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), bh, bl);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh, acc[cb], 0, 0, 0);
+    }
+}
+
 // The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
 // (plain functions rather than capturing lambdas, so that the arrays stay in registers).
 template <typename T>
@@ -679,7 +737,8 @@ __device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4
   fetch_tile(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
   fetch_rows(pV, vb, n * C, L, tid);
   fetch_tile(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
-  frag_f32(pra, St + pr * CD, w, lane);
+  if constexpr (std::is_same<T, __bf16>::value) rows32(pra, St + pr * CD, w, lane);  // for the bf16x3 logits
+  else frag_f32(pra, St + pr * CD, w, lane);
   if (fl != nullptr) {
     pF = fl[(size_t)bh * Lp + (size_t)n * C + (tid & 63)];
     poff = Off[pr];
@@ -801,7 +860,13 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
       __syncthreads();
       fetch_tile(pP, Pm + ((size_t)bh * M + (n > 1 ? n - 1 : 0)) * CD, tid);
       zero4(R);
-      mm64<false, false>(R, Xs, Ps, w, lane);  // r P_n^T
+      if constexpr (kBf) {  // r P_n^T
+        bf16x8 ah[2], al[2];
+        split_rows<kS>(ah, al, Xs, w, lane);
+        mm64_x3(R, ah, al, Ps, lane);
+      } else {
+        mm64<false, false>(R, Xs, Ps, w, lane);
+      }
     }
   }
 
@@ -864,7 +929,13 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     if (n > 0) mm64<false, true>(G, Xs, Ps, w, lane);  // dr^(n-1) P_n
     zero4(Z);
     zero4(DP);
-    mm64_ra<false>(Z, ra, Ks, lane);
+    if constexpr (kBf) {
+      bf16x8 ah[2], al[2];
+      split_regs(ah, al, ra);
+      mm64_x3(Z, ah, al, Ks, lane);
+    } else {
+      mm64_ra<false>(Z, ra, Ks, lane);
+    }
     if constexpr (kBf) mm64_bf16(DP, ob16, Vs, lane);
     else mm64_ra<false>(DP, oa, Vs, lane);
 #pragma unroll
@@ -927,8 +998,9 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   // fragments for a bf16 input)
   constexpr bool kBf = std::is_same<T, __bf16>::value;
   float ka[16], va[16];
-  bf16x8 vb16[2];
-  frag_f32(ka, kt + rown * 64, w, lane);
+  bf16x8 vb16[2], kah[2], kal[2];
+  if constexpr (kBf) split_rows<64>(kah, kal, kt + rown * 64, w, lane);
+  else frag_f32(ka, kt + rown * 64, w, lane);
   if constexpr (kBf) frag_bf16(vb16, reinterpret_cast<const __bf16*>(vb), n * C, L, w, lane);
   else frag_rows(va, vb, n * C, L, w, lane);
 
@@ -994,7 +1066,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     f32x4 ZT[4], DT[4];
     zero4(ZT);
     zero4(DT);
-    mm64_ra<false>(ZT, ka, Rs, lane);  // (r ktilde^T)^T
+    if constexpr (kBf) mm64_x3(ZT, kah, kal, Rs, lane);  // (r ktilde^T)^T
+    else mm64_ra<false>(ZT, ka, Rs, lane);
     if constexpr (kBf) mm64_bf16(DT, vb16, Os, lane);  // (dO v^T)^T
     else mm64_ra<false>(DT, va, Os, lane);
     float gz[4][4];
