@@ -722,6 +722,26 @@ __device__ __forceinline__ void mm64_x3(f32x4 (&acc)[4], const bf16x8 (&ah)[2], 
     }
 }
 
+// acc[cb] += sum_k A(16w + r', k) B[k][16cb + r'']: A as split fragments, B an fp32 LDS tile (stride kS) read
+// by columns and split while it is read
+__device__ __forceinline__ void mm64_x3_cols(f32x4 (&acc)[4], const bf16x8 (&ah)[2], const bf16x8 (&al)[2],
+                                             const float* __restrict__ B, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = B[(32 * ks + 8 * g + i) * kS + 16 * cb + r];
+      bf16x8 bh, bl;
+      split8(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}, bh, bl);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh, acc[cb], 0, 0, 0);
+    }
+}
+
 // The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
 // (plain functions rather than capturing lambdas, so that the arrays stay in registers).
 template <typename T>
@@ -926,7 +946,15 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
                      lane);
     f32x4 Z[4], DP[4];
     zero4(G);
-    if (n > 0) mm64<false, true>(G, Xs, Ps, w, lane);  // dr^(n-1) P_n
+    if (n > 0) {  // dr^(n-1) P_n
+      if constexpr (kBf) {
+        bf16x8 ah[2], al[2];
+        split_rows<kS>(ah, al, Xs, w, lane);
+        mm64_x3_cols(G, ah, al, Ps, lane);
+      } else {
+        mm64<false, true>(G, Xs, Ps, w, lane);
+      }
+    }
     zero4(Z);
     zero4(DP);
     if constexpr (kBf) {
@@ -948,7 +976,13 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
         rsum[e] += dz;
         Xs[a * kS + b] = kLn2 * dz;  // the wave's own rows; the reads of dr^(n-1) above came first
       }
-    mm64<false, true>(G, Xs, Ks, w, lane);  // + g ktilde_n
+    if constexpr (kBf) {  // + g ktilde_n
+      bf16x8 ah[2], al[2];
+      split_rows<kS>(ah, al, Xs, w, lane);
+      mm64_x3_cols(G, ah, al, Ks, lane);
+    } else {
+      mm64<false, true>(G, Xs, Ks, w, lane);
+    }
   }
   }
 
@@ -1089,6 +1123,7 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) Xs[(16 * w + 4 * g + e) * kS + 16 * cb + r] = gz[cb][e];  // after the reads of p
+    // (fp32 products: as bf16x3 these two push the kernel past its register budget)
     mm64<false, true>(aK, Xs, Rs, w, lane);            // d ktilde_n += g^T r
     if (n > 0) mm64<true, true>(aP, Gq, Rs, w, lane);  // dP_n += dr^(n-1)^T r
   }
