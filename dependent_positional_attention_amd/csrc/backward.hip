@@ -742,6 +742,61 @@ __device__ __forceinline__ void mm64_x3_cols(f32x4 (&acc)[4], const bf16x8 (&ah)
     }
 }
 
+// mm64 on the bf16 matrix cores (bf16 inputs): acc[cb] += sum_k A(16w + r', k) B(k, 16cb + r''), operands as
+// in mm64 (AT, BK, row strides SA, SB; LDS tiles or global fp32 tiles).  An operand flagged exact (EA, EB:
+// it holds bf16 numbers, i.e. w, q or k of a bf16 input) is converted exactly; any other is split into
+// hi + lo bf16, and the product sums hi*hi, hi*lo and lo*hi (about 2^-16 relative; lo*lo dropped).
+template <bool KT, int S>
+__device__ __forceinline__ void load8(float (&v)[8], const float* __restrict__ M, int rc, int k0) {
+  if constexpr (!KT) {  // M[rc][k0 .. k0 + 7]
+    const f32x4 x = *reinterpret_cast<const f32x4*>(M + rc * S + k0);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(M + rc * S + k0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = x[i], v[4 + i] = y[i];
+  } else {  // M[k0 .. k0 + 7][rc]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = M[(k0 + i) * S + rc];
+  }
+}
+template <bool EXACT>
+__device__ __forceinline__ void to_bf8(const float (&v)[8], bf16x8& h, bf16x8& l) {
+  if constexpr (EXACT) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (__bf16)v[i];
+  } else {
+    split8(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}, h, l);
+  }
+}
+template <bool AT, bool BK, int SA, int SB, bool EA, bool EB>
+__device__ __forceinline__ void mm64_bf(f32x4 (&acc)[4], const float* __restrict__ A, const float* __restrict__ B,
+                                        int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int k0 = 32 * ks + 8 * g;
+    float av[8];
+    load8<AT, SA>(av, A, 16 * w + r, k0);
+    bf16x8 ah, al;
+    to_bf8<EA>(av, ah, al);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      float bv[8];
+      load8<BK, SB>(bv, B, 16 * cb + r, k0);
+      bf16x8 bh, bl;
+      to_bf8<EB>(bv, bh, bl);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[cb], 0, 0, 0);
+      if constexpr (!EB) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[cb], 0, 0, 0);
+      if constexpr (!EA) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[cb], 0, 0, 0);
+    }
+  }
+}
+// mm64, on the bf16 matrix cores for a bf16 input
+template <typename T, bool AT, bool BK, int SA = kS, int SB = kS, bool EA = false, bool EB = false>
+__device__ __forceinline__ void mmx(f32x4 (&acc)[4], const float* A, const float* B, int w, int lane) {
+  if constexpr (std::is_same<T, __bf16>::value) mm64_bf<AT, BK, SA, SB, EA, EB>(acc, A, B, w, lane);
+  else mm64<AT, BK, SA, SB>(acc, A, B, w, lane);
+}
+
 // The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
 // (plain functions rather than capturing lambdas, so that the arrays stay in registers).
 template <typename T>
@@ -1396,64 +1451,64 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
   global_to_acc(ak, dK, wv, lane);  // dk = d ktilde + ...
   zero4(aw);
   zero4(t);
-  mm64<false, true>(t, S3, S4, wv, lane);  // X = Ti U
+  mmx<T, false, true, kS, kS, false, false>(t, S3, S4, wv, lane);  // X = Ti U
   acc_store(t, S7, wv, lane, keep);
   zero4(t);
-  mm64<false, true>(t, S5, S3, wv, lane);  // Y = R Ti
+  mmx<T, false, true, kS, kS, false, false>(t, S5, S3, wv, lane);  // Y = R Ti
   acc_store(t, S8, wv, lane, keep);
-  mm64<false, true, 64, kS>(aq, dS, S2, wv, lane);  // dq += dS K
-  mm64<true, true, 64, kS>(ak, dS, S1, wv, lane);   // dk += dS^T Q
+  mmx<T, false, true, 64, kS, false, true>(aq, dS, S2, wv, lane);  // dq += dS K
+  mmx<T, true, true, 64, kS, false, true>(ak, dS, S1, wv, lane);   // dk += dS^T Q
   __syncthreads();
   zero4(t);
-  mm64<false, true, kS, 64>(t, S7, dQ, wv, lane);  // X dqtilde
-  mm64<true, true, kS, 64>(t, S8, dK, wv, lane);   // + Y^T dktilde
+  mmx<T, false, true, kS, 64, false, false>(t, S7, dQ, wv, lane);  // X dqtilde
+  mmx<T, true, true, kS, 64, false, false>(t, S8, dK, wv, lane);   // + Y^T dktilde
   sub4(aw, t);
   zero4(u);
-  mm64<false, false, kS, 64>(u, S0, dQ, wv, lane);  // -dX = W dqtilde^T
+  mmx<T, false, false, kS, 64, true, false>(u, S0, dQ, wv, lane);  // -dX = W dqtilde^T
   zero4(t);
-  mm64<false, false, 64, kS>(t, dK, S0, wv, lane);  // -dY = dktilde W^T
-  mm64<true, false, 64, kS>(t, dS, S4, wv, lane);   //       + dS^T U^T
+  mmx<T, false, false, 64, kS, false, true>(t, dK, S0, wv, lane);  // -dY = dktilde W^T
+  mmx<T, true, false, 64, kS, false, false>(t, dS, S4, wv, lane);   //       + dS^T U^T
   zero4(rU);
-  mm64<true, false, kS, 64>(rU, S8, dS, wv, lane);  // (dS Y)^T
+  mmx<T, true, false, kS, 64, false, false>(rU, S8, dS, wv, lane);  // (dS Y)^T
   __syncthreads();
   acc_store(u, S7, wv, lane, neg);  // dX
   acc_store(t, S8, wv, lane, neg);  // dY
   __syncthreads();
   zero4(u);
-  mm64<true, true>(u, S3, S7, wv, lane);  // dU = Ti^T dX - (dS Y)^T
+  mmx<T, true, true, kS, kS, false, false>(u, S3, S7, wv, lane);  // dU = Ti^T dX - (dS Y)^T
   sub4(u, rU);
   zero4(rG);
-  mm64<false, false>(rG, S7, S4, wv, lane);  // dTi = dX U^T
-  mm64<true, true>(rG, S5, S8, wv, lane);    //     + R^T dY
+  mmx<T, false, false, kS, kS, false, false>(rG, S7, S4, wv, lane);  // dTi = dX U^T
+  mmx<T, true, true, kS, kS, false, false>(rG, S5, S8, wv, lane);    //     + R^T dY
   zero4(t);
-  mm64<false, false>(t, S8, S3, wv, lane);  // dR = dY Ti^T
+  mmx<T, false, false, kS, kS, false, false>(t, S8, S3, wv, lane);  // dR = dY Ti^T
   __syncthreads();
   acc_store(u, S4, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; });
   acc_store(t, S5, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; });
   __syncthreads();
-  mm64<false, true>(aw, S4, S1, wv, lane);  // dW += dU Q
-  mm64<true, true>(aw, S5, S2, wv, lane);   //     + dR^T K
-  mm64<true, true>(aq, S4, S0, wv, lane);   // dq += dU^T W
-  mm64<false, true>(ak, S5, S0, wv, lane);  // dk += dR W
+  mmx<T, false, true, kS, kS, false, true>(aw, S4, S1, wv, lane);  // dW += dU Q
+  mmx<T, true, true, kS, kS, false, true>(aw, S5, S2, wv, lane);   //     + dR^T K
+  mmx<T, true, true, kS, kS, false, true>(aq, S4, S0, wv, lane);   // dq += dU^T W
+  mmx<T, false, true, kS, kS, false, true>(ak, S5, S0, wv, lane);  // dk += dR W
   zero4(t);
-  mm64<false, true, kS, 64>(t, S0, dP, wv, lane);  // W dP
+  mmx<T, false, true, kS, 64, true, false>(t, S0, dP, wv, lane);  // W dP
   zero4(u);
-  mm64<false, false, kS, 64>(u, S0, dP, wv, lane);  // W dP^T
+  mmx<T, false, false, kS, 64, true, false>(u, S0, dP, wv, lane);  // W dP^T
   acc_store(t, S7, wv, lane, keep);
   acc_store(u, S8, wv, lane, keep);
   __syncthreads();
   zero4(t);
-  mm64<false, false>(t, S7, S0, wv, lane);  // dTi -= W dP W^T
+  mmx<T, false, false, kS, kS, false, true>(t, S7, S0, wv, lane);  // dTi -= W dP W^T
   sub4(rG, t);
   zero4(t);
-  mm64<false, true>(t, S3, S8, wv, lane);  // dW -= Ti W dP^T
-  mm64<true, true>(t, S3, S7, wv, lane);   //      + Ti^T W dP
+  mmx<T, false, true, kS, kS, false, false>(t, S3, S8, wv, lane);  // dW -= Ti W dP^T
+  mmx<T, true, true, kS, kS, false, false>(t, S3, S7, wv, lane);   //      + Ti^T W dP
   sub4(aw, t);
   __syncthreads();
   acc_store(rG, S4, wv, lane, keep);
   __syncthreads();
   zero4(t);
-  mm64<true, true>(t, S6, S4, wv, lane);  // M1 = A^{-T} dTi; dbeta += diag(M1)
+  mmx<T, true, true, kS, kS, false, false>(t, S6, S4, wv, lane);  // M1 = A^{-T} dTi; dbeta += diag(M1)
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -1462,7 +1517,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
   acc_store(t, S5, wv, lane, keep);
   __syncthreads();
   zero4(t);
-  mm64<false, false>(t, S5, S3, wv, lane);  // M1 Ti^T
+  mmx<T, false, false, kS, kS, false, false>(t, S5, S3, wv, lane);  // M1 Ti^T
   zero4(u);
   mm64_rows<T>(u, S0, S0, wv, lane);  // w_r . w_s
   {
@@ -1488,8 +1543,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
   }
   acc_store(t, S7, wv, lane, keep);
   __syncthreads();
-  mm64<false, true>(aw, S7, S0, wv, lane);  // dW += dN W
-  mm64<true, true>(aw, S7, S0, wv, lane);   //      + dN^T W
+  mmx<T, false, true, kS, kS, false, true>(aw, S7, S0, wv, lane);  // dW += dN W
+  mmx<T, true, true, kS, kS, false, true>(aw, S7, S0, wv, lane);   //      + dN^T W
   __syncthreads();
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
