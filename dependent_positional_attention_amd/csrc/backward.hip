@@ -1341,12 +1341,12 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
   __syncthreads();
   f32x4 t[4], u[4];
   zero4(t);
-  mm64<false, true>(t, Ta, Ut, wv, lane);  // X = Ti U
+  mmx<T, false, true, kS, kS, false, false>(t, Ta, Ut, wv, lane);  // X = Ti U
   acc_store(t, Xt, wv, lane, [](int, int, float x) { return x; });
   zero4(u);
-  mm64<false, true>(u, Rt, Ta, wv, lane);  // Y = R Ti
+  mmx<T, false, true, kS, kS, false, false>(u, Rt, Ta, wv, lane);  // Y = R Ti
   zero4(t);
-  mm64<false, true>(t, Ta, Wt, wv, lane);  // Z2 = Ti W
+  mmx<T, false, true, kS, kS, false, true>(t, Ta, Wt, wv, lane);  // Z2 = Ti W
   __syncthreads();
   acc_store(u, Ai, wv, lane, [](int, int, float x) { return x; });  // Y
   acc_store(t, Rt, wv, lane, [](int, int, float x) { return x; });  // Z2
@@ -1355,7 +1355,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
   zero4(t);
   mm64_rows<T>(t, Qt, Kt, wv, lane);
   zero4(u);
-  mm64<true, false>(u, Ut, Ai, wv, lane);
+  mmx<T, true, false, kS, kS, false, false>(u, Ut, Ai, wv, lane);
   sub4(t, u);
   {
     const int r = lane & 15, g = lane >> 4;
@@ -1370,7 +1370,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
   }
   // qtilde = Q - X^T W (scaled), ktilde = K - Y W, P = I - W^T Z2
   zero4(t);
-  mm64<true, true>(t, Xt, Wt, wv, lane);
+  mmx<T, true, true, kS, kS, false, true>(t, Xt, Wt, wv, lane);
   {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -1382,7 +1382,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
       }
   }
   zero4(t);
-  mm64<false, true>(t, Ai, Wt, wv, lane);
+  mmx<T, false, true, kS, kS, false, true>(t, Ai, Wt, wv, lane);
   {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -1394,7 +1394,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
       }
   }
   zero4(t);
-  mm64<true, true>(t, Wt, Rt, wv, lane);
+  mmx<T, true, true, kS, kS, true, false>(t, Wt, Rt, wv, lane);
   {
     const int r = lane & 15, g = lane >> 4;
     float* Pc = Pm + ((size_t)bh * M + c) * 64 * 64;
