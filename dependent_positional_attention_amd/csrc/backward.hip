@@ -1,4 +1,8 @@
-// PaTH / PaTH-FoX backward pass (fp32 arithmetic throughout, vector ALU).
+// PaTH / PaTH-FoX backward pass.  fp32 accumulation throughout.  At d = chunk = 64 the 64 x 64 x 64
+// products run on the matrix cores: fp32 (16x16x4) for fp32 inputs; bf16 (16x16x32) for bf16 inputs,
+// where a product of input values (w, q, k, v, dO are bf16 numbers) is exact and any other fp32 operand
+// is split into hi + lo bf16 (hi*hi + hi*lo + lo*hi, about 2^-16 relative).  Other sizes use the fp32
+// vector-ALU kernels.
 //
 // The pages give the forward only (PaTH summary, gist.science/ko/paper/2505.16381, section 3, and the
 // lecture notes on PaTH, brianyu43.github.io/gpumode/lecture_074.html, whose "limitations" part only

@@ -284,7 +284,10 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
  *   dlog_forget    [B,H,L] fp32 or NULL     written; given iff log_forget is
  *   chunk          16, 32 or 64 (0 = 64); d 16, 32 or 64
  *
- * All arithmetic is fp32 (bf16 inputs are widened, gradients rounded once).
+ * Accumulation is fp32 and gradients are rounded to the input dtype once.  With
+ * bf16 inputs at d = chunk = 64 the matrix products run on the bf16 matrix
+ * cores: exact for products of input values, with other fp32 operands split
+ * into hi + lo bf16 (about 2^-16 relative); fp32 inputs keep fp32 products.
  * Workspace: path_attn_bwd_workspace_bytes; it grows as B*H*(L/chunk)^2*chunk*d
  * (two fp32 vectors per key of every chunk pair: about 12.7 GB at B=8, H=24,
  * L=4096, d=64, chunk 64).  Errors as for path_attn_fwd; nothing is enqueued
