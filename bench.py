@@ -206,12 +206,17 @@ def bench_backward(args, res, ctx):
             assert torch.isfinite(g.float()).all(), "non-finite gradient"
     F = backward_flops(B, H, L, d, C)
     tf = F / (ms * 1e-3) / 1e12
+    x3_peak = MFMA_BF16_PEAK_TFLOPS / 3  # fp32-accurate products as three bf16 products (hi.hi + hi.lo + lo.hi)
     log(f"[bench] backward: {ms:.2f} ms, {B * L / (ms * 1e-3) / 1e6:.3f} M tokens/s, {tf:.2f} TFLOP/s = "
-        f"{tf / FP32_VECTOR_PEAK_TFLOPS:.3f} of fp32 vector peak (workspace {nbytes / 2**30:.1f} GiB)")
+        f"{tf / FP32_VECTOR_PEAK_TFLOPS:.3f} of the fp32 peak, {tf / x3_peak:.3f} of the bf16x3 peak "
+        f"(workspace {nbytes / 2**30:.1f} GiB)")
     del ws
     return {"workload": f"PaTH backward, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16 in/out, fp32 arithmetic",
-            "ms": ms, "steps": n, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf, "bound": "alu",
+            "ms": ms, "steps": n, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf, "bound": "mfma",
             "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / FP32_VECTOR_PEAK_TFLOPS,
+            "bf16x3_peak": x3_peak, "frac_of_bf16x3_peak": tf / x3_peak,
+            "note": "fp32-accurate arithmetic: fp32 matrix products, or bf16 products (exact for input values, "
+                    "hi+lo split otherwise); peak = fp32 matrix/vector peak, bf16x3_peak = bf16 peak / 3",
             "workspace_bytes": nbytes}
 
 
