@@ -1182,8 +1182,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) Xs[(16 * w + 4 * g + e) * kS + 16 * cb + r] = gz[cb][e];  // after the reads of p
-    // (fp32 products: as bf16x3 these two push the kernel past its register budget)
-    mm64<false, true>(aK, Xs, Rs, w, lane);            // d ktilde_n += g^T r
+    mmx<T, false, true>(aK, Xs, Rs, w, lane);  // d ktilde_n += g^T r
+    // (fp32 product: as bf16x3 it would push the kernel past its register budget)
     if (n > 0) mm64<true, true>(aP, Gq, Rs, w, lane);  // dP_n += dr^(n-1)^T r
   }
   }
