@@ -250,3 +250,15 @@ def test_bwd_validation(L):
     assert bwd_call(L, Lq=-1) == INVALID
     assert bwd_call(L, Lq=0, q=None) == OK  # empty: nothing to do
     assert bwd_call(L, B=0) == OK
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N with N > 1 exits (status 2) with a message, before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "ONE MI355X" in r.stderr and "not supported" in r.stderr
+    assert r.stdout.strip() == ""
