@@ -514,7 +514,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures PaTH attention on ONE MI355X: this build has no multi-GPU path, so "
+        print("bench.py measures PaTH attention on ONE MI355X: this library has no multi-GPU path, so "
               "--gpus N with N > 1 is not supported.", file=sys.stderr)
         sys.exit(2)
     import torch
