@@ -450,34 +450,65 @@ __global__ __launch_bounds__(kDecThreads) void decode_deferred_kernel(
   merge_block<D, VN, LPK>(mrun, lrun, o, part + ((size_t)bh * splits + split) * (D + 2));
 }
 
+// Merge of the split partials (m, l, o[D]) of one (b, h): one wave.  Lanes stride over the splits for the
+// reference max and the denominator (wave reductions); the weights of each run of 64 splits go through LDS
+// once, and each output column sums its partials with independent loads.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part, int splits,
                                                             const int* __restrict__ t_batch, int H, int64_t t_max,
                                                             T* __restrict__ out, float* __restrict__ lse) {
+  constexpr int XP = (D + 63) / 64;  // output columns per lane
+  __shared__ float wsh[64];
   const int64_t bh = blockIdx.x;
+  const int lane = threadIdx.x;
   if (seq_tokens(t_batch, bh, H, t_max) < 0) {  // invalid token count: NaN out, nothing else touched
-    for (int x = threadIdx.x; x < D; x += blockDim.x) out[bh * D + x] = from_f32<T>(__builtin_nanf(""));
-    if (lse != nullptr && threadIdx.x == 0) lse[bh] = __builtin_nanf("");
+    for (int x = lane; x < D; x += 64) out[bh * D + x] = from_f32<T>(__builtin_nanf(""));
+    if (lse != nullptr && lane == 0) lse[bh] = __builtin_nanf("");
     return;
   }
   const float* pp = part + (size_t)bh * splits * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
+  for (int s = lane; s < splits; s += 64) M = fmaxf(M, pp[(size_t)s * (D + 2)]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   float Lsum = 0.f;
-  for (int s = 0; s < splits; ++s) {
+  for (int s = lane; s < splits; s += 64) {
     const float m = pp[(size_t)s * (D + 2)];
     if (m != -INFINITY) Lsum += pp[(size_t)s * (D + 2) + 1] * fast_exp2(m - M);
   }
-  const float inv = 1.f / Lsum;
-  for (int x = threadIdx.x; x < D; x += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float m = pp[(size_t)s * (D + 2)];
-      if (m != -INFINITY) acc += pp[(size_t)s * (D + 2) + 2 + x] * fast_exp2(m - M);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) Lsum += __shfl_xor(Lsum, o, 64);
+  float acc[XP];
+#pragma unroll
+  for (int j = 0; j < XP; ++j) acc[j] = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += 64) {
+    const int n = splits - s0 < 64 ? splits - s0 : 64;
+    {
+      const float m = lane < n ? pp[(size_t)(s0 + lane) * (D + 2)] : -INFINITY;
+      wsh[lane] = m != -INFINITY ? fast_exp2(m - M) : 0.f;  // empty splits weigh nothing
     }
-    out[bh * D + x] = from_f32<T>(acc * inv);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int j = 0; j < XP; ++j) {
+      const int x = lane + 64 * j;
+      if (x < D) {
+        float a = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < n; ++i) a += wsh[i] * pp[(size_t)(s0 + i) * (D + 2) + 2 + x];
+        acc[j] += a;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
-  if (lse != nullptr && threadIdx.x == 0) lse[bh] = (M + fast_log2(Lsum)) * kLn2;
+  const float inv = 1.f / Lsum;
+#pragma unroll
+  for (int j = 0; j < XP; ++j) {
+    const int x = lane + 64 * j;
+    if (x < D) out[bh * D + x] = from_f32<T>(acc[j] * inv);
+  }
+  if (lse != nullptr && lane == 0) lse[bh] = (M + fast_log2(Lsum)) * kLn2;
 }
 
 template <typename T, int D>
