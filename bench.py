@@ -8,11 +8,13 @@ step = one path_attn_fwd call (per-chunk prep + attention scan) over inputs
 already resident in HBM; value = B*L / step time, in tokens/s.
 
 Also reported on the same JSON line:
-  roofline      the attention-scan kernel (the dominant one), timed alone with
-                HIP events on the stream it runs on: algorithmic flops per launch
-                (4 d L(L+1)/2 B H for QK^T and PV over the causal pairs, plus
-                2 C d^2 (M-1)(M-2)/2 B H for the chunk-to-chunk query transport)
-                over the measured launch time, against the bf16 MFMA peak.
+  roofline      the whole path_attn_fwd call (per-chunk prep + attention scan),
+                timed with HIP events on the stream it runs on: algorithmic flops
+                per call (4 d L(L+1)/2 B H for QK^T and PV over the causal pairs,
+                plus 2 C d^2 (M-1)(M-2)/2 B H for the chunk-to-chunk query
+                transport) over the measured call time, against the bf16 MFMA
+                peak.  The scan kernel alone, and the attention flops alone, are
+                detail fields.
   cpu_baseline  the fp64 CPU oracle timed on this host over a bounded sample of
                 the same workload (whole heads), scaled to tokens/s.
   decode        batch 32, H=24, d=64, 65536 cached tokens, 128 steps timed back
@@ -161,9 +163,10 @@ def bench_prefill(args):
     assert torch.isfinite(out.float()).all(), "non-finite output"
     F = prefill_flops(B, H, L, d, C)
     tflops = F / (ms_scan * 1e-3) / 1e12
-    log(f"[bench] prefill: step {ms_step:.3f} ms (wall {wall_ms:.3f}), prep {ms_prep:.3f} ms, scan {ms_scan:.3f} ms, "
-        f"scan {tflops:.1f} TFLOP/s = {tflops / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak; "
-        f"whole step {F / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s")
+    step_tf = F / (ms_step * 1e-3) / 1e12
+    log(f"[bench] prefill: step {ms_step:.3f} ms (wall {wall_ms:.3f}) = {step_tf:.1f} TFLOP/s = "
+        f"{step_tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak (whole call); prep alone {ms_prep:.3f} ms, "
+        f"scan alone {ms_scan:.3f} ms = {tflops / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak")
     res = dict(B=B, H=H, L=L, d=d, C=C, recipe=recipe, ms_step=ms_step, wall_ms=wall_ms, ms_prep=ms_prep,
                ms_scan=ms_scan, flops=F, scan_tflops=tflops, tokens_per_s=B * L / (ms_step * 1e-3))
     return res, x, dict(q=q, k=k, v=v, w=w, beta=beta, logf=logf, scale=x.scale, ws=ws, out=out, lse=lse)
@@ -208,15 +211,17 @@ def bench_backward(args, res, ctx):
     tf = F / (ms * 1e-3) / 1e12
     x3_peak = MFMA_BF16_PEAK_TFLOPS / 3  # fp32-accurate products as three bf16 products (hi.hi + hi.lo + lo.hi)
     log(f"[bench] backward: {ms:.2f} ms, {B * L / (ms * 1e-3) / 1e6:.3f} M tokens/s, {tf:.2f} TFLOP/s = "
-        f"{tf / FP32_VECTOR_PEAK_TFLOPS:.3f} of the fp32 peak, {tf / x3_peak:.3f} of the bf16x3 peak "
-        f"(workspace {nbytes / 2**30:.1f} GiB)")
+        f"{tf / MFMA_BF16_PEAK_TFLOPS:.3f} of the dense bf16 peak, {tf / x3_peak:.3f} of the bf16x3 peak, "
+        f"{tf / FP32_VECTOR_PEAK_TFLOPS:.3f} of the fp32 peak (workspace {nbytes / 2**30:.1f} GiB)")
     del ws
     return {"workload": f"PaTH backward, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16 in/out, fp32 arithmetic",
             "ms": ms, "steps": n, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf, "bound": "mfma",
-            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / FP32_VECTOR_PEAK_TFLOPS,
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
             "bf16x3_peak": x3_peak, "frac_of_bf16x3_peak": tf / x3_peak,
-            "note": "fp32-accurate arithmetic: fp32 matrix products, or bf16 products (exact for input values, "
-                    "hi+lo split otherwise); peak = fp32 matrix/vector peak, bf16x3_peak = bf16 peak / 3",
+            "fp32_peak": FP32_VECTOR_PEAK_TFLOPS, "frac_of_fp32_peak": tf / FP32_VECTOR_PEAK_TFLOPS,
+            "note": "most products run on the bf16 matrix cores (exact for input values, hi+lo split otherwise), "
+                    "so peak = dense bf16 peak; bf16x3_peak = bf16 peak / 3 (an fp32-accurate product as three "
+                    "bf16 products); fp32_peak = fp32 matrix/vector peak",
             "workspace_bytes": nbytes}
 
 
@@ -343,12 +348,29 @@ def bench_cpu(x, args):
     t = run(hs)
     scale = (B * H) / n
     tok_s = B * L / (t * scale)
+    # one head on one thread (the oracle's serial cost)
+    t0 = time.perf_counter()
+    oracle.fwd(x.q[0, :1], x.k[0, :1], x.v[0, :1], x.w[0, :1], x.beta[0, :1],
+               logf=None if x.logf is None else x.logf[0, :1], scale=x.scale, nthreads=1)
+    t1 = time.perf_counter() - t0
+    model = cpu_model()
     log(f"[bench] cpu oracle: {n} of {B * H} heads (all {L} rows each) in {t:.2f} s on {cores} threads "
-        f"-> {tok_s:.1f} tokens/s for the full workload")
+        f"-> {tok_s:.1f} tokens/s for the full workload; one head on one thread {t1:.2f} s ({model})")
     return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {B * H} (batch, head) slices, every one of the {L} query rows, fp64; "
                       f"time scaled by {scale:.2f} to the full B={B}, H={H} workload",
-            "seconds": t}
+            "seconds": t, "cpu_model": model, "single_thread_one_head_s": t1}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def bench_long(args):
@@ -388,7 +410,7 @@ def bench_long(args):
                             "frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
         del ws
     return {"workload": "PaTH prefill, long context: B=1, H=24, L=32768, d=64, bf16, transport " + args.transport,
-            **res}
+            "transport": args.transport, **res}
 
 
 def bench_decode(args):
@@ -541,7 +563,14 @@ def main():
     long_ctx = None if args.no_long else bench_long(args)
     peaks = measure_peaks(args)
     F = res["flops"]
-    achieved = F / (res["ms_scan"] * 1e-3) / 1e12
+    achieved = F / (res["ms_step"] * 1e-3) / 1e12
+    scan_tf = F / (res["ms_scan"] * 1e-3) / 1e12
+    B_, H_, L_, d_ = res["B"], res["H"], res["L"], res["d"]
+    attn_flops = 4.0 * d_ * (L_ * (L_ + 1) / 2) * B_ * H_
+    ktag = "<{},{},1,2,4>".format("true" if args.fox else "false", "true" if args.transport == "bf16x3" else "false")
+    ptag = "<{}>".format("true" if args.transport == "bf16x3" else "false")
+    t_scan = measured_traffic(PREFILL_COUNTERS, "mfma_attn_kernel" + ktag, "mfma_path.hip")
+    t_prep = measured_traffic(PREFILL_COUNTERS, "mfma_prep_kernel" + ptag, "mfma_path.hip")
     line = {
         "metric": "PaTH fwd tokens/s + MFMA TFLOPS% at L=4096; decode GB/s% at 64K cache",
         "value": res["tokens_per_s"],
@@ -560,12 +589,16 @@ def main():
                    "transport": args.transport, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(PREFILL_COUNTERS, "mfma_attn_kernel<{},{},1,2,4>".format(
-                         "true" if args.fox else "false", "true" if args.transport == "bf16x3" else "false"),
-                         "mfma_path.hip"),
-                     "traffic_unit": "bytes per launch", "kernel": "mfma_attn_kernel",
-                     "launch_ms": res["ms_scan"], "flops_per_launch": F,
-                     "frac_of_measured_gemm": achieved / peaks["bf16_gemm_tflops"]},
+                     "traffic": None if t_scan is None or t_prep is None else t_scan + t_prep,
+                     "traffic_unit": "HBM bytes per path_attn_fwd call (prep + scan kernels)",
+                     "kernel": "path_attn_fwd = mfma_prep_kernel + mfma_attn_kernel",
+                     "launch_ms": res["ms_step"], "flops_per_launch": F,
+                     "frac_of_measured_gemm": achieved / peaks["bf16_gemm_tflops"],
+                     "attention_flops_per_launch": attn_flops,
+                     "attention_only_frac": attn_flops / (res["ms_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "scan_only": {"kernel": "mfma_attn_kernel", "launch_ms": res["ms_scan"], "achieved": scan_tf,
+                                   "frac": scan_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": t_scan},
+                     "prep_only": {"kernel": "mfma_prep_kernel", "launch_ms": res["ms_prep"], "traffic": t_prep}},
         "prefill_detail": {"ms_prep": res["ms_prep"], "ms_scan": res["ms_scan"], "wall_ms_per_step": res["wall_ms"],
                            "step_tflops": F / (res["ms_step"] * 1e-3) / 1e12,
                            "step_frac_of_peak": F / (res["ms_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},

@@ -5,7 +5,9 @@ own exact forward.
 Tolerance (per gradient tensor, relative to its largest reference entry): the fp32 path keeps fp32
 throughout, so its error is fp32 rounding carried through the chunk chain; the bf16 path widens bf16
 inputs, works in fp32, and rounds each gradient to bf16 once (2^-9 relative) after using the forward's
-bf16-rounded output in D_i = dO_i . o_i, which moves every dz by up to p_ij |dO_i| |o_i| 2^-9.
+bf16-rounded output in D_i = dO_i . o_i, which moves every dz by up to p_ij |dO_i| |o_i| 2^-9.  The bf16
+bound is the spec bf16 relative-L2 bound, 1e-2, applied to max-abs (relative to the largest entry)
+and to rel-L2 alike.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ from tests.gpu_util import dev, errors, fwd_inputs_dev, host
 
 pytestmark = pytest.mark.gpu
 
-GRAD_TOL = {"f32": 1e-5, "bf16": 1.5e-2}
+GRAD_TOL = {"f32": 1e-5, "bf16": 1e-2}
 NAMES = ("dq", "dk", "dv", "dw", "dbeta", "dlogf")
 
 
@@ -44,12 +46,15 @@ def check(x: synth.FwdInputs, chunk: int, what: str, seed: int = 0):
             continue
         assert np.all(np.isfinite(g)), f"{what} {name}: non-finite values"
         if float(np.max(np.abs(r))) == 0.0:
-            # an exactly zero gradient (of q, k, w, beta, f with a single token, whose output is v_0): only
-            # the rounding of the forward's output enters, through D_i = dO_i . o_i, which moves each dz by at
-            # most 2^-9 |dO_i| |o_i| with |o_i| <= max |v|; the gradients multiply dz by q, k, w values
-            bound = (2.0 ** -9 * np.max(np.abs(dout)) * np.max(np.abs(x.v)) *
-                     max(np.max(np.abs(x.q)), np.max(np.abs(x.k)), 1.0) * x.shape[-2])
-            assert np.max(np.abs(g)) <= bound, f"{what} {name}: {np.max(np.abs(g)):.3e} where the gradient is 0"
+            # an exactly zero gradient (a single token: o_0 = v_0 exactly, so dz_00 = dO_0 . v_0 - D_0 is 0 in
+            # exact arithmetic).  The kernels form dO . v and D = dO . o as two fp32 sums of the same d
+            # products in different orders, each within d 2^-24 sum|dO_x v_x| <= d 2^-24 |dO| |v| of the exact
+            # value; every gradient multiplies dz by at most two of scale q, scale k, w, beta (<= 2).
+            nrm = lambda a: float(np.max(np.linalg.norm(np.asarray(a, np.float64), axis=-1)))
+            e_dz = 2 * x.shape[-1] * 2.0 ** -24 * nrm(dout) * nrm(x.v)
+            bound = e_dz * 2 * (1 + x.scale) * max(nrm(x.q), 1.0) * max(nrm(x.k), 1.0)
+            assert np.max(np.abs(g)) <= bound, \
+                f"{what} {name}: {np.max(np.abs(g)):.3e} where the gradient is 0 (bound {bound:.1e})"
             worst[name] = (0.0, 0.0)
             continue
         ma, rel = errors(g, r)
