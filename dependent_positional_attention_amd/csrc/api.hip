@@ -33,6 +33,8 @@ hipError_t decode_step(bool bf16, int d, void* kc, void* vc, float* fc, int64_t 
                        const float* beta_t, const float* f_t, void* out, float* lse, int64_t BH, float scale,
                        int splits, float* part, hipStream_t st);
 hipError_t slot_bias_run(const float* logf, int64_t BH, int64_t L, int64_t cap, float* fc, hipStream_t st);
+size_t decode_scratch_floats();
+hipError_t decode_scratch(hipStream_t st, float** ptr);
 int decode_max_period();
 hipError_t decode_step_deferred(bool bf16, int d, void* kc, void* vc, float* fc, int64_t cap, int64_t t,
                                 int64_t t_cur, int period, float* state, const void* q_t, const void* k_t,
@@ -132,6 +134,8 @@ const char* path_status_string(int status) {
       return "unsupported configuration";
     case PATH_ERR_HIP:
       return "HIP runtime error";
+    case PATH_ERR_SCRATCH:
+      return "problem exceeds the library's fixed scratch buffer (use the entry point with a workspace)";
     default:
       return "unknown status";
   }
@@ -290,6 +294,36 @@ path_status path_decode_step(void* kcache, void* vcache, float* fcache, int64_t 
                               k_t, v_t, w_t, beta_t, log_forget_t, out, lse, BH, scale, (int)S,
                               static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
+
+path_status path_decode_step_noalloc(void* kcache, void* vcache, float* fcache, int64_t capacity, int64_t t,
+                                     const int* t_batch, const void* q_t, const void* k_t, const void* v_t,
+                                     const void* w_t, const float* beta_t, const float* log_forget_t, void* out,
+                                     float* lse, int64_t B, int64_t H, int d, float scale, int dtype, int splits,
+                                     void* stream) {
+  if (B < 0 || H < 0 || capacity < 0 || splits < 0) return PATH_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype) || !decode_supported(d)) return PATH_ERR_UNSUPPORTED;
+  if (t < 0 || t >= capacity) return PATH_ERR_INVALID_ARG;
+  if ((log_forget_t == nullptr) != (fcache == nullptr)) return PATH_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  if (BH == 0) return PATH_OK;
+  if (!kcache || !vcache || !q_t || !k_t || !v_t || !w_t || !beta_t || !out) return PATH_ERR_INVALID_ARG;
+  if (misaligned(kcache) || misaligned(vcache) || misaligned(q_t) || misaligned(k_t) || misaligned(v_t) ||
+      misaligned(w_t) || misaligned(beta_t) || misaligned(out) || misaligned(lse) || misaligned(fcache) ||
+      misaligned(log_forget_t) || misaligned(t_batch))
+    return PATH_ERR_UNSUPPORTED;
+  if (H > (int64_t)0x7fffffff || BH > kMaxGridY) return PATH_ERR_UNSUPPORTED;
+  const int64_t S = splits > 0 ? splits : decode_auto_splits(t + 1);
+  if (S > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
+  // the split partials must fit the fixed scratch array (checked before anything touches the device)
+  if (BH > (int64_t)decode_scratch_floats() / (S * (int64_t)(d + 2))) return PATH_ERR_SCRATCH;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* part = nullptr;
+  if (decode_scratch(st, &part) != hipSuccess) return PATH_ERR_HIP;
+  return from_hip(decode_step(dtype == PATH_DTYPE_BF16, d, kcache, vcache, fcache, capacity, t, t_batch, (int)H, q_t,
+                              k_t, v_t, w_t, beta_t, log_forget_t, out, lse, BH, scale, (int)S, part, st));
+}
+
+size_t path_decode_noalloc_scratch_bytes(void) { return decode_scratch_floats() * sizeof(float); }
 
 path_status path_decode_deferred_state_bytes(int64_t B, int64_t H, int d, size_t* bytes) {
   if (bytes == nullptr || B < 0 || H < 0) return PATH_ERR_INVALID_ARG;

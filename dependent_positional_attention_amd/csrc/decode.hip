@@ -18,6 +18,8 @@
 // exactly like the keys absorb the newest transition; the new slot starts at 0.
 // Ragged batches: an optional per-sequence token count replaces the uniform t;
 // the split of the key range is sized for the uniform bound.
+#include <mutex>
+
 #include "common.h"
 
 namespace pathattn {
@@ -576,6 +578,52 @@ hipError_t decode_step_deferred(bool bf16, int d, void* kc, void* vc, float* fc,
 }
 
 bool decode_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// ------------------------------------------------------------------------------------ fixed scratch
+// The split partials of path_decode_step_noalloc live in this file-scope device array instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy for the life of the process.  In
+// host code the array's name is only a stand-in: its device address is resolved once per device with
+// hipGetSymbolAddress (with that device current) and that address is what the kernels receive.  Every
+// (b, h, split) partial is written by the update/attend kernel before the combine kernel reads it, so the
+// array needs no clearing between calls; calls that overlap on one device race on it.
+constexpr size_t kScratchFloats = (size_t)8 << 20;  // 32 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t decode_scratch_floats() { return kScratchFloats; }
+
+// Device address of the scratch array on the device that runs `st` (the current device for the null
+// stream), resolved on the first call for that device with the device made current for the lookup.
+hipError_t decode_scratch(hipStream_t st, float** ptr) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (st != nullptr) {
+    e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // Keys per split chosen automatically: about 1024, so a 64K cache uses 64 splits per (b, h).
 int64_t decode_auto_splits(int64_t keys) {

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # PATHATTN_LIB points the binding at another build of the same library (A/B comparisons).
 LIB_PATH = os.environ.get("PATHATTN_LIB") or os.path.join(_HERE, "libpathattn.so")
 
-PATH_OK, PATH_ERR_INVALID_ARG, PATH_ERR_UNSUPPORTED, PATH_ERR_HIP = 0, 1, 2, 3
+PATH_OK, PATH_ERR_INVALID_ARG, PATH_ERR_UNSUPPORTED, PATH_ERR_HIP, PATH_ERR_SCRATCH = 0, 1, 2, 3, 4
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 TRANSPORT = {"bf16": 0, "bf16x3": 1}
 
@@ -45,7 +45,8 @@ class WsLayout(ctypes.Structure):
 EXPORTS = ("path_abi_version", "path_status_string", "path_attn_fwd_workspace_bytes", "path_attn_fwd",
            "path_attn_prep", "path_attn_scan", "path_attn_workspace_layout", "path_decode_workspace_bytes",
            "path_decode_step", "path_attn_cache_from_prefill", "path_decode_deferred_state_bytes",
-           "path_decode_step_deferred", "path_attn_bwd_workspace_bytes", "path_attn_bwd")
+           "path_decode_step_deferred", "path_attn_bwd_workspace_bytes", "path_attn_bwd", "path_decode_step_noalloc",
+           "path_decode_noalloc_scratch_bytes")
 
 
 def lib():
@@ -73,12 +74,15 @@ def lib():
         L.path_decode_deferred_state_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         L.path_decode_step_deferred.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, i64, i64, i32, f32, i32, i32, vp, sz, vp]
+        L.path_decode_step_noalloc.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32,
+                                               f32, i32, i32, vp]
+        L.path_decode_noalloc_scratch_bytes.argtypes, L.path_decode_noalloc_scratch_bytes.restype = [], sz
         L.path_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(sz)]
         L.path_attn_bwd.argtypes = [vp] * 15 + [i64, i64, i64, i32, i32, f32, i32, vp, sz, vp]
         for f in ("path_attn_fwd_workspace_bytes", "path_attn_workspace_layout", "path_attn_fwd", "path_attn_prep",
                   "path_attn_scan", "path_decode_workspace_bytes", "path_decode_step", "path_attn_cache_from_prefill",
                   "path_decode_deferred_state_bytes", "path_decode_step_deferred", "path_attn_bwd_workspace_bytes",
-                  "path_attn_bwd"):
+                  "path_attn_bwd", "path_decode_step_noalloc"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -272,6 +276,39 @@ def path_decode_step(kcache, vcache, t: int, q_t, k_t, v_t, w_t, beta_t, log_for
         _ptr(kcache), _ptr(vcache), _ptr(fcache), cap, int(t), _ptr(t_batch), _ptr(q_t), _ptr(k_t), _ptr(v_t),
         _ptr(w_t), _ptr(beta_t), _ptr(log_forget_t), _ptr(out), _ptr(lse), B, H, d, float(scale),
         DTYPE[kcache.dtype], int(splits), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def path_decode_noalloc_scratch_bytes() -> int:
+    return int(lib().path_decode_noalloc_scratch_bytes())
+
+
+def path_decode_step_noalloc(kcache, vcache, t: int, q_t, k_t, v_t, w_t, beta_t, log_forget_t=None, *, fcache=None,
+                             t_batch=None, scale: Optional[float] = None, splits: int = 0, out, lse=None,
+                             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """path_decode_step with the split partials in the library's fixed scratch array (no workspace): the
+    caller passes every output buffer (out, and lse unless it is not wanted), so nothing is allocated here."""
+    _require(kcache, "kcache")
+    B, H, cap, d = kcache.shape
+    _require(vcache, "vcache", kcache.dtype, kcache.shape)
+    for name, x in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t), ("out", out)):
+        _require(x, name, kcache.dtype, (B, H, d))
+    _require(beta_t, "beta_t", torch.float32, (B, H))
+    if (log_forget_t is None) != (fcache is None):
+        raise ValueError("PaTH-FoX decode needs both log_forget_t and fcache")
+    if log_forget_t is not None:
+        _require(log_forget_t, "log_forget_t", torch.float32, (B, H))
+        _require(fcache, "fcache", torch.float32, (B, H, cap))
+    if t_batch is not None:
+        _require(t_batch, "t_batch", torch.int32, (B,))
+    if lse is not None:
+        _require(lse, "lse", torch.float32, (B, H))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("path_decode_step_noalloc", lib().path_decode_step_noalloc(
+        _ptr(kcache), _ptr(vcache), _ptr(fcache), cap, int(t), _ptr(t_batch), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+        _ptr(w_t), _ptr(beta_t), _ptr(log_forget_t), _ptr(out), _ptr(lse), B, H, d, float(scale),
+        DTYPE[kcache.dtype], int(splits), _stream(stream)))
     return out, lse
 
 

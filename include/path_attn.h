@@ -15,8 +15,9 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or synchronises, and keeps no global mutable
- *     state.  All work is enqueued asynchronously on `stream` (a hipStream_t;
- *     NULL is the null stream).
+ *     state (except path_decode_step_noalloc's fixed per-device scratch
+ *     array, described there).  All work is enqueued asynchronously on
+ *     `stream` (a hipStream_t; NULL is the null stream).
  *   - Layouts are dense row-major: q, k, v, w, out are [B, H, L, d] with d
  *     fastest; beta, log_forget, lse are [B, H, L].  Element type of q, k, v,
  *     w and out is `dtype`; beta, log_forget and lse are always fp32.
@@ -38,13 +39,14 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 6
+#define PATH_ABI_VERSION 7
 
 typedef enum {
   PATH_OK = 0,
   PATH_ERR_INVALID_ARG = 1, /* null pointer, negative size, t >= capacity, workspace too small, ... */
   PATH_ERR_UNSUPPORTED = 2, /* head dim / chunk / dtype combination not built, misaligned pointer */
-  PATH_ERR_HIP = 3          /* a HIP launch or runtime call failed */
+  PATH_ERR_HIP = 3,         /* a HIP launch or runtime call failed */
+  PATH_ERR_SCRATCH = 4      /* the problem exceeds the fixed scratch buffer of a no-allocation entry point */
 } path_status;
 
 typedef enum { PATH_DTYPE_F32 = 0, PATH_DTYPE_BF16 = 1 } path_dtype;
@@ -200,6 +202,37 @@ path_status path_decode_step(void* kcache, void* vcache, float* fcache, int64_t 
                              const float* beta_t, const float* log_forget_t, void* out, float* lse, int64_t B,
                              int64_t H, int d, float scale, int dtype, int splits, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * path_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results as
+ * path_decode_step (bit for bit); the split partials go to a fixed scratch
+ * array inside the library instead of a caller workspace.  Nothing is
+ * allocated or freed and nothing synchronises.
+ *
+ * Limit: B * H * S * (d + 2) * 4 bytes must fit the scratch array
+ * (path_decode_noalloc_scratch_bytes(), 32 MiB), where S is `splits` or, for
+ * splits = 0, the automatic count (about one split per 1024 keys).  Larger
+ * problems return PATH_ERR_SCRATCH and enqueue nothing.  The batch-32,
+ * 24-head, d = 64 decode with a 64K-token cache uses 13.2 MiB.
+ *
+ * Each GPU holds its own copy of the array for the life of the process, and
+ * every call on that GPU shares it (its contents are left over from the last
+ * call; the kernels overwrite every partial they read, so nothing needs
+ * clearing).  Calls that overlap on one GPU -- concurrent streams, or threads
+ * sharing a device -- race on the array: serialise them.  The first call on a
+ * device resolves the array's device address (a host-side lookup, not an
+ * allocation).
+ */
+path_status path_decode_step_noalloc(void* kcache, void* vcache, float* fcache, int64_t capacity, int64_t t,
+                                     const int* t_batch, const void* q_t, const void* k_t, const void* v_t,
+                                     const void* w_t, const float* beta_t, const float* log_forget_t, void* out,
+                                     float* lse, int64_t B, int64_t H, int d, float scale, int dtype, int splits,
+                                     void* stream);
+
+/* Size in bytes of path_decode_step_noalloc's fixed scratch array. */
+size_t path_decode_noalloc_scratch_bytes(void);
 
 /*
  * Decode with deferred key updates.  The step is path_decode_step's (same

@@ -40,8 +40,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 6
-    for s in range(4):
+    assert L.path_abi_version() == 7
+    for s in range(5):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"
 
