@@ -25,9 +25,10 @@ Also reported on the same JSON line:
                 64-token sub-chunks; the scan moves its queries once per chunk).
   cache_handoff the prefill workspace turned into a decode cache (path_attn_cache_from_prefill)
                 at the prefill shape: time and HBM bytes it must move.
-  long_context  B=1, H=24, L=32768: whole prefill step at chunk 64 and at
-                chunk 128 (transport once per 128 keys), tokens/s and the
-                fraction of bf16 peak for each chunk size's own flop count.
+  long_context  B=1, H=24, L=32768: whole prefill step at chunk 64, 128 and
+                256 (transport once per chunk), tokens/s and the fraction of
+                bf16 peak for each chunk size's own flop count; with the chunk
+                sweep at L=4096 this is the table chunk = 0 follows.
 """
 from __future__ import annotations
 
@@ -322,7 +323,7 @@ def bench_chunks(args, ctx):
         res[f"chunk{C}"] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3)}
         log(f"[bench] chunk sweep: chunk {C}: {ms:.3f} ms per step, {B * L / (ms * 1e-3) / 1e6:.2f} M tokens/s")
     return {"workload": f"PaTH prefill step at B={B}, H={H}, L={L}, d={d}, bf16, transport {args.transport}; "
-                        "median of 4 interleaved rounds of 5 steps", **res}
+                        "median of 4 interleaved rounds of 5 steps", "auto_chunk": auto_chunk(B, H, L, d), **res}
 
 
 def bench_cpu(x, args):
@@ -373,8 +374,17 @@ def cpu_model():
     return "unknown"
 
 
+def auto_chunk(B, H, L, d):
+    """The chunk path_attn_fwd uses for chunk = 0 (from the workspace layout it plans)."""
+    import torch
+    from dependent_positional_attention_amd import native
+    lay = native.path_attn_workspace_layout(B, H, L, d, 0, torch.bfloat16, "bf16")
+    return 64 if lay.layout_id == 1 else -(-L // lay.num_chunks)
+
+
 def bench_long(args):
-    """Long-context prefill (B=1, H=24, L=32768, d=64, bf16): chunk 64 and chunk 128, whole step."""
+    """Long-context prefill (B=1, H=24, L=32768, d=64, bf16): whole step at chunk 64, 128 and 256, interleaved
+    round by round (median of 3 rounds of 3 steps), each against its own flop count."""
     import torch
     from dependent_positional_attention_amd import native, synth
 
@@ -389,28 +399,33 @@ def bench_long(args):
     beta = torch.from_numpy(x.beta).cuda()
     out = torch.empty_like(q)
     lse = torch.empty((B, H, L), device="cuda", dtype=torch.float32)
-    res = {}
-    for C in (64, 128):
-        nbytes = native.path_attn_fwd_workspace_bytes(B, H, L, d, C, torch.bfloat16, args.transport)
-        ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
-
-        def step():
-            native.path_attn_fwd(q, k, v, w, beta, None, scale=x.scale, chunk=C, transport=args.transport,
-                                 out=out, lse=lse, workspace=ws)
-
+    chunks = (64, 128, 256)
+    wss = {C: torch.empty(native.path_attn_fwd_workspace_bytes(B, H, L, d, C, torch.bfloat16, args.transport),
+                          device="cuda", dtype=torch.uint8) for C in chunks}
+    steps = {C: (lambda C=C: native.path_attn_fwd(q, k, v, w, beta, None, scale=x.scale, chunk=C,
+                                                  transport=args.transport, out=out, lse=lse, workspace=wss[C]))
+             for C in chunks}
+    for C in chunks:
         for _ in range(2):
-            step()
-        torch.cuda.synchronize()
-        ms = timed(step, 5)
+            steps[C]()
+    torch.cuda.synchronize()
+    times = {C: [] for C in chunks}
+    for _ in range(3):
+        for C in chunks:
+            times[C].append(timed(steps[C], 3))
+    res = {}
+    for C in chunks:
+        ms = sorted(times[C])[len(times[C]) // 2]
         F = prefill_flops(B, H, L, d, C)
         tf = F / (ms * 1e-3) / 1e12
         log(f"[bench] long context chunk {C}: step {ms:.3f} ms, {B * L / (ms * 1e-3) / 1e6:.2f} M tokens/s, "
-            f"{tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak (whole step)")
+            f"{tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak (whole step, own flop count)")
         res[f"chunk{C}"] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf,
                             "frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
-        del ws
-    return {"workload": "PaTH prefill, long context: B=1, H=24, L=32768, d=64, bf16, transport " + args.transport,
-            "transport": args.transport, **res}
+    del wss
+    return {"workload": "PaTH prefill, long context: B=1, H=24, L=32768, d=64, bf16, transport " + args.transport
+                        + "; median of 3 interleaved rounds of 3 steps",
+            "transport": args.transport, "auto_chunk": auto_chunk(B, H, L, d), **res}
 
 
 def bench_decode(args):

@@ -53,11 +53,17 @@ bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintpt
 
 bool valid_dtype(int dt) { return dt == PATH_DTYPE_F32 || dt == PATH_DTYPE_BF16; }
 
-// chunk 0 selects the chunk measured fastest for the path: 256 on the matrix-core path (the scan then
-// moves its queries once per 256 keys), 64 on the vector path.
-int resolve_chunk(int d, int dtype, int chunk) {
+// chunk 0 selects the chunk measured fastest for the path and length.  Matrix-core path (bf16, d = 64),
+// whole prefill call, chunk 64 / 128 / 256 at about 3.1M tokens per call:
+//   L = 512, 1024, 2048:          chunk 64 fastest (the grouping kernel and the partial top group cost more
+//                                  than the transports they save at 8-32 chunks per sequence)
+//   L = 4096, 8192, 16384, 32768: chunk 256 fastest (4-10% ahead of chunk 64; the scan moves its queries
+//                                  once per 256 keys)
+// so lengths up to kAutoChunkSplit take 64 and longer ones 256.  The vector path takes 64.
+constexpr int64_t kAutoChunkSplit = 2048;
+int resolve_chunk(int d, int dtype, int chunk, int64_t L) {
   if (chunk != 0) return chunk;
-  if (dtype == PATH_DTYPE_BF16 && mfma_supported(d, 256)) return 256;
+  if (dtype == PATH_DTYPE_BF16 && mfma_supported(d, 256) && L > kAutoChunkSplit) return 256;
   return 64;
 }
 
@@ -65,7 +71,7 @@ int resolve_chunk(int d, int dtype, int chunk) {
 // for the shape, the vector path otherwise.
 path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype, int transport,
                      path_ws_layout* lay) {
-  chunk = resolve_chunk(d, dtype, chunk);
+  chunk = resolve_chunk(d, dtype, chunk, L);
   if (B < 0 || H < 0 || L < 0 || d <= 0 || chunk <= 0) return PATH_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return PATH_ERR_UNSUPPORTED;
   if (transport != PATH_TRANSPORT_BF16 && transport != PATH_TRANSPORT_BF16X3) return PATH_ERR_INVALID_ARG;
@@ -173,7 +179,7 @@ path_status run_fwd(int phases, const void* q, const void* k, const void* v, con
   path_ws_layout lay;
   const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
   if (s != PATH_OK) return s;
-  chunk = resolve_chunk(d, dtype, chunk);
+  chunk = resolve_chunk(d, dtype, chunk, L);
   const int64_t BH = B * H;
   if (BH == 0 || L == 0) return PATH_OK;
   if (!workspace) return PATH_ERR_INVALID_ARG;
@@ -235,7 +241,7 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
   path_ws_layout lay;
   const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
   if (s != PATH_OK) return s;
-  chunk = resolve_chunk(d, dtype, chunk);
+  chunk = resolve_chunk(d, dtype, chunk, L);
   if (capacity < L) return PATH_ERR_INVALID_ARG;
   if ((log_forget == nullptr) != (fcache == nullptr)) return PATH_ERR_INVALID_ARG;
   const int64_t BH = B * H;

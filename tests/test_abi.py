@@ -90,9 +90,9 @@ def test_workspace_planning_grouped_chunks(L, chunk, groups):
 
 
 def test_chunk_zero_selects_the_fastest_chunk(L):
-    """chunk 0 plans exactly what chunk 256 plans on the matrix-core path and chunk 64 on the vector path."""
-    for args, chunk in (((2, 3, 1000, 64), 256), ((1, 2, 100, 16), 64)):
-        dtype = BF16 if chunk == 256 else F32
+    """chunk 0 plans exactly what the measured table picks: chunk 256 on the matrix-core path beyond 2048
+    tokens, chunk 64 up to 2048 tokens and on the vector path."""
+    for args, chunk, dtype in (((2, 3, 5000, 64), 256, BF16), ((2, 3, 1000, 64), 64, BF16), ((1, 2, 100, 16), 64, F32)):
         for transport in (0, 1):
             a, b = native.WsLayout(), native.WsLayout()
             assert L.path_attn_workspace_layout(*args, 0, dtype, transport, ctypes.byref(a)) == OK
@@ -262,3 +262,18 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "ONE MI355X" in r.stderr and "not supported" in r.stderr
     assert r.stdout.strip() == ""
+
+
+@pytest.mark.parametrize("L,layout_id", [(64, 1), (2048, 1), (2049, 2), (4096, 2), (32768, 2)])
+def test_automatic_chunk_table(L, layout_id):
+    """chunk = 0 on the matrix-core path (bf16, d = 64): 64-token chunks (layout 1) up to 2048 tokens,
+    256-token chunks (layout 2, four sub-chunks per chunk) beyond, as measured fastest; the vector path
+    (fp32) takes 64."""
+    lay = native.WsLayout()
+    lib = native.lib()
+    assert lib.path_attn_workspace_layout(1, 2, L, 64, 0, BF16, 0, ctypes.byref(lay)) == OK
+    assert lay.layout_id == layout_id
+    if layout_id == 2:
+        assert lay.num_chunks == -(-L // 256) and lay.num_sub_chunks == -(-L // 64)
+    assert lib.path_attn_workspace_layout(1, 2, L, 64, 0, F32, 0, ctypes.byref(lay)) == OK
+    assert lay.layout_id == 0 and lay.num_chunks == -(-L // 64)
