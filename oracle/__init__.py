@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "path_oracle.c")
-_LIB = os.path.join(_HERE, "libpathoracle.so")
+# PATHORACLE_LIB points the loader at another build of the same source (the sanitizer run builds one)
+_LIB = os.environ.get("PATHORACLE_LIB") or os.path.join(_HERE, "libpathoracle.so")
 _lib = None
 
 _D = ctypes.POINTER(ctypes.c_double)
