@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued (see path_attn.h).
 #include "path_attn.h"
 
+#include "backward.h"
 #include "common.h"
 
 namespace pathattn {
@@ -20,11 +21,6 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
                     void* p2_hi, void* p2_lo, float* Sm, float* fl, float* ftot, hipStream_t st);
 hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
                           int64_t BH, int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st);
-// backward.hip
-hipError_t bwd_run(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
-                   const float* beta, const float* logf, const void* out, const float* lse, const void* dout,
-                   void* dq, void* dk, void* dv, void* dw, float* dbeta, float* dlogf, int64_t BH, int64_t L,
-                   float scale, const bwd_buffers& b, hipStream_t st);
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
@@ -375,7 +371,7 @@ namespace {
 
 // Byte offsets of the backward's buffers in its workspace (chunk already resolved).
 struct bwd_plan {
-  int64_t off[17];
+  int64_t off[18];
   int64_t total;
 };
 
@@ -383,15 +379,16 @@ path_status plan_bwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   if (B < 0 || H < 0 || L < 0 || d <= 0 || chunk <= 0) return PATH_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return PATH_ERR_UNSUPPORTED;
   if (!vec_supported(d, chunk)) return PATH_ERR_UNSUPPORTED;
-  const int64_t BH = B * H, M = (L + chunk - 1) / chunk, Lp = M * chunk, NP = M * (M - 1) / 2;
+  const int64_t BH = B * H, M = (L + chunk - 1) / chunk, Lp = M * chunk, NPB = bwd_band_pairs(M);
   const int64_t rows = BH * Lp * 4, mat = BH * Lp * d * 4, dd = BH * M * d * d * 4, cc = BH * M * chunk * chunk * 4;
-  const int64_t pairs = BH * NP * chunk * d * 4;
-  const int64_t sizes[17] = {mat, mat, dd, cc, rows, BH * M * 4,      // qt kt Pm Sm fl ftot
-                             pairs, pairs, BH * NP * 4,               // St Gst Off
+  const int64_t pairs = BH * NPB * chunk * d * 4;  // one band of query chunks at a time
+  const int64_t sizes[18] = {mat, mat, dd, cc, rows, BH * M * 4,      // qt kt Pm Sm fl ftot
+                             pairs, pairs, BH * NPB * 4,              // St Gst Off
                              rows, rows, rows, rows,                  // lse2 Dv drow dcol
-                             mat, mat, dd, cc};                       // dqt dkt dPm dSm
+                             mat, mat, dd, cc,                        // dqt dkt dPm dSm
+                             mat};                                    // dva
   int64_t o = 0;
-  for (int i = 0; i < 17; ++i) {
+  for (int i = 0; i < 18; ++i) {
     p->off[i] = o;
     o = round_up(o + sizes[i], kAlign);
   }
@@ -440,7 +437,7 @@ path_status path_attn_bwd(const void* q, const void* k, const void* v, const voi
   char* ws = static_cast<char*>(workspace);
   auto f = [&](int i) { return reinterpret_cast<float*>(ws + p.off[i]); };
   const bwd_buffers b{f(0), f(1), f(2), f(3), f(4), f(5), f(6), f(7), f(8),
-                      f(9), f(10), f(11), f(12), f(13), f(14), f(15), f(16)};
+                      f(9), f(10), f(11), f(12), f(13), f(14), f(15), f(16), f(17)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == PATH_DTYPE_BF16;
   return from_hip(bwd_run(bf16, d, chunk, q, k, v, w, beta, log_forget, out, lse, dout, dq, dk, dv, dw, dbeta,

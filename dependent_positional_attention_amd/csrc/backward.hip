@@ -12,7 +12,9 @@
 //   forward per query chunk m:  r^(m-1) = qtilde_m (scaled by scale*log2e),
 //                               z_mn = r^(n) ktilde_n^T (+ FoX bias), r^(n-1) = r^(n) P_n^T
 //   backward per query chunk m: the states r^(n) are kept (they cannot be recovered from r^(n-1):
-//                               P_n is singular when some beta_s = 1), then, for n = 0 .. m-1,
+//                               P_n is singular when some beta_s = 1; the query chunks go in bands
+//                               of about sqrt(M), so only one band's states are held), then, for
+//                               n = 0 .. m-1,
 //                               dr^(n) = g_mn ktilde_n + dr^(n-1) P_n,   g = ln2 * dz
 //   dP_n     = sum_{m > n} dr^(n-1)_m^T r^(n)_m          (d x d, reduced per key chunk)
 //   dktilde_n = sum_{m > n} g_mn^T r^(n)_m,  dv_n = sum_{m >= n} p_mn^T dO_m
@@ -35,6 +37,7 @@
 // PaTH-FoX: z_ij carries F_i - F_j, so dF_t = sum_j dz_tj - sum_i dz_it and df_s = sum_{t >= s} dF_t.
 #include <type_traits>
 
+#include "backward.h"
 #include "common.h"
 
 namespace pathattn {
@@ -55,20 +58,31 @@ struct BwdShape {
 
 __host__ __device__ inline int64_t pair_index(int64_t m, int64_t n) { return m * (m - 1) / 2 + n; }
 
+// The chunk-pair kernels run one band of query chunks [mb, me) at a time (bands ascending, about
+// sqrt(M) chunks each), so that only that band's pair states are held: the states of pair (m, n < m)
+// sit in per-head slabs of `stride` pairs, in pair_index order from (mb, 0).  The key-side sums over
+// query chunks carry over from band to band in the workspace (fixed order: deterministic).
+struct pair_band {
+  int64_t mb, me, stride;
+  __host__ __device__ size_t slot(int64_t bh, int64_t m, int64_t n) const {
+    return (size_t)bh * stride + (size_t)(pair_index(m, n) - pair_index(mb, 0));
+  }
+};
+
 }  // namespace
 
 // ------------------------------------------------------------------------------- query chunks
-// One block per (query chunk m, batch*head).  Writes the states r^(n) and incoming gradients
-// dr^(n-1) of every pair (m, n < m), the FoX offsets of each pair, the row statistics, the
+// One block per (query chunk m of the band, batch*head).  Writes the states r^(n) and incoming
+// gradients dr^(n-1) of every pair (m, n < m), the FoX offsets of each pair, the row statistics, the
 // in-chunk logit gradient dS (unscaled units), d qtilde (unscaled) and the row sums of dz.
 template <typename T, int D, int C>
 __global__ __launch_bounds__(256) void bwd_query_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
-    int64_t L, int64_t M, float scale, float* __restrict__ St, float* __restrict__ Gst, float* __restrict__ Off,
-    float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow, float* __restrict__ dqt,
-    float* __restrict__ dSm) {
+    int64_t L, int64_t M, float scale, pair_band band, float* __restrict__ St, float* __restrict__ Gst,
+    float* __restrict__ Off, float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow,
+    float* __restrict__ dqt, float* __restrict__ dSm) {
   using S = BwdShape<C, D>;
   constexpr int DP = S::DP, CP = S::CP, CD = S::CD, NE = S::NE;
   extern __shared__ float sm[];
@@ -85,8 +99,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   float* rs = Fn + C;       // row sums of dz
 
   const int tid = threadIdx.x;
-  const int64_t m = (int64_t)gridDim.x - 1 - blockIdx.x;  // longest rows first
-  const int64_t bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const int64_t m = band.me - 1 - blockIdx.x;  // longest rows of the band first
+  const int64_t bh = blockIdx.y, Lp = M * C;
   const bool fox = fl != nullptr;
   const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
 
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
   }
   float off = 0.f;
   for (int64_t n = m - 1; n >= 0; --n) {
-    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    const size_t pr = band.slot(bh, m, n);
     if (fox) off += ftot[bh * M + n];
     if (tid == 0) Off[pr] = off;
     for (int j = 0; j < NE; ++j) {
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
 
   // pass 2: n = 0 .. m-1, gradients flow back up the chain of transports
   for (int64_t n = 0; n < m; ++n) {
-    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    const size_t pr = band.slot(bh, m, n);
     __syncthreads();
     for (int j = 0; j < NE; ++j) {
       const int e = tid + 256 * j;
@@ -252,13 +266,16 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
 }
 
 // ------------------------------------------------------------------------------- key chunks
-// One block per (key chunk n, batch*head): dv, d ktilde, dP_n and the column sums of dz.
+// One block per (key chunk n < me, batch*head): the band's share of dv, d ktilde, dP_n and the column
+// sums of dz.  The band holding query chunk n starts the sums (with the in-chunk block); later bands add
+// to them (dv in fp32 in `dva` until the last band rounds it to the output dtype).
 template <typename T, int D, int C>
 __global__ __launch_bounds__(256) void bwd_key_kernel(
     const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
     const T* __restrict__ v, const T* __restrict__ dout, const float* __restrict__ St, const float* __restrict__ Gst,
     const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
-    int64_t M, T* __restrict__ dv, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol) {
+    int64_t M, pair_band band, T* __restrict__ dv, float* __restrict__ dva, float* __restrict__ dkt,
+    float* __restrict__ dPm, float* __restrict__ dcol) {
   using S = BwdShape<C, D>;
   constexpr int DP = S::DP, CP = S::CP, CD = S::CD, NE = S::NE, NDD = S::NDD;
   extern __shared__ float sm[];
@@ -275,9 +292,11 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
   float* cs = Fn + C;
 
   const int tid = threadIdx.x;
-  const int64_t n = blockIdx.x, bh = blockIdx.y, Lp = M * C, NP = M * (M - 1) / 2;
+  const int64_t n = blockIdx.x, bh = blockIdx.y, Lp = M * C;
   const bool fox = fl != nullptr;
   const size_t rown = (size_t)bh * Lp + (size_t)n * C;
+  const bool first = n >= band.mb;  // query chunk n is in this band: the sums start here
+  const bool last = band.me == M;   // the sums end here
 
   auto stage_rows = [&](float* dst, const T* src, int64_t c0) PA_INLINE {
     for (int e = tid; e < CD; e += 256) {
@@ -298,16 +317,24 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
   stage_rows(Vs, v, n * C);
   for (int a = tid; a < C; a += 256) {
     Fn[a] = fox ? fl[rown + a] : 0.f;
-    cs[a] = 0.f;
+    cs[a] = first ? 0.f : dcol[rown + a];
   }
-  stage_rows(Os, dout, n * C);
-  stage_stats(n);
   float aK[NE], aV[NE], aP[NDD];
-  for (int j = 0; j < NE; ++j) aK[j] = aV[j] = 0.f;
-  for (int j = 0; j < NDD; ++j) aP[j] = 0.f;
-  __syncthreads();
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    aK[j] = (!first && e < CD) ? dkt[rown * D + e] : 0.f;
+    aV[j] = (!first && e < CD) ? dva[rown * D + e] : 0.f;
+  }
+  for (int j = 0; j < NDD; ++j) {
+    const int e = tid + 256 * j;
+    aP[j] = (!first && e < D * D) ? dPm[((size_t)bh * M + n) * D * D + e] : 0.f;
+  }
 
   // in-chunk block
+  if (first) {
+  stage_rows(Os, dout, n * C);
+  stage_stats(n);
+  __syncthreads();
   {
     const float* Sc = Sm + ((size_t)bh * M + n) * C * C;
     for (int e = tid; e < C * C; e += 256) {
@@ -342,9 +369,10 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
     for (int a = 0; a < C; ++a) s += Zs[a * CP + b];
     cs[b] += s;
   }
+  }
 
-  for (int64_t m = n + 1; m < M; ++m) {
-    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+  for (int64_t m = (n + 1 > band.mb ? n + 1 : band.mb); m < band.me; ++m) {
+    const size_t pr = band.slot(bh, m, n);
     __syncthreads();
     for (int e = tid; e < CD; e += 256) {
       const int a = e / D, x = e % D;
@@ -406,7 +434,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
     if (e < CD) {
       const int b = e / D;
       dkt[rown * D + e] = aK[j];
-      if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * D + e % D] = from_f32<T>(aV[j]);
+      if (!last) dva[rown * D + e] = aV[j];
+      else if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * D + e % D] = from_f32<T>(aV[j]);
     }
   }
   for (int j = 0; j < NDD; ++j) {
@@ -808,11 +837,12 @@ __device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4
                                                  float& pF, float& poff, const float* __restrict__ kt,
                                                  const T* __restrict__ vb, const float* __restrict__ Pm,
                                                  const float* __restrict__ St, const float* __restrict__ fl,
-                                                 const float* __restrict__ Off, int64_t bh, int64_t m, int64_t n,
-                                                 int64_t M, int64_t L, int tid, int w, int lane) {
+                                                 const float* __restrict__ Off, const pair_band& band, int64_t bh,
+                                                 int64_t m, int64_t n, int64_t M, int64_t L, int tid, int w,
+                                                 int lane) {
   constexpr int C = 64, CD = 64 * 64;
-  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
-  const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+  const int64_t Lp = M * C;
+  const size_t pr = band.slot(bh, m, n);
   fetch_tile(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
   fetch_rows(pV, vb, n * C, L, tid);
   fetch_tile(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
@@ -828,11 +858,11 @@ __device__ __forceinline__ void fetch_key_pair(f32x4 (&pR)[4], f32x4 (&pG)[4], r
                                                float& pDv, float& poff, const float* __restrict__ St,
                                                const float* __restrict__ Gst, const T* __restrict__ ob,
                                                const float* __restrict__ lse2w, const float* __restrict__ Dw,
-                                               const float* __restrict__ Off, bool fox, int64_t bh, int64_t m,
-                                               int64_t n, int64_t M, int64_t L, int tid) {
+                                               const float* __restrict__ Off, bool fox, const pair_band& band,
+                                               int64_t bh, int64_t m, int64_t n, int64_t M, int64_t L, int tid) {
   constexpr int C = 64, CD = 64 * 64;
-  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
-  const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+  const int64_t Lp = M * C;
+  const size_t pr = band.slot(bh, m, n);
   fetch_tile(pR, St + pr * CD, tid);
   fetch_tile(pG, Gst + pr * CD, tid);  // not written for n = 0 (no transport there): fetched, not used
   fetch_rows(pO, ob, m * C, L, tid);
@@ -871,9 +901,9 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
-    int64_t L, int64_t M, float scale, float* __restrict__ St, float* __restrict__ Gst, float* __restrict__ Off,
-    float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow, float* __restrict__ dqt,
-    float* __restrict__ dSm, int64_t BH) {
+    int64_t L, int64_t M, float scale, pair_band band, float* __restrict__ St, float* __restrict__ Gst,
+    float* __restrict__ Off, float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow,
+    float* __restrict__ dqt, float* __restrict__ dSm, int64_t BH) {
   constexpr int C = 64, CD = 64 * 64;
   extern __shared__ float sm[];
   float* Ks = sm;           // ktilde_n
@@ -885,10 +915,10 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   float* Fn = Dv + C;
 
   int64_t bh, q;
-  if (!bwd_pair_block(BH, M, bh, q)) return;  // whole block
+  if (!bwd_pair_block(BH, band.me - band.mb, bh, q)) return;  // whole block
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
-  const int64_t m = M - 1 - q;  // longest first
-  const int64_t Lp = M * C, NP = M * (M - 1) / 2;
+  const int64_t m = band.me - 1 - q;  // longest of the band first
+  const int64_t Lp = M * C;
   const bool fox = fl != nullptr;
   const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
   const T* vb = v + (size_t)bh * L * 64;
@@ -928,7 +958,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   fetch_tile(pP, Pm + ((size_t)bh * M + (m > 0 ? m - 1 : 0)) * CD, tid);
   float off = 0.f;
   for (int64_t n = m - 1; n >= 0; --n) {
-    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    const size_t pr = band.slot(bh, m, n);
     if (fox) off += ftot[bh * M + n];
     if (tid == 0) Off[pr] = off;
     acc_to_global(R, St + pr * CD, w, lane);
@@ -984,9 +1014,9 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   raw4<T> pV[4];
   float pra[16], ra[16];
   float pF = 0.f, poff = 0.f;
-  fetch_query_pair(pK, pV, pP, pra, pF, poff, kt, vb, Pm, St, fl, Off, bh, m, 0, M, L, tid, w, lane);
+  fetch_query_pair(pK, pV, pP, pra, pF, poff, kt, vb, Pm, St, fl, Off, band, bh, m, 0, M, L, tid, w, lane);
   for (int64_t n = 0; n < m; ++n) {
-    const size_t pr = (size_t)bh * NP + (size_t)pair_index(m, n);
+    const size_t pr = band.slot(bh, m, n);
     __syncthreads();  // every wave is done with the previous ktilde, v, P, FoX prefix
     put_tile(Ks, pK, tid);
     put_rows<T>(Vs, pV, n * C, L, tid);
@@ -1001,8 +1031,8 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     }
     __syncthreads();
     // the last step fetches its own pair again (not used)
-    fetch_query_pair(pK, pV, pP, pra, pF, poff, kt, vb, Pm, St, fl, Off, bh, m, n + 1 < m ? n + 1 : n, M, L, tid, w,
-                     lane);
+    fetch_query_pair(pK, pV, pP, pra, pF, poff, kt, vb, Pm, St, fl, Off, band, bh, m, n + 1 < m ? n + 1 : n, M, L,
+                     tid, w, lane);
     f32x4 Z[4], DP[4];
     zero4(G);
     if (n > 0) {  // dr^(n-1) P_n
@@ -1066,8 +1096,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
     const T* __restrict__ v, const T* __restrict__ dout, const float* __restrict__ St, const float* __restrict__ Gst,
     const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
-    int64_t M, T* __restrict__ dv, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol,
-    int64_t BH) {
+    int64_t M, pair_band band, T* __restrict__ dv, float* __restrict__ dva, float* __restrict__ dkt,
+    float* __restrict__ dPm, float* __restrict__ dcol, int64_t BH) {
   constexpr int C = 64, CD = 64 * 64;
   extern __shared__ float sm[];
   float* Rs = sm;           // r^(n)_m
@@ -1079,11 +1109,13 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   float* Fn = Dv + C;
 
   int64_t bh, n;
-  if (!bwd_pair_block(BH, M, bh, n)) return;  // whole block; low key chunks (the longest) first
+  if (!bwd_pair_block(BH, band.me, bh, n)) return;  // whole block; low key chunks first
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int64_t Lp = M * C;
   const bool fox = fl != nullptr;
   const size_t rown = (size_t)bh * Lp + (size_t)n * C;
+  const bool first = n >= band.mb;  // query chunk n is in this band: the sums start here (in-chunk block)
+  const bool last = band.me == M;   // the sums end here
   const T* vb = v + (size_t)bh * L * 64;
   const T* ob = dout + (size_t)bh * L * 64;
 
@@ -1097,19 +1129,23 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   if constexpr (kBf) frag_bf16(vb16, reinterpret_cast<const __bf16*>(vb), n * C, L, w, lane);
   else frag_rows(va, vb, n * C, L, w, lane);
 
+  f32x4 aV[4], aK[4], aP[4];
+  float csum[4] = {0.f, 0.f, 0.f, 0.f};  // key rows 16w + 4g + e, this band's share
+  if (tid < C) Fn[tid] = fox ? fl[rown + tid] : 0.f;
+  if (!first) {  // the sums of the earlier bands
+    global_to_acc(aV, dva + rown * 64, w, lane);
+    global_to_acc(aK, dkt + rown * 64, w, lane);
+    global_to_acc(aP, dPm + ((size_t)bh * M + n) * CD, w, lane);
+  } else {
+  zero4(aV);
+  zero4(aK);
+  zero4(aP);
   tile_rows(Os, ob, n * C, L, tid);
   if (tid < C) {
-    Fn[tid] = fox ? fl[rown + tid] : 0.f;
     l2[tid] = lse2w[rown + tid];
     Dv[tid] = Dw[rown + tid];
   }
   __syncthreads();
-
-  f32x4 aV[4], aK[4], aP[4];
-  zero4(aV);
-  zero4(aK);
-  zero4(aP);
-  float csum[4] = {0.f, 0.f, 0.f, 0.f};  // key rows 16w + 4g + e
 
   // in-chunk block (m = n): D^T = V dO^T on the matrix cores, logits from S
   {
@@ -1135,14 +1171,16 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   }
   if constexpr (kBf) mm64_split_bf16(aV, Xs, Os, w, lane);  // dv_n += p^T dO_n
   else mm64<false, true>(aV, Xs, Os, w, lane);
+  }
 
-  // query chunks m = n+1 .. M-1; the next pair's tiles arrive in registers one step ahead
-  if (n + 1 < M) {
+  // the band's query chunks m > n; the next pair's tiles arrive in registers one step ahead
+  const int64_t m0 = n + 1 > band.mb ? n + 1 : band.mb;
+  if (m0 < band.me) {
   f32x4 pR[4], pG[4];
   raw4<T> pO[4];
   float pl2 = 0.f, pDv = 0.f, poff = 0.f;
-  fetch_key_pair(pR, pG, pO, pl2, pDv, poff, St, Gst, ob, lse2w, Dw, Off, fox, bh, n + 1, n, M, L, tid);
-  for (int64_t m = n + 1; m < M; ++m) {
+  fetch_key_pair(pR, pG, pO, pl2, pDv, poff, St, Gst, ob, lse2w, Dw, Off, fox, band, bh, m0, n, M, L, tid);
+  for (int64_t m = m0; m < band.me; ++m) {
     __syncthreads();  // every wave is done with the previous r, dO, dr, row statistics
     put_tile(Rs, pR, tid);
     if (n > 0) put_tile(Gq, pG, tid);
@@ -1154,8 +1192,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const float offn = poff;
     __syncthreads();
     // the last step fetches its own pair again (not used)
-    fetch_key_pair(pR, pG, pO, pl2, pDv, poff, St, Gst, ob, lse2w, Dw, Off, fox, bh, m + 1 < M ? m + 1 : m, n, M, L,
-                   tid);
+    fetch_key_pair(pR, pG, pO, pl2, pDv, poff, St, Gst, ob, lse2w, Dw, Off, fox, band, bh,
+                   m + 1 < band.me ? m + 1 : m, n, M, L, tid);
     f32x4 ZT[4], DT[4];
     zero4(ZT);
     zero4(DT);
@@ -1190,13 +1228,17 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
 
   acc_to_global(aK, dkt + rown * 64, w, lane);
   acc_to_global(aP, dPm + ((size_t)bh * M + n) * CD, w, lane);
+  if (!last) {
+    acc_to_global(aV, dva + rown * 64, w, lane);
+  } else {
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int b = 16 * w + 4 * g + e;
-      if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * 64 + 16 * cb + r] = from_f32<T>(aV[cb][e]);
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int b = 16 * w + 4 * g + e;
+        if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * 64 + 16 * cb + r] = from_f32<T>(aV[cb][e]);
+      }
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     float s = csum[e];
@@ -1204,7 +1246,10 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     s += __shfl_xor(s, 2);
     s += __shfl_xor(s, 4);
     s += __shfl_xor(s, 8);
-    if (r == 0) dcol[rown + 16 * w + 4 * g + e] = s;
+    if (r == 0) {
+      const size_t i = rown + 16 * w + 4 * g + e;
+      dcol[i] = (first ? 0.f : dcol[i]) + s;
+    }
   }
 }
 
@@ -1957,7 +2002,8 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   auto lds = [](const void* f, size_t bytes) {
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   };
-  if constexpr (D == 64 && C == 64) {  // everything on the fp32 matrix cores
+  const int64_t G = bwd_band_chunks(M), NPB = bwd_band_pairs(M);
+  if constexpr (D == 64 && C == 64) {  // the matrix cores: bf16 products for bf16 inputs, fp32 ones for fp32
     if ((e = lds((const void*)bwd_chunk_fwd_mfma_kernel<T>, kLdsChunkFwdMfma)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_query_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_key_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
@@ -1965,15 +2011,18 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
     bwd_chunk_fwd_mfma_kernel<T><<<grid, 256, kLdsChunkFwdMfma, st>>>(
         (const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 pair_grid((unsigned)(kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd) * M));
-    bwd_query_mfma_kernel<T><<<pair_grid, 256, kLdsPairMfma, st>>>(
-        b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
-        scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm, BH);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_key_mfma_kernel<T><<<pair_grid, 256, kLdsPairMfma, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
-                                                                 (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv,
-                                                                 L, M, (T*)dv, b.dkt, b.dPm, b.dcol, BH);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t xh = kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd);
+    for (int64_t mb = 0; mb < M; mb += G) {
+      const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
+      bwd_query_mfma_kernel<T><<<dim3((unsigned)(xh * (band.me - band.mb))), 256, kLdsPairMfma, st>>>(
+          b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
+          M, scale, band, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm, BH);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      bwd_key_mfma_kernel<T><<<dim3((unsigned)(xh * band.me)), 256, kLdsPairMfma, st>>>(
+          b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
+          band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     bwd_chunk_grad_mfma_kernel<T><<<grid, 256, kLdsChunkMfma, st>>>((const T*)q, (const T*)k, (const T*)w, beta,
                                                                     b.dqt, b.dkt, b.dPm, b.dSm, L, M, (T*)dq,
                                                                     (T*)dk, (T*)dw, dbeta);
@@ -1985,14 +2034,17 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
     if ((e = lds((const void*)bwd_query_kernel<T, D, C>, S::lds_query)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_key_kernel<T, D, C>, S::lds_key)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_prep_kernel<T, D, C>, S::lds_prep)) != hipSuccess) return e;
-    bwd_query_kernel<T, D, C><<<grid, 256, S::lds_query, st>>>(
-        b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L, M,
-        scale, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_key_kernel<T, D, C><<<grid, 256, S::lds_key, st>>>(b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v,
-                                                          (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
-                                                          (T*)dv, b.dkt, b.dPm, b.dcol);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    for (int64_t mb = 0; mb < M; mb += G) {
+      const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
+      bwd_query_kernel<T, D, C><<<dim3((unsigned)(band.me - band.mb), (unsigned)BH), 256, S::lds_query, st>>>(
+          b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
+          M, scale, band, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      bwd_key_kernel<T, D, C><<<dim3((unsigned)band.me, (unsigned)BH), 256, S::lds_key, st>>>(
+          b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
+          band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     bwd_prep_kernel<T, D, C><<<grid, 256, S::lds_prep, st>>>((const T*)q, (const T*)k, (const T*)w, beta, b.dqt,
                                                             b.dkt, b.dPm, b.dSm, L, M, (T*)dq, (T*)dk, (T*)dw,
                                                             dbeta);

@@ -30,14 +30,6 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Lambdas inside kernels must inline (an outlined call passes register arrays through scratch).
 #define PA_INLINE __attribute__((always_inline))
 
-// Device buffers of the backward pass (fp32), carved from its workspace.
-struct bwd_buffers {
-  float *qt, *kt, *Pm, *Sm, *fl, *ftot;  // per-chunk terms of the forward (scaled as the forward's)
-  float *St, *Gst, *Off;                 // per (query chunk, key chunk) pair: states, their gradients, FoX offsets
-  float *lse2, *Dv, *drow, *dcol;        // per row: log2-unit lse, dO . o, row and column sums of dz
-  float *dqt, *dkt, *dPm, *dSm;          // gradients of the per-chunk terms
-};
-
 // Round x up to a multiple of a (a power of two).
 __host__ __device__ constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 

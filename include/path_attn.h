@@ -302,10 +302,12 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
  * the forward only (summary, sections 2 and 3; the lecture notes' "limitations"
  * say the backward is the costlier part); this differentiates the blockwise
  * forward with the chain rule: logits of each pair of chunks are recomputed from
- * lse, the running queries of every (query chunk, key chunk) pair are kept in the
- * workspace (a transition with beta = 1 is singular, so they cannot be recovered
- * backwards), and each chunk's UT-transform terms are differentiated back to
- * q, k, w and beta.
+ * lse, the running queries and their gradients of each (query chunk, key chunk)
+ * pair are kept in the workspace (a transition with beta = 1 is singular, so
+ * they cannot be recovered backwards) for one band of about sqrt(L / chunk)
+ * query chunks at a time, the key-side sums carrying over from band to band,
+ * and each chunk's UT-transform terms are differentiated back to q, k, w and
+ * beta.
  *
  *   q, k, v, w     [B,H,L,d] dtype          the forward's inputs
  *   beta           [B,H,L] fp32
@@ -322,10 +324,11 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
  * bf16 inputs at d = chunk = 64 the matrix products run on the bf16 matrix
  * cores: exact for products of input values, with other fp32 operands split
  * into hi + lo bf16 (about 2^-16 relative); fp32 inputs keep fp32 products.
- * Workspace: path_attn_bwd_workspace_bytes; it grows as B*H*(L/chunk)^2*chunk*d
- * (two fp32 vectors per key of every chunk pair: about 12.7 GB at B=8, H=24,
- * L=4096, d=64, chunk 64).  Errors as for path_attn_fwd; nothing is enqueued
- * on an error.
+ * Workspace: path_attn_bwd_workspace_bytes; it grows as B*H*L*d*sqrt(L/chunk)
+ * (two fp32 vectors per key of every chunk pair of one band: about 4.8 GB at
+ * B=8, H=24, L=4096, d=64, chunk 64, and 10.8 GB at B=1, H=24, L=32768).  The
+ * kernels are deterministic: the same inputs give the same bits.  Errors as
+ * for path_attn_fwd; nothing is enqueued on an error.
  */
 path_status path_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
                                           size_t* bytes);

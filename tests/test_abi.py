@@ -221,8 +221,10 @@ def bwd_call(L, **kw):
 def test_bwd_workspace_planning(L):
     n = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 64, BF16, ctypes.byref(n)) == OK
-    pairs = 64 * 63 // 2
-    assert n.value >= 2 * 8 * 24 * pairs * 64 * 64 * 4  # kept states and their gradients
+    # states and their gradients of one band of query chunks at a time: 64 chunks in bands of 8, the
+    # largest band (chunks 56 .. 63) holding 56 + ... + 63 pairs
+    pairs = sum(range(56, 64))
+    assert n.value >= 2 * 8 * 24 * pairs * 64 * 64 * 4
     assert n.value < 2 * 8 * 24 * pairs * 64 * 64 * 4 + (2 << 30)
     n0 = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 0, BF16, ctypes.byref(n0)) == OK
@@ -234,6 +236,18 @@ def test_bwd_workspace_planning(L):
     assert L.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 64, F32, None) == INVALID
     assert L.path_attn_bwd_workspace_bytes(1, 1, 64, 16, 16, F32, ctypes.byref(n)) == OK  # one chunk... of 4
     assert L.path_attn_bwd_workspace_bytes(1, 1, 16, 16, 16, F32, ctypes.byref(n)) == OK and n.value > 0
+
+
+def test_bwd_workspace_grows_as_l_sqrt_l(L):
+    """The backward keeps per-pair states for one band of about sqrt(M) query chunks at a time, so its
+    workspace grows as L^1.5 (a factor 8 per factor 4 in L), not as L^2 (a factor 16)."""
+    def size(Lq, B=1, H=1):
+        n = ctypes.c_size_t(0)
+        assert L.path_attn_bwd_workspace_bytes(B, H, Lq, 64, 64, BF16, ctypes.byref(n)) == OK
+        return n.value
+    for Lq in (4096, 16384):
+        assert size(4 * Lq) <= 8.5 * size(Lq), Lq
+    assert size(32768, 1, 24) < 12e9  # long-context shape: 24 heads of 32768 tokens
 
 
 def test_bwd_validation(L):
