@@ -202,7 +202,8 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
   float* Fs = Bs + 64;                               // unused pad (keeps the plan aligned)
   (void)Fs;
 
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  // the wave index is wave-uniform: keep it in a scalar register, so that branches on it are uniform
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, r = l & 15, g = l >> 4;
   const int c = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t Lp = M * kC;
@@ -243,6 +244,8 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
   f32x4 kq[4];
   {
     f32x4 ua[4], ra[4];
+    const float4 bw = *reinterpret_cast<const float4*>(Bs + 16 * wave + 4 * g);  // beta of rows 16 wave + 4g + i
+    const float bwi[4] = {bw.x, bw.y, bw.z, bw.w};
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       f32x4 ga = zero, u4 = zero, r4 = zero, k4 = zero;
@@ -261,8 +264,9 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
         const int rw = 16 * tt + 4 * g + i;  // t (for U) or s (for R)
         u4[i] = (rw <= col_wave) ? u4[i] : 0.f;
         r4[i] = (rw > col_wave) ? r4[i] : 0.f;
+        // the lower triangle (zeros here) is overwritten by Z^T before anything reads it
         const int srow = 16 * wave + 4 * g + i, tcol = 16 * tt + r;
-        if (srow < tcol) Af[srow * kLDF + tcol] = Bs[srow] * ga[i];
+        Af[srow * kLDF + tcol] = (srow < tcol) ? bwi[i] * ga[i] : 0.f;
       }
       ua[tt] = u4;
       ra[tt] = r4;
@@ -281,20 +285,21 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     k4s[xt] = *reinterpret_cast<const bf16x4*>(Kt + swz(row, x0 >> 3) + (x0 & 7));
   }
   __builtin_amdgcn_wave_barrier();
-  // Z_II (block I = wave) by back substitution, lane l < 16 owning column l; stored transposed.
+  // Z_II (block I = wave) by back substitution, lane l < 16 owning column l = A_II^{-1} e_l; stored
+  // transposed.  Column-oriented: once z[kk] is final its multiple of column kk of A leaves the rows
+  // above, so the 15 dependent steps each carry up to 15 independent FMAs.
   if (l < 16) {
     const int base = 16 * wave;
     float z[16];
 #pragma unroll
-    for (int ii = 15; ii >= 0; --ii) {
-      float sacc = 0.f;
+    for (int ii = 0; ii < 16; ++ii) z[ii] = (ii == l) ? 1.f : 0.f;
 #pragma unroll
-      for (int kk = ii + 1; kk < 16; ++kk) sacc += Af[(base + ii) * kLDF + base + kk] * z[kk];
-      z[ii] = (ii == l) ? 1.f : (ii < l ? -sacc : 0.f);
-    }
+    for (int kk = 15; kk >= 1; --kk)
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii)
-      if (ii <= l) Af[(base + l) * kLDF + base + ii] = z[ii];
+      for (int ii = 0; ii < kk; ++ii) z[ii] = __builtin_fmaf(-Af[(base + ii) * kLDF + base + kk], z[kk], z[ii]);
+    // (z[ii] = 0 for ii > l: those stores clear the block's upper half, whose A entries are no longer read)
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) Af[(base + l) * kLDF + base + ii] = z[ii];
   }
   __syncthreads();
 
@@ -303,25 +308,41 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
   //   T = sum_{K=I+1..J} A_IK Z_KJ,   Z_IJ = -Z_II T,   J = I + lv,
   // both on the fp32 matrix cores (16x16x4: lane (r, q) brings A[r][q] and B[q][r]), straight from LDS.
   // In the second product the contraction index kk = 4q + m of step m makes T's accumulator slot m
-  // the B-operand of the same lane.
+  // the B-operand of the same lane.  The A entries and the Z_II entries a wave uses at every level are
+  // read into registers first, so that after each level's barrier only that level's Z entries are read
+  // (together: the levels are unrolled); the first sum runs in two accumulators.
+  float arow[12];  // A[16I + r][16(I+1) + 4st + g], st < 4 (3 - I)
+#pragma unroll
+  for (int st = 0; st < 12; ++st) {
+    const int kk = 16 * (wave + 1) + 4 * st + g;
+    arow[st] = Af[(16 * wave + r) * kLDF + (kk < 64 ? kk : 63)];
+  }
+  float zdiag[4];  // Z[16I + r][16I + 4g + m] (upper triangular: zero for 4g + m < r)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int kk = 4 * g + m;
+    const float zv = Af[(16 * wave + kk) * kLDF + 16 * wave + r];
+    zdiag[m] = (kk >= r) ? zv : 0.f;
+  }
+#pragma unroll
   for (int lv = 1; lv < 4; ++lv) {
     const int I = wave, J = wave + lv;
     if (J < 4) {
-      f32x4 tacc = zero;
-      for (int k0 = 16 * (I + 1); k0 < 16 * (J + 1); k0 += 4) {
-        const int kk = k0 + g;
-        const float a = Af[(16 * I + r) * kLDF + kk];  // A[16I + r][kk]
-        const float zb = Af[(16 * J + r) * kLDF + kk];  // Z[kk][16J + r]; Z_JJ is upper triangular
-        const float b = (kk >= 16 * J && kk - 16 * J > r) ? 0.f : zb;
-        tacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, tacc, 0, 0, 0);
+      float zb[12];
+#pragma unroll
+      for (int st = 0; st < 4 * lv; ++st) {
+        const int kk = 16 * (I + 1) + 4 * st + g;
+        const float zv = Af[(16 * J + r) * kLDF + kk];  // Z[kk][16J + r]; Z_JJ is upper triangular
+        zb[st] = (kk >= 16 * J && kk - 16 * J > r) ? 0.f : zv;
       }
+      f32x4 t2[2] = {zero, zero};
+#pragma unroll
+      for (int st = 0; st < 4 * lv; ++st)
+        t2[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[st], zb[st], t2[st & 1], 0, 0, 0);
+      const f32x4 tacc = t2[0] + t2[1];
       f32x4 zacc = zero;  // D[ii][jj] = sum_kk Z[16I + ii][16I + kk] T[kk][jj]
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int kk = 4 * g + m;
-        const float a = (kk >= r) ? Af[(16 * I + kk) * kLDF + 16 * I + r] : 0.f;  // Z[16I + r][16I + kk]
-        zacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, tacc[m], zacc, 0, 0, 0);
-      }
+      for (int m = 0; m < 4; ++m) zacc = __builtin_amdgcn_mfma_f32_16x16x4f32(zdiag[m], tacc[m], zacc, 0, 0, 0);
       // lane (r, g) holds Z_IJ[4g + e][r] = Z[16I + 4g + e][16J + r], stored at Af[16J + r][16I + 4g + e]
       *reinterpret_cast<float4*>(Af + (16 * J + r) * kLDF + 16 * I + 4 * g) =
           make_float4(-zacc[0], -zacc[1], -zacc[2], -zacc[3]);
@@ -329,15 +350,19 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     __syncthreads();
   }
 
-  // T^{-T}[t][s] = Z[s][t] beta_t (t >= s), hi/lo, stored with permuted columns
+  // T^{-T}[t][s] = Z[s][t] beta_t (t >= s), hi/lo, stored with permuted columns: stored slots 8 ch + j
+  // of row t hold columns c0 + 16 (j / 4) + j % 4, c0 = 32 (ch / 4) + 4 (ch % 4)
   for (int e = tid; e < 512; e += 256) {
-    const int t = e >> 3, ch = e & 7;
+    const int t = e >> 3, ch = e & 7, c0 = 32 * (ch >> 2) + 4 * (ch & 3);
+    const float4 v0 = *reinterpret_cast<const float4*>(Af + t * kLDF + c0);
+    const float4 v1 = *reinterpret_cast<const float4*>(Af + t * kLDF + c0 + 16);
+    const float zt[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float bt = Bs[t];
     bf16x8 h8, l8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int pslot = 8 * ch + j;
-      const int sc_ = (pslot & 32) + ((pslot & 7) >> 2) * 16 + ((pslot >> 3) & 3) * 4 + (pslot & 3);  // column held
-      const float v = (t >= sc_) ? Af[t * kLDF + sc_] * Bs[t] : 0.f;
+      const int sc_ = c0 + 16 * (j >> 2) + (j & 3);  // column held
+      const float v = (t >= sc_) ? zt[j] * bt : 0.f;
       const __bf16 hh = (__bf16)v;
       h8[j] = hh;
       l8[j] = (__bf16)(v - (float)hh);
