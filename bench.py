@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--min-warmup-s", type=float, default=0.5,
+                    help="prefill warm-up runs at least this long (and at least --warmup steps)")
     ap.add_argument("--transport", default="bf16", choices=["bf16", "bf16x3"])
     ap.add_argument("--fox", action="store_true", help="PaTH-FoX prefill (log-forget gates) instead of PaTH")
     ap.add_argument("--L", type=int, default=4096)
@@ -149,10 +151,16 @@ def bench_prefill(args):
         native.path_attn_scan(v, logf, chunk=C, transport=args.transport, workspace=ws, out=out,
                               lse=lse)
 
-    for _ in range(args.warmup):
+    # at least W warm-up steps, and at least --min-warmup-s seconds of them: on a freshly started GPU the
+    # clock settles over the first ~20 steps (~20 ms), which a short warm-up would leave in the timed region
+    n_warm, t_w = 0, time.perf_counter()
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
         step()
+        n_warm += 1
+        if n_warm % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    log(f"[bench] prefill warmup done; timing {args.steps} steps")
+    log(f"[bench] prefill warmup done ({n_warm} steps); timing {args.steps} steps")
     t0 = time.perf_counter()
     ms_step = timed(step, args.steps)
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
@@ -168,7 +176,8 @@ def bench_prefill(args):
     log(f"[bench] prefill: step {ms_step:.3f} ms (wall {wall_ms:.3f}) = {step_tf:.1f} TFLOP/s = "
         f"{step_tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak (whole call); prep alone {ms_prep:.3f} ms, "
         f"scan alone {ms_scan:.3f} ms = {tflops / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak")
-    res = dict(B=B, H=H, L=L, d=d, C=C, recipe=recipe, ms_step=ms_step, wall_ms=wall_ms, ms_prep=ms_prep,
+    res = dict(B=B, H=H, L=L, d=d, C=C, recipe=recipe, warmup_steps_run=n_warm, ms_step=ms_step, wall_ms=wall_ms,
+               ms_prep=ms_prep,
                ms_scan=ms_scan, flops=F, scan_tflops=tflops, tokens_per_s=B * L / (ms_step * 1e-3))
     return res, x, dict(q=q, k=k, v=v, w=w, beta=beta, logf=logf, scale=x.scale, ws=ws, out=out, lse=lse)
 
@@ -615,6 +624,7 @@ def main():
                                    "frac": scan_tf / MFMA_BF16_PEAK_TFLOPS, "traffic": t_scan},
                      "prep_only": {"kernel": "mfma_prep_kernel", "launch_ms": res["ms_prep"], "traffic": t_prep}},
         "prefill_detail": {"ms_prep": res["ms_prep"], "ms_scan": res["ms_scan"], "wall_ms_per_step": res["wall_ms"],
+                           "warmup_steps_run": res["warmup_steps_run"],
                            "step_tflops": F / (res["ms_step"] * 1e-3) / 1e12,
                            "step_frac_of_peak": F / (res["ms_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,

@@ -29,7 +29,8 @@ for f in "$ROOT"/dependent_positional_attention_amd/csrc/*.hip; do
     -Xarch_host -fno-omit-frame-pointer -c "$f" -o "$o" 2>&1 | grep -v "packed-fp32" || true
   objs+=("$o")
 done
-$HIPCC --offload-arch=gfx950 -shared -fPIC -fsanitize=address,undefined -o "$OUT/libpathattn_san.so" "${objs[@]}"
+$HIPCC --offload-arch=gfx950 -shared -fPIC -Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined \
+  -o "$OUT/libpathattn_san.so" "${objs[@]}"
 CLANG_RT=$(ls /opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so | head -1)
 ( cd "$ROOT" && PATHATTN_LIB="$OUT/libpathattn_san.so" LD_PRELOAD="$CLANG_RT" \
   python -m pytest -x -q -m "not gpu" -p no:cacheprovider tests/test_abi.py tests/test_zz_no_alloc.py )
