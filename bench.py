@@ -107,6 +107,20 @@ def prefill_flops(B, H, L, d, C):
     return 4.0 * d * (L * (L + 1) / 2) * B * H + 2.0 * C * d * d * ((M - 1) * (M - 2) / 2) * B * H
 
 
+def warm_up(fn, steps, seconds):
+    """Run fn at least `steps` times and for at least `seconds` (synchronising every 10 calls so that the
+    time is the GPU's): the clock of an idle GPU takes ~20 ms of work to settle."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < steps or time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def timed(fn, n):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -153,13 +167,7 @@ def bench_prefill(args):
 
     # at least W warm-up steps, and at least --min-warmup-s seconds of them: on a freshly started GPU the
     # clock settles over the first ~20 steps (~20 ms), which a short warm-up would leave in the timed region
-    n_warm, t_w = 0, time.perf_counter()
-    while n_warm < args.warmup or time.perf_counter() - t_w < args.min_warmup_s:
-        step()
-        n_warm += 1
-        if n_warm % 10 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+    n_warm = warm_up(step, args.warmup, args.min_warmup_s)
     log(f"[bench] prefill warmup done ({n_warm} steps); timing {args.steps} steps")
     t0 = time.perf_counter()
     ms_step = timed(step, args.steps)
@@ -269,7 +277,8 @@ def bench_handoff(args, res, ctx):
 
 def bench_fox(args, ctx):
     """PaTH-FoX prefill at the same shape (the same q, k, v, w, beta plus log-forget gates
-    logsigmoid(N(3, 1))): whole step and the scan alone."""
+    logsigmoid(N(3, 1))): whole step and the scan alone, interleaved round by round with the plain
+    PaTH step on the same inputs (median of 3 rounds of 10 steps each) so that both see the same clock."""
     import numpy as np
     import torch
     from dependent_positional_attention_amd import native, synth
@@ -281,26 +290,36 @@ def bench_fox(args, ctx):
     out = torch.empty_like(q)
     lse = torch.empty((B, H, L), device="cuda", dtype=torch.float32)
 
-    def step():
-        native.path_attn_fwd(q, k, v, w, beta, logf, scale=scale, chunk=C, transport=args.transport, out=out,
+    def step(f):
+        native.path_attn_fwd(q, k, v, w, beta, f, scale=scale, chunk=C, transport=args.transport, out=out,
                              lse=lse, workspace=ws)
 
-    def scan():
-        native.path_attn_scan(v, logf, chunk=C, transport=args.transport, workspace=ws, out=out, lse=lse)
+    def scan(f):
+        native.path_attn_scan(v, f, chunk=C, transport=args.transport, workspace=ws, out=out, lse=lse)
 
-    for _ in range(5):
-        step()
+    warm_up(lambda: step(logf), 10, args.min_warmup_s)
+    t = {"fox": [], "plain": [], "fox_scan": [], "plain_scan": []}
+    for _ in range(3):
+        t["fox"].append(timed(lambda: step(logf), 10))
+        t["plain"].append(timed(lambda: step(None), 10))
+        t["fox_scan"].append(timed(lambda: scan(logf), 10))
+        t["plain_scan"].append(timed(lambda: scan(None), 10))
+    med = {key: sorted(v_)[1] for key, v_ in t.items()}
+    step(logf)
     torch.cuda.synchronize()
-    ms = timed(step, 10)
-    ms_scan = timed(scan, 10)
     assert torch.isfinite(out.float()).all(), "non-finite FoX output"
+    ms, ms_scan = med["fox"], med["fox_scan"]
     F = prefill_flops(B, H, L, d, C)
     tf = F / (ms_scan * 1e-3) / 1e12
-    log(f"[bench] PaTH-FoX prefill: step {ms:.3f} ms, {B * L / (ms * 1e-3) / 1e6:.2f} M tokens/s; scan {ms_scan:.3f} ms "
-        f"= {tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak")
+    log(f"[bench] PaTH-FoX prefill: step {ms:.3f} ms, {B * L / (ms * 1e-3) / 1e6:.2f} M tokens/s "
+        f"({ms / med['plain']:.3f}x the plain step's {med['plain']:.3f} ms, interleaved); scan {ms_scan:.3f} ms "
+        f"= {tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak ({ms_scan / med['plain_scan']:.3f}x the plain scan)")
     return {"workload": f"PaTH-FoX prefill forward, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16, "
-                        f"transport {args.transport}", "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
-            "scan_ms": ms_scan, "scan_tflops": tf, "scan_frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+                        f"transport {args.transport}; median of 3 rounds of 10 steps, interleaved with the plain step",
+            "ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3),
+            "scan_ms": ms_scan, "scan_tflops": tf, "scan_frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+            "plain_ms_per_step_interleaved": med["plain"], "ratio_to_plain": ms / med["plain"],
+            "plain_scan_ms_interleaved": med["plain_scan"], "scan_ratio_to_plain": ms_scan / med["plain_scan"]}
 
 
 def bench_chunks(args, ctx):
@@ -321,8 +340,7 @@ def bench_chunks(args, ctx):
              for C in chunks}
     times = {C: [] for C in chunks}
     for C in chunks:
-        steps[C]()
-    torch.cuda.synchronize()
+        warm_up(steps[C], 2, args.min_warmup_s / 3)
     for _ in range(4):
         for C in chunks:
             times[C].append(timed(steps[C], 5))
@@ -415,9 +433,7 @@ def bench_long(args):
                                                   transport=args.transport, out=out, lse=lse, workspace=wss[C]))
              for C in chunks}
     for C in chunks:
-        for _ in range(2):
-            steps[C]()
-    torch.cuda.synchronize()
+        warm_up(steps[C], 2, args.min_warmup_s / 3)
     times = {C: [] for C in chunks}
     for _ in range(3):
         for C in chunks:
