@@ -102,7 +102,10 @@ __device__ __forceinline__ void dma_tile(__bf16* tile, const __bf16* src, int rm
   for (int i = i0; i < i0 + CNT; ++i) {
     const int row = 8 * i + (l >> 3), slot = l & 7;
     const int rs = row < rmax ? row : rmax - 1;
-    const uint32_t off = (uint32_t)(rs * 128 + ((slot ^ (row & 7)) << 4));
+    uint32_t off = (uint32_t)(rs * 128 + ((slot ^ (row & 7)) << 4));
+    // (an empty asm keeps the offset a fresh 32-bit register, so that the copy takes the scalar-base +
+    // 32-bit-offset form instead of a 64-bit vector address rebuilt with a vector add per copy)
+    __asm__ volatile("" : "+v"(off));
     __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(src) + off),
                                      (lds_void*)(tile + i * 512), 16, 0, 0);
   }
@@ -884,9 +887,10 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
     const int64_t vrows = L - n * kC;
     return (t == 1 && vrows < kC) ? (int)vrows : kC;
   };
-  auto stage = [&](int64_t n, int s) PA_INLINE {
+  // full: chunk n is known to be whole (n < M - 1), so no value row needs the clamp
+  auto stage = [&](int64_t n, int s, bool full = false) PA_INLINE {
 #pragma unroll
-    for (int t = 0; t < NM; ++t) dma_tile<kCp>(lds[s][t], chunk_src(n, t), chunk_rows(n, t), i0);
+    for (int t = 0; t < NM; ++t) dma_tile<kCp>(lds[s][t], chunk_src(n, t), full ? kC : chunk_rows(n, t), i0);
     if constexpr (FOX) {
       if (l < 64 / W)
         __builtin_amdgcn_global_load_lds((const void*)(fl + bh * Lp + n * kC + (64 / W) * wave + l),
@@ -984,6 +988,36 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
         advance(n);
         --n;
       }
+    }
+  } else if constexpr (NB == 3) {
+    // Three steps per turn of the ring, so that every step's slot (and with it every LDS address) is
+    // a compile-time constant; the chunks staged here (n - 2 <= M - 3) are whole.
+    auto body_step = [&](auto slot_c) PA_INLINE {
+      constexpr int S = decltype(slot_c)::value;
+      if constexpr (FOX) off += lfl[S][63];
+      step(std::true_type{}, lds[S][0], lds[S][1], lds[S][2], lds[S][NM - 1], lfl[S]);
+      if (n >= 2) {
+        stage(n - 2, (S + 2) % 3, true);
+        wait_vm<OPS>();  // chunk n-1 (issued one step earlier) has landed
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();
+      --n;
+    };
+    while (n >= 1) {
+      if (cur == 0) {
+        body_step(std::integral_constant<int, 0>{});
+        cur = 1;
+        if (n < 1) break;
+      }
+      if (cur == 1) {
+        body_step(std::integral_constant<int, 1>{});
+        cur = 2;
+        if (n < 1) break;
+      }
+      body_step(std::integral_constant<int, 2>{});
+      cur = 0;
     }
   } else {
     for (; n >= 1; --n) {
