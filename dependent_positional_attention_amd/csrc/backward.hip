@@ -446,8 +446,10 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
 }
 
 // ------------------------------------------------------------------------------- matrix-core variants
-// C = D = 64: the 64 x 64 x 64 products of the two chunk-pair kernels above run on the fp32 matrix
-// cores (16x16x4), so the fp32 accuracy is kept.  Four waves; wave w owns output rows 16w .. 16w+15.
+// C = D = 64: the 64 x 64 x 64 products of the chunk-pair kernels run on the matrix cores: the fp32 ones
+// (16x16x4, the helpers here) for fp32 inputs, so the fp32 accuracy is kept, and the bf16 ones (16x16x32,
+// the helpers further down: exact for products of input values, hi + lo splits otherwise) for bf16
+// inputs.  Four waves; wave w owns output rows 16w .. 16w+15.
 // Tiles are row-major in LDS with a 68-float row stride (16-byte aligned rows).  In one 16x16x4 step
 // lane (r, g) (r = lane % 16, g = lane / 16) brings A[row r][slot g] and B[slot g][col r], and holds
 // D[4g + e][r] (e = 0..3) of the accumulator; within 16-wide k blocks slot g of step j is

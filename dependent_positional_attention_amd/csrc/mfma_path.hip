@@ -306,52 +306,61 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- C: off-diagonal blocks of Z, by distance
-  // Z[i][j] (i <= j) lives at Af[j][i].  Wave I owns row block I:
-  //   T = sum_{K=I+1..J} A_IK Z_KJ,   Z_IJ = -Z_II T,   J = I + lv,
-  // both on the fp32 matrix cores (16x16x4: lane (r, q) brings A[r][q] and B[q][r]), straight from LDS.
-  // In the second product the contraction index kk = 4q + m of step m makes T's accumulator slot m
-  // the B-operand of the same lane.  The A entries and the Z_II entries a wave uses at every level are
-  // read into registers first, so that after each level's barrier only that level's Z entries are read
-  // (together: the levels are unrolled); the first sum runs in two accumulators.
-  float arow[12];  // A[16I + r][16(I+1) + 4st + g], st < 4 (3 - I)
+  // ---------------------------------------------------------------- C: off-diagonal blocks of Z, two levels
+  // Z[i][j] (i <= j) lives at Af[j][i]; the upper halves of the diagonal blocks' storage are zero.  With
+  // 16 x 16 blocks I, J = 0..3:
+  //   level 1 (waves 0, 2):  Z_{I,I+1} = -Z_II A_{I,I+1} Z_{I+1,I+1}, the 32 x 32 diagonal blocks of Z;
+  //   level 2 (wave w: i = w / 2, j = 2 + w % 2):  the 32 x 32 corner
+  //     T_kj = sum_{k'=2..j} A_{k k'} Z_{k' j}  (k = 0, 1),   Z_ij = -sum_{k=i..1} Z_ik T_kj,
+  //   each wave forming every T it needs itself (T_1j twice), so the corner needs no barrier inside.
+  // Products on the fp32 matrix cores (16x16x4: lane (r, q) brings A[r][q] and B[q][r]) from the fp32
+  // LDS copy of A and Z; in Z T the contraction index kk = 4q + m of step m makes T's accumulator slot m
+  // the B-operand of the same lane.  The first sums run in two accumulators.
+  auto t_prod = [&](int row0, int k0, int steps, int J) PA_INLINE {  // sum_kk A[row0 + r][kk] Z[kk][16J + r]
+    f32x4 t2[2] = {zero, zero};
 #pragma unroll
-  for (int st = 0; st < 12; ++st) {
-    const int kk = 16 * (wave + 1) + 4 * st + g;
-    arow[st] = Af[(16 * wave + r) * kLDF + (kk < 64 ? kk : 63)];
-  }
-  float zdiag[4];  // Z[16I + r][16I + 4g + m] (upper triangular: zero for 4g + m < r)
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int kk = 4 * g + m;
-    const float zv = Af[(16 * wave + kk) * kLDF + 16 * wave + r];
-    zdiag[m] = (kk >= r) ? zv : 0.f;
-  }
-#pragma unroll
-  for (int lv = 1; lv < 4; ++lv) {
-    const int I = wave, J = wave + lv;
-    if (J < 4) {
-      float zb[12];
-#pragma unroll
-      for (int st = 0; st < 4 * lv; ++st) {
-        const int kk = 16 * (I + 1) + 4 * st + g;
-        const float zv = Af[(16 * J + r) * kLDF + kk];  // Z[kk][16J + r]; Z_JJ is upper triangular
-        zb[st] = (kk >= 16 * J && kk - 16 * J > r) ? 0.f : zv;
+    for (int st = 0; st < 8; ++st) {
+      if (st < steps) {
+        const int kk = k0 + 4 * st + g;
+        const float a = Af[(row0 + r) * kLDF + kk];
+        const float zv = Af[(16 * J + r) * kLDF + kk];
+        const float b = (kk >= 16 * J && kk - 16 * J > r) ? 0.f : zv;  // Z_JJ is upper triangular
+        t2[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t2[st & 1], 0, 0, 0);
       }
-      f32x4 t2[2] = {zero, zero};
-#pragma unroll
-      for (int st = 0; st < 4 * lv; ++st)
-        t2[st & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[st], zb[st], t2[st & 1], 0, 0, 0);
-      const f32x4 tacc = t2[0] + t2[1];
-      f32x4 zacc = zero;  // D[ii][jj] = sum_kk Z[16I + ii][16I + kk] T[kk][jj]
-#pragma unroll
-      for (int m = 0; m < 4; ++m) zacc = __builtin_amdgcn_mfma_f32_16x16x4f32(zdiag[m], tacc[m], zacc, 0, 0, 0);
-      // lane (r, g) holds Z_IJ[4g + e][r] = Z[16I + 4g + e][16J + r], stored at Af[16J + r][16I + 4g + e]
-      *reinterpret_cast<float4*>(Af + (16 * J + r) * kLDF + 16 * I + 4 * g) =
-          make_float4(-zacc[0], -zacc[1], -zacc[2], -zacc[3]);
     }
-    __syncthreads();
+    return t2[0] + t2[1];
+  };
+  // zacc += Z[16I + r][16K + 4g + m] (block (I, K)) times T's slot m
+  auto z_prod = [&](f32x4 zacc, int I, int K, const f32x4& t) PA_INLINE {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int kk = 4 * g + m;
+      const float zv = Af[(16 * K + kk) * kLDF + 16 * I + r];
+      const float a = (I == K && kk < r) ? 0.f : zv;
+      zacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, t[m], zacc, 0, 0, 0);
+    }
+    return zacc;
+  };
+  // lane (r, g) holds Z_IJ[4g + e][r] = Z[16I + 4g + e][16J + r], stored at Af[16J + r][16I + 4g + e]
+  auto z_store = [&](int I, int J, const f32x4& z) PA_INLINE {
+    *reinterpret_cast<float4*>(Af + (16 * J + r) * kLDF + 16 * I + 4 * g) = make_float4(-z[0], -z[1], -z[2], -z[3]);
+  };
+  if ((wave & 1) == 0) {  // level 1
+    const int I = wave, J = wave + 1;
+    z_store(I, J, z_prod(zero, I, I, t_prod(16 * I, 16 * J, 4, J)));
   }
+  __syncthreads();
+  {  // level 2
+    const int i = wave >> 1, J = 2 + (wave & 1), steps = 4 * (J - 1);
+    const f32x4 t1 = t_prod(16, 32, steps, J);
+    if (i == 1) {
+      z_store(1, J, z_prod(zero, 1, 1, t1));
+    } else {
+      const f32x4 t0 = t_prod(0, 32, steps, J);
+      z_store(0, J, z_prod(z_prod(zero, 0, 0, t0), 0, 1, t1));
+    }
+  }
+  __syncthreads();
 
   // T^{-T}[t][s] = Z[s][t] beta_t (t >= s), hi/lo, stored with permuted columns: stored slots 8 ch + j
   // of row t hold columns c0 + 16 (j / 4) + j % 4, c0 = 32 (ch / 4) + 4 (ch % 4)
