@@ -447,7 +447,22 @@ def bench_long(args):
             f"{tf:.1f} TFLOP/s = {tf / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak (whole step, own flop count)")
         res[f"chunk{C}"] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf,
                             "frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
-    del wss
+    # prompt -> decode hand-off from the chunk-64 workspace (its last step above left the per-chunk terms)
+    steps[64]()
+    kc = torch.empty((B, H, L, d), device="cuda", dtype=torch.bfloat16)
+    vc = torch.empty_like(kc)
+    hand = lambda: native.path_attn_cache_from_prefill(v, None, workspace=wss[64], capacity=L, chunk=64,
+                                                       transport=args.transport, kcache=kc, vcache=vc)
+    hand()
+    torch.cuda.synchronize()
+    ms_h = timed(hand, 10)
+    nbytes = B * H * (L // 64) * 40 * 1024  # ktilde, P, V read and the K, V slots written, per 64-token chunk
+    gbs = nbytes / (ms_h * 1e-3) / 1e9
+    log(f"[bench] long context hand-off: {ms_h * 1e3:.1f} us, {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of HBM peak "
+        f"(each head's {L // 64}-chunk chain cut into segments)")
+    res["cache_handoff"] = {"ms": ms_h, "bytes": nbytes, "achieved_gbs": gbs, "peak_gbs": HBM_PEAK_GBS,
+                            "frac": gbs / HBM_PEAK_GBS}
+    del wss, kc, vc
     return {"workload": "PaTH prefill, long context: B=1, H=24, L=32768, d=64, bf16, transport " + args.transport
                         + "; median of 3 interleaved rounds of 3 steps",
             "transport": args.transport, "auto_chunk": auto_chunk(B, H, L, d), **res}

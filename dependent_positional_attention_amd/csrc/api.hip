@@ -20,7 +20,8 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
                     int64_t L, float scale, void* qt, void* qt_lo, void* kt, void* p_hi, void* p_lo, void* kt2,
                     void* p2_hi, void* p2_lo, float* Sm, float* fl, float* ftot, hipStream_t st);
 hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
-                          int64_t BH, int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st);
+                          int64_t BH, int64_t L, int64_t cap, void* scratch, void* kc, void* vc, hipStream_t st);
+size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M);
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
@@ -66,7 +67,7 @@ int resolve_chunk(int d, int dtype, int chunk, int64_t L) {
 // Which kernels serve (d, chunk, dtype): the matrix-core path for bf16 when built
 // for the shape, the vector path otherwise.
 path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype, int transport,
-                     path_ws_layout* lay) {
+                     path_ws_layout* lay, int64_t* off_handoff = nullptr) {
   chunk = resolve_chunk(d, dtype, chunk, L);
   if (B < 0 || H < 0 || L < 0 || d <= 0 || chunk <= 0) return PATH_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return PATH_ERR_UNSUPPORTED;
@@ -114,6 +115,8 @@ path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   lay->off_s = take(BH * M * (int64_t)sub * sub * 4);
   lay->off_fox_local = take(BH * Lp * 4);
   lay->off_fox_total = take(BH * M * 4);
+  const int64_t oh = take(mfma ? (int64_t)mfma_handoff_scratch_bytes(BH, M) : 0);  // hand-off scratch, last
+  if (off_handoff != nullptr) *off_handoff = oh;
   lay->total_bytes = off;
   return PATH_OK;
 }
@@ -230,12 +233,13 @@ path_status path_attn_scan(const void* v, const float* log_forget, void* out, fl
                  dtype, transport, workspace, workspace_bytes, stream);
 }
 
-path_status path_attn_cache_from_prefill(const void* v, const float* log_forget, const void* workspace,
+path_status path_attn_cache_from_prefill(const void* v, const float* log_forget, void* workspace,
                                          size_t workspace_bytes, void* kcache, void* vcache, float* fcache,
                                          int64_t capacity, int64_t B, int64_t H, int64_t L, int d, int chunk,
                                          int dtype, int transport, void* stream) {
   path_ws_layout lay;
-  const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay);
+  int64_t off_handoff = 0;
+  const path_status s = plan_fwd(B, H, L, d, chunk, dtype, transport, &lay, &off_handoff);
   if (s != PATH_OK) return s;
   chunk = resolve_chunk(d, dtype, chunk, L);
   if (capacity < L) return PATH_ERR_INVALID_ARG;
@@ -248,12 +252,12 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
     return PATH_ERR_UNSUPPORTED;
   if (workspace_bytes < (size_t)lay.total_bytes) return PATH_ERR_INVALID_ARG;
   if (BH > (int64_t)0x7fffffff) return PATH_ERR_UNSUPPORTED;
-  const char* ws = static_cast<const char*>(workspace);
+  char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (lay.layout_id >= 1)
     e = mfma_cache_run(transport, ws + lay.off_ktilde, ws + lay.off_p, lay.off_p_lo >= 0 ? ws + lay.off_p_lo : nullptr,
-                       v, BH, L, capacity, kcache, vcache, st);
+                       v, BH, L, capacity, ws + off_handoff, kcache, vcache, st);
   else
     e = vec_cache_run(dtype == PATH_DTYPE_BF16, d, chunk, reinterpret_cast<const float*>(ws + lay.off_ktilde),
                       reinterpret_cast<const float*>(ws + lay.off_p), v, BH, L, capacity, kcache, vcache, st);

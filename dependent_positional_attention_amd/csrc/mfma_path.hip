@@ -1108,13 +1108,19 @@ __device__ __forceinline__ void chain_advance(const ChainFrags& F, const bf16x8 
   }
 }
 
-// Run `steps` chain steps.  src(i, t) is the global tile of step i (t = 0: P hi, 1: ktilde, 2: P lo);
-// emit(i, rh, rl, F) runs on the compute waves before the step's R <- P R (skipped for the last step
-// unless advance_last).  All waves of the block call this.
-template <bool X3, int NB, typename Src, typename Emit>
-__device__ __forceinline__ void chain_run(__bf16 (*ring)[X3 ? 3 : 2][kTile], int64_t steps, bool advance_last,
+// Run `steps` chain steps.  src(i, t) is the global tile of step i (t = 0: P hi, 1: ktilde, 2: P lo;
+// without KEYS no ktilde tile is streamed); emit(i, rh, rl, F) runs on the compute waves before the
+// step's R <- P R (skipped for the last step unless advance_last).  All waves of the block call this.
+template <bool X3, bool KEYS>
+struct ChainTiles {
+  static constexpr int value = (KEYS ? 2 : 1) + (X3 ? 1 : 0);
+};
+template <bool X3, bool KEYS>
+using ChainSlot = __bf16[ChainTiles<X3, KEYS>::value][kTile];  // one ring slot: the step's tiles
+template <bool X3, int NB, bool KEYS = true, typename Src, typename Emit>
+__device__ __forceinline__ void chain_run(ChainSlot<X3, KEYS>* ring, int64_t steps, bool advance_last,
                                           f32x4 (&racc)[4], Src src, Emit emit) {
-  constexpr int NT = X3 ? 3 : 2;
+  constexpr int NT = ChainTiles<X3, KEYS>::value;
   constexpr int D = 8 * NT;  // copy instructions per step (the copy wave moves whole tiles)
   static_assert((NB - 2) * D <= 63, "vmcnt field");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1122,7 +1128,7 @@ __device__ __forceinline__ void chain_run(__bf16 (*ring)[X3 ? 3 : 2][kTile], int
   const bool copier = wave == 4;
   auto stage = [&](int64_t i) PA_INLINE {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) dma_tile<8>(ring[i % NB][t], src(i, t), kC, 0);
+    for (int t = 0; t < NT; ++t) dma_tile<8>(ring[i % NB][t], src(i, (KEYS || t == 0) ? t : 2), kC, 0);
   };
   if (copier) {
     for (int64_t i = 0; i < NB - 1 && i < steps; ++i) stage(i);
@@ -1144,7 +1150,7 @@ __device__ __forceinline__ void chain_run(__bf16 (*ring)[X3 ? 3 : 2][kTile], int
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           F.ph[t][ks] = tile_frag(ring[i % NB][0], 16 * t + r, 4 * ks + g);
-          F.k[t][ks] = tile_frag(ring[i % NB][1], 16 * t + r, 4 * ks + g);
+          if constexpr (KEYS) F.k[t][ks] = tile_frag(ring[i % NB][1], 16 * t + r, 4 * ks + g);
           if constexpr (X3) F.pl[t][ks] = tile_frag(ring[i % NB][NT - 1], 16 * t + r, 4 * ks + g);
         }
       bf16x8 rh[2], rl[2];
@@ -1232,26 +1238,131 @@ __global__ __launch_bounds__(256) void mfma_group_kernel(const __bf16* __restric
 // the key after every later transition, H_{L-1} ... H_{j+1} k_j).  In chunk terms, with R_n the
 // product of the chunk matrices after chunk n,
 //   R_{M-1} = I,   R_{n-1} = P_n R_n,   cache rows of chunk n = ktilde_n R_n   (row form),
-// the chain above over all 64-token (sub-)chunks, reusing the prep's ktilde and P.  One block per
-// (b, h); each compute wave also copies its quarter of the chunk's value rows.
+// the chain above over all 64-token (sub-)chunks, reusing the prep's ktilde and P.  With few (b, h)
+// pairs one chain per pair would leave most of the chip idle (a 32768-token prompt is a 512-step chain
+// on 24 blocks), so each pair's chain is cut into segments s of chunks lo_s .. hi_s:
+//   Q_s = P_{lo_s} ... P_{hi_s}                          (kernel 4a, segments s >= 1, in parallel)
+//   S_s = Q_{s+1} ... Q_{last} = Q_{s+1} S_{s+1}        (kernel 4b, one short chain per pair)
+//   R_{hi_s} = S_s, then the chain above down to lo_s   (kernel 4c, every segment in parallel)
+// Q_s is kept as hi + lo bf16 in the P tile layout (rows natural, columns permuted) and S_s in fp32.
+int64_t mfma_handoff_segment_chunks(int64_t BH, int64_t M) {
+  if (BH >= 128 || BH <= 0 || M < 8) return M > 0 ? M : 1;  // one segment (about a block per CU or more)
+  const int64_t want = (512 + BH - 1) / BH, most = M / 4;  // about 512 blocks, segments of >= 4 chunks
+  const int64_t nseg = want < most ? want : most;
+  return (M + nseg - 1) / nseg;
+}
+constexpr size_t kSegBytes = 2 * kTile * 2 + kD * kD * 4;  // Q_s hi, lo (bf16) and S_s (fp32) per segment
+
+// Kernel 4a: one block (4 compute waves + the copy wave) per (segment s >= 1, b, h).  The chain runs
+// from hi_s down to lo_s + 1 (R = P_{lo_s + 1} ... P_{hi_s}); the last product, with P_{lo_s}, is taken
+// transposed (Q_s^T = R^T P_{lo_s}^T, the key product's shape) so that each lane stores four
+// consecutive columns of Q_s.
+template <bool X3>
+__global__ __launch_bounds__(kChainThreads, 1) void mfma_handoff_prod_kernel(const __bf16* __restrict__ p_hi,
+                                                                             const __bf16* __restrict__ p_lo,
+                                                                             int64_t M, int64_t Gs, int64_t nseg,
+                                                                             char* __restrict__ seg) {
+  constexpr int NB = 4;
+  __shared__ __align__(1024) __bf16 ring[NB][ChainTiles<X3, false>::value][kTile];
+  const int64_t sg = blockIdx.x + 1, bh = blockIdx.y;
+  const int64_t lo = sg * Gs, hi = (lo + Gs < M ? lo + Gs : M) - 1;
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  f32x4 racc[4];
+  if (wave < 4) chain_identity(racc);
+  char* base = seg + ((size_t)bh * nseg + sg) * kSegBytes;
+  __bf16* qh = reinterpret_cast<__bf16*>(base);
+  __bf16* ql = qh + kTile;
+  auto src = [&](int64_t i, int t) -> const __bf16* {
+    return (t == 0 ? p_hi : p_lo) + ((size_t)bh * M + (hi - i)) * kD * kD;
+  };
+  const int64_t steps = hi - lo + 1;
+  auto emit = [&](int64_t i, const bf16x8 (&rh)[2], const bf16x8 (&rl)[2], const ChainFrags& F) PA_INLINE {
+    if (i != steps - 1) return;
+    // Q_s^T[y][x] = sum_m R[m][y] P_lo[x][m]: lane gets row x = 16 xt + r, columns y = 16 wave + 4g ..
+#pragma unroll
+    for (int xt = 0; xt < 4; ++xt) {
+      f32x4 a = chain_keys(rh, rl, F.ph[xt]);
+      if constexpr (X3) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) a = mfma16(rh[ks], F.pl[xt][ks], a);
+      }
+      bf16x4 h4, l4;
+      split4(a[0], a[1], a[2], a[3], h4, l4);
+      const size_t o = (size_t)(16 * xt + r) * kD + perm_pos(16 * wave + 4 * g);
+      *reinterpret_cast<bf16x4*>(qh + o) = h4;
+      *reinterpret_cast<bf16x4*>(ql + o) = l4;
+    }
+  };
+  chain_run<X3, NB, false>(ring, steps, false, racc, src, emit);
+}
+
+// Kernel 4b: one block of 4 waves per (b, h): S_{last} = I, S_s = Q_{s+1} S_{s+1} down to s = 0, each
+// wave carrying a 64 x 16 column block of S in fp32 accumulators (the chain step with Q_{s+1} as a hi + lo
+// "P"), stored in fp32 with natural columns.
+__global__ __launch_bounds__(256) void mfma_handoff_suffix_kernel(int64_t nseg, char* __restrict__ seg) {
+  const int64_t bh = blockIdx.x;
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  f32x4 racc[4];
+  chain_identity(racc);
+  for (int64_t sg = nseg - 2; sg >= 0; --sg) {
+    const char* qb = seg + ((size_t)bh * nseg + sg + 1) * kSegBytes;
+    const __bf16* qh = reinterpret_cast<const __bf16*>(qb);
+    const __bf16* ql = qh + kTile;
+    ChainFrags F;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const size_t o = (size_t)(16 * t + r) * kD + 8 * (4 * ks + g);
+        F.ph[t][ks] = *reinterpret_cast<const bf16x8*>(qh + o);
+        F.pl[t][ks] = *reinterpret_cast<const bf16x8*>(ql + o);
+      }
+    bf16x8 rh[2], rl[2];
+    acc_to_op(racc, rh, rl);
+    chain_advance<true>(F, rh, rl, racc);
+    float* so = reinterpret_cast<float*>(seg + ((size_t)bh * nseg + sg) * kSegBytes + 2 * kTile * 2);
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) so[(16 * jt + 4 * g + e) * kD + 16 * wave + r] = racc[jt][e];
+  }
+}
+
+// Kernel 4c: one block (4 compute waves + the copy wave) per (b, h, segment), 1-D grid; the chain
+// starts from S_s (the identity for the last segment) at hi_s and emits the segment's key slots; each
+// compute wave also copies its quarter of the chunk's value rows.
 template <bool X3>
 __global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf16* __restrict__ kt,
                                                                       const __bf16* __restrict__ p_hi,
                                                                       const __bf16* __restrict__ p_lo,
                                                                       const __bf16* __restrict__ v, int64_t L,
-                                                                      int64_t M, int64_t cap,
+                                                                      int64_t M, int64_t cap, int64_t Gs,
+                                                                      int64_t nseg, const char* __restrict__ seg,
                                                                       __bf16* __restrict__ kc,
                                                                       __bf16* __restrict__ vc) {
   constexpr int NB = 4;
-  __shared__ __align__(1024) __bf16 ring[NB][X3 ? 3 : 2][kTile];
+  __shared__ __align__(1024) __bf16 ring[NB][ChainTiles<X3, true>::value][kTile];
   __shared__ __align__(1024) __bf16 kst[2][kTile];  // finished key rows of the last two chunks (swizzled)
-  const int64_t bh = blockIdx.x, Lp = M * kC;
+  const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg, Lp = M * kC;
+  const int64_t lo = sg * Gs, hi = (lo + Gs < M ? lo + Gs : M) - 1;
   const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   f32x4 racc[4];
-  if (wave < 4) chain_identity(racc);
+  if (wave < 4) {
+    if (sg == nseg - 1) {
+      chain_identity(racc);
+    } else {  // S_s, fp32 with natural columns: lane (r, g) holds rows 16 jt + 4g + e of column 16 wave + r
+      const float* si = reinterpret_cast<const float*>(seg + ((size_t)bh * nseg + sg) * kSegBytes + 2 * kTile * 2);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) racc[jt][e] = si[(16 * jt + 4 * g + e) * kD + 16 * wave + r];
+    }
+  }
   auto src = [&](int64_t i, int t) -> const __bf16* {
-    const int64_t n = M - 1 - i;
+    const int64_t n = hi - i;
     if (t == 1) return kt + ((size_t)bh * Lp + n * kC) * kD;
     return (t == 0 ? p_hi : p_lo) + ((size_t)bh * M + n) * kD * kD;
   };
@@ -1259,13 +1370,13 @@ __global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf
   uint4 va = {}, vb = {};
   auto vload = [&](int64_t n) PA_INLINE {
     const int64_t j = n * kC + 16 * wave + (l >> 2);
-    if (n >= 0 && j < L) {
+    if (n >= lo && j < L) {
       const uint4* s = reinterpret_cast<const uint4*>(v + ((size_t)bh * L + j) * kD + 16 * (l & 3));
       va = s[0];
       vb = s[1];
     }
   };
-  if (wave < 4) vload(M - 1);
+  if (wave < 4) vload(hi);
   // key rows 16 wave .. 16 wave + 15 of chunk n from a staging tile: 8 lanes per 128-byte row
   auto flush = [&](int64_t n, const __bf16* tile) PA_INLINE {
 #pragma unroll
@@ -1277,7 +1388,7 @@ __global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf
     }
   };
   auto emit = [&](int64_t i, const bf16x8 (&rh)[2], const bf16x8 (&rl)[2], const ChainFrags& F) PA_INLINE {
-    const int64_t n = M - 1 - i;
+    const int64_t n = hi - i;
     {
       const int64_t j = n * kC + 16 * wave + (l >> 2);
       if (j < L) {
@@ -1297,8 +1408,9 @@ __global__ __launch_bounds__(kChainThreads, 1) void mfma_cache_kernel(const __bf
       *reinterpret_cast<bf16x4*>(kst[i & 1] + swz(row, c0 >> 3) + (c0 & 7)) = pack4(a[0], a[1], a[2], a[3]);
     }
   };
-  chain_run<X3, NB>(ring, M, false, racc, src, emit);
-  if (wave < 4) flush(0, kst[(M - 1) & 1]);
+  const int64_t steps = hi - lo + 1;
+  chain_run<X3, NB>(ring, steps, false, racc, src, emit);
+  if (wave < 4) flush(lo, kst[(steps - 1) & 1]);
 }
 
 // =========================================================================== host
@@ -1401,18 +1513,44 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
   return e;
 }
 
-// Decode cache from a prefill workspace (kernel 4): one block (4 compute waves + the copy wave) per (b, h).
+// Scratch the hand-off needs in the prefill workspace (segment products), bytes.
+size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M) {
+  if (BH <= 0 || M <= 0) return 0;
+  const int64_t Gs = mfma_handoff_segment_chunks(BH, M);
+  const int64_t nseg = (M + Gs - 1) / Gs;
+  return nseg > 1 ? (size_t)(BH * nseg) * kSegBytes : 0;
+}
+
+// Decode cache from a prefill workspace (kernel 4): segment products and their suffix products when
+// the chain is cut, then one block (4 compute waves + the copy wave) per (b, h, segment).
 hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
-                          int64_t BH, int64_t L, int64_t cap, void* kc, void* vc, hipStream_t st) {
+                          int64_t BH, int64_t L, int64_t cap, void* scratch, void* kc, void* vc, hipStream_t st) {
   const int64_t M = (L + kC - 1) / kC;
-  if (transport == 1)
-    mfma_cache_kernel<true><<<dim3((unsigned)BH), kChainThreads, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi,
-                                                                (const __bf16*)p_lo, (const __bf16*)v, L, M, cap,
-                                                                (__bf16*)kc, (__bf16*)vc);
+  const int64_t Gs = mfma_handoff_segment_chunks(BH, M), nseg = (M + Gs - 1) / Gs;
+  char* seg = static_cast<char*>(scratch);
+  if (nseg > 1 && seg == nullptr) return hipErrorInvalidValue;
+  const bool x3 = transport == 1;
+  const auto* ph = (const __bf16*)p_hi;
+  const auto* pl = x3 ? (const __bf16*)p_lo : nullptr;
+  if (nseg > 1) {
+    if (x3)
+      mfma_handoff_prod_kernel<true><<<dim3((unsigned)(nseg - 1), (unsigned)BH), kChainThreads, 0, st>>>(ph, pl, M, Gs,
+                                                                                                      nseg, seg);
+    else
+      mfma_handoff_prod_kernel<false><<<dim3((unsigned)(nseg - 1), (unsigned)BH), kChainThreads, 0, st>>>(ph, pl, M,
+                                                                                                       Gs, nseg, seg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    mfma_handoff_suffix_kernel<<<dim3((unsigned)BH), 256, 0, st>>>(nseg, seg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(BH * nseg));
+  if (x3)
+    mfma_cache_kernel<true><<<grid, kChainThreads, 0, st>>>((const __bf16*)kt, ph, pl, (const __bf16*)v, L, M, cap,
+                                                            Gs, nseg, seg, (__bf16*)kc, (__bf16*)vc);
   else
-    mfma_cache_kernel<false><<<dim3((unsigned)BH), kChainThreads, 0, st>>>((const __bf16*)kt, (const __bf16*)p_hi, nullptr,
-                                                                 (const __bf16*)v, L, M, cap, (__bf16*)kc,
-                                                                 (__bf16*)vc);
+    mfma_cache_kernel<false><<<grid, kChainThreads, 0, st>>>((const __bf16*)kt, ph, nullptr, (const __bf16*)v, L, M,
+                                                             cap, Gs, nseg, seg, (__bf16*)kc, (__bf16*)vc);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 7
+#define PATH_ABI_VERSION 8
 
 typedef enum {
   PATH_OK = 0,
@@ -281,7 +281,10 @@ path_status path_decode_step_deferred(void* kcache, void* vcache, float* fcache,
  *
  *   v               [B,H,L,d] dtype         the prompt's values (copied)
  *   log_forget      [B,H,L] fp32 or NULL    PaTH-FoX: the prompt's gates
- *   workspace       prefill workspace (read only)
+ *   workspace       prefill workspace: its per-chunk terms are read; on the
+ *                   matrix-core path its hand-off scratch (sized into
+ *                   path_attn_fwd_workspace_bytes, after every per-chunk term)
+ *                   is written
  *   kcache, vcache  [B,H,capacity,d] dtype  slots 0..L-1 written; slots >= L untouched
  *   fcache          [B,H,capacity] fp32 or NULL  PaTH-FoX: slot j <- sum_{s=j+1..L-1} f_s
  *                   (the slot bias path_decode_step expects); given iff log_forget is
@@ -289,9 +292,12 @@ path_status path_decode_step_deferred(void* kcache, void* vcache, float* fcache,
  *
  * The bf16 path chains the chunk products with fp32 accumulation (the running
  * product enters the matrix cores as hi + lo bf16) and rounds each slot to bf16
- * once; the fp32 path works in fp32.  Slot biases are fp32 sums.
+ * once; with fewer than 128 (b, h) pairs it cuts each pair's chain into
+ * segments run in parallel (products of whole segments kept as hi + lo bf16,
+ * their suffix products in fp32).  The fp32 path works in fp32.  Slot biases are
+ * fp32 sums.
  */
-path_status path_attn_cache_from_prefill(const void* v, const float* log_forget, const void* workspace,
+path_status path_attn_cache_from_prefill(const void* v, const float* log_forget, void* workspace,
                                          size_t workspace_bytes, void* kcache, void* vcache, float* fcache,
                                          int64_t capacity, int64_t B, int64_t H, int64_t L, int d, int chunk,
                                          int dtype, int transport, void* stream);

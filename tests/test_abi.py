@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 7
+    assert L.path_abi_version() == 8
     for s in range(5):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"

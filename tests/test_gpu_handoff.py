@@ -89,6 +89,8 @@ def oracle_slots(x, L, heads=None, rows=None):
     ("bf16", 64, 64, "bf16x3", 512, "beta2"),    # norm-preserving transitions
     ("bf16", 64, 128, "bf16x3", 333, "lm"),      # 128-token chunks: the hand-off chains 64-token halves
     ("bf16", 64, 128, "bf16", 64, "lm"),         # one half-chunk
+    ("bf16", 64, 64, "bf16", 1100, "lm"),        # 18 chunks: the chain cut into segments of 5, 5, 5, 3
+    ("bf16", 64, 64, "bf16x3", 1100, "beta2"),   # the same, norm-preserving, bf16x3 segment products
     ("bf16", 64, 64, "bf16", 1, "lm"),           # one token: the slot is the key
     ("bf16", 32, 32, "bf16", 100, "lm"),         # vector path, bf16 storage
     ("f32", 64, 64, "bf16", 200, "lm"),          # vector path, fp32
