@@ -1983,6 +1983,11 @@ __global__ __launch_bounds__(256) void bwd_forget_kernel(const float* __restrict
 }
 
 // ------------------------------------------------------------------------------- launch
+// mfma_path.hip: the forward's per-chunk terms in fp32 from bf16 inputs at d = chunk = 64 (the prefill's prep
+// kernel with fp32 outputs)
+hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
+                             int64_t BH, int64_t L, float qs, float* qt, float* kt, float* Pm, float* Sm, float* fl,
+                             float* ftot, hipStream_t st);
 // vector_path.hip: the forward's per-chunk terms in fp32 (other shapes than d = chunk = 64)
 hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
                    const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
@@ -2006,13 +2011,20 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   };
   const int64_t G = bwd_band_chunks(M), NPB = bwd_band_pairs(M);
   if constexpr (D == 64 && C == 64) {  // the matrix cores: bf16 products for bf16 inputs, fp32 ones for fp32
-    if ((e = lds((const void*)bwd_chunk_fwd_mfma_kernel<T>, kLdsChunkFwdMfma)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_query_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_key_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_chunk_grad_mfma_kernel<T>, kLdsChunkMfma)) != hipSuccess) return e;
-    bwd_chunk_fwd_mfma_kernel<T><<<grid, 256, kLdsChunkFwdMfma, st>>>(
-        (const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (std::is_same<T, __bf16>::value) {  // the prefill's prep, fp32 outputs
+      if ((e = mfma_prep_f32_run(q, k, w, beta, logf, BH, L, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot,
+                                 st)) != hipSuccess)
+        return e;
+    } else {
+      if ((e = lds((const void*)bwd_chunk_fwd_mfma_kernel<T>, kLdsChunkFwdMfma)) != hipSuccess) return e;
+      bwd_chunk_fwd_mfma_kernel<T><<<grid, 256, kLdsChunkFwdMfma, st>>>(
+          (const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl,
+          b.ftot);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int64_t xh = kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd);
     for (int64_t mb = 0; mb < M; mb += G) {
       const pair_band band{mb, mb + G < M ? mb + G : M, NPB};

@@ -186,7 +186,9 @@ static_assert(kPrepLds <= 160 * 1024 / 3, "prep LDS plan must allow three blocks
 __device__ __forceinline__ int perm_col(int c) { return perm_pos(c); }
 
 // X3: the lo halves of qtilde and P (bf16x3 transport) are formed and stored; without it only hi.
-template <bool X3>
+// F32: qtilde, ktilde and P are stored in fp32 with natural columns instead (the per-chunk terms the
+// backward pass works from; qt, kt and p_hi then point to fp32 arrays of the same shapes).
+template <bool X3, bool F32 = false>
 __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
     const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, float qs,
@@ -459,7 +461,10 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
       const bf16x4 q4 = q4s[xt];
       const float v0 = ((float)q4[0] - dq[0]) * qs, v1 = ((float)q4[1] - dq[1]) * qs,
                   v2 = ((float)q4[2] - dq[2]) * qs, v3 = ((float)q4[3] - dq[3]) * qs;
-      if constexpr (X3) {
+      if constexpr (F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(qt) + (chunk_rows + a) * kD + x0) =
+            make_float4(v0, v1, v2, v3);
+      } else if constexpr (X3) {
         bf16x4 h4, l4;
         split4(v0, v1, v2, v3, h4, l4);
         *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
@@ -471,8 +476,13 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     // ktilde[b][x] = k_b[x] - D[x][b]
     {
       const bf16x4 k4 = k4s[xt];
-      *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) =
-          pack4((float)k4[0] - dk[0], (float)k4[1] - dk[1], (float)k4[2] - dk[2], (float)k4[3] - dk[3]);
+      const float u0 = (float)k4[0] - dk[0], u1 = (float)k4[1] - dk[1], u2 = (float)k4[2] - dk[2],
+                  u3 = (float)k4[3] - dk[3];
+      if constexpr (F32)
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(kt) + (chunk_rows + a) * kD + x0) =
+            make_float4(u0, u1, u2, u3);
+      else
+        *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) = pack4(u0, u1, u2, u3);
     }
     // P[x][y] = delta - D[y][x]  (lane: row x = 16 xt + r, columns y = 16 wave + 4g .. +3)
     {
@@ -480,7 +490,10 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
       const float e0 = (y0 == xr ? 1.f : 0.f) - dp[0], e1 = (y0 + 1 == xr ? 1.f : 0.f) - dp[1],
                   e2 = (y0 + 2 == xr ? 1.f : 0.f) - dp[2], e3 = (y0 + 3 == xr ? 1.f : 0.f) - dp[3];
       const int py = perm_pos(y0);
-      if constexpr (X3) {
+      if constexpr (F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p_hi) + chunk_mat + (size_t)xr * kD + y0) =
+            make_float4(e0, e1, e2, e3);
+      } else if constexpr (X3) {
         bf16x4 ph, pl;
         split4(e0, e1, e2, e3, ph, pl);
         *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = ph;
@@ -1519,6 +1532,21 @@ size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M) {
   const int64_t Gs = mfma_handoff_segment_chunks(BH, M);
   const int64_t nseg = (M + Gs - 1) / Gs;
   return nseg > 1 ? (size_t)(BH * nseg) * kSegBytes : 0;
+}
+
+// The prep in fp32 output form for the backward pass (bf16 inputs, d = chunk = 64): qtilde and S
+// scaled by qs, ktilde, P, FoX chunk-local prefixes and chunk totals, all fp32 with natural columns.
+hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
+                             int64_t BH, int64_t L, float qs, float* qt, float* kt, float* Pm, float* Sm, float* fl,
+                             float* ftot, hipStream_t st) {
+  const int64_t M = (L + kC - 1) / kC;
+  hipError_t e = hipFuncSetAttribute((const void*)mfma_prep_kernel<false, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPrepLds);
+  if (e != hipSuccess) return e;
+  mfma_prep_kernel<false, true><<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
+      (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, qs, reinterpret_cast<__bf16*>(qt),
+      nullptr, reinterpret_cast<__bf16*>(kt), reinterpret_cast<__bf16*>(Pm), nullptr, Sm, fl, ftot);
+  return hipGetLastError();
 }
 
 // Decode cache from a prefill workspace (kernel 4): segment products and their suffix products when
