@@ -623,7 +623,7 @@ def main():
     B_, H_, L_, d_ = res["B"], res["H"], res["L"], res["d"]
     attn_flops = 4.0 * d_ * (L_ * (L_ + 1) / 2) * B_ * H_
     ktag = "<{},{},1,2,4>".format("true" if args.fox else "false", "true" if args.transport == "bf16x3" else "false")
-    ptag = "<{}>".format("true" if args.transport == "bf16x3" else "false")
+    ptag = "<{},false>".format("true" if args.transport == "bf16x3" else "false")
     t_scan = measured_traffic(PREFILL_COUNTERS, "mfma_attn_kernel" + ktag, "mfma_path.hip")
     t_prep = measured_traffic(PREFILL_COUNTERS, "mfma_prep_kernel" + ptag, "mfma_path.hip")
     line = {

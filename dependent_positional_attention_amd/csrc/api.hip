@@ -52,12 +52,12 @@ bool valid_dtype(int dt) { return dt == PATH_DTYPE_F32 || dt == PATH_DTYPE_BF16;
 
 // chunk 0 selects the chunk measured fastest for the path and length.  Matrix-core path (bf16, d = 64),
 // whole prefill call, chunk 64 / 128 / 256 at about 3.1M tokens per call:
-//   L = 512, 1024, 2048:          chunk 64 fastest (the grouping kernel and the partial top group cost more
-//                                  than the transports they save at 8-32 chunks per sequence)
-//   L = 4096, 8192, 16384, 32768: chunk 256 fastest (4-10% ahead of chunk 64; the scan moves its queries
-//                                  once per 256 keys)
+//   L = 512, 1024, 2048, 4096: chunk 64 fastest (the grouping kernel and the partial top group cost more
+//                               than the transports they save at 8-64 chunks per sequence; 2-3% at 4096)
+//   L = 8192, 16384, 32768:    chunk 256 fastest (3-7% ahead of chunk 64; the scan moves its queries
+//                               once per 256 keys)
 // so lengths up to kAutoChunkSplit take 64 and longer ones 256.  The vector path takes 64.
-constexpr int64_t kAutoChunkSplit = 2048;
+constexpr int64_t kAutoChunkSplit = 4096;
 int resolve_chunk(int d, int dtype, int chunk, int64_t L) {
   if (chunk != 0) return chunk;
   if (dtype == PATH_DTYPE_BF16 && mfma_supported(d, 256) && L > kAutoChunkSplit) return 256;

@@ -90,7 +90,7 @@ path_status path_attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d
  *   scale        multiplies k^T(...)q; the FoX bias is added after scaling
  *   chunk        block length C of the scan; results do not depend on it beyond rounding;
  *                0 selects the fastest measured chunk for the path and length: on the
- *                matrix-core path 64 for L <= 2048 and 256 for longer sequences, on the
+ *                matrix-core path 64 for L <= 4096 and 256 for longer sequences, on the
  *                vector path 64; the same choice in every call with the same L
  *   workspace    device buffer of at least path_attn_fwd_workspace_bytes bytes,
  *                caller-owned; its contents on return hold the per-chunk terms

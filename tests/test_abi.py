@@ -90,8 +90,8 @@ def test_workspace_planning_grouped_chunks(L, chunk, groups):
 
 
 def test_chunk_zero_selects_the_fastest_chunk(L):
-    """chunk 0 plans exactly what the measured table picks: chunk 256 on the matrix-core path beyond 2048
-    tokens, chunk 64 up to 2048 tokens and on the vector path."""
+    """chunk 0 plans exactly what the measured table picks: chunk 256 on the matrix-core path beyond 4096
+    tokens, chunk 64 up to 4096 tokens and on the vector path."""
     for args, chunk, dtype in (((2, 3, 5000, 64), 256, BF16), ((2, 3, 1000, 64), 64, BF16), ((1, 2, 100, 16), 64, F32)):
         for transport in (0, 1):
             a, b = native.WsLayout(), native.WsLayout()
@@ -278,9 +278,9 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.stdout.strip() == ""
 
 
-@pytest.mark.parametrize("L,layout_id", [(64, 1), (2048, 1), (2049, 2), (4096, 2), (32768, 2)])
+@pytest.mark.parametrize("L,layout_id", [(64, 1), (4096, 1), (4097, 2), (8192, 2), (32768, 2)])
 def test_automatic_chunk_table(L, layout_id):
-    """chunk = 0 on the matrix-core path (bf16, d = 64): 64-token chunks (layout 1) up to 2048 tokens,
+    """chunk = 0 on the matrix-core path (bf16, d = 64): 64-token chunks (layout 1) up to 4096 tokens,
     256-token chunks (layout 2, four sub-chunks per chunk) beyond, as measured fastest; the vector path
     (fp32) takes 64."""
     lay = native.WsLayout()

@@ -158,10 +158,10 @@ def test_small_shapes_grouped_chunks(B, H, L, recipe, transport, chunk):
     assert_parity(gl, rl, "bf16", "lse")
 
 
-@pytest.mark.parametrize("L,expect", [(777, 64), (2048, 64), (2049, 256), (4096, 256), (32768, 256)])
+@pytest.mark.parametrize("L,expect", [(777, 64), (4096, 64), (4097, 256), (32768, 256)])
 def test_chunk_zero_follows_the_measured_table(L, expect):
     """The automatic chunk on the matrix-core path is the one the chunk sweep measured fastest: 64 up to
-    2048 tokens, 256 beyond (the 760M-class length 4096 and the long-context length 32768 included):
+    4096 tokens (the 760M-class length included), 256 beyond (the long-context length 32768 included):
     bit-identical outputs to that chunk."""
     x = synth.make_fwd_inputs(1, 2 if L <= 4096 else 1, L, D, recipe="fox", dtype="bf16", seed=6)
     print(f"[case] chunk 0 at L={L} (expect {expect})", flush=True)
