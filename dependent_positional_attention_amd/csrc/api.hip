@@ -22,6 +22,7 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
 hipError_t mfma_cache_run(int transport, const void* kt, const void* p_hi, const void* p_lo, const void* v,
                           int64_t BH, int64_t L, int64_t cap, void* scratch, void* kc, void* vc, hipStream_t st);
 size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M);
+size_t mfma_s_chunk_bytes();
 // decode.hip
 bool decode_supported(int d);
 int64_t decode_auto_splits(int64_t keys);
@@ -112,7 +113,7 @@ path_status plan_fwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
       if (transport == PATH_TRANSPORT_BF16X3) lay->off_p_c2_lo = take(BH * MG * d * d * 2);
     }
   }
-  lay->off_s = take(BH * M * (int64_t)sub * sub * 4);
+  lay->off_s = take(BH * M * (mfma ? (int64_t)mfma_s_chunk_bytes() : (int64_t)sub * sub * 4));
   lay->off_fox_local = take(BH * Lp * 4);
   lay->off_fox_total = take(BH * M * 4);
   const int64_t oh = take(mfma ? (int64_t)mfma_handoff_scratch_bytes(BH, M) : 0);  // hand-off scratch, last

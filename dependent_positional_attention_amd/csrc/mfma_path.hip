@@ -185,6 +185,15 @@ static_assert(kPrepLds <= 160 * 1024 / 3, "prep LDS plan must allow three blocks
 
 __device__ __forceinline__ int perm_col(int c) { return perm_pos(c); }
 
+// In-chunk logits S of the bf16 forms, packed: only entries on or below the diagonal are ever read, so
+// row a keeps its 4-float groups 0 .. a/4 (columns 0 .. 4(a/4) + 3; the entries of the last group
+// past the diagonal are unspecified), rows back to back.  Row a starts at group
+// a + sum_{b<a} floor(b/4) = a + 2u(u - 1) + uv (u = a/4, v = a%4); a 64-token chunk takes 544
+// groups, 53% of the square.
+constexpr int kSGroups = 544;
+__host__ __device__ constexpr int s_row_group(int a) { return a + 2 * (a >> 2) * ((a >> 2) - 1) + (a >> 2) * (a & 3); }
+static_assert(s_row_group(kC) == kSGroups, "packed S size");
+
 // X3: the lo halves of qtilde and P (bf16x3 transport) are formed and stored; without it only hi.
 // F32: qtilde, ktilde and P are stored in fp32 with natural columns instead (the per-chunk terms the
 // backward pass works from; qt, kt and p_hi then point to fp32 arrays of the same shapes).
@@ -502,12 +511,17 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
         *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = pack4(e0, e1, e2, e3);
       }
     }
-    // S[a][b] = (q_a.k_b - D[b][a]) * qs  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3)
+    // S[a][b] = (q_a.k_b - D[b][a]) * qs  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3):
+    // the fp32 form keeps the square, the bf16 forms the packed lower triangle
     {
       const int aq = 16 * xt + r, b0 = 16 * wave + 4 * g;
       const float4 s4 = make_float4((kq[xt][0] - ds[0]) * qs, (kq[xt][1] - ds[1]) * qs, (kq[xt][2] - ds[2]) * qs,
                                     (kq[xt][3] - ds[3]) * qs);
-      *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kC + aq) * kC + b0) = s4;
+      if constexpr (F32) {
+        *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kC + aq) * kC + b0) = s4;
+      } else if (b0 <= aq) {
+        *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kSGroups + s_row_group(aq) + (b0 >> 2)) * 4) = s4;
+      }
     }
   }
   (void)ia;
@@ -783,13 +797,17 @@ __global__ __launch_bounds__(64 * W, (ScanShape<X3, QT, W>::kWaves)) void mfma_a
   float4 own_s[4][QT], own_f[4];
   bf16x8 own_q[QT][2], own_ql[QT][2];
   auto own_load = [&]() PA_INLINE {
-    const float* Sb = Sm + ((size_t)bh * M + m) * kC * kC;
+    // packed S: a group past row a's last (columns beyond the diagonal, masked below) re-reads the last
+    const float* Sb = Sm + ((size_t)bh * M + m) * kSGroups * 4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (FOX) own_f[t] = *reinterpret_cast<const float4*>(fl + bh * Lp + m * kC + 16 * t + 4 * g);
 #pragma unroll
-      for (int qi = 0; qi < QT; ++qi)
-        own_s[t][qi] = *reinterpret_cast<const float4*>(Sb + (q0 + 16 * qi + r) * kC + 16 * t + 4 * g);
+      for (int qi = 0; qi < QT; ++qi) {
+        const int a = q0 + 16 * qi + r, last = a >> 2;
+        const int grp = (4 * t + g < last) ? 4 * t + g : last;
+        own_s[t][qi] = *reinterpret_cast<const float4*>(Sb + (s_row_group(a) + grp) * 4);
+      }
     }
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi)
@@ -1525,6 +1543,9 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
   }
   return e;
 }
+
+// Bytes of one 64-token chunk's packed in-chunk logits (bf16 forms).
+size_t mfma_s_chunk_bytes() { return (size_t)kSGroups * 4 * sizeof(float); }
 
 // Scratch the hand-off needs in the prefill workspace (segment products), bytes.
 size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M) {

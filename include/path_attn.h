@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 8
+#define PATH_ABI_VERSION 9
 
 typedef enum {
   PATH_OK = 0,
@@ -139,7 +139,10 @@ path_status path_attn_scan(const void* v, const float* log_forget, void* out, fl
  *   layout_id 1 (matrix-core path): qtilde, ktilde [B*H, M*C, d] bf16 with columns permuted
  *     within each 32-wide block (stored slot 8g+j holds column 16(j/4)+4g+(j%4));
  *     qtilde_lo (bf16x3 transport only): the bf16 residual qtilde - qtilde_hi, same layout;
- *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S as layout 0;
+ *     P (hi) and P_lo [B*H, M, d, d] bf16 (rows natural, columns permuted); S fp32 as in layout 0
+ *     but packed per chunk as the lower triangle in groups of 4 columns: row a holds columns
+ *     0 .. 4 floor(a/4) + 3 (those past the diagonal unspecified) and starts at float
+ *     4 (a + 2u(u-1) + uv), u = floor(a/4), v = a mod 4; a chunk takes 2176 floats;
  *     qtilde (hi + lo) and S carry the factor scale * log2(e) as in layout 0.
  *   layout_id 2 (matrix-core path, chunk 128 or 256 = G sub-chunks of 64): every term of layout 1
  *     for the 64-token sub-chunks (C = 64, M = num_sub_chunks), plus ktilde_c2 [B*H, M*64, d] bf16:

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_strings(L):
-    assert L.path_abi_version() == 8
+    assert L.path_abi_version() == 9
     for s in range(5):
         assert L.path_status_string(s)
     assert L.path_status_string(99) == b"unknown status"
@@ -87,6 +87,21 @@ def test_workspace_planning_grouped_chunks(L, chunk, groups):
     assert ws_bytes(L, 1, 1, 300, 64, chunk, F32, 0)[0] == UNSUPPORTED  # fp32 has no grouped chunks
     assert ws_bytes(L, 1, 1, 300, 32, chunk, BF16, 0)[0] == UNSUPPORTED
     assert ws_bytes(L, 1, 1, 300, 64, 512, BF16, 0)[0] == UNSUPPORTED
+
+
+def test_packed_in_chunk_logits_region(L):
+    """The matrix-core layouts keep the in-chunk logits S as a packed lower triangle of 4-float groups:
+    sum over rows a = 0..63 of (floor(a/4) + 1) groups = 544 groups = 2176 floats per 64-token chunk
+    (the vector path keeps the full C x C square)."""
+    groups = sum(a // 4 + 1 for a in range(64))
+    assert groups == 544
+    for chunk in (64, 128):
+        lay = native.WsLayout()
+        assert L.path_attn_workspace_layout(2, 3, 300, 64, chunk, BF16, 0, ctypes.byref(lay)) == OK
+        M = lay.num_sub_chunks
+        assert lay.off_fox_local - lay.off_s == -(-(6 * M * groups * 16) // 256) * 256
+    assert L.path_attn_workspace_layout(2, 3, 100, 16, 16, F32, 0, ctypes.byref(lay)) == OK
+    assert lay.off_fox_local - lay.off_s == -(-(6 * 7 * 16 * 16 * 4) // 256) * 256
 
 
 def test_chunk_zero_selects_the_fastest_chunk(L):

@@ -47,6 +47,22 @@ def run(x, transport="bf16", chunk=C, keep_ws=False):
     return host(out), host(lse)
 
 
+S_CHUNK = 2176  # floats of one chunk's packed in-chunk logits (matrix-core layouts)
+
+
+def unpack_s(flat, BH, M):
+    """The packed lower-triangle S of the matrix-core layouts as [BH, M, C, C] (zeros where nothing is
+    stored): row a of a chunk holds columns 0 .. 4 floor(a/4) + 3 from float 4 (a + 2u(u-1) + uv),
+    u = floor(a/4), v = a mod 4."""
+    flat = np.asarray(flat).reshape(BH, M, S_CHUNK)
+    out = np.zeros((BH, M, C, C))
+    for a in range(C):
+        u, v = divmod(a, 4)
+        start, n = 4 * (a + 2 * u * (u - 1) + u * v), 4 * (u + 1)
+        out[:, :, a, :n] = flat[:, :, start:start + n]
+    return out
+
+
 def ws_view(ws, off, count, dtype):
     b = ws[off:off + count * (2 if dtype == torch.bfloat16 else 4)]
     return b.view(dtype).float().cpu().numpy().astype(np.float64)
@@ -91,7 +107,7 @@ def test_chunk_intermediates(recipe, transport):
     qt = unpermute_cols(qt.reshape(B * H, Lp, D))
     P = unpermute_cols(ph.reshape(B * H, M, D, D))
     kt = unpermute_cols(ws_view(ws, lay.off_ktilde, B * H * Lp * D, torch.bfloat16).reshape(B * H, Lp, D))
-    S = ws_view(ws, lay.off_s, B * H * M * C * C, torch.float32).reshape(B * H, M, C, C)
+    S = unpack_s(ws_view(ws, lay.off_s, B * H * M * S_CHUNK, torch.float32), B * H, M)
     store = 0.0 if x3 else 2.0 ** -8  # relative rounding of the stored qtilde and P (bf16 unit roundoff)
     worst = dict(q=0.0, k=0.0, p=0.0, s=0.0)
     for bh in range(B * H):
