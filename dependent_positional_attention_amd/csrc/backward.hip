@@ -591,6 +591,29 @@ __device__ __forceinline__ void put_tile(float* dst, const f32x4 (&reg)[4], int 
   }
 }
 
+// The pair states r^(n) and dr^(n-1) of the matrix-core chunk-pair kernels are stored in bf16 for a bf16
+// input (the forward rounds its running queries to bf16 in the same way; the chains themselves run in
+// fp32 registers) and in fp32 for an fp32 input.  Tiles are row-major with row stride 64.
+template <typename T>
+using state_t = typename std::conditional<std::is_same<T, __bf16>::value, __bf16, float>::type;
+template <typename S>
+__device__ __forceinline__ void acc_to_state(const f32x4 (&acc)[4], S* dst, int w, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[(16 * w + 4 * g + e) * 64 + 16 * cb + r] = from_f32<S>(acc[cb][e]);
+}
+// a state tile into registers in the fetch_tile layout, widened to fp32
+template <typename S>
+__device__ __forceinline__ void fetch_state(f32x4 (&reg)[4], const S* __restrict__ src, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, row = e >> 4, c4 = (e & 15) * 4;
+    reg[i] = widen4<S>(*reinterpret_cast<const raw4<S>*>(src + row * 64 + c4));
+  }
+}
+
 // A-operand of mm64 held in registers: a[4 kb + j] = A(16w + r, 16 kb + 4g + j), i.e. the wave's own
 // 16 rows of a row-major 64 x 64 operand.
 __device__ __forceinline__ void frag_f32(float (&a)[16], const float* __restrict__ src, int w, int lane) {
@@ -728,15 +751,14 @@ __device__ __forceinline__ void split_regs(bf16x8 (&h)[2], bf16x8 (&l)[2], const
     split8(f32x4{v[8 * ks], v[8 * ks + 1], v[8 * ks + 2], v[8 * ks + 3]},
            f32x4{v[8 * ks + 4], v[8 * ks + 5], v[8 * ks + 6], v[8 * ks + 7]}, h[ks], l[ks]);
 }
-// fp32 values of the wave's rows in that layout, from a global fp32 tile (row stride 64)
-__device__ __forceinline__ void rows32(float (&v)[16], const float* __restrict__ A, int w, int lane) {
+// the same values from a bf16 state tile (row stride 64), widened
+__device__ __forceinline__ void rows_bf16(float (&v)[16], const __bf16* __restrict__ A, int w, int lane) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const float* p = A + (16 * w + r) * 64 + 32 * ks + 8 * g;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(A + (16 * w + r) * 64 + 32 * ks + 8 * g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[8 * ks + i] = x[i], v[8 * ks + 4 + i] = y[i];
+    for (int i = 0; i < 8; ++i) v[8 * ks + i] = (float)x[i];
   }
 }
 // acc[cb] += sum_k A(16w + r', k) B[16cb + r''][k]: A as split fragments, B an fp32 LDS tile (stride kS)
@@ -838,7 +860,7 @@ template <typename T>
 __device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4], f32x4 (&pP)[4], float (&pra)[16],
                                                  float& pF, float& poff, const float* __restrict__ kt,
                                                  const T* __restrict__ vb, const float* __restrict__ Pm,
-                                                 const float* __restrict__ St, const float* __restrict__ fl,
+                                                 const state_t<T>* __restrict__ St, const float* __restrict__ fl,
                                                  const float* __restrict__ Off, const pair_band& band, int64_t bh,
                                                  int64_t m, int64_t n, int64_t M, int64_t L, int tid, int w,
                                                  int lane) {
@@ -848,7 +870,7 @@ __device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4
   fetch_tile(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
   fetch_rows(pV, vb, n * C, L, tid);
   fetch_tile(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
-  if constexpr (std::is_same<T, __bf16>::value) rows32(pra, St + pr * CD, w, lane);  // for the bf16x3 logits
+  if constexpr (std::is_same<T, __bf16>::value) rows_bf16(pra, St + pr * CD, w, lane);  // for the bf16 logits
   else frag_f32(pra, St + pr * CD, w, lane);
   if (fl != nullptr) {
     pF = fl[(size_t)bh * Lp + (size_t)n * C + (tid & 63)];
@@ -857,16 +879,16 @@ __device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4
 }
 template <typename T>
 __device__ __forceinline__ void fetch_key_pair(f32x4 (&pR)[4], f32x4 (&pG)[4], raw4<T> (&pO)[4], float& pl2,
-                                               float& pDv, float& poff, const float* __restrict__ St,
-                                               const float* __restrict__ Gst, const T* __restrict__ ob,
+                                               float& pDv, float& poff, const state_t<T>* __restrict__ St,
+                                               const state_t<T>* __restrict__ Gst, const T* __restrict__ ob,
                                                const float* __restrict__ lse2w, const float* __restrict__ Dw,
                                                const float* __restrict__ Off, bool fox, const pair_band& band,
                                                int64_t bh, int64_t m, int64_t n, int64_t M, int64_t L, int tid) {
   constexpr int C = 64, CD = 64 * 64;
   const int64_t Lp = M * C;
   const size_t pr = band.slot(bh, m, n);
-  fetch_tile(pR, St + pr * CD, tid);
-  fetch_tile(pG, Gst + pr * CD, tid);  // not written for n = 0 (no transport there): fetched, not used
+  fetch_state(pR, St + pr * CD, tid);
+  fetch_state(pG, Gst + pr * CD, tid);  // not written for n = 0 (no transport there): fetched, not used
   fetch_rows(pO, ob, m * C, L, tid);
   const size_t r0 = (size_t)bh * Lp + (size_t)m * C;
   pl2 = lse2w[r0 + (tid & 63)];
@@ -903,7 +925,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
-    int64_t L, int64_t M, float scale, pair_band band, float* __restrict__ St, float* __restrict__ Gst,
+    int64_t L, int64_t M, float scale, pair_band band, state_t<T>* __restrict__ St, state_t<T>* __restrict__ Gst,
     float* __restrict__ Off, float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow,
     float* __restrict__ dqt, float* __restrict__ dSm, int64_t BH) {
   constexpr int C = 64, CD = 64 * 64;
@@ -963,7 +985,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const size_t pr = band.slot(bh, m, n);
     if (fox) off += ftot[bh * M + n];
     if (tid == 0) Off[pr] = off;
-    acc_to_global(R, St + pr * CD, w, lane);
+    acc_to_state(R, St + pr * CD, w, lane);
     if (n > 0) {
       acc_to_lds(R, Xs, w, lane);
       __syncthreads();  // every wave is done with the previous P
@@ -1029,7 +1051,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     for (int x = 0; x < 16; ++x) ra[x] = pra[x];
     if (n > 0) {
       acc_to_lds(G, Xs, w, lane);  // dr^(n-1), this wave's rows
-      acc_to_global(G, Gst + pr * CD, w, lane);
+      acc_to_state(G, Gst + pr * CD, w, lane);
     }
     __syncthreads();
     // the last step fetches its own pair again (not used)
@@ -1096,7 +1118,8 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
 template <typename T>
 __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
-    const T* __restrict__ v, const T* __restrict__ dout, const float* __restrict__ St, const float* __restrict__ Gst,
+    const T* __restrict__ v, const T* __restrict__ dout, const state_t<T>* __restrict__ St,
+    const state_t<T>* __restrict__ Gst,
     const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
     int64_t M, pair_band band, T* __restrict__ dv, float* __restrict__ dva, float* __restrict__ dkt,
     float* __restrict__ dPm, float* __restrict__ dcol, int64_t BH) {
@@ -2030,10 +2053,12 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
       const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
       bwd_query_mfma_kernel<T><<<dim3((unsigned)(xh * (band.me - band.mb))), 256, kLdsPairMfma, st>>>(
           b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
-          M, scale, band, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm, BH);
+          M, scale, band, reinterpret_cast<state_t<T>*>(b.St), reinterpret_cast<state_t<T>*>(b.Gst), b.Off, b.lse2,
+          b.Dv, b.drow, b.dqt, b.dSm, BH);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       bwd_key_mfma_kernel<T><<<dim3((unsigned)(xh * band.me)), 256, kLdsPairMfma, st>>>(
-          b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L, M,
+          b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, reinterpret_cast<const state_t<T>*>(b.St),
+          reinterpret_cast<const state_t<T>*>(b.Gst), b.Off, b.lse2, b.Dv, L, M,
           band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }

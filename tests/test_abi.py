@@ -236,11 +236,14 @@ def bwd_call(L, **kw):
 def test_bwd_workspace_planning(L):
     n = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 64, BF16, ctypes.byref(n)) == OK
-    # states and their gradients of one band of query chunks at a time: 64 chunks in bands of 8, the
-    # largest band (chunks 56 .. 63) holding 56 + ... + 63 pairs
+    # states and their gradients of one band of query chunks at a time (bf16 for a bf16 input): 64 chunks
+    # in bands of 8, the largest band (chunks 56 .. 63) holding 56 + ... + 63 pairs
     pairs = sum(range(56, 64))
-    assert n.value >= 2 * 8 * 24 * pairs * 64 * 64 * 4
-    assert n.value < 2 * 8 * 24 * pairs * 64 * 64 * 4 + (2 << 30)
+    assert n.value >= 2 * 8 * 24 * pairs * 64 * 64 * 2
+    assert n.value < 2 * 8 * 24 * pairs * 64 * 64 * 2 + (2 << 30)
+    nf = ctypes.c_size_t(0)
+    assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 64, F32, ctypes.byref(nf)) == OK
+    assert nf.value - n.value == 2 * 8 * 24 * pairs * 64 * 64 * 2  # fp32 states for an fp32 input
     n0 = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 0, BF16, ctypes.byref(n0)) == OK
     assert n0.value == n.value  # chunk 0 = 64
