@@ -779,6 +779,28 @@ __device__ __forceinline__ void mm64_x3(f32x4 (&acc)[4], const bf16x8 (&ah)[2], 
     }
 }
 
+// acc[cb] += sum_k A(16w + r', k) B[16cb + r''][k] for A holding bf16 numbers (fragments converted
+// exactly from fp32 values in registers, v as in split_regs), B an fp32 LDS tile split while it is read:
+// two products instead of three (A has no lo part)
+__device__ __forceinline__ void mm64_x2(f32x4 (&acc)[4], const float (&v)[16], const float* __restrict__ B,
+                                        int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (__bf16)v[8 * ks + i];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const float* p = B + (16 * cb + r) * kS + 32 * ks + 8 * g;
+      bf16x8 bh, bl;
+      split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), bh, bl);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[cb], 0, 0, 0);
+    }
+  }
+}
+
 // acc[cb] += sum_k A(16w + r', k) B[k][16cb + r'']: A as split fragments, B an fp32 LDS tile (stride kS) read
 // by columns and split while it is read
 __device__ __forceinline__ void mm64_x3_cols(f32x4 (&acc)[4], const bf16x8 (&ah)[2], const bf16x8 (&al)[2],
@@ -1071,9 +1093,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     zero4(Z);
     zero4(DP);
     if constexpr (kBf) {
-      bf16x8 ah[2], al[2];
-      split_regs(ah, al, ra);
-      mm64_x3(Z, ah, al, Ks, lane);
+      mm64_x2(Z, ra, Ks, lane);  // r^(n) is stored in bf16
     } else {
       mm64_ra<false>(Z, ra, Ks, lane);
     }
@@ -1222,8 +1242,12 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     f32x4 ZT[4], DT[4];
     zero4(ZT);
     zero4(DT);
-    if constexpr (kBf) mm64_x3(ZT, kah, kal, Rs, lane);  // (r ktilde^T)^T
-    else mm64_ra<false>(ZT, ka, Rs, lane);
+    if constexpr (kBf) {  // (r ktilde^T)^T; r^(n) is stored in bf16
+      mm64_bf16(ZT, kah, Rs, lane);
+      mm64_bf16(ZT, kal, Rs, lane);
+    } else {
+      mm64_ra<false>(ZT, ka, Rs, lane);
+    }
     if constexpr (kBf) mm64_bf16(DT, vb16, Os, lane);  // (dO v^T)^T
     else mm64_ra<false>(DT, va, Os, lane);
     float gz[4][4];
@@ -1245,9 +1269,11 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) Xs[(16 * w + 4 * g + e) * kS + 16 * cb + r] = gz[cb][e];  // after the reads of p
-    mmx<T, false, true>(aK, Xs, Rs, w, lane);  // d ktilde_n += g^T r
-    // (fp32 product: as bf16x3 it would push the kernel past its register budget)
-    if (n > 0) mm64<true, true>(aP, Gq, Rs, w, lane);  // dP_n += dr^(n-1)^T r
+    mmx<T, false, true, kS, kS, false, true>(aK, Xs, Rs, w, lane);  // d ktilde_n += g^T r
+    if (n > 0) {  // dP_n += dr^(n-1)^T r: both states bf16 numbers for a bf16 input, one exact product
+      if constexpr (kBf) mm64_bf<true, true, kS, kS, true, true>(aP, Gq, Rs, w, lane);
+      else mm64<true, true>(aP, Gq, Rs, w, lane);
+    }
   }
   }
 
