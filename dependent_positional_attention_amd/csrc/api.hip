@@ -376,7 +376,7 @@ namespace {
 
 // Byte offsets of the backward's buffers in its workspace (chunk already resolved).
 struct bwd_plan {
-  int64_t off[18];
+  int64_t off[19];
   int64_t total;
 };
 
@@ -389,13 +389,14 @@ path_status plan_bwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   // one band of query chunks at a time; the matrix-core kernels keep a bf16 input's pair states in bf16
   const int64_t state_bytes = (dtype == PATH_DTYPE_BF16 && d == 64 && chunk == 64) ? 2 : 4;
   const int64_t pairs = BH * NPB * chunk * d * state_bytes;
-  const int64_t sizes[18] = {mat, mat, dd, cc, rows, BH * M * 4,      // qt kt Pm Sm fl ftot
+  const int64_t zi = state_bytes == 2 ? cc : 0;  // A^{-1} per chunk from the matrix-core forward terms
+  const int64_t sizes[19] = {mat, mat, dd, cc, rows, BH * M * 4,      // qt kt Pm Sm fl ftot
                              pairs, pairs, BH * NPB * 4,              // St Gst Off
                              rows, rows, rows, rows,                  // lse2 Dv drow dcol
                              mat, mat, dd, cc,                        // dqt dkt dPm dSm
-                             mat};                                    // dva
+                             mat, zi};                                // dva Zi
   int64_t o = 0;
-  for (int i = 0; i < 18; ++i) {
+  for (int i = 0; i < 19; ++i) {
     p->off[i] = o;
     o = round_up(o + sizes[i], kAlign);
   }
@@ -443,8 +444,8 @@ path_status path_attn_bwd(const void* q, const void* k, const void* v, const voi
   if (BH > kMaxGridY || M > kMaxGridY) return PATH_ERR_UNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
   auto f = [&](int i) { return reinterpret_cast<float*>(ws + p.off[i]); };
-  const bwd_buffers b{f(0), f(1), f(2), f(3), f(4), f(5), f(6), f(7), f(8),
-                      f(9), f(10), f(11), f(12), f(13), f(14), f(15), f(16), f(17)};
+  const bwd_buffers b{f(0),  f(1),  f(2),  f(3),  f(4),  f(5),  f(6),  f(7),  f(8), f(9),
+                      f(10), f(11), f(12), f(13), f(14), f(15), f(16), f(17), f(18)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == PATH_DTYPE_BF16;
   return from_hip(bwd_run(bf16, d, chunk, q, k, v, w, beta, log_forget, out, lse, dout, dq, dk, dv, dw, dbeta,

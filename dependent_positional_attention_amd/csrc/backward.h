@@ -14,6 +14,7 @@ struct bwd_buffers {
   float *lse2, *Dv, *drow, *dcol;        // per row: log2-unit lse, dO . o, row and column sums of dz
   float *dqt, *dkt, *dPm, *dSm;          // gradients of the per-chunk terms
   float *dva;                            // dv summed over the bands so far (fp32)
+  float *Zi;                             // A^{-1} per chunk (bf16 inputs at d = chunk = 64), else unused
 };
 
 // The chunk-pair kernels take the query chunks in bands of ceil(sqrt(M)) chunks (M chunks per head) and

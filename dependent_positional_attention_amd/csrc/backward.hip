@@ -1509,13 +1509,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
 }
 
 // Gradients of the per-chunk terms back to q, k, w, beta (the same outputs as bwd_prep_kernel<T, 64, 64>).
-// d qtilde, d ktilde, dS and dP are read straight from global memory (fp32 tiles, row stride 64).
+// d qtilde, d ktilde, dS and dP are read straight from global memory (fp32 tiles, row stride 64); so is
+// A^{-1} when the forward-terms kernel stored it (Zi), else it is formed here by back substitution.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ w, const float* __restrict__ beta,
     const float* __restrict__ dqt, const float* __restrict__ dkt, const float* __restrict__ dPm,
-    const float* __restrict__ dSm, int64_t L, int64_t M, T* __restrict__ dq, T* __restrict__ dk,
-    T* __restrict__ dw, float* __restrict__ dbeta) {
+    const float* __restrict__ dSm, const float* __restrict__ Zi, int64_t L, int64_t M, T* __restrict__ dq,
+    T* __restrict__ dk, T* __restrict__ dw, float* __restrict__ dbeta) {
   extern __shared__ float sm[];
   float* S0 = sm;        // W
   float* S1 = S0 + kT;   // Q
@@ -1539,7 +1540,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
   if (tid < 64) dB[tid] = 0.f;
   chunk_setup(q, k, w, beta, bh, c, L, S0, S1, S2, S3, S4, S5, Bs, tid, wv, lane);
   __syncthreads();
-  unit_upper_inverse(S3, S6, tid);
+  if (Zi != nullptr) tile_f32(S6, Zi + ((size_t)bh * M + c) * 64 * 64, tid);
+  else unit_upper_inverse(S3, S6, tid);
   __syncthreads();
   for (int e = tid; e < 64 * 64; e += 256) S3[(e >> 6) * kS + (e & 63)] = S6[(e >> 6) * kS + (e & 63)] * Bs[e & 63];
   __syncthreads();
@@ -2036,7 +2038,7 @@ __global__ __launch_bounds__(256) void bwd_forget_kernel(const float* __restrict
 // kernel with fp32 outputs)
 hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
                              int64_t BH, int64_t L, float qs, float* qt, float* kt, float* Pm, float* Sm, float* fl,
-                             float* ftot, hipStream_t st);
+                             float* ftot, float* Zi, hipStream_t st);
 // vector_path.hip: the forward's per-chunk terms in fp32 (other shapes than d = chunk = 64)
 hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
                    const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
@@ -2065,7 +2067,7 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
     if ((e = lds((const void*)bwd_chunk_grad_mfma_kernel<T>, kLdsChunkMfma)) != hipSuccess) return e;
     if constexpr (std::is_same<T, __bf16>::value) {  // the prefill's prep, fp32 outputs
       if ((e = mfma_prep_f32_run(q, k, w, beta, logf, BH, L, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot,
-                                 st)) != hipSuccess)
+                                 b.Zi, st)) != hipSuccess)
         return e;
     } else {
       if ((e = lds((const void*)bwd_chunk_fwd_mfma_kernel<T>, kLdsChunkFwdMfma)) != hipSuccess) return e;
@@ -2088,9 +2090,9 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
           band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    bwd_chunk_grad_mfma_kernel<T><<<grid, 256, kLdsChunkMfma, st>>>((const T*)q, (const T*)k, (const T*)w, beta,
-                                                                    b.dqt, b.dkt, b.dPm, b.dSm, L, M, (T*)dq,
-                                                                    (T*)dk, (T*)dw, dbeta);
+    bwd_chunk_grad_mfma_kernel<T><<<grid, 256, kLdsChunkMfma, st>>>(
+        (const T*)q, (const T*)k, (const T*)w, beta, b.dqt, b.dkt, b.dPm, b.dSm,
+        std::is_same<T, __bf16>::value ? b.Zi : nullptr, L, M, (T*)dq, (T*)dk, (T*)dw, dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
     e = vec_run(1, std::is_same<T, __bf16>::value, D, C, q, k, v, w, beta, logf, nullptr, nullptr, BH, L, scale, b.qt,

@@ -196,13 +196,15 @@ static_assert(s_row_group(kC) == kSGroups, "packed S size");
 
 // X3: the lo halves of qtilde and P (bf16x3 transport) are formed and stored; without it only hi.
 // F32: qtilde, ktilde and P are stored in fp32 with natural columns instead (the per-chunk terms the
-// backward pass works from; qt, kt and p_hi then point to fp32 arrays of the same shapes).
+// backward pass works from; qt, kt and p_hi then point to fp32 arrays of the same shapes), S as the full
+// C x C square, and, when Zo is given, Z = A^{-1} as well ([chunk][i][j] fp32, unit upper triangular,
+// zeros below the diagonal), which the backward's gradient kernel needs.
 template <bool X3, bool F32 = false>
 __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
     const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, float qs,
     __bf16* __restrict__ qt, __bf16* __restrict__ qt_lo, __bf16* __restrict__ kt, __bf16* __restrict__ p_hi, __bf16* __restrict__ p_lo,
-    float* __restrict__ Sm, float* __restrict__ fl, float* __restrict__ ftot) {
+    float* __restrict__ Sm, float* __restrict__ fl, float* __restrict__ ftot, float* __restrict__ Zo) {
   extern __shared__ __align__(1024) char smem[];
   __bf16* Wt = reinterpret_cast<__bf16*>(smem);  // W [s][x]            (swizzled, natural columns)
   __bf16* Qt = Wt + kTile;                       // Q [a][x]
@@ -372,6 +374,15 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     }
   }
   __syncthreads();
+  if constexpr (F32) {  // Z for the backward: Z[i][j] (i <= j) from Af[j][i]
+    if (Zo != nullptr) {
+      float* zc = Zo + ((size_t)bh * M + c) * kC * kC;
+      for (int e = tid; e < kC * kC; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        zc[e] = i <= j ? Af[j * kLDF + i] : 0.f;
+      }
+    }
+  }
 
   // T^{-T}[t][s] = Z[s][t] beta_t (t >= s), hi/lo, stored with permuted columns: stored slots 8 ch + j
   // of row t hold columns c0 + 16 (j / 4) + j % 4, c0 = 32 (ch / 4) + 4 (ch % 4)
@@ -1490,7 +1501,8 @@ hipError_t mfma_run(int phases, int chunk, int transport, const void* q, const v
       if (err != hipSuccess) return err;
       kernel<<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
           (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, scale * kLog2e, (__bf16*)qt,
-          x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot);
+          x3 ? (__bf16*)qt_lo : nullptr, (__bf16*)kt, (__bf16*)p_hi, x3 ? (__bf16*)p_lo : nullptr, Sm, fl, ftot,
+          nullptr);
       return hipGetLastError();
     };
     e = x3 ? prep(mfma_prep_kernel<true>) : prep(mfma_prep_kernel<false>);
@@ -1559,14 +1571,14 @@ size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M) {
 // scaled by qs, ktilde, P, FoX chunk-local prefixes and chunk totals, all fp32 with natural columns.
 hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
                              int64_t BH, int64_t L, float qs, float* qt, float* kt, float* Pm, float* Sm, float* fl,
-                             float* ftot, hipStream_t st) {
+                             float* ftot, float* Zi, hipStream_t st) {
   const int64_t M = (L + kC - 1) / kC;
   hipError_t e = hipFuncSetAttribute((const void*)mfma_prep_kernel<false, true>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPrepLds);
   if (e != hipSuccess) return e;
   mfma_prep_kernel<false, true><<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
       (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, qs, reinterpret_cast<__bf16*>(qt),
-      nullptr, reinterpret_cast<__bf16*>(kt), reinterpret_cast<__bf16*>(Pm), nullptr, Sm, fl, ftot);
+      nullptr, reinterpret_cast<__bf16*>(kt), reinterpret_cast<__bf16*>(Pm), nullptr, Sm, fl, ftot, Zi);
   return hipGetLastError();
 }
 
