@@ -386,11 +386,13 @@ path_status plan_bwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   if (!vec_supported(d, chunk)) return PATH_ERR_UNSUPPORTED;
   const int64_t BH = B * H, M = (L + chunk - 1) / chunk, Lp = M * chunk, NPB = bwd_band_pairs(M);
   const int64_t rows = BH * Lp * 4, mat = BH * Lp * d * 4, dd = BH * M * d * d * 4, cc = BH * M * chunk * chunk * 4;
-  // one band of query chunks at a time; the matrix-core kernels keep a bf16 input's pair states in bf16
+  // one band of query chunks at a time; the matrix-core kernels keep a bf16 input's pair states, ktilde
+  // and P in bf16
   const int64_t state_bytes = (dtype == PATH_DTYPE_BF16 && d == 64 && chunk == 64) ? 2 : 4;
   const int64_t pairs = BH * NPB * chunk * d * state_bytes;
   const int64_t zi = state_bytes == 2 ? cc : 0;  // A^{-1} per chunk from the matrix-core forward terms
-  const int64_t sizes[19] = {mat, mat, dd, cc, rows, BH * M * 4,      // qt kt Pm Sm fl ftot
+  const int64_t kt = BH * Lp * d * state_bytes, pm = BH * M * d * d * state_bytes;
+  const int64_t sizes[19] = {mat, kt, pm, cc, rows, BH * M * 4,       // qt kt Pm Sm fl ftot
                              pairs, pairs, BH * NPB * 4,              // St Gst Off
                              rows, rows, rows, rows,                  // lse2 Dv drow dcol
                              mat, mat, dd, cc,                        // dqt dkt dPm dSm

@@ -591,9 +591,10 @@ __device__ __forceinline__ void put_tile(float* dst, const f32x4 (&reg)[4], int 
   }
 }
 
-// The pair states r^(n) and dr^(n-1) of the matrix-core chunk-pair kernels are stored in bf16 for a bf16
-// input (the forward rounds its running queries to bf16 in the same way; the chains themselves run in
-// fp32 registers) and in fp32 for an fp32 input.  Tiles are row-major with row stride 64.
+// The pair states r^(n) and dr^(n-1) of the matrix-core chunk-pair kernels, and the forward terms
+// ktilde and P they read, are bf16 for a bf16 input (the forward's bf16 transport rounds its running
+// queries, ktilde and P to bf16 in the same way; the chains themselves run in fp32 registers) and fp32
+// for an fp32 input.  Tiles are row-major with row stride 64.
 template <typename T>
 using state_t = typename std::conditional<std::is_same<T, __bf16>::value, __bf16, float>::type;
 template <typename S>
@@ -744,13 +745,6 @@ __device__ __forceinline__ void split_rows(bf16x8 (&h)[2], bf16x8 (&l)[2], const
     split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), h[ks], l[ks]);
   }
 }
-// the same fragments from fp32 values in registers, v[8 ks + i] = A(16w + r, 32 ks + 8g + i)
-__device__ __forceinline__ void split_regs(bf16x8 (&h)[2], bf16x8 (&l)[2], const float (&v)[16]) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    split8(f32x4{v[8 * ks], v[8 * ks + 1], v[8 * ks + 2], v[8 * ks + 3]},
-           f32x4{v[8 * ks + 4], v[8 * ks + 5], v[8 * ks + 6], v[8 * ks + 7]}, h[ks], l[ks]);
-}
 // the same values from a bf16 state tile (row stride 64), widened
 __device__ __forceinline__ void rows_bf16(float (&v)[16], const __bf16* __restrict__ A, int w, int lane) {
   const int r = lane & 15, g = lane >> 4;
@@ -761,65 +755,30 @@ __device__ __forceinline__ void rows_bf16(float (&v)[16], const __bf16* __restri
     for (int i = 0; i < 8; ++i) v[8 * ks + i] = (float)x[i];
   }
 }
-// acc[cb] += sum_k A(16w + r', k) B[16cb + r''][k]: A as split fragments, B an fp32 LDS tile (stride kS)
-// split while it is read
-__device__ __forceinline__ void mm64_x3(f32x4 (&acc)[4], const bf16x8 (&ah)[2], const bf16x8 (&al)[2],
-                                        const float* __restrict__ B, int lane) {
+
+
+// acc[cb] += sum_k A(16w + r', k) B[k][16cb + r''] on the bf16 matrix cores: A as bf16 fragments, B an fp32
+// LDS tile (stride kS) holding bf16 numbers, read by columns and converted exactly
+__device__ __forceinline__ void mm64_bf16_cols(f32x4 (&acc)[4], const bf16x8 (&a)[2], const float* __restrict__ B,
+                                               int lane) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const float* p = B + (16 * cb + r) * kS + 32 * ks + 8 * g;
-      bf16x8 bh, bl;
-      split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), bh, bl);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh, acc[cb], 0, 0, 0);
+      bf16x8 b;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = (__bf16)B[(32 * ks + 8 * g + i) * kS + 16 * cb + r];
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc[cb], 0, 0, 0);
     }
 }
-
-// acc[cb] += sum_k A(16w + r', k) B[16cb + r''][k] for A holding bf16 numbers (fragments converted
-// exactly from fp32 values in registers, v as in split_regs), B an fp32 LDS tile split while it is read:
-// two products instead of three (A has no lo part)
-__device__ __forceinline__ void mm64_x2(f32x4 (&acc)[4], const float (&v)[16], const float* __restrict__ B,
-                                        int lane) {
+// bf16 fragments, a[ks] = A(16w + r, 32 ks + 8g .. +7), of a bf16 tile in global memory (row stride 64)
+__device__ __forceinline__ void frag_tile_bf16(bf16x8 (&a)[2], const __bf16* __restrict__ A, int w, int lane) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 a;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (__bf16)v[8 * ks + i];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const float* p = B + (16 * cb + r) * kS + 32 * ks + 8 * g;
-      bf16x8 bh, bl;
-      split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), bh, bl);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[cb], 0, 0, 0);
-    }
-  }
+  for (int ks = 0; ks < 2; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(A + (16 * w + r) * 64 + 32 * ks + 8 * g);
 }
 
-// acc[cb] += sum_k A(16w + r', k) B[k][16cb + r'']: A as split fragments, B an fp32 LDS tile (stride kS) read
-// by columns and split while it is read
-__device__ __forceinline__ void mm64_x3_cols(f32x4 (&acc)[4], const bf16x8 (&ah)[2], const bf16x8 (&al)[2],
-                                             const float* __restrict__ B, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = B[(32 * ks + 8 * g + i) * kS + 16 * cb + r];
-      bf16x8 bh, bl;
-      split8(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}, bh, bl);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bh, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bl, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bh, acc[cb], 0, 0, 0);
-    }
-}
 
 // mm64 on the bf16 matrix cores (bf16 inputs): acc[cb] += sum_k A(16w + r', k) B(k, 16cb + r''), operands as
 // in mm64 (AT, BK, row strides SA, SB; LDS tiles or global fp32 tiles).  An operand flagged exact (EA, EB:
@@ -880,8 +839,8 @@ __device__ __forceinline__ void mmx(f32x4 (&acc)[4], const float* A, const float
 // (plain functions rather than capturing lambdas, so that the arrays stay in registers).
 template <typename T>
 __device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4], f32x4 (&pP)[4], float (&pra)[16],
-                                                 float& pF, float& poff, const float* __restrict__ kt,
-                                                 const T* __restrict__ vb, const float* __restrict__ Pm,
+                                                 float& pF, float& poff, const state_t<T>* __restrict__ kt,
+                                                 const T* __restrict__ vb, const state_t<T>* __restrict__ Pm,
                                                  const state_t<T>* __restrict__ St, const float* __restrict__ fl,
                                                  const float* __restrict__ Off, const pair_band& band, int64_t bh,
                                                  int64_t m, int64_t n, int64_t M, int64_t L, int tid, int w,
@@ -889,9 +848,9 @@ __device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4
   constexpr int C = 64, CD = 64 * 64;
   const int64_t Lp = M * C;
   const size_t pr = band.slot(bh, m, n);
-  fetch_tile(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
+  fetch_state(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
   fetch_rows(pV, vb, n * C, L, tid);
-  fetch_tile(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
+  fetch_state(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
   if constexpr (std::is_same<T, __bf16>::value) rows_bf16(pra, St + pr * CD, w, lane);  // for the bf16 logits
   else frag_f32(pra, St + pr * CD, w, lane);
   if (fl != nullptr) {
@@ -944,7 +903,7 @@ constexpr size_t kLdsPairMfma = sizeof(float) * (4 * 64 * kS + 3 * 64);
 // Query-chunk kernel on the matrix cores (same outputs as bwd_query_kernel<T, 64, 64>).
 template <typename T>
 __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
-    const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
+    const float* __restrict__ qt, const state_t<T>* __restrict__ kt, const state_t<T>* __restrict__ Pm,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
     int64_t L, int64_t M, float scale, pair_band band, state_t<T>* __restrict__ St, state_t<T>* __restrict__ Gst,
@@ -1001,7 +960,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   // (fetched unconditionally, at a clamped index: a conditionally written register array would be
   // kept in scratch memory)
   f32x4 pP[4];
-  fetch_tile(pP, Pm + ((size_t)bh * M + (m > 0 ? m - 1 : 0)) * CD, tid);
+  fetch_state(pP, Pm + ((size_t)bh * M + (m > 0 ? m - 1 : 0)) * CD, tid);
   float off = 0.f;
   for (int64_t n = m - 1; n >= 0; --n) {
     const size_t pr = band.slot(bh, m, n);
@@ -1013,12 +972,13 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
       __syncthreads();  // every wave is done with the previous P
       put_tile(Ps, pP, tid);
       __syncthreads();
-      fetch_tile(pP, Pm + ((size_t)bh * M + (n > 1 ? n - 1 : 0)) * CD, tid);
+      fetch_state(pP, Pm + ((size_t)bh * M + (n > 1 ? n - 1 : 0)) * CD, tid);
       zero4(R);
       if constexpr (kBf) {  // r P_n^T
         bf16x8 ah[2], al[2];
         split_rows<kS>(ah, al, Xs, w, lane);
-        mm64_x3(R, ah, al, Ps, lane);
+        mm64_bf16(R, ah, Ps, lane);  // P_n holds bf16 numbers
+        mm64_bf16(R, al, Ps, lane);
       } else {
         mm64<false, false>(R, Xs, Ps, w, lane);
       }
@@ -1085,7 +1045,8 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
       if constexpr (kBf) {
         bf16x8 ah[2], al[2];
         split_rows<kS>(ah, al, Xs, w, lane);
-        mm64_x3_cols(G, ah, al, Ps, lane);
+        mm64_bf16_cols(G, ah, Ps, lane);
+        mm64_bf16_cols(G, al, Ps, lane);
       } else {
         mm64<false, true>(G, Xs, Ps, w, lane);
       }
@@ -1093,7 +1054,10 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     zero4(Z);
     zero4(DP);
     if constexpr (kBf) {
-      mm64_x2(Z, ra, Ks, lane);  // r^(n) is stored in bf16
+      bf16x8 a[2];  // r^(n) and ktilde_n are bf16 numbers: one product
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a[i >> 3][i & 7] = (__bf16)ra[i];
+      mm64_bf16(Z, a, Ks, lane);
     } else {
       mm64_ra<false>(Z, ra, Ks, lane);
     }
@@ -1112,7 +1076,8 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     if constexpr (kBf) {  // + g ktilde_n
       bf16x8 ah[2], al[2];
       split_rows<kS>(ah, al, Xs, w, lane);
-      mm64_x3_cols(G, ah, al, Ks, lane);
+      mm64_bf16_cols(G, ah, Ks, lane);
+      mm64_bf16_cols(G, al, Ks, lane);
     } else {
       mm64<false, true>(G, Xs, Ks, w, lane);
     }
@@ -1137,7 +1102,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
 // the products that reduce over the queries.
 template <typename T>
 __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
-    const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
+    const state_t<T>* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
     const T* __restrict__ v, const T* __restrict__ dout, const state_t<T>* __restrict__ St,
     const state_t<T>* __restrict__ Gst,
     const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
@@ -1168,8 +1133,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   // fragments for a bf16 input)
   constexpr bool kBf = std::is_same<T, __bf16>::value;
   float ka[16], va[16];
-  bf16x8 vb16[2], kah[2], kal[2];
-  if constexpr (kBf) split_rows<64>(kah, kal, kt + rown * 64, w, lane);
+  bf16x8 vb16[2], kah[2];
+  if constexpr (kBf) frag_tile_bf16(kah, kt + rown * 64, w, lane);
   else frag_f32(ka, kt + rown * 64, w, lane);
   if constexpr (kBf) frag_bf16(vb16, reinterpret_cast<const __bf16*>(vb), n * C, L, w, lane);
   else frag_rows(va, vb, n * C, L, w, lane);
@@ -1243,8 +1208,7 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     zero4(ZT);
     zero4(DT);
     if constexpr (kBf) {  // (r ktilde^T)^T; r^(n) is stored in bf16
-      mm64_bf16(ZT, kah, Rs, lane);
-      mm64_bf16(ZT, kal, Rs, lane);
+      mm64_bf16(ZT, kah, Rs, lane);  // ktilde_n is bf16 too: one product
     } else {
       mm64_ra<false>(ZT, ka, Rs, lane);
     }
@@ -2037,7 +2001,7 @@ __global__ __launch_bounds__(256) void bwd_forget_kernel(const float* __restrict
 // mfma_path.hip: the forward's per-chunk terms in fp32 from bf16 inputs at d = chunk = 64 (the prefill's prep
 // kernel with fp32 outputs)
 hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
-                             int64_t BH, int64_t L, float qs, float* qt, float* kt, float* Pm, float* Sm, float* fl,
+                             int64_t BH, int64_t L, float qs, float* qt, void* kt, void* Pm, float* Sm, float* fl,
                              float* ftot, float* Zi, hipStream_t st);
 // vector_path.hip: the forward's per-chunk terms in fp32 (other shapes than d = chunk = 64)
 hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
@@ -2080,12 +2044,12 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
     for (int64_t mb = 0; mb < M; mb += G) {
       const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
       bwd_query_mfma_kernel<T><<<dim3((unsigned)(xh * (band.me - band.mb))), 256, kLdsPairMfma, st>>>(
-          b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
+          b.qt, reinterpret_cast<const state_t<T>*>(b.kt), reinterpret_cast<const state_t<T>*>(b.Pm), b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
           M, scale, band, reinterpret_cast<state_t<T>*>(b.St), reinterpret_cast<state_t<T>*>(b.Gst), b.Off, b.lse2,
           b.Dv, b.drow, b.dqt, b.dSm, BH);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       bwd_key_mfma_kernel<T><<<dim3((unsigned)(xh * band.me)), 256, kLdsPairMfma, st>>>(
-          b.kt, b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, reinterpret_cast<const state_t<T>*>(b.St),
+          reinterpret_cast<const state_t<T>*>(b.kt), b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, reinterpret_cast<const state_t<T>*>(b.St),
           reinterpret_cast<const state_t<T>*>(b.Gst), b.Off, b.lse2, b.Dv, L, M,
           band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
       if ((e = hipGetLastError()) != hipSuccess) return e;

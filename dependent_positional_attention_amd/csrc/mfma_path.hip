@@ -195,10 +195,10 @@ __host__ __device__ constexpr int s_row_group(int a) { return a + 2 * (a >> 2) *
 static_assert(s_row_group(kC) == kSGroups, "packed S size");
 
 // X3: the lo halves of qtilde and P (bf16x3 transport) are formed and stored; without it only hi.
-// F32: qtilde, ktilde and P are stored in fp32 with natural columns instead (the per-chunk terms the
-// backward pass works from; qt, kt and p_hi then point to fp32 arrays of the same shapes), S as the full
-// C x C square, and, when Zo is given, Z = A^{-1} as well ([chunk][i][j] fp32, unit upper triangular,
-// zeros below the diagonal), which the backward's gradient kernel needs.
+// F32: the per-chunk terms the backward pass works from: qtilde in fp32 (qt then points to an fp32
+// array of the same shape), ktilde and P in bf16 with natural columns, S as the full C x C square, and,
+// when Zo is given, Z = A^{-1} as well ([chunk][i][j] fp32, unit upper triangular, zeros below the
+// diagonal), which the backward's gradient kernel needs.
 template <bool X3, bool F32 = false>
 __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
@@ -498,11 +498,7 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
       const bf16x4 k4 = k4s[xt];
       const float u0 = (float)k4[0] - dk[0], u1 = (float)k4[1] - dk[1], u2 = (float)k4[2] - dk[2],
                   u3 = (float)k4[3] - dk[3];
-      if constexpr (F32)
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(kt) + (chunk_rows + a) * kD + x0) =
-            make_float4(u0, u1, u2, u3);
-      else
-        *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) = pack4(u0, u1, u2, u3);
+      *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + (F32 ? x0 : pos)) = pack4(u0, u1, u2, u3);
     }
     // P[x][y] = delta - D[y][x]  (lane: row x = 16 xt + r, columns y = 16 wave + 4g .. +3)
     {
@@ -511,8 +507,7 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
                   e2 = (y0 + 2 == xr ? 1.f : 0.f) - dp[2], e3 = (y0 + 3 == xr ? 1.f : 0.f) - dp[3];
       const int py = perm_pos(y0);
       if constexpr (F32) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p_hi) + chunk_mat + (size_t)xr * kD + y0) =
-            make_float4(e0, e1, e2, e3);
+        *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + y0) = pack4(e0, e1, e2, e3);
       } else if constexpr (X3) {
         bf16x4 ph, pl;
         split4(e0, e1, e2, e3, ph, pl);
@@ -1570,7 +1565,7 @@ size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M) {
 // The prep in fp32 output form for the backward pass (bf16 inputs, d = chunk = 64): qtilde and S
 // scaled by qs, ktilde, P, FoX chunk-local prefixes and chunk totals, all fp32 with natural columns.
 hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
-                             int64_t BH, int64_t L, float qs, float* qt, float* kt, float* Pm, float* Sm, float* fl,
+                             int64_t BH, int64_t L, float qs, float* qt, void* kt, void* Pm, float* Sm, float* fl,
                              float* ftot, float* Zi, hipStream_t st) {
   const int64_t M = (L + kC - 1) / kC;
   hipError_t e = hipFuncSetAttribute((const void*)mfma_prep_kernel<false, true>,

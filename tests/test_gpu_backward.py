@@ -123,6 +123,14 @@ def test_full_size_backward_sampled_heads_equal_single_head_runs():
             assert torch.isfinite(g1.float()).all()
 
 
+def test_bf16_backward_long_chain():
+    """A 32-chunk chain (L = 2048, one head, PaTH-FoX, beta spread over (0, 2)) against the oracle: the
+    states and their gradients pass through up to 31 chunk transitions, which bounds how the bf16
+    rounding of the per-pair states accumulates along the chain."""
+    x = synth.make_fwd_inputs(1, 1, 2048, 64, recipe="fox", dtype="bf16", seed=41)
+    check(x, 64, "bf16 L=2048", seed=42)
+
+
 @pytest.mark.parametrize("L", [1, 40, 64, 65, 129])
 def test_bf16_backward_short_and_ragged(L):
     """The matrix-core backward (d = chunk = 64) at its edges: one partial chunk (no chunk pairs at all),
