@@ -81,7 +81,7 @@ def kernel_digest(*sources):
     """Digest of kernel sources (ties HBM counter readings to the code they measured)."""
     import hashlib
     h = hashlib.sha256()
-    for f in sources + ("common.h",):
+    for f in sources + ("common.h", "tiles.h"):
         with open(os.path.join(ROOT, "dependent_positional_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

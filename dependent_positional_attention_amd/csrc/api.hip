@@ -391,8 +391,10 @@ path_status plan_bwd(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtyp
   const int64_t state_bytes = (dtype == PATH_DTYPE_BF16 && d == 64 && chunk == 64) ? 2 : 4;
   const int64_t pairs = BH * NPB * chunk * d * state_bytes;
   const int64_t zi = state_bytes == 2 ? cc : 0;  // A^{-1} per chunk from the matrix-core forward terms
-  const int64_t kt = BH * Lp * d * state_bytes, pm = BH * M * d * d * state_bytes;
-  const int64_t sizes[19] = {mat, kt, pm, cc, rows, BH * M * 4,       // qt kt Pm Sm fl ftot
+  // (for those the forward terms are the prefill's own: qtilde too in bf16, the in-chunk logits packed)
+  const int64_t qt = BH * Lp * d * state_bytes, kt = qt, pm = BH * M * d * d * state_bytes;
+  const int64_t sm = state_bytes == 2 ? BH * M * (int64_t)mfma_s_chunk_bytes() : cc;
+  const int64_t sizes[19] = {qt, kt, pm, sm, rows, BH * M * 4,        // qt kt Pm Sm fl ftot
                              pairs, pairs, BH * NPB * 4,              // St Gst Off
                              rows, rows, rows, rows,                  // lse2 Dv drow dcol
                              mat, mat, dd, cc,                        // dqt dkt dPm dSm

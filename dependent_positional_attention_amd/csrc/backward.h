@@ -37,6 +37,40 @@ inline int64_t bwd_band_pairs(int64_t M) {
   return most;
 }
 
+__host__ __device__ inline int64_t pair_index(int64_t m, int64_t n) { return m * (m - 1) / 2 + n; }
+
+// The chunk-pair kernels run one band of query chunks [mb, me) at a time (bands ascending, about
+// sqrt(M) chunks each), so that only that band's pair states are held: the states of pair (m, n < m)
+// sit in per-head slabs of `stride` pairs, in pair_index order from (mb, 0).  The key-side sums over
+// query chunks carry over from band to band in the workspace (fixed order: deterministic).
+struct pair_band {
+  int64_t mb, me, stride;
+  __host__ __device__ size_t slot(int64_t bh, int64_t m, int64_t n) const {
+    return (size_t)bh * stride + (size_t)(pair_index(m, n) - pair_index(mb, 0));
+  }
+};
+
+// Block -> (batch*head, chunk) of the two chunk-pair kernels (1-D grid of kBwdXcd * ceil(BH / kBwdXcd) * M
+// blocks): workgroup b runs on XCD b % 8, each with its own L2, so every block of one (batch, head),
+// which all read that head's ktilde, v and P tiles, lands on the same XCD; heads are dealt round-robin
+// to XCDs and within an XCD the q-th block of every head goes before the (q+1)-th.  Returns false for
+// the surplus blocks of XCDs with fewer heads.
+constexpr int kBwdXcd = 8;
+__device__ __forceinline__ bool bwd_pair_block(int64_t BH, int64_t M, int64_t& bh, int64_t& q) {
+  const int64_t xcd = blockIdx.x % kBwdXcd, slot = blockIdx.x / kBwdXcd;
+  const int64_t heads_here = (BH - xcd + kBwdXcd - 1) / kBwdXcd;
+  if (slot >= heads_here * M) return false;
+  bh = xcd + kBwdXcd * (slot % heads_here);
+  q = slot / heads_here;
+  return true;
+}
+
+// backward_tiles.hip: one band of the chunk-pair kernels for bf16 inputs at d = chunk = 64 (the prefill's
+// bf16 per-chunk terms in qt, kt, Pm, Sm; bf16 pair states in St, Gst).
+hipError_t bwd_pair_tiles_run(bool fox, const void* v, const void* out, const void* dout, const float* lse,
+                              int64_t BH, int64_t L, float scale, pair_band band, const bwd_buffers& b, void* dv,
+                              hipStream_t st);
+
 hipError_t bwd_run(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
                    const float* beta, const float* logf, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, void* dw, float* dbeta, float* dlogf, int64_t BH, int64_t L,

@@ -56,18 +56,6 @@ struct BwdShape {
   static constexpr size_t lds_prep = sizeof(float) * (9 * SL + 2 * C);
 };
 
-__host__ __device__ inline int64_t pair_index(int64_t m, int64_t n) { return m * (m - 1) / 2 + n; }
-
-// The chunk-pair kernels run one band of query chunks [mb, me) at a time (bands ascending, about
-// sqrt(M) chunks each), so that only that band's pair states are held: the states of pair (m, n < m)
-// sit in per-head slabs of `stride` pairs, in pair_index order from (mb, 0).  The key-side sums over
-// query chunks carry over from band to band in the workspace (fixed order: deterministic).
-struct pair_band {
-  int64_t mb, me, stride;
-  __host__ __device__ size_t slot(int64_t bh, int64_t m, int64_t n) const {
-    return (size_t)bh * stride + (size_t)(pair_index(m, n) - pair_index(mb, 0));
-  }
-};
 
 }  // namespace
 
@@ -877,20 +865,6 @@ __device__ __forceinline__ void fetch_key_pair(f32x4 (&pR)[4], f32x4 (&pG)[4], r
   if (fox) poff = Off[pr];
 }
 
-// Block -> (batch*head, chunk) of the two chunk-pair kernels (1-D grid of kBwdXcd * ceil(BH / kBwdXcd) * M
-// blocks): workgroup b runs on XCD b % 8, each with its own L2, so every block of one (batch, head),
-// which all read that head's ktilde, v and P tiles, lands on the same XCD; heads are dealt round-robin
-// to XCDs and within an XCD the q-th block of every head goes before the (q+1)-th.  Returns false for
-// the surplus blocks of XCDs with fewer heads.
-constexpr int kBwdXcd = 8;
-__device__ __forceinline__ bool bwd_pair_block(int64_t BH, int64_t M, int64_t& bh, int64_t& q) {
-  const int64_t xcd = blockIdx.x % kBwdXcd, slot = blockIdx.x / kBwdXcd;
-  const int64_t heads_here = (BH - xcd + kBwdXcd - 1) / kBwdXcd;
-  if (slot >= heads_here * M) return false;
-  bh = xcd + kBwdXcd * (slot % heads_here);
-  q = slot / heads_here;
-  return true;
-}
 
 // Both chunk-pair kernels keep four 64 x 64 LDS tiles (about 70 KB, so two blocks share a CU): three
 // tiles that every wave reads whole, and one whose rows 16w .. 16w+15 only wave w writes and reads
@@ -2003,6 +1977,9 @@ __global__ __launch_bounds__(256) void bwd_forget_kernel(const float* __restrict
 hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
                              int64_t BH, int64_t L, float qs, float* qt, void* kt, void* Pm, float* Sm, float* fl,
                              float* ftot, float* Zi, hipStream_t st);
+hipError_t mfma_prep_bwd_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
+                             int64_t BH, int64_t L, float qs, void* qt, void* kt, void* Pm, float* Sm, float* fl,
+                             float* ftot, float* Zi, hipStream_t st);
 // vector_path.hip: the forward's per-chunk terms in fp32 (other shapes than d = chunk = 64)
 hipError_t vec_run(int phases, bool bf16, int d, int chunk, const void* q, const void* k, const void* v,
                    const void* w, const float* beta, const float* logf, void* out, float* lse, int64_t BH, int64_t L,
@@ -2026,33 +2003,37 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   };
   const int64_t G = bwd_band_chunks(M), NPB = bwd_band_pairs(M);
   if constexpr (D == 64 && C == 64) {  // the matrix cores: bf16 products for bf16 inputs, fp32 ones for fp32
-    if ((e = lds((const void*)bwd_query_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
-    if ((e = lds((const void*)bwd_key_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
     if ((e = lds((const void*)bwd_chunk_grad_mfma_kernel<T>, kLdsChunkMfma)) != hipSuccess) return e;
-    if constexpr (std::is_same<T, __bf16>::value) {  // the prefill's prep, fp32 outputs
-      if ((e = mfma_prep_f32_run(q, k, w, beta, logf, BH, L, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot,
+    if constexpr (std::is_same<T, __bf16>::value) {  // the prefill's own per-chunk terms, and the tile kernels
+      if ((e = mfma_prep_bwd_run(q, k, w, beta, logf, BH, L, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot,
                                  b.Zi, st)) != hipSuccess)
         return e;
+      for (int64_t mb = 0; mb < M; mb += G) {
+        const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
+        if ((e = bwd_pair_tiles_run(fox, v, out, dout, lse, BH, L, scale, band, b, dv, st)) != hipSuccess) return e;
+      }
     } else {
       if ((e = lds((const void*)bwd_chunk_fwd_mfma_kernel<T>, kLdsChunkFwdMfma)) != hipSuccess) return e;
       bwd_chunk_fwd_mfma_kernel<T><<<grid, 256, kLdsChunkFwdMfma, st>>>(
           (const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl,
           b.ftot);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    const int64_t xh = kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd);
-    for (int64_t mb = 0; mb < M; mb += G) {
-      const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
-      bwd_query_mfma_kernel<T><<<dim3((unsigned)(xh * (band.me - band.mb))), 256, kLdsPairMfma, st>>>(
-          b.qt, reinterpret_cast<const state_t<T>*>(b.kt), reinterpret_cast<const state_t<T>*>(b.Pm), b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
-          M, scale, band, reinterpret_cast<state_t<T>*>(b.St), reinterpret_cast<state_t<T>*>(b.Gst), b.Off, b.lse2,
-          b.Dv, b.drow, b.dqt, b.dSm, BH);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      bwd_key_mfma_kernel<T><<<dim3((unsigned)(xh * band.me)), 256, kLdsPairMfma, st>>>(
-          reinterpret_cast<const state_t<T>*>(b.kt), b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, reinterpret_cast<const state_t<T>*>(b.St),
-          reinterpret_cast<const state_t<T>*>(b.Gst), b.Off, b.lse2, b.Dv, L, M,
-          band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = lds((const void*)bwd_query_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
+      if ((e = lds((const void*)bwd_key_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
+      const int64_t xh = kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd);
+      for (int64_t mb = 0; mb < M; mb += G) {
+        const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
+        bwd_query_mfma_kernel<T><<<dim3((unsigned)(xh * (band.me - band.mb))), 256, kLdsPairMfma, st>>>(
+            b.qt, reinterpret_cast<const state_t<T>*>(b.kt), reinterpret_cast<const state_t<T>*>(b.Pm), b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
+            M, scale, band, reinterpret_cast<state_t<T>*>(b.St), reinterpret_cast<state_t<T>*>(b.Gst), b.Off, b.lse2,
+            b.Dv, b.drow, b.dqt, b.dSm, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        bwd_key_mfma_kernel<T><<<dim3((unsigned)(xh * band.me)), 256, kLdsPairMfma, st>>>(
+            reinterpret_cast<const state_t<T>*>(b.kt), b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, reinterpret_cast<const state_t<T>*>(b.St),
+            reinterpret_cast<const state_t<T>*>(b.Gst), b.Off, b.lse2, b.Dv, L, M,
+            band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
     bwd_chunk_grad_mfma_kernel<T><<<grid, 256, kLdsChunkMfma, st>>>(
         (const T*)q, (const T*)k, (const T*)w, beta, b.dqt, b.dkt, b.dPm, b.dSm,

@@ -1,0 +1,539 @@
+// PaTH / PaTH-FoX backward, chunk-pair kernels for bf16 inputs at d = chunk = 64, in the operand
+// conventions of the matrix-core prefill (tiles.h).  The recurrences are those of backward.hip
+// (PaTH summary, gist.science/ko/paper/2505.16381, section 3, differentiated):
+//   forward per query chunk m:  r^(m-1) = qtilde_m,  z_mn = r^(n) ktilde_n^T,  r^(n-1) = r^(n) P_n^T
+//   backward:                   dr^(n) = g_mn ktilde_n + dr^(n-1) P_n   (n = 0 .. m-1, g = ln2 dz)
+//                               dP_n = sum_m dr^(n-1)_m^T r^(n)_m,  dktilde_n = sum_m g_mn^T r^(n)_m,
+//                               dv_n = sum_m p_mn^T dO_m
+// The forward's own per-chunk terms are used (qtilde, ktilde and P in bf16 with permuted columns, the
+// packed in-chunk logits), and the running states are rounded to bf16 after every transition exactly
+// as the forward's bf16 transport rounds its running queries, so the recomputed logits are the
+// forward's.  Chains are held transposed (d x queries, as accumulator tiles), so an accumulator turns
+// into an MFMA operand in registers (acc_to_op); a state's operand form is also a row of a tile with
+// permuted columns, so the pair states r^(n) and dr^(n-1) are stored as such tiles with one 16-byte
+// store per lane and k-step, and the key-side kernel reads them back as row fragments (tile_frag) and
+// as column fragments (LDS transpose reads, tr_frag).  ktilde, V and P stream through a ring of three
+// LDS slots filled by direct global->LDS copies, as in the prefill's scan.
+#include "backward.h"
+#include "tiles.h"
+
+namespace pathattn {
+
+namespace {
+
+constexpr int kRingSlots = 3;
+constexpr int kPairTiles = 3;  // tiles per ring slot
+
+// Copies of one ring slot per wave: three tiles (2 instructions each) and `extra` 4-byte row loads.
+template <int EXTRA>
+constexpr int slot_ops() { return kPairTiles * 2 + EXTRA; }
+
+// 16 lanes of every wave copy 16 floats of a 64-float row into LDS (lane l < 16 of wave w writes
+// dst[16 w + l]).
+__device__ __forceinline__ void row_to_lds(float* dst, const float* src, int wave, int l) {
+  if (l < 16)
+    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * wave + l), (lds_void*)(dst + 16 * wave), 4, 0, 0);
+}
+
+}  // namespace
+
+// Query-chunk kernel: one block of 4 waves per (query chunk m of the band, batch*head); wave w owns the
+// queries a = 16w .. 16w+15 of the chunk (lane (r, g) query 16w + r).  Writes the states r^(n) and the
+// incoming gradients dr^(n-1) of every pair (m, n < m) (bf16 tiles [query][d], columns permuted), the
+// FoX offsets of each pair, the row statistics (lse2, D), the in-chunk logit gradient dS (unscaled
+// units, fp32 square), d qtilde (unscaled, fp32) and the row sums of dz.
+template <bool FOX>
+__global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
+    const __bf16* __restrict__ qt, const __bf16* __restrict__ kt, const __bf16* __restrict__ Pm,
+    const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
+    const __bf16* __restrict__ v, const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
+    const float* __restrict__ lse, int64_t L, int64_t M, float scale, pair_band band, __bf16* __restrict__ St,
+    __bf16* __restrict__ Gst, float* __restrict__ Off, float* __restrict__ lse2w, float* __restrict__ Dw,
+    float* __restrict__ drow, float* __restrict__ dqt, float* __restrict__ dSm, int64_t BH) {
+  constexpr int OPS = slot_ops<FOX ? 1 : 0>();
+  __shared__ __align__(1024) __bf16 tl[kRingSlots][kPairTiles][kTile];  // ktilde_n, V_n, P_n
+  __shared__ __align__(16) float tf[kRingSlots][64];                     // FoX chunk-local prefix of chunk n
+
+  int64_t bh, q;
+  if (!bwd_pair_block(BH, band.me - band.mb, bh, q)) return;  // whole block
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, r = l & 15, g = l >> 4;
+  const int64_t m = band.me - 1 - q;  // longest of the band first
+  const int64_t Lp = M * 64;
+  const size_t row0 = (size_t)bh * Lp + (size_t)m * 64;
+  const int a = 16 * wave + r;   // this lane's query within chunk m
+  const int64_t ia = m * 64 + a;
+  const bool qvalid = ia < L;
+  const int i0 = 2 * wave;       // this wave's share of every tile copy (rows 16 wave .. +15)
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  // dO_a (natural columns) as the B-operand of V dO^T; D_a = dO_a . o_a; the row statistics
+  bf16x8 dob[2];
+  float Da, l2a;
+  {
+    const size_t ro = ((size_t)bh * L + (size_t)(qvalid ? ia : L - 1)) * 64;
+    float ds = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(dout + ro + 32 * ks + 8 * g);
+      const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + ro + 32 * ks + 8 * g);
+      dob[ks] = qvalid ? x : bf16x8{};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ds = __builtin_fmaf((float)dob[ks][j], (float)o[j], ds);
+    }
+    Da = colsum4(ds);  // over the four lanes of query a
+    const float Fa = FOX ? fl[row0 + a] : 0.f;
+    const float lv = lse[bh * L + (qvalid ? ia : L - 1)];
+    l2a = qvalid ? kLog2e * (lv - Fa) : INFINITY;  // padded query: p = 0
+    if (g == 0) {
+      lse2w[row0 + a] = l2a;
+      Dw[row0 + a] = Da;
+    }
+  }
+
+  // ---------------------------------------------------------------- pass 1: the states r^(n)
+  // r^(n) of this wave's queries as the operand rb (query a, d in the permuted key order), stored per
+  // pair and moved across P_n (n >= 1), rounded to bf16 after every transition.  P_n fragments come
+  // straight from global memory into registers, one step ahead.
+  bf16x8 rb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) rb[ks] = *reinterpret_cast<const bf16x8*>(qt + (row0 + a) * 64 + 32 * ks + 8 * g);
+  {
+    bf16x8 pf[4][2];  // P_n rows 16 dt + r, stored columns 32 ks + 8g .. +7
+    auto fetch_p = [&](int64_t n) PA_INLINE {
+      const __bf16* pn = Pm + ((size_t)bh * M + (size_t)(n > 0 ? n : 0)) * 4096;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pf[dt][ks] = *reinterpret_cast<const bf16x8*>(pn + (16 * dt + r) * 64 + 32 * ks + 8 * g);
+    };
+    fetch_p(m - 1);
+    float off = 0.f;
+    for (int64_t n = m - 1; n >= 0; --n) {
+      const size_t pr = band.slot(bh, m, n);
+      if constexpr (FOX) off += ftot[bh * M + n];
+      if (l == 0) Off[pr] = off;  // every wave writes the same value
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        *reinterpret_cast<bf16x8*>(St + pr * 4096 + a * 64 + 32 * ks + 8 * g) = rb[ks];
+      if (n == 0) break;
+      f32x4 rt[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        rt[dt] = zero;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) rt[dt] = mfma16(pf[dt][ks], rb[ks], rt[dt]);
+      }
+      fetch_p(n - 1);  // (P_0 when n = 1: fetched, not used)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rb[ks][j] = (__bf16)rt[2 * ks + (j >> 2)][j & 3];
+    }
+  }
+
+  // ---------------------------------------------------------------- key chunks through the LDS ring
+  // stream position j: 0 = the own chunk m (in-chunk block), then n = j - 1 = 0 .. m-1
+  auto chunk_at = [&](int64_t j) PA_INLINE -> int64_t { return j == 0 ? m : j - 1; };
+  auto stage = [&](int64_t j, int s) PA_INLINE {
+    const int64_t n = chunk_at(j);
+    const int64_t vr = L - n * 64;
+    dma_tile<2>(tl[s][0], kt + ((size_t)bh * Lp + (size_t)n * 64) * 64, 64, i0);
+    dma_tile<2>(tl[s][1], v + ((size_t)bh * L + (size_t)n * 64) * 64, vr < 64 ? (int)vr : 64, i0);
+    dma_tile<2>(tl[s][2], Pm + ((size_t)bh * M + (size_t)n) * 4096, 64, i0);
+    if constexpr (FOX) row_to_lds(tf[s], fl + (size_t)bh * Lp + (size_t)n * 64, wave, l);
+  };
+  const int64_t steps = m + 1;
+  stage(0, 0);
+  if (steps > 1) {
+    stage(1, 1);
+    wait_vm<OPS>();
+  } else {
+    wait_vm<0>();
+  }
+  lds_barrier();
+
+  float rs = 0.f;  // row sum of dz for query a, this lane's keys
+  // in-chunk block: logits from the packed S, dO V_m^T on the matrix cores
+  {
+    const __bf16* Vt = tl[0][1];
+    f32x4 dp[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dp[t] = zero;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dp[t] = mfma16(tile_frag(Vt, 16 * t + r, 4 * ks + g), dob[ks], dp[t]);
+    }
+    const float* Sb = Sm + ((size_t)bh * M + (size_t)m) * kSGroups * 4;
+    float* dSc = dSm + ((size_t)bh * M + (size_t)m) * 4096 + (size_t)a * 64;
+    const int last = a >> 2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int grp = (4 * t + g < last) ? 4 * t + g : last;  // groups past the diagonal re-read the last
+      const float4 s4 = *reinterpret_cast<const float4*>(Sb + (s_row_group(a) + grp) * 4);
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      float dz4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 16 * t + 4 * g + i;
+        float dz = 0.f;
+        if (b <= a) {
+          const float z2 = sv[i] - (FOX ? kLog2e * tf[0][b] : 0.f);
+          dz = fast_exp2(z2 - l2a) * (dp[t][i] - Da);
+        }
+        rs += dz;
+        dz4[i] = scale * dz;
+      }
+      *reinterpret_cast<float4*>(dSc + 16 * t + 4 * g) = make_float4(dz4[0], dz4[1], dz4[2], dz4[3]);
+    }
+  }
+
+  // key chunks n = 0 .. m-1: z^T = ktilde_n r^(n)T, p, dz; dr^(n)T = ktilde_n^T g^T + P_n^T dr^(n-1)T
+  f32x4 dR[4];  // dr^(n-1) transposed: [d 16 dt + 4g + i][query a]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) dR[dt] = zero;
+  bf16x8 rn[2];  // r^(n) of the next step, from the pair states
+  float offn = 0.f;
+  auto fetch_state = [&](int64_t n) PA_INLINE {
+    const size_t pr = band.slot(bh, m, n);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) rn[ks] = *reinterpret_cast<const bf16x8*>(St + pr * 4096 + a * 64 + 32 * ks + 8 * g);
+    if constexpr (FOX) offn = Off[pr];
+  };
+  if (m > 0) fetch_state(0);
+  int cur = 0;
+  for (int64_t j = 1; j < steps; ++j) {
+    // advance the ring: chunk j + 1 into the slot two ahead (after the last LDS read of step j - 1),
+    // chunk j (issued one step earlier) has landed
+    {
+      const int nxt = cur == 2 ? 0 : cur + 1;
+      if (j + 1 < steps) {
+        stage(j + 1, nxt == 2 ? 0 : nxt + 1);
+        wait_vm<OPS>();
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();
+      cur = nxt;
+    }
+    const int64_t n = j - 1;
+    const size_t pr = band.slot(bh, m, n);
+    const __bf16* Kt = tl[cur][0];
+    const __bf16* Vt = tl[cur][1];
+    const __bf16* Pt = tl[cur][2];
+    bf16x8 rcur[2] = {rn[0], rn[1]};
+    const float ofs = offn;
+    // dr^(n-1) as the operand (hi + lo); its hi part is the pair's stored gradient state
+    bf16x8 dh[2], dl[2];
+    acc_to_op(dR, dh, dl);
+    if (n > 0) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<bf16x8*>(Gst + pr * 4096 + a * 64 + 32 * ks + 8 * g) = dh[ks];
+    }
+    if (n + 1 < m) fetch_state(n + 1);
+    f32x4 zt[4], dp[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      zt[t] = zero;
+      dp[t] = zero;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        zt[t] = mfma16(tile_frag(Kt, 16 * t + r, 4 * ks + g), rcur[ks], zt[t]);
+        dp[t] = mfma16(tile_frag(Vt, 16 * t + r, 4 * ks + g), dob[ks], dp[t]);
+      }
+    }
+    f32x4 gt[4];  // ln2 dz, transposed: [key 16t + 4g + i][query a]
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 16 * t + 4 * g + i;
+        const float z2 = zt[t][i] + (FOX ? kLog2e * (ofs - tf[cur][b]) : 0.f);
+        const float dz = fast_exp2(z2 - l2a) * (dp[t][i] - Da);
+        rs += dz;
+        gt[t][i] = kLn2 * dz;
+      }
+    bf16x8 gh[2], gl[2];
+    acc_to_op(gt, gh, gl);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 acc = zero;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 kx = tr_frag(Kt, 16 * dt, ks, perm_pos);  // ktilde_n^T rows d = 16 dt + r, k = keys
+        acc = mfma16(kx, gh[ks], acc);
+        acc = mfma16(kx, gl[ks], acc);
+      }
+      if (n > 0) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 px = tr_frag(Pt, 16 * dt, ks, perm_pos);  // P_n^T rows d = 16 dt + r, k = d'
+          acc = mfma16(px, dh[ks], acc);
+          acc = mfma16(px, dl[ks], acc);
+        }
+      }
+      dR[dt] = acc;
+    }
+  }
+
+  // d qtilde = dr^(m-1) (qtilde entered the scan scaled by scale * log2e), row sums of dz
+  {
+    const float sq = scale * kLog2e;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<float4*>(dqt + (row0 + a) * 64 + 16 * dt + 4 * g) =
+          make_float4(sq * dR[dt][0], sq * dR[dt][1], sq * dR[dt][2], sq * dR[dt][3]);
+    const float s = colsum4(rs);
+    if (g == 0) drow[row0 + a] = s;
+  }
+}
+
+// Key-chunk kernel: one block of 4 waves per (key chunk n < me, batch*head); wave w owns the keys
+// b = 16w .. 16w+15 of the chunk (lane (r, g) key 16w + r).  The band's share of dv, d ktilde, dP_n and
+// the column sums of dz, added to the earlier bands' sums (fixed order: deterministic).  Per query chunk
+// m the pair states r^(n)_m, dr^(n-1)_m and the rows of dO_m stream through a ring of LDS slots.
+//   z[a][b] = r^(n)_m[a] . ktilde_n[b]  (queries x keys; accumulator rows a, column b)
+//   dv^T += dO_m^T p,  dktilde^T += r^T g,  dP_n[x][y] += sum_a dr[a][x] r[a][y]
+template <bool FOX>
+__global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
+    const __bf16* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
+    const __bf16* __restrict__ v, const __bf16* __restrict__ dout, const __bf16* __restrict__ St,
+    const __bf16* __restrict__ Gst, const float* __restrict__ Off, const float* __restrict__ lse2w,
+    const float* __restrict__ Dw, int64_t L, int64_t M, pair_band band, __bf16* __restrict__ dv,
+    float* __restrict__ dva, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol,
+    int64_t BH) {
+  __shared__ __align__(1024) __bf16 tl[kRingSlots][kPairTiles][kTile];  // r^(n)_m, dr^(n-1)_m, dO_m
+  __shared__ __align__(16) float ts[kRingSlots][2][64];                  // lse2 and D rows of chunk m
+
+  int64_t bh, n;
+  if (!bwd_pair_block(BH, band.me, bh, n)) return;  // whole block; low key chunks first
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, r = l & 15, g = l >> 4;
+  const int64_t Lp = M * 64;
+  const size_t rown = (size_t)bh * Lp + (size_t)n * 64;
+  const bool first = n >= band.mb;  // key chunk n's own query chunk is in this band: the sums start here
+  const bool last = band.me == M;   // the sums end here
+  const bool trans = n > 0;         // pairs (m, n) carry a transition below them (dr^(n-1) exists)
+  const int b = 16 * wave + r;      // this lane's key within chunk n
+  const int64_t ib = n * 64 + b;
+  const int i0 = 2 * wave;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  // ktilde_b (d in the permuted key order) and v_b (natural) as B-operands
+  bf16x8 kb[2], vb[2];
+  {
+    const size_t rv = ((size_t)bh * L + (size_t)(ib < L ? ib : L - 1)) * 64;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      kb[ks] = *reinterpret_cast<const bf16x8*>(kt + (rown + b) * 64 + 32 * ks + 8 * g);
+      vb[ks] = *reinterpret_cast<const bf16x8*>(v + rv + 32 * ks + 8 * g);
+    }
+  }
+  const float Fb = FOX ? fl[rown + b] : 0.f;
+
+  f32x4 aV[4], aK[4], aP[4];  // dv^T, dktilde^T: [x 16 xt + 4g + i][key b];  dP: [x 16 wave + 4g + i][y 16 yt + r]
+  float cs = 0.f;             // column sum of dz for key b, this lane's queries
+  const size_t pbase = ((size_t)bh * M + (size_t)n) * 4096;
+  if (!first) {  // the sums of the earlier bands
+#pragma unroll
+    for (int xt = 0; xt < 4; ++xt) {
+      const float4 x = *reinterpret_cast<const float4*>(dva + (rown + b) * 64 + 16 * xt + 4 * g);
+      const float4 y = *reinterpret_cast<const float4*>(dkt + (rown + b) * 64 + 16 * xt + 4 * g);
+      aV[xt] = f32x4{x.x, x.y, x.z, x.w};
+      aK[xt] = f32x4{y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) aP[xt][i] = dPm[pbase + (16 * wave + 4 * g + i) * 64 + 16 * xt + r];
+    }
+  } else {
+#pragma unroll
+    for (int xt = 0; xt < 4; ++xt) aV[xt] = aK[xt] = aP[xt] = zero;
+  }
+
+  // p (or g) of a step as the k = queries operand, hi + lo
+  auto dv_update = [&](const __bf16* Ot, const f32x4 (&pt)[4]) PA_INLINE {
+    bf16x8 ph[2], pl[2];
+    acc_to_op(pt, ph, pl);
+#pragma unroll
+    for (int xt = 0; xt < 4; ++xt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 ox = tr_frag(Ot, 16 * xt, ks, col_identity);  // dO_m^T rows x = 16 xt + r, k = queries
+        aV[xt] = mfma16(ox, ph[ks], aV[xt]);
+        aV[xt] = mfma16(ox, pl[ks], aV[xt]);
+      }
+  };
+  auto stage_rows = [&](int64_t mm, int s) PA_INLINE {
+    const int64_t vr = L - mm * 64;
+    dma_tile<2>(tl[s][2], dout + ((size_t)bh * L + (size_t)mm * 64) * 64, vr < 64 ? (int)vr : 64, i0);
+    row_to_lds(ts[s][0], lse2w + (size_t)bh * Lp + (size_t)mm * 64, wave, l);
+    row_to_lds(ts[s][1], Dw + (size_t)bh * Lp + (size_t)mm * 64, wave, l);
+  };
+
+  // in-chunk block (m = n): logits from the packed S; dv only
+  if (first) {
+    stage_rows(n, 0);
+    wait_vm<0>();
+    lds_barrier();
+    const __bf16* Ot = tl[0][2];
+    const float* Sb = Sm + ((size_t)bh * M + (size_t)n) * kSGroups * 4;
+    f32x4 pt[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      f32x4 dp = zero;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dp = mfma16(tile_frag(Ot, 16 * qt + r, 4 * ks + g), vb[ks], dp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = 16 * qt + 4 * g + i;
+        float p = 0.f, dz = 0.f;
+        if (b <= a) {
+          const float z2 = Sb[s_row_group(a) * 4 + b] - (FOX ? kLog2e * Fb : 0.f);
+          p = fast_exp2(z2 - ts[0][0][a]);
+          dz = p * (dp[i] - ts[0][1][a]);
+        }
+        cs += dz;
+        pt[qt][i] = p;
+      }
+    }
+    dv_update(Ot, pt);
+    lds_barrier();  // every wave is done with slot 0 before the ring reuses it
+  }
+
+  // the band's query chunks m > n
+  const int64_t m0 = n + 1 > band.mb ? n + 1 : band.mb;
+  const int64_t steps = band.me - m0;
+  if (steps > 0) {
+    auto stage = [&](int64_t k, int s) PA_INLINE {
+      const int64_t mm = m0 + k;
+      const size_t pr = band.slot(bh, mm, n);
+      dma_tile<2>(tl[s][0], St + pr * 4096, 64, i0);
+      dma_tile<2>(tl[s][1], Gst + pr * 4096, 64, i0);  // (not written for n = 0: copied, not used)
+      stage_rows(mm, s);
+    };
+    constexpr int OPS = slot_ops<2>();
+    float offn = FOX ? Off[band.slot(bh, m0, n)] : 0.f;
+    stage(0, 0);
+    if (steps > 1) {
+      stage(1, 1);
+      wait_vm<OPS>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();
+    int cur = 0;
+    for (int64_t k = 0; k < steps; ++k) {
+      const __bf16* Rt = tl[cur][0];
+      const __bf16* Gt = tl[cur][1];
+      const __bf16* Ot = tl[cur][2];
+      const float* l2r = ts[cur][0];
+      const float* Dr = ts[cur][1];
+      const float ofs = offn;
+      if constexpr (FOX) offn = Off[band.slot(bh, m0 + (k + 1 < steps ? k + 1 : k), n)];
+      f32x4 zt[4], pt[4], gt[4];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        f32x4 z = zero, dp = zero;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          z = mfma16(tile_frag(Rt, 16 * qt + r, 4 * ks + g), kb[ks], z);
+          dp = mfma16(tile_frag(Ot, 16 * qt + r, 4 * ks + g), vb[ks], dp);
+        }
+        const float4 l4 = *reinterpret_cast<const float4*>(l2r + 16 * qt + 4 * g);
+        const float4 d4 = *reinterpret_cast<const float4*>(Dr + 16 * qt + 4 * g);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z2 = z[i] + (FOX ? kLog2e * (ofs - Fb) : 0.f);
+          const float p = fast_exp2(z2 - lv[i]);
+          const float dz = p * (dp[i] - dv4[i]);
+          cs += dz;
+          pt[qt][i] = p;
+          gt[qt][i] = kLn2 * dz;
+        }
+        zt[qt] = z;
+      }
+      (void)zt;
+      dv_update(Ot, pt);
+      {
+        bf16x8 gh[2], gl[2];
+        acc_to_op(gt, gh, gl);
+#pragma unroll
+        for (int xt = 0; xt < 4; ++xt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 rx = tr_frag(Rt, 16 * xt, ks, perm_pos);  // r^T rows x = 16 xt + r, k = queries
+            aK[xt] = mfma16(rx, gh[ks], aK[xt]);
+            aK[xt] = mfma16(rx, gl[ks], aK[xt]);
+          }
+      }
+      if (trans) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 gx = tr_frag(Gt, 16 * wave, ks, perm_pos);  // dr^T rows x = 16 wave + r, k = queries
+#pragma unroll
+          for (int yt = 0; yt < 4; ++yt) aP[yt] = mfma16(gx, tr_frag(Rt, 16 * yt, ks, perm_pos), aP[yt]);
+        }
+      }
+      // ring: query chunk k + 2 into the slot two ahead, chunk k + 1 has landed
+      const int nxt = cur == 2 ? 0 : cur + 1;
+      if (k + 2 < steps) {
+        stage(k + 2, nxt == 2 ? 0 : nxt + 1);
+        wait_vm<OPS>();
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();
+      cur = nxt;
+    }
+  }
+
+  // outputs
+#pragma unroll
+  for (int xt = 0; xt < 4; ++xt) {
+    const size_t o = (rown + b) * 64 + 16 * xt + 4 * g;
+    *reinterpret_cast<float4*>(dkt + o) = make_float4(aK[xt][0], aK[xt][1], aK[xt][2], aK[xt][3]);
+    if (!last) {
+      *reinterpret_cast<float4*>(dva + o) = make_float4(aV[xt][0], aV[xt][1], aV[xt][2], aV[xt][3]);
+    } else if (ib < L) {
+      bf16x4 h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = (__bf16)aV[xt][i];
+      *reinterpret_cast<bf16x4*>(dv + ((size_t)bh * L + (size_t)ib) * 64 + 16 * xt + 4 * g) = h;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dPm[pbase + (16 * wave + 4 * g + i) * 64 + 16 * xt + r] = aP[xt][i];
+  }
+  const float s = colsum4(cs);
+  if (g == 0) dcol[rown + b] = (first ? 0.f : dcol[rown + b]) + s;
+}
+
+// One band of query chunks: the query-side kernel, then the key-side kernel.
+hipError_t bwd_pair_tiles_run(bool fox, const void* v, const void* out, const void* dout, const float* lse,
+                              int64_t BH, int64_t L, float scale, pair_band band, const bwd_buffers& b,
+                              void* dv, hipStream_t st) {
+  const int64_t M = (L + 63) / 64;
+  const int64_t xh = kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd);
+  const __bf16* qt = reinterpret_cast<const __bf16*>(b.qt);
+  const __bf16* kt = reinterpret_cast<const __bf16*>(b.kt);
+  const __bf16* Pm = reinterpret_cast<const __bf16*>(b.Pm);
+  __bf16* St = reinterpret_cast<__bf16*>(b.St);
+  __bf16* Gst = reinterpret_cast<__bf16*>(b.Gst);
+  const dim3 gq((unsigned)(xh * (band.me - band.mb))), gk((unsigned)(xh * band.me));
+  auto q = [&](auto kernel) {
+    kernel<<<gq, 256, 0, st>>>(qt, kt, Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const __bf16*)v, (const __bf16*)out,
+                              (const __bf16*)dout, lse, L, M, scale, band, St, Gst, b.Off, b.lse2, b.Dv, b.drow,
+                              b.dqt, b.dSm, BH);
+  };
+  if (fox) q(bwd_query_tile_kernel<true>);
+  else q(bwd_query_tile_kernel<false>);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto k = [&](auto kernel) {
+    kernel<<<gk, 256, 0, st>>>(kt, b.Sm, fox ? b.fl : nullptr, (const __bf16*)v, (const __bf16*)dout, St, Gst, b.Off,
+                              b.lse2, b.Dv, L, M, band, (__bf16*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
+  };
+  if (fox) k(bwd_key_tile_kernel<true>);
+  else k(bwd_key_tile_kernel<false>);
+  return hipGetLastError();
+}
+
+}  // namespace pathattn

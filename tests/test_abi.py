@@ -243,10 +243,12 @@ def test_bwd_workspace_planning(L):
     assert n.value < 2 * 8 * 24 * pairs * 64 * 64 * 2 + (2 << 30)
     nf = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 64, F32, ctypes.byref(nf)) == OK
-    # an fp32 input: fp32 states, ktilde [BH, L, 64] and P [BH, 64 chunks, 64, 64], and no stored A^{-1}
+    # an fp32 input: fp32 states, qtilde and ktilde [BH, L, 64], P [BH, 64 chunks, 64, 64] and the full
+    # square of in-chunk logits (a bf16 input keeps 544 4-float groups per chunk), and no stored A^{-1}
     # per chunk (64 x 64 fp32 for each of the 64 chunks)
-    assert nf.value - n.value == (2 * 8 * 24 * pairs * 64 * 64 * 2 + 8 * 24 * 4096 * 64 * 2
-                                  + 8 * 24 * 64 * 64 * 64 * 2 - 8 * 24 * 64 * 64 * 64 * 4)
+    BH, chunks = 8 * 24, 64
+    assert nf.value - n.value == (2 * BH * pairs * 64 * 64 * 2 + 2 * BH * 4096 * 64 * 2 + BH * chunks * 64 * 64 * 2
+                                  + BH * chunks * (64 * 64 - 544 * 4) * 4 - BH * chunks * 64 * 64 * 4)
     n0 = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 0, BF16, ctypes.byref(n0)) == OK
     assert n0.value == n.value  # chunk 0 = 64
