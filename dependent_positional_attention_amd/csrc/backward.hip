@@ -579,30 +579,6 @@ __device__ __forceinline__ void put_tile(float* dst, const f32x4 (&reg)[4], int 
   }
 }
 
-// The pair states r^(n) and dr^(n-1) of the matrix-core chunk-pair kernels, and the forward terms
-// ktilde and P they read, are bf16 for a bf16 input (the forward's bf16 transport rounds its running
-// queries, ktilde and P to bf16 in the same way; the chains themselves run in fp32 registers) and fp32
-// for an fp32 input.  Tiles are row-major with row stride 64.
-template <typename T>
-using state_t = typename std::conditional<std::is_same<T, __bf16>::value, __bf16, float>::type;
-template <typename S>
-__device__ __forceinline__ void acc_to_state(const f32x4 (&acc)[4], S* dst, int w, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[(16 * w + 4 * g + e) * 64 + 16 * cb + r] = from_f32<S>(acc[cb][e]);
-}
-// a state tile into registers in the fetch_tile layout, widened to fp32
-template <typename S>
-__device__ __forceinline__ void fetch_state(f32x4 (&reg)[4], const S* __restrict__ src, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i, row = e >> 4, c4 = (e & 15) * 4;
-    reg[i] = widen4<S>(*reinterpret_cast<const raw4<S>*>(src + row * 64 + c4));
-  }
-}
-
 // A-operand of mm64 held in registers: a[4 kb + j] = A(16w + r, 16 kb + 4g + j), i.e. the wave's own
 // 16 rows of a row-major 64 x 64 operand.
 __device__ __forceinline__ void frag_f32(float (&a)[16], const float* __restrict__ src, int w, int lane) {
@@ -652,65 +628,6 @@ __device__ __forceinline__ void mm64_ra(f32x4 (&acc)[4], const float (&a)[16], c
   }
 }
 
-// Products of bf16 numbers (v and dO of a bf16 input) are exact in fp32, so with bf16 inputs the dO v^T
-// products run on the bf16 matrix cores (16x16x32, fp32 accumulation; only the summation order differs
-// from the fp32 16x16x4 products).  A-fragments a[ks] = A(16w + r, 32 ks + 8g .. +7) come from global
-// memory (rows >= L zero); B(k, j) = B[j][k] from an fp32 LDS tile (stride kS) that holds bf16 numbers.
-__device__ __forceinline__ void frag_bf16(bf16x8 (&a)[2], const __bf16* __restrict__ src, int64_t c0, int64_t L,
-                                          int w, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-  const int64_t row = c0 + 16 * w + r;
-  const int64_t rr = row < L ? row : L - 1;  // clamped (valid) row; masked below
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + (size_t)rr * 64 + 32 * ks + 8 * g);
-    a[ks] = row < L ? v : bf16x8{};
-  }
-}
-__device__ __forceinline__ void mm64_bf16(f32x4 (&acc)[4], const bf16x8 (&a)[2], const float* __restrict__ B,
-                                          int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const float* p = B + (16 * cb + r) * kS + 32 * ks + 8 * g;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
-      const bf16x8 b = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
-                        (__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc[cb], 0, 0, 0);
-    }
-}
-
-// acc[cb] += sum_k A(16w + r', k) B(k, 16cb + r'') on the bf16 matrix cores for B holding bf16 numbers
-// (dO of a bf16 input): A from the wave's own rows of an fp32 LDS tile, split into hi + lo bf16 (about
-// 2^-16 relative), B(k, j) = B[k][j] from an fp32 LDS tile, converted exactly.
-__device__ __forceinline__ void mm64_split_bf16(f32x4 (&acc)[4], const float* __restrict__ A,
-                                                const float* __restrict__ B, int w, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {  // one k-block's fragments live at a time
-    const float* p = A + (16 * w + r) * kS + 32 * ks + 8 * g;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
-    bf16x8 ah, al;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float vi = i < 4 ? x[i] : y[i - 4];
-      const __bf16 hi = (__bf16)vi;
-      ah[i] = hi;
-      al[i] = (__bf16)(vi - (float)hi);
-    }
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      bf16x8 b;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = (__bf16)B[(32 * ks + 8 * g + i) * kS + 16 * cb + r];
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[cb], 0, 0, 0);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[cb], 0, 0, 0);
-    }
-  }
-}
-
 // bf16x3 products (bf16 inputs): an fp32 operand x = hi + lo with hi = bf16(x), lo = bf16(x - hi); a product
 // sums hi*hi + hi*lo + lo*hi on the bf16 matrix cores (about 2^-16 relative; lo*lo dropped).
 __device__ __forceinline__ void split8(const f32x4& x, const f32x4& y, bf16x8& h, bf16x8& l) {
@@ -722,51 +639,6 @@ __device__ __forceinline__ void split8(const f32x4& x, const f32x4& y, bf16x8& h
     l[i] = (__bf16)(v - (float)hi);
   }
 }
-// A-fragments of the wave's rows, a[ks] = A(16w + r, 32 ks + 8g .. +7), from fp32 rows of stride S
-template <int S>
-__device__ __forceinline__ void split_rows(bf16x8 (&h)[2], bf16x8 (&l)[2], const float* __restrict__ A, int w,
-                                          int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const float* p = A + (16 * w + r) * S + 32 * ks + 8 * g;
-    split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), h[ks], l[ks]);
-  }
-}
-// the same values from a bf16 state tile (row stride 64), widened
-__device__ __forceinline__ void rows_bf16(float (&v)[16], const __bf16* __restrict__ A, int w, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(A + (16 * w + r) * 64 + 32 * ks + 8 * g);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[8 * ks + i] = (float)x[i];
-  }
-}
-
-
-// acc[cb] += sum_k A(16w + r', k) B[k][16cb + r''] on the bf16 matrix cores: A as bf16 fragments, B an fp32
-// LDS tile (stride kS) holding bf16 numbers, read by columns and converted exactly
-__device__ __forceinline__ void mm64_bf16_cols(f32x4 (&acc)[4], const bf16x8 (&a)[2], const float* __restrict__ B,
-                                               int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      bf16x8 b;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = (__bf16)B[(32 * ks + 8 * g + i) * kS + 16 * cb + r];
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b, acc[cb], 0, 0, 0);
-    }
-}
-// bf16 fragments, a[ks] = A(16w + r, 32 ks + 8g .. +7), of a bf16 tile in global memory (row stride 64)
-__device__ __forceinline__ void frag_tile_bf16(bf16x8 (&a)[2], const __bf16* __restrict__ A, int w, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(A + (16 * w + r) * 64 + 32 * ks + 8 * g);
-}
-
 
 // mm64 on the bf16 matrix cores (bf16 inputs): acc[cb] += sum_k A(16w + r', k) B(k, 16cb + r''), operands as
 // in mm64 (AT, BK, row strides SA, SB; LDS tiles or global fp32 tiles).  An operand flagged exact (EA, EB:
@@ -825,39 +697,36 @@ __device__ __forceinline__ void mmx(f32x4 (&acc)[4], const float* A, const float
 
 // The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
 // (plain functions rather than capturing lambdas, so that the arrays stay in registers).
-template <typename T>
-__device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], raw4<T> (&pV)[4], f32x4 (&pP)[4], float (&pra)[16],
-                                                 float& pF, float& poff, const state_t<T>* __restrict__ kt,
-                                                 const T* __restrict__ vb, const state_t<T>* __restrict__ Pm,
-                                                 const state_t<T>* __restrict__ St, const float* __restrict__ fl,
+__device__ __forceinline__ void fetch_query_pair(f32x4 (&pK)[4], f32x4 (&pV)[4], f32x4 (&pP)[4], float (&pra)[16],
+                                                 float& pF, float& poff, const float* __restrict__ kt,
+                                                 const float* __restrict__ vb, const float* __restrict__ Pm,
+                                                 const float* __restrict__ St, const float* __restrict__ fl,
                                                  const float* __restrict__ Off, const pair_band& band, int64_t bh,
                                                  int64_t m, int64_t n, int64_t M, int64_t L, int tid, int w,
                                                  int lane) {
   constexpr int C = 64, CD = 64 * 64;
   const int64_t Lp = M * C;
   const size_t pr = band.slot(bh, m, n);
-  fetch_state(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
+  fetch_tile(pK, kt + ((size_t)bh * Lp + (size_t)n * C) * 64, tid);
   fetch_rows(pV, vb, n * C, L, tid);
-  fetch_state(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
-  if constexpr (std::is_same<T, __bf16>::value) rows_bf16(pra, St + pr * CD, w, lane);  // for the bf16 logits
-  else frag_f32(pra, St + pr * CD, w, lane);
+  fetch_tile(pP, Pm + ((size_t)bh * M + n) * CD, tid);  // P_0 when n = 0: fetched, not used
+  frag_f32(pra, St + pr * CD, w, lane);
   if (fl != nullptr) {
     pF = fl[(size_t)bh * Lp + (size_t)n * C + (tid & 63)];
     poff = Off[pr];
   }
 }
-template <typename T>
-__device__ __forceinline__ void fetch_key_pair(f32x4 (&pR)[4], f32x4 (&pG)[4], raw4<T> (&pO)[4], float& pl2,
-                                               float& pDv, float& poff, const state_t<T>* __restrict__ St,
-                                               const state_t<T>* __restrict__ Gst, const T* __restrict__ ob,
+__device__ __forceinline__ void fetch_key_pair(f32x4 (&pR)[4], f32x4 (&pG)[4], f32x4 (&pO)[4], float& pl2,
+                                               float& pDv, float& poff, const float* __restrict__ St,
+                                               const float* __restrict__ Gst, const float* __restrict__ ob,
                                                const float* __restrict__ lse2w, const float* __restrict__ Dw,
                                                const float* __restrict__ Off, bool fox, const pair_band& band,
                                                int64_t bh, int64_t m, int64_t n, int64_t M, int64_t L, int tid) {
   constexpr int C = 64, CD = 64 * 64;
   const int64_t Lp = M * C;
   const size_t pr = band.slot(bh, m, n);
-  fetch_state(pR, St + pr * CD, tid);
-  fetch_state(pG, Gst + pr * CD, tid);  // not written for n = 0 (no transport there): fetched, not used
+  fetch_tile(pR, St + pr * CD, tid);
+  fetch_tile(pG, Gst + pr * CD, tid);  // not written for n = 0 (no transport there): fetched, not used
   fetch_rows(pO, ob, m * C, L, tid);
   const size_t r0 = (size_t)bh * Lp + (size_t)m * C;
   pl2 = lse2w[r0 + (tid & 63)];
@@ -874,13 +743,14 @@ constexpr size_t kLdsPairMfma = sizeof(float) * (4 * 64 * kS + 3 * 64);
 
 }  // namespace
 
-// Query-chunk kernel on the matrix cores (same outputs as bwd_query_kernel<T, 64, 64>).
-template <typename T>
+// Query-chunk kernel on the fp32 matrix cores, fp32 inputs (same outputs as bwd_query_kernel<float, 64, 64>;
+// bf16 inputs take bwd_query_tile_kernel).
 __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
-    const float* __restrict__ qt, const state_t<T>* __restrict__ kt, const state_t<T>* __restrict__ Pm,
+    const float* __restrict__ qt, const float* __restrict__ kt, const float* __restrict__ Pm,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
-    const T* __restrict__ v, const T* __restrict__ out, const T* __restrict__ dout, const float* __restrict__ lse,
-    int64_t L, int64_t M, float scale, pair_band band, state_t<T>* __restrict__ St, state_t<T>* __restrict__ Gst,
+    const float* __restrict__ v, const float* __restrict__ out, const float* __restrict__ dout,
+    const float* __restrict__ lse, int64_t L, int64_t M, float scale, pair_band band, float* __restrict__ St,
+    float* __restrict__ Gst,
     float* __restrict__ Off, float* __restrict__ lse2w, float* __restrict__ Dw, float* __restrict__ drow,
     float* __restrict__ dqt, float* __restrict__ dSm, int64_t BH) {
   constexpr int C = 64, CD = 64 * 64;
@@ -900,14 +770,11 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   const int64_t Lp = M * C;
   const bool fox = fl != nullptr;
   const size_t row0 = (size_t)bh * Lp + (size_t)m * C;
-  const T* vb = v + (size_t)bh * L * 64;
+  const float* vb = v + (size_t)bh * L * 64;
 
-  // dO_m rows of this wave (the A-operand of dO V^T: bf16 fragments for a bf16 input), and D_i = dO_i . o_i
-  constexpr bool kBf = std::is_same<T, __bf16>::value;
+  // dO_m rows of this wave (the A-operand of dO V^T), and D_i = dO_i . o_i
   float oa[16];
   frag_rows(oa, dout + (size_t)bh * L * 64, m * C, L, w, lane);
-  bf16x8 ob16[2];
-  if constexpr (kBf) frag_bf16(ob16, reinterpret_cast<const __bf16*>(dout) + (size_t)bh * L * 64, m * C, L, w, lane);
   {
     float ob[16];
     frag_rows(ob, out + (size_t)bh * L * 64, m * C, L, w, lane);
@@ -934,28 +801,21 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   // (fetched unconditionally, at a clamped index: a conditionally written register array would be
   // kept in scratch memory)
   f32x4 pP[4];
-  fetch_state(pP, Pm + ((size_t)bh * M + (m > 0 ? m - 1 : 0)) * CD, tid);
+  fetch_tile(pP, Pm + ((size_t)bh * M + (m > 0 ? m - 1 : 0)) * CD, tid);
   float off = 0.f;
   for (int64_t n = m - 1; n >= 0; --n) {
     const size_t pr = band.slot(bh, m, n);
     if (fox) off += ftot[bh * M + n];
     if (tid == 0) Off[pr] = off;
-    acc_to_state(R, St + pr * CD, w, lane);
+    acc_to_global(R, St + pr * CD, w, lane);
     if (n > 0) {
       acc_to_lds(R, Xs, w, lane);
       __syncthreads();  // every wave is done with the previous P
       put_tile(Ps, pP, tid);
       __syncthreads();
-      fetch_state(pP, Pm + ((size_t)bh * M + (n > 1 ? n - 1 : 0)) * CD, tid);
+      fetch_tile(pP, Pm + ((size_t)bh * M + (n > 1 ? n - 1 : 0)) * CD, tid);
       zero4(R);
-      if constexpr (kBf) {  // r P_n^T
-        bf16x8 ah[2], al[2];
-        split_rows<kS>(ah, al, Xs, w, lane);
-        mm64_bf16(R, ah, Ps, lane);  // P_n holds bf16 numbers
-        mm64_bf16(R, al, Ps, lane);
-      } else {
-        mm64<false, false>(R, Xs, Ps, w, lane);
-      }
+      mm64<false, false>(R, Xs, Ps, w, lane);  // r P_n^T
     }
   }
 
@@ -968,8 +828,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   {
     f32x4 DP[4];
     zero4(DP);
-    if constexpr (kBf) mm64_bf16(DP, ob16, Vs, lane);
-    else mm64_ra<false>(DP, oa, Vs, lane);
+    mm64_ra<false>(DP, oa, Vs, lane);
     const float* Sc = Sm + ((size_t)bh * M + m) * C * C;
     float* dSc = dSm + ((size_t)bh * M + m) * C * C;
 #pragma unroll
@@ -991,7 +850,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   // arrive in registers one step ahead
   if (m > 0) {
   f32x4 pK[4];
-  raw4<T> pV[4];
+  f32x4 pV[4];
   float pra[16], ra[16];
   float pF = 0.f, poff = 0.f;
   fetch_query_pair(pK, pV, pP, pra, pF, poff, kt, vb, Pm, St, fl, Off, band, bh, m, 0, M, L, tid, w, lane);
@@ -999,7 +858,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const size_t pr = band.slot(bh, m, n);
     __syncthreads();  // every wave is done with the previous ktilde, v, P, FoX prefix
     put_tile(Ks, pK, tid);
-    put_rows<T>(Vs, pV, n * C, L, tid);
+    put_rows<float>(Vs, pV, n * C, L, tid);
     if (n > 0) put_tile(Ps, pP, tid);
     if (fox && tid < C) Fn[tid] = pF;
     const float offn = poff;
@@ -1007,7 +866,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     for (int x = 0; x < 16; ++x) ra[x] = pra[x];
     if (n > 0) {
       acc_to_lds(G, Xs, w, lane);  // dr^(n-1), this wave's rows
-      acc_to_state(G, Gst + pr * CD, w, lane);
+      acc_to_global(G, Gst + pr * CD, w, lane);
     }
     __syncthreads();
     // the last step fetches its own pair again (not used)
@@ -1015,28 +874,11 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
                      tid, w, lane);
     f32x4 Z[4], DP[4];
     zero4(G);
-    if (n > 0) {  // dr^(n-1) P_n
-      if constexpr (kBf) {
-        bf16x8 ah[2], al[2];
-        split_rows<kS>(ah, al, Xs, w, lane);
-        mm64_bf16_cols(G, ah, Ps, lane);
-        mm64_bf16_cols(G, al, Ps, lane);
-      } else {
-        mm64<false, true>(G, Xs, Ps, w, lane);
-      }
-    }
+    if (n > 0) mm64<false, true>(G, Xs, Ps, w, lane);  // dr^(n-1) P_n
     zero4(Z);
     zero4(DP);
-    if constexpr (kBf) {
-      bf16x8 a[2];  // r^(n) and ktilde_n are bf16 numbers: one product
-#pragma unroll
-      for (int i = 0; i < 16; ++i) a[i >> 3][i & 7] = (__bf16)ra[i];
-      mm64_bf16(Z, a, Ks, lane);
-    } else {
-      mm64_ra<false>(Z, ra, Ks, lane);
-    }
-    if constexpr (kBf) mm64_bf16(DP, ob16, Vs, lane);
-    else mm64_ra<false>(DP, oa, Vs, lane);
+    mm64_ra<false>(Z, ra, Ks, lane);
+    mm64_ra<false>(DP, oa, Vs, lane);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -1047,14 +889,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
         rsum[e] += dz;
         Xs[a * kS + b] = kLn2 * dz;  // the wave's own rows; the reads of dr^(n-1) above came first
       }
-    if constexpr (kBf) {  // + g ktilde_n
-      bf16x8 ah[2], al[2];
-      split_rows<kS>(ah, al, Xs, w, lane);
-      mm64_bf16_cols(G, ah, Ks, lane);
-      mm64_bf16_cols(G, al, Ks, lane);
-    } else {
-      mm64<false, true>(G, Xs, Ks, w, lane);
-    }
+    mm64<false, true>(G, Xs, Ks, w, lane);  // + g ktilde_n
   }
   }
 
@@ -1071,16 +906,15 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   }
 }
 
-// Key-chunk kernel on the matrix cores (same outputs as bwd_key_kernel<T, 64, 64>).  The logits of a
-// pair are formed transposed (rows = keys of chunk n), so that p and g are stored k-contiguous for
-// the products that reduce over the queries.
-template <typename T>
+// Key-chunk kernel on the fp32 matrix cores, fp32 inputs (same outputs as bwd_key_kernel<float, 64, 64>;
+// bf16 inputs take bwd_key_tile_kernel).  The logits of a pair are formed transposed (rows = keys of
+// chunk n), so that p and g are stored k-contiguous for the products that reduce over the queries.
 __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
-    const state_t<T>* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
-    const T* __restrict__ v, const T* __restrict__ dout, const state_t<T>* __restrict__ St,
-    const state_t<T>* __restrict__ Gst,
+    const float* __restrict__ kt, const float* __restrict__ Sm, const float* __restrict__ fl,
+    const float* __restrict__ v, const float* __restrict__ dout, const float* __restrict__ St,
+    const float* __restrict__ Gst,
     const float* __restrict__ Off, const float* __restrict__ lse2w, const float* __restrict__ Dw, int64_t L,
-    int64_t M, pair_band band, T* __restrict__ dv, float* __restrict__ dva, float* __restrict__ dkt,
+    int64_t M, pair_band band, float* __restrict__ dv, float* __restrict__ dva, float* __restrict__ dkt,
     float* __restrict__ dPm, float* __restrict__ dcol, int64_t BH) {
   constexpr int C = 64, CD = 64 * 64;
   extern __shared__ float sm[];
@@ -1100,18 +934,13 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   const size_t rown = (size_t)bh * Lp + (size_t)n * C;
   const bool first = n >= band.mb;  // query chunk n is in this band: the sums start here (in-chunk block)
   const bool last = band.me == M;   // the sums end here
-  const T* vb = v + (size_t)bh * L * 64;
-  const T* ob = dout + (size_t)bh * L * 64;
+  const float* vb = v + (size_t)bh * L * 64;
+  const float* ob = dout + (size_t)bh * L * 64;
 
-  // this wave's rows of ktilde_n and v_n: the A-operands of the transposed logits and of V dO^T (bf16
-  // fragments for a bf16 input)
-  constexpr bool kBf = std::is_same<T, __bf16>::value;
+  // this wave's rows of ktilde_n and v_n: the A-operands of the transposed logits and of V dO^T
   float ka[16], va[16];
-  bf16x8 vb16[2], kah[2];
-  if constexpr (kBf) frag_tile_bf16(kah, kt + rown * 64, w, lane);
-  else frag_f32(ka, kt + rown * 64, w, lane);
-  if constexpr (kBf) frag_bf16(vb16, reinterpret_cast<const __bf16*>(vb), n * C, L, w, lane);
-  else frag_rows(va, vb, n * C, L, w, lane);
+  frag_f32(ka, kt + rown * 64, w, lane);
+  frag_rows(va, vb, n * C, L, w, lane);
 
   f32x4 aV[4], aK[4], aP[4];
   float csum[4] = {0.f, 0.f, 0.f, 0.f};  // key rows 16w + 4g + e, this band's share
@@ -1135,8 +964,7 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   {
     f32x4 DT[4];
     zero4(DT);
-    if constexpr (kBf) mm64_bf16(DT, vb16, Os, lane);
-    else mm64_ra<false>(DT, va, Os, lane);
+    mm64_ra<false>(DT, va, Os, lane);
     const float* Sc = Sm + ((size_t)bh * M + n) * C * C;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -1153,22 +981,21 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
         Xs[b * kS + a] = p;  // the wave's own rows
       }
   }
-  if constexpr (kBf) mm64_split_bf16(aV, Xs, Os, w, lane);  // dv_n += p^T dO_n
-  else mm64<false, true>(aV, Xs, Os, w, lane);
+  mm64<false, true>(aV, Xs, Os, w, lane);  // dv_n += p^T dO_n
   }
 
   // the band's query chunks m > n; the next pair's tiles arrive in registers one step ahead
   const int64_t m0 = n + 1 > band.mb ? n + 1 : band.mb;
   if (m0 < band.me) {
   f32x4 pR[4], pG[4];
-  raw4<T> pO[4];
+  f32x4 pO[4];
   float pl2 = 0.f, pDv = 0.f, poff = 0.f;
   fetch_key_pair(pR, pG, pO, pl2, pDv, poff, St, Gst, ob, lse2w, Dw, Off, fox, band, bh, m0, n, M, L, tid);
   for (int64_t m = m0; m < band.me; ++m) {
     __syncthreads();  // every wave is done with the previous r, dO, dr, row statistics
     put_tile(Rs, pR, tid);
     if (n > 0) put_tile(Gq, pG, tid);
-    put_rows<T>(Os, pO, m * C, L, tid);
+    put_rows<float>(Os, pO, m * C, L, tid);
     if (tid < C) {
       l2[tid] = pl2;
       Dv[tid] = pDv;
@@ -1181,13 +1008,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     f32x4 ZT[4], DT[4];
     zero4(ZT);
     zero4(DT);
-    if constexpr (kBf) {  // (r ktilde^T)^T; r^(n) is stored in bf16
-      mm64_bf16(ZT, kah, Rs, lane);  // ktilde_n is bf16 too: one product
-    } else {
-      mm64_ra<false>(ZT, ka, Rs, lane);
-    }
-    if constexpr (kBf) mm64_bf16(DT, vb16, Os, lane);  // (dO v^T)^T
-    else mm64_ra<false>(DT, va, Os, lane);
+    mm64_ra<false>(ZT, ka, Rs, lane);  // (r ktilde^T)^T
+    mm64_ra<false>(DT, va, Os, lane);  // (dO v^T)^T
     float gz[4][4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -1201,17 +1023,13 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
         Xs[b * kS + a] = p;
         gz[cb][e] = kLn2 * dz;
       }
-    if constexpr (kBf) mm64_split_bf16(aV, Xs, Os, w, lane);  // dv_n += p^T dO_m
-    else mm64<false, true>(aV, Xs, Os, w, lane);
+    mm64<false, true>(aV, Xs, Os, w, lane);  // dv_n += p^T dO_m
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) Xs[(16 * w + 4 * g + e) * kS + 16 * cb + r] = gz[cb][e];  // after the reads of p
-    mmx<T, false, true, kS, kS, false, true>(aK, Xs, Rs, w, lane);  // d ktilde_n += g^T r
-    if (n > 0) {  // dP_n += dr^(n-1)^T r: both states bf16 numbers for a bf16 input, one exact product
-      if constexpr (kBf) mm64_bf<true, true, kS, kS, true, true>(aP, Gq, Rs, w, lane);
-      else mm64<true, true>(aP, Gq, Rs, w, lane);
-    }
+    mm64<false, true>(aK, Xs, Rs, w, lane);           // d ktilde_n += g^T r
+    if (n > 0) mm64<true, true>(aP, Gq, Rs, w, lane);  // dP_n += dr^(n-1)^T r
   }
   }
 
@@ -1225,7 +1043,7 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int b = 16 * w + 4 * g + e;
-        if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * 64 + 16 * cb + r] = from_f32<T>(aV[cb][e]);
+        if (n * C + b < L) dv[((size_t)bh * L + n * C + b) * 64 + 16 * cb + r] = aV[cb][e];
       }
   }
 #pragma unroll
@@ -1972,11 +1790,8 @@ __global__ __launch_bounds__(256) void bwd_forget_kernel(const float* __restrict
 }
 
 // ------------------------------------------------------------------------------- launch
-// mfma_path.hip: the forward's per-chunk terms in fp32 from bf16 inputs at d = chunk = 64 (the prefill's prep
-// kernel with fp32 outputs)
-hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
-                             int64_t BH, int64_t L, float qs, float* qt, void* kt, void* Pm, float* Sm, float* fl,
-                             float* ftot, float* Zi, hipStream_t st);
+// mfma_path.hip: the prefill's per-chunk terms (bf16 transport form) for bf16 inputs at d = chunk = 64, plus
+// A^{-1} per chunk
 hipError_t mfma_prep_bwd_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
                              int64_t BH, int64_t L, float qs, void* qt, void* kt, void* Pm, float* Sm, float* fl,
                              float* ftot, float* Zi, hipStream_t st);
@@ -2018,20 +1833,18 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
           (const T*)q, (const T*)k, (const T*)w, beta, logf, L, M, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl,
           b.ftot);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if ((e = lds((const void*)bwd_query_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
-      if ((e = lds((const void*)bwd_key_mfma_kernel<T>, kLdsPairMfma)) != hipSuccess) return e;
+      if ((e = lds((const void*)bwd_query_mfma_kernel, kLdsPairMfma)) != hipSuccess) return e;
+      if ((e = lds((const void*)bwd_key_mfma_kernel, kLdsPairMfma)) != hipSuccess) return e;
       const int64_t xh = kBwdXcd * ((BH + kBwdXcd - 1) / kBwdXcd);
       for (int64_t mb = 0; mb < M; mb += G) {
         const pair_band band{mb, mb + G < M ? mb + G : M, NPB};
-        bwd_query_mfma_kernel<T><<<dim3((unsigned)(xh * (band.me - band.mb))), 256, kLdsPairMfma, st>>>(
-            b.qt, reinterpret_cast<const state_t<T>*>(b.kt), reinterpret_cast<const state_t<T>*>(b.Pm), b.Sm, fox ? b.fl : nullptr, b.ftot, (const T*)v, (const T*)out, (const T*)dout, lse, L,
-            M, scale, band, reinterpret_cast<state_t<T>*>(b.St), reinterpret_cast<state_t<T>*>(b.Gst), b.Off, b.lse2,
-            b.Dv, b.drow, b.dqt, b.dSm, BH);
+        bwd_query_mfma_kernel<<<dim3((unsigned)(xh * (band.me - band.mb))), 256, kLdsPairMfma, st>>>(
+            b.qt, b.kt, b.Pm, b.Sm, fox ? b.fl : nullptr, b.ftot, (const float*)v, (const float*)out,
+            (const float*)dout, lse, L, M, scale, band, b.St, b.Gst, b.Off, b.lse2, b.Dv, b.drow, b.dqt, b.dSm, BH);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        bwd_key_mfma_kernel<T><<<dim3((unsigned)(xh * band.me)), 256, kLdsPairMfma, st>>>(
-            reinterpret_cast<const state_t<T>*>(b.kt), b.Sm, fox ? b.fl : nullptr, (const T*)v, (const T*)dout, reinterpret_cast<const state_t<T>*>(b.St),
-            reinterpret_cast<const state_t<T>*>(b.Gst), b.Off, b.lse2, b.Dv, L, M,
-            band, (T*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
+        bwd_key_mfma_kernel<<<dim3((unsigned)(xh * band.me)), 256, kLdsPairMfma, st>>>(
+            b.kt, b.Sm, fox ? b.fl : nullptr, (const float*)v, (const float*)dout, b.St, b.Gst, b.Off, b.lse2, b.Dv, L,
+            M, band, (float*)dv, b.dva, b.dkt, b.dPm, b.dcol, BH);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     }

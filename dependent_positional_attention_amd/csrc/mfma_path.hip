@@ -69,11 +69,9 @@ __device__ __forceinline__ int perm_col(int c) { return perm_pos(c); }
 
 
 // X3: the lo halves of qtilde and P (bf16x3 transport) are formed and stored; without it only hi.
-// F32: the per-chunk terms the backward pass works from: qtilde in fp32 (qt then points to an fp32
-// array of the same shape), ktilde and P in bf16 with natural columns, S as the full C x C square, and,
-// when Zo is given, Z = A^{-1} as well ([chunk][i][j] fp32, unit upper triangular, zeros below the
+// Zo (optional): Z = A^{-1} as well ([chunk][i][j] fp32, unit upper triangular, zeros below the
 // diagonal), which the backward's gradient kernel needs.
-template <bool X3, bool F32 = false>
+template <bool X3>
 __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
     const float* __restrict__ beta, const float* __restrict__ logf, int64_t L, int64_t M, float qs,
@@ -353,10 +351,7 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
       const bf16x4 q4 = q4s[xt];
       const float v0 = ((float)q4[0] - dq[0]) * qs, v1 = ((float)q4[1] - dq[1]) * qs,
                   v2 = ((float)q4[2] - dq[2]) * qs, v3 = ((float)q4[3] - dq[3]) * qs;
-      if constexpr (F32) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(qt) + (chunk_rows + a) * kD + x0) =
-            make_float4(v0, v1, v2, v3);
-      } else if constexpr (X3) {
+      if constexpr (X3) {
         bf16x4 h4, l4;
         split4(v0, v1, v2, v3, h4, l4);
         *reinterpret_cast<bf16x4*>(qt + (chunk_rows + a) * kD + pos) = h4;
@@ -370,7 +365,7 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
       const bf16x4 k4 = k4s[xt];
       const float u0 = (float)k4[0] - dk[0], u1 = (float)k4[1] - dk[1], u2 = (float)k4[2] - dk[2],
                   u3 = (float)k4[3] - dk[3];
-      *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + (F32 ? x0 : pos)) = pack4(u0, u1, u2, u3);
+      *reinterpret_cast<bf16x4*>(kt + (chunk_rows + a) * kD + pos) = pack4(u0, u1, u2, u3);
     }
     // P[x][y] = delta - D[y][x]  (lane: row x = 16 xt + r, columns y = 16 wave + 4g .. +3)
     {
@@ -378,9 +373,7 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
       const float e0 = (y0 == xr ? 1.f : 0.f) - dp[0], e1 = (y0 + 1 == xr ? 1.f : 0.f) - dp[1],
                   e2 = (y0 + 2 == xr ? 1.f : 0.f) - dp[2], e3 = (y0 + 3 == xr ? 1.f : 0.f) - dp[3];
       const int py = perm_pos(y0);
-      if constexpr (F32) {
-        *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + y0) = pack4(e0, e1, e2, e3);
-      } else if constexpr (X3) {
+      if constexpr (X3) {
         bf16x4 ph, pl;
         split4(e0, e1, e2, e3, ph, pl);
         *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = ph;
@@ -389,17 +382,14 @@ __global__ __launch_bounds__(256, 3) void mfma_prep_kernel(
         *reinterpret_cast<bf16x4*>(p_hi + chunk_mat + (size_t)xr * kD + py) = pack4(e0, e1, e2, e3);
       }
     }
-    // S[a][b] = (q_a.k_b - D[b][a]) * qs  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3):
-    // the fp32 form keeps the square, the bf16 forms the packed lower triangle
+    // S[a][b] = (q_a.k_b - D[b][a]) * qs  (lane: query a = 16 xt + r, keys b = 16 wave + 4g .. +3), as the
+    // packed lower triangle
     {
       const int aq = 16 * xt + r, b0 = 16 * wave + 4 * g;
       const float4 s4 = make_float4((kq[xt][0] - ds[0]) * qs, (kq[xt][1] - ds[1]) * qs, (kq[xt][2] - ds[2]) * qs,
                                     (kq[xt][3] - ds[3]) * qs);
-      if constexpr (F32) {
-        *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kC + aq) * kC + b0) = s4;
-      } else if (b0 <= aq) {
+      if (b0 <= aq)
         *reinterpret_cast<float4*>(Sm + (((size_t)bh * M + c) * kSGroups + s_row_group(aq) + (b0 >> 2)) * 4) = s4;
-      }
     }
   }
   (void)ia;
@@ -1412,31 +1402,16 @@ size_t mfma_handoff_scratch_bytes(int64_t BH, int64_t M) {
   return nseg > 1 ? (size_t)(BH * nseg) * kSegBytes : 0;
 }
 
-// The prep in fp32 output form for the backward pass (bf16 inputs, d = chunk = 64): qtilde and S
-// scaled by qs, ktilde, P, FoX chunk-local prefixes and chunk totals, all fp32 with natural columns.
-hipError_t mfma_prep_f32_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
-                             int64_t BH, int64_t L, float qs, float* qt, void* kt, void* Pm, float* Sm, float* fl,
-                             float* ftot, float* Zi, hipStream_t st) {
-  const int64_t M = (L + kC - 1) / kC;
-  hipError_t e = hipFuncSetAttribute((const void*)mfma_prep_kernel<false, true>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPrepLds);
-  if (e != hipSuccess) return e;
-  mfma_prep_kernel<false, true><<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
-      (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, qs, reinterpret_cast<__bf16*>(qt),
-      nullptr, reinterpret_cast<__bf16*>(kt), reinterpret_cast<__bf16*>(Pm), nullptr, Sm, fl, ftot, Zi);
-  return hipGetLastError();
-}
-
 // The prefill's per-chunk terms (bf16 transport form) for the backward pass of bf16 inputs, plus
 // Z = A^{-1} per chunk for its gradient kernel.
 hipError_t mfma_prep_bwd_run(const void* q, const void* k, const void* w, const float* beta, const float* logf,
                              int64_t BH, int64_t L, float qs, void* qt, void* kt, void* Pm, float* Sm, float* fl,
                              float* ftot, float* Zi, hipStream_t st) {
   const int64_t M = (L + kC - 1) / kC;
-  hipError_t e = hipFuncSetAttribute((const void*)mfma_prep_kernel<false, false>,
+  hipError_t e = hipFuncSetAttribute((const void*)mfma_prep_kernel<false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPrepLds);
   if (e != hipSuccess) return e;
-  mfma_prep_kernel<false, false><<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
+  mfma_prep_kernel<false><<<dim3((unsigned)M, (unsigned)BH), 256, kPrepLds, st>>>(
       (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, logf, L, M, qs, reinterpret_cast<__bf16*>(qt),
       nullptr, reinterpret_cast<__bf16*>(kt), reinterpret_cast<__bf16*>(Pm), nullptr, Sm, fl, ftot, Zi);
   return hipGetLastError();

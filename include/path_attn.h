@@ -331,13 +331,16 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
  *
  * Accumulation is fp32 and gradients are rounded to the input dtype once.  With
  * bf16 inputs at d = chunk = 64 the matrix products run on the bf16 matrix
- * cores: exact for products of input values, with other fp32 operands split
- * into hi + lo bf16 (about 2^-16 relative); fp32 inputs keep fp32 products.
+ * cores from the prefill's own per-chunk terms (bf16 transport form): the
+ * running queries are rounded to bf16 after every chunk transition as in the
+ * forward, other fp32 operands are split into hi + lo bf16 (about 2^-16
+ * relative); fp32 inputs keep fp32 products throughout.
  * Workspace: path_attn_bwd_workspace_bytes; it grows as B*H*L*d*sqrt(L/chunk)
- * (two fp32 vectors per key of every chunk pair of one band: about 4.8 GB at
- * B=8, H=24, L=4096, d=64, chunk 64, and 10.8 GB at B=1, H=24, L=32768).  The
- * kernels are deterministic: the same inputs give the same bits.  Errors as
- * for path_attn_fwd; nothing is enqueued on an error.
+ * (two vectors per key of every chunk pair of one band, bf16 for bf16 inputs:
+ * about 3.1 GB at B=8, H=24, L=4096, d=64, chunk 64 and 6.1 GB at B=1, H=24,
+ * L=32768; 4.8 and 10.8 GB for fp32 inputs).  The kernels are deterministic:
+ * the same inputs give the same bits.  Errors as for path_attn_fwd; nothing is
+ * enqueued on an error.
  */
 path_status path_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int d, int chunk, int dtype,
                                           size_t* bytes);
