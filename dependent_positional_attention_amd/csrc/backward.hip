@@ -454,9 +454,10 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // operands' row strides (kS for LDS tiles, 64 for fp32 tiles read straight from global memory).
 //   AT = false: A(i, k) = A[i][k] (float4 reads)    AT = true: A(i, k) = A[k][i]
 //   BK = false: B(k, j) = B[j][k] (float4 reads)    BK = true: B(k, j) = B[k][j]
-template <bool AT, bool BK, int SA = kS, int SB = kS>
-__device__ __forceinline__ void mm64(f32x4 (&acc)[4], const float* __restrict__ A, const float* __restrict__ B,
-                                     int w, int lane) {
+// (acc[c] holds column block cb0 + c: a wave may cover NC < 4 of the four)
+template <bool AT, bool BK, int SA = kS, int SB = kS, int NC>
+__device__ __forceinline__ void mm64(f32x4 (&acc)[NC], const float* __restrict__ A, const float* __restrict__ B,
+                                     int w, int lane, int cb0 = 0) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll 2
   for (int k0 = 0; k0 < 64; k0 += 16) {
@@ -469,7 +470,8 @@ __device__ __forceinline__ void mm64(f32x4 (&acc)[4], const float* __restrict__ 
       for (int j = 0; j < 4; ++j) a[j] = A[(k0 + 4 * g + j) * SA + 16 * w + r];
     }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int c = 0; c < NC; ++c) {
+      const int cb = cb0 + c;
       float b[4];
       if constexpr (!BK) {
         const float4 v = *reinterpret_cast<const float4*>(B + (16 * cb + r) * SB + k0 + 4 * g);
@@ -479,14 +481,15 @@ __device__ __forceinline__ void mm64(f32x4 (&acc)[4], const float* __restrict__ 
         for (int j = 0; j < 4; ++j) b[j] = B[(k0 + 4 * g + j) * SB + 16 * cb + r];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[cb] = mfma4(a[j], b[j], acc[cb]);
+      for (int j = 0; j < 4; ++j) acc[c] = mfma4(a[j], b[j], acc[c]);
     }
   }
 }
 
-__device__ __forceinline__ void zero4(f32x4 (&acc)[4]) {
+template <int NC>
+__device__ __forceinline__ void zero4(f32x4 (&acc)[NC]) {
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // accumulator layout <-> row-major 64 x 64 (LDS stride kS, or global stride 64)
@@ -504,17 +507,18 @@ __device__ __forceinline__ void acc_to_global(const f32x4 (&acc)[4], float* T, i
 #pragma unroll
     for (int e = 0; e < 4; ++e) T[(16 * w + 4 * g + e) * 64 + 16 * cb + r] = mul * acc[cb][e];
 }
-__device__ __forceinline__ void global_to_acc(f32x4 (&acc)[4], const float* T, int w, int lane) {
+template <int NC>
+__device__ __forceinline__ void global_to_acc(f32x4 (&acc)[NC], const float* T, int w, int lane, int cb0 = 0) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[cb][e] = T[(16 * w + 4 * g + e) * 64 + 16 * cb + r];
+    for (int e = 0; e < 4; ++e) acc[c][e] = T[(16 * w + 4 * g + e) * 64 + 16 * (cb0 + c) + r];
 }
 
 // 64 x 64 fp32 tile from global (row stride 64) into LDS (stride kS), float4 loads.
-__device__ __forceinline__ void tile_f32(float* dst, const float* __restrict__ src, int tid) {
-  for (int e = tid; e < 64 * 16; e += 256) {
+__device__ __forceinline__ void tile_f32(float* dst, const float* __restrict__ src, int tid, int nt = 256) {
+  for (int e = tid; e < 64 * 16; e += nt) {
     const int row = e >> 4, c4 = (e & 15) * 4;
     *reinterpret_cast<float4*>(dst + row * kS + c4) = *reinterpret_cast<const float4*>(src + row * 64 + c4);
   }
@@ -522,8 +526,9 @@ __device__ __forceinline__ void tile_f32(float* dst, const float* __restrict__ s
 
 // 64 rows of a [.., L, 64] input starting at row c0 (rows >= L read as zero), widened to fp32.
 template <typename T>
-__device__ __forceinline__ void tile_rows(float* dst, const T* __restrict__ src, int64_t c0, int64_t L, int tid) {
-  for (int e = tid; e < 64 * 16; e += 256) {
+__device__ __forceinline__ void tile_rows(float* dst, const T* __restrict__ src, int64_t c0, int64_t L, int tid,
+                                          int nt = 256) {
+  for (int e = tid; e < 64 * 16; e += nt) {
     const int row = e >> 4, c4 = (e & 15) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c0 + row < L) {
@@ -665,9 +670,9 @@ __device__ __forceinline__ void to_bf8(const float (&v)[8], bf16x8& h, bf16x8& l
     split8(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}, h, l);
   }
 }
-template <bool AT, bool BK, int SA, int SB, bool EA, bool EB>
-__device__ __forceinline__ void mm64_bf(f32x4 (&acc)[4], const float* __restrict__ A, const float* __restrict__ B,
-                                        int w, int lane) {
+template <bool AT, bool BK, int SA, int SB, bool EA, bool EB, int NC>
+__device__ __forceinline__ void mm64_bf(f32x4 (&acc)[NC], const float* __restrict__ A, const float* __restrict__ B,
+                                        int w, int lane, int cb0 = 0) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -677,22 +682,22 @@ __device__ __forceinline__ void mm64_bf(f32x4 (&acc)[4], const float* __restrict
     bf16x8 ah, al;
     to_bf8<EA>(av, ah, al);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int c = 0; c < NC; ++c) {
       float bv[8];
-      load8<BK, SB>(bv, B, 16 * cb + r, k0);
+      load8<BK, SB>(bv, B, 16 * (cb0 + c) + r, k0);
       bf16x8 bh, bl;
       to_bf8<EB>(bv, bh, bl);
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[cb], 0, 0, 0);
-      if constexpr (!EB) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[cb], 0, 0, 0);
-      if constexpr (!EA) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[cb], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[c], 0, 0, 0);
+      if constexpr (!EB) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[c], 0, 0, 0);
+      if constexpr (!EA) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[c], 0, 0, 0);
     }
   }
 }
 // mm64, on the bf16 matrix cores for a bf16 input
-template <typename T, bool AT, bool BK, int SA = kS, int SB = kS, bool EA = false, bool EB = false>
-__device__ __forceinline__ void mmx(f32x4 (&acc)[4], const float* A, const float* B, int w, int lane) {
-  if constexpr (std::is_same<T, __bf16>::value) mm64_bf<AT, BK, SA, SB, EA, EB>(acc, A, B, w, lane);
-  else mm64<AT, BK, SA, SB>(acc, A, B, w, lane);
+template <typename T, bool AT, bool BK, int SA = kS, int SB = kS, bool EA = false, bool EB = false, int NC>
+__device__ __forceinline__ void mmx(f32x4 (&acc)[NC], const float* A, const float* B, int w, int lane, int cb0 = 0) {
+  if constexpr (std::is_same<T, __bf16>::value) mm64_bf<AT, BK, SA, SB, EA, EB>(acc, A, B, w, lane, cb0);
+  else mm64<AT, BK, SA, SB>(acc, A, B, w, lane, cb0);
 }
 
 // The next chunk pair's operands of the two chunk-pair kernels, fetched into registers one step ahead
@@ -1064,25 +1069,26 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
 namespace {
 
 constexpr int kT = 64 * kS;                                     // one 64 x 64 LDS tile
-constexpr size_t kLdsChunkMfma = sizeof(float) * (9 * kT + 2 * 64);     // gradient kernel
+constexpr size_t kLdsChunkMfma = sizeof(float) * (9 * kT + 3 * 64);     // gradient kernel
 constexpr size_t kLdsChunkFwdMfma = sizeof(float) * (8 * kT + 64);   // forward-terms kernel
 
 // Element (i, j) of the accumulator layout: i = 16w + 4g + e, j = 16cb + r.
-template <typename F>
-__device__ __forceinline__ void acc_store(const f32x4 (&acc)[4], float* T, int w, int lane, F f) {
+template <typename F, int NC>
+__device__ __forceinline__ void acc_store(const f32x4 (&acc)[NC], float* T, int w, int lane, F f, int cb0 = 0) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e, j = 16 * cb + r;
-      T[i * kS + j] = f(i, j, acc[cb][e]);
+      const int i = 16 * w + 4 * g + e, j = 16 * (cb0 + c) + r;
+      T[i * kS + j] = f(i, j, acc[c][e]);
     }
 }
 
-__device__ __forceinline__ void sub4(f32x4 (&acc)[4], const f32x4 (&t)[4]) {
+template <int NC>
+__device__ __forceinline__ void sub4(f32x4 (&acc)[NC], const f32x4 (&t)[NC]) {
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] -= t[cb];
+  for (int c = 0; c < NC; ++c) acc[c] -= t[c];
 }
 
 // A = I + diag(beta) strict_upper(W W^T) is read from tile Aa (only r < s), A^{-1} written to Ai
@@ -1114,46 +1120,49 @@ __device__ __forceinline__ bf16x8 row8_bf16(const float* p) {
   return bf16x8{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
                 (__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
 }
-__device__ __forceinline__ void mm64_rows_bf16(f32x4 (&acc)[4], const float* __restrict__ A,
-                                               const float* __restrict__ B, int w, int lane) {
+template <int NC>
+__device__ __forceinline__ void mm64_rows_bf16(f32x4 (&acc)[NC], const float* __restrict__ A,
+                                               const float* __restrict__ B, int w, int lane, int cb0) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const bf16x8 a = row8_bf16(A + (16 * w + r) * kS + 32 * ks + 8 * g);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, row8_bf16(B + (16 * cb + r) * kS + 32 * ks + 8 * g),
-                                                        acc[cb], 0, 0, 0);
+    for (int c = 0; c < NC; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          a, row8_bf16(B + (16 * (cb0 + c) + r) * kS + 32 * ks + 8 * g), acc[c], 0, 0, 0);
   }
 }
 // mm64<false, false>, on the bf16 matrix cores when the operands hold bf16 numbers
-template <typename T>
-__device__ __forceinline__ void mm64_rows(f32x4 (&acc)[4], const float* A, const float* B, int w, int lane) {
-  if constexpr (std::is_same<T, __bf16>::value) mm64_rows_bf16(acc, A, B, w, lane);
-  else mm64<false, false>(acc, A, B, w, lane);
+template <typename T, int NC>
+__device__ __forceinline__ void mm64_rows(f32x4 (&acc)[NC], const float* A, const float* B, int w, int lane,
+                                          int cb0 = 0) {
+  if constexpr (std::is_same<T, __bf16>::value) mm64_rows_bf16(acc, A, B, w, lane, cb0);
+  else mm64<false, false>(acc, A, B, w, lane, cb0);
 }
 
-// W, Q, K of chunk c (rows >= L zero), beta, then A (into Aa), U (t <= a), R (s > b).
-template <typename T>
+// W, Q, K of chunk c (rows >= L zero), beta, then A (into Aa), U (t <= a), R (s > b).  NT threads; each
+// wave covers NC column blocks from cb0.
+template <typename T, int NC = 4, int NT = 256>
 __device__ __forceinline__ void chunk_setup(const T* q, const T* k, const T* w, const float* beta, int64_t bh,
                                             int64_t c, int64_t L, float* Wt, float* Qt, float* Kt, float* Aa,
-                                            float* Ut, float* Rt, float* Bs, int tid, int wv, int lane) {
+                                            float* Ut, float* Rt, float* Bs, int tid, int wv, int lane, int cb0 = 0) {
   const size_t base = (size_t)bh * L * 64;
-  tile_rows(Wt, w + base, c * 64, L, tid);
-  tile_rows(Qt, q + base, c * 64, L, tid);
-  tile_rows(Kt, k + base, c * 64, L, tid);
+  tile_rows(Wt, w + base, c * 64, L, tid, NT);
+  tile_rows(Qt, q + base, c * 64, L, tid, NT);
+  tile_rows(Kt, k + base, c * 64, L, tid, NT);
   if (tid < 64) Bs[tid] = c * 64 + tid < L ? beta[bh * L + c * 64 + tid] : 0.f;  // padded: identity
   __syncthreads();
-  f32x4 t[4];
+  f32x4 t[NC];
   zero4(t);
-  mm64_rows<T>(t, Wt, Wt, wv, lane);  // w_r . w_s
-  acc_store(t, Aa, wv, lane, [&](int i, int j, float x) { return i < j ? Bs[i] * x : 0.f; });
+  mm64_rows<T>(t, Wt, Wt, wv, lane, cb0);  // w_r . w_s
+  acc_store(t, Aa, wv, lane, [&](int i, int j, float x) { return i < j ? Bs[i] * x : 0.f; }, cb0);
   zero4(t);
-  mm64_rows<T>(t, Wt, Qt, wv, lane);  // w_t . q_a
-  acc_store(t, Ut, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; });
+  mm64_rows<T>(t, Wt, Qt, wv, lane, cb0);  // w_t . q_a
+  acc_store(t, Ut, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; }, cb0);
   zero4(t);
-  mm64_rows<T>(t, Kt, Wt, wv, lane);  // k_b . w_s
-  acc_store(t, Rt, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; });
+  mm64_rows<T>(t, Kt, Wt, wv, lane, cb0);  // k_b . w_s
+  acc_store(t, Rt, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; }, cb0);
 }
 
 }  // namespace
@@ -1268,7 +1277,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
 // d qtilde, d ktilde, dS and dP are read straight from global memory (fp32 tiles, row stride 64); so is
 // A^{-1} when the forward-terms kernel stored it (Zi), else it is formed here by back substitution.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
+__global__ __launch_bounds__(512) void bwd_chunk_grad_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ w, const float* __restrict__ beta,
     const float* __restrict__ dqt, const float* __restrict__ dkt, const float* __restrict__ dPm,
     const float* __restrict__ dSm, const float* __restrict__ Zi, int64_t L, int64_t M, T* __restrict__ dq,
@@ -1284,8 +1293,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
   float* S7 = S6 + kT;   // X, dX, W dP, dN
   float* S8 = S7 + kT;   // Y, dY, W dP^T
   float* Bs = S8 + kT;
-  float* dB = Bs + 64;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, g = lane >> 4;
+  float* dB = Bs + 64;  // dbeta partials, one row of 64 per column half (each filled by single waves)
+  // eight waves: wave 4h + wv works on rows 16 wv .. 16 wv + 15 and column blocks cb0 = 2h, 2h + 1 of every
+  // product (two waves per SIMD with the one block the LDS plan allows per CU)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wv = wave & 3, cb0 = 2 * (wave >> 2);
+  const int r = lane & 15, g = lane >> 4;
   const int64_t c = blockIdx.x, bh = blockIdx.y, Lp = M * 64;
   const size_t row0 = (size_t)bh * Lp + (size_t)c * 64;
   const float* dQ = dqt + row0 * 64;                         // d qtilde  [a][x]
@@ -1293,101 +1305,101 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
   const float* dS = dSm + ((size_t)bh * M + c) * 64 * 64;   // dS        [a][b]
   const float* dP = dPm + ((size_t)bh * M + c) * 64 * 64;   // dP        [x][y]
 
-  if (tid < 64) dB[tid] = 0.f;
-  chunk_setup(q, k, w, beta, bh, c, L, S0, S1, S2, S3, S4, S5, Bs, tid, wv, lane);
+  if (tid < 128) dB[tid] = 0.f;
+  chunk_setup<T, 2, 512>(q, k, w, beta, bh, c, L, S0, S1, S2, S3, S4, S5, Bs, tid, wv, lane, cb0);
   __syncthreads();
-  if (Zi != nullptr) tile_f32(S6, Zi + ((size_t)bh * M + c) * 64 * 64, tid);
+  if (Zi != nullptr) tile_f32(S6, Zi + ((size_t)bh * M + c) * 64 * 64, tid, 512);
   else unit_upper_inverse(S3, S6, tid);
   __syncthreads();
-  for (int e = tid; e < 64 * 64; e += 256) S3[(e >> 6) * kS + (e & 63)] = S6[(e >> 6) * kS + (e & 63)] * Bs[e & 63];
+  for (int e = tid; e < 64 * 64; e += 512) S3[(e >> 6) * kS + (e & 63)] = S6[(e >> 6) * kS + (e & 63)] * Bs[e & 63];
   __syncthreads();
 
   auto keep = [](int, int, float x) { return x; };
   auto neg = [](int, int, float x) { return -x; };
-  f32x4 aq[4], ak[4], aw[4], t[4], u[4], rU[4], rG[4];
-  global_to_acc(aq, dQ, wv, lane);  // dq = d qtilde + ...
-  global_to_acc(ak, dK, wv, lane);  // dk = d ktilde + ...
+  f32x4 aq[2], ak[2], aw[2], t[2], u[2], rU[2], rG[2];
+  global_to_acc(aq, dQ, wv, lane, cb0);  // dq = d qtilde + ...
+  global_to_acc(ak, dK, wv, lane, cb0);  // dk = d ktilde + ...
   zero4(aw);
   zero4(t);
-  mmx<T, false, true, kS, kS, false, false>(t, S3, S4, wv, lane);  // X = Ti U
-  acc_store(t, S7, wv, lane, keep);
+  mmx<T, false, true, kS, kS, false, false>(t, S3, S4, wv, lane, cb0);  // X = Ti U
+  acc_store(t, S7, wv, lane, keep, cb0);
   zero4(t);
-  mmx<T, false, true, kS, kS, false, false>(t, S5, S3, wv, lane);  // Y = R Ti
-  acc_store(t, S8, wv, lane, keep);
-  mmx<T, false, true, 64, kS, false, true>(aq, dS, S2, wv, lane);  // dq += dS K
-  mmx<T, true, true, 64, kS, false, true>(ak, dS, S1, wv, lane);   // dk += dS^T Q
+  mmx<T, false, true, kS, kS, false, false>(t, S5, S3, wv, lane, cb0);  // Y = R Ti
+  acc_store(t, S8, wv, lane, keep, cb0);
+  mmx<T, false, true, 64, kS, false, true>(aq, dS, S2, wv, lane, cb0);  // dq += dS K
+  mmx<T, true, true, 64, kS, false, true>(ak, dS, S1, wv, lane, cb0);   // dk += dS^T Q
   __syncthreads();
   zero4(t);
-  mmx<T, false, true, kS, 64, false, false>(t, S7, dQ, wv, lane);  // X dqtilde
-  mmx<T, true, true, kS, 64, false, false>(t, S8, dK, wv, lane);   // + Y^T dktilde
+  mmx<T, false, true, kS, 64, false, false>(t, S7, dQ, wv, lane, cb0);  // X dqtilde
+  mmx<T, true, true, kS, 64, false, false>(t, S8, dK, wv, lane, cb0);   // + Y^T dktilde
   sub4(aw, t);
   zero4(u);
-  mmx<T, false, false, kS, 64, true, false>(u, S0, dQ, wv, lane);  // -dX = W dqtilde^T
+  mmx<T, false, false, kS, 64, true, false>(u, S0, dQ, wv, lane, cb0);  // -dX = W dqtilde^T
   zero4(t);
-  mmx<T, false, false, 64, kS, false, true>(t, dK, S0, wv, lane);  // -dY = dktilde W^T
-  mmx<T, true, false, 64, kS, false, false>(t, dS, S4, wv, lane);   //       + dS^T U^T
+  mmx<T, false, false, 64, kS, false, true>(t, dK, S0, wv, lane, cb0);  // -dY = dktilde W^T
+  mmx<T, true, false, 64, kS, false, false>(t, dS, S4, wv, lane, cb0);   //       + dS^T U^T
   zero4(rU);
-  mmx<T, true, false, kS, 64, false, false>(rU, S8, dS, wv, lane);  // (dS Y)^T
+  mmx<T, true, false, kS, 64, false, false>(rU, S8, dS, wv, lane, cb0);  // (dS Y)^T
   __syncthreads();
-  acc_store(u, S7, wv, lane, neg);  // dX
-  acc_store(t, S8, wv, lane, neg);  // dY
+  acc_store(u, S7, wv, lane, neg, cb0);  // dX
+  acc_store(t, S8, wv, lane, neg, cb0);  // dY
   __syncthreads();
   zero4(u);
-  mmx<T, true, true, kS, kS, false, false>(u, S3, S7, wv, lane);  // dU = Ti^T dX - (dS Y)^T
+  mmx<T, true, true, kS, kS, false, false>(u, S3, S7, wv, lane, cb0);  // dU = Ti^T dX - (dS Y)^T
   sub4(u, rU);
   zero4(rG);
-  mmx<T, false, false, kS, kS, false, false>(rG, S7, S4, wv, lane);  // dTi = dX U^T
-  mmx<T, true, true, kS, kS, false, false>(rG, S5, S8, wv, lane);    //     + R^T dY
+  mmx<T, false, false, kS, kS, false, false>(rG, S7, S4, wv, lane, cb0);  // dTi = dX U^T
+  mmx<T, true, true, kS, kS, false, false>(rG, S5, S8, wv, lane, cb0);    //     + R^T dY
   zero4(t);
-  mmx<T, false, false, kS, kS, false, false>(t, S8, S3, wv, lane);  // dR = dY Ti^T
+  mmx<T, false, false, kS, kS, false, false>(t, S8, S3, wv, lane, cb0);  // dR = dY Ti^T
   __syncthreads();
-  acc_store(u, S4, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; });
-  acc_store(t, S5, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; });
+  acc_store(u, S4, wv, lane, [](int i, int j, float x) { return i <= j ? x : 0.f; }, cb0);
+  acc_store(t, S5, wv, lane, [](int i, int j, float x) { return j > i ? x : 0.f; }, cb0);
   __syncthreads();
-  mmx<T, false, true, kS, kS, false, true>(aw, S4, S1, wv, lane);  // dW += dU Q
-  mmx<T, true, true, kS, kS, false, true>(aw, S5, S2, wv, lane);   //     + dR^T K
-  mmx<T, true, true, kS, kS, false, true>(aq, S4, S0, wv, lane);   // dq += dU^T W
-  mmx<T, false, true, kS, kS, false, true>(ak, S5, S0, wv, lane);  // dk += dR W
+  mmx<T, false, true, kS, kS, false, true>(aw, S4, S1, wv, lane, cb0);  // dW += dU Q
+  mmx<T, true, true, kS, kS, false, true>(aw, S5, S2, wv, lane, cb0);   //     + dR^T K
+  mmx<T, true, true, kS, kS, false, true>(aq, S4, S0, wv, lane, cb0);   // dq += dU^T W
+  mmx<T, false, true, kS, kS, false, true>(ak, S5, S0, wv, lane, cb0);  // dk += dR W
   zero4(t);
-  mmx<T, false, true, kS, 64, true, false>(t, S0, dP, wv, lane);  // W dP
+  mmx<T, false, true, kS, 64, true, false>(t, S0, dP, wv, lane, cb0);  // W dP
   zero4(u);
-  mmx<T, false, false, kS, 64, true, false>(u, S0, dP, wv, lane);  // W dP^T
-  acc_store(t, S7, wv, lane, keep);
-  acc_store(u, S8, wv, lane, keep);
+  mmx<T, false, false, kS, 64, true, false>(u, S0, dP, wv, lane, cb0);  // W dP^T
+  acc_store(t, S7, wv, lane, keep, cb0);
+  acc_store(u, S8, wv, lane, keep, cb0);
   __syncthreads();
   zero4(t);
-  mmx<T, false, false, kS, kS, false, true>(t, S7, S0, wv, lane);  // dTi -= W dP W^T
+  mmx<T, false, false, kS, kS, false, true>(t, S7, S0, wv, lane, cb0);  // dTi -= W dP W^T
   sub4(rG, t);
   zero4(t);
-  mmx<T, false, true, kS, kS, false, false>(t, S3, S8, wv, lane);  // dW -= Ti W dP^T
-  mmx<T, true, true, kS, kS, false, false>(t, S3, S7, wv, lane);   //      + Ti^T W dP
+  mmx<T, false, true, kS, kS, false, false>(t, S3, S8, wv, lane, cb0);  // dW -= Ti W dP^T
+  mmx<T, true, true, kS, kS, false, false>(t, S3, S7, wv, lane, cb0);   //      + Ti^T W dP
   sub4(aw, t);
   __syncthreads();
-  acc_store(rG, S4, wv, lane, keep);
+  acc_store(rG, S4, wv, lane, keep, cb0);
   __syncthreads();
   zero4(t);
-  mmx<T, true, true, kS, kS, false, false>(t, S6, S4, wv, lane);  // M1 = A^{-T} dTi; dbeta += diag(M1)
+  mmx<T, true, true, kS, kS, false, false>(t, S6, S4, wv, lane, cb0);  // M1 = A^{-T} dTi; dbeta += diag(M1)
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (16 * wv + 4 * g + e == 16 * cb + r) atomicAdd(&dB[16 * cb + r], t[cb][e]);
-  acc_store(t, S5, wv, lane, keep);
+      if (16 * wv + 4 * g + e == 16 * (cb0 + cc) + r) atomicAdd(&dB[32 * cb0 + 16 * (cb0 + cc) + r], t[cc][e]);
+  acc_store(t, S5, wv, lane, keep, cb0);
   __syncthreads();
   zero4(t);
-  mmx<T, false, false, kS, kS, false, false>(t, S5, S3, wv, lane);  // M1 Ti^T
+  mmx<T, false, false, kS, kS, false, false>(t, S5, S3, wv, lane, cb0);  // M1 Ti^T
   zero4(u);
-  mm64_rows<T>(u, S0, S0, wv, lane);  // w_r . w_s
+  mm64_rows<T>(u, S0, S0, wv, lane, cb0);  // w_r . w_s
   {
     float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * wv + 4 * g + e, j = 16 * cb + r;
-        const float z = i < j ? -t[cb][e] : 0.f;  // dA[i][j]
-        rowp[e] += z * u[cb][e];
-        t[cb][e] = Bs[i] * z;  // dN
+        const int i = 16 * wv + 4 * g + e, j = 16 * (cb0 + cc) + r;
+        const float z = i < j ? -t[cc][e] : 0.f;  // dA[i][j]
+        rowp[e] += z * u[cc][e];
+        t[cc][e] = Bs[i] * z;  // dN
       }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1396,28 +1408,28 @@ __global__ __launch_bounds__(256) void bwd_chunk_grad_mfma_kernel(
       x += __shfl_xor(x, 2);
       x += __shfl_xor(x, 4);
       x += __shfl_xor(x, 8);
-      if (r == 0) atomicAdd(&dB[16 * wv + 4 * g + e], x);
+      if (r == 0) atomicAdd(&dB[32 * cb0 + 16 * wv + 4 * g + e], x);
     }
   }
-  acc_store(t, S7, wv, lane, keep);
+  acc_store(t, S7, wv, lane, keep, cb0);
   __syncthreads();
-  mmx<T, false, true, kS, kS, false, true>(aw, S7, S0, wv, lane);  // dW += dN W
-  mmx<T, true, true, kS, kS, false, true>(aw, S7, S0, wv, lane);   //      + dN^T W
+  mmx<T, false, true, kS, kS, false, true>(aw, S7, S0, wv, lane, cb0);  // dW += dN W
+  mmx<T, true, true, kS, kS, false, true>(aw, S7, S0, wv, lane, cb0);   //      + dN^T W
   __syncthreads();
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int a = 16 * wv + 4 * g + e, x = 16 * cb + r;
+      const int a = 16 * wv + 4 * g + e, x = 16 * (cb0 + cc) + r;
       const int64_t i = c * 64 + a;
       if (i < L) {
         const size_t o = ((size_t)bh * L + i) * 64 + x;
-        dq[o] = from_f32<T>(aq[cb][e]);
-        dk[o] = from_f32<T>(ak[cb][e]);
-        dw[o] = from_f32<T>(aw[cb][e]);
+        dq[o] = from_f32<T>(aq[cc][e]);
+        dk[o] = from_f32<T>(ak[cc][e]);
+        dw[o] = from_f32<T>(aw[cc][e]);
       }
     }
-  if (tid < 64 && c * 64 + tid < L) dbeta[bh * L + c * 64 + tid] = dB[tid];
+  if (tid < 64 && c * 64 + tid < L) dbeta[bh * L + c * 64 + tid] = dB[tid] + dB[64 + tid];
 }
 
 // ------------------------------------------------------------------------------- UT-transform terms
@@ -1848,7 +1860,7 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     }
-    bwd_chunk_grad_mfma_kernel<T><<<grid, 256, kLdsChunkMfma, st>>>(
+    bwd_chunk_grad_mfma_kernel<T><<<grid, 512, kLdsChunkMfma, st>>>(
         (const T*)q, (const T*)k, (const T*)w, beta, b.dqt, b.dkt, b.dPm, b.dSm,
         std::is_same<T, __bf16>::value ? b.Zi : nullptr, L, M, (T*)dq, (T*)dk, (T*)dw, dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
