@@ -92,45 +92,63 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
 
   // ---------------------------------------------------------------- pass 1: the states r^(n)
   // r^(n) of this wave's queries as the operand rb (query a, d in the permuted key order), stored per
-  // pair and moved across P_n (n >= 1), rounded to bf16 after every transition.  P_n fragments come
-  // straight from global memory into registers, one step ahead.
+  // pair and moved across P_n (n >= 1), rounded to bf16 after every transition.  P_{m-1} .. P_1 stream
+  // through the LDS ring (one copy per block; P_{n-2} is issued after the transport of step n).  A
+  // step's stores go out after its copy wait, so that the next step's wait covers them.
   bf16x8 rb[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) rb[ks] = *reinterpret_cast<const bf16x8*>(qt + (row0 + a) * 64 + 32 * ks + 8 * g);
   {
-    bf16x8 pf[4][2];  // P_n rows 16 dt + r, stored columns 32 ks + 8g .. +7
-    auto fetch_p = [&](int64_t n) PA_INLINE {
-      const __bf16* pn = Pm + ((size_t)bh * M + (size_t)(n > 0 ? n : 0)) * 4096;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pf[dt][ks] = *reinterpret_cast<const bf16x8*>(pn + (16 * dt + r) * 64 + 32 * ks + 8 * g);
+    auto stage_p = [&](int64_t n, int s) PA_INLINE {
+      dma_tile<2>(tl[s][2], Pm + ((size_t)bh * M + (size_t)n) * 4096, 64, i0);
     };
-    fetch_p(m - 1);
+    if (m >= 2) {
+      stage_p(m - 1, 0);
+      if (m >= 3) {
+        stage_p(m - 2, 1);
+        wait_vm<2>();
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();
+    }
     float off = 0.f;
+    int cur = 0;
     for (int64_t n = m - 1; n >= 0; --n) {
       const size_t pr = band.slot(bh, m, n);
       if constexpr (FOX) off += ftot[bh * M + n];
+      bf16x8 rn[2] = {rb[0], rb[1]};
+      if (n > 0) {
+        f32x4 rt[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          rt[dt] = zero;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) rt[dt] = mfma16(tile_frag(tl[cur][2], 16 * dt + r, 4 * ks + g), rb[ks], rt[dt]);
+        }
+        const int nxt = cur == 2 ? 0 : cur + 1;
+        if (n - 2 >= 1) {
+          stage_p(n - 2, nxt == 2 ? 0 : nxt + 1);
+          wait_vm<2>();
+        } else {
+          wait_vm<0>();
+        }
+        lds_barrier();
+        cur = nxt;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rn[ks][j] = (__bf16)rt[2 * ks + (j >> 2)][j & 3];
+      }
       if (l == 0) Off[pr] = off;  // every wave writes the same value
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         *reinterpret_cast<bf16x8*>(St + pr * 4096 + a * 64 + 32 * ks + 8 * g) = rb[ks];
-      if (n == 0) break;
-      f32x4 rt[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        rt[dt] = zero;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) rt[dt] = mfma16(pf[dt][ks], rb[ks], rt[dt]);
-      }
-      fetch_p(n - 1);  // (P_0 when n = 1: fetched, not used)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rb[ks][j] = (__bf16)rt[2 * ks + (j >> 2)][j & 3];
+      rb[0] = rn[0];
+      rb[1] = rn[1];
     }
   }
+  lds_barrier();  // every wave is done with the P slots before the ring below reuses them
 
   // ---------------------------------------------------------------- key chunks through the LDS ring
   // stream position j: 0 = the own chunk m (in-chunk block), then n = j - 1 = 0 .. m-1
