@@ -41,7 +41,6 @@ import time
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU, dense
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CUs x 2.4 GHz x 128 fp32 lanes x 2 flop (FMA) per clock
 
 
 def log(*a):
@@ -229,17 +228,16 @@ def bench_backward(args, res, ctx):
     tf = F / (ms * 1e-3) / 1e12
     x3_peak = MFMA_BF16_PEAK_TFLOPS / 3  # fp32-accurate products as three bf16 products (hi.hi + hi.lo + lo.hi)
     log(f"[bench] backward: {ms:.2f} ms, {B * L / (ms * 1e-3) / 1e6:.3f} M tokens/s, {tf:.2f} TFLOP/s = "
-        f"{tf / MFMA_BF16_PEAK_TFLOPS:.3f} of the dense bf16 peak, {tf / x3_peak:.3f} of the bf16x3 peak, "
-        f"{tf / FP32_VECTOR_PEAK_TFLOPS:.3f} of the fp32 peak (workspace {nbytes / 2**30:.1f} GiB)")
+        f"{tf / MFMA_BF16_PEAK_TFLOPS:.3f} of the dense bf16 peak, {tf / x3_peak:.3f} of the bf16x3 peak "
+        f"(workspace {nbytes / 2**30:.1f} GiB)")
     del ws
-    return {"workload": f"PaTH backward, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16 in/out, fp32 arithmetic",
+    return {"workload": f"PaTH backward, B={B}, H={H}, L={L}, d={d}, chunk {C}, bf16 in/out, fp32 accumulation",
             "ms": ms, "steps": n, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf, "bound": "mfma",
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
             "bf16x3_peak": x3_peak, "frac_of_bf16x3_peak": tf / x3_peak,
-            "fp32_peak": FP32_VECTOR_PEAK_TFLOPS, "frac_of_fp32_peak": tf / FP32_VECTOR_PEAK_TFLOPS,
-            "note": "most products run on the bf16 matrix cores (exact for input values, hi+lo split otherwise), "
-                    "so peak = dense bf16 peak; bf16x3_peak = bf16 peak / 3 (an fp32-accurate product as three "
-                    "bf16 products); fp32_peak = fp32 matrix/vector peak",
+            "note": "the products run on the bf16 matrix cores (bf16 operands exact, other fp32 operands split "
+                    "into hi+lo), so peak = dense bf16 peak; bf16x3_peak = bf16 peak / 3 (an fp32-accurate "
+                    "product as three bf16 products)",
             "workspace_bytes": nbytes}
 
 
@@ -623,7 +621,7 @@ def main():
     B_, H_, L_, d_ = res["B"], res["H"], res["L"], res["d"]
     attn_flops = 4.0 * d_ * (L_ * (L_ + 1) / 2) * B_ * H_
     ktag = "<{},{},1,2,4>".format("true" if args.fox else "false", "true" if args.transport == "bf16x3" else "false")
-    ptag = "<{},false>".format("true" if args.transport == "bf16x3" else "false")
+    ptag = "<{}>".format("true" if args.transport == "bf16x3" else "false")
     t_scan = measured_traffic(PREFILL_COUNTERS, "mfma_attn_kernel" + ktag, "mfma_path.hip")
     t_prep = measured_traffic(PREFILL_COUNTERS, "mfma_prep_kernel" + ptag, "mfma_path.hip")
     line = {
