@@ -237,8 +237,8 @@ def test_bwd_workspace_planning(L):
     n = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 64, BF16, ctypes.byref(n)) == OK
     # states and their gradients of one band of query chunks at a time (bf16 for a bf16 input): 64 chunks
-    # in bands of 8, the largest band (chunks 56 .. 63) holding 56 + ... + 63 pairs
-    pairs = sum(range(56, 64))
+    # in bands of 2 ceil(sqrt(64)) = 16, the largest band (chunks 48 .. 63) holding 48 + ... + 63 pairs
+    pairs = sum(range(48, 64))
     assert n.value >= 2 * 8 * 24 * pairs * 64 * 64 * 2
     assert n.value < 2 * 8 * 24 * pairs * 64 * 64 * 2 + (2 << 30)
     nf = ctypes.c_size_t(0)
