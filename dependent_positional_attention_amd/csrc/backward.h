@@ -71,6 +71,11 @@ __device__ __forceinline__ bool bwd_pair_block(int64_t BH, int64_t M, int64_t& b
 hipError_t bwd_pair_tiles_run(bool fox, const void* v, const void* out, const void* dout, const float* lse,
                               int64_t BH, int64_t L, float scale, pair_band band, const bwd_buffers& b, void* dv,
                               hipStream_t st);
+// backward_tiles.hip: per-chunk gradients (dq, dk, dw, dbeta) of bf16 inputs at d = chunk = 64, from the
+// chain's d qtilde, d ktilde, dP, dS and the stored A^{-1} (b.Zi)
+hipError_t bwd_chunk_grad_tiles_run(const void* q, const void* k, const void* w, const float* beta, int64_t BH,
+                                    int64_t L, const bwd_buffers& b, void* dq, void* dk, void* dw, float* dbeta,
+                                    hipStream_t st);
 
 hipError_t bwd_run(bool bf16, int d, int chunk, const void* q, const void* k, const void* v, const void* w,
                    const float* beta, const float* logf, const void* out, const float* lse, const void* dout,

@@ -516,14 +516,6 @@ __device__ __forceinline__ void global_to_acc(f32x4 (&acc)[NC], const float* T, 
     for (int e = 0; e < 4; ++e) acc[c][e] = T[(16 * w + 4 * g + e) * 64 + 16 * (cb0 + c) + r];
 }
 
-// 64 x 64 fp32 tile from global (row stride 64) into LDS (stride kS), float4 loads.
-__device__ __forceinline__ void tile_f32(float* dst, const float* __restrict__ src, int tid, int nt = 256) {
-  for (int e = tid; e < 64 * 16; e += nt) {
-    const int row = e >> 4, c4 = (e & 15) * 4;
-    *reinterpret_cast<float4*>(dst + row * kS + c4) = *reinterpret_cast<const float4*>(src + row * 64 + c4);
-  }
-}
-
 // 64 rows of a [.., L, 64] input starting at row c0 (rows >= L read as zero), widened to fp32.
 template <typename T>
 __device__ __forceinline__ void tile_rows(float* dst, const T* __restrict__ src, int64_t c0, int64_t L, int tid,
@@ -1273,14 +1265,14 @@ __global__ __launch_bounds__(256) void bwd_chunk_fwd_mfma_kernel(
   }
 }
 
-// Gradients of the per-chunk terms back to q, k, w, beta (the same outputs as bwd_prep_kernel<T, 64, 64>).
-// d qtilde, d ktilde, dS and dP are read straight from global memory (fp32 tiles, row stride 64); so is
-// A^{-1} when the forward-terms kernel stored it (Zi), else it is formed here by back substitution.
+// Gradients of the per-chunk terms back to q, k, w, beta (the same outputs as bwd_prep_kernel<T, 64, 64>),
+// fp32 inputs (bf16 ones take bwd_chunk_grad_tile_kernel).  d qtilde, d ktilde, dS and dP are read
+// straight from global memory (fp32 tiles, row stride 64); A^{-1} is formed here by back substitution.
 template <typename T>
 __global__ __launch_bounds__(512) void bwd_chunk_grad_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ w, const float* __restrict__ beta,
     const float* __restrict__ dqt, const float* __restrict__ dkt, const float* __restrict__ dPm,
-    const float* __restrict__ dSm, const float* __restrict__ Zi, int64_t L, int64_t M, T* __restrict__ dq,
+    const float* __restrict__ dSm, int64_t L, int64_t M, T* __restrict__ dq,
     T* __restrict__ dk, T* __restrict__ dw, float* __restrict__ dbeta) {
   extern __shared__ float sm[];
   float* S0 = sm;        // W
@@ -1308,8 +1300,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_mfma_kernel(
   if (tid < 128) dB[tid] = 0.f;
   chunk_setup<T, 2, 512>(q, k, w, beta, bh, c, L, S0, S1, S2, S3, S4, S5, Bs, tid, wv, lane, cb0);
   __syncthreads();
-  if (Zi != nullptr) tile_f32(S6, Zi + ((size_t)bh * M + c) * 64 * 64, tid, 512);
-  else unit_upper_inverse(S3, S6, tid);
+  unit_upper_inverse(S3, S6, tid);
   __syncthreads();
   for (int e = tid; e < 64 * 64; e += 512) S3[(e >> 6) * kS + (e & 63)] = S6[(e >> 6) * kS + (e & 63)] * Bs[e & 63];
   __syncthreads();
@@ -1830,7 +1821,6 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   };
   const int64_t G = bwd_band_chunks(M), NPB = bwd_band_pairs(M);
   if constexpr (D == 64 && C == 64) {  // the matrix cores: bf16 products for bf16 inputs, fp32 ones for fp32
-    if ((e = lds((const void*)bwd_chunk_grad_mfma_kernel<T>, kLdsChunkMfma)) != hipSuccess) return e;
     if constexpr (std::is_same<T, __bf16>::value) {  // the prefill's own per-chunk terms, and the tile kernels
       if ((e = mfma_prep_bwd_run(q, k, w, beta, logf, BH, L, scale * kLog2e, b.qt, b.kt, b.Pm, b.Sm, b.fl, b.ftot,
                                  b.Zi, st)) != hipSuccess)
@@ -1860,10 +1850,15 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     }
-    bwd_chunk_grad_mfma_kernel<T><<<grid, 512, kLdsChunkMfma, st>>>(
-        (const T*)q, (const T*)k, (const T*)w, beta, b.dqt, b.dkt, b.dPm, b.dSm,
-        std::is_same<T, __bf16>::value ? b.Zi : nullptr, L, M, (T*)dq, (T*)dk, (T*)dw, dbeta);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (std::is_same<T, __bf16>::value) {
+      if ((e = bwd_chunk_grad_tiles_run(q, k, w, beta, BH, L, b, dq, dk, dw, dbeta, st)) != hipSuccess) return e;
+    } else {
+      if ((e = lds((const void*)bwd_chunk_grad_mfma_kernel<T>, kLdsChunkMfma)) != hipSuccess) return e;
+      bwd_chunk_grad_mfma_kernel<T><<<grid, 512, kLdsChunkMfma, st>>>(
+          (const T*)q, (const T*)k, (const T*)w, beta, b.dqt, b.dkt, b.dPm, b.dSm, L, M, (T*)dq, (T*)dk,
+          (T*)dw, dbeta);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   } else {
     e = vec_run(1, std::is_same<T, __bf16>::value, D, C, q, k, v, w, beta, logf, nullptr, nullptr, BH, L, scale, b.qt,
                 b.kt, b.Pm, b.Sm, b.fl, b.ftot, st);
