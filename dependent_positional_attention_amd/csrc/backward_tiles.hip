@@ -532,71 +532,52 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
 //   dbeta = diag(M1) + rowsum(dA o W W^T),  dN = diag(beta) dA
 //   dW = -X dqtilde - Y^T dktilde - Ti W dP^T - Ti^T W dP + dU Q + dR^T K + (dN + dN^T) W
 //   dQ = dqtilde + dS K + dU^T W,   dK = dktilde + dS^T Q + dR W
-// Every LDS operand is a bf16 tile with permuted columns (swizzled): w, q and k exactly, the fp32
-// intermediates as hi + lo pairs split once when stored, so that a fragment in either orientation is one
-// LDS read (tile_frag by rows, tr_frag by columns) in the accumulator key order; d qtilde, d ktilde, dS
-// and dP are read from global memory in that order and split in registers.  Eight waves: wave 4h + w
-// works on rows 16 w .. 16 w + 15 and column blocks 2h, 2h + 1 of every product.
+// Every operand is a bf16 LDS tile with permuted columns (swizzled): w, q and k exactly, every fp32 matrix
+// (the inputs d qtilde, d ktilde, dS, dP, A^{-1} and the intermediates) as a hi + lo pair split once when
+// it is stored, so that a fragment in either orientation is one LDS read (tile_frag by rows, tr_frag by
+// columns) in the accumulator key order.  Eight waves: wave 4h + w works on rows 16 w .. 16 w + 15 and
+// column blocks 2h, 2h + 1 of every product.
 namespace {
 
 struct GradOp {
   const __bf16* hi;
-  const __bf16* lo;   // (split tiles)
-  const float* glob;  // (fp32 in global memory, row stride 64)
+  const __bf16* lo;  // (split tiles; unused for exact ones)
 };
-enum { kExact = 0, kSplit = 1, kGlobal = 2 };
 
 // fragment of rows (TR = false: M[base16 + r][k]) or columns (TR = true: M[k][base16 + r]), k in the
 // accumulator key order 32 ks + 16 (j / 4) + 4g + j % 4
-template <int KIND, bool TR>
+template <bool SPLIT, bool TR>
 __device__ __forceinline__ void grad_frag(const GradOp& o, int base16, int ks, bf16x8& h, bf16x8& l) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  if constexpr (KIND == kGlobal) {
-    float v[8];
-    if constexpr (!TR) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float4 x = *reinterpret_cast<const float4*>(o.glob + (base16 + r) * 64 + 32 * ks + 16 * hh + 4 * g);
-        v[4 * hh] = x.x, v[4 * hh + 1] = x.y, v[4 * hh + 2] = x.z, v[4 * hh + 3] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = o.glob[(32 * ks + 16 * (j >> 2) + 4 * g + (j & 3)) * 64 + base16 + r];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 hv = (__bf16)v[j];
-      h[j] = hv;
-      l[j] = (__bf16)(v[j] - (float)hv);
-    }
-  } else if constexpr (TR) {
+  if constexpr (TR) {
     h = tr_frag(o.hi, base16, ks, perm_pos);
-    if constexpr (KIND == kSplit) l = tr_frag(o.lo, base16, ks, perm_pos);
+    if constexpr (SPLIT) l = tr_frag(o.lo, base16, ks, perm_pos);
   } else {
     h = tile_frag(o.hi, base16 + r, 4 * ks + g);
-    if constexpr (KIND == kSplit) l = tile_frag(o.lo, base16 + r, 4 * ks + g);
+    if constexpr (SPLIT) l = tile_frag(o.lo, base16 + r, 4 * ks + g);
   }
 }
 
 // acc[c] += sum_k A(16w + r', k) B(k, 16(cb0 + c) + r''); AT: A(i, k) = A[k][i], else A[i][k]; BK:
 // B(k, j) = B[k][j], else B[j][k].  An exact operand contributes one bf16 product, a split one its hi and
 // lo parts (hi*hi + hi*lo + lo*hi; lo*lo dropped).
-template <int KA, bool AT, int KB, bool BK>
+template <bool SA, bool AT, bool SB, bool BK>
 __device__ __forceinline__ void gmm(f32x4 (&acc)[2], const GradOp& A, const GradOp& B, int w, int cb0) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     bf16x8 ah, al;
-    grad_frag<KA, AT>(A, 16 * w, ks, ah, al);
+    grad_frag<SA, AT>(A, 16 * w, ks, ah, al);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       bf16x8 bh, bl;
-      grad_frag<KB, BK>(B, 16 * (cb0 + c), ks, bh, bl);
+      grad_frag<SB, BK>(B, 16 * (cb0 + c), ks, bh, bl);
       acc[c] = mfma16(ah, bh, acc[c]);
-      if constexpr (KB != kExact) acc[c] = mfma16(ah, bl, acc[c]);
-      if constexpr (KA != kExact) acc[c] = mfma16(al, bh, acc[c]);
+      if constexpr (SB) acc[c] = mfma16(ah, bl, acc[c]);
+      if constexpr (SA) acc[c] = mfma16(al, bh, acc[c]);
     }
   }
 }
+constexpr bool kE = false, kS2 = true;  // exact / split operand
 
 __device__ __forceinline__ int tile_slot(int row, int col) {
   const int pp = perm_pos(col);
@@ -616,6 +597,23 @@ __device__ __forceinline__ void gstore(const f32x4 (&acc)[2], __bf16* hi, __bf16
       hi[tile_slot(i, j)] = hv;
       lo[tile_slot(i, j)] = (__bf16)(v - (float)hv);
     }
+}
+// a [64][64] fp32 matrix in global memory (row stride 64), times a per-column factor, into a split tile
+// pair (512 threads)
+template <bool COLSCALE>
+__device__ __forceinline__ void stage_split(__bf16* hi, __bf16* lo, const float* __restrict__ m, const float* cs,
+                                            int tid) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int e = tid + 512 * it, row = e >> 4, c4 = (e & 15) * 4;
+    float4 x = *reinterpret_cast<const float4*>(m + row * 64 + c4);
+    if constexpr (COLSCALE) x.x *= cs[c4], x.y *= cs[c4 + 1], x.z *= cs[c4 + 2], x.w *= cs[c4 + 3];
+    bf16x4 h, l;
+    split4(x.x, x.y, x.z, x.w, h, l);
+    const int sl = tile_slot(row, c4);
+    *reinterpret_cast<bf16x4*>(hi + sl) = h;
+    *reinterpret_cast<bf16x4*>(lo + sl) = l;
+  }
 }
 __device__ __forceinline__ void zero2(f32x4 (&acc)[2]) { acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ void sub2(f32x4 (&acc)[2], const f32x4 (&t)[2]) {
@@ -639,25 +637,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
     const float* __restrict__ dPm, const float* __restrict__ dSm, const float* __restrict__ Zi, int64_t L,
     int64_t M, __bf16* __restrict__ dq, __bf16* __restrict__ dk, __bf16* __restrict__ dw,
     float* __restrict__ dbeta) {
-  __shared__ __align__(1024) __bf16 te[3][kTile];     // W, Q, K (exact)
-  __shared__ __align__(1024) __bf16 ts[6][2][kTile];  // split pairs: Ti, U/dU/dTi, R/dR/M1, A^{-1}, X/dX/WdP/dN, Y/dY/WdP^T
+  __shared__ __align__(1024) __bf16 te[3][kTile];  // W, Q, K (exact)
+  // split pairs: Ti | U, dU, dTi | R, dR, M1 | dS, A^{-1} | X, dX, W dP, dN | Y, dY, W dP^T | dqtilde, dP | dktilde
+  __shared__ __align__(1024) __bf16 ts[8][2][kTile];
   __shared__ float Bs[64];
   __shared__ float dB[128];  // dbeta partials, one row of 64 per column half (each filled by single waves)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wv = wave & 3, cb0 = 2 * (wave >> 2);
   const int r = lane & 15, g = lane >> 4;
   const int64_t c = blockIdx.x, bh = blockIdx.y, Lp = M * 64;
   const size_t row0 = (size_t)bh * Lp + (size_t)c * 64;
-  const GradOp W{te[0], nullptr, nullptr}, Q{te[1], nullptr, nullptr}, K{te[2], nullptr, nullptr};
-  auto split = [&](int i) PA_INLINE { return GradOp{ts[i][0], ts[i][1], nullptr}; };
+  const GradOp W{te[0], nullptr}, Q{te[1], nullptr}, K{te[2], nullptr};
+  auto split = [&](int i) PA_INLINE { return GradOp{ts[i][0], ts[i][1]}; };
   const GradOp S3 = split(0), S4 = split(1), S5 = split(2), S6 = split(3), S7 = split(4), S8 = split(5);
-  const GradOp dQ{nullptr, nullptr, dqt + row0 * 64};                        // d qtilde  [a][x]
-  const GradOp dK{nullptr, nullptr, dkt + row0 * 64};                        // d ktilde  [b][x]
-  const GradOp dS{nullptr, nullptr, dSm + ((size_t)bh * M + c) * 64 * 64};  // dS        [a][b]
-  const GradOp dP{nullptr, nullptr, dPm + ((size_t)bh * M + c) * 64 * 64};  // dP        [x][y]
+  const GradOp dS = split(3), dQ = split(6), dP = split(6), dK = split(7);
+  const float* zc = Zi + ((size_t)bh * M + c) * 64 * 64;  // A^{-1}
+  const float* dSg = dSm + ((size_t)bh * M + c) * 64 * 64;
   auto keep = [](int, int, float x) { return x; };
   auto neg = [](int, int, float x) { return -x; };
 
-  // W, Q, K of the chunk (rows past L zero) and beta (padded tokens: identity)
+  // W, Q, K of the chunk (rows past L zero), beta (padded tokens: identity); Ti = A^{-1} diag(beta), and
+  // d qtilde, d ktilde, dS
   if (tid < 128) dB[tid] = 0.f;
   if (tid < 64) Bs[tid] = c * 64 + tid < L ? beta[bh * L + c * 64 + tid] : 0.f;
   {
@@ -670,101 +669,84 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
       *reinterpret_cast<bf16x4*>(te[t] + tile_slot(row, c4)) = tok < L ? v : bf16x4{};
     }
   }
+  stage_split<false>(ts[3][0], ts[3][1], dSg, nullptr, tid);
+  stage_split<false>(ts[6][0], ts[6][1], dqt + row0 * 64, nullptr, tid);
+  stage_split<false>(ts[7][0], ts[7][1], dkt + row0 * 64, nullptr, tid);
   __syncthreads();
-  // A^{-1} and Ti = A^{-1} diag(beta) (split); U (t <= a), R (s > b)
-  {
-    const float* zc = Zi + ((size_t)bh * M + c) * 64 * 64;
-    for (int e = tid; e < 64 * 16; e += 512) {
-      const int row = e >> 4, c4 = (e & 15) * 4;
-      const float4 z4 = *reinterpret_cast<const float4*>(zc + row * 64 + c4);
-      const float zv[4] = {z4.x, z4.y, z4.z, z4.w};
-      bf16x4 zh, zl, th, tl4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float tv = zv[i] * Bs[c4 + i];
-        zh[i] = (__bf16)zv[i];
-        zl[i] = (__bf16)(zv[i] - (float)zh[i]);
-        th[i] = (__bf16)tv;
-        tl4[i] = (__bf16)(tv - (float)th[i]);
-      }
-      const int sl = tile_slot(row, c4);
-      *reinterpret_cast<bf16x4*>(ts[3][0] + sl) = zh;
-      *reinterpret_cast<bf16x4*>(ts[3][1] + sl) = zl;
-      *reinterpret_cast<bf16x4*>(ts[0][0] + sl) = th;
-      *reinterpret_cast<bf16x4*>(ts[0][1] + sl) = tl4;
-    }
-  }
+  stage_split<true>(ts[0][0], ts[0][1], zc, Bs, tid);
   f32x4 aq[2], ak[2], aw[2], t[2], u[2], rU[2], rG[2];
   zero2(t);
-  gmm<kExact, false, kExact, false>(t, W, Q, wv, cb0);  // w_t . q_a
+  gmm<kE, false, kE, false>(t, W, Q, wv, cb0);  // w_t . q_a
   gstore(t, ts[1][0], ts[1][1], wv, cb0, [](int i, int j, float x) { return i <= j ? x : 0.f; });
   zero2(t);
-  gmm<kExact, false, kExact, false>(t, K, W, wv, cb0);  // k_b . w_s
+  gmm<kE, false, kE, false>(t, K, W, wv, cb0);  // k_b . w_s
   gstore(t, ts[2][0], ts[2][1], wv, cb0, [](int i, int j, float x) { return j > i ? x : 0.f; });
   __syncthreads();
 
-  glob_acc(aq, dQ.glob, wv, cb0);  // dq = d qtilde + ...
-  glob_acc(ak, dK.glob, wv, cb0);  // dk = d ktilde + ...
+  glob_acc(aq, dqt + row0 * 64, wv, cb0);  // dq = d qtilde + ...
+  glob_acc(ak, dkt + row0 * 64, wv, cb0);  // dk = d ktilde + ...
   zero2(aw);
   zero2(t);
-  gmm<kSplit, false, kSplit, true>(t, S3, S4, wv, cb0);  // X = Ti U
+  gmm<kS2, false, kS2, true>(t, S3, S4, wv, cb0);  // X = Ti U
   gstore(t, ts[4][0], ts[4][1], wv, cb0, keep);
   zero2(t);
-  gmm<kSplit, false, kSplit, true>(t, S5, S3, wv, cb0);  // Y = R Ti
+  gmm<kS2, false, kS2, true>(t, S5, S3, wv, cb0);  // Y = R Ti
   gstore(t, ts[5][0], ts[5][1], wv, cb0, keep);
-  gmm<kGlobal, false, kExact, true>(aq, dS, K, wv, cb0);  // dq += dS K
-  gmm<kGlobal, true, kExact, true>(ak, dS, Q, wv, cb0);   // dk += dS^T Q
+  gmm<kS2, false, kE, true>(aq, dS, K, wv, cb0);  // dq += dS K
+  gmm<kS2, true, kE, true>(ak, dS, Q, wv, cb0);   // dk += dS^T Q
   __syncthreads();
   zero2(t);
-  gmm<kSplit, false, kGlobal, true>(t, S7, dQ, wv, cb0);  // X dqtilde
-  gmm<kSplit, true, kGlobal, true>(t, S8, dK, wv, cb0);   // + Y^T dktilde
+  gmm<kS2, false, kS2, true>(t, S7, dQ, wv, cb0);  // X dqtilde
+  gmm<kS2, true, kS2, true>(t, S8, dK, wv, cb0);   // + Y^T dktilde
   sub2(aw, t);
   zero2(u);
-  gmm<kExact, false, kGlobal, false>(u, W, dQ, wv, cb0);  // -dX = W dqtilde^T
+  gmm<kE, false, kS2, false>(u, W, dQ, wv, cb0);  // -dX = W dqtilde^T
   zero2(t);
-  gmm<kGlobal, false, kExact, false>(t, dK, W, wv, cb0);  // -dY = dktilde W^T
-  gmm<kGlobal, true, kSplit, false>(t, dS, S4, wv, cb0);  //       + dS^T U^T
+  gmm<kS2, false, kE, false>(t, dK, W, wv, cb0);   // -dY = dktilde W^T
+  gmm<kS2, true, kS2, false>(t, dS, S4, wv, cb0);  //       + dS^T U^T
   zero2(rU);
-  gmm<kSplit, true, kGlobal, false>(rU, S8, dS, wv, cb0);  // (dS Y)^T
+  gmm<kS2, true, kS2, false>(rU, S8, dS, wv, cb0);  // (dS Y)^T
   __syncthreads();
   gstore(u, ts[4][0], ts[4][1], wv, cb0, neg);  // dX
   gstore(t, ts[5][0], ts[5][1], wv, cb0, neg);  // dY
+  stage_split<false>(ts[6][0], ts[6][1], dPm + ((size_t)bh * M + c) * 64 * 64, nullptr, tid);  // dP
+  stage_split<false>(ts[3][0], ts[3][1], zc, nullptr, tid);                                    // A^{-1}
   __syncthreads();
   zero2(u);
-  gmm<kSplit, true, kSplit, true>(u, S3, S7, wv, cb0);  // dU = Ti^T dX - (dS Y)^T
+  gmm<kS2, true, kS2, true>(u, S3, S7, wv, cb0);  // dU = Ti^T dX - (dS Y)^T
   sub2(u, rU);
   zero2(rG);
-  gmm<kSplit, false, kSplit, false>(rG, S7, S4, wv, cb0);  // dTi = dX U^T
-  gmm<kSplit, true, kSplit, true>(rG, S5, S8, wv, cb0);    //     + R^T dY
+  gmm<kS2, false, kS2, false>(rG, S7, S4, wv, cb0);  // dTi = dX U^T
+  gmm<kS2, true, kS2, true>(rG, S5, S8, wv, cb0);    //     + R^T dY
   zero2(t);
-  gmm<kSplit, false, kSplit, false>(t, S8, S3, wv, cb0);  // dR = dY Ti^T
+  gmm<kS2, false, kS2, false>(t, S8, S3, wv, cb0);  // dR = dY Ti^T
   __syncthreads();
   gstore(u, ts[1][0], ts[1][1], wv, cb0, [](int i, int j, float x) { return i <= j ? x : 0.f; });
   gstore(t, ts[2][0], ts[2][1], wv, cb0, [](int i, int j, float x) { return j > i ? x : 0.f; });
   __syncthreads();
-  gmm<kSplit, false, kExact, true>(aw, S4, Q, wv, cb0);  // dW += dU Q
-  gmm<kSplit, true, kExact, true>(aw, S5, K, wv, cb0);   //     + dR^T K
-  gmm<kSplit, true, kExact, true>(aq, S4, W, wv, cb0);   // dq += dU^T W
-  gmm<kSplit, false, kExact, true>(ak, S5, W, wv, cb0);  // dk += dR W
+  gmm<kS2, false, kE, true>(aw, S4, Q, wv, cb0);  // dW += dU Q
+  gmm<kS2, true, kE, true>(aw, S5, K, wv, cb0);   //     + dR^T K
+  gmm<kS2, true, kE, true>(aq, S4, W, wv, cb0);   // dq += dU^T W
+  gmm<kS2, false, kE, true>(ak, S5, W, wv, cb0);  // dk += dR W
   zero2(t);
-  gmm<kExact, false, kGlobal, true>(t, W, dP, wv, cb0);  // W dP
+  gmm<kE, false, kS2, true>(t, W, dP, wv, cb0);  // W dP
   zero2(u);
-  gmm<kExact, false, kGlobal, false>(u, W, dP, wv, cb0);  // W dP^T
+  gmm<kE, false, kS2, false>(u, W, dP, wv, cb0);  // W dP^T
   gstore(t, ts[4][0], ts[4][1], wv, cb0, keep);
   gstore(u, ts[5][0], ts[5][1], wv, cb0, keep);
   __syncthreads();
   zero2(t);
-  gmm<kSplit, false, kExact, false>(t, S7, W, wv, cb0);  // dTi -= W dP W^T
+  gmm<kS2, false, kE, false>(t, S7, W, wv, cb0);  // dTi -= W dP W^T
   sub2(rG, t);
   zero2(t);
-  gmm<kSplit, false, kSplit, true>(t, S3, S8, wv, cb0);  // dW -= Ti W dP^T
-  gmm<kSplit, true, kSplit, true>(t, S3, S7, wv, cb0);   //      + Ti^T W dP
+  gmm<kS2, false, kS2, true>(t, S3, S8, wv, cb0);  // dW -= Ti W dP^T
+  gmm<kS2, true, kS2, true>(t, S3, S7, wv, cb0);   //      + Ti^T W dP
   sub2(aw, t);
   __syncthreads();
   gstore(rG, ts[1][0], ts[1][1], wv, cb0, keep);
   __syncthreads();
   zero2(t);
-  gmm<kSplit, true, kSplit, true>(t, S6, S4, wv, cb0);  // M1 = A^{-T} dTi; dbeta += diag(M1)
+  gmm<kS2, true, kS2, true>(t, S6, S4, wv, cb0);  // M1 = A^{-T} dTi; dbeta += diag(M1)
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -773,9 +755,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   gstore(t, ts[2][0], ts[2][1], wv, cb0, keep);
   __syncthreads();
   zero2(t);
-  gmm<kSplit, false, kSplit, false>(t, S5, S3, wv, cb0);  // M1 Ti^T
+  gmm<kS2, false, kS2, false>(t, S5, S3, wv, cb0);  // M1 Ti^T
   zero2(u);
-  gmm<kExact, false, kExact, false>(u, W, W, wv, cb0);  // w_r . w_s
+  gmm<kE, false, kE, false>(u, W, W, wv, cb0);  // w_r . w_s
   {
     float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -799,8 +781,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   }
   gstore(t, ts[4][0], ts[4][1], wv, cb0, keep);
   __syncthreads();
-  gmm<kSplit, false, kExact, true>(aw, S7, W, wv, cb0);  // dW += dN W
-  gmm<kSplit, true, kExact, true>(aw, S7, W, wv, cb0);   //      + dN^T W
+  gmm<kS2, false, kE, true>(aw, S7, W, wv, cb0);  // dW += dN W
+  gmm<kS2, true, kE, true>(aw, S7, W, wv, cb0);   //      + dN^T W
   __syncthreads();
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
