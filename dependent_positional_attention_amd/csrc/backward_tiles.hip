@@ -271,8 +271,8 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
         rs += dz;
         gt[t][i] = kLn2 * dz;
       }
-    bf16x8 gh[2], gl[2];
-    acc_to_op(gt, gh, gl);
+    bf16x8 gh[2];
+    acc_to_bf(gt, gh);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       f32x4 acc = zero;
@@ -280,7 +280,6 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 kx = tr_frag(Kt, 16 * dt, ks, perm_pos);  // ktilde_n^T rows d = 16 dt + r, k = keys
         acc = mfma16(kx, gh[ks], acc);
-        acc = mfma16(kx, gl[ks], acc);
       }
       if (n > 0) {
 #pragma unroll
@@ -366,17 +365,16 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
     for (int xt = 0; xt < 4; ++xt) aV[xt] = aK[xt] = aP[xt] = zero;
   }
 
-  // p (or g) of a step as the k = queries operand, hi + lo
+  // p of a step as the k = queries operand (bf16)
   auto dv_update = [&](const __bf16* Ot, const f32x4 (&pt)[4]) PA_INLINE {
-    bf16x8 ph[2], pl[2];
-    acc_to_op(pt, ph, pl);
+    bf16x8 ph[2];
+    acc_to_bf(pt, ph);
 #pragma unroll
     for (int xt = 0; xt < 4; ++xt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 ox = tr_frag(Ot, 16 * xt, ks, col_identity);  // dO_m^T rows x = 16 xt + r, k = queries
         aV[xt] = mfma16(ox, ph[ks], aV[xt]);
-        aV[xt] = mfma16(ox, pl[ks], aV[xt]);
       }
   };
   auto stage_rows = [&](int64_t mm, int s) PA_INLINE {
@@ -472,15 +470,14 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
       (void)zt;
       dv_update(Ot, pt);
       {
-        bf16x8 gh[2], gl[2];
-        acc_to_op(gt, gh, gl);
+        bf16x8 gh[2];
+        acc_to_bf(gt, gh);
 #pragma unroll
         for (int xt = 0; xt < 4; ++xt)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const bf16x8 rx = tr_frag(Rt, 16 * xt, ks, perm_pos);  // r^T rows x = 16 xt + r, k = queries
             aK[xt] = mfma16(rx, gh[ks], aK[xt]);
-            aK[xt] = mfma16(rx, gl[ks], aK[xt]);
           }
       }
       if (trans) {

@@ -130,6 +130,14 @@ __device__ __forceinline__ void acc_to_op(const f32x4 (&acc)[4], bf16x8 (&hi)[2]
     }
 }
 
+// The same operand rounded to bf16 once (no lo part).
+__device__ __forceinline__ void acc_to_bf(const f32x4 (&acc)[4], bf16x8 (&hi)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hi[ks][j] = (__bf16)acc[2 * ks + (j >> 2)][j & 3];
+}
+
 // In-chunk logits S of the bf16 forms, packed: only entries on or below the diagonal are ever read, so
 // row a keeps its 4-float groups 0 .. a/4 (columns 0 .. 4(a/4) + 3; the entries of the last group
 // past the diagonal are unspecified), rows back to back.  Row a starts at group

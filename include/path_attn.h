@@ -333,8 +333,11 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
  * bf16 inputs at d = chunk = 64 the matrix products run on the bf16 matrix
  * cores from the prefill's own per-chunk terms (bf16 transport form): the
  * running queries are rounded to bf16 after every chunk transition as in the
- * forward, other fp32 operands are split into hi + lo bf16 (about 2^-16
- * relative); fp32 inputs keep fp32 products throughout.
+ * forward; the probabilities p and logit gradients dz enter their products
+ * (dv, dktilde and the incoming state gradient) rounded to bf16 once, as
+ * flash-attention backward kernels round P and dS; other fp32 operands are
+ * split into hi + lo bf16 (about 2^-16 relative); fp32 inputs keep fp32
+ * products throughout.
  * Workspace: path_attn_bwd_workspace_bytes; it grows as B*H*L*d*sqrt(L/chunk)
  * (two vectors per key of every chunk pair of one band, bf16 for bf16 inputs:
  * about 4.4 GB at B=8, H=24, L=4096, d=64, chunk 64 and 10.4 GB at B=1, H=24,
