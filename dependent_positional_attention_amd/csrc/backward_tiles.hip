@@ -555,17 +555,26 @@ __device__ __forceinline__ void grad_frag(const GradOp& o, int base16, int ks, b
   }
 }
 
+#ifndef PATHATTN_GRAD_WAVES
+#define PATHATTN_GRAD_WAVES 8
+#endif
+// Waves of the per-chunk gradient kernel: 4 row blocks x (waves / 4) column groups of 16 / (waves / 4) * 16
+// columns each.
+constexpr int kGradWaves = PATHATTN_GRAD_WAVES, kGradThreads = 64 * kGradWaves;
+constexpr int kGradGroups = kGradWaves / 4, kGradNc = 4 / kGradGroups;
+static_assert(kGradWaves == 8 || kGradWaves == 16, "gradient kernel waves");
+
 // acc[c] += sum_k A(16w + r', k) B(k, 16(cb0 + c) + r''); AT: A(i, k) = A[k][i], else A[i][k]; BK:
 // B(k, j) = B[k][j], else B[j][k].  An exact operand contributes one bf16 product, a split one its hi and
 // lo parts (hi*hi + hi*lo + lo*hi; lo*lo dropped).
 template <bool SA, bool AT, bool SB, bool BK>
-__device__ __forceinline__ void gmm(f32x4 (&acc)[2], const GradOp& A, const GradOp& B, int w, int cb0) {
+__device__ __forceinline__ void gmm(f32x4 (&acc)[kGradNc], const GradOp& A, const GradOp& B, int w, int cb0) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     bf16x8 ah, al;
     grad_frag<SA, AT>(A, 16 * w, ks, ah, al);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < kGradNc; ++c) {
       bf16x8 bh, bl;
       grad_frag<SB, BK>(B, 16 * (cb0 + c), ks, bh, bl);
       acc[c] = mfma16(ah, bh, acc[c]);
@@ -582,10 +591,10 @@ __device__ __forceinline__ int tile_slot(int row, int col) {
 }
 // accumulator (rows 16w + 4g + e, columns 16(cb0 + c) + r) -> split tile pair, through f(i, j, x)
 template <typename F>
-__device__ __forceinline__ void gstore(const f32x4 (&acc)[2], __bf16* hi, __bf16* lo, int w, int cb0, F f) {
+__device__ __forceinline__ void gstore(const f32x4 (&acc)[kGradNc], __bf16* hi, __bf16* lo, int w, int cb0, F f) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < kGradNc; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * w + 4 * g + e, j = 16 * (cb0 + c) + r;
@@ -595,15 +604,23 @@ __device__ __forceinline__ void gstore(const f32x4 (&acc)[2], __bf16* hi, __bf16
       lo[tile_slot(i, j)] = (__bf16)(v - (float)hv);
     }
 }
-// a [64][64] fp32 matrix in global memory (row stride 64), times a per-column factor, into a split tile
-// pair (512 threads)
-template <bool COLSCALE>
-__device__ __forceinline__ void stage_split(__bf16* hi, __bf16* lo, const float* __restrict__ m, const float* cs,
-                                            int tid) {
+// A [64][64] fp32 matrix in global memory (row stride 64) as float4 pieces held by the block's threads
+// (piece tid + kGradThreads it), and those pieces, times a per-column factor, into a split tile pair.
+constexpr int kGradPieces = 1024 / kGradThreads;
+__device__ __forceinline__ void load_pieces(float4 (&f)[kGradPieces], const float* __restrict__ m, int tid) {
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int e = tid + 512 * it, row = e >> 4, c4 = (e & 15) * 4;
-    float4 x = *reinterpret_cast<const float4*>(m + row * 64 + c4);
+  for (int it = 0; it < kGradPieces; ++it) {
+    const int e = tid + kGradThreads * it;
+    f[it] = *reinterpret_cast<const float4*>(m + (e >> 4) * 64 + (e & 15) * 4);
+  }
+}
+template <bool COLSCALE>
+__device__ __forceinline__ void put_split(__bf16* hi, __bf16* lo, const float4 (&f)[kGradPieces], const float* cs,
+                                          int tid) {
+#pragma unroll
+  for (int it = 0; it < kGradPieces; ++it) {
+    const int e = tid + kGradThreads * it, row = e >> 4, c4 = (e & 15) * 4;
+    float4 x = f[it];
     if constexpr (COLSCALE) x.x *= cs[c4], x.y *= cs[c4 + 1], x.z *= cs[c4 + 2], x.w *= cs[c4 + 3];
     bf16x4 h, l;
     split4(x.x, x.y, x.z, x.w, h, l);
@@ -612,23 +629,26 @@ __device__ __forceinline__ void stage_split(__bf16* hi, __bf16* lo, const float*
     *reinterpret_cast<bf16x4*>(lo + sl) = l;
   }
 }
-__device__ __forceinline__ void zero2(f32x4 (&acc)[2]) { acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ void sub2(f32x4 (&acc)[2], const f32x4 (&t)[2]) {
-  acc[0] -= t[0];
-  acc[1] -= t[1];
+__device__ __forceinline__ void zero2(f32x4 (&acc)[kGradNc]) {
+#pragma unroll
+  for (int c = 0; c < kGradNc; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+__device__ __forceinline__ void sub2(f32x4 (&acc)[kGradNc], const f32x4 (&t)[kGradNc]) {
+#pragma unroll
+  for (int c = 0; c < kGradNc; ++c) acc[c] -= t[c];
 }
 // rows of a global fp32 [64][64] matrix into the accumulator layout
-__device__ __forceinline__ void glob_acc(f32x4 (&acc)[2], const float* m, int w, int cb0) {
+__device__ __forceinline__ void glob_acc(f32x4 (&acc)[kGradNc], const float* m, int w, int cb0) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < kGradNc; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[c][e] = m[(16 * w + 4 * g + e) * 64 + 16 * (cb0 + c) + r];
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
+__global__ __launch_bounds__(kGradThreads) void bwd_chunk_grad_tile_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ w,
     const float* __restrict__ beta, const float* __restrict__ dqt, const float* __restrict__ dkt,
     const float* __restrict__ dPm, const float* __restrict__ dSm, const float* __restrict__ Zi, int64_t L,
@@ -638,8 +658,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   // split pairs: Ti | U, dU, dTi | R, dR, M1 | dS, A^{-1} | X, dX, W dP, dN | Y, dY, W dP^T | dqtilde, dP | dktilde
   __shared__ __align__(1024) __bf16 ts[8][2][kTile];
   __shared__ float Bs[64];
-  __shared__ float dB[128];  // dbeta partials, one row of 64 per column half (each filled by single waves)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wv = wave & 3, cb0 = 2 * (wave >> 2);
+  __shared__ float dB[64 * kGradGroups];  // dbeta partials, one row of 64 per column group (each address
+                                         // filled by a single wave)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wv = wave & 3, cgrp = wave >> 2, cb0 = kGradNc * cgrp;
   const int r = lane & 15, g = lane >> 4;
   const int64_t c = blockIdx.x, bh = blockIdx.y, Lp = M * 64;
   const size_t row0 = (size_t)bh * Lp + (size_t)c * 64;
@@ -652,26 +673,45 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   auto keep = [](int, int, float x) { return x; };
   auto neg = [](int, int, float x) { return -x; };
 
-  // W, Q, K of the chunk (rows past L zero), beta (padded tokens: identity); Ti = A^{-1} diag(beta), and
-  // d qtilde, d ktilde, dS
-  if (tid < 128) dB[tid] = 0.f;
-  if (tid < 64) Bs[tid] = c * 64 + tid < L ? beta[bh * L + c * 64 + tid] : 0.f;
+  // Every global input of the first phases is requested before any is waited for (one memory round
+  // trip): W, Q, K of the chunk (rows past L zero), beta (padded tokens: identity), d qtilde, d ktilde,
+  // dS, A^{-1} and the rows of d qtilde, d ktilde that seed dq, dk; dP follows once the first tiles
+  // are stored, and A^{-1} stays in registers until its tile is free.
+  constexpr int kWqk = 3 * 1024 / kGradThreads;  // bf16x4 pieces of W, Q, K per thread
+  bf16x4 wqk[kWqk];
   {
     const size_t base = (size_t)bh * L * 64;
-    for (int e = tid; e < 3 * 64 * 16; e += 512) {
-      const int t = e >> 10, row = (e >> 4) & 63, c4 = (e & 15) * 4;
-      const __bf16* src = t == 0 ? w : (t == 1 ? q : k);
+#pragma unroll
+    for (int i = 0; i < kWqk; ++i) {
+      const int e = tid + kGradThreads * i, tt = e >> 10, row = (e >> 4) & 63, c4 = (e & 15) * 4;
+      const __bf16* src = tt == 0 ? w : (tt == 1 ? q : k);
       const int64_t tok = c * 64 + row;
-      const bf16x4 v = *reinterpret_cast<const bf16x4*>(src + base + (size_t)(tok < L ? tok : L - 1) * 64 + c4);
-      *reinterpret_cast<bf16x4*>(te[t] + tile_slot(row, c4)) = tok < L ? v : bf16x4{};
+      wqk[i] = *reinterpret_cast<const bf16x4*>(src + base + (size_t)(tok < L ? tok : L - 1) * 64 + c4);
     }
   }
-  stage_split<false>(ts[3][0], ts[3][1], dSg, nullptr, tid);
-  stage_split<false>(ts[6][0], ts[6][1], dqt + row0 * 64, nullptr, tid);
-  stage_split<false>(ts[7][0], ts[7][1], dkt + row0 * 64, nullptr, tid);
+  float bv = 0.f;
+  if (tid < 64) bv = beta[bh * L + (c * 64 + tid < L ? c * 64 + tid : L - 1)];
+  float4 fS[kGradPieces], fQ[kGradPieces], fK[kGradPieces], fZ[kGradPieces], fP[kGradPieces];
+  load_pieces(fS, dSg, tid);
+  load_pieces(fQ, dqt + row0 * 64, tid);
+  load_pieces(fK, dkt + row0 * 64, tid);
+  load_pieces(fZ, zc, tid);
+  f32x4 aq[kGradNc], ak[kGradNc], aw[kGradNc], t[kGradNc], u[kGradNc], rU[kGradNc], rG[kGradNc];
+  glob_acc(aq, dqt + row0 * 64, wv, cb0);  // dq = d qtilde + ...
+  glob_acc(ak, dkt + row0 * 64, wv, cb0);  // dk = d ktilde + ...
+  if (tid < 64 * kGradGroups) dB[tid] = 0.f;
+  if (tid < 64) Bs[tid] = c * 64 + tid < L ? bv : 0.f;
+#pragma unroll
+  for (int i = 0; i < kWqk; ++i) {
+    const int e = tid + kGradThreads * i, tt = e >> 10, row = (e >> 4) & 63, c4 = (e & 15) * 4;
+    *reinterpret_cast<bf16x4*>(te[tt] + tile_slot(row, c4)) = c * 64 + row < L ? wqk[i] : bf16x4{};
+  }
+  put_split<false>(ts[3][0], ts[3][1], fS, nullptr, tid);
+  put_split<false>(ts[6][0], ts[6][1], fQ, nullptr, tid);
+  put_split<false>(ts[7][0], ts[7][1], fK, nullptr, tid);
   __syncthreads();
-  stage_split<true>(ts[0][0], ts[0][1], zc, Bs, tid);
-  f32x4 aq[2], ak[2], aw[2], t[2], u[2], rU[2], rG[2];
+  load_pieces(fP, dPm + ((size_t)bh * M + c) * 64 * 64, tid);
+  put_split<true>(ts[0][0], ts[0][1], fZ, Bs, tid);  // Ti = A^{-1} diag(beta)
   zero2(t);
   gmm<kE, false, kE, false>(t, W, Q, wv, cb0);  // w_t . q_a
   gstore(t, ts[1][0], ts[1][1], wv, cb0, [](int i, int j, float x) { return i <= j ? x : 0.f; });
@@ -680,8 +720,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   gstore(t, ts[2][0], ts[2][1], wv, cb0, [](int i, int j, float x) { return j > i ? x : 0.f; });
   __syncthreads();
 
-  glob_acc(aq, dqt + row0 * 64, wv, cb0);  // dq = d qtilde + ...
-  glob_acc(ak, dkt + row0 * 64, wv, cb0);  // dk = d ktilde + ...
   zero2(aw);
   zero2(t);
   gmm<kS2, false, kS2, true>(t, S3, S4, wv, cb0);  // X = Ti U
@@ -706,8 +744,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   __syncthreads();
   gstore(u, ts[4][0], ts[4][1], wv, cb0, neg);  // dX
   gstore(t, ts[5][0], ts[5][1], wv, cb0, neg);  // dY
-  stage_split<false>(ts[6][0], ts[6][1], dPm + ((size_t)bh * M + c) * 64 * 64, nullptr, tid);  // dP
-  stage_split<false>(ts[3][0], ts[3][1], zc, nullptr, tid);                                    // A^{-1}
+  put_split<false>(ts[6][0], ts[6][1], fP, nullptr, tid);  // dP
+  put_split<false>(ts[3][0], ts[3][1], fZ, nullptr, tid);  // A^{-1}
   __syncthreads();
   zero2(u);
   gmm<kS2, true, kS2, true>(u, S3, S7, wv, cb0);  // dU = Ti^T dX - (dS Y)^T
@@ -745,10 +783,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   zero2(t);
   gmm<kS2, true, kS2, true>(t, S6, S4, wv, cb0);  // M1 = A^{-T} dTi; dbeta += diag(M1)
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
+  for (int cc = 0; cc < kGradNc; ++cc)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (16 * wv + 4 * g + e == 16 * (cb0 + cc) + r) atomicAdd(&dB[32 * cb0 + 16 * (cb0 + cc) + r], t[cc][e]);
+      if (16 * wv + 4 * g + e == 16 * (cb0 + cc) + r) atomicAdd(&dB[64 * cgrp + 16 * (cb0 + cc) + r], t[cc][e]);
   gstore(t, ts[2][0], ts[2][1], wv, cb0, keep);
   __syncthreads();
   zero2(t);
@@ -758,7 +796,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   {
     float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int cc = 0; cc < kGradNc; ++cc)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * wv + 4 * g + e, j = 16 * (cb0 + cc) + r;
@@ -773,7 +811,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
       x += __shfl_xor(x, 2);
       x += __shfl_xor(x, 4);
       x += __shfl_xor(x, 8);
-      if (r == 0) atomicAdd(&dB[32 * cb0 + 16 * wv + 4 * g + e], x);
+      if (r == 0) atomicAdd(&dB[64 * cgrp + 16 * wv + 4 * g + e], x);
     }
   }
   gstore(t, ts[4][0], ts[4][1], wv, cb0, keep);
@@ -782,7 +820,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
   gmm<kS2, true, kE, true>(aw, S7, W, wv, cb0);   //      + dN^T W
   __syncthreads();
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
+  for (int cc = 0; cc < kGradNc; ++cc)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int a = 16 * wv + 4 * g + e, x = 16 * (cb0 + cc) + r;
@@ -794,14 +832,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_tile_kernel(
         dw[o] = (__bf16)aw[cc][e];
       }
     }
-  if (tid < 64 && c * 64 + tid < L) dbeta[bh * L + c * 64 + tid] = dB[tid] + dB[64 + tid];
+  if (tid < 64 && c * 64 + tid < L) {
+    float sb = dB[tid];
+#pragma unroll
+    for (int h = 1; h < kGradGroups; ++h) sb += dB[64 * h + tid];
+    dbeta[bh * L + c * 64 + tid] = sb;
+  }
 }
 
 hipError_t bwd_chunk_grad_tiles_run(const void* q, const void* k, const void* w, const float* beta, int64_t BH,
                                     int64_t L, const bwd_buffers& b, void* dq, void* dk, void* dw, float* dbeta,
                                     hipStream_t st) {
   const int64_t M = (L + 63) / 64;
-  bwd_chunk_grad_tile_kernel<<<dim3((unsigned)M, (unsigned)BH), 512, 0, st>>>(
+  bwd_chunk_grad_tile_kernel<<<dim3((unsigned)M, (unsigned)BH), kGradThreads, 0, st>>>(
       (const __bf16*)q, (const __bf16*)k, (const __bf16*)w, beta, b.dqt, b.dkt, b.dPm, b.dSm, b.Zi, L, M,
       (__bf16*)dq, (__bf16*)dk, (__bf16*)dw, dbeta);
   return hipGetLastError();
