@@ -14,6 +14,8 @@
 // store per lane and k-step, and the key-side kernel reads them back as row fragments (tile_frag) and
 // as column fragments (LDS transpose reads, tr_frag).  ktilde, V and P stream through a ring of three
 // LDS slots filled by direct global->LDS copies, as in the prefill's scan.
+#include <type_traits>
+
 #include "backward.h"
 #include "tiles.h"
 
@@ -34,6 +36,32 @@ __device__ __forceinline__ void row_to_lds(float* dst, const float* src, int wav
   if (l < 16)
     __builtin_amdgcn_global_load_lds((const void*)(src + 16 * wave + l), (lds_void*)(dst + 16 * wave), 4, 0, 0);
 }
+
+// One slot of the chunk-pair kernels' LDS ring: three tiles and two 64-float rows, each an LDS variable
+// of its own.  The ring loops are unrolled over the slots, so each LDS access names its variable at
+// compile time, and an address is at most a few steps from it: the compiler then keeps the variable's
+// alias scope on the access, sees that a transpose read of one slot cannot touch the copies still in
+// flight into the others, and does not drain them before it.  (A read whose scope is lost waits for
+// every copy in flight.)
+struct PairSlot {
+  __bf16* t[kPairTiles];
+  float* rows[2];
+};
+#define PA_PAIR_RING_LDS(name)                                                                          \
+  __shared__ __align__(1024) __bf16 name##_t00[kTile], name##_t01[kTile], name##_t02[kTile];          \
+  __shared__ __align__(1024) __bf16 name##_t10[kTile], name##_t11[kTile], name##_t12[kTile];          \
+  __shared__ __align__(1024) __bf16 name##_t20[kTile], name##_t21[kTile], name##_t22[kTile];          \
+  __shared__ __align__(16) float name##_r00[64], name##_r01[64], name##_r10[64], name##_r11[64],     \
+      name##_r20[64], name##_r21[64];                                                                 \
+  auto name = [&](auto S) PA_INLINE -> PairSlot {                                                     \
+    constexpr int sidx = decltype(S)::value;                                                          \
+    static_assert(sidx >= 0 && sidx < kRingSlots, "ring slot");                                       \
+    if constexpr (sidx == 0) return PairSlot{{name##_t00, name##_t01, name##_t02}, {name##_r00, name##_r01}}; \
+    else if constexpr (sidx == 1) return PairSlot{{name##_t10, name##_t11, name##_t12}, {name##_r10, name##_r11}}; \
+    else return PairSlot{{name##_t20, name##_t21, name##_t22}, {name##_r20, name##_r21}};             \
+  }
+template <int S>
+using slot_c = std::integral_constant<int, S>;
 
 }  // namespace
 
@@ -319,8 +347,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
     const float* __restrict__ Dw, int64_t L, int64_t M, pair_band band, __bf16* __restrict__ dv,
     float* __restrict__ dva, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol,
     int64_t BH) {
-  __shared__ __align__(1024) __bf16 tl[kRingSlots][kPairTiles][kTile];  // r^(n)_m, dr^(n-1)_m, dO_m
-  __shared__ __align__(16) float ts[kRingSlots][2][64];                  // lse2 and D rows of chunk m
+  // ring slots: r^(n)_m, dr^(n-1)_m, dO_m tiles; lse2 and D rows of chunk m
+  PA_PAIR_RING_LDS(ring);
 
   int64_t bh, n;
   if (!bwd_pair_block(BH, band.me, bh, n)) return;  // whole block; low key chunks first
@@ -377,19 +405,20 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
         aV[xt] = mfma16(ox, ph[ks], aV[xt]);
       }
   };
-  auto stage_rows = [&](int64_t mm, int s) PA_INLINE {
+  auto stage_rows = [&](int64_t mm, const PairSlot& sl) PA_INLINE {
     const int64_t vr = L - mm * 64;
-    dma_tile<2>(tl[s][2], dout + ((size_t)bh * L + (size_t)mm * 64) * 64, vr < 64 ? (int)vr : 64, i0);
-    row_to_lds(ts[s][0], lse2w + (size_t)bh * Lp + (size_t)mm * 64, wave, l);
-    row_to_lds(ts[s][1], Dw + (size_t)bh * Lp + (size_t)mm * 64, wave, l);
+    dma_tile<2>(sl.t[2], dout + ((size_t)bh * L + (size_t)mm * 64) * 64, vr < 64 ? (int)vr : 64, i0);
+    row_to_lds(sl.rows[0], lse2w + (size_t)bh * Lp + (size_t)mm * 64, wave, l);
+    row_to_lds(sl.rows[1], Dw + (size_t)bh * Lp + (size_t)mm * 64, wave, l);
   };
 
   // in-chunk block (m = n): logits from the packed S; dv only
   if (first) {
-    stage_rows(n, 0);
+    const PairSlot s0 = ring(slot_c<0>{});
+    stage_rows(n, s0);
     wait_vm<0>();
     lds_barrier();
-    const __bf16* Ot = tl[0][2];
+    const __bf16* Ot = s0.t[2];
     const float* Sb = Sm + ((size_t)bh * M + (size_t)n) * kSGroups * 4;
     f32x4 pt[4];
 #pragma unroll
@@ -400,12 +429,13 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int a = 16 * qt + 4 * g + i;
-        float p = 0.f, dz = 0.f;
-        if (b <= a) {
-          const float z2 = Sb[s_row_group(a) * 4 + b] - (FOX ? kLog2e * Fb : 0.f);
-          p = fast_exp2(z2 - ts[0][0][a]);
-          dz = p * (dp[i] - ts[0][1][a]);
-        }
+        // every lane loads (entries past the diagonal read the diagonal's), then selects: no load waits
+        // inside a branch
+        const float sab = Sb[s_row_group(a) * 4 + (b <= a ? b : a)];
+        const float z2 = sab - (FOX ? kLog2e * Fb : 0.f);
+        const float pe = fast_exp2(z2 - s0.rows[0][a]);
+        const float p = b <= a ? pe : 0.f;
+        const float dz = p * (dp[i] - s0.rows[1][a]);
         cs += dz;
         pt[qt][i] = p;
       }
@@ -418,33 +448,35 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
   const int64_t m0 = n + 1 > band.mb ? n + 1 : band.mb;
   const int64_t steps = band.me - m0;
   if (steps > 0) {
-    auto stage = [&](int64_t k, int s) PA_INLINE {
+    auto stage = [&](int64_t k, const PairSlot& sl) PA_INLINE {
       const int64_t mm = m0 + k;
       const size_t pr = band.slot(bh, mm, n);
-      dma_tile<2>(tl[s][0], St + pr * 4096, 64, i0);
-      dma_tile<2>(tl[s][1], Gst + pr * 4096, 64, i0);  // (not written for n = 0: copied, not used)
-      stage_rows(mm, s);
+      dma_tile<2>(sl.t[0], St + pr * 4096, 64, i0);
+      dma_tile<2>(sl.t[1], Gst + pr * 4096, 64, i0);  // (not written for n = 0: copied, not used)
+      stage_rows(mm, sl);
     };
     constexpr int OPS = slot_ops<2>();
     float offn = FOX ? Off[band.slot(bh, m0, n)] : 0.f;
-    stage(0, 0);
+    stage(0, ring(slot_c<0>{}));
     if (steps > 1) {
-      stage(1, 1);
+      stage(1, ring(slot_c<1>{}));
       wait_vm<OPS>();
     } else {
       wait_vm<0>();
     }
     lds_barrier();
-    int cur = 0;
-    for (int64_t k = 0; k < steps; ++k) {
-      const __bf16* Rt = tl[cur][0];
-      const __bf16* Gt = tl[cur][1];
-      const __bf16* Ot = tl[cur][2];
-      const float* l2r = ts[cur][0];
-      const float* Dr = ts[cur][1];
+    // step k reads slot k % 3; query chunk k + 2 goes into slot (k + 2) % 3, last read in step k - 1
+    auto step = [&](auto S, int64_t k) PA_INLINE {
+      constexpr int sc = decltype(S)::value;
+      const PairSlot cur = ring(S);
+      const __bf16* Rt = cur.t[0];
+      const __bf16* Gt = cur.t[1];
+      const __bf16* Ot = cur.t[2];
+      const float* l2r = cur.rows[0];
+      const float* Dr = cur.rows[1];
       const float ofs = offn;
       if constexpr (FOX) offn = Off[band.slot(bh, m0 + (k + 1 < steps ? k + 1 : k), n)];
-      f32x4 zt[4], pt[4], gt[4];
+      f32x4 pt[4], gt[4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
         f32x4 z = zero, dp = zero;
@@ -465,9 +497,7 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
           pt[qt][i] = p;
           gt[qt][i] = kLn2 * dz;
         }
-        zt[qt] = z;
       }
-      (void)zt;
       dv_update(Ot, pt);
       {
         bf16x8 gh[2];
@@ -489,15 +519,18 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
         }
       }
       // ring: query chunk k + 2 into the slot two ahead, chunk k + 1 has landed
-      const int nxt = cur == 2 ? 0 : cur + 1;
       if (k + 2 < steps) {
-        stage(k + 2, nxt == 2 ? 0 : nxt + 1);
+        stage(k + 2, ring(slot_c<(sc + 2) % kRingSlots>{}));
         wait_vm<OPS>();
       } else {
         wait_vm<0>();
       }
       lds_barrier();
-      cur = nxt;
+    };
+    for (int64_t k = 0; k < steps; k += kRingSlots) {
+      step(slot_c<0>{}, k);
+      if (k + 1 < steps) step(slot_c<1>{}, k + 1);
+      if (k + 2 < steps) step(slot_c<2>{}, k + 2);
     }
   }
 
