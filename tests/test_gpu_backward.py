@@ -86,6 +86,15 @@ def test_beta_zero_leaves_w_without_gradient():
     assert np.all(got[3] == 0.0)
 
 
+def test_bf16_beta_zero_leaves_w_without_gradient():
+    """The matrix-core backward (bf16, d = chunk = 64) at beta = 0: the output does not depend on w, and
+    every term of dw in the per-chunk gradient kernel is a product with diag(beta) = 0 (Ti = A^-1 diag(beta),
+    X = Ti U, Y = R Ti, dU, dR and dN all vanish), so dw must be exactly zero, not merely small."""
+    x = synth.make_fwd_inputs(1, 2, 200, 64, recipe="beta0", dtype="bf16", seed=5)
+    got, _ = check(x, 64, "bf16 beta0", seed=6)
+    assert np.all(got[3] == 0.0)
+
+
 @pytest.mark.parametrize("recipe", ["lm", "fox", "stress_qk"])
 def test_bf16_backward(recipe):
     x = synth.make_fwd_inputs(1, 2, 300, 64, recipe=recipe, dtype="bf16", seed=11)
