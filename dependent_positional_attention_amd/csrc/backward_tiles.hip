@@ -65,22 +65,32 @@ using slot_c = std::integral_constant<int, S>;
 
 }  // namespace
 
+#ifndef PATHATTN_QUERY_BLOCKS_PER_CU
+#define PATHATTN_QUERY_BLOCKS_PER_CU 3
+#endif
+constexpr int kQueryBlocksPerCu = PATHATTN_QUERY_BLOCKS_PER_CU;
+
 // Query-chunk kernel: one block of 4 waves per (query chunk m of the band, batch*head); wave w owns the
 // queries a = 16w .. 16w+15 of the chunk (lane (r, g) query 16w + r).  Writes the states r^(n) and the
 // incoming gradients dr^(n-1) of every pair (m, n < m) (bf16 tiles [query][d], columns permuted), the
 // FoX offsets of each pair, the row statistics (lse2, D), the in-chunk logit gradient dS (unscaled
 // units, fp32 square), d qtilde (unscaled, fp32) and the row sums of dz.
 template <bool FOX>
-__global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
+__global__ __launch_bounds__(256, kQueryBlocksPerCu) void bwd_query_tile_kernel(
     const __bf16* __restrict__ qt, const __bf16* __restrict__ kt, const __bf16* __restrict__ Pm,
     const float* __restrict__ Sm, const float* __restrict__ fl, const float* __restrict__ ftot,
     const __bf16* __restrict__ v, const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
     const float* __restrict__ lse, int64_t L, int64_t M, float scale, pair_band band, __bf16* __restrict__ St,
     __bf16* __restrict__ Gst, float* __restrict__ Off, float* __restrict__ lse2w, float* __restrict__ Dw,
     float* __restrict__ drow, float* __restrict__ dqt, float* __restrict__ dSm, int64_t BH) {
-  constexpr int OPS = slot_ops<FOX ? 1 : 0>();
-  __shared__ __align__(1024) __bf16 tl[kRingSlots][kPairTiles][kTile];  // ktilde_n, V_n, P_n
-  __shared__ __align__(16) float tf[kRingSlots][64];                     // FoX chunk-local prefix of chunk n
+  // two ring slots of ktilde_n, V_n, P_n tiles and the FoX chunk-local prefix of chunk n, every tile and
+  // row an LDS variable of its own (as in PairSlot; the loops below name their slots at compile time)
+  __shared__ __align__(1024) __bf16 qk0[kTile], qv0[kTile], qp0[kTile], qk1[kTile], qv1[kTile], qp1[kTile];
+  __shared__ __align__(16) float qf0[64], qf1[64];
+  auto qslot = [&](auto S) PA_INLINE -> PairSlot {
+    if constexpr (decltype(S)::value == 0) return PairSlot{{qk0, qv0, qp0}, {qf0, qf0}};
+    else return PairSlot{{qk1, qv1, qp1}, {qf1, qf1}};
+  };
 
   int64_t bh, q;
   if (!bwd_pair_block(BH, band.me - band.mb, bh, q)) return;  // whole block
@@ -127,42 +137,34 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) rb[ks] = *reinterpret_cast<const bf16x8*>(qt + (row0 + a) * 64 + 32 * ks + 8 * g);
   {
-    auto stage_p = [&](int64_t n, int s) PA_INLINE {
-      dma_tile<2>(tl[s][2], Pm + ((size_t)bh * M + (size_t)n) * 4096, 64, i0);
+    auto stage_p = [&](int64_t n, const PairSlot& sl) PA_INLINE {
+      dma_tile<2>(sl.t[2], Pm + ((size_t)bh * M + (size_t)n) * 4096, 64, i0);
     };
     if (m >= 2) {
-      stage_p(m - 1, 0);
-      if (m >= 3) {
-        stage_p(m - 2, 1);
-        wait_vm<2>();
-      } else {
-        wait_vm<0>();
-      }
+      stage_p(m - 1, qslot(slot_c<0>{}));
+      wait_vm<0>();
       lds_barrier();
     }
     float off = 0.f;
-    int cur = 0;
-    for (int64_t n = m - 1; n >= 0; --n) {
+    // step i of the pass (n = m - 1 - i) reads slot i & 1 and first sends P_{n-1} into the other slot
+    // (last read in step i - 1, which every wave has left)
+    auto p1step = [&](auto S, int64_t n) PA_INLINE {
+      constexpr int sc = decltype(S)::value;
       const size_t pr = band.slot(bh, m, n);
       if constexpr (FOX) off += ftot[bh * M + n];
       bf16x8 rn[2] = {rb[0], rb[1]};
       if (n > 0) {
+        if (n - 1 >= 1) stage_p(n - 1, qslot(slot_c<sc ^ 1>{}));
+        const __bf16* Pt = qslot(S).t[2];
         f32x4 rt[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           rt[dt] = zero;
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) rt[dt] = mfma16(tile_frag(tl[cur][2], 16 * dt + r, 4 * ks + g), rb[ks], rt[dt]);
+          for (int ks = 0; ks < 2; ++ks) rt[dt] = mfma16(tile_frag(Pt, 16 * dt + r, 4 * ks + g), rb[ks], rt[dt]);
         }
-        const int nxt = cur == 2 ? 0 : cur + 1;
-        if (n - 2 >= 1) {
-          stage_p(n - 2, nxt == 2 ? 0 : nxt + 1);
-          wait_vm<2>();
-        } else {
-          wait_vm<0>();
-        }
+        wait_vm<0>();
         lds_barrier();
-        cur = nxt;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -174,6 +176,10 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
         *reinterpret_cast<bf16x8*>(St + pr * 4096 + a * 64 + 32 * ks + 8 * g) = rb[ks];
       rb[0] = rn[0];
       rb[1] = rn[1];
+    };
+    for (int64_t i = 0; i < m; i += 2) {
+      p1step(slot_c<0>{}, m - 1 - i);
+      if (i + 1 < m) p1step(slot_c<1>{}, m - 2 - i);
     }
   }
   lds_barrier();  // every wave is done with the P slots before the ring below reuses them
@@ -181,28 +187,37 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
   // ---------------------------------------------------------------- key chunks through the LDS ring
   // stream position j: 0 = the own chunk m (in-chunk block), then n = j - 1 = 0 .. m-1
   auto chunk_at = [&](int64_t j) PA_INLINE -> int64_t { return j == 0 ? m : j - 1; };
-  auto stage = [&](int64_t j, int s) PA_INLINE {
+  auto stage = [&](int64_t j, const PairSlot& sl) PA_INLINE {
     const int64_t n = chunk_at(j);
     const int64_t vr = L - n * 64;
-    dma_tile<2>(tl[s][0], kt + ((size_t)bh * Lp + (size_t)n * 64) * 64, 64, i0);
-    dma_tile<2>(tl[s][1], v + ((size_t)bh * L + (size_t)n * 64) * 64, vr < 64 ? (int)vr : 64, i0);
-    dma_tile<2>(tl[s][2], Pm + ((size_t)bh * M + (size_t)n) * 4096, 64, i0);
-    if constexpr (FOX) row_to_lds(tf[s], fl + (size_t)bh * Lp + (size_t)n * 64, wave, l);
+    dma_tile<2>(sl.t[0], kt + ((size_t)bh * Lp + (size_t)n * 64) * 64, 64, i0);
+    dma_tile<2>(sl.t[1], v + ((size_t)bh * L + (size_t)n * 64) * 64, vr < 64 ? (int)vr : 64, i0);
+    dma_tile<2>(sl.t[2], Pm + ((size_t)bh * M + (size_t)n) * 4096, 64, i0);
+    if constexpr (FOX) row_to_lds(sl.rows[0], fl + (size_t)bh * Lp + (size_t)n * 64, wave, l);
   };
   const int64_t steps = m + 1;
-  stage(0, 0);
-  if (steps > 1) {
-    stage(1, 1);
-    wait_vm<OPS>();
-  } else {
-    wait_vm<0>();
-  }
+  stage(0, qslot(slot_c<0>{}));
+  wait_vm<0>();
   lds_barrier();
+  // the first key chunk and its state are requested before the in-chunk block (which reads slot 0 only)
+  bf16x8 rn[2];  // r^(n) of the next step, from the pair states
+  float offn = 0.f;
+  auto fetch_state = [&](int64_t n) PA_INLINE {
+    const size_t pr = band.slot(bh, m, n);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) rn[ks] = *reinterpret_cast<const bf16x8*>(St + pr * 4096 + a * 64 + 32 * ks + 8 * g);
+    if constexpr (FOX) offn = Off[pr];
+  };
+  if (m > 0) {
+    fetch_state(0);
+    stage(1, qslot(slot_c<1>{}));
+  }
 
   float rs = 0.f;  // row sum of dz for query a, this lane's keys
   // in-chunk block: logits from the packed S, dO V_m^T on the matrix cores
   {
-    const __bf16* Vt = tl[0][1];
+    const PairSlot s0 = qslot(slot_c<0>{});
+    const __bf16* Vt = s0.t[1];
     f32x4 dp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -222,11 +237,10 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int b = 16 * t + 4 * g + i;
-        float dz = 0.f;
-        if (b <= a) {
-          const float z2 = sv[i] - (FOX ? kLog2e * tf[0][b] : 0.f);
-          dz = fast_exp2(z2 - l2a) * (dp[t][i] - Da);
-        }
+        // computed for every key, kept on and below the diagonal (entries past it are unspecified)
+        const float z2 = sv[i] - (FOX ? kLog2e * s0.rows[0][b] : 0.f);
+        const float dze = fast_exp2(z2 - l2a) * (dp[t][i] - Da);
+        const float dz = b <= a ? dze : 0.f;
         rs += dz;
         dz4[i] = scale * dz;
       }
@@ -238,37 +252,24 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
   f32x4 dR[4];  // dr^(n-1) transposed: [d 16 dt + 4g + i][query a]
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dR[dt] = zero;
-  bf16x8 rn[2];  // r^(n) of the next step, from the pair states
-  float offn = 0.f;
-  auto fetch_state = [&](int64_t n) PA_INLINE {
-    const size_t pr = band.slot(bh, m, n);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) rn[ks] = *reinterpret_cast<const bf16x8*>(St + pr * 4096 + a * 64 + 32 * ks + 8 * g);
-    if constexpr (FOX) offn = Off[pr];
-  };
-  if (m > 0) fetch_state(0);
-  int cur = 0;
-  for (int64_t j = 1; j < steps; ++j) {
-    // advance the ring: chunk j + 1 into the slot two ahead (after the last LDS read of step j - 1),
-    // chunk j (issued one step earlier) has landed
-    {
-      const int nxt = cur == 2 ? 0 : cur + 1;
-      if (j + 1 < steps) {
-        stage(j + 1, nxt == 2 ? 0 : nxt + 1);
-        wait_vm<OPS>();
-      } else {
-        wait_vm<0>();
-      }
-      lds_barrier();
-      cur = nxt;
+  // step j reads slot j & 1; it waits for everything (its chunk and state, requested one step earlier),
+  // then requests the next step's state and chunk (into the slot of step j - 1, which every wave has left)
+  auto p2step = [&](auto S, int64_t j) PA_INLINE {
+    constexpr int sc = decltype(S)::value;
+    wait_vm<0>();
+    lds_barrier();
+    bf16x8 rcur[2] = {rn[0], rn[1]};
+    const float ofs = offn;
+    if (j + 1 < steps) {
+      fetch_state(j);  // r^(j), the state of step j + 1 (requested before the copies, into live registers)
+      stage(j + 1, qslot(slot_c<sc ^ 1>{}));
     }
     const int64_t n = j - 1;
     const size_t pr = band.slot(bh, m, n);
-    const __bf16* Kt = tl[cur][0];
-    const __bf16* Vt = tl[cur][1];
-    const __bf16* Pt = tl[cur][2];
-    bf16x8 rcur[2] = {rn[0], rn[1]};
-    const float ofs = offn;
+    const PairSlot cur = qslot(S);
+    const __bf16* Kt = cur.t[0];
+    const __bf16* Vt = cur.t[1];
+    const __bf16* Pt = cur.t[2];
     // dr^(n-1) as the operand (hi + lo); its hi part is the pair's stored gradient state
     bf16x8 dh[2], dl[2];
     acc_to_op(dR, dh, dl);
@@ -276,7 +277,6 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<bf16x8*>(Gst + pr * 4096 + a * 64 + 32 * ks + 8 * g) = dh[ks];
     }
-    if (n + 1 < m) fetch_state(n + 1);
     f32x4 zt[4], dp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int b = 16 * t + 4 * g + i;
-        const float z2 = zt[t][i] + (FOX ? kLog2e * (ofs - tf[cur][b]) : 0.f);
+        const float z2 = zt[t][i] + (FOX ? kLog2e * (ofs - cur.rows[0][b]) : 0.f);
         const float dz = fast_exp2(z2 - l2a) * (dp[t][i] - Da);
         rs += dz;
         gt[t][i] = kLn2 * dz;
@@ -319,6 +319,10 @@ __global__ __launch_bounds__(256, 2) void bwd_query_tile_kernel(
       }
       dR[dt] = acc;
     }
+   };
+  for (int64_t j = 1; j < steps; j += 2) {
+    p2step(slot_c<1>{}, j);
+    if (j + 1 < steps) p2step(slot_c<0>{}, j + 1);
   }
 
   // d qtilde = dr^(m-1) (qtilde entered the scan scaled by scale * log2e), row sums of dz
