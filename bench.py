@@ -235,8 +235,8 @@ def bench_backward(args, res, ctx):
             "ms": ms, "steps": n, "tokens_per_s": B * L / (ms * 1e-3), "flops": F, "tflops": tf, "bound": "mfma",
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
             "bf16x3_peak": x3_peak, "frac_of_bf16x3_peak": tf / x3_peak,
-            "note": "the products run on the bf16 matrix cores (bf16 operands exact, other fp32 operands split "
-                    "into hi+lo), so peak = dense bf16 peak; bf16x3_peak = bf16 peak / 3 (an fp32-accurate "
+            "note": "the products run on the bf16 matrix cores (bf16 operands exact, p and dz rounded to bf16 "
+                    "once, other fp32 operands split into hi+lo), so peak = dense bf16 peak; bf16x3_peak = bf16 peak / 3 (an fp32-accurate "
                     "product as three bf16 products)",
             "workspace_bytes": nbytes}
 
