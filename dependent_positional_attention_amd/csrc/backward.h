@@ -17,14 +17,18 @@ struct bwd_buffers {
   float *Zi;                             // A^{-1} per chunk (bf16 inputs at d = chunk = 64), else unused
 };
 
-// The chunk-pair kernels take the query chunks in bands of 2 ceil(sqrt(M)) chunks (M chunks per head) and
+// The chunk-pair kernels take the query chunks in bands of 4 ceil(sqrt(M)) chunks (M chunks per head) and
 // hold the per-pair states of one band at a time, so that the workspace grows as L d sqrt(L / chunk)
 // per head rather than as L^2 d / chunk.  (The key-side sums are re-read and re-written once per band:
-// bands twice as wide halve that traffic for twice the states.)
+// bands twice as wide halve that traffic for about twice the states.  At B=8, H=24, L=4096, per call:
+// bands of 2, 4 and 8 ceil(sqrt(M)) chunks 6.00, 5.64-5.71 and 5.60-5.65 ms for 4.4, 6.4 and 7.9 GB.)
+#ifndef PATHATTN_BAND_FACTOR
+#define PATHATTN_BAND_FACTOR 4
+#endif
 inline int64_t bwd_band_chunks(int64_t M) {
   int64_t b = 1;
   while (b * b < M) ++b;
-  return 2 * b < M ? 2 * b : (M > 0 ? M : 1);
+  return PATHATTN_BAND_FACTOR * b < M ? PATHATTN_BAND_FACTOR * b : (M > 0 ? M : 1);
 }
 // Pairs (m, n < m) of the largest band: the per-head slab of the pair states.
 inline int64_t bwd_band_pairs(int64_t M) {

@@ -313,7 +313,7 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
  * forward with the chain rule: logits of each pair of chunks are recomputed from
  * lse, the running queries and their gradients of each (query chunk, key chunk)
  * pair are kept in the workspace (a transition with beta = 1 is singular, so
- * they cannot be recovered backwards) for one band of about 2 sqrt(L / chunk)
+ * they cannot be recovered backwards) for one band of about 4 sqrt(L / chunk)
  * query chunks at a time, the key-side sums carrying over from band to band,
  * and each chunk's UT-transform terms are differentiated back to q, k, w and
  * beta.
@@ -340,8 +340,8 @@ path_status path_attn_cache_from_prefill(const void* v, const float* log_forget,
  * products throughout.
  * Workspace: path_attn_bwd_workspace_bytes; it grows as B*H*L*d*sqrt(L/chunk)
  * (two vectors per key of every chunk pair of one band, bf16 for bf16 inputs:
- * about 4.4 GB at B=8, H=24, L=4096, d=64, chunk 64 and 10.4 GB at B=1, H=24,
- * L=32768; 7.4 and 19.3 GB for fp32 inputs).  The kernels are deterministic:
+ * about 6.4 GB at B=8, H=24, L=4096, d=64, chunk 64 and 16.6 GB at B=1, H=24,
+ * L=32768; 11.4 and 31.8 GB for fp32 inputs).  The kernels are deterministic:
  * the same inputs give the same bits.  Errors as for path_attn_fwd; nothing is
  * enqueued on an error.
  */

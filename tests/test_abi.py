@@ -237,8 +237,8 @@ def test_bwd_workspace_planning(L):
     n = ctypes.c_size_t(0)
     assert L.path_attn_bwd_workspace_bytes(8, 24, 4096, 64, 64, BF16, ctypes.byref(n)) == OK
     # states and their gradients of one band of query chunks at a time (bf16 for a bf16 input): 64 chunks
-    # in bands of 2 ceil(sqrt(64)) = 16, the largest band (chunks 48 .. 63) holding 48 + ... + 63 pairs
-    pairs = sum(range(48, 64))
+    # in bands of 4 ceil(sqrt(64)) = 32, the largest band (chunks 32 .. 63) holding 32 + ... + 63 pairs
+    pairs = sum(range(32, 64))
     assert n.value >= 2 * 8 * 24 * pairs * 64 * 64 * 2
     assert n.value < 2 * 8 * 24 * pairs * 64 * 64 * 2 + (2 << 30)
     nf = ctypes.c_size_t(0)
@@ -270,7 +270,7 @@ def test_bwd_workspace_grows_as_l_sqrt_l(L):
         return n.value
     for Lq in (4096, 16384):
         assert size(4 * Lq) <= 8.5 * size(Lq), Lq
-    assert size(32768, 1, 24) < 12e9  # long-context shape: 24 heads of 32768 tokens
+    assert size(32768, 1, 24) < 18e9  # long-context shape: 24 heads of 32768 tokens
 
 
 def test_bwd_validation(L):
