@@ -12,8 +12,9 @@
 // into an MFMA operand in registers (acc_to_op); a state's operand form is also a row of a tile with
 // permuted columns, so the pair states r^(n) and dr^(n-1) are stored as such tiles with one 16-byte
 // store per lane and k-step, and the key-side kernel reads them back as row fragments (tile_frag) and
-// as column fragments (LDS transpose reads, tr_frag).  ktilde, V and P stream through a ring of three
-// LDS slots filled by direct global->LDS copies, as in the prefill's scan.
+// as column fragments (LDS transpose reads, tr_frag).  The streamed tiles (ktilde, V and P on the query
+// side, the pair states and dO on the key side) pass through rings of LDS slots (two on the query side,
+// three on the key side) filled by direct global->LDS copies, as in the prefill's scan.
 #include <type_traits>
 
 #include "backward.h"
@@ -23,7 +24,7 @@ namespace pathattn {
 
 namespace {
 
-constexpr int kRingSlots = 3;
+constexpr int kRingSlots = 3;  // ring slots of the key-side kernel
 constexpr int kPairTiles = 3;  // tiles per ring slot
 
 // Copies of one ring slot per wave: three tiles (2 instructions each) and `extra` 4-byte row loads.
@@ -37,34 +38,23 @@ __device__ __forceinline__ void row_to_lds(float* dst, const float* src, int wav
     __builtin_amdgcn_global_load_lds((const void*)(src + 16 * wave + l), (lds_void*)(dst + 16 * wave), 4, 0, 0);
 }
 
-// One slot of the chunk-pair kernels' LDS ring: three tiles and two 64-float rows, each an LDS variable
-// of its own.  The ring loops are unrolled over the slots, so each LDS access names its variable at
-// compile time, and an address is at most a few steps from it: the compiler then keeps the variable's
-// alias scope on the access, sees that a transpose read of one slot cannot touch the copies still in
+// One slot of the chunk-pair kernels' LDS rings: three tiles and up to two 64-float rows, each an LDS
+// variable of its own.  The ring loops are unrolled over the slots, so each LDS access names its
+// variable at compile time, and an address is at most a few steps from it: the compiler then keeps the
+// variable's alias scope on the access, sees that a read of one slot cannot touch the copies still in
 // flight into the others, and does not drain them before it.  (A read whose scope is lost waits for
 // every copy in flight.)
 struct PairSlot {
   __bf16* t[kPairTiles];
   float* rows[2];
 };
-#define PA_PAIR_RING_LDS(name)                                                                          \
-  __shared__ __align__(1024) __bf16 name##_t00[kTile], name##_t01[kTile], name##_t02[kTile];          \
-  __shared__ __align__(1024) __bf16 name##_t10[kTile], name##_t11[kTile], name##_t12[kTile];          \
-  __shared__ __align__(1024) __bf16 name##_t20[kTile], name##_t21[kTile], name##_t22[kTile];          \
-  __shared__ __align__(16) float name##_r00[64], name##_r01[64], name##_r10[64], name##_r11[64],     \
-      name##_r20[64], name##_r21[64];                                                                 \
-  auto name = [&](auto S) PA_INLINE -> PairSlot {                                                     \
-    constexpr int sidx = decltype(S)::value;                                                          \
-    static_assert(sidx >= 0 && sidx < kRingSlots, "ring slot");                                       \
-    if constexpr (sidx == 0) return PairSlot{{name##_t00, name##_t01, name##_t02}, {name##_r00, name##_r01}}; \
-    else if constexpr (sidx == 1) return PairSlot{{name##_t10, name##_t11, name##_t12}, {name##_r10, name##_r11}}; \
-    else return PairSlot{{name##_t20, name##_t21, name##_t22}, {name##_r20, name##_r21}};             \
-  }
 template <int S>
 using slot_c = std::integral_constant<int, S>;
 
 }  // namespace
 
+// The query-side kernel's two ring slots take 49 KB of LDS, so three blocks share a CU when their registers
+// fit (launch bound): 760 against 795 us per band with two blocks and three slots.
 #ifndef PATHATTN_QUERY_BLOCKS_PER_CU
 #define PATHATTN_QUERY_BLOCKS_PER_CU 3
 #endif
@@ -88,8 +78,8 @@ __global__ __launch_bounds__(256, kQueryBlocksPerCu) void bwd_query_tile_kernel(
   __shared__ __align__(1024) __bf16 qk0[kTile], qv0[kTile], qp0[kTile], qk1[kTile], qv1[kTile], qp1[kTile];
   __shared__ __align__(16) float qf0[64], qf1[64];
   auto qslot = [&](auto S) PA_INLINE -> PairSlot {
-    if constexpr (decltype(S)::value == 0) return PairSlot{{qk0, qv0, qp0}, {qf0, qf0}};
-    else return PairSlot{{qk1, qv1, qp1}, {qf1, qf1}};
+    if constexpr (decltype(S)::value == 0) return PairSlot{{qk0, qv0, qp0}, {qf0, nullptr}};
+    else return PairSlot{{qk1, qv1, qp1}, {qf1, nullptr}};
   };
 
   int64_t bh, q;
@@ -352,7 +342,16 @@ __global__ __launch_bounds__(256, 2) void bwd_key_tile_kernel(
     float* __restrict__ dva, float* __restrict__ dkt, float* __restrict__ dPm, float* __restrict__ dcol,
     int64_t BH) {
   // ring slots: r^(n)_m, dr^(n-1)_m, dO_m tiles; lse2 and D rows of chunk m
-  PA_PAIR_RING_LDS(ring);
+  __shared__ __align__(1024) __bf16 kr0[kTile], kg0[kTile], ko0[kTile], kr1[kTile], kg1[kTile], ko1[kTile];
+  __shared__ __align__(1024) __bf16 kr2[kTile], kg2[kTile], ko2[kTile];
+  __shared__ __align__(16) float kl0[64], kd0[64], kl1[64], kd1[64], kl2[64], kd2[64];
+  auto ring = [&](auto S) PA_INLINE -> PairSlot {
+    constexpr int sidx = decltype(S)::value;
+    static_assert(sidx >= 0 && sidx < kRingSlots, "ring slot");
+    if constexpr (sidx == 0) return PairSlot{{kr0, kg0, ko0}, {kl0, kd0}};
+    else if constexpr (sidx == 1) return PairSlot{{kr1, kg1, ko1}, {kl1, kd1}};
+    else return PairSlot{{kr2, kg2, ko2}, {kl2, kd2}};
+  };
 
   int64_t bh, n;
   if (!bwd_pair_block(BH, band.me, bh, n)) return;  // whole block; low key chunks first
