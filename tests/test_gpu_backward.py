@@ -79,6 +79,15 @@ def test_fp32_backward_ragged(L):
     check(x, 16, f"ragged L={L}", seed=L)
 
 
+@pytest.mark.parametrize("L,d,chunk", [(704, 16, 16), (1664, 64, 64)])
+def test_fp32_backward_two_bands(L, d, chunk):
+    """fp32 inputs long enough for two bands of query chunks (4 ceil(sqrt(M)) chunks each: M = 44 and 26
+    chunks), so the key-side sums carry from one band to the next, on the vector kernels and on the fp32
+    matrix cores; PaTH-FoX, one head."""
+    x = synth.make_fwd_inputs(1, 1, L, d, recipe="fox", dtype="f32", seed=L)
+    check(x, chunk, f"f32 two bands L={L} d={d} C={chunk}", seed=L + 1)
+
+
 def test_beta_zero_leaves_w_without_gradient():
     """With every beta = 0 the output does not depend on w: dw must be exactly zero."""
     x = synth.make_fwd_inputs(1, 2, 130, 32, recipe="beta0", dtype="f32", seed=4)
