@@ -217,9 +217,13 @@ def bench_backward(args, res, ctx):
     def run():
         native.path_attn_bwd(q, k, v, w, beta, out, lse, dout, logf, scale=scale, chunk=C, workspace=ws, grads=grads)
 
-    run()
-    torch.cuda.synchronize()
-    n = 3
+    # warm up as the prefill does (the clock settles over the first runs): at least 3 calls and 0.3 s
+    t0, runs = time.perf_counter(), 0
+    while runs < 3 or time.perf_counter() - t0 < 0.3:
+        run()
+        torch.cuda.synchronize()
+        runs += 1
+    n = 5
     ms = timed(run, n)
     for g in grads:
         if g is not None:
