@@ -149,6 +149,14 @@ def test_bf16_backward_long_chain():
     check(x, 64, "bf16 L=2048", seed=42)
 
 
+def test_bf16_backward_two_bands_ragged():
+    """The matrix-core backward over two bands of query chunks (L = 1637: 26 chunks in bands of 24) with a
+    ragged last chunk (37 tokens), two heads, PaTH-FoX: the band boundary, the key-side sums carried
+    across it and the clamped rows of the last chunk together."""
+    x = synth.make_fwd_inputs(1, 2, 1637, 64, recipe="fox", dtype="bf16", seed=51)
+    check(x, 64, "bf16 two bands ragged L=1637", seed=52)
+
+
 @pytest.mark.parametrize("L", [1, 40, 64, 65, 129])
 def test_bf16_backward_short_and_ragged(L):
     """The matrix-core backward (d = chunk = 64) at its edges: one partial chunk (no chunk pairs at all),
